@@ -1,0 +1,247 @@
+"""CPU oracle for the fused MoE layer (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  It wraps oracle/moe_oracle.c, a plain scalar C
+implementation of the layer's definition, through ctypes.  It shares no code
+with the GPU library (moe_layer_align_amd), and the GPU library never falls
+back to it.
+
+Functions:
+  build()                      compile moe_oracle.c with gcc
+  route(logits, k)             -> ids int32 [M,k], weights fp32 [M,k]
+  align(ids, E, B, cap)        -> counts, offsets, sorted_ids, block_expert, num_padded
+  layer(inputs, tokens, ...)   -> y_ref float64 [len(tokens), H] and intermediates
+  bf16_encode / e4m3_encode / e4m3_decode   number-format helpers (numpy)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+DTYPE_BF16 = 0
+DTYPE_E4M3 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no contraction, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _LayerArgs(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64),
+        ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p),
+        ("logits", ctypes.c_void_p),
+        ("w13", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("w13_scale", ctypes.c_float), ("w2_scale", ctypes.c_float),
+        ("x_scale_static", ctypes.c_int32), ("x_scale", ctypes.c_float),
+        ("h_scale_static", ctypes.c_int32), ("h_scale", ctypes.c_float),
+        ("tokens", ctypes.c_void_p), ("n_tokens", ctypes.c_int64),
+        ("y", ctypes.c_void_p),
+        ("ids", ctypes.c_void_p),
+        ("weights", ctypes.c_void_p),
+        ("s_x_out", ctypes.c_void_p),
+        ("s_h_out", ctypes.c_void_p),
+        ("all_pairs_h", ctypes.c_int32),
+    ]
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_bf16_decode.restype = ctypes.c_double
+    lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_encode.restype = ctypes.c_uint16
+    lib.oracle_bf16_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_scale_from_amax.restype = ctypes.c_float
+    lib.oracle_scale_from_amax.argtypes = [ctypes.c_float]
+    lib.oracle_route.restype = ctypes.c_int
+    lib.oracle_route.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_align.restype = ctypes.c_int
+    lib.oracle_align.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_layer.restype = ctypes.c_int
+    lib.oracle_layer.argtypes = [ctypes.POINTER(_LayerArgs)]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _np(t) -> np.ndarray:
+    """torch tensor or array -> contiguous numpy view (host)."""
+    if hasattr(t, "detach"):
+        import torch
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
+        return t.numpy()
+    return np.ascontiguousarray(t)
+
+
+# ---------------------------------------------------------------- formats
+def bf16_encode(v: np.ndarray) -> np.ndarray:
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    return np.array([lib.oracle_bf16_encode(float(a)) for a in v], dtype=np.uint16)
+
+
+def bf16_decode(c: np.ndarray) -> np.ndarray:
+    lib = _load()
+    return np.array([lib.oracle_bf16_decode(int(a)) for a in np.ravel(c)], dtype=np.float64)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    return np.array([lib.oracle_e4m3_encode(float(a)) for a in v], dtype=np.uint8)
+
+
+def e4m3_decode(c: np.ndarray) -> np.ndarray:
+    lib = _load()
+    return np.array([lib.oracle_e4m3_decode(int(a)) for a in np.ravel(c)], dtype=np.float64)
+
+
+def scale_from_amax(amax: float) -> float:
+    return float(_load().oracle_scale_from_amax(float(amax)))
+
+
+# ---------------------------------------------------------------- routing
+def route(logits, k: int):
+    lib = _load()
+    lg = np.ascontiguousarray(_np(logits), dtype=np.float32)
+    M, E = lg.shape
+    ids = np.zeros((M, k), dtype=np.int32)
+    w = np.zeros((M, k), dtype=np.float32)
+    rc = lib.oracle_route(_ptr(lg), M, E, k, _ptr(ids), _ptr(w))
+    if rc:
+        raise ValueError("oracle_route failed with code %d" % rc)
+    return ids, w
+
+
+def align_capacity(P: int, E: int, B: int) -> int:
+    """Upper bound on the padded length: every expert that holds a pair can
+    add at most B-1 sentinels, and at most min(E, P) experts hold one."""
+    cap = P + min(E, P) * (B - 1)
+    return ((cap + B - 1) // B) * B
+
+
+def align(ids, E: int, B: int, capacity: Optional[int] = None):
+    lib = _load()
+    f = np.ascontiguousarray(_np(ids), dtype=np.int32).ravel()
+    P = f.size
+    cap = align_capacity(P, E, B) if capacity is None else capacity
+    counts = np.zeros(E, dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    sorted_ids = np.full(max(cap, 1), -7, dtype=np.int32)
+    nblk = max(cap // B, 1)
+    block_expert = np.full(nblk, -7, dtype=np.int32)
+    num = np.zeros(1, dtype=np.int32)
+    rc = lib.oracle_align(_ptr(f), P, E, B, _ptr(counts), _ptr(offsets), _ptr(sorted_ids), cap,
+                          _ptr(block_expert), cap // B, _ptr(num))
+    if rc:
+        raise ValueError("oracle_align failed with code %d" % rc)
+    return dict(counts=counts, offsets=offsets, sorted_ids=sorted_ids[:cap], block_expert=block_expert[:cap // B],
+                num_padded=int(num[0]))
+
+
+# ---------------------------------------------------------------- layer
+def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = None,
+          w2_scale: Optional[float] = None, x_scale: Optional[float] = None, h_scale: Optional[float] = None,
+          tokens: Optional[Sequence[int]] = None, experts: Optional[dict] = None, all_pairs_h: Optional[bool] = None):
+    """Reference output of the layer.
+
+    x: bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] / w2 [E,H,I] (bf16 or e4m3
+    codes), or None together with `experts`, a dict e -> (w13_e, w2_e) holding
+    only the experts that are needed.  x_scale/h_scale: static fp8 activation
+    scales, None = dynamic amax/448.  tokens: rows of y to produce (default all).
+    Returns dict(y=float64 [T,H], ids, weights, s_x, s_h).
+    """
+    lib = _load()
+    xa = _np(x)
+    if xa.dtype != np.uint16:
+        raise TypeError("x must be bf16")
+    lg = np.ascontiguousarray(_np(logits), dtype=np.float32)
+    M, H = xa.shape
+    E = lg.shape[1]
+    fp8 = dtype == "fp8"
+    keep = []  # keep numpy buffers alive
+    p13 = (ctypes.c_void_p * E)()
+    p2 = (ctypes.c_void_p * E)()
+    I = None
+    if experts is None:
+        a13, a2 = _np(w13), _np(w2)
+        keep += [a13, a2]
+        I = a13.shape[1] // 2
+        for e in range(E):
+            p13[e] = a13[e].ctypes.data
+            p2[e] = a2[e].ctypes.data
+    else:
+        for e in range(E):
+            if e in experts:
+                a13, a2 = _np(experts[e][0]), _np(experts[e][1])
+                keep += [a13, a2]
+                I = a13.shape[0] // 2
+                p13[e] = a13.ctypes.data
+                p2[e] = a2.ctypes.data
+            else:
+                p13[e] = None
+                p2[e] = None
+    if tokens is None:
+        tokens = list(range(M))
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    y = np.zeros((len(tok), H), dtype=np.float64)
+    ids = np.zeros((M, k), dtype=np.int32)
+    w = np.zeros((M, k), dtype=np.float32)
+    sx = np.zeros(1, dtype=np.float32)
+    sh = np.zeros(1, dtype=np.float32)
+    if all_pairs_h is None:
+        all_pairs_h = fp8 and h_scale is None
+    args = _LayerArgs(
+        M=M, E=E, H=H, I=I, k=k, dtype=DTYPE_E4M3 if fp8 else DTYPE_BF16,
+        x=_ptr(xa), logits=_ptr(lg),
+        w13=ctypes.cast(p13, ctypes.c_void_p), w2=ctypes.cast(p2, ctypes.c_void_p),
+        w13_scale=float(w13_scale or 0.0), w2_scale=float(w2_scale or 0.0),
+        x_scale_static=int(x_scale is not None), x_scale=float(x_scale or 0.0),
+        h_scale_static=int(h_scale is not None), h_scale=float(h_scale or 0.0),
+        tokens=_ptr(tok) if tok.size else None, n_tokens=tok.size,
+        y=_ptr(y) if y.size else None, ids=_ptr(ids) if ids.size else None, weights=_ptr(w) if w.size else None,
+        s_x_out=_ptr(sx), s_h_out=_ptr(sh), all_pairs_h=int(bool(all_pairs_h)),
+    )
+    rc = lib.oracle_layer(ctypes.byref(args))
+    if rc:
+        raise ValueError("oracle_layer failed with code %d" % rc)
+    return dict(y=y, ids=ids, weights=w, s_x=float(sx[0]), s_h=float(sh[0]))
