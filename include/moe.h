@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused Mixture-of-Experts layer.
+ *
+ * The layer, as the web pages on the subject describe it, combines token
+ * routing, the movement of tokens to their experts and the expert computation
+ * into one batched GPU operation (wagnersolution, "AWS describes a fused MoE
+ * optimization for the NVIDIA Hopper architecture", body), with scaling, the
+ * matrix products and the aggregation of expert outputs fused rather than
+ * round-tripped through HBM (The Neural Net, "AWS details MoE kernel fixes
+ * for SageMaker ...", body), in bf16 or with FP8 tensor-quantised experts
+ * ("Fused MoE on Hopper, ...", TL;DR).  The pages give no formulas; the
+ * operations below state the definitions this library implements.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless stated otherwise.  Every buffer is
+ *    owned by the caller; the library allocates no device memory, keeps no
+ *    per-call state and is re-entrant.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    All work is enqueued on it in order; outputs are valid once the stream
+ *    reaches the call.  Inputs are never written.
+ *  - Arguments are validated on the host before anything is enqueued.  On any
+ *    error nothing is enqueued and the error code is returned.
+ *    MOE_ERR_INVALID_ARG: a required pointer is NULL, a size is negative,
+ *    top_k < 1 or top_k > E, a pointer is misaligned (16 bytes for tensors,
+ *    4 bytes for scalars), or a scale pointer is given in bf16 mode.
+ *    MOE_ERR_UNSUPPORTED: a shape outside the built envelope
+ *    (E <= 512, top_k <= 16, H and I multiples of 128, block a power of two
+ *    in [1, 256], M*top_k < 2^31).
+ *    MOE_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the required size.
+ *    MOE_ERR_DEVICE: a launch failed (hipGetLastError after the launch).
+ *  - M = 0 is valid: route and the fused forward enqueue nothing; align
+ *    writes the empty layout.
+ *  - Kernels are compiled ahead of time for gfx950; no argument value
+ *    (token count included) triggers a compilation.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_DEVICE = 4
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3 = 1 } moe_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status_t status);
+
+/* ABI version of this header; bumped on any incompatible change. */
+int32_t moe_abi_version(void);
+
+/*
+ * Router top-k ("token routing", wagnersolution page, body; the decode batch
+ * holds one token per sequence, M = 1..63 in the pages' flowchart).
+ * For every token m (row of `logits`, fp32 [M,E] row-major): the top_k
+ * largest logits, in decreasing order; equal logits go to the lower expert
+ * index, and -0.0 equals +0.0.  topk_ids int32 [M,top_k] receives the
+ * experts, topk_weights fp32 [M,top_k] the softmax over the selected logits
+ * (equal to the softmax over all E renormalised over the selection).
+ * Logits must be finite (otherwise the selection is unspecified).
+ */
+moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
+                            float* topk_weights, void* stream);
+
+/*
+ * Host-only: length of `sorted_ids` needed by moe_align, in elements:
+ * P + min(E,P)*(block-1) rounded up to a multiple of block, P = M*top_k
+ * (every expert that holds a pair adds at most block-1 padding entries).
+ * Returns 0 for invalid arguments.  block_expert needs capacity/block entries.
+ */
+size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block);
+
+/*
+ * Sort and pad (the "data transfers" step between routing and the expert
+ * products, wagnersolution page, body): groups the P = M*top_k pairs
+ * f = m*top_k + j by expert so that each expert's tokens form one contiguous,
+ * tile-aligned operand.
+ *   expert_counts  int32 [E]   pairs routed to each expert
+ *   expert_offsets int32 [E+1] exclusive prefix sum of ceil(count/block)*block
+ *   sorted_ids     int32 [capacity]  for each expert, its pair indices in
+ *                  increasing f, then the sentinel P up to the padded length;
+ *                  entries at or beyond num_padded are left unwritten
+ *   block_expert   int32 [capacity/block] expert of each block, -1 for blocks
+ *                  at or beyond num_padded/block
+ *   num_padded     int32 [1]  sum of the padded lengths; -1 if an id was
+ *                  outside [0,E) (such ids are ignored, never dereferenced)
+ * The result is deterministic (no dependence on scheduling).
+ */
+moe_status_t moe_align(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E, int32_t block,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
+                       int32_t* block_expert, int32_t* num_padded, void* stream);
+
+/*
+ * Per-tensor FP8 quantisation of an fp32 vector with a given scale:
+ * out[i] = e4m3(saturate(in[i] * fp32(1/scale))), OCP E4M3FN (max 448),
+ * round to nearest even, magnitudes above 448 clamp to 448.
+ * scale: device pointer to one fp32 (> 0).  This is the conversion the fused
+ * forward applies to its activations ("FP8 tensor-quantized" MoE, "Fused MoE
+ * on Hopper, ..." TL;DR; The Neural Net page, the facts).
+ */
+moe_status_t moe_quant_e4m3(const float* in, int64_t n, const float* scale, uint8_t* out, void* stream);
+
+/*
+ * Optional tuning of the fused forward; NULL selects the built-in table.
+ * Any field <= 0 keeps its default.  Values outside the supported set return
+ * MOE_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  int32_t gemm1_ksplit;   /* waves of a workgroup splitting K of the gate/up product: 1, 2 or 4 */
+  int32_t gemm2_ksplit;   /* K slices of the down product, each a separate wave: 1..16 */
+  int32_t token_tiles;    /* 16-token tiles held per pass: 1..4 */
+  int32_t unroll;         /* MFMA K-steps per pipeline stage: 1, 2 or 4 */
+} moe_tuning_t;
+
+/*
+ * The fused layer, all in one stream-ordered call:
+ *   route (as moe_route_topk) -> align (as moe_align, block 16) ->
+ *   for each pair (m,j) with expert e = topk_ids[m,j]:
+ *     g = W13[e][0:I] . a_m,  u = W13[e][I:2I] . a_m       (fp32 accumulation)
+ *     h = SiLU(g) * u,  SiLU(g) = g / (1 + exp(-g))
+ *     o = W2[e] . h
+ *   y[m] = bf16( sum_j topk_weights[m,j] * o_(m,j) )        (fp32 accumulation)
+ * bf16 mode: a_m = x[m]; h is rounded to bf16 before the second product.
+ * fp8 mode: a_m = e4m3(x[m] / s_x) and hq = e4m3(h / s_h) (moe_quant_e4m3's
+ * rounding); the products are rescaled by s_x*s_w13 and s_h*s_w2.  s_x and
+ * s_h are the caller's static scales when given, else amax/448 over all of x
+ * and over h of all pairs (1.0 when the amax is 0).
+ * The expert products put expert-weight rows in the wide MFMA operand and
+ * the few tokens in the narrow one; at decode sizes this is the orientation
+ * the pages call Swap-AB (B^T A^T instead of A B, "Fused MoE on Hopper, ..."
+ * TL;DR and flowchart; wagnersolution page, body).
+ */
+typedef struct {
+  int32_t M, E, H, I, top_k;
+  moe_dtype_t dtype;
+  const void* x;           /* [M,H] bf16 hidden states */
+  const float* logits;     /* [M,E] fp32 router logits */
+  const void* w13;         /* [E,2I,H] bf16 or e4m3; rows [0,I) gate, [I,2I) up */
+  const void* w2;          /* [E,H,I] bf16 or e4m3 */
+  const float* w13_scale;  /* fp8: device fp32[1]; bf16: NULL */
+  const float* w2_scale;   /* fp8: device fp32[1]; bf16: NULL */
+  const float* x_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
+  const float* h_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
+  void* y;                 /* [M,H] bf16 output (overwritten) */
+  int32_t* topk_ids;       /* optional out [M,top_k]; NULL = kept in the workspace */
+  float* topk_weights;     /* optional out [M,top_k] */
+  int32_t* expert_counts;  /* optional out [E] */
+  float* scales_out;       /* optional out fp32[2]: s_x, s_h used (fp8 only) */
+  void* workspace;         /* device scratch, 256-byte aligned */
+  size_t workspace_bytes;
+  const moe_tuning_t* tuning; /* host pointer or NULL */
+} moe_fused_args_t;
+
+/* Host-only: workspace bytes needed by moe_fused_forward for these sizes. */
+size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype);
+
+moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream);
+
+/*
+ * Profiling support: when `events` (host array of hipEvent_t, passed as
+ * void*) is non-NULL, moe_fused_forward_profiled records events[2*s] before
+ * and events[2*s+1] after each of its MOE_NUM_STAGES launches on `stream`
+ * (stage order: route, align, gate/up product, down product, finalize).
+ * A stage that is not launched still records both events back to back.
+ */
+#define MOE_NUM_STAGES 5
+moe_status_t moe_fused_forward_profiled(const moe_fused_args_t* args, void* stream, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,230 @@
+"""MI355X (gfx950) fused Mixture-of-Experts layer.
+
+Thin ctypes binding over libmoe_mi355x.so, the C ABI in include/moe.h.  The
+functions here only check tensor shapes/dtypes/devices and marshal pointers;
+every step of the layer runs in the library's HIP kernels.  PyTorch provides
+device memory and the current stream.  There is no fallback: if the library
+is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "MoEError", "load", "LIB_PATH", "route_topk", "align_capacity", "align", "quant_e4m3",
+    "workspace_size", "fused_forward", "Tuning", "STATUS", "NUM_STAGES", "STAGE_NAMES",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE_TOO_SMALL",
+          4: "MOE_ERR_DEVICE"}
+DTYPE_BF16, DTYPE_FP8 = 0, 1
+NUM_STAGES = 5
+STAGE_NAMES = ("route", "align", "gate_up", "down", "finalize")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s failed: %s (%d)" % (fn, STATUS.get(code, "?"), code))
+        self.code = code
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [("gemm1_ksplit", ctypes.c_int32), ("gemm2_ksplit", ctypes.c_int32),
+                ("token_tiles", ctypes.c_int32), ("unroll", ctypes.c_int32)]
+
+
+class _FusedArgs(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int32), ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+        ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+        ("h_scale", ctypes.c_void_p), ("y", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p),
+        ("topk_weights", ctypes.c_void_p), ("expert_counts", ctypes.c_void_p), ("scales_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("tuning", ctypes.POINTER(Tuning)),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmoe_mi355x.so is not built (run `python -c 'import __graft_entry__ as g; g.build()'`)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_abi_version.restype = i32
+    lib.moe_route_topk.restype = ctypes.c_int
+    lib.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.moe_align_capacity.restype = sz
+    lib.moe_align_capacity.argtypes = [i32, i32, i32, i32]
+    lib.moe_align.restype = ctypes.c_int
+    lib.moe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.moe_quant_e4m3.restype = ctypes.c_int
+    lib.moe_quant_e4m3.argtypes = [vp, i64, vp, vp, vp]
+    lib.moe_fused_workspace_size.restype = sz
+    lib.moe_fused_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.moe_fused_forward.restype = ctypes.c_int
+    lib.moe_fused_forward.argtypes = [ctypes.POINTER(_FusedArgs), vp]
+    lib.moe_fused_forward_profiled.restype = ctypes.c_int
+    lib.moe_fused_forward_profiled.argtypes = [ctypes.POINTER(_FusedArgs), vp, vp]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise MoEError(fn, code)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape: Sequence[int]):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def route_topk(logits: torch.Tensor, top_k: int, ids: Optional[torch.Tensor] = None,
+               weights: Optional[torch.Tensor] = None, stream=None):
+    """Top-k experts per token and their softmax weights (moe_route_topk)."""
+    M, E = logits.shape
+    _need(logits, "logits", torch.float32, (M, E))
+    if ids is None:
+        ids = torch.empty(M, top_k, dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty(M, top_k, dtype=torch.float32, device=logits.device)
+    _need(ids, "ids", torch.int32, (M, top_k))
+    _need(weights, "weights", torch.float32, (M, top_k))
+    _check("moe_route_topk", load().moe_route_topk(_ptr(logits), M, E, top_k, _ptr(ids), _ptr(weights),
+                                                   _stream(stream)))
+    return ids, weights
+
+
+def align_capacity(M: int, top_k: int, E: int, block: int) -> int:
+    return int(load().moe_align_capacity(M, top_k, E, block))
+
+
+def align(ids: torch.Tensor, E: int, block: int, stream=None):
+    """Sort-and-pad of the (token, slot) pairs by expert (moe_align)."""
+    M, k = ids.shape
+    _need(ids, "ids", torch.int32, (M, k))
+    cap = align_capacity(M, k, E, block)
+    dev = ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap // block, 1), dtype=torch.int32, device=dev)
+    num = torch.empty(1, dtype=torch.int32, device=dev)
+    _check("moe_align", load().moe_align(_ptr(ids), M, k, E, block, _ptr(counts), _ptr(offsets), _ptr(sorted_ids),
+                                         _ptr(block_expert), _ptr(num), _stream(stream)))
+    return dict(counts=counts, offsets=offsets, sorted_ids=sorted_ids[:cap], block_expert=block_expert[:cap // block],
+                num_padded=num)
+
+
+def quant_e4m3(x: torch.Tensor, scale: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """e4m3 codes of fp32 data with a per-tensor scale (moe_quant_e4m3)."""
+    _need(x, "x", torch.float32, x.shape)
+    _need(scale, "scale", torch.float32, (1,))
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need(out, "out", torch.uint8, x.shape)
+    _check("moe_quant_e4m3", load().moe_quant_e4m3(_ptr(x), x.numel(), _ptr(scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def workspace_size(M: int, E: int, H: int, I: int, top_k: int, dtype: str) -> int:
+    return int(load().moe_fused_workspace_size(M, E, H, I, top_k, DTYPE_FP8 if dtype == "fp8" else DTYPE_BF16))
+
+
+def fused_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: int,
+                  dtype: str = "bf16", w13_scale: Optional[torch.Tensor] = None,
+                  w2_scale: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None,
+                  h_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
+                  topk_weights: Optional[torch.Tensor] = None, expert_counts: Optional[torch.Tensor] = None,
+                  scales_out: Optional[torch.Tensor] = None, tuning: Optional[Tuning] = None, stream=None,
+                  events=None) -> torch.Tensor:
+    """The fused layer (moe_fused_forward).
+
+    x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
+    (dtype "bf16") or uint8 e4m3fn codes (dtype "fp8") with fp32 [1] device
+    scales; x_scale/h_scale: static fp8 activation scales or None (dynamic).
+    events: optional list of 2*NUM_STAGES hipEvent_t handles (ints) recorded
+    around the stages on the stream.
+    """
+    M, H = x.shape
+    E = logits.shape[1]
+    fp8 = dtype == "fp8"
+    I = w2.shape[2]
+    wdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(x, "x", torch.bfloat16, (M, H))
+    _need(logits, "logits", torch.float32, (M, E))
+    _need(w13, "w13", wdt, (E, 2 * I, H))
+    _need(w2, "w2", wdt, (E, H, I))
+    for name, s in (("w13_scale", w13_scale), ("w2_scale", w2_scale), ("x_scale", x_scale), ("h_scale", h_scale)):
+        if s is not None:
+            _need(s, name, torch.float32, (1,))
+    if out is None:
+        out = torch.empty(M, H, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (M, H))
+    if topk_ids is not None:
+        _need(topk_ids, "topk_ids", torch.int32, (M, top_k))
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, (M, top_k))
+    if expert_counts is not None:
+        _need(expert_counts, "expert_counts", torch.int32, (E,))
+    if scales_out is not None:
+        _need(scales_out, "scales_out", torch.float32, (2,))
+    lib = load()
+    need = int(lib.moe_fused_workspace_size(M, E, H, I, top_k, DTYPE_FP8 if fp8 else DTYPE_BF16))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    args = _FusedArgs(
+        M=M, E=E, H=H, I=I, top_k=top_k, dtype=DTYPE_FP8 if fp8 else DTYPE_BF16,
+        x=_ptr(x), logits=_ptr(logits), w13=_ptr(w13), w2=_ptr(w2),
+        w13_scale=_ptr(w13_scale), w2_scale=_ptr(w2_scale), x_scale=_ptr(x_scale), h_scale=_ptr(h_scale),
+        y=_ptr(out), topk_ids=_ptr(topk_ids), topk_weights=_ptr(topk_weights),
+        expert_counts=_ptr(expert_counts), scales_out=_ptr(scales_out),
+        workspace=_ptr(workspace), workspace_bytes=workspace.numel(),
+        tuning=ctypes.pointer(tuning) if tuning is not None else None,
+    )
+    if events is None:
+        _check("moe_fused_forward", lib.moe_fused_forward(ctypes.byref(args), _stream(stream)))
+    else:
+        if len(events) != 2 * NUM_STAGES:
+            raise ValueError("events must hold %d hipEvent_t handles" % (2 * NUM_STAGES))
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check("moe_fused_forward_profiled",
+               lib.moe_fused_forward_profiled(ctypes.byref(args), _stream(stream), ctypes.cast(arr, ctypes.c_void_p)))
+    return out

@@ -1,0 +1,437 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace carving, variant selection and stream-ordered launches.
+// No device memory is allocated here and no call synchronises the stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <type_traits>
+
+#include "moe.h"
+#include "gemm_decode.h"
+#include "moe_device.h"
+#include "route_align.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kAlignBlockFused = 16;  // token tile of the MFMA B operand
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2i(int v) {
+  int b = 0;
+  while ((1 << b) < v) ++b;
+  return b;
+}
+
+moe_status_t launch_status() {
+  hipError_t err = hipGetLastError();
+  return err == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+int64_t align_capacity(int64_t P, int E, int B) {
+  int64_t cap = P + std::min<int64_t>(E, P) * (B - 1);
+  return cdiv(cap, B) * B;
+}
+
+// ---------------------------------------------------------------- workspace
+struct Layout {
+  size_t ids, wts, counts, offsets, sorted, block_expert, num_padded, active, num_active;
+  size_t xamax_part, scale_slot, h_amax, xq, h, y_acc, total;
+  int64_t capacity;
+  int n_blocks, n_route_wg;
+};
+
+Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
+  Layout L{};
+  const int64_t P = (int64_t)M * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += round_up(std::max<size_t>(bytes, 4), 256);
+    return o;
+  };
+  L.capacity = align_capacity(P, E, kAlignBlockFused);
+  L.n_blocks = (int)(L.capacity / kAlignBlockFused);
+  L.n_route_wg = (int)cdiv(M, 4);
+  L.ids = take(P * 4);
+  L.wts = take(P * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.sorted = take(L.capacity * 4);
+  L.block_expert = take((size_t)L.n_blocks * 4);
+  L.num_padded = take(4);
+  L.active = take((size_t)E * 4);
+  L.num_active = take(4);
+  L.xamax_part = take((size_t)L.n_route_wg * 4);
+  L.scale_slot = take(4);
+  L.h_amax = take(4);
+  const bool fp8 = dt == MOE_DTYPE_FP8_E4M3;
+  L.xq = take(fp8 ? (size_t)M * H : 0);
+  L.h = take((size_t)P * I * (fp8 ? 4 : 2));
+  L.y_acc = take((size_t)M * H * 4);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- variants
+struct Plan {
+  int nt, passes, u1, ks1, u2, ks2, lds2;
+};
+
+int default_u(bool fp8, int nt) { return fp8 ? (nt <= 2 ? 2 : 1) : (nt <= 2 ? 4 : 2); }
+
+bool valid_u(bool fp8, int u) { return fp8 ? (u == 1 || u == 2) : (u == 2 || u == 4); }
+
+moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, const moe_tuning_t* t, Plan* p) {
+  const int kstep = fp8 ? 128 : 32;
+  const int64_t P = (int64_t)M * k;
+  const int n_act = (int)std::min<int64_t>(E, P);
+  p->nt = (int)std::min<int64_t>(4, std::max<int64_t>(1, cdiv(std::min(M, 64), 16)));
+  if (p->nt == 3) p->nt = 4;
+  if (t && t->token_tiles > 0) {
+    if (t->token_tiles > 4) return MOE_ERR_UNSUPPORTED;
+    p->nt = t->token_tiles == 3 ? 4 : t->token_tiles;
+  }
+  p->passes = (int)cdiv(M, p->nt * 16);
+  p->u1 = p->u2 = default_u(fp8, p->nt);
+  if (t && t->unroll > 0) {
+    if (!valid_u(fp8, t->unroll)) return MOE_ERR_UNSUPPORTED;
+    p->u1 = p->u2 = t->unroll;
+  }
+  // gate/up: split K over the 4 waves when each wave keeps >= 2 stages
+  p->ks1 = 1;
+  for (int ks : {4, 2}) {
+    if ((H / ks) % kstep == 0 && (H / ks) / kstep >= 2 * p->u1) {
+      p->ks1 = ks;
+      break;
+    }
+  }
+  if (t && t->gemm1_ksplit > 0) {
+    const int ks = t->gemm1_ksplit;
+    if (!(ks == 1 || ks == 2 || ks == 4) || (H / ks) % kstep != 0) return MOE_ERR_UNSUPPORTED;
+    p->ks1 = ks;
+  }
+  // down: K slices are independent waves; aim for ~8192 waves in flight
+  const int nsteps2 = I / kstep;
+  const int64_t base_waves = (int64_t)(H / 32) * n_act * p->passes;
+  const int64_t want = std::max<int64_t>(1, 8192 / std::max<int64_t>(1, base_waves));
+  auto lds_ok = [&](int ks) {
+    return !qh || (int64_t)p->nt * 16 * gemm2_lds_stride(I / ks) <= 65536;
+  };
+  p->ks2 = 0;
+  for (int ks = 1; ks <= 16; ++ks) {
+    if (nsteps2 % ks != 0 || !lds_ok(ks)) continue;
+    if (p->ks2 == 0) p->ks2 = ks;  // smallest feasible
+    if (ks <= want && nsteps2 / ks >= p->u2) p->ks2 = ks;
+  }
+  if (t && t->gemm2_ksplit > 0) {
+    const int ks = t->gemm2_ksplit;
+    if (ks > 16 || nsteps2 % ks != 0 || !lds_ok(ks)) return MOE_ERR_UNSUPPORTED;
+    p->ks2 = ks;
+  }
+  if (p->ks2 == 0) return MOE_ERR_UNSUPPORTED;
+  p->lds2 = qh ? p->nt * 16 * gemm2_lds_stride(I / p->ks2) : 0;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- dispatch
+template <bool FP8, int HF, int NT, int U, int KS>
+void launch_g1(dim3 g, hipStream_t st, const Gemm1Args& a) {
+  gemm1_decode_kernel<FP8, HF, NT, U, KS><<<g, 256, 0, st>>>(a);
+}
+
+template <bool FP8, int HF, int NT, int U>
+bool g1_ks(int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
+  switch (ks) {
+    case 1: launch_g1<FP8, HF, NT, U, 1>(g, st, a); return true;
+    case 2: launch_g1<FP8, HF, NT, U, 2>(g, st, a); return true;
+    case 4: launch_g1<FP8, HF, NT, U, 4>(g, st, a); return true;
+  }
+  return false;
+}
+
+template <bool FP8, int HF, int NT>
+bool g1_u(int u, int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
+  if constexpr (FP8) {
+    if (u == 1) return g1_ks<FP8, HF, NT, 1>(ks, g, st, a);
+    if (u == 2) return g1_ks<FP8, HF, NT, 2>(ks, g, st, a);
+  } else {
+    if (u == 2) return g1_ks<FP8, HF, NT, 2>(ks, g, st, a);
+    if (u == 4) return g1_ks<FP8, HF, NT, 4>(ks, g, st, a);
+  }
+  return false;
+}
+
+template <bool FP8, int HF>
+bool g1_nt(int nt, int u, int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
+  switch (nt) {
+    case 1: return g1_u<FP8, HF, 1>(u, ks, g, st, a);
+    case 2: return g1_u<FP8, HF, 2>(u, ks, g, st, a);
+    case 4: return g1_u<FP8, HF, 4>(u, ks, g, st, a);
+  }
+  return false;
+}
+
+template <bool FP8, int HF, int NT, int U>
+void launch_g2(dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+  gemm2_decode_kernel<FP8, HF, NT, U><<<g, 256, lds, st>>>(a);
+}
+
+template <bool FP8, int HF, int NT>
+bool g2_u(int u, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+  if constexpr (FP8) {
+    if (u == 1) { launch_g2<FP8, HF, NT, 1>(g, lds, st, a); return true; }
+    if (u == 2) { launch_g2<FP8, HF, NT, 2>(g, lds, st, a); return true; }
+  } else {
+    if (u == 2) { launch_g2<FP8, HF, NT, 2>(g, lds, st, a); return true; }
+    if (u == 4) { launch_g2<FP8, HF, NT, 4>(g, lds, st, a); return true; }
+  }
+  return false;
+}
+
+template <bool FP8, int HF>
+bool g2_nt(int nt, int u, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+  switch (nt) {
+    case 1: return g2_u<FP8, HF, 1>(u, g, lds, st, a);
+    case 2: return g2_u<FP8, HF, 2>(u, g, lds, st, a);
+    case 4: return g2_u<FP8, HF, 4>(u, g, lds, st, a);
+  }
+  return false;
+}
+
+bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float* wts, const RouteFusedArgs& fa,
+                  hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(M, 4));
+  const int npl = (int)cdiv(E, 64);
+  if (npl <= 1)
+    route_topk_kernel<1><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+  else if (npl <= 2)
+    route_topk_kernel<2><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+  else if (npl <= 4)
+    route_topk_kernel<4><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+  else
+    route_topk_kernel<8><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+  return true;
+}
+
+void launch_align(const int32_t* ids, int64_t P, int E, int B, const AlignOut& o, const QuantXArgs& q, int n_quant_wg,
+                  hipStream_t st) {
+  const int n_align = (int)std::max<int64_t>(1, cdiv(P, kAlignChunk));
+  align_kernel<<<n_align + n_quant_wg, 256, 0, st>>>(ids, (int)P, E, B, log2i(B), log2i(E), n_align, o, q);
+}
+
+moe_status_t check_shape(int M, int E, int k) {
+  if (M < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)M * k >= (int64_t)INT32_MAX - kAlignChunk) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+int32_t moe_abi_version(void) { return 1; }
+
+moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
+                            float* topk_weights, void* stream) {
+  moe_status_t rc = check_shape(M, E, top_k);
+  if (rc != MOE_OK) return rc;
+  if (M == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4)) return MOE_ERR_INVALID_ARG;
+  launch_route(logits, M, E, top_k, topk_ids, topk_weights, RouteFusedArgs{}, (hipStream_t)stream);
+  return launch_status();
+}
+
+size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
+  if (check_shape(M, E, top_k) != MOE_OK || !is_pow2(block) || block > 256) return 0;
+  return (size_t)align_capacity((int64_t)M * top_k, E, block);
+}
+
+moe_status_t moe_align(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E, int32_t block,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* block_expert,
+                       int32_t* num_padded, void* stream) {
+  moe_status_t rc = check_shape(M, E, top_k);
+  if (rc != MOE_OK) return rc;
+  if (!is_pow2(block) || block > 256) return block > 256 && is_pow2(block) ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
+  const int64_t P = (int64_t)M * top_k;
+  const int64_t cap = align_capacity(P, E, block);
+  if ((P > 0 && !topk_ids) || !expert_counts || !expert_offsets || !num_padded) return MOE_ERR_INVALID_ARG;
+  if (cap > 0 && (!sorted_ids || !block_expert)) return MOE_ERR_INVALID_ARG;
+  for (const void* p : {(const void*)topk_ids, (const void*)expert_counts, (const void*)expert_offsets,
+                        (const void*)sorted_ids, (const void*)block_expert, (const void*)num_padded})
+    if (!aligned(p, 4)) return MOE_ERR_INVALID_ARG;
+  AlignOut o{expert_counts, expert_offsets, sorted_ids, block_expert, num_padded, nullptr, nullptr,
+             (int)(cap / block)};
+  launch_align(topk_ids, P, E, block, o, QuantXArgs{}, 0, (hipStream_t)stream);
+  return launch_status();
+}
+
+moe_status_t moe_quant_e4m3(const float* in, int64_t n, const float* scale, uint8_t* out, void* stream) {
+  if (n < 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!in || !scale || !out || !aligned(in, 16) || !aligned(out, 4) || !aligned(scale, 4))
+    return MOE_ERR_INVALID_ARG;
+  quant_f32_kernel<<<(unsigned)cdiv(n, 1024), 256, 0, (hipStream_t)stream>>>(in, n, scale, out);
+  return launch_status();
+}
+
+size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype) {
+  if (check_shape(M, E, top_k) != MOE_OK || H < 128 || I < 128 || H % 128 || I % 128) return 0;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3) return 0;
+  return make_layout(M, E, H, I, top_k, dtype).total;
+}
+
+static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  auto rec = [&](int i) {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], st);
+  };
+  moe_status_t rc = check_shape(a->M, a->E, a->top_k);
+  if (rc != MOE_OK) return rc;
+  if (a->dtype != MOE_DTYPE_BF16 && a->dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (a->H < 128 || a->I < 128 || a->H % 128 || a->I % 128) return MOE_ERR_UNSUPPORTED;
+  const bool fp8 = a->dtype == MOE_DTYPE_FP8_E4M3;
+  const int M = a->M, E = a->E, H = a->H, I = a->I, k = a->top_k;
+  if (!fp8 && (a->w13_scale || a->w2_scale || a->x_scale || a->h_scale)) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) {
+    if (ev)
+      for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) rec(i);
+    return MOE_OK;
+  }
+  if (!a->x || !a->logits || !a->w13 || !a->w2 || !a->y || !a->workspace) return MOE_ERR_INVALID_ARG;
+  for (const void* p : {a->x, a->w13, a->w2, (const void*)a->y}) if (!aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(a->workspace, 256)) return MOE_ERR_INVALID_ARG;
+  for (const void* p : {(const void*)a->logits, (const void*)a->w13_scale, (const void*)a->w2_scale,
+                        (const void*)a->x_scale, (const void*)a->h_scale, (const void*)a->topk_ids,
+                        (const void*)a->topk_weights, (const void*)a->expert_counts, (const void*)a->scales_out})
+    if (!aligned(p, 4)) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(M, E, H, I, k, a->dtype);
+  if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const bool hdyn = fp8 && !a->h_scale;
+  Plan plan;
+  rc = make_plan(M, E, H, I, k, fp8, hdyn, a->tuning, &plan);
+  if (rc != MOE_OK) return rc;
+
+  uint8_t* ws = (uint8_t*)a->workspace;
+  int32_t* ids = a->topk_ids ? a->topk_ids : (int32_t*)(ws + L.ids);
+  float* wts = a->topk_weights ? a->topk_weights : (float*)(ws + L.wts);
+  int32_t* counts = a->expert_counts ? a->expert_counts : (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* sorted = (int32_t*)(ws + L.sorted);
+  int32_t* active = (int32_t*)(ws + L.active);
+  int32_t* num_active = (int32_t*)(ws + L.num_active);
+  float* xamax_part = (float*)(ws + L.xamax_part);
+  float* scale_slot = (float*)(ws + L.scale_slot);
+  unsigned* h_amax = (unsigned*)(ws + L.h_amax);
+  uint8_t* xq = ws + L.xq;
+  uint8_t* h = ws + L.h;
+  float* y_acc = (float*)(ws + L.y_acc);
+  const int64_t P = (int64_t)M * k;
+  const int n_act = (int)std::min<int64_t>(E, P);
+
+  // 1. routing (+ per-workgroup amax of x, clearing of the accumulators)
+  rec(0);
+  RouteFusedArgs fa{(const uint16_t*)a->x, H, (fp8 && !a->x_scale) ? xamax_part : nullptr, y_acc,
+                    hdyn ? h_amax : nullptr};
+  launch_route(a->logits, M, E, k, ids, wts, fa, st);
+  rec(1);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+
+  // 2. align (+ activation quantisation in fp8 mode)
+  rec(2);
+  AlignOut o{counts, offsets, sorted, (int32_t*)(ws + L.block_expert), (int32_t*)(ws + L.num_padded), active,
+             num_active, L.n_blocks};
+  QuantXArgs q{};
+  int n_quant = 0;
+  if (fp8) {
+    q.x = (const uint16_t*)a->x;
+    q.n = (int64_t)M * H;
+    q.amax_part = xamax_part;
+    q.n_part = L.n_route_wg;
+    q.static_scale = a->x_scale;
+    q.xq = xq;
+    q.scale_slot = scale_slot;
+    n_quant = (int)cdiv(q.n, 256 * 16);
+  }
+  launch_align(ids, P, E, kAlignBlockFused, o, q, n_quant, st);
+  rec(3);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+
+  const Segments segs{sorted, offsets, counts, active, num_active};
+  const int hf = !fp8 ? H_BF16 : (hdyn ? H_F32 : H_E4M3);
+
+  // 3. gate/up product + SiLU(gate)*up
+  rec(4);
+  {
+    Gemm1Args g{(const uint8_t*)a->w13, fp8 ? xq : (const uint8_t*)a->x, segs, H, I, k, a->w13_scale, scale_slot,
+                a->h_scale, h, h_amax};
+    const int tpw = 4 / plan.ks1;
+    const dim3 grid((unsigned)(I / 16 / tpw), (unsigned)n_act, (unsigned)plan.passes);
+    bool ok;
+    if (!fp8)
+      ok = g1_nt<false, H_BF16>(plan.nt, plan.u1, plan.ks1, grid, st, g);
+    else if (hdyn)
+      ok = g1_nt<true, H_F32>(plan.nt, plan.u1, plan.ks1, grid, st, g);
+    else
+      ok = g1_nt<true, H_E4M3>(plan.nt, plan.u1, plan.ks1, grid, st, g);
+    if (!ok) return MOE_ERR_UNSUPPORTED;
+  }
+  rec(5);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+
+  // 4. down product + weighted scatter-add
+  rec(6);
+  {
+    Gemm2Args g{(const uint8_t*)a->w2, h, segs, wts, H, I, k, plan.ks2, a->w2_scale, a->h_scale, h_amax, y_acc};
+    const dim3 grid((unsigned)(H / 128), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes));
+    bool ok;
+    if (hf == H_BF16)
+      ok = g2_nt<false, H_BF16>(plan.nt, plan.u2, grid, 0, st, g);
+    else if (hf == H_F32)
+      ok = g2_nt<true, H_F32>(plan.nt, plan.u2, grid, plan.lds2, st, g);
+    else
+      ok = g2_nt<true, H_E4M3>(plan.nt, plan.u2, grid, 0, st, g);
+    if (!ok) return MOE_ERR_UNSUPPORTED;
+  }
+  rec(7);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+
+  // 5. y = bf16(y_acc)
+  rec(8);
+  {
+    const int64_t n = (int64_t)M * H;
+    finalize_kernel<<<(unsigned)cdiv(n, 2048), 256, 0, st>>>(y_acc, (uint16_t*)a->y, n, scale_slot, h_amax,
+                                                             a->h_scale, fp8 ? a->scales_out : nullptr);
+  }
+  rec(9);
+  return launch_status();
+}
+
+moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream) {
+  return fused_forward(args, (hipStream_t)stream, nullptr);
+}
+
+moe_status_t moe_fused_forward_profiled(const moe_fused_args_t* args, void* stream, void* const* events) {
+  return fused_forward(args, (hipStream_t)stream, events);
+}
+
+}  // extern "C"

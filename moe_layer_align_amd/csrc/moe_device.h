@@ -1,0 +1,101 @@
+// Device-side building blocks for gfx950 (CDNA4): vector types, MFMA
+// wrappers, number-format conversions and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 16;
+constexpr float kE4m3Max = 448.0f;
+
+// ---------------------------------------------------------------- MFMA
+// 16x16x32 bf16 -> fp32.  A: lane l holds row (l%16), 8 consecutive k at
+// 8*(l/16); B: lane l holds column (l%16), the same 8 k.  C: lane l holds
+// rows 4*(l/16)+0..3 of column (l%16).
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// 16x16x128 OCP e4m3 x e4m3 -> fp32 (format code 0 for both operands; block
+// scales fixed at 2^0, E8M0 code 127).  Each lane supplies 32 bytes of A
+// (row l%16) and 32 bytes of B (column l%16) covering the same k positions,
+// so the product does not depend on how the hardware orders k inside a lane.
+__device__ __forceinline__ f32x4 mfma_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
+  i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------- formats
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (hardware conversion).
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (unsigned)__builtin_bit_cast(unsigned short, x) | ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+}
+
+__device__ __forceinline__ float sat_e4m3(float v) { return fminf(fmaxf(v, -kE4m3Max), kE4m3Max); }
+
+// Four fp32 -> four OCP e4m3 bytes (byte i from v_i), nearest even, after
+// clamping to +-448 so the conversion never sees an out-of-range value.
+__device__ __forceinline__ unsigned pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+  return (unsigned)w;
+}
+
+// Scale from an amax: amax/448, or 1 when amax is 0.
+__device__ __forceinline__ float scale_from_amax(float amax) { return amax > 0.0f ? amax / kE4m3Max : 1.0f; }
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    unsigned lo = __shfl_xor((unsigned)k, off);
+    unsigned hi = __shfl_xor((unsigned)(k >> 32), off);
+    unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace moe

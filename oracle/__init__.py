@@ -90,6 +90,7 @@ def _load():
                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.oracle_layer.restype = ctypes.c_int
     lib.oracle_layer.argtypes = [ctypes.POINTER(_LayerArgs)]
+    lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -133,6 +134,11 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
 def e4m3_decode(c: np.ndarray) -> np.ndarray:
     lib = _load()
     return np.array([lib.oracle_e4m3_decode(int(a)) for a in np.ravel(c)], dtype=np.float64)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def scale_from_amax(amax: float) -> float:

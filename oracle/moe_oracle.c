@@ -391,4 +391,12 @@ int oracle_layer(oracle_layer_args* A) {
   return ORC_OK;
 }
 
+/* Threads the parallel loops use (OpenMP's default team size). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif
+
 int oracle_abi_version(void) { return 1; }

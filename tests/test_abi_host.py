@@ -1,0 +1,158 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+The library loads, exports every function include/moe.h declares, and its
+host-only helpers and argument validation behave as documented: invalid
+calls return their error code before anything is enqueued (so they never
+touch a device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import moe_layer_align_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so is not built; run __graft_entry__.build()")
+    return m.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_route_topk", "moe_align", "moe_fused_forward", "moe_align_capacity",
+              "moe_fused_workspace_size", "moe_status_string", "moe_quant_e4m3"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.moe_abi_version() == 1
+
+
+def capacity_formula(M, k, E, B):
+    P = M * k
+    cap = P + min(E, P) * (B - 1)
+    return -(-cap // B) * B
+
+
+@pytest.mark.parametrize("M,k,E,B", [(0, 2, 8, 16), (1, 2, 8, 16), (63, 2, 8, 64), (4096, 8, 128, 64),
+                                     (128, 8, 256, 16), (5, 16, 512, 256), (3, 1, 1, 1)])
+def test_align_capacity(lib, M, k, E, B):
+    assert lib.moe_align_capacity(M, k, E, B) == capacity_formula(M, k, E, B)
+
+
+def test_align_capacity_invalid(lib):
+    assert lib.moe_align_capacity(4, 3, 2, 16) == 0     # k > E
+    assert lib.moe_align_capacity(4, 2, 8, 24) == 0     # not a power of two
+    assert lib.moe_align_capacity(4, 2, 8, 512) == 0    # block too large
+    assert lib.moe_align_capacity(-1, 2, 8, 16) == 0
+    assert lib.moe_align_capacity(4, 2, 1024, 16) == 0  # E beyond the envelope
+
+
+def test_workspace_size(lib):
+    bf = lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 0)
+    f8 = lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 1)
+    assert bf > 0 and f8 > 0 and bf % 256 == 0
+    # the fp32 accumulator and the h buffer alone
+    assert bf >= 4 * 256 * 4 + 8 * 512 * 2
+    assert lib.moe_fused_workspace_size(4, 8, 200, 512, 2, 0) == 0  # H not a multiple of 128
+    assert lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 7) == 0  # unknown dtype
+
+
+FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+def test_route_validation(lib):
+    r = lib.moe_route_topk
+    assert r(FAKE, 4, 8, 9, FAKE, FAKE, None) == 1      # k > E
+    assert r(FAKE, 4, 8, 0, FAKE, FAKE, None) == 1      # k < 1
+    assert r(FAKE, -1, 8, 2, FAKE, FAKE, None) == 1     # M < 0
+    assert r(FAKE, 4, 600, 2, FAKE, FAKE, None) == 2    # E beyond 512
+    assert r(FAKE, 4, 64, 17, FAKE, FAKE, None) == 2    # k beyond 16
+    assert r(None, 4, 8, 2, FAKE, FAKE, None) == 1      # null logits
+    assert r(FAKE + 2, 4, 8, 2, FAKE, FAKE, None) == 1  # misaligned
+    assert r(None, 0, 8, 2, None, None, None) == 0      # M = 0: nothing to do
+
+
+def test_align_validation(lib):
+    a = lib.moe_align
+    assert a(FAKE, 4, 2, 8, 24, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1   # block not a power of two
+    assert a(FAKE, 4, 2, 8, 512, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2  # block too large
+    assert a(FAKE, 4, 3, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1   # k > E
+    assert a(None, 4, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1   # null ids
+    assert a(FAKE, 4, 2, 8, 16, None, FAKE, FAKE, FAKE, FAKE, None) == 1   # null counts
+    assert a(FAKE, 4, 2, 8, 16, FAKE, FAKE, FAKE + 1, FAKE, FAKE, None) == 1  # misaligned
+
+
+def test_quant_validation(lib):
+    q = lib.moe_quant_e4m3
+    assert q(FAKE, -1, FAKE, FAKE, None) == 1
+    assert q(None, 10, FAKE, FAKE, None) == 1
+    assert q(FAKE + 4, 10, FAKE, FAKE, None) == 1  # input needs 16-byte alignment
+    assert q(None, 0, None, None, None) == 0
+
+
+def fused_args(**kw):
+    import moe_layer_align_amd as m
+    base = dict(M=4, E=8, H=256, I=512, top_k=2, dtype=0, x=FAKE, logits=FAKE, w13=FAKE, w2=FAKE, y=FAKE,
+                workspace=FAKE, workspace_bytes=1 << 30)
+    base.update(kw)
+    return m._FusedArgs(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(top_k=9), 1),
+    (dict(M=-1), 1),
+    (dict(dtype=5), 1),
+    (dict(H=200), 2),
+    (dict(I=64), 2),
+    (dict(E=1024), 2),
+    (dict(x=None), 1),
+    (dict(w13=FAKE + 8), 1),
+    (dict(workspace=FAKE + 16), 1),
+    (dict(workspace_bytes=100), 3),
+    (dict(w13_scale=FAKE), 1),           # a scale in bf16 mode
+    (dict(dtype=1), 1),                  # fp8 without weight scales
+    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE + 1), 1),  # misaligned scale
+])
+def test_fused_validation(lib, kw, code):
+    args = fused_args(**kw)
+    assert lib.moe_fused_forward(ctypes.byref(args), None) == code
+
+
+def test_fused_tuning_validation(lib):
+    import moe_layer_align_amd as m
+    for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17)):
+        args = fused_args(tuning=ctypes.pointer(t))
+        assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
+
+
+def test_fused_m0_is_noop(lib):
+    args = fused_args(M=0, x=None, logits=None, y=None, workspace=None, workspace_bytes=0)
+    assert lib.moe_fused_forward(ctypes.byref(args), None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import moe_layer_align_amd as m
+    with pytest.raises(ValueError):
+        m.route_topk(torch.zeros(2, 8), 2)

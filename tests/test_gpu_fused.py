@@ -1,0 +1,164 @@
+"""GPU parity of the fused layer (moe_fused_forward) against the CPU oracle.
+
+Every case checks: topk ids and per-expert counts bit-exact, topk weights
+within 1e-6, the fp8 activation scale s_x bit-exact and s_h within 1e-4
+(h differs by summation order), and the output within
+max|y - y_ref| / max|y_ref| <= 1e-2 (bf16) or 3e-2 (fp8), y_ref being the
+oracle's output before bf16 rounding.
+
+Shapes: small layers that span several weight tiles, token tiles and token
+passes with ragged tails (the oracle evaluates them whole), the tiny
+workload, and the four full-size workloads at every token count of their
+sweeps; the fp8 prefill layer at M=4096 is compared on sampled tokens with
+static activation scales (the dynamic h scale needs h of all 32768 pairs),
+and with dynamic scales at M=256.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_layer_align_amd as moe
+from gpu_common import DEV, TOL, compare, run_gpu, say
+from synth import CONFIGS, MoEConfig, gen_logits, gen_weights, gen_x
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg_of(dtype, E, k, H, I, logits="normal"):
+    return MoEConfig("small", E=E, k=k, H=H, I=I, dtype=dtype, ms=(1,), logits=logits)
+
+
+# ---------------------------------------------------------------- small layers, whole output compared
+@pytest.mark.parametrize("dtype,xs,hs", [("bf16", None, None), ("fp8", None, None), ("fp8", 0.02, 0.02)])
+@pytest.mark.parametrize("M", [1, 5, 17, 40, 100])
+def test_small_layer(dtype, xs, hs, M):
+    cfg = cfg_of(dtype, 6, 2, 512, 384)
+    compare(cfg, M, seed=M, x_scale=xs, h_scale=hs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_single_expert_top1(dtype):
+    compare(cfg_of(dtype, 1, 1, 256, 256), 9, seed=3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_all_experts_selected(dtype):
+    compare(cfg_of(dtype, 4, 4, 256, 128), 21, seed=4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_many_tokens_one_expert(dtype):
+    # every token picks expert 2 first: one expert holds 150 pairs (3 token passes)
+    cfg = cfg_of(dtype, 5, 2, 256, 256)
+    lg = gen_logits(cfg, 150, sub=150)
+    lg[:, 2] += 100.0
+    compare(cfg, 150, seed=5, logits=lg)
+
+
+def test_max_experts_and_topk():
+    compare(cfg_of("fp8", 512, 16, 256, 256), 11, seed=6)
+
+
+def test_tuning_variants_agree():
+    cfg = cfg_of("bf16", 8, 2, 1024, 512)
+    w = gen_weights(cfg, 7, device=DEV)
+    for t in [moe.Tuning(gemm1_ksplit=1, gemm2_ksplit=1, token_tiles=1, unroll=2),
+              moe.Tuning(gemm1_ksplit=2, gemm2_ksplit=4, token_tiles=2, unroll=4),
+              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=16, token_tiles=4, unroll=2)]:
+        compare(cfg, 33, seed=7, weights=w, tuning=t)
+    cfg8 = cfg_of("fp8", 8, 2, 1024, 512)
+    w8 = gen_weights(cfg8, 7, device=DEV)
+    for t in [moe.Tuning(gemm1_ksplit=1, gemm2_ksplit=1, token_tiles=1, unroll=1),
+              moe.Tuning(gemm1_ksplit=2, gemm2_ksplit=2, token_tiles=2, unroll=2),
+              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=4, token_tiles=4, unroll=1)]:
+        compare(cfg8, 33, seed=7, weights=w8, tuning=t)
+        compare(cfg8, 33, seed=7, weights=w8, tuning=t, x_scale=0.03, h_scale=0.02)
+
+
+def test_m0_is_noop():
+    cfg = cfg_of("bf16", 4, 2, 128, 128)
+    w13, w2, _, _ = gen_weights(cfg, 0, device=DEV)
+    y = moe.fused_forward(torch.empty(0, 128, dtype=torch.bfloat16, device=DEV),
+                          torch.empty(0, 4, device=DEV), w13, w2, 2)
+    assert y.shape == (0, 128)
+
+
+def test_repeat_calls_reuse_workspace():
+    cfg = cfg_of("fp8", 16, 4, 512, 256)
+    w = gen_weights(cfg, 8, device=DEV)
+    x = gen_x(cfg.H, 40, 8, sub=40)
+    lg = gen_logits(cfg, 40, 8, sub=40)
+    ws = torch.empty(moe.workspace_size(40, 16, 512, 256, 4, "fp8"), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xFF)  # stale contents must not matter
+    s13 = torch.tensor([w[2]], device=DEV)
+    s2 = torch.tensor([w[3]], device=DEV)
+    ys = [moe.fused_forward(x.to(DEV), lg.to(DEV), w[0], w[1], 4, "fp8", s13, s2, workspace=ws).clone()
+          for _ in range(3)]
+    assert torch.equal(ys[0].isfinite(), torch.ones_like(ys[0], dtype=torch.bool))
+    for y in ys[1:]:
+        err = (y.float() - ys[0].float()).abs().max() / ys[0].float().abs().max()
+        assert err < 1e-3  # fp32 atomics make the last bits order-dependent
+
+
+# ---------------------------------------------------------------- the workloads
+def test_tiny():
+    cfg = CONFIGS["tiny"]
+    compare(cfg, 4, seed=0)
+
+
+@pytest.fixture(scope="module")
+def mixtral_w():
+    w = gen_weights(CONFIGS["mixtral"], 0, device=DEV)
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", CONFIGS["mixtral"].ms)
+def test_mixtral(mixtral_w, M):
+    compare(CONFIGS["mixtral"], M, seed=0, weights=mixtral_w)
+
+
+@pytest.fixture(scope="module")
+def qwen3_w():
+    w = gen_weights(CONFIGS["qwen3"], 0, device=DEV)
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", CONFIGS["qwen3"].ms)
+def test_qwen3(qwen3_w, M):
+    compare(CONFIGS["qwen3"], M, seed=0, weights=qwen3_w)
+
+
+@pytest.fixture(scope="module")
+def deepseek_w():
+    w = gen_weights(CONFIGS["deepseek"], 0, device=DEV)
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", CONFIGS["deepseek"].ms)
+def test_deepseek(deepseek_w, M):
+    toks = None if M <= 16 else sorted({0, 1, M // 3, M // 2, M - 2, M - 1})
+    compare(CONFIGS["deepseek"], M, seed=0, weights=deepseek_w, tokens=toks)
+
+
+@pytest.fixture(scope="module")
+def prefill_w():
+    w = gen_weights(CONFIGS["prefill"], 0, device=DEV)
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_prefill_full_static_scales(prefill_w):
+    M = 4096
+    toks = [0, 1, 777, 2048, 3000, 4095]
+    compare(CONFIGS["prefill"], M, seed=0, weights=prefill_w, tokens=toks, x_scale=0.011, h_scale=0.02)
+
+
+def test_prefill_dynamic_scales(prefill_w):
+    compare(CONFIGS["prefill"], 256, seed=0, weights=prefill_w, tokens=[0, 5, 100, 255])
