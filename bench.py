@@ -7,12 +7,19 @@ fused forward (routing, align, gate/up product with SiLU*up, down product
 with the weighted combine, finalize) at each M of the sweep, on seeded
 synthetic inputs already resident in HBM.
 
+Cold cache: before every layer call a 1 GiB buffer is overwritten, which
+evicts the 256 MB Infinity Cache and the L2s, so no expert weight is served
+from a cache filled by the previous call.  The layer's time is the span
+between HIP events recorded on the launch stream right before its first
+kernel and right after its last one; the flush is outside the span.
+
 value = expert-weight bytes of the experts that received tokens, summed over
-the sweep, divided by the step time (GB/s).  Per-M span, per-stage times
-(HIP events recorded by the library around each launch on the stream) and
-the roofline of the dominant kernel (the gate/up product) are reported on
-the same JSON line, with the CPU oracle timed on a bounded sample of the
-same workload.
+the sweep, divided by the summed layer spans (GB/s); for the prefill
+workload, real-pair flops 6*M*k*H*I over the span (TFLOP/s).  The roofline
+object covers the dominant kernel (the gate/up product): its algorithmic
+bytes (or flops) over its launch durations, both from HIP events around that
+launch inside the timed region.  The CPU oracle is timed on a bounded sample
+of the same workload.
 
 Other workloads (--config qwen3|deepseek|prefill|tiny) print the same line
 for that layer; they are measurement aids, not the headline.
@@ -20,6 +27,7 @@ for that layer; they are measurement aids, not the headline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -34,6 +42,17 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "fused-MoE layer µs + weight HBM GB/s (frac of peak) at M=1..64; prefill TFLOP/s"
+FLUSH_BYTES = 1 << 30
+
+# HBM bytes per launch of the gate/up product, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs of this script (scaled by the reading of a 1 GiB copy), and
+# the SHA-256 of the kernel sources they were taken on.  The figure is
+# reported only while the sources are unchanged.
+KERNEL_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
+TRAFFIC = {
+    "mixtral": {"src_sha256": "5cbc9acf0d3b4f64658e98922c56a34917045524d485c56290cf6a5d8eb90279",
+                "bytes_per_launch": 1509012210},
+}
 
 
 def log(msg: str):
@@ -41,14 +60,26 @@ def log(msg: str):
     sys.stderr.flush()
 
 
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="mixtral", choices=["mixtral", "qwen3", "deepseek", "prefill", "tiny"])
+    ap.add_argument("--no-flush", action="store_true", help="hot-cache numbers: skip the cache flush before each call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times (reference reading for "
+                         "the FETCH_SIZE/WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is built and timed on a single MI355X; "
@@ -62,6 +93,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy)
     moe.load()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     cfg = CONFIGS[args.config]
@@ -82,10 +115,15 @@ def main() -> int:
         calls.append(dict(M=M, x=x, lg=lg, ws=ws, y=y, counts=counts))
 
     stream = torch.cuda.current_stream()
+    flush_buf = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
 
     def run(c, events=None):
         moe.fused_forward(c["x"], c["lg"], w13, w2, cfg.k, cfg.dtype, s13_t, s2_t, out=c["y"], workspace=c["ws"],
                           expert_counts=c["counts"], stream=stream, events=events)
+
+    def flush(i):
+        if flush_buf is not None:
+            flush_buf.fill_(i)
 
     # active experts from the layer's own routing, for the byte and flop accounting
     for c in calls:
@@ -97,21 +135,27 @@ def main() -> int:
         c["w_bytes"] = c["active"] * 3 * cfg.H * cfg.I * esz
         c["g1_bytes"] = c["active"] * 2 * cfg.H * cfg.I * esz
         c["flops"] = 6.0 * c["M"] * cfg.k * cfg.H * cfg.I
+        c["g1_flops"] = 4.0 * c["M"] * cfg.k * cfg.H * cfg.I
 
     log("warmup %d steps" % args.warmup)
-    for _ in range(args.warmup):
+    for s in range(args.warmup):
         for c in calls:
+            flush(s)
             run(c)
     torch.cuda.synchronize()
 
+    # Timed region: events only at the layer's start and end and around the
+    # gate/up launch (slots 0, 4, 5 and 9 of the library's stage events).
     ns = moe.NUM_STAGES
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)] for _ in calls] for _ in range(args.steps)]
+    timed_slots = (0, 4, 5, 2 * ns - 1)
+    evs = [[{i: torch.cuda.Event(enable_timing=True) for i in timed_slots} for _ in calls] for _ in range(args.steps)]
     for step in evs:  # materialise the hipEvent_t handles
         for per_call in step:
-            for e in per_call:
+            for e in per_call.values():
                 e.record(stream)
     torch.cuda.synchronize()
-    handles = [[[e.cuda_event for e in per_call] for per_call in step] for step in evs]
+    handles = [[[per_call[i].cuda_event if i in per_call else None for i in range(2 * ns)] for per_call in step]
+               for step in evs]
 
     log("timing %d steps" % args.steps)
     t_start = torch.cuda.Event(enable_timing=True)
@@ -120,44 +164,64 @@ def main() -> int:
     t_start.record(stream)
     for s in range(args.steps):
         for j, c in enumerate(calls):
+            flush(s + j)
             run(c, handles[s][j])
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    wall_ms = t_start.elapsed_time(t_end)
+
+    span_ms = [[evs[s][j][0].elapsed_time(evs[s][j][2 * ns - 1]) for s in range(args.steps)] for j in range(len(calls))]
+    g1_ms = [[evs[s][j][4].elapsed_time(evs[s][j][5]) for s in range(args.steps)] for j in range(len(calls))]
+    layer_ms_per_step = sum(sum(v) for v in span_ms) / args.steps
+
+    # Per-stage breakdown, outside the timed region (all ten events per call).
+    log("per-stage breakdown")
+    n_prof = min(args.steps, 10)
+    stage_ms = []
+    for j, c in enumerate(calls):
+        per = []
+        for s in range(n_prof):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)]
+            flush(s)
+            run(c, _materialise(e, stream))
+            per.append(e)
+        torch.cuda.synchronize()
+        stage_ms.append([statistics.median(p[2 * q].elapsed_time(p[2 * q + 1]) for p in per) for q in range(ns)])
 
     per_m = []
-    g1_ms_sum = 0.0
-    g1_bytes_sum = 0.0
     for j, c in enumerate(calls):
-        span = [evs[s][j][0].elapsed_time(evs[s][j][2 * ns - 1]) for s in range(args.steps)]
-        stage = [[evs[s][j][2 * q].elapsed_time(evs[s][j][2 * q + 1]) for s in range(args.steps)] for q in range(ns)]
-        g1_ms_sum += sum(stage[2])
-        g1_bytes_sum += c["g1_bytes"] * args.steps
-        us = statistics.median(span) * 1e3
+        us = statistics.median(span_ms[j]) * 1e3
         entry = dict(M=c["M"], us=round(us, 2), active_experts=c["active"], weight_bytes=c["w_bytes"],
                      gbps=round(c["w_bytes"] / us / 1e3, 1), hbm_frac=round(c["w_bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
-                     tflops=round(c["flops"] / us / 1e6, 2))
+                     tflops=round(c["flops"] / us / 1e6, 2),
+                     gate_up_gbps=round(c["g1_bytes"] / (statistics.median(g1_ms[j]) * 1e3) / 1e3, 1))
         for q, name in enumerate(moe.STAGE_NAMES):
-            entry["%s_us" % name] = round(statistics.median(stage[q]) * 1e3, 2)
+            entry["%s_us" % name] = round(stage_ms[j][q] * 1e3, 2)
         per_m.append(entry)
 
     total_bytes = sum(c["w_bytes"] for c in calls)
     total_flops = sum(c["flops"] for c in calls)
+    g1_total_ms = sum(sum(v) for v in g1_ms)
+    n_g1 = args.steps * len(calls)
     if cfg.name == "prefill":
-        value = total_flops / (ms_per_step * 1e-3) / 1e12
+        value = total_flops / (layer_ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-        g1_flops = 4.0 * calls[0]["M"] * cfg.k * cfg.H * cfg.I * args.steps
-        ach = g1_flops / (g1_ms_sum * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(ach, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / FP8_PEAK_TFLOPS, 4), traffic=None)
+        ach = sum(c["g1_flops"] for c in calls) * args.steps / (g1_total_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 1), peak=FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s")
     else:
-        value = total_bytes / (ms_per_step * 1e-3) / 1e9
+        value = total_bytes / (layer_ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
-        ach = g1_bytes_sum / (g1_ms_sum * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+        ach = sum(c["g1_bytes"] for c in calls) * args.steps / (g1_total_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = round(ach / roof["peak"], 4)
+    tr = TRAFFIC.get(cfg.name)
+    roof["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256()
+                                                 and not args.no_flush) else None
+    roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
     roof["kernel"] = "gemm1_decode_kernel (gate/up product + SiLU*up)"
+    roof["avg_launch_us"] = round(g1_total_ms * 1e3 / n_g1, 2)
+    roof["launches"] = n_g1
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -171,7 +235,9 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(layer_ms_per_step, 4),
+        "wall_ms_per_step": round(wall_ms / args.steps, 4),
+        "cache": "hot" if args.no_flush else "cold (1 GiB overwritten before each call, outside the layer span)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -190,32 +256,78 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(cfg, calls, weights, budget_s, unit):
-    """The CPU oracle on the same inputs, as many sweep points as fit the budget."""
+def _materialise(events, stream):
+    """hipEvent_t handles of fresh torch events (torch creates them lazily)."""
+    for e in events:
+        e.record(stream)
+    return [e.cuda_event for e in events]
+
+
+def calibrate_copy(mib: int) -> int:
+    """A plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
+    WRITE_SIZE readings per dispatch, divided by the bytes it must move,
+    give the factor that turns those counters into HBM bytes."""
     import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 5}), flush=True)
+    return 0
+
+
+def cpu_baseline(cfg, calls, weights, budget_s, unit, min_s=10.0):
+    """The CPU oracle on the same inputs, timed on a bounded sample.
+
+    The oracle evaluates every (token, expert) pair with dense loops, so its
+    time is proportional to the number of pairs it evaluates.  For each point
+    of the sweep (smallest M first) it runs the whole layer when that fits the
+    remaining budget, else an evenly spaced subset of the tokens, and its rate
+    is extrapolated to all M*k pairs of that point.  Short sweeps are repeated
+    until about min_s seconds have been spent.
+    """
     import oracle
 
     w13, w2, s13, s2 = weights
     log("cpu baseline: copying weights to the host")
     w13h, w2h = w13.cpu(), w2.cpu()
-    done, secs, work = [], 0.0, 0.0
-    for c in sorted(calls, key=lambda c: c["M"]):
-        x = c["x"].cpu()
-        lg = c["lg"].cpu()
-        # expected cost from the last measured rate; stop before the budget is exceeded
-        if done and secs / work * (c["w_bytes"] if unit == "GB/s" else c["flops"]) + secs > budget_s:
+    work_sum, secs_sum, spent, parts, rounds = 0.0, 0.0, 0.0, [], 0
+    sec_per_pair = None
+    while rounds == 0 or (spent < min(min_s, budget_s) and all(p.endswith(":all") for p in parts)):
+        rounds += 1
+        for c in sorted(calls, key=lambda c: c["M"]):
+            M = c["M"]
+            left = budget_s / len(calls) if sec_per_pair is None else (budget_s - spent) / len(calls)
+            n_tok = M if sec_per_pair is None else int(max(1, min(M, left / (sec_per_pair * cfg.k))))
+            if sec_per_pair is None and M * cfg.k > 256:
+                n_tok = max(1, 256 // cfg.k)  # probe the rate first
+            toks = sorted({int(round(i * (M - 1) / max(n_tok - 1, 1))) for i in range(n_tok)}) if n_tok < M else None
+            log("cpu baseline: oracle at M=%d on %s tokens" % (M, M if toks is None else len(toks)))
+            x, lg = c["x"].cpu(), c["lg"].cpu()
+            t0 = time.perf_counter()
+            oracle.layer(x, lg, w13h, w2h, cfg.k, cfg.dtype, s13, s2, tokens=toks,
+                         all_pairs_h=False if toks is not None else None)
+            dt = time.perf_counter() - t0
+            spent += dt
+            n_pairs = (M if toks is None else len(toks)) * cfg.k
+            sec_per_pair = dt / n_pairs
+            work_sum += c["w_bytes"] if unit == "GB/s" else c["flops"]
+            secs_sum += sec_per_pair * M * cfg.k
+            if rounds == 1:
+                parts.append("M=%d:%s" % (M, "all" if toks is None else "%d/%d tokens" % (len(toks), M)))
+            if spent > budget_s:
+                break
+        if spent > budget_s:
             break
-        log("cpu baseline: oracle at M=%d" % c["M"])
-        t0 = time.perf_counter()
-        oracle.layer(x, lg, w13h, w2h, cfg.k, cfg.dtype, s13, s2)
-        secs += time.perf_counter() - t0
-        work += c["w_bytes"] if unit == "GB/s" else c["flops"]
-        done.append(c["M"])
-    val = work / secs / (1e9 if unit == "GB/s" else 1e12)
+    val = work_sum / secs_sum / (1e9 if unit == "GB/s" else 1e12)
     return {"value": round(val, 4), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
-            "seconds": round(secs, 2),
-            "sample": "full layer (all tokens) at M in {%s} of the sweep; weights already in host memory"
-                      % ",".join(str(m) for m in done)}
+            "seconds": round(spent, 2),
+            "sample": "oracle (scalar fp64, OpenMP) on the same seeded inputs, weights in host memory; "
+                      "points %s, %d pass(es); a token subset is extrapolated by pairs to the full layer"
+                      % (", ".join(parts), rounds)}
 
 
 if __name__ == "__main__":

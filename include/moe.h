@@ -172,6 +172,8 @@ moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream);
  * and events[2*s+1] after each of its MOE_NUM_STAGES launches on `stream`
  * (stage order: route, align, gate/up product, down product, finalize).
  * A stage that is not launched still records both events back to back.
+ * NULL entries of `events` are skipped, so a caller can time only the stages
+ * it needs without adding markers between the others.
  */
 #define MOE_NUM_STAGES 5
 moe_status_t moe_fused_forward_profiled(const moe_fused_args_t* args, void* stream, void* const* events);

@@ -302,7 +302,7 @@ size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int3
 static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev) {
   if (!a) return MOE_ERR_INVALID_ARG;
   auto rec = [&](int i) {
-    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], st);
+    if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
   };
   moe_status_t rc = check_shape(a->M, a->E, a->top_k);
   if (rc != MOE_OK) return rc;
