@@ -116,10 +116,12 @@ moe_status_t moe_quant_e4m3(const float* in, int64_t n, const float* scale, uint
  * MOE_ERR_UNSUPPORTED.
  */
 typedef struct {
-  int32_t gemm1_ksplit;   /* waves of a workgroup splitting K of the gate/up product: 1, 2 or 4 */
-  int32_t gemm2_ksplit;   /* K slices of the down product, each a separate wave: 1..16 */
-  int32_t token_tiles;    /* 16-token tiles held per pass: 1..4 */
-  int32_t unroll;         /* MFMA K-steps per pipeline stage: 1, 2 or 4 */
+  int32_t gemm1_ksplit;      /* waves of a gate/up workgroup splitting K: 1, 2 or 4 */
+  int32_t gemm2_ksplit;      /* K slices of the down product in separate workgroups: 1..16, within the
+                                workspace's partial-sum capacity */
+  int32_t token_tiles;       /* 16-token tiles held per pass, both products: 1..4 */
+  int32_t unroll;            /* MFMA K-steps per pipeline stage, both products: bf16 2 or 4, fp8 1 or 2 */
+  int32_t gemm2_wave_ksplit; /* waves of a down workgroup splitting K: 1, 2 or 4 */
 } moe_tuning_t;
 
 /*

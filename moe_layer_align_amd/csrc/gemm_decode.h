@@ -57,6 +57,79 @@ __device__ __forceinline__ f32x4 mma(const Frag<FP8>& a, const Frag<FP8>& b, f32
 }
 
 // --------------------------------------------------------------------------
+// K-loop shared by both products: NA weight tiles (A operands) times NB
+// token tiles (B operands), U MFMA k-steps per pipeline stage, two stages in
+// registers.  The steady state has no branches between a stage's loads and
+// the MFMAs of the previous stage, so the compiler's wait before those MFMAs
+// covers only the older stage and one full stage of loads stays in flight
+// while the wave computes.  pa[i] / pb[t] point at the lane's first bytes;
+// consecutive k-steps are SB bytes apart.
+// --------------------------------------------------------------------------
+template <bool FP8, int NA, int NB, int U>
+struct StageRegs {
+  Frag<FP8> a[U][NA];
+  Frag<FP8> b[U][NB];
+};
+
+template <bool FP8, int NA, int NB, int U, int SB>
+__device__ __forceinline__ void stage_load(StageRegs<FP8, NA, NB, U>& s, const uint8_t* const* pa,
+                                           const uint8_t* const* pb, int64_t off) {
+#pragma unroll
+  for (int q = 0; q < U; ++q) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) load_frag<FP8>(s.a[q][i], pa[i] + off + q * SB);
+#pragma unroll
+    for (int t = 0; t < NB; ++t) load_frag<FP8>(s.b[q][t], pb[t] + off + q * SB);
+  }
+}
+
+template <bool FP8, int NA, int NB, int U>
+__device__ __forceinline__ void stage_mma(const StageRegs<FP8, NA, NB, U>& s, f32x4 (&acc)[NA][NB]) {
+#pragma unroll
+  for (int q = 0; q < U; ++q)
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < NA; ++i) acc[i][t] = mma<FP8>(s.a[q][i], s.b[q][t], acc[i][t]);
+}
+
+// acc += sum over nsteps k-steps of A_i . B_t
+template <bool FP8, int NA, int NB, int U, int SB>
+__device__ __forceinline__ void stream_k(const uint8_t* const* pa, const uint8_t* const* pb, int nsteps,
+                                         f32x4 (&acc)[NA][NB]) {
+  constexpr int SS = U * SB;  // bytes per row per stage
+  const int nfull = nsteps / U;
+  if (nfull > 0) {
+    StageRegs<FP8, NA, NB, U> s0, s1;
+    stage_load<FP8, NA, NB, U, SB>(s0, pa, pb, 0);
+    int it = 0;
+    for (; it + 2 < nfull; it += 2) {
+      stage_load<FP8, NA, NB, U, SB>(s1, pa, pb, (int64_t)(it + 1) * SS);
+      __builtin_amdgcn_sched_barrier(0);  // keep the whole stage's loads ahead of the MFMAs
+      stage_mma<FP8, NA, NB, U>(s0, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_load<FP8, NA, NB, U, SB>(s0, pa, pb, (int64_t)(it + 2) * SS);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_mma<FP8, NA, NB, U>(s1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (it + 1 < nfull) {
+      stage_load<FP8, NA, NB, U, SB>(s1, pa, pb, (int64_t)(it + 1) * SS);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_mma<FP8, NA, NB, U>(s0, acc);
+      stage_mma<FP8, NA, NB, U>(s1, acc);
+    } else {
+      stage_mma<FP8, NA, NB, U>(s0, acc);
+    }
+  }
+  for (int st = nfull * U; st < nsteps; ++st) {
+    StageRegs<FP8, NA, NB, 1> s;
+    stage_load<FP8, NA, NB, 1, SB>(s, pa, pb, (int64_t)st * SB);
+    stage_mma<FP8, NA, NB, 1>(s, acc);
+  }
+}
+
+// --------------------------------------------------------------------------
 // Gate/up product with the SiLU(gate)*up epilogue.
 //
 // Wave tile: 16 output features i0..i0+15, i.e. gate rows i0.. and up rows
@@ -77,104 +150,47 @@ struct Gemm1Args {
   unsigned* h_amax;          // fp8 dynamic: running max of |h| (float bits)
 };
 
-template <bool FP8, int HFMT, int NT, int U, int KSPLIT>
-__global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
+// Body for NB (<= NT) token tiles; the kernel picks NB from the workgroup's
+// token count so that tiles with no token issue no loads and no MFMAs.
+template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT>
+__device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int e, int seg, int cnt, int pass0) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;   // k per MFMA
   constexpr int LB = FP8 ? 32 : 16;       // bytes per lane per operand per step
   constexpr int SB = KSTEP * ESZ;         // bytes per row per step
   constexpr int TPW = 4 / KSPLIT;         // feature tiles per workgroup
-  __shared__ f32x4 s_red[KSPLIT > 1 ? (KSPLIT - 1) * TPW * 2 * NT * 64 : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KSPLIT, tile = wave / KSPLIT;
-  const int s = blockIdx.y;
-  if (s >= *a.seg.num_active) return;
-  const int e = a.seg.active[s];
-  const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
-  const int pass0 = blockIdx.z * NT * 16;
-  if (pass0 >= cnt) return;
-
   const int r16 = lane & 15, kq = lane >> 4;
   const int i0 = (blockIdx.x * TPW + tile) * 16;
   const int Kw = a.H / KSPLIT;
   const int kbeg = kpart * Kw;
-  const int nsteps = Kw / KSTEP;
 
   const int64_t rowb = (int64_t)a.H * ESZ;
-  const uint8_t* pg = a.w13 + ((int64_t)e * 2 * a.I + i0 + r16) * rowb + (int64_t)kbeg * ESZ + kq * LB;
-  const uint8_t* pu = pg + (int64_t)a.I * rowb;
-  const uint8_t* pb[NT];
+  const uint8_t* pa[2];
+  pa[0] = a.w13 + ((int64_t)e * 2 * a.I + i0 + r16) * rowb + (int64_t)kbeg * ESZ + kq * LB;  // gate rows
+  pa[1] = pa[0] + (int64_t)a.I * rowb;                                                         // up rows
+  const uint8_t* pb[NB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < NB; ++t) {
     const int slot = min(pass0 + t * 16 + r16, cnt - 1);
     const int m = a.seg.sorted_ids[seg + slot] / a.top_k;
     pb[t] = a.act + (int64_t)m * rowb + (int64_t)kbeg * ESZ + kq * LB;
   }
 
-  f32x4 accg[NT], accu[NT];
+  f32x4 acc[2][NB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    accg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  struct Stage {
-    Frag<FP8> g[U], u[U], b[U][NT];
-  };
-  auto load_stage = [&](Stage& st, int step0) {
-#pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const int64_t off = (int64_t)(step0 + q) * SB;
-      load_frag<FP8>(st.g[q], pg + off);
-      load_frag<FP8>(st.u[q], pu + off);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) load_frag<FP8>(st.b[q][t], pb[t] + off);
-    }
-  };
-  auto compute_stage = [&](const Stage& st) {
-#pragma unroll
-    for (int q = 0; q < U; ++q)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        accg[t] = mma<FP8>(st.g[q], st.b[q][t], accg[t]);
-        accu[t] = mma<FP8>(st.u[q], st.b[q][t], accu[t]);
-      }
-  };
-
-  const int nfull = nsteps / U;
-  if (nfull > 0) {
-    Stage s0, s1;
-    load_stage(s0, 0);
-    for (int it = 0; it < nfull; it += 2) {
-      if (it + 1 < nfull) load_stage(s1, (it + 1) * U);
-      compute_stage(s0);
-      if (it + 1 < nfull) {
-        if (it + 2 < nfull) load_stage(s0, (it + 2) * U);
-        compute_stage(s1);
-      }
-    }
-  }
-  for (int st = nfull * U; st < nsteps; ++st) {
-    Frag<FP8> g, u, b[NT];
-    load_frag<FP8>(g, pg + (int64_t)st * SB);
-    load_frag<FP8>(u, pu + (int64_t)st * SB);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) load_frag<FP8>(b[t], pb[t] + (int64_t)st * SB);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      accg[t] = mma<FP8>(g, b[t], accg[t]);
-      accu[t] = mma<FP8>(u, b[t], accu[t]);
-    }
-  }
+  for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_k<FP8, 2, NB, U, SB>(pa, pb, Kw / KSTEP, acc);
 
   if constexpr (KSPLIT > 1) {
     if (kpart > 0) {
       f32x4* dst = s_red + (((kpart - 1) * TPW + tile) * 2 * NT) * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        dst[(2 * t) * 64] = accg[t];
-        dst[(2 * t + 1) * 64] = accu[t];
+      for (int t = 0; t < NB; ++t) {
+        dst[(2 * t) * 64] = acc[0][t];
+        dst[(2 * t + 1) * 64] = acc[1][t];
       }
     }
     __syncthreads();
@@ -183,9 +199,9 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
     for (int p = 0; p < KSPLIT - 1; ++p) {
       const f32x4* src = s_red + ((p * TPW + tile) * 2 * NT) * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        accg[t] += src[(2 * t) * 64];
-        accu[t] += src[(2 * t + 1) * 64];
+      for (int t = 0; t < NB; ++t) {
+        acc[0][t] += src[(2 * t) * 64];
+        acc[1][t] += src[(2 * t + 1) * 64];
       }
     }
   }
@@ -195,15 +211,15 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
   float hmax = 0.0f;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < NB; ++t) {
     const int slot = pass0 + t * 16 + r16;
     if (slot < cnt) {
       const int f = a.seg.sorted_ids[seg + slot];
       float hv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float g = accg[t][r] * deq;
-        const float u = accu[t][r] * deq;
+        const float g = acc[0][t][r] * deq;
+        const float u = acc[1][t][r] * deq;
         hv[r] = g / (1.0f + expf(-g)) * u;
         hmax = fmaxf(hmax, fabsf(hv[r]));
       }
@@ -224,13 +240,36 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
   }
 }
 
+template <bool FP8, int HFMT, int NT, int U, int KSPLIT>
+__global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
+  constexpr int TPW = 4 / KSPLIT;
+  __shared__ f32x4 s_red[KSPLIT > 1 ? (KSPLIT - 1) * TPW * 2 * NT * 64 : 1];
+  const int s = blockIdx.y;
+  if (s >= *a.seg.num_active) return;
+  const int e = a.seg.active[s];
+  const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
+  const int pass0 = blockIdx.z * NT * 16;
+  if (pass0 >= cnt) return;
+  const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
+  if constexpr (NT >= 4)
+    if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
+  if constexpr (NT >= 3)
+    if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
+  if constexpr (NT >= 2)
+    if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
+  gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
+}
+
 // --------------------------------------------------------------------------
-// Down product with the routing-weighted scatter-add combine.
+// Down product.
 //
-// Wave tile: 32 output rows (two 16-row MFMA tiles of W2[e]) over one K slice
-// of I, times NT 16-token tiles.  Every wave adds w[pair] * (partial product)
-// into the fp32 accumulator y_acc[m] with hardware float atomics, so K slices
-// need no other reduction and the top-k combine is part of the epilogue.
+// Wave tile: 32 output rows (two 16-row MFMA tiles of W2[e]) over one K
+// slice of I, times the workgroup's 16-token tiles.  Each wave stores its
+// dequantised partial sums with plain stores into part[kslice][pair][row]:
+// every element is written by exactly one wave, so no atomics and no
+// clearing are needed, and the top-k combine (the routing-weighted sum over
+// the token's experts and over the K slices) happens in a fixed order in
+// the finalize kernel, which makes the layer's output bitwise reproducible.
 //
 // Token operand: bf16 h or static-scale e4m3 h is read from global memory
 // (L2-resident) like the weights.  With a dynamic fp8 scale h is kept in fp32
@@ -248,48 +287,47 @@ struct Gemm2Args {
   const float* w_scale;      // fp8: s_w2
   const float* h_scale;      // fp8 static: s_h
   const unsigned* h_amax;    // fp8 dynamic: max |h| (float bits)
-  float* y_acc;              // [M][H]
+  float* part;               // [ksplit][P][H] partial outputs
+  int P;
 };
 
 // LDS row stride (bytes) of the quantised token slice: Kw plus 16 bytes so
 // that the 16 token rows read by one instruction fall in different banks.
 __host__ __device__ constexpr int gemm2_lds_stride(int kw_bytes) { return kw_bytes + 16; }
 
-template <bool FP8, int HFMT, int NT, int U>
-__global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
+// Body for NB (<= NT) token tiles.  WKS waves of the workgroup split the
+// slice's K range and are summed through LDS (s_red); 4/WKS groups of 32 rows
+// per workgroup.
+template <bool FP8, int HFMT, int NT, int NB, int U, int WKS>
+__device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f32x4* s_red, int e, int seg, int cnt,
+                                           int pass0, int kslice) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;
   constexpr int LB = FP8 ? 32 : 16;
   constexpr int SB = KSTEP * ESZ;
   constexpr int HSZ = HFMT == H_BF16 ? 2 : (HFMT == H_F32 ? 4 : 1);
   constexpr bool QH = FP8 && HFMT == H_F32;  // token operand staged in LDS
-  extern __shared__ __align__(16) uint8_t s_tok[];
+  constexpr int TPW = 4 / WKS;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int s = blockIdx.y;
-  if (s >= *a.seg.num_active) return;
-  const int e = a.seg.active[s];
-  const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
-  const int kslice = blockIdx.z % a.ksplit;
-  const int pass0 = (blockIdx.z / a.ksplit) * NT * 16;
-  if (pass0 >= cnt) return;
-
+  const int kpart = wave % WKS, tile = wave / WKS;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int n0 = (blockIdx.x * 4 + wave) * 32;
-  const int Kw = a.I / a.ksplit;
+  const int n0 = (blockIdx.x * TPW + tile) * 32;
+  const int Kw = a.I / a.ksplit;       // K range of the workgroup
   const int kbeg = kslice * Kw;
-  const int nsteps = Kw / KSTEP;
+  const int Kp = Kw / WKS;             // K range of the wave
+  const int koff = kpart * Kp;
 
   float deq = 1.0f;
   if constexpr (FP8) {
     const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
     deq = sh * (*a.w_scale);
     if constexpr (QH) {
-      // quantise the workgroup's token slice into LDS: NT*16 rows of Kw bytes
+      // quantise the workgroup's token slice into LDS: NB*16 rows of Kw bytes
       const float rh = 1.0f / sh;
       const int stride = gemm2_lds_stride(Kw);
       const int per_row = Kw / 16;  // 16 elements per thread-step
-      for (int idx = threadIdx.x; idx < NT * 16 * per_row; idx += 256) {
+      for (int idx = threadIdx.x; idx < NB * 16 * per_row; idx += 256) {
         const int row = idx / per_row, c = (idx - row * per_row) * 16;
         const int slot = min(pass0 + row, cnt - 1);
         const int f = a.seg.sorted_ids[seg + slot];
@@ -307,107 +345,133 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   }
 
   const int64_t rowb = (int64_t)a.I * ESZ;
-  const uint8_t* pa0 = a.w2 + ((int64_t)e * a.H + n0 + r16) * rowb + (int64_t)kbeg * ESZ + kq * LB;
-  const uint8_t* pa1 = pa0 + 16 * rowb;
-  const uint8_t* pb[NT];
+  const uint8_t* pa[2];
+  pa[0] = a.w2 + ((int64_t)e * a.H + n0 + r16) * rowb + (int64_t)(kbeg + koff) * ESZ + kq * LB;
+  pa[1] = pa[0] + 16 * rowb;
+  const uint8_t* pb[NB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < NB; ++t) {
     if constexpr (QH) {
-      pb[t] = s_tok + (t * 16 + r16) * gemm2_lds_stride(Kw) + kq * LB;
+      pb[t] = s_tok + (t * 16 + r16) * gemm2_lds_stride(Kw) + koff + kq * LB;
     } else {
       const int slot = min(pass0 + t * 16 + r16, cnt - 1);
       const int f = a.seg.sorted_ids[seg + slot];
-      pb[t] = a.h + ((int64_t)f * a.I + kbeg) * HSZ + kq * LB;
+      pb[t] = a.h + ((int64_t)f * a.I + kbeg + koff) * HSZ + kq * LB;
     }
   }
 
-  f32x4 acc0[NT], acc1[NT];
+  f32x4 acc[2][NB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    acc0[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_k<FP8, 2, NB, U, SB>(pa, pb, Kp / KSTEP, acc);
 
-  struct Stage {
-    Frag<FP8> w0[U], w1[U], b[U][NT];
-  };
-  auto load_stage = [&](Stage& st, int step0) {
+  if constexpr (WKS > 1) {
+    if (kpart > 0) {
+      f32x4* dst = s_red + (((kpart - 1) * TPW + tile) * 2 * NT) * 64 + lane;
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const int64_t off = (int64_t)(step0 + q) * SB;
-      load_frag<FP8>(st.w0[q], pa0 + off);
-      load_frag<FP8>(st.w1[q], pa1 + off);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) load_frag<FP8>(st.b[q][t], pb[t] + off);
-    }
-  };
-  auto compute_stage = [&](const Stage& st) {
-#pragma unroll
-    for (int q = 0; q < U; ++q)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        acc0[t] = mma<FP8>(st.w0[q], st.b[q][t], acc0[t]);
-        acc1[t] = mma<FP8>(st.w1[q], st.b[q][t], acc1[t]);
+      for (int t = 0; t < NB; ++t) {
+        dst[(2 * t) * 64] = acc[0][t];
+        dst[(2 * t + 1) * 64] = acc[1][t];
       }
-  };
-
-  const int nfull = nsteps / U;
-  if (nfull > 0) {
-    Stage s0, s1;
-    load_stage(s0, 0);
-    for (int it = 0; it < nfull; it += 2) {
-      if (it + 1 < nfull) load_stage(s1, (it + 1) * U);
-      compute_stage(s0);
-      if (it + 1 < nfull) {
-        if (it + 2 < nfull) load_stage(s0, (it + 2) * U);
-        compute_stage(s1);
+    }
+    __syncthreads();
+    if (kpart > 0) return;
+#pragma unroll
+    for (int p = 0; p < WKS - 1; ++p) {
+      const f32x4* src = s_red + ((p * TPW + tile) * 2 * NT) * 64 + lane;
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        acc[0][t] += src[(2 * t) * 64];
+        acc[1][t] += src[(2 * t + 1) * 64];
       }
     }
   }
-  for (int st = nfull * U; st < nsteps; ++st) {
-    Frag<FP8> w0, w1, b[NT];
-    load_frag<FP8>(w0, pa0 + (int64_t)st * SB);
-    load_frag<FP8>(w1, pa1 + (int64_t)st * SB);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) load_frag<FP8>(b[t], pb[t] + (int64_t)st * SB);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      acc0[t] = mma<FP8>(w0, b[t], acc0[t]);
-      acc1[t] = mma<FP8>(w1, b[t], acc1[t]);
-    }
-  }
 
+  float* part = a.part + (int64_t)kslice * a.P * a.H;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < NB; ++t) {
     const int slot = pass0 + t * 16 + r16;
     if (slot < cnt) {
       const int f = a.seg.sorted_ids[seg + slot];
-      const int m = f / a.top_k;
-      const float w = a.topk_w[f] * deq;
-      float* yr = a.y_acc + (int64_t)m * a.H + n0 + kq * 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        unsafeAtomicAdd(yr + r, acc0[t][r] * w);
-        unsafeAtomicAdd(yr + 16 + r, acc1[t][r] * w);
-      }
+      float* dst = part + (int64_t)f * a.H + n0 + kq * 4;
+      *(f32x4*)dst = acc[0][t] * deq;
+      *(f32x4*)(dst + 16) = acc[1][t] * deq;
     }
   }
 }
 
-// y = bf16(y_acc), 8 elements per thread; also reports the scales in effect.
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ y_acc, uint16_t* __restrict__ y,
-                                                       int64_t n, const float* x_scale, const unsigned* h_amax,
+// Grid: x = groups of 32*(4/WKS) output rows, y = active expert, z = K slice
+// + ksplit * token pass.
+template <bool FP8, int HFMT, int NT, int U, int WKS>
+__global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
+  extern __shared__ __align__(16) uint8_t s_tok[];
+  constexpr int TPW = 4 / WKS;
+  __shared__ f32x4 s_red[WKS > 1 ? (WKS - 1) * TPW * 2 * NT * 64 : 1];
+  const int s = blockIdx.y;
+  if (s >= *a.seg.num_active) return;
+  const int e = a.seg.active[s];
+  const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
+  const int kslice = blockIdx.z % a.ksplit;
+  const int pass0 = (blockIdx.z / a.ksplit) * NT * 16;
+  if (pass0 >= cnt) return;
+  const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
+  if constexpr (NT >= 4)
+    if (ntile == 4) return gemm2_body<FP8, HFMT, NT, 4, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+  if constexpr (NT >= 3)
+    if (ntile == 3) return gemm2_body<FP8, HFMT, NT, 3, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+  if constexpr (NT >= 2)
+    if (ntile == 2) return gemm2_body<FP8, HFMT, NT, 2, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+  gemm2_body<FP8, HFMT, NT, 1, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+}
+
+// LDS of a down-product workgroup: the K-split reduction buffer.
+__host__ __device__ constexpr int gemm2_red_bytes(int nt, int wks) {
+  return wks > 1 ? (wks - 1) * (4 / wks) * 2 * nt * 64 * 16 : 16;
+}
+
+// Top-k combine and output rounding:
+//   y[m,n] = bf16( sum_j w[m,j] * (sum_s part[s][m*k+j][n]) )
+// One lane per (group of four outputs, expert slot j): the lane loads its
+// K slices all at once (s ascending), scales by w[m,j], and the KP lanes of a
+// group (KP = k rounded up to a power of two) add their terms by a fixed
+// xor-butterfly, so the result does not depend on scheduling and every call
+// gives the same bits.  Also reports the fp8 scales in effect.
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, const float* __restrict__ topk_w,
+                                                       uint16_t* __restrict__ y, int M, int H, int top_k, int log2kp,
+                                                       int ksplit, const float* x_scale, const unsigned* h_amax,
                                                        const float* h_scale, float* scales_out) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (scales_out && blockIdx.x == 0 && threadIdx.x == 0) {
     scales_out[0] = *x_scale;
     scales_out[1] = h_scale ? *h_scale : scale_from_amax(__uint_as_float(*h_amax));
   }
-  if (i >= n) return;
-  const f32x4 a = *(const f32x4*)(y_acc + i);
-  const f32x4 b = *(const f32x4*)(y_acc + i + 4);
-  u32x4 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
-  *(u32x4*)(y + i) = o;
+  const int kp = 1 << log2kp;
+  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> log2kp;  // output group
+  const int j = threadIdx.x & (kp - 1);
+  const int64_t i = g * 4;
+  const bool live = i < (int64_t)M * H;
+  const int m = live ? (int)(i / H) : 0, n = live ? (int)(i - (int64_t)m * H) : 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (live && j < top_k) {
+    const int64_t f = (int64_t)m * top_k + j;
+    const int64_t slice = (int64_t)M * top_k * H;
+    const float* p = part + f * H + n;
+    f32x4 v[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) v[s] = s < ksplit ? *(const f32x4*)(p + s * slice) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 o = v[0];
+#pragma unroll
+    for (int s = 1; s < 16; ++s)
+      if (s < ksplit) o += v[s];
+    acc = o * topk_w[f];
+  }
+  for (int off = 1; off < kp; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+  }
+  if (live && j == 0) {
+    uint2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *(uint2*)(y + i) = out;
+  }
 }
 
 // Stand-alone per-tensor e4m3 quantisation of fp32 data with a given scale.

@@ -33,6 +33,27 @@ moe_status_t launch_status() {
   return err == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
+constexpr int kDownLdsMax = 65536;  // LDS of one down-product workgroup staging e4m3 h
+
+// Largest K split of the down product that the workspace holds partial sums
+// for (ksplit * P * H fp32): as many slices as fit 64 MB, at most 16, and in
+// fp8 mode at least the smallest split whose e4m3 token slice (64 tokens)
+// fits the down product's LDS.
+int down_ksplit_cap(int64_t P, int H, int I, bool fp8) {
+  const int64_t per = std::max<int64_t>(1, P * (int64_t)H * 4);
+  int cap = (int)std::max<int64_t>(1, std::min<int64_t>(16, (int64_t(64) << 20) / per));
+  if (fp8) {
+    const int nsteps = I / 128;
+    for (int ks = 1; ks <= 16; ++ks) {
+      if (nsteps % ks == 0 && 64 * gemm2_lds_stride(I / ks) <= kDownLdsMax) {
+        cap = std::max(cap, ks);
+        break;
+      }
+    }
+  }
+  return cap;
+}
+
 int64_t align_capacity(int64_t P, int E, int B) {
   int64_t cap = P + std::min<int64_t>(E, P) * (B - 1);
   return cdiv(cap, B) * B;
@@ -41,7 +62,7 @@ int64_t align_capacity(int64_t P, int E, int B) {
 // ---------------------------------------------------------------- workspace
 struct Layout {
   size_t ids, wts, counts, offsets, sorted, block_expert, num_padded, active, num_active;
-  size_t xamax_part, scale_slot, h_amax, xq, h, y_acc, total;
+  size_t xamax_part, scale_slot, h_amax, xq, h, part, total;
   int64_t capacity;
   int n_blocks, n_route_wg;
 };
@@ -73,69 +94,89 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
   const bool fp8 = dt == MOE_DTYPE_FP8_E4M3;
   L.xq = take(fp8 ? (size_t)M * H : 0);
   L.h = take((size_t)P * I * (fp8 ? 4 : 2));
-  L.y_acc = take((size_t)M * H * 4);
+  L.part = take((size_t)down_ksplit_cap(P, H, I, dt == MOE_DTYPE_FP8_E4M3) * (size_t)P * H * 4);
   L.total = off;
   return L;
 }
 
 // ---------------------------------------------------------------- variants
+// Launch shape of the two products.  The defaults come from cold-cache sweeps
+// on the Mixtral-, Qwen3- and DeepSeek-shaped decode layers: streaming expert
+// weights from HBM favours fewer waves with deeper software pipelines (the
+// 4-token-tile variants keep a workgroup's registers high on purpose) over
+// high occupancy.
 struct Plan {
-  int nt, passes, u1, ks1, u2, ks2, lds2;
+  int nt1, passes1, u1, ks1;               // gate/up
+  int nt2, passes2, u2, ks2, wks2, lds2;   // down
 };
 
-int default_u(bool fp8, int nt) { return fp8 ? (nt <= 2 ? 2 : 1) : (nt <= 2 ? 4 : 2); }
-
 bool valid_u(bool fp8, int u) { return fp8 ? (u == 1 || u == 2) : (u == 2 || u == 4); }
+bool valid_wsplit(int ks) { return ks == 1 || ks == 2 || ks == 4; }
 
 moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, const moe_tuning_t* t, Plan* p) {
   const int kstep = fp8 ? 128 : 32;
   const int64_t P = (int64_t)M * k;
-  const int n_act = (int)std::min<int64_t>(E, P);
-  p->nt = (int)std::min<int64_t>(4, std::max<int64_t>(1, cdiv(std::min(M, 64), 16)));
-  if (p->nt == 3) p->nt = 4;
+  const int n_act = (int)std::min<int64_t>(E, P);  // upper bound on experts with tokens
+  if (fp8) {
+    p->nt1 = M >= 8 ? 4 : 1;
+    p->u1 = (p->nt1 == 4 && H < 4096) ? 1 : 2;
+    p->ks1 = (p->nt1 == 4 && H >= 4096) ? 1 : 4;
+    p->nt2 = 1;
+    p->u2 = 1;
+    p->wks2 = 1;
+  } else {
+    p->nt1 = p->nt2 = 2;
+    p->u1 = p->u2 = 4;
+    p->ks1 = 4;
+    p->wks2 = 4;
+  }
   if (t && t->token_tiles > 0) {
     if (t->token_tiles > 4) return MOE_ERR_UNSUPPORTED;
-    p->nt = t->token_tiles == 3 ? 4 : t->token_tiles;
+    p->nt1 = p->nt2 = t->token_tiles == 3 ? 4 : t->token_tiles;
   }
-  p->passes = (int)cdiv(M, p->nt * 16);
-  p->u1 = p->u2 = default_u(fp8, p->nt);
   if (t && t->unroll > 0) {
     if (!valid_u(fp8, t->unroll)) return MOE_ERR_UNSUPPORTED;
     p->u1 = p->u2 = t->unroll;
   }
-  // gate/up: split K over the 4 waves when each wave keeps >= 2 stages
-  p->ks1 = 1;
-  for (int ks : {4, 2}) {
-    if ((H / ks) % kstep == 0 && (H / ks) / kstep >= 2 * p->u1) {
-      p->ks1 = ks;
-      break;
-    }
-  }
   if (t && t->gemm1_ksplit > 0) {
-    const int ks = t->gemm1_ksplit;
-    if (!(ks == 1 || ks == 2 || ks == 4) || (H / ks) % kstep != 0) return MOE_ERR_UNSUPPORTED;
-    p->ks1 = ks;
+    if (!valid_wsplit(t->gemm1_ksplit)) return MOE_ERR_UNSUPPORTED;
+    p->ks1 = t->gemm1_ksplit;
+  } else {
+    while (p->ks1 > 1 && (H / p->ks1) % kstep != 0) p->ks1 /= 2;  // each wave takes whole K-steps
   }
-  // down: K slices are independent waves; aim for ~8192 waves in flight
+  if (t && t->gemm2_wave_ksplit > 0) {
+    if (!valid_wsplit(t->gemm2_wave_ksplit)) return MOE_ERR_UNSUPPORTED;
+    p->wks2 = t->gemm2_wave_ksplit;
+  }
+  if ((H / p->ks1) % kstep != 0) return MOE_ERR_UNSUPPORTED;
+  p->passes1 = (int)cdiv(M, p->nt1 * 16);
+  p->passes2 = (int)cdiv(M, p->nt2 * 16);
+
+  // down: K slices in separate workgroups; each slice's K range must split
+  // evenly over wks2 waves, and with a dynamic fp8 h scale the quantised
+  // token slice must fit the workgroup's LDS.  Default: the fewest slices
+  // that give at least 1024 workgroups (4 per CU).
   const int nsteps2 = I / kstep;
-  const int64_t base_waves = (int64_t)(H / 32) * n_act * p->passes;
-  const int64_t want = std::max<int64_t>(1, 8192 / std::max<int64_t>(1, base_waves));
-  auto lds_ok = [&](int ks) {
-    return !qh || (int64_t)p->nt * 16 * gemm2_lds_stride(I / ks) <= 65536;
+  auto fits = [&](int ks) {
+    if (nsteps2 % (ks * p->wks2) != 0) return false;
+    const int64_t lds = (qh ? (int64_t)p->nt2 * 16 * gemm2_lds_stride(I / ks) : 0) + gemm2_red_bytes(p->nt2, p->wks2);
+    return lds <= kDownLdsMax;
   };
+  const int ks_cap = down_ksplit_cap(P, H, I, fp8);
+  const int64_t wgs_per_slice = (int64_t)(H / (32 * (4 / p->wks2))) * n_act * p->passes2;
   p->ks2 = 0;
-  for (int ks = 1; ks <= 16; ++ks) {
-    if (nsteps2 % ks != 0 || !lds_ok(ks)) continue;
-    if (p->ks2 == 0) p->ks2 = ks;  // smallest feasible
-    if (ks <= want && nsteps2 / ks >= p->u2) p->ks2 = ks;
+  for (int ks = 1; ks <= ks_cap; ++ks) {
+    if (!fits(ks)) continue;
+    p->ks2 = ks;
+    if (wgs_per_slice * ks >= 1024) break;
   }
   if (t && t->gemm2_ksplit > 0) {
     const int ks = t->gemm2_ksplit;
-    if (ks > 16 || nsteps2 % ks != 0 || !lds_ok(ks)) return MOE_ERR_UNSUPPORTED;
+    if (ks > ks_cap || !fits(ks)) return MOE_ERR_UNSUPPORTED;
     p->ks2 = ks;
   }
   if (p->ks2 == 0) return MOE_ERR_UNSUPPORTED;
-  p->lds2 = qh ? p->nt * 16 * gemm2_lds_stride(I / p->ks2) : 0;
+  p->lds2 = qh ? p->nt2 * 16 * gemm2_lds_stride(I / p->ks2) : 0;
   return MOE_OK;
 }
 
@@ -177,29 +218,39 @@ bool g1_nt(int nt, int u, int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
   return false;
 }
 
-template <bool FP8, int HF, int NT, int U>
+template <bool FP8, int HF, int NT, int U, int WKS>
 void launch_g2(dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  gemm2_decode_kernel<FP8, HF, NT, U><<<g, 256, lds, st>>>(a);
+  gemm2_decode_kernel<FP8, HF, NT, U, WKS><<<g, 256, lds, st>>>(a);
+}
+
+template <bool FP8, int HF, int NT, int U>
+bool g2_wks(int wks, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+  switch (wks) {
+    case 1: launch_g2<FP8, HF, NT, U, 1>(g, lds, st, a); return true;
+    case 2: launch_g2<FP8, HF, NT, U, 2>(g, lds, st, a); return true;
+    case 4: launch_g2<FP8, HF, NT, U, 4>(g, lds, st, a); return true;
+  }
+  return false;
 }
 
 template <bool FP8, int HF, int NT>
-bool g2_u(int u, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+bool g2_u(int u, int wks, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
   if constexpr (FP8) {
-    if (u == 1) { launch_g2<FP8, HF, NT, 1>(g, lds, st, a); return true; }
-    if (u == 2) { launch_g2<FP8, HF, NT, 2>(g, lds, st, a); return true; }
+    if (u == 1) return g2_wks<FP8, HF, NT, 1>(wks, g, lds, st, a);
+    if (u == 2) return g2_wks<FP8, HF, NT, 2>(wks, g, lds, st, a);
   } else {
-    if (u == 2) { launch_g2<FP8, HF, NT, 2>(g, lds, st, a); return true; }
-    if (u == 4) { launch_g2<FP8, HF, NT, 4>(g, lds, st, a); return true; }
+    if (u == 2) return g2_wks<FP8, HF, NT, 2>(wks, g, lds, st, a);
+    if (u == 4) return g2_wks<FP8, HF, NT, 4>(wks, g, lds, st, a);
   }
   return false;
 }
 
 template <bool FP8, int HF>
-bool g2_nt(int nt, int u, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+bool g2_nt(int nt, int u, int wks, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
   switch (nt) {
-    case 1: return g2_u<FP8, HF, 1>(u, g, lds, st, a);
-    case 2: return g2_u<FP8, HF, 2>(u, g, lds, st, a);
-    case 4: return g2_u<FP8, HF, 4>(u, g, lds, st, a);
+    case 1: return g2_u<FP8, HF, 1>(u, wks, g, lds, st, a);
+    case 2: return g2_u<FP8, HF, 2>(u, wks, g, lds, st, a);
+    case 4: return g2_u<FP8, HF, 4>(u, wks, g, lds, st, a);
   }
   return false;
 }
@@ -217,6 +268,19 @@ bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float*
   else
     route_topk_kernel<8><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
   return true;
+}
+
+void launch_prologue_small(const float* logits, int M, int E, int k, int32_t* ids, float* wts, int B,
+                           const AlignOut& o, const SmallQuant& q, hipStream_t st) {
+  const int npl = (int)cdiv(E, 64), lb = log2i(B), ib = log2i(E);
+  if (npl <= 1)
+    prologue_small_kernel<1><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+  else if (npl <= 2)
+    prologue_small_kernel<2><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+  else if (npl <= 4)
+    prologue_small_kernel<4><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+  else
+    prologue_small_kernel<8><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
 }
 
 void launch_align(const int32_t* ids, int64_t P, int E, int B, const AlignOut& o, const QuantXArgs& q, int n_quant_wg,
@@ -247,7 +311,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -344,37 +408,49 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   unsigned* h_amax = (unsigned*)(ws + L.h_amax);
   uint8_t* xq = ws + L.xq;
   uint8_t* h = ws + L.h;
-  float* y_acc = (float*)(ws + L.y_acc);
+  float* part = (float*)(ws + L.part);
   const int64_t P = (int64_t)M * k;
   const int n_act = (int)std::min<int64_t>(E, P);
 
-  // 1. routing (+ per-workgroup amax of x, clearing of the accumulators)
-  rec(0);
-  RouteFusedArgs fa{(const uint16_t*)a->x, H, (fp8 && !a->x_scale) ? xamax_part : nullptr, y_acc,
-                    hdyn ? h_amax : nullptr};
-  launch_route(a->logits, M, E, k, ids, wts, fa, st);
-  rec(1);
-  if ((rc = launch_status()) != MOE_OK) return rc;
-
-  // 2. align (+ activation quantisation in fp8 mode)
-  rec(2);
   AlignOut o{counts, offsets, sorted, (int32_t*)(ws + L.block_expert), (int32_t*)(ws + L.num_padded), active,
              num_active, L.n_blocks};
-  QuantXArgs q{};
-  int n_quant = 0;
-  if (fp8) {
-    q.x = (const uint16_t*)a->x;
-    q.n = (int64_t)M * H;
-    q.amax_part = xamax_part;
-    q.n_part = L.n_route_wg;
-    q.static_scale = a->x_scale;
-    q.xq = xq;
-    q.scale_slot = scale_slot;
-    n_quant = (int)cdiv(q.n, 256 * 16);
+  const bool small = P <= kSmallPairs && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
+  if (small) {
+    // 1+2. routing, align (and fp8 activation quantisation) in one workgroup
+    rec(0);
+    SmallQuant q{(const uint16_t*)a->x, H, a->x_scale, fp8 ? xq : nullptr, scale_slot, hdyn ? h_amax : nullptr};
+    launch_prologue_small(a->logits, M, E, k, ids, wts, kAlignBlockFused, o, q, st);
+    rec(1);
+    rec(2);
+    rec(3);
+    if ((rc = launch_status()) != MOE_OK) return rc;
+  } else {
+    // 1. routing (+ per-workgroup amax of x)
+    rec(0);
+    RouteFusedArgs fa{(const uint16_t*)a->x, H, (fp8 && !a->x_scale) ? xamax_part : nullptr,
+                      hdyn ? h_amax : nullptr};
+    launch_route(a->logits, M, E, k, ids, wts, fa, st);
+    rec(1);
+    if ((rc = launch_status()) != MOE_OK) return rc;
+
+    // 2. align (+ activation quantisation in fp8 mode)
+    rec(2);
+    QuantXArgs q{};
+    int n_quant = 0;
+    if (fp8) {
+      q.x = (const uint16_t*)a->x;
+      q.n = (int64_t)M * H;
+      q.amax_part = xamax_part;
+      q.n_part = L.n_route_wg;
+      q.static_scale = a->x_scale;
+      q.xq = xq;
+      q.scale_slot = scale_slot;
+      n_quant = (int)cdiv(q.n, 256 * 16);
+    }
+    launch_align(ids, P, E, kAlignBlockFused, o, q, n_quant, st);
+    rec(3);
+    if ((rc = launch_status()) != MOE_OK) return rc;
   }
-  launch_align(ids, P, E, kAlignBlockFused, o, q, n_quant, st);
-  rec(3);
-  if ((rc = launch_status()) != MOE_OK) return rc;
 
   const Segments segs{sorted, offsets, counts, active, num_active};
   const int hf = !fp8 ? H_BF16 : (hdyn ? H_F32 : H_E4M3);
@@ -385,42 +461,45 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     Gemm1Args g{(const uint8_t*)a->w13, fp8 ? xq : (const uint8_t*)a->x, segs, H, I, k, a->w13_scale, scale_slot,
                 a->h_scale, h, h_amax};
     const int tpw = 4 / plan.ks1;
-    const dim3 grid((unsigned)(I / 16 / tpw), (unsigned)n_act, (unsigned)plan.passes);
+    const dim3 grid((unsigned)(I / 16 / tpw), (unsigned)n_act, (unsigned)plan.passes1);
     bool ok;
     if (!fp8)
-      ok = g1_nt<false, H_BF16>(plan.nt, plan.u1, plan.ks1, grid, st, g);
+      ok = g1_nt<false, H_BF16>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
     else if (hdyn)
-      ok = g1_nt<true, H_F32>(plan.nt, plan.u1, plan.ks1, grid, st, g);
+      ok = g1_nt<true, H_F32>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
     else
-      ok = g1_nt<true, H_E4M3>(plan.nt, plan.u1, plan.ks1, grid, st, g);
+      ok = g1_nt<true, H_E4M3>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
     if (!ok) return MOE_ERR_UNSUPPORTED;
   }
   rec(5);
   if ((rc = launch_status()) != MOE_OK) return rc;
 
-  // 4. down product + weighted scatter-add
+  // 4. down product (partial sums per K slice)
   rec(6);
   {
-    Gemm2Args g{(const uint8_t*)a->w2, h, segs, wts, H, I, k, plan.ks2, a->w2_scale, a->h_scale, h_amax, y_acc};
-    const dim3 grid((unsigned)(H / 128), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes));
+    Gemm2Args g{(const uint8_t*)a->w2, h, segs, wts, H, I, k, plan.ks2, a->w2_scale, a->h_scale, h_amax, part,
+                (int)P};
+    const dim3 grid((unsigned)(H / (32 * (4 / plan.wks2))), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
     bool ok;
     if (hf == H_BF16)
-      ok = g2_nt<false, H_BF16>(plan.nt, plan.u2, grid, 0, st, g);
+      ok = g2_nt<false, H_BF16>(plan.nt2, plan.u2, plan.wks2, grid, 0, st, g);
     else if (hf == H_F32)
-      ok = g2_nt<true, H_F32>(plan.nt, plan.u2, grid, plan.lds2, st, g);
+      ok = g2_nt<true, H_F32>(plan.nt2, plan.u2, plan.wks2, grid, plan.lds2, st, g);
     else
-      ok = g2_nt<true, H_E4M3>(plan.nt, plan.u2, grid, 0, st, g);
+      ok = g2_nt<true, H_E4M3>(plan.nt2, plan.u2, plan.wks2, grid, 0, st, g);
     if (!ok) return MOE_ERR_UNSUPPORTED;
   }
   rec(7);
   if ((rc = launch_status()) != MOE_OK) return rc;
 
-  // 5. y = bf16(y_acc)
+  // 5. y = bf16(sum_j w_j * sum_s part_s), fixed order
   rec(8);
   {
-    const int64_t n = (int64_t)M * H;
-    finalize_kernel<<<(unsigned)cdiv(n, 2048), 256, 0, st>>>(y_acc, (uint16_t*)a->y, n, scale_slot, h_amax,
-                                                             a->h_scale, fp8 ? a->scales_out : nullptr);
+    const int64_t groups = (int64_t)M * H / 4;
+    const int lkp = log2i(k);
+    finalize_kernel<<<(unsigned)cdiv(groups << lkp, 256), 256, 0, st>>>(part, wts, (uint16_t*)a->y, M, H, k, lkp,
+                                                                        plan.ks2, scale_slot, h_amax, a->h_scale,
+                                                                        fp8 ? a->scales_out : nullptr);
   }
   rec(9);
   return launch_status();

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def capacity_formula(M, k, E, B):
@@ -72,8 +72,8 @@ def test_workspace_size(lib):
     bf = lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 0)
     f8 = lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 1)
     assert bf > 0 and f8 > 0 and bf % 256 == 0
-    # the fp32 accumulator and the h buffer alone
-    assert bf >= 4 * 256 * 4 + 8 * 512 * 2
+    # the fp32 partial outputs of the down product (at least one K slice) and the h buffer alone
+    assert bf >= 8 * 256 * 4 + 8 * 512 * 2
     assert lib.moe_fused_workspace_size(4, 8, 200, 512, 2, 0) == 0  # H not a multiple of 128
     assert lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 7) == 0  # unknown dtype
 
@@ -141,7 +141,8 @@ def test_fused_validation(lib, kw, code):
 
 def test_fused_tuning_validation(lib):
     import moe_layer_align_amd as m
-    for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17)):
+    for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17),
+              m.Tuning(gemm2_wave_ksplit=3)):
         args = fused_args(tuning=ctypes.pointer(t))
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 

@@ -30,8 +30,9 @@ def cfg_of(dtype, E, k, H, I, logits="normal"):
 
 # ---------------------------------------------------------------- small layers, whole output compared
 @pytest.mark.parametrize("dtype,xs,hs", [("bf16", None, None), ("fp8", None, None), ("fp8", 0.02, 0.02)])
-@pytest.mark.parametrize("M", [1, 5, 17, 40, 100])
+@pytest.mark.parametrize("M", [1, 5, 17, 40, 100, 600])
 def test_small_layer(dtype, xs, hs, M):
+    # M*k <= 1024 takes the one-workgroup prologue, M = 600 (1200 pairs) the router + align launches
     cfg = cfg_of(dtype, 6, 2, 512, 384)
     compare(cfg, M, seed=M, x_scale=xs, h_scale=hs)
 
@@ -62,15 +63,16 @@ def test_max_experts_and_topk():
 def test_tuning_variants_agree():
     cfg = cfg_of("bf16", 8, 2, 1024, 512)
     w = gen_weights(cfg, 7, device=DEV)
-    for t in [moe.Tuning(gemm1_ksplit=1, gemm2_ksplit=1, token_tiles=1, unroll=2),
-              moe.Tuning(gemm1_ksplit=2, gemm2_ksplit=4, token_tiles=2, unroll=4),
-              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=16, token_tiles=4, unroll=2)]:
+    for t in [moe.Tuning(gemm1_ksplit=1, gemm2_ksplit=1, token_tiles=1, unroll=2, gemm2_wave_ksplit=4),
+              moe.Tuning(gemm1_ksplit=2, gemm2_ksplit=4, token_tiles=2, unroll=4, gemm2_wave_ksplit=2),
+              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=16, token_tiles=4, unroll=2, gemm2_wave_ksplit=1),
+              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=2, token_tiles=3, unroll=2, gemm2_wave_ksplit=4)]:
         compare(cfg, 33, seed=7, weights=w, tuning=t)
     cfg8 = cfg_of("fp8", 8, 2, 1024, 512)
     w8 = gen_weights(cfg8, 7, device=DEV)
-    for t in [moe.Tuning(gemm1_ksplit=1, gemm2_ksplit=1, token_tiles=1, unroll=1),
-              moe.Tuning(gemm1_ksplit=2, gemm2_ksplit=2, token_tiles=2, unroll=2),
-              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=4, token_tiles=4, unroll=1)]:
+    for t in [moe.Tuning(gemm1_ksplit=1, gemm2_ksplit=1, token_tiles=1, unroll=1, gemm2_wave_ksplit=4),
+              moe.Tuning(gemm1_ksplit=2, gemm2_ksplit=2, token_tiles=2, unroll=2, gemm2_wave_ksplit=2),
+              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=4, token_tiles=4, unroll=1, gemm2_wave_ksplit=1)]:
         compare(cfg8, 33, seed=7, weights=w8, tuning=t)
         compare(cfg8, 33, seed=7, weights=w8, tuning=t, x_scale=0.03, h_scale=0.02)
 
@@ -96,8 +98,8 @@ def test_repeat_calls_reuse_workspace():
           for _ in range(3)]
     assert torch.equal(ys[0].isfinite(), torch.ones_like(ys[0], dtype=torch.bool))
     for y in ys[1:]:
-        err = (y.float() - ys[0].float()).abs().max() / ys[0].float().abs().max()
-        assert err < 1e-3  # fp32 atomics make the last bits order-dependent
+        # the top-k combine sums in a fixed order: repeated calls are bitwise identical
+        assert torch.equal(y, ys[0])
 
 
 # ---------------------------------------------------------------- the workloads
