@@ -9,6 +9,7 @@
 
 #include "moe.h"
 #include "gemm_decode.h"
+#include "gemm_prefill.h"
 #include "moe_device.h"
 #include "route_align.h"
 
@@ -16,7 +17,12 @@ using namespace moe;
 
 namespace {
 
-constexpr int kAlignBlockFused = 16;  // token tile of the MFMA B operand
+constexpr int kAlignBlockFused = 16;   // token tile of the decode products' B operand
+constexpr int kPrefillMinPairs = 8192; // fp8 layers with at least this many pairs take the prefill products
+
+// fp8 layers with many pairs use the tiled prefill products (token block 128).
+bool use_prefill(int64_t P, moe_dtype_t dt) { return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs; }
+int align_block(int64_t P, moe_dtype_t dt) { return use_prefill(P, dt) ? kPfTile : kAlignBlockFused; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -76,8 +82,9 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
     off += round_up(std::max<size_t>(bytes, 4), 256);
     return o;
   };
-  L.capacity = align_capacity(P, E, kAlignBlockFused);
-  L.n_blocks = (int)(L.capacity / kAlignBlockFused);
+  const int B = align_block(P, dt);
+  L.capacity = align_capacity(P, E, B);
+  L.n_blocks = (int)(L.capacity / B);
   L.n_route_wg = (int)cdiv(M, 4);
   L.ids = take(P * 4);
   L.wts = take(P * 4);
@@ -270,6 +277,17 @@ bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float*
   return true;
 }
 
+template <int MODE, bool HDYN>
+void launch_prefill(dim3 grid, hipStream_t st, const PrefillArgs& g) {
+  static bool lds_set = false;  // the dynamic LDS ceiling is raised once per kernel
+  if (!lds_set) {
+    (void)hipFuncSetAttribute((const void*)prefill_gemm_kernel<MODE, HDYN>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds);
+    lds_set = true;
+  }
+  prefill_gemm_kernel<MODE, HDYN><<<grid, 256, kPfLds, st>>>(g);
+}
+
 void launch_prologue_small(const float* logits, int M, int E, int k, int32_t* ids, float* wts, int B,
                            const AlignOut& o, const SmallQuant& q, hipStream_t st) {
   const int npl = (int)cdiv(E, 64), lb = log2i(B), ib = log2i(E);
@@ -363,6 +381,74 @@ size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int3
   return make_layout(M, E, H, I, top_k, dtype).total;
 }
 
+// fp8 prefill: router, align (block 128) with the activation quantisation,
+// the two tiled products and the per-token combine.
+static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev, const Layout& L,
+                                    uint8_t* ws, int32_t* ids, float* wts, const AlignOut& o, float* xamax_part,
+                                    float* scale_slot, unsigned* h_amax, uint8_t* xq, uint8_t* h, float* part,
+                                    bool hdyn) {
+  auto rec = [&](int i) {
+    if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
+  };
+  moe_status_t rc;
+  const int M = a->M, E = a->E, H = a->H, I = a->I, k = a->top_k;
+  const int64_t P = (int64_t)M * k;
+  rec(0);
+  RouteFusedArgs fa{(const uint16_t*)a->x, H, a->x_scale ? nullptr : xamax_part, hdyn ? h_amax : nullptr};
+  launch_route(a->logits, M, E, k, ids, wts, fa, st);
+  rec(1);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+  rec(2);
+  QuantXArgs q{};
+  q.x = (const uint16_t*)a->x;
+  q.n = (int64_t)M * H;
+  q.amax_part = xamax_part;
+  q.n_part = L.n_route_wg;
+  q.static_scale = a->x_scale;
+  q.xq = xq;
+  q.scale_slot = scale_slot;
+  launch_align(ids, P, E, kPfTile, o, q, (int)cdiv(q.n, 256 * 16), st);
+  rec(3);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+
+  const PrefillSeg seg{o.sorted_ids, o.block_expert, o.offsets, o.counts, o.num_padded};
+  uint8_t* hq = hdyn ? h + (size_t)P * I * 2 : h;  // e4m3 h read by the down product
+  rec(4);
+  {
+    PrefillArgs g{(const uint8_t*)a->w13, xq, seg, wts, H, I, k, (int)P, a->w13_scale, scale_slot, nullptr,
+                  a->h_scale, h, h_amax};
+    const dim3 grid((unsigned)(I / 64), (unsigned)L.n_blocks);
+    if (hdyn)
+      launch_prefill<0, true>(grid, st, g);
+    else
+      launch_prefill<0, false>(grid, st, g);
+  }
+  rec(5);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+  rec(6);
+  {
+    if (hdyn) {
+      const int64_t n = P * I;
+      prefill_quant_h_kernel<<<(unsigned)cdiv(n, 4096), 256, 0, st>>>((const uint16_t*)h, n, h_amax, hq);
+      if ((rc = launch_status()) != MOE_OK) return rc;
+    }
+    PrefillArgs g{(const uint8_t*)a->w2, hq, seg, wts, H, I, k, (int)P, a->w2_scale, a->h_scale, h_amax, nullptr,
+                  (uint8_t*)part, nullptr};
+    const dim3 grid((unsigned)(H / kPfTile), (unsigned)L.n_blocks);
+    if (hdyn)
+      launch_prefill<1, true>(grid, st, g);
+    else
+      launch_prefill<1, false>(grid, st, g);
+  }
+  rec(7);
+  if ((rc = launch_status()) != MOE_OK) return rc;
+  rec(8);
+  prefill_finalize_kernel<<<(unsigned)cdiv((int64_t)M * H, 2048), 256, 0, st>>>(
+      (const uint16_t*)part, (uint16_t*)a->y, M, H, k, scale_slot, h_amax, a->h_scale, a->scales_out);
+  rec(9);
+  return launch_status();
+}
+
 static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev) {
   if (!a) return MOE_ERR_INVALID_ARG;
   auto rec = [&](int i) {
@@ -391,9 +477,12 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const Layout L = make_layout(M, E, H, I, k, a->dtype);
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const bool hdyn = fp8 && !a->h_scale;
-  Plan plan;
-  rc = make_plan(M, E, H, I, k, fp8, hdyn, a->tuning, &plan);
-  if (rc != MOE_OK) return rc;
+  const bool prefill = use_prefill((int64_t)M * k, a->dtype);
+  Plan plan{};
+  if (!prefill) {
+    rc = make_plan(M, E, H, I, k, fp8, hdyn, a->tuning, &plan);
+    if (rc != MOE_OK) return rc;
+  }
 
   uint8_t* ws = (uint8_t*)a->workspace;
   int32_t* ids = a->topk_ids ? a->topk_ids : (int32_t*)(ws + L.ids);
@@ -414,6 +503,8 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
 
   AlignOut o{counts, offsets, sorted, (int32_t*)(ws + L.block_expert), (int32_t*)(ws + L.num_padded), active,
              num_active, L.n_blocks};
+  if (prefill)
+    return prefill_forward(a, st, ev, L, ws, ids, wts, o, xamax_part, scale_slot, h_amax, xq, h, part, hdyn);
   const bool small = P <= kSmallPairs && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
   if (small) {
     // 1+2. routing, align (and fp8 activation quantisation) in one workgroup

@@ -156,6 +156,18 @@ def prefill_w():
     torch.cuda.empty_cache()
 
 
+# Tiled prefill products (fp8 with at least 8192 pairs) at sizes the oracle
+# evaluates quickly: Zipf routing leaves experts empty and blocks partial.
+def test_prefill_path_dynamic_scales_all_tokens():
+    cfg = MoEConfig("pf_small", E=16, k=8, H=256, I=128, dtype="fp8", ms=(1100,), logits="zipf")
+    compare(cfg, 1100, seed=11)
+
+
+def test_prefill_path_static_scales_long_k():
+    cfg = MoEConfig("pf_long", E=16, k=8, H=1024, I=512, dtype="fp8", ms=(1100,), logits="zipf")
+    compare(cfg, 1100, seed=12, tokens=[0, 1, 2, 500, 777, 1098, 1099], x_scale=0.012, h_scale=0.01)
+
+
 def test_prefill_full_static_scales(prefill_w):
     M = 4096
     toks = [0, 1, 777, 2048, 3000, 4095]
