@@ -2,22 +2,21 @@
 //
 // At prefill every active expert holds hundreds to thousands of tokens, so the
 // products are compute-bound and both operands are reused: a workgroup
-// computes a 128 x 128 tile (128 weight rows x 128 tokens of one expert) and
+// computes a 256 x 128 tile (256 weight rows x 128 tokens of one expert) and
 // stages both operands through LDS, K-step by K-step.  The token dimension is
 // grouped by the align step with a block of 128: block b holds tokens of
 // expert block_expert[b] only, padded with the sentinel, so a workgroup's
 // tokens share one expert.  Weight rows stay the MFMA's A operand and tokens
 // the B operand, as in the decode kernels; the 32x32x64 fp8 MFMA is used,
-// each wave owning a 64 x 64 sub-tile (2 x 2 MFMA tiles).
+// each of the eight waves owning a 64 x 64 sub-tile (2 x 2 MFMA tiles).
 //
-// Grid: x = weight-row tile, y = token block.  Workgroups are dispatched to
-// the eight XCDs round robin by linear id; with gridDim.x a multiple of 8 the
-// same weight tile always lands on the same XCD, so its reuse across token
+// Grid: one dimension, mapped to (weight tile, token block) so that each
+// weight tile stays on one XCD (pf_map), where its reuse across the token
 // blocks of one expert hits that XCD's L2.
 //
-// Pipeline: both operand tiles of each 64-byte K-step are loaded from global
-// memory straight into a four-deep LDS ring (direct-to-LDS loads, no staging
-// registers), three steps ahead of the MFMAs, with one barrier per step.
+// Pipeline: both operand tiles of each 128-byte K-step are loaded from global
+// memory straight into a three-deep LDS ring (direct-to-LDS loads, no staging
+// registers), two steps ahead of the MFMAs, with one barrier per step.
 #pragma once
 
 #include <type_traits>
@@ -55,11 +54,15 @@ __device__ __forceinline__ void wait_vm() {
 // wait for every vector-memory operation, draining the prefetch queue.)
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-constexpr int kPfTile = 128;                        // weight rows and tokens per workgroup
-constexpr int kPfBK = 64;                           // K bytes per step (fp8): one MFMA k-step
-constexpr int kPfStages = 4;                        // LDS ring depth
-constexpr int kPfHalf = kPfTile * kPfBK;            // bytes of one operand tile per stage (8 KB)
-constexpr int kPfLds = kPfStages * 2 * kPfHalf;     // 64 KB: two workgroups per CU
+constexpr int kPfTok = 128;                          // tokens per workgroup (the align block)
+constexpr int kPfRows = 256;                         // weight rows per workgroup
+constexpr int kPfBK = 128;                           // K bytes per step (fp8): two MFMA k-steps
+constexpr int kPfStages = 3;                         // LDS ring depth
+constexpr int kPfStageA = kPfRows * kPfBK;           // 32 KB
+constexpr int kPfStageB = kPfTok * kPfBK;            // 16 KB
+constexpr int kPfStage = kPfStageA + kPfStageB;      // 48 KB
+constexpr int kPfLds = kPfStages * kPfStage;         // 144 KB: one workgroup of 8 waves per CU
+constexpr int kPfThreads = 512;
 
 struct PrefillSeg {
   const int32_t* sorted_ids;    // [capacity] pair ids grouped by expert, block 128
@@ -69,10 +72,29 @@ struct PrefillSeg {
   const int32_t* num_padded;    // [1]
 };
 
-// LDS layout of one operand tile in one stage: 128 rows x 64 bytes, the four
-// 16-byte chunks of row r stored at chunk position c ^ ((r >> 1) & 3), so the
-// MFMA fragment reads (32 rows, same chunk) spread over all banks.
-__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// LDS layout of an operand tile in one stage: rows of 128 bytes, the eight
+// 16-byte chunks of row r stored at chunk position c ^ (r & 7), so the MFMA
+// fragment reads (32 rows, same chunk) spread over all banks.
+__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ (row & 7)) << 4); }
+
+// Workgroup -> (weight tile, token block), XCD-aware.  Workgroups are handed
+// to the eight XCDs round robin by linear id; XCD c owns weight tiles c, c+8,
+// ... for every block, and the T % 8 tiles left over are shared out as
+// contiguous (tile, block) ranges, so each weight tile is read by as few XCDs
+// (L2s) as possible.  nblk must be a multiple of 8.
+__device__ __forceinline__ void pf_map(int L, int T, int nblk, int* tile, int* blk) {
+  const int c = L & 7, j = L >> 3;
+  const int full = T >> 3, rem = T & 7;
+  if (j < full * nblk) {
+    *blk = j / full;
+    *tile = c + 8 * (j - *blk * full);
+  } else {
+    const int per = rem * nblk / 8;
+    const int p = c * per + (j - full * nblk);
+    *tile = 8 * full + p / nblk;
+    *blk = p - (p / nblk) * nblk;
+  }
+}
 
 // ---------------------------------------------------------------- products
 struct PrefillArgs {
@@ -81,6 +103,7 @@ struct PrefillArgs {
   PrefillSeg seg;
   const float* topk_w;     // [P] (down)
   int H, I, top_k, P;
+  int tiles, nblk;         // weight tiles (2I/256 or H/256) and token blocks (rounded up to 8)
   const float* w_scale;    // s_w13 or s_w2
   const float* a_scale;    // gate/up: s_x in effect; down: static s_h (null = dynamic)
   const unsigned* h_amax;  // down with dynamic scale: max |h| (float bits)
@@ -89,79 +112,97 @@ struct PrefillArgs {
   unsigned* h_amax_out;    // gate/up with dynamic scale
 };
 
-// MODE 0: gate/up product, tile rows = 64 gate + 64 up rows of the same 64
+// MODE 0: gate/up product, tile rows = 128 gate + 128 up rows of the same 128
 //   features, epilogue SiLU(g)*u -> h.  HDYN: h stored as bf16 with a running
 //   amax (quantised by prefill_quant_h_kernel), else as e4m3 with the static
 //   scale.
-// MODE 1: down product, tile rows = 128 output features, epilogue
+// MODE 1: down product, tile rows = 256 output features, epilogue
 //   w[pair] * s_h * s_w2 * acc -> bf16 part[pair][feature].
 //
-// Each K-step of 64 bytes: every wave DMA-loads 32 rows of the A tile and 32
-// rows of the B tile (two 1 KB load instructions each, lane i filling bytes
-// 16i..16i+15 of a 16-row block) straight into the LDS ring, three steps
-// ahead; one barrier per step.
+// Eight waves: wave (wr = 0..3, wc = 0..1) owns 64 weight rows x 64 tokens
+// (2 x 2 MFMA tiles; in MODE 0 the 32 gate and the 32 up rows of the same 32
+// features).  Each 128-byte K-step: every wave DMA-loads 32 rows of the A
+// tile and 16 rows of the B tile (six 1 KB load instructions, lane i filling
+// bytes 16i..16i+15 of an 8-row block) into a three-deep LDS ring two steps
+// ahead; one barrier per step; 8 MFMAs per wave per step.
 template <int MODE, bool HDYN>
-__global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  const int blk = blockIdx.y;
+  int tile, blk;
+  pf_map(blockIdx.x, a.tiles, a.nblk, &tile, &blk);
   const int npad = *a.seg.num_padded;
-  if (blk * kPfTile >= npad) return;
+  if (blk * kPfTok >= npad) return;
   const int e = a.seg.block_expert[blk];
   if (e < 0) return;
   const int seg_end = a.seg.offsets[e] + a.seg.counts[e];  // first padding slot of the expert
-  const int tok0 = blk * kPfTile;
-  const int ntok = min(kPfTile, seg_end - tok0);           // valid tokens of the block (>= 1)
+  const int tok0 = blk * kPfTok;
+  const int ntok = min(kPfTok, seg_end - tok0);            // valid tokens of the block (>= 1)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the wave's branches scalar
-  const int K = MODE == 0 ? a.H : a.I;                      // contraction length (bytes)
-  const int64_t wrows = MODE == 0 ? 2 * a.I : a.H;          // rows of one expert's weight
+  const int K = MODE == 0 ? a.H : a.I;                        // contraction length (bytes)
+  const int64_t wrows = MODE == 0 ? 2 * a.I : a.H;            // rows of one expert's weight
 
-  // DMA sources of this lane: rows 32*wave + 16*q + lane/4 (q = 0, 1) of the A
-  // and B tiles, logical chunk (lane%4) ^ ((row >> 1) & 3) of each K-step
-  const uint8_t* srcA[2];
+  // DMA sources of this lane: A rows 32*wave + 8*q + lane/8 (q < 4), B rows
+  // 16*wave + 8*q + lane/8 (q < 2), logical chunk (lane%8) ^ (row & 7)
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  const uint8_t* srcA[4];
   const uint8_t* srcB[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 32 * wave + 16 * q + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+  for (int q = 0; q < 4; ++q) {
+    const int row = 32 * wave + 8 * q + lrow;
     int64_t wrow;
     if (MODE == 0) {
-      const int f0 = blockIdx.x * 64;
-      wrow = row < 64 ? f0 + row : a.I + f0 + (row - 64);
+      const int f0 = tile * 128;
+      wrow = row < 128 ? f0 + row : a.I + f0 + (row - 128);
     } else {
-      wrow = (int64_t)blockIdx.x * kPfTile + row;
+      wrow = (int64_t)tile * kPfRows + row;
     }
-    srcA[q] = a.w + ((int64_t)e * wrows + wrow) * K + chunk * 16;
+    srcA[q] = a.w + ((int64_t)e * wrows + wrow) * K + ((lchunk ^ (row & 7)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * wave + 8 * q + lrow;
     // padding slots read the first token of the block (their results are dropped)
     const int f = a.seg.sorted_ids[tok0 + (row < ntok ? row : 0)];
     const int64_t brow = MODE == 0 ? f / a.top_k : f;
-    srcB[q] = a.act + brow * K + chunk * 16;
+    srcB[q] = a.act + brow * K + ((lchunk ^ (row & 7)) << 4);
   }
   auto issue = [&](int s) {  // DMA of K-step s into ring slot s % kPfStages
-    lds_u8* base = smem + (s % kPfStages) * 2 * kPfHalf;
+    lds_u8* base = smem + (s % kPfStages) * kPfStage;
     const int kb = s * kPfBK;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r0 = 32 * wave + 16 * q;
-      __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + kb), (void __attribute__((address_space(3)))*)(base + r0 * kPfBK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + kb), (void __attribute__((address_space(3)))*)(base + kPfHalf + r0 * kPfBK), 16, 0, 0);
-    }
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + kb),
+                                       (void __attribute__((address_space(3)))*)(base + (32 * wave + 8 * q) * kPfBK),
+                                       16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcB[q] + kb),
+          (void __attribute__((address_space(3)))*)(base + kPfStageA + (16 * wave + 8 * q) * kPfBK), 16, 0, 0);
   };
 
   // wave sub-tile: two 32-row A tiles and 64 tokens
-  const int wr = wave & 1, wc = wave >> 1;
-  const int arow0 = MODE == 0 ? 32 * wr : 64 * wr;       // gate rows (MODE 0)
-  const int arow1 = MODE == 0 ? 64 + 32 * wr : 64 * wr + 32;  // up rows of the same features (MODE 0)
+  const int wr = wave & 3, wc = wave >> 2;
+  const int arow0 = MODE == 0 ? 32 * wr : 64 * wr;             // gate rows (MODE 0)
+  const int arow1 = MODE == 0 ? 128 + 32 * wr : 64 * wr + 32;  // up rows of the same features (MODE 0)
   const int brow0 = 64 * wc;
   const bool live0 = brow0 < ntok, live1 = brow0 + 32 < ntok;  // 32-token sub-tiles that hold tokens
-  // fragment addresses within a stage: row l%32 of each tile, chunks 2*(l/32) and +1
+  // fragment addresses within a stage: row l%32 of each tile, k-step ks uses
+  // chunks 4*ks + 2*(l/32) and +1
   const int fr = lane & 31, fc = (lane >> 5) * 2;
-  const int offA0[2] = {pf_swz(arow0 + fr, fc), pf_swz(arow0 + fr, fc + 1)};
-  const int offA1[2] = {pf_swz(arow1 + fr, fc), pf_swz(arow1 + fr, fc + 1)};
-  const int offB0[2] = {kPfHalf + pf_swz(brow0 + fr, fc), kPfHalf + pf_swz(brow0 + fr, fc + 1)};
-  const int offB1[2] = {kPfHalf + pf_swz(brow0 + 32 + fr, fc), kPfHalf + pf_swz(brow0 + 32 + fr, fc + 1)};
+  int offA0[2][2], offA1[2][2], offB0[2][2], offB1[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      offA0[ks][c] = pf_swz(arow0 + fr, 4 * ks + fc + c);
+      offA1[ks][c] = pf_swz(arow1 + fr, 4 * ks + fc + c);
+      offB0[ks][c] = kPfStageA + pf_swz(brow0 + fr, 4 * ks + fc + c);
+      offB1[ks][c] = kPfStageA + pf_swz(brow0 + 32 + fr, 4 * ks + fc + c);
+    }
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -178,33 +219,34 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
     constexpr int NJ = decltype(nj_tag)::value;
     issue(0);
     if (nk > 1) issue(1);
-    if (nk > 2) issue(2);
     for (int s = 0; s < nk; ++s) {
-      // this wave's DMA of step s is complete once at most the younger steps' loads (4 per step) are in flight
-      const int younger = min(2, nk - 1 - s);
-      if (younger == 2)
-        wait_vm<8>();
-      else if (younger == 1)
-        wait_vm<4>();
+      // this wave's DMA of step s is complete once at most the next step's six loads are in flight
+      if (s + 1 < nk)
+        wait_vm<6>();
       else
         wait_vm<0>();
-      ring_barrier();  // every wave's step-s data is in LDS; slot (s+3)%4 is no longer read
-      if (s + 3 < nk) issue(s + 3);
+      ring_barrier();  // every wave's step-s data is in LDS; slot (s+2)%3 is no longer read
+      if (s + 2 < nk) issue(s + 2);
       if constexpr (NJ > 0) {
-        const lds_u8* st = smem + (s % kPfStages) * 2 * kPfHalf;
-        u32x4 a0[2], a1[2], b0[2], b1[2];
+        const lds_u8* st = smem + (s % kPfStages) * kPfStage;
+        u32x4 a0[2][2], a1[2][2], b0[2][2], b1[2][2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          a0[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA0[c]);
-          a1[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA1[c]);
-          b0[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB0[c]);
-          if constexpr (NJ > 1) b1[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB1[c]);
-        }
-        acc[0][0] = mfma32_fp8(a0[0], a0[1], b0[0], b0[1], acc[0][0]);
-        acc[1][0] = mfma32_fp8(a1[0], a1[1], b0[0], b0[1], acc[1][0]);
-        if constexpr (NJ > 1) {
-          acc[0][1] = mfma32_fp8(a0[0], a0[1], b1[0], b1[1], acc[0][1]);
-          acc[1][1] = mfma32_fp8(a1[0], a1[1], b1[0], b1[1], acc[1][1]);
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            a0[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA0[ks][c]);
+            a1[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA1[ks][c]);
+            b0[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB0[ks][c]);
+            if constexpr (NJ > 1) b1[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB1[ks][c]);
+          }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          acc[0][0] = mfma32_fp8(a0[ks][0], a0[ks][1], b0[ks][0], b0[ks][1], acc[0][0]);
+          acc[1][0] = mfma32_fp8(a1[ks][0], a1[ks][1], b0[ks][0], b0[ks][1], acc[1][0]);
+          if constexpr (NJ > 1) {
+            acc[0][1] = mfma32_fp8(a0[ks][0], a0[ks][1], b1[ks][0], b1[ks][1], acc[0][1]);
+            acc[1][1] = mfma32_fp8(a1[ks][0], a1[ks][1], b1[ks][0], b1[ks][1], acc[1][1]);
+          }
         }
       }
     }
@@ -227,7 +269,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       const int t = brow0 + 32 * j + col;
       if (t < ntok) {
         const int f = a.seg.sorted_ids[tok0 + t];
-        const int fbase = blockIdx.x * 64 + 32 * wr;
+        const int fbase = tile * 128 + 32 * wr;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float hv[4];
@@ -261,7 +303,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
       if (t < ntok) {
         const int f = a.seg.sorted_ids[tok0 + t];
         const float w = a.topk_w[f] * deq;
-        uint16_t* dst = (uint16_t*)a.out + (int64_t)f * a.H + (int64_t)blockIdx.x * kPfTile + 64 * wr;
+        uint16_t* dst = (uint16_t*)a.out + (int64_t)f * a.H + (int64_t)tile * kPfRows + 64 * wr;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll

@@ -20,9 +20,12 @@ namespace {
 constexpr int kAlignBlockFused = 16;   // token tile of the decode products' B operand
 constexpr int kPrefillMinPairs = 8192; // fp8 layers with at least this many pairs take the prefill products
 
-// fp8 layers with many pairs use the tiled prefill products (token block 128).
-bool use_prefill(int64_t P, moe_dtype_t dt) { return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs; }
-int align_block(int64_t P, moe_dtype_t dt) { return use_prefill(P, dt) ? kPfTile : kAlignBlockFused; }
+// fp8 layers with many pairs use the tiled prefill products (token block 128,
+// weight tiles of 256 rows: H a multiple of 256).
+bool use_prefill(int64_t P, moe_dtype_t dt, int H) {
+  return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0;
+}
+int align_block(int64_t P, moe_dtype_t dt, int H) { return use_prefill(P, dt, H) ? kPfTok : kAlignBlockFused; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -82,7 +85,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
     off += round_up(std::max<size_t>(bytes, 4), 256);
     return o;
   };
-  const int B = align_block(P, dt);
+  const int B = align_block(P, dt, H);
   L.capacity = align_capacity(P, E, B);
   L.n_blocks = (int)(L.capacity / B);
   L.n_route_wg = (int)cdiv(M, 4);
@@ -278,14 +281,14 @@ bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float*
 }
 
 template <int MODE, bool HDYN>
-void launch_prefill(dim3 grid, hipStream_t st, const PrefillArgs& g) {
+void launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
   static bool lds_set = false;  // the dynamic LDS ceiling is raised once per kernel
   if (!lds_set) {
     (void)hipFuncSetAttribute((const void*)prefill_gemm_kernel<MODE, HDYN>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds);
     lds_set = true;
   }
-  prefill_gemm_kernel<MODE, HDYN><<<grid, 256, kPfLds, st>>>(g);
+  prefill_gemm_kernel<MODE, HDYN><<<wgs, kPfThreads, kPfLds, st>>>(g);
 }
 
 void launch_prologue_small(const float* logits, int M, int E, int k, int32_t* ids, float* wts, int B,
@@ -407,21 +410,22 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   q.static_scale = a->x_scale;
   q.xq = xq;
   q.scale_slot = scale_slot;
-  launch_align(ids, P, E, kPfTile, o, q, (int)cdiv(q.n, 256 * 16), st);
+  launch_align(ids, P, E, kPfTok, o, q, (int)cdiv(q.n, 256 * 16), st);
   rec(3);
   if ((rc = launch_status()) != MOE_OK) return rc;
 
   const PrefillSeg seg{o.sorted_ids, o.block_expert, o.offsets, o.counts, o.num_padded};
   uint8_t* hq = hdyn ? h + (size_t)P * I * 2 : h;  // e4m3 h read by the down product
+  const int nblk = (int)round_up((size_t)L.n_blocks, 8);
   rec(4);
   {
-    PrefillArgs g{(const uint8_t*)a->w13, xq, seg, wts, H, I, k, (int)P, a->w13_scale, scale_slot, nullptr,
-                  a->h_scale, h, h_amax};
-    const dim3 grid((unsigned)(I / 64), (unsigned)L.n_blocks);
+    const int T = I / 128;  // 256-row tiles of W13: 128 gate + 128 up rows
+    PrefillArgs g{(const uint8_t*)a->w13, xq, seg, wts, H, I, k, (int)P, T, nblk, a->w13_scale, scale_slot,
+                  nullptr, a->h_scale, h, h_amax};
     if (hdyn)
-      launch_prefill<0, true>(grid, st, g);
+      launch_prefill<0, true>(T * nblk, st, g);
     else
-      launch_prefill<0, false>(grid, st, g);
+      launch_prefill<0, false>(T * nblk, st, g);
   }
   rec(5);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -432,13 +436,13 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
       prefill_quant_h_kernel<<<(unsigned)cdiv(n, 4096), 256, 0, st>>>((const uint16_t*)h, n, h_amax, hq);
       if ((rc = launch_status()) != MOE_OK) return rc;
     }
-    PrefillArgs g{(const uint8_t*)a->w2, hq, seg, wts, H, I, k, (int)P, a->w2_scale, a->h_scale, h_amax, nullptr,
-                  (uint8_t*)part, nullptr};
-    const dim3 grid((unsigned)(H / kPfTile), (unsigned)L.n_blocks);
+    const int T = H / kPfRows;
+    PrefillArgs g{(const uint8_t*)a->w2, hq, seg, wts, H, I, k, (int)P, T, nblk, a->w2_scale, a->h_scale, h_amax,
+                  nullptr, (uint8_t*)part, nullptr};
     if (hdyn)
-      launch_prefill<1, true>(grid, st, g);
+      launch_prefill<1, true>(T * nblk, st, g);
     else
-      launch_prefill<1, false>(grid, st, g);
+      launch_prefill<1, false>(T * nblk, st, g);
   }
   rec(7);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -477,7 +481,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const Layout L = make_layout(M, E, H, I, k, a->dtype);
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const bool hdyn = fp8 && !a->h_scale;
-  const bool prefill = use_prefill((int64_t)M * k, a->dtype);
+  const bool prefill = use_prefill((int64_t)M * k, a->dtype, a->H);
   Plan plan{};
   if (!prefill) {
     rc = make_plan(M, E, H, I, k, fp8, hdyn, a->tuning, &plan);
