@@ -10,9 +10,10 @@
 // the B operand, as in the decode kernels; the 32x32x64 fp8 MFMA is used,
 // each of the eight waves owning a 64 x 64 sub-tile (2 x 2 MFMA tiles).
 //
-// Grid: one dimension, mapped to (weight tile, token block) so that each
-// weight tile stays on one XCD (pf_map), where its reuse across the token
-// blocks of one expert hits that XCD's L2.
+// Work items (weight tile, token block) are numbered so that each XCD works
+// on its own range of token blocks, rasterised so that concurrent workgroups
+// share operands in that XCD's L2 (pf_map); one persistent workgroup per CU
+// walks them.
 //
 // Pipeline: both operand tiles of each 128-byte K-step are loaded from global
 // memory straight into a three-deep LDS ring (direct-to-LDS loads, no staging
@@ -63,6 +64,9 @@ constexpr int kPfStageB = kPfTok * kPfBK;            // 16 KB
 constexpr int kPfStage = kPfStageA + kPfStageB;      // 48 KB
 constexpr int kPfLds = kPfStages * kPfStage;         // 144 KB: one workgroup of 8 waves per CU
 constexpr int kPfThreads = 512;
+// third descriptor word of a raw byte buffer resource on CDNA (32-bit data
+// format, no swizzle, no index stride)
+constexpr int kBufferWord3 = 0x00020000;
 
 struct PrefillSeg {
   const int32_t* sorted_ids;    // [capacity] pair ids grouped by expert, block 128
@@ -78,22 +82,28 @@ struct PrefillSeg {
 __device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ (row & 7)) << 4); }
 
 // Workgroup -> (weight tile, token block), XCD-aware.  Workgroups are handed
-// to the eight XCDs round robin by linear id; XCD c owns weight tiles c, c+8,
-// ... for every block, and the T % 8 tiles left over are shared out as
-// contiguous (tile, block) ranges, so each weight tile is read by as few XCDs
-// (L2s) as possible.  nblk must be a multiple of 8.
-__device__ __forceinline__ void pf_map(int L, int T, int nblk, int* tile, int* blk) {
+// to the eight XCDs round robin by linear id.  XCD c takes a contiguous eighth
+// of the token blocks that hold tokens (blocks are ordered by expert, so an
+// XCD's range covers a few experts; only experts cut by a range boundary have
+// their weights read by two XCDs) and all weight tiles for them.  Inside an
+// XCD the work is rasterised in groups of kPfGT tiles x kPfGB blocks, about
+// one workgroup per CU, so the workgroups running together share weight
+// tiles and token blocks in that XCD's L2.  Returns false for surplus
+// workgroups (the grid is sized for the largest possible block count).
+constexpr int kPfGT = 4;  // weight tiles per raster group
+constexpr int kPfGB = 8;  // token blocks per raster group
+
+__device__ __forceinline__ bool pf_map(int L, int T, int nb, int* tile, int* blk) {
   const int c = L & 7, j = L >> 3;
-  const int full = T >> 3, rem = T & 7;
-  if (j < full * nblk) {
-    *blk = j / full;
-    *tile = c + 8 * (j - *blk * full);
-  } else {
-    const int per = rem * nblk / 8;
-    const int p = c * per + (j - full * nblk);
-    *tile = 8 * full + p / nblk;
-    *blk = p - (p / nblk) * nblk;
-  }
+  const int nbx = (nb + 7) >> 3;                     // blocks per XCD
+  const int ntg = (T + kPfGT - 1) / kPfGT;           // tile groups
+  const int g = j / (kPfGT * kPfGB), r = j - g * (kPfGT * kPfGB);
+  const int bg = g / ntg, tg = g - bg * ntg;
+  const int t = tg * kPfGT + r / kPfGB, b = bg * kPfGB + (r % kPfGB);
+  if (t >= T || b >= nbx) return false;
+  *tile = t;
+  *blk = c * nbx + b;
+  return *blk < nb;
 }
 
 // ---------------------------------------------------------------- products
@@ -101,9 +111,9 @@ struct PrefillArgs {
   const uint8_t* w;        // W13 [E][2I][H] or W2 [E][H][I], e4m3
   const uint8_t* act;      // gate/up: xq [M][H]; down: hq [P][I], e4m3
   PrefillSeg seg;
-  const float* topk_w;     // [P] (down)
   int H, I, top_k, P;
-  int tiles, nblk;         // weight tiles (2I/256 or H/256) and token blocks (rounded up to 8)
+  int tiles;               // weight tiles: 2I/256 or H/256
+  int items;               // linear work items covered by pf_map (>= tiles x blocks)
   const float* w_scale;    // s_w13 or s_w2
   const float* a_scale;    // gate/up: s_x in effect; down: static s_h (null = dynamic)
   const unsigned* h_amax;  // down with dynamic scale: max |h| (float bits)
@@ -112,84 +122,169 @@ struct PrefillArgs {
   unsigned* h_amax_out;    // gate/up with dynamic scale
 };
 
+// DMA sources of one work item for one lane (see prefill_gemm_kernel).  At
+// namespace scope: with the struct local to the kernel, the host compilation
+// pass silently drops the kernel's launch stub.
+struct PfSrc {
+  const uint8_t* wa;  // the expert's weight matrix (a buffer resource is made from it at issue)
+  int offA[4], offB[2];
+  int fb[2];  // pair ids of this lane's B rows, until finish_src turns them into offB
+  int f[2];   // pair ids of this lane's epilogue tokens brow0 + 32*j + lane%32 (clamped)
+};
+
+// One work item: weight tile x token block of one expert.
+struct PfItem {
+  int tile, blk, e;
+  int ntok;  // tokens of the block that belong to the expert (1..128)
+};
+
+// The next work item at or after linear index L (stepping by `stride`), or
+// false when none is left.  Uniform across the workgroup; the skip over
+// surplus indices is arithmetic only, so the loads are issued once and
+// waited for where their values are first used.
+__device__ __forceinline__ bool pf_next(const PrefillArgs& a, int nb, int& L, int stride, PfItem& it) {
+  int tile = 0, blk = 0;
+  for (; L < a.items; L += stride)
+    if (pf_map(L, a.tiles, nb, &tile, &blk)) break;
+  if (L >= a.items) return false;
+  const int e = a.seg.block_expert[blk];  // every block below num_padded belongs to an expert
+  it.tile = tile;
+  it.blk = blk;
+  it.e = e;
+  it.ntok = min(kPfTok, a.seg.offsets[e] + a.seg.counts[e] - blk * kPfTok);
+  return true;
+}
+
 // MODE 0: gate/up product, tile rows = 128 gate + 128 up rows of the same 128
 //   features, epilogue SiLU(g)*u -> h.  HDYN: h stored as bf16 with a running
 //   amax (quantised by prefill_quant_h_kernel), else as e4m3 with the static
 //   scale.
 // MODE 1: down product, tile rows = 256 output features, epilogue
-//   w[pair] * s_h * s_w2 * acc -> bf16 part[pair][feature].
+//   s_h * s_w2 * acc -> bf16 part[pair][feature] (the routing weight is
+//   applied when the pairs of a token are summed).
+//
+// Persistent: one workgroup per CU walks the work items L = blockIdx.x,
+// blockIdx.x + gridDim.x, ... (gridDim.x a multiple of 8 keeps every
+// workgroup on the XCD that pf_map assigns its items to).  The LDS ring runs
+// on across items: the last two K-steps of an item load the first two of the
+// next, whose metadata was fetched one item earlier, so an item's epilogue
+// overlaps the next item's first loads and no workgroup start or metadata
+// latency sits between items.
 //
 // Eight waves: wave (wr = 0..3, wc = 0..1) owns 64 weight rows x 64 tokens
 // (2 x 2 MFMA tiles; in MODE 0 the 32 gate and the 32 up rows of the same 32
 // features).  Each 128-byte K-step: every wave DMA-loads 32 rows of the A
 // tile and 16 rows of the B tile (six 1 KB load instructions, lane i filling
 // bytes 16i..16i+15 of an 8-row block) into a three-deep LDS ring two steps
-// ahead; one barrier per step; 8 MFMAs per wave per step.
+// ahead; one barrier per step; 8 MFMAs per wave per step, issued in the same
+// window as the LDS reads of the next step.
+//
+// Wait accounting: the waits count vector-memory operations, which complete
+// in issue order.  Before the barrier of step s a wave waits until at most
+// six are outstanding, the six loads of step s+1 issued after step s's: any
+// other vector-memory operation (token ids, epilogue stores) only makes that
+// wait stricter.  When no load follows step s (the last step of the last
+// item) the wait is for zero.
 template <int MODE, bool HDYN>
 __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  int tile, blk;
-  pf_map(blockIdx.x, a.tiles, a.nblk, &tile, &blk);
-  const int npad = *a.seg.num_padded;
-  if (blk * kPfTok >= npad) return;
-  const int e = a.seg.block_expert[blk];
-  if (e < 0) return;
-  const int seg_end = a.seg.offsets[e] + a.seg.counts[e];  // first padding slot of the expert
-  const int tok0 = blk * kPfTok;
-  const int ntok = min(kPfTok, seg_end - tok0);            // valid tokens of the block (>= 1)
+  const int nb = *a.seg.num_padded / kPfTok;
+  const int stride = gridDim.x;
+  int L = blockIdx.x;
+  PfItem cur;
+  if (!pf_next(a, nb, L, stride, cur)) return;
+  PfItem nxt = cur;  // stays a valid item when there is no next one (its loads are then unused)
+  L += stride;
+  bool has_next = pf_next(a, nb, L, stride, nxt);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the wave's branches scalar
   const int K = MODE == 0 ? a.H : a.I;                        // contraction length (bytes)
-  const int64_t wrows = MODE == 0 ? 2 * a.I : a.H;            // rows of one expert's weight
-
-  // DMA sources of this lane: A rows 32*wave + 8*q + lane/8 (q < 4), B rows
-  // 16*wave + 8*q + lane/8 (q < 2), logical chunk (lane%8) ^ (row & 7)
+  const int nk = K / kPfBK;                                   // >= 2 (host)
+  const int wrows = MODE == 0 ? 2 * a.I : a.H;                // rows of one expert's weight
   const int lrow = lane >> 3, lchunk = lane & 7;
-  const uint8_t* srcA[4];
-  const uint8_t* srcB[2];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 32 * wave + 8 * q + lrow;
-    int64_t wrow;
-    if (MODE == 0) {
-      const int f0 = tile * 128;
-      wrow = row < 128 ? f0 + row : a.I + f0 + (row - 128);
-    } else {
-      wrow = (int64_t)tile * kPfRows + row;
-    }
-    srcA[q] = a.w + ((int64_t)e * wrows + wrow) * K + ((lchunk ^ (row & 7)) << 4);
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 16 * wave + 8 * q + lrow;
-    // padding slots read the first token of the block (their results are dropped)
-    const int f = a.seg.sorted_ids[tok0 + (row < ntok ? row : 0)];
-    const int64_t brow = MODE == 0 ? f / a.top_k : f;
-    srcB[q] = a.act + brow * K + ((lchunk ^ (row & 7)) << 4);
-  }
-  auto issue = [&](int s) {  // DMA of K-step s into ring slot s % kPfStages
-    lds_u8* base = smem + (s % kPfStages) * kPfStage;
-    const int kb = s * kPfBK;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + kb),
-                                       (void __attribute__((address_space(3)))*)(base + (32 * wave + 8 * q) * kPfBK),
-                                       16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(srcB[q] + kb),
-          (void __attribute__((address_space(3)))*)(base + kPfStageA + (16 * wave + 8 * q) * kPfBK), 16, 0, 0);
-  };
-
   // wave sub-tile: two 32-row A tiles and 64 tokens
   const int wr = wave & 3, wc = wave >> 2;
   const int arow0 = MODE == 0 ? 32 * wr : 64 * wr;             // gate rows (MODE 0)
   const int arow1 = MODE == 0 ? 128 + 32 * wr : 64 * wr + 32;  // up rows of the same features (MODE 0)
   const int brow0 = 64 * wc;
-  const bool live0 = brow0 < ntok, live1 = brow0 + 32 < ntok;  // 32-token sub-tiles that hold tokens
+  const int col = lane & 31, rq = (lane >> 5) * 4;
+
+  // DMA sources of an item for this lane: A rows 32*wave + 8*q + lane/8
+  // (q < 4), B rows 16*wave + 8*q + lane/8 (q < 2), logical chunk
+  // (lane%8) ^ (row & 7).  The loads go through buffer resources (the
+  // expert's weight matrix and the activation matrix, byte offsets below
+  // 2^31, checked by the host) rather than flat-global addresses: the
+  // compiler's wait-count model treats a flat-global load into LDS as a
+  // possible LDS access for as long as it is in flight, which would turn
+  // every wait for LDS reads into a full drain.
+
+  const __amdgpu_buffer_rsrc_t rsrcB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, 0x7fffffff, kBufferWord3);
+  auto make_src = [&](const PfItem& it, PfSrc& sr) {
+    sr.wa = a.w + (int64_t)it.e * wrows * K;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 32 * wave + 8 * q + lrow;
+      int wrow;
+      if (MODE == 0) {
+        const int f0 = it.tile * 128;
+        wrow = row < 128 ? f0 + row : a.I + f0 + (row - 128);
+      } else {
+        wrow = it.tile * kPfRows + row;
+      }
+      sr.offA[q] = wrow * K + ((lchunk ^ (row & 7)) << 4);
+    }
+    // token ids: padding slots read the block's last token (their results are dropped)
+    const int32_t* ids = a.seg.sorted_ids + it.blk * kPfTok;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) sr.fb[q] = ids[min(16 * wave + 8 * q + lrow, it.ntok - 1)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sr.f[j] = ids[min(brow0 + 32 * j + col, it.ntok - 1)];
+  };
+  // B-row offsets from the token ids: kept apart from make_src so that the
+  // wait for the ids falls where the offsets are first needed (the empty asm
+  // pins the conversion here; otherwise the compiler hoists it next to the
+  // loads, waiting for them there)
+  auto finish_src = [&](PfSrc& sr) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = 16 * wave + 8 * q + lrow;
+      int f = sr.fb[q];
+      asm volatile("" : "+v"(f));
+      const int brow = MODE == 0 ? f / a.top_k : f;
+      sr.offB[q] = brow * K + ((lchunk ^ (row & 7)) << 4);
+    }
+  };
+  // element-wise choice between two sources (a choice of struct address
+  // would force both structs into scratch memory)
+  auto pick = [](bool first, const PfSrc& x, const PfSrc& y) {
+    PfSrc r;
+    r.wa = first ? x.wa : y.wa;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.offA[q] = first ? x.offA[q] : y.offA[q];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) r.offB[q] = first ? x.offB[q] : y.offB[q];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r.f[j] = 0;
+    return r;
+  };
+  auto issue = [&](const PfSrc& sr, int kstep, int slot) {  // DMA of one K-step into ring slot `slot`
+    lds_u8* base = smem + slot * kPfStage;
+    const int kb = kstep * kPfBK;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)sr.wa, (short)0, wrows * K, kBufferWord3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (void __attribute__((address_space(3)))*)(base + (32 * wave + 8 * q) * kPfBK),
+                                               16, sr.offA[q], kb, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrcB, (void __attribute__((address_space(3)))*)(base + kPfStageA + (16 * wave + 8 * q) * kPfBK), 16, sr.offB[q],
+          kb, 0, 0);
+  };
+
   // fragment addresses within a stage: row l%32 of each tile, k-step ks uses
   // chunks 4*ks + 2*(l/32) and +1
   const int fr = lane & 31, fc = (lane >> 5) * 2;
@@ -212,108 +307,195 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = K / kPfBK;
-  // K-loop with NJ (0, 1 or 2) of the wave's 32-token sub-tiles multiplied;
-  // one version per NJ so that the loop body has no branches
+  // epilogue constants
+  const float deq = MODE == 0 ? (*a.a_scale) * (*a.w_scale)
+                              : (HDYN ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.a_scale) * (*a.w_scale);
+  const float rhs = (MODE == 0 && !HDYN) ? 1.0f / *a.h_scale : 1.0f;
+  float hmax = 0.0f;
+
+  PfSrc cs, ns;
+  make_src(cur, cs);
+  finish_src(cs);
+  int slot0 = 0;  // ring slot of the current item's first K-step
+  issue(cs, 0, 0);
+  issue(cs, 1, 1);
+
+  // Fragments of one 64-byte MFMA k-step for up to two token sub-tiles.
+  struct Frags {
+    u32x4 a0[2], a1[2], b0[2], b1[2];
+  };
+  // K-loop of the current item with NJ (0, 1 or 2) of the wave's 32-token
+  // sub-tiles multiplied; one version per NJ so that the loop body has no
+  // branches.  Software pipelined by half K-steps over two register sets:
+  // the LDS reads of one MFMA k-step are in flight while the MFMAs of the
+  // previous one run, so the LDS and matrix pipes overlap.
   auto kloop = [&](auto nj_tag) {
     constexpr int NJ = decltype(nj_tag)::value;
-    issue(0);
-    if (nk > 1) issue(1);
-    for (int s = 0; s < nk; ++s) {
-      // this wave's DMA of step s is complete once at most the next step's six loads are in flight
-      if (s + 1 < nk)
+    auto slot = [&](int s) { return (slot0 + s) % kPfStages; };
+    auto read = [&](Frags& F, int s, int ks) {
+      const lds_u8* st = smem + slot(s) * kPfStage;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        F.a0[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA0[ks][c]);
+        F.a1[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA1[ks][c]);
+        F.b0[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB0[ks][c]);
+        if constexpr (NJ > 1) F.b1[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB1[ks][c]);
+      }
+    };
+    auto mma = [&](const Frags& F) {
+      acc[0][0] = mfma32_fp8(F.a0[0], F.a0[1], F.b0[0], F.b0[1], acc[0][0]);
+      acc[1][0] = mfma32_fp8(F.a1[0], F.a1[1], F.b0[0], F.b0[1], acc[1][0]);
+      if constexpr (NJ > 1) {
+        acc[0][1] = mfma32_fp8(F.a0[0], F.a0[1], F.b1[0], F.b1[1], acc[0][1]);
+        acc[1][1] = mfma32_fp8(F.a1[0], F.a1[1], F.b1[0], F.b1[1], acc[1][1]);
+      }
+    };
+    // step s >= 1: wait for this wave's DMA of step s, barrier, DMA of step
+    // s+2 (of this item, else of the next)
+    auto sync = [&](int s) {
+      if (s + 1 < nk || has_next)
         wait_vm<6>();
       else
         wait_vm<0>();
       ring_barrier();  // every wave's step-s data is in LDS; slot (s+2)%3 is no longer read
-      if (s + 2 < nk) issue(s + 2);
-      if constexpr (NJ > 0) {
-        const lds_u8* st = smem + (s % kPfStages) * kPfStage;
-        u32x4 a0[2][2], a1[2][2], b0[2][2], b1[2][2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            a0[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA0[ks][c]);
-            a1[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA1[ks][c]);
-            b0[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB0[ks][c]);
-            if constexpr (NJ > 1) b1[ks][c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB1[ks][c]);
-          }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          acc[0][0] = mfma32_fp8(a0[ks][0], a0[ks][1], b0[ks][0], b0[ks][1], acc[0][0]);
-          acc[1][0] = mfma32_fp8(a1[ks][0], a1[ks][1], b0[ks][0], b0[ks][1], acc[1][0]);
-          if constexpr (NJ > 1) {
-            acc[0][1] = mfma32_fp8(a0[ks][0], a0[ks][1], b1[ks][0], b1[ks][1], acc[0][1]);
-            acc[1][1] = mfma32_fp8(a1[ks][0], a1[ks][1], b1[ks][0], b1[ks][1], acc[1][1]);
-          }
+      const bool own = s + 2 < nk;
+      if (own || has_next) issue(pick(own, cs, ns), own ? s + 2 : s + 2 - nk, slot(s + 2));
+    };
+    // step 0 also loads the next item's token ids, ahead of the step-2 DMA
+    auto sync0 = [&]() {
+      wait_vm<6>();  // nk >= 2: step 1's loads follow step 0's
+      ring_barrier();
+      make_src(nxt, ns);  // unconditional: a conditional load would be copied at the join, waiting for it
+      if (2 < nk) {
+        issue(cs, 2, slot(2));  // independent of the token ids just requested
+      } else {
+        finish_src(ns);
+        if (has_next) issue(ns, 0, slot(2));
+      }
+    };
+    if constexpr (NJ == 0) {
+      sync0();
+      int s = 1;
+      for (; s + 2 < nk; ++s) {
+        wait_vm<6>();
+        ring_barrier();
+        issue(cs, s + 2, slot(s + 2));
+      }
+      if (nk > 2) finish_src(ns);
+      for (; s < nk; ++s) sync(s);
+    } else {
+      Frags F0, F1;
+      sync0();
+      read(F0, 0, 0);
+      // The scheduling barriers keep each MFMA batch between the reads it is
+      // meant to overlap; the steady-state body is branch-free so that the
+      // compiler cannot sink the first batch into a join block.
+      int s = 0;
+      for (; s + 3 < nk; ++s) {
+        read(F1, s, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(F0);  // k-step 0 of step s
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<6>();    // this wave's DMA of step s+1 has landed
+        ring_barrier();  // also waits for the reads into F1
+        issue(cs, s + 3, slot(s + 3));
+        read(F0, s + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(F1);  // k-step 1 of step s
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (nk > 2) finish_src(ns);
+      for (; s < nk; ++s) {  // the last (up to three) steps
+        read(F1, s, 1);
+        mma(F0);
+        if (s + 1 < nk) {
+          sync(s + 1);
+          read(F0, s + 1, 0);
         }
+        mma(F1);
       }
     }
   };
-  if (live1)
-    kloop(std::integral_constant<int, 2>{});
-  else if (live0)
-    kloop(std::integral_constant<int, 1>{});
-  else
-    kloop(std::integral_constant<int, 0>{});
 
-  // epilogue
-  const int col = lane & 31, rq = (lane >> 5) * 4;
-  if (MODE == 0) {
-    const float deq = (*a.a_scale) * (*a.w_scale);
-    const float rhs = HDYN ? 1.0f : 1.0f / *a.h_scale;
-    float hmax = 0.0f;
+  while (true) {
+    const bool live0 = brow0 < cur.ntok, live1 = brow0 + 32 < cur.ntok;  // 32-token sub-tiles that hold tokens
+    if (live1)
+      kloop(std::integral_constant<int, 2>{});
+    else if (live0)
+      kloop(std::integral_constant<int, 1>{});
+    else
+      kloop(std::integral_constant<int, 0>{});
+
+    // metadata of the item after the next, waited for at its first use
+    PfItem nn = nxt;
+    bool has_nn = false;
+    if (has_next) {
+      L += stride;
+      has_nn = pf_next(a, nb, L, stride, nn);
+    }
+
+    // epilogue (no LDS: the next item's first loads are landing in the ring)
+    if (MODE == 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = brow0 + 32 * j + col;
-      if (t < ntok) {
-        const int f = a.seg.sorted_ids[tok0 + t];
-        const int fbase = tile * 128 + 32 * wr;
+      for (int j = 0; j < 2; ++j) {
+        const int t = brow0 + 32 * j + col;
+        if (t < cur.ntok) {
+          const int f = cs.f[j];
+          const int fbase = cur.tile * 128 + 32 * wr;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float hv[4];
+          for (int g = 0; g < 4; ++g) {
+            float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float gt = acc[0][j][4 * g + q] * deq;
-            const float up = acc[1][j][4 * g + q] * deq;
-            hv[q] = gt / (1.0f + expf(-gt)) * up;
-            hmax = fmaxf(hmax, fabsf(hv[q]));
-          }
-          const int64_t idx = (int64_t)f * a.I + fbase + 8 * g + rq;
-          if (HDYN) {
-            u32x2 o = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            *(u32x2*)(a.out + idx * 2) = o;
-          } else {
-            *(unsigned*)(a.out + idx) = pack_e4m3x4(hv[0] * rhs, hv[1] * rhs, hv[2] * rhs, hv[3] * rhs);
+            for (int q = 0; q < 4; ++q) {
+              const float gt = acc[0][j][4 * g + q] * deq;
+              const float up = acc[1][j][4 * g + q] * deq;
+              hv[q] = gt / (1.0f + expf(-gt)) * up;
+              hmax = fmaxf(hmax, fabsf(hv[q]));
+            }
+            const int64_t idx = (int64_t)f * a.I + fbase + 8 * g + rq;
+            if (HDYN) {
+              u32x2 o = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+              *(u32x2*)(a.out + idx * 2) = o;
+            } else {
+              *(unsigned*)(a.out + idx) = pack_e4m3x4(hv[0] * rhs, hv[1] * rhs, hv[2] * rhs, hv[3] * rhs);
+            }
           }
         }
       }
-    }
-    if (HDYN) {
-      hmax = wave_max(hmax);
-      if (lane == 0) atomicMax(a.h_amax_out, __float_as_uint(hmax));
-    }
-  } else {
-    const float sh = HDYN ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.a_scale;
-    const float deq = sh * (*a.w_scale);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = brow0 + 32 * j + col;
-      if (t < ntok) {
-        const int f = a.seg.sorted_ids[tok0 + t];
-        const float w = a.topk_w[f] * deq;
-        uint16_t* dst = (uint16_t*)a.out + (int64_t)f * a.H + (int64_t)tile * kPfRows + 64 * wr;
+      for (int j = 0; j < 2; ++j) {
+        const int t = brow0 + 32 * j + col;
+        if (t < cur.ntok) {
+          uint16_t* dst = (uint16_t*)a.out + (int64_t)cs.f[j] * a.H + (int64_t)cur.tile * kPfRows + 64 * wr;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x16& c = acc[i][j];
-            u32x2 o = {pack_bf16x2(c[4 * g] * w, c[4 * g + 1] * w), pack_bf16x2(c[4 * g + 2] * w, c[4 * g + 3] * w)};
-            *(u32x2*)(dst + 32 * i + 8 * g + rq) = o;
-          }
+            for (int g = 0; g < 4; ++g) {
+              const f32x16& c = acc[i][j];
+              u32x2 o = {pack_bf16x2(c[4 * g] * deq, c[4 * g + 1] * deq), pack_bf16x2(c[4 * g + 2] * deq, c[4 * g + 3] * deq)};
+              *(u32x2*)(dst + 32 * i + 8 * g + rq) = o;
+            }
+        }
       }
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    if (!has_next) break;
+    cur = nxt;
+    cs = ns;
+    nxt = nn;
+    has_next = has_nn;
+    slot0 = (slot0 + nk) % kPfStages;
+  }
+  if (MODE == 0 && HDYN) {
+    hmax = wave_max(hmax);
+    if (lane == 0) atomicMax(a.h_amax_out, __float_as_uint(hmax));
   }
 }
 
@@ -332,9 +514,10 @@ __global__ __launch_bounds__(256) void prefill_quant_h_kernel(const uint16_t* __
   *(u32x4*)(hq + i) = o;
 }
 
-// y[m,n] = bf16( sum_j part[m*k+j][n] ), j ascending, fp32 sum; 8 outputs per
-// thread.
+// y[m,n] = bf16( sum_j w[m*k+j] * part[m*k+j][n] ), j ascending, fp32 sum;
+// 8 outputs per thread.
 __global__ __launch_bounds__(256) void prefill_finalize_kernel(const uint16_t* __restrict__ part,
+                                                               const float* __restrict__ topk_w,
                                                                uint16_t* __restrict__ y, int M, int H, int top_k,
                                                                const float* x_scale, const unsigned* h_amax,
                                                                const float* h_scale, float* scales_out) {
@@ -347,11 +530,12 @@ __global__ __launch_bounds__(256) void prefill_finalize_kernel(const uint16_t* _
   const int64_t m = i / H, n = i - m * H;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < top_k; ++j) {
+    const float w = topk_w[m * top_k + j];
     const u32x4 v = *(const u32x4*)(part + (m * top_k + j) * H + n);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += bf16_lo(v[q]);
-      acc[2 * q + 1] += bf16_hi(v[q]);
+      acc[2 * q] += w * bf16_lo(v[q]);
+      acc[2 * q + 1] += w * bf16_hi(v[q]);
     }
   }
   u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),

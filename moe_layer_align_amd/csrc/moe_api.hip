@@ -21,11 +21,17 @@ constexpr int kAlignBlockFused = 16;   // token tile of the decode products' B o
 constexpr int kPrefillMinPairs = 8192; // fp8 layers with at least this many pairs take the prefill products
 
 // fp8 layers with many pairs use the tiled prefill products (token block 128,
-// weight tiles of 256 rows: H a multiple of 256).
-bool use_prefill(int64_t P, moe_dtype_t dt, int H) {
-  return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0;
+// weight tiles of 256 rows: H a multiple of 256; at least two 128-byte
+// K-steps in both products).  Their operand loads take 32-bit byte offsets
+// into one expert's weights and into the activations.
+bool use_prefill(int M, int k, moe_dtype_t dt, int H, int I) {
+  const int64_t P = (int64_t)M * k, lim = INT32_MAX;
+  return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0 && I >= 2 * kPfBK &&
+         2 * (int64_t)I * H <= lim && (int64_t)M * H <= lim && P * I <= lim;
 }
-int align_block(int64_t P, moe_dtype_t dt, int H) { return use_prefill(P, dt, H) ? kPfTok : kAlignBlockFused; }
+int align_block(int M, int k, moe_dtype_t dt, int H, int I) {
+  return use_prefill(M, k, dt, H, I) ? kPfTok : kAlignBlockFused;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -85,7 +91,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
     off += round_up(std::max<size_t>(bytes, 4), 256);
     return o;
   };
-  const int B = align_block(P, dt, H);
+  const int B = align_block(M, k, dt, H, I);
   L.capacity = align_capacity(P, E, B);
   L.n_blocks = (int)(L.capacity / B);
   L.n_route_wg = (int)cdiv(M, 4);
@@ -280,6 +286,27 @@ bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float*
   return true;
 }
 
+// Workgroups of a persistent launch with one workgroup per CU: the current
+// device's CU count rounded down to a multiple of 8, so that workgroup b stays
+// on XCD b % 8 while it walks items b, b + wgs, ...  Cached per device.
+moe_status_t persistent_wgs(int* wgs) {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_DEVICE;
+  if (dev < kMaxDevices && cached[dev] > 0) {
+    *wgs = cached[dev];
+    return MOE_OK;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    return MOE_ERR_DEVICE;
+  const int n = cus / 8 * 8;
+  if (dev < kMaxDevices) cached[dev] = n;
+  *wgs = n;
+  return MOE_OK;
+}
+
 template <int MODE, bool HDYN>
 void launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
   static bool lds_set = false;  // the dynamic LDS ceiling is raised once per kernel
@@ -416,16 +443,25 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
 
   const PrefillSeg seg{o.sorted_ids, o.block_expert, o.offsets, o.counts, o.num_padded};
   uint8_t* hq = hdyn ? h + (size_t)P * I * 2 : h;  // e4m3 h read by the down product
-  const int nblk = (int)round_up((size_t)L.n_blocks, 8);
+  // work items: 8 XCDs x the raster groups that the largest possible block count needs
+  auto prefill_items = [&](int T) {
+    const int nbx = (int)cdiv(L.n_blocks, 8);
+    const int groups = (int)(cdiv(T, kPfGT) * cdiv(nbx, kPfGB));
+    return 8 * groups * kPfGT * kPfGB;
+  };
+  // persistent workgroups: one per CU, a multiple of 8 (one XCD each)
+  int wgs = 0;
+  if ((rc = persistent_wgs(&wgs)) != MOE_OK) return rc;
   rec(4);
   {
     const int T = I / 128;  // 256-row tiles of W13: 128 gate + 128 up rows
-    PrefillArgs g{(const uint8_t*)a->w13, xq, seg, wts, H, I, k, (int)P, T, nblk, a->w13_scale, scale_slot,
-                  nullptr, a->h_scale, h, h_amax};
+    const int items = prefill_items(T);
+    PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
+                  a->h_scale, h, h_amax};
     if (hdyn)
-      launch_prefill<0, true>(T * nblk, st, g);
+      launch_prefill<0, true>(std::min(wgs, items), st, g);
     else
-      launch_prefill<0, false>(T * nblk, st, g);
+      launch_prefill<0, false>(std::min(wgs, items), st, g);
   }
   rec(5);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -437,18 +473,19 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
       if ((rc = launch_status()) != MOE_OK) return rc;
     }
     const int T = H / kPfRows;
-    PrefillArgs g{(const uint8_t*)a->w2, hq, seg, wts, H, I, k, (int)P, T, nblk, a->w2_scale, a->h_scale, h_amax,
-                  nullptr, (uint8_t*)part, nullptr};
+    const int items = prefill_items(T);
+    PrefillArgs g{(const uint8_t*)a->w2, hq, seg, H, I, k, (int)P, T, items, a->w2_scale, a->h_scale, h_amax, nullptr,
+                  (uint8_t*)part, nullptr};
     if (hdyn)
-      launch_prefill<1, true>(T * nblk, st, g);
+      launch_prefill<1, true>(std::min(wgs, items), st, g);
     else
-      launch_prefill<1, false>(T * nblk, st, g);
+      launch_prefill<1, false>(std::min(wgs, items), st, g);
   }
   rec(7);
   if ((rc = launch_status()) != MOE_OK) return rc;
   rec(8);
   prefill_finalize_kernel<<<(unsigned)cdiv((int64_t)M * H, 2048), 256, 0, st>>>(
-      (const uint16_t*)part, (uint16_t*)a->y, M, H, k, scale_slot, h_amax, a->h_scale, a->scales_out);
+      (const uint16_t*)part, wts, (uint16_t*)a->y, M, H, k, scale_slot, h_amax, a->h_scale, a->scales_out);
   rec(9);
   return launch_status();
 }
@@ -481,7 +518,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const Layout L = make_layout(M, E, H, I, k, a->dtype);
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const bool hdyn = fp8 && !a->h_scale;
-  const bool prefill = use_prefill((int64_t)M * k, a->dtype, a->H);
+  const bool prefill = use_prefill(M, k, a->dtype, a->H, a->I);
   Plan plan{};
   if (!prefill) {
     rc = make_plan(M, E, H, I, k, fp8, hdyn, a->tuning, &plan);

@@ -102,6 +102,27 @@ def test_repeat_calls_reuse_workspace():
         assert torch.equal(y, ys[0])
 
 
+def test_bf16_batch_invariance_with_fixed_splits():
+    # With the K splits fixed by the caller, a bf16 token's output depends on
+    # that token alone: each MFMA output column is one token, routing is per
+    # token, and the combine adds in a fixed order.  The same token alone, and
+    # at two positions of batches of 17 and 64 other tokens, gives the same bits.
+    cfg = cfg_of("bf16", 8, 2, 512, 384)
+    w13, w2, _, _ = gen_weights(cfg, 9, device=DEV)
+    t = moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=3, gemm2_wave_ksplit=4, token_tiles=2)
+    x1 = gen_x(cfg.H, 1, 9, sub=1)
+    lg1 = gen_logits(cfg, 1, 9, sub=1)
+    y1 = moe.fused_forward(x1.to(DEV), lg1.to(DEV), w13, w2, cfg.k, tuning=t)
+    for M, pos in ((17, 0), (17, 16), (64, 5), (64, 63)):
+        x = gen_x(cfg.H, M, 10 + M, sub=M)
+        lg = gen_logits(cfg, M, 10 + M, sub=M)
+        x[pos] = x1[0]
+        lg[pos] = lg1[0]
+        y = moe.fused_forward(x.to(DEV), lg.to(DEV), w13, w2, cfg.k, tuning=t)
+        torch.cuda.synchronize()
+        assert torch.equal(y[pos], y1[0]), (M, pos)
+
+
 # ---------------------------------------------------------------- the workloads
 def test_tiny():
     cfg = CONFIGS["tiny"]
@@ -159,8 +180,23 @@ def prefill_w():
 # Tiled prefill products (fp8 with at least 8192 pairs) at sizes the oracle
 # evaluates quickly: Zipf routing leaves experts empty and blocks partial.
 def test_prefill_path_dynamic_scales_all_tokens():
-    cfg = MoEConfig("pf_small", E=16, k=8, H=256, I=128, dtype="fp8", ms=(1100,), logits="zipf")
+    # two 128-byte K-steps in both products: the shortest prefill K-loop
+    cfg = MoEConfig("pf_small", E=16, k=8, H=256, I=256, dtype="fp8", ms=(1100,), logits="zipf")
     compare(cfg, 1100, seed=11)
+
+
+def test_prefill_path_three_k_steps():
+    # down product with three K-steps: the next item's first loads are issued
+    # from the first tail step
+    cfg = MoEConfig("pf_k3", E=16, k=8, H=768, I=384, dtype="fp8", ms=(1100,), logits="zipf")
+    compare(cfg, 1100, seed=13, tokens=[0, 1, 2, 3, 400, 401, 777, 1098, 1099])
+
+
+def test_prefill_path_many_items_per_workgroup():
+    # several hundred (tile, block) items per product: every persistent
+    # workgroup walks several of them with the LDS ring running across items
+    cfg = MoEConfig("pf_items", E=8, k=2, H=1024, I=1024, dtype="fp8", ms=(4096,), logits="zipf")
+    compare(cfg, 4096, seed=14, tokens=[0, 1, 2, 3, 100, 1000, 2047, 2048, 3000, 4093, 4094, 4095])
 
 
 def test_prefill_path_static_scales_long_k():
