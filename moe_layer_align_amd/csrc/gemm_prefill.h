@@ -1,23 +1,31 @@
 // Grouped expert products for large token counts (prefill), gfx950 fp8 MFMA.
 //
 // At prefill every active expert holds hundreds to thousands of tokens, so the
-// products are compute-bound and both operands are reused: a workgroup
-// computes a 256 x 128 tile (256 weight rows x 128 tokens of one expert) and
-// stages both operands through LDS, K-step by K-step.  The token dimension is
-// grouped by the align step with a block of 128: block b holds tokens of
-// expert block_expert[b] only, padded with the sentinel, so a workgroup's
-// tokens share one expert.  Weight rows stay the MFMA's A operand and tokens
-// the B operand, as in the decode kernels; the 32x32x64 fp8 MFMA is used,
-// each of the eight waves owning a 64 x 64 sub-tile (2 x 2 MFMA tiles).
+// products are compute-bound and both operands are reused: a work item is a
+// 512 x 128 tile (512 weight rows x 128 tokens of one expert) whose operands
+// are staged through LDS, K-step by K-step.  The token dimension is grouped by
+// the align step with a block of 128: block b holds tokens of expert
+// block_expert[b] only, padded with the sentinel, so an item's tokens share
+// one expert.  Weight rows stay the MFMA's A operand and tokens the B operand,
+// as in the decode kernels; the 32x32x64 fp8 MFMA is used.
+//
+// Four waves, one per SIMD, each own 128 weight rows x all 128 tokens (4 x 4
+// MFMA tiles, accumulators in AGPRs).  That shape needs the fewest LDS bytes
+// per MFMA: per 64-byte K-step a CU reads 64 KB of fragments and writes 40 KB
+// of operands into LDS against 16 MFMAs per SIMD, which keeps the LDS port
+// (128 bytes per clock) below the matrix pipes.  With one wave per SIMD there
+// is no second wave to fill the matrix pipe, so every LDS read and DMA is
+// interleaved between MFMAs (sched_group_barrier) instead of being issued as a
+// block.
 //
 // Work items (weight tile, token block) are numbered so that each XCD works
 // on its own range of token blocks, rasterised so that concurrent workgroups
 // share operands in that XCD's L2 (pf_map); one persistent workgroup per CU
 // walks them.
 //
-// Pipeline: both operand tiles of each 128-byte K-step are loaded from global
-// memory straight into a three-deep LDS ring (direct-to-LDS loads, no staging
-// registers), two steps ahead of the MFMAs, with one barrier per step.
+// Pipeline: both operand tiles of each 64-byte K-step are loaded from global
+// memory straight into a four-deep LDS ring (direct-to-LDS loads, no staging
+// registers), three steps ahead of the MFMAs, with one barrier per step.
 #pragma once
 
 #include <type_traits>
@@ -52,18 +60,24 @@ __device__ __forceinline__ void wait_vm() {
 // only (lgkmcnt 0), not for its outstanding global-to-LDS loads, whose
 // completion the K-loop waits for explicitly; the memory clobber keeps the
 // compiler from moving LDS accesses across it.  (__syncthreads() would also
-// wait for every vector-memory operation, draining the prefetch queue.)
-__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// wait for every vector-memory operation, draining the prefetch queue.)  The
+// leading builtin repeats the LDS wait where the compiler's counter model
+// sees it, so that it does not wait again for reads that already completed.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-constexpr int kPfTok = 128;                          // tokens per workgroup (the align block)
-constexpr int kPfRows = 256;                         // weight rows per workgroup
-constexpr int kPfBK = 128;                           // K bytes per step (fp8): two MFMA k-steps
-constexpr int kPfStages = 3;                         // LDS ring depth
-constexpr int kPfStageA = kPfRows * kPfBK;           // 32 KB
-constexpr int kPfStageB = kPfTok * kPfBK;            // 16 KB
-constexpr int kPfStage = kPfStageA + kPfStageB;      // 48 KB
-constexpr int kPfLds = kPfStages * kPfStage;         // 144 KB: one workgroup of 8 waves per CU
-constexpr int kPfThreads = 512;
+constexpr int kPfTok = 128;                      // tokens per work item (the align block)
+constexpr int kPfRows = 512;                     // weight rows per work item
+constexpr int kPfBK = 64;                        // K bytes per step: one MFMA k-step
+constexpr int kPfStages = 4;                     // LDS ring depth: loads run three steps ahead
+constexpr int kPfStageA = kPfRows * kPfBK;       // 32 KB
+constexpr int kPfStageB = kPfTok * kPfBK;        // 8 KB
+constexpr int kPfStage = kPfStageA + kPfStageB;  // 40 KB
+constexpr int kPfLds = kPfStages * kPfStage;     // 160 KB: the whole LDS, one workgroup per CU
+constexpr int kPfThreads = 256;                  // four waves
+constexpr int kPfDma = 10;                       // DMA instructions per wave per step: 8 A + 2 B
 // third descriptor word of a raw byte buffer resource on CDNA (32-bit data
 // format, no swizzle, no index stride)
 constexpr int kBufferWord3 = 0x00020000;
@@ -76,34 +90,39 @@ struct PrefillSeg {
   const int32_t* num_padded;    // [1]
 };
 
-// LDS layout of an operand tile in one stage: rows of 128 bytes, the eight
-// 16-byte chunks of row r stored at chunk position c ^ (r & 7), so the MFMA
-// fragment reads (32 rows, same chunk) spread over all banks.
-__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ (row & 7)) << 4); }
+// LDS layout of an operand tile in one stage: rows of 64 bytes, the four
+// 16-byte chunks of row r stored at chunk position c ^ ((r >> 1) & 3).  Eight
+// consecutive rows with the same logical chunk then fall on the eight
+// different 16-byte bank groups of a 128-byte line, so the MFMA fragment reads
+// (32 rows, same chunk) are free of bank conflicts.
+__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
-// Workgroup -> (weight tile, token block), XCD-aware.  Workgroups are handed
-// to the eight XCDs round robin by linear id.  XCD c takes a contiguous eighth
-// of the token blocks that hold tokens (blocks are ordered by expert, so an
-// XCD's range covers a few experts; only experts cut by a range boundary have
-// their weights read by two XCDs) and all weight tiles for them.  Inside an
-// XCD the work is rasterised in groups of kPfGT tiles x kPfGB blocks, about
-// one workgroup per CU, so the workgroups running together share weight
-// tiles and token blocks in that XCD's L2.  Returns false for surplus
-// workgroups (the grid is sized for the largest possible block count).
+// Work item -> (weight tile, token block), XCD-aware.  Workgroups are handed
+// to the eight XCDs round robin by linear id, and item L belongs to XCD L % 8.
+// XCD c takes a contiguous eighth of the token blocks that hold tokens
+// (blocks are ordered by expert, so an XCD's range covers a few experts; only
+// experts cut by a range boundary have their weights read by two XCDs) and
+// all weight tiles for them.  Inside an XCD the items are numbered densely
+// (no holes, so the workgroups walking them round robin get equal shares):
+// by groups of kPfGB blocks, within a block group by groups of kPfGT tiles,
+// the last group of either kind possibly smaller.  A full group of kPfGT x
+// kPfGB items is about one per CU of an XCD, so workgroups running together
+// share weight tiles and token blocks in that XCD's L2.  Returns false past
+// the XCD's last item (all later indices of that XCD are past it too).
 constexpr int kPfGT = 4;  // weight tiles per raster group
 constexpr int kPfGB = 8;  // token blocks per raster group
 
 __device__ __forceinline__ bool pf_map(int L, int T, int nb, int* tile, int* blk) {
   const int c = L & 7, j = L >> 3;
-  const int nbx = (nb + 7) >> 3;                     // blocks per XCD
-  const int ntg = (T + kPfGT - 1) / kPfGT;           // tile groups
-  const int g = j / (kPfGT * kPfGB), r = j - g * (kPfGT * kPfGB);
-  const int bg = g / ntg, tg = g - bg * ntg;
-  const int t = tg * kPfGT + r / kPfGB, b = bg * kPfGB + (r % kPfGB);
-  if (t >= T || b >= nbx) return false;
-  *tile = t;
-  *blk = c * nbx + b;
-  return *blk < nb;
+  const int nbx = (nb + 7) >> 3;                    // blocks per XCD
+  const int nbc = max(0, min(nbx, nb - c * nbx));  // blocks of XCD c
+  if (j >= T * nbc) return false;
+  const int bg = j / (T * kPfGB), r = j - bg * (T * kPfGB);
+  const int gb = min(kPfGB, nbc - bg * kPfGB);       // blocks in this block group
+  const int tg = r / (kPfGT * gb), rr = r - tg * (kPfGT * gb);
+  *tile = tg * kPfGT + rr / gb;
+  *blk = c * nbx + bg * kPfGB + rr % gb;
+  return true;
 }
 
 // ---------------------------------------------------------------- products
@@ -112,13 +131,13 @@ struct PrefillArgs {
   const uint8_t* act;      // gate/up: xq [M][H]; down: hq [P][I], e4m3
   PrefillSeg seg;
   int H, I, top_k, P;
-  int tiles;               // weight tiles: 2I/256 or H/256
-  int items;               // linear work items covered by pf_map (>= tiles x blocks)
+  int tiles;               // weight tiles: 2I/512 or H/512
+  int items;               // bound on the linear item index: 8 x tiles x blocks per XCD (largest case)
   const float* w_scale;    // s_w13 or s_w2
   const float* a_scale;    // gate/up: s_x in effect; down: static s_h (null = dynamic)
   const unsigned* h_amax;  // down with dynamic scale: max |h| (float bits)
   const float* h_scale;    // gate/up: static s_h (null = dynamic: h written as bf16)
-  uint8_t* out;            // gate/up: h; down: part [P][H] bf16
+  uint8_t* out;            // gate/up: h (fp32 or e4m3); down: part [P][H] bf16
   unsigned* h_amax_out;    // gate/up with dynamic scale
 };
 
@@ -127,9 +146,10 @@ struct PrefillArgs {
 // pass silently drops the kernel's launch stub.
 struct PfSrc {
   const uint8_t* wa;  // the expert's weight matrix (a buffer resource is made from it at issue)
-  int offA[4], offB[2];
-  int fb[2];  // pair ids of this lane's B rows, until finish_src turns them into offB
-  int f[2];   // pair ids of this lane's epilogue tokens brow0 + 32*j + lane%32 (clamped)
+  int offA;     // byte offset of this lane's first A row (row q adds 16*q rows)
+  int offB[2];  // byte offsets of this lane's two B rows
+  int fb[2];    // pair ids of this lane's B rows, until finish_src turns them into offB
+  int f[4];     // pair ids of this lane's epilogue tokens 32*j + lane%32 (clamped)
 };
 
 // One work item: weight tile x token block of one expert.
@@ -138,15 +158,12 @@ struct PfItem {
   int ntok;  // tokens of the block that belong to the expert (1..128)
 };
 
-// The next work item at or after linear index L (stepping by `stride`), or
-// false when none is left.  Uniform across the workgroup; the skip over
-// surplus indices is arithmetic only, so the loads are issued once and
-// waited for where their values are first used.
+// The work item at linear index L, or false when the workgroup has none left
+// (stride, a multiple of 8, keeps L on one XCD).  Uniform across the
+// workgroup; the loads are waited for where their values are first used.
 __device__ __forceinline__ bool pf_next(const PrefillArgs& a, int nb, int& L, int stride, PfItem& it) {
   int tile = 0, blk = 0;
-  for (; L < a.items; L += stride)
-    if (pf_map(L, a.tiles, nb, &tile, &blk)) break;
-  if (L >= a.items) return false;
+  if (L >= a.items || !pf_map(L, a.tiles, nb, &tile, &blk)) return false;  // later indices of this XCD are past its items too
   const int e = a.seg.block_expert[blk];  // every block below num_padded belongs to an expert
   it.tile = tile;
   it.blk = blk;
@@ -155,36 +172,62 @@ __device__ __forceinline__ bool pf_next(const PrefillArgs& a, int nb, int& L, in
   return true;
 }
 
-// MODE 0: gate/up product, tile rows = 128 gate + 128 up rows of the same 128
-//   features, epilogue SiLU(g)*u -> h.  HDYN: h stored as bf16 with a running
+// SiLU(x) = x / (1 + e^-x) with the hardware exp2 and reciprocal (about one
+// ulp each in fp32, far below the e4m3 / bf16 rounding that follows): the
+// libm exp and the IEEE division cost several times more, and with one wave
+// per SIMD nothing hides the epilogue.  Large |x| behave: e^-x overflows to
+// inf for x << 0 (result -0), and underflows to 0 for x >> 0 (result x).
+__device__ __forceinline__ float silu_fast(float x) {
+  const float e = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Scheduling pattern of one K-step with NMF MFMAs: the step's NDS LDS
+// fragment reads follow the MFMAs of the first half, its NVM DMA loads those
+// of the second half, spread as evenly as the counts allow.
+template <int K, int NMF, int NDS, int NVM, int ID>
+__device__ __forceinline__ void pf_interleave() {
+  if constexpr (K < NMF) {
+    constexpr int H = NMF / 2;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // one MFMA
+    if constexpr (K < H) {
+      constexpr int n = NDS * (K + 1) / H - NDS * K / H;
+      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, ID);  // LDS reads
+    } else {
+      constexpr int n = NVM * (K - H + 1) / (NMF - H) - NVM * (K - H) / (NMF - H);
+      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, ID);  // vector-memory loads
+    }
+    pf_interleave<K + 1, NMF, NDS, NVM, ID>();
+  }
+}
+
+// MODE 0: gate/up product, tile rows = 256 gate + 256 up rows of the same 256
+//   features, epilogue SiLU(g)*u -> h.  HDYN: h stored as fp32 with a running
 //   amax (quantised by prefill_quant_h_kernel), else as e4m3 with the static
 //   scale.
-// MODE 1: down product, tile rows = 256 output features, epilogue
+// MODE 1: down product, tile rows = 512 output features, epilogue
 //   s_h * s_w2 * acc -> bf16 part[pair][feature] (the routing weight is
 //   applied when the pairs of a token are summed).
 //
 // Persistent: one workgroup per CU walks the work items L = blockIdx.x,
 // blockIdx.x + gridDim.x, ... (gridDim.x a multiple of 8 keeps every
 // workgroup on the XCD that pf_map assigns its items to).  The LDS ring runs
-// on across items: the last two K-steps of an item load the first two of the
-// next, whose metadata was fetched one item earlier, so an item's epilogue
+// on across items: the last three K-steps of an item load the first three of
+// the next, whose metadata was fetched one item earlier, so an item's epilogue
 // overlaps the next item's first loads and no workgroup start or metadata
 // latency sits between items.
 //
-// Eight waves: wave (wr = 0..3, wc = 0..1) owns 64 weight rows x 64 tokens
-// (2 x 2 MFMA tiles; in MODE 0 the 32 gate and the 32 up rows of the same 32
-// features).  Each 128-byte K-step: every wave DMA-loads 32 rows of the A
-// tile and 16 rows of the B tile (six 1 KB load instructions, lane i filling
-// bytes 16i..16i+15 of an 8-row block) into a three-deep LDS ring two steps
-// ahead; one barrier per step; 8 MFMAs per wave per step, issued in the same
-// window as the LDS reads of the next step.
+// Wave w owns weight rows 128w..128w+127 of the tile (MODE 0: gate and up
+// rows of features 64w..64w+63) and all 128 tokens.  Each 64-byte K-step every
+// wave DMA-loads 128 rows of the A tile and 32 rows of the B tile (ten 1 KB
+// load instructions, lane i filling bytes 16i..16i+15 of a 16-row block).
 //
 // Wait accounting: the waits count vector-memory operations, which complete
-// in issue order.  Before the barrier of step s a wave waits until at most
-// six are outstanding, the six loads of step s+1 issued after step s's: any
-// other vector-memory operation (token ids, epilogue stores) only makes that
-// wait stricter.  When no load follows step s (the last step of the last
-// item) the wait is for zero.
+// in issue order.  Before the barrier that precedes the reads of step s+1 a
+// wave waits until at most ten are outstanding: the loads of step s+2, issued
+// after those of step s+1.  Any other vector-memory operation (token ids,
+// epilogue stores) only makes that wait stricter.  When no load follows step
+// s+1 (the end of the last item) the wait is for zero.
 template <int MODE, bool HDYN>
 __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -201,47 +244,41 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the wave's branches scalar
   const int K = MODE == 0 ? a.H : a.I;                        // contraction length (bytes)
-  const int nk = K / kPfBK;                                   // >= 2 (host)
+  const int nk = K / kPfBK;                                   // >= 4 (host)
   const int wrows = MODE == 0 ? 2 * a.I : a.H;                // rows of one expert's weight
-  const int lrow = lane >> 3, lchunk = lane & 7;
-  // wave sub-tile: two 32-row A tiles and 64 tokens
-  const int wr = wave & 3, wc = wave >> 2;
-  const int arow0 = MODE == 0 ? 32 * wr : 64 * wr;             // gate rows (MODE 0)
-  const int arow1 = MODE == 0 ? 128 + 32 * wr : 64 * wr + 32;  // up rows of the same features (MODE 0)
-  const int brow0 = 64 * wc;
+  const int drow = lane >> 2, dchunk = lane & 3;              // DMA: row in a 16-row block, chunk position
   const int col = lane & 31, rq = (lane >> 5) * 4;
 
-  // DMA sources of an item for this lane: A rows 32*wave + 8*q + lane/8
-  // (q < 4), B rows 16*wave + 8*q + lane/8 (q < 2), logical chunk
-  // (lane%8) ^ (row & 7).  The loads go through buffer resources (the
+  // DMA sources of an item for this lane: A rows 128*wave + 16*q + lane/4
+  // (q < 8), B rows 32*wave + 16*q + lane/4 (q < 2), logical chunk
+  // (lane%4) ^ ((row >> 1) & 3).  The loads go through buffer resources (the
   // expert's weight matrix and the activation matrix, byte offsets below
   // 2^31, checked by the host) rather than flat-global addresses: the
   // compiler's wait-count model treats a flat-global load into LDS as a
   // possible LDS access for as long as it is in flight, which would turn
   // every wait for LDS reads into a full drain.
-
-  const __amdgpu_buffer_rsrc_t rsrcB =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, 0x7fffffff, kBufferWord3);
   auto make_src = [&](const PfItem& it, PfSrc& sr) {
     sr.wa = a.w + (int64_t)it.e * wrows * K;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 32 * wave + 8 * q + lrow;
+    {
+      // rows 128*wave + 16*q + lane/4: in MODE 0 waves 0, 1 hold gate rows and
+      // waves 2, 3 the up rows of the same features; the swizzle depends on
+      // lane/4 only
+      const int row = 128 * wave + drow;
       int wrow;
       if (MODE == 0) {
-        const int f0 = it.tile * 128;
-        wrow = row < 128 ? f0 + row : a.I + f0 + (row - 128);
+        const int f0 = it.tile * 256;
+        wrow = row < 256 ? f0 + row : a.I + f0 + (row - 256);
       } else {
         wrow = it.tile * kPfRows + row;
       }
-      sr.offA[q] = wrow * K + ((lchunk ^ (row & 7)) << 4);
+      sr.offA = wrow * K + ((dchunk ^ ((drow >> 1) & 3)) << 4);
     }
     // token ids: padding slots read the block's last token (their results are dropped)
     const int32_t* ids = a.seg.sorted_ids + it.blk * kPfTok;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) sr.fb[q] = ids[min(16 * wave + 8 * q + lrow, it.ntok - 1)];
+    for (int q = 0; q < 2; ++q) sr.fb[q] = ids[min(32 * wave + 16 * q + drow, it.ntok - 1)];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sr.f[j] = ids[min(brow0 + 32 * j + col, it.ntok - 1)];
+    for (int j = 0; j < 4; ++j) sr.f[j] = ids[min(32 * j + col, it.ntok - 1)];
   };
   // B-row offsets from the token ids: kept apart from make_src so that the
   // wait for the ids falls where the offsets are first needed (the empty asm
@@ -250,11 +287,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   auto finish_src = [&](PfSrc& sr) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int row = 16 * wave + 8 * q + lrow;
+      const int row = 32 * wave + 16 * q + drow;
       int f = sr.fb[q];
       asm volatile("" : "+v"(f));
       const int brow = MODE == 0 ? f / a.top_k : f;
-      sr.offB[q] = brow * K + ((lchunk ^ (row & 7)) << 4);
+      sr.offB[q] = brow * K + ((dchunk ^ ((row >> 1) & 3)) << 4);
     }
   };
   // element-wise choice between two sources (a choice of struct address
@@ -262,50 +299,48 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   auto pick = [](bool first, const PfSrc& x, const PfSrc& y) {
     PfSrc r;
     r.wa = first ? x.wa : y.wa;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r.offA[q] = first ? x.offA[q] : y.offA[q];
+    r.offA = first ? x.offA : y.offA;
 #pragma unroll
     for (int q = 0; q < 2; ++q) r.offB[q] = first ? x.offB[q] : y.offB[q];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) r.f[j] = 0;
+    for (int q = 0; q < 2; ++q) r.fb[q] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.f[j] = 0;
     return r;
   };
+  const __amdgpu_buffer_rsrc_t rsrcB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, 0x7fffffff, kBufferWord3);
   auto issue = [&](const PfSrc& sr, int kstep, int slot) {  // DMA of one K-step into ring slot `slot`
     lds_u8* base = smem + slot * kPfStage;
     const int kb = kstep * kPfBK;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)sr.wa, (short)0, wrows * K, kBufferWord3);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (void __attribute__((address_space(3)))*)(base + (32 * wave + 8 * q) * kPfBK),
-                                               16, sr.offA[q], kb, 0, 0);
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (void __attribute__((address_space(3)))*)(base + (128 * wave + 16 * q) * kPfBK), 16, sr.offA,
+          kb + 16 * q * K, 0, 0);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrcB, (void __attribute__((address_space(3)))*)(base + kPfStageA + (16 * wave + 8 * q) * kPfBK), 16, sr.offB[q],
-          kb, 0, 0);
+          rsrcB, (void __attribute__((address_space(3)))*)(base + kPfStageA + (32 * wave + 16 * q) * kPfBK), 16,
+          sr.offB[q], kb, 0, 0);
   };
 
-  // fragment addresses within a stage: row l%32 of each tile, k-step ks uses
-  // chunks 4*ks + 2*(l/32) and +1
+  // fragment addresses within a stage: A tile i rows arow(i) + lane%32, B tile
+  // j rows 32*j + lane%32, chunks 2*(lane/32) + c.  Tiles differ by whole
+  // 32-row multiples, which leave the chunk swizzle unchanged, so a tile is a
+  // constant byte offset from the c-th base.
   const int fr = lane & 31, fc = (lane >> 5) * 2;
-  int offA0[2][2], offA1[2][2], offB0[2][2], offB1[2][2];
+  const int arow0 = MODE == 0 ? 64 * wave : 128 * wave;
+  int baseA[2], baseB[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      offA0[ks][c] = pf_swz(arow0 + fr, 4 * ks + fc + c);
-      offA1[ks][c] = pf_swz(arow1 + fr, 4 * ks + fc + c);
-      offB0[ks][c] = kPfStageA + pf_swz(brow0 + fr, 4 * ks + fc + c);
-      offB1[ks][c] = kPfStageA + pf_swz(brow0 + 32 + fr, 4 * ks + fc + c);
-    }
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  for (int c = 0; c < 2; ++c) {
+    baseA[c] = pf_swz(arow0 + fr, fc + c);
+    baseB[c] = kPfStageA + pf_swz(fr, fc + c);
+  }
+  // row offset of A tile i from arow0 (MODE 0: tiles 0, 1 gate, 2, 3 the up
+  // rows of the same features)
+  auto arow_off = [](int i) { return MODE == 0 ? (i & 1) * 32 + (i >> 1) * 256 : 32 * i; };
 
   // epilogue constants
   const float deq = MODE == 0 ? (*a.a_scale) * (*a.w_scale)
@@ -317,200 +352,201 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   make_src(cur, cs);
   finish_src(cs);
   int slot0 = 0;  // ring slot of the current item's first K-step
-  issue(cs, 0, 0);
+  issue(cs, 0, 0);  // steps 0..2 (each item's start issues its step 3)
   issue(cs, 1, 1);
+  issue(cs, 2, 2);
 
-  // Fragments of one 64-byte MFMA k-step for up to two token sub-tiles.
+  // Fragments of one K-step: the wave's four A tiles and up to four B tiles.
   struct Frags {
-    u32x4 a0[2], a1[2], b0[2], b1[2];
+    u32x4 a[4][2], b[4][2];
   };
-  // K-loop of the current item with NJ (0, 1 or 2) of the wave's 32-token
-  // sub-tiles multiplied; one version per NJ so that the loop body has no
-  // branches.  Software pipelined by half K-steps over two register sets:
-  // the LDS reads of one MFMA k-step are in flight while the MFMAs of the
-  // previous one run, so the LDS and matrix pipes overlap.
-  auto kloop = [&](auto nj_tag) {
+  PfItem nn = nxt;  // the item after the next (fetched during each item)
+  bool has_nn = false;
+  // One item with its NJ (1..4) 32-token tiles multiplied; one version per NJ
+  // so that the K-step body has no branches, each with its own accumulators
+  // and epilogue (a join of the versions' 256 accumulators would be copied
+  // out of AGPRs).  Fragments are double-buffered: the reads of step k+1 run
+  // while the MFMAs of step k do.  Each step's barrier follows this wave's
+  // wait for its loads of step k+1 (those of k+2 and k+3 may still be in
+  // flight); then step k+4 is loaded into the slot of step k, whose reads the
+  // barrier has just drained.
+  auto item = [&](auto nj_tag) {
     constexpr int NJ = decltype(nj_tag)::value;
-    auto slot = [&](int s) { return (slot0 + s) % kPfStages; };
-    auto read = [&](Frags& F, int s, int ks) {
-      const lds_u8* st = smem + slot(s) * kPfStage;
+    constexpr int NMF = 4 * NJ, NDS = 8 + 2 * NJ;
+    f32x16 acc[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    auto slot = [&](int k) { return (slot0 + k) % kPfStages; };
+    auto read = [&](Frags& F, int k) {
+      const lds_u8* st = smem + slot(k) * kPfStage;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        F.a0[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA0[ks][c]);
-        F.a1[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offA1[ks][c]);
-        F.b0[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB0[ks][c]);
-        if constexpr (NJ > 1) F.b1[c] = *(const __attribute__((address_space(3))) u32x4*)(st + offB1[ks][c]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          F.a[i][c] = *(const __attribute__((address_space(3))) u32x4*)(st + baseA[c] + arow_off(i) * kPfBK);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          F.b[j][c] = *(const __attribute__((address_space(3))) u32x4*)(st + baseB[c] + 32 * j * kPfBK);
       }
     };
     auto mma = [&](const Frags& F) {
-      acc[0][0] = mfma32_fp8(F.a0[0], F.a0[1], F.b0[0], F.b0[1], acc[0][0]);
-      acc[1][0] = mfma32_fp8(F.a1[0], F.a1[1], F.b0[0], F.b0[1], acc[1][0]);
-      if constexpr (NJ > 1) {
-        acc[0][1] = mfma32_fp8(F.a0[0], F.a0[1], F.b1[0], F.b1[1], acc[0][1]);
-        acc[1][1] = mfma32_fp8(F.a1[0], F.a1[1], F.b1[0], F.b1[1], acc[1][1]);
-      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32_fp8(F.a[i][0], F.a[i][1], F.b[j][0], F.b[j][1], acc[i][j]);
     };
-    // step s >= 1: wait for this wave's DMA of step s, barrier, DMA of step
-    // s+2 (of this item, else of the next)
-    auto sync = [&](int s) {
-      if (s + 1 < nk || has_next)
-        wait_vm<6>();
-      else
-        wait_vm<0>();
-      ring_barrier();  // every wave's step-s data is in LDS; slot (s+2)%3 is no longer read
-      const bool own = s + 2 < nk;
-      if (own || has_next) issue(pick(own, cs, ns), own ? s + 2 : s + 2 - nk, slot(s + 2));
-    };
-    // step 0 also loads the next item's token ids, ahead of the step-2 DMA
-    auto sync0 = [&]() {
-      wait_vm<6>();  // nk >= 2: step 1's loads follow step 0's
+    // Every K-step loads step k+3 of the ring: this item's, the next item's
+    // or, after the last item, a dummy copy of this item's first steps into
+    // a slot nothing reads again; so every wait is the same (the loads of the
+    // two following steps may be in flight) and every step has the same
+    // interleaved body.  The kernel drains these loads before it ends.
+    auto src_of = [&](int k) -> PfSrc { return pick(k < nk, cs, ns); };
+    auto kstep_of = [&](int k) { return k < nk ? k : k - nk; };
+    Frags F0, F1;
+    // item start: step 0 landed, load step 3 (of this item: nk >= 4)
+    wait_vm<2 * kPfDma>();
+    ring_barrier();
+    issue(cs, 3, slot(3));
+    make_src(nxt, ns);  // next item's token ids (unconditional: a conditional load would be copied at the join, waiting for it)
+    read(F0, 0);
+    // one K-step: multiply step k, read step k+1, load step k+4
+    auto body = [&](Frags& Fc, Frags& Fn, int k, const PfSrc& src, auto id_tag) {
+      constexpr int ID = decltype(id_tag)::value;
+      wait_vm<2 * kPfDma>();  // step k+1 landed; k+2 and k+3 may be in flight
       ring_barrier();
-      make_src(nxt, ns);  // unconditional: a conditional load would be copied at the join, waiting for it
-      if (2 < nk) {
-        issue(cs, 2, slot(2));  // independent of the token ids just requested
-      } else {
-        finish_src(ns);
-        if (has_next) issue(ns, 0, slot(2));
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      read(Fn, k + 1);
+      issue(src, kstep_of(k + 4), slot(k + 4));
+      mma(Fc);
+      pf_interleave<0, NMF, NDS, kPfDma, ID>();
+      __builtin_amdgcn_sched_barrier(0);
     };
-    if constexpr (NJ == 0) {
-      sync0();
-      int s = 1;
-      for (; s + 2 < nk; ++s) {
-        wait_vm<6>();
-        ring_barrier();
-        issue(cs, s + 2, slot(s + 2));
-      }
-      if (nk > 2) finish_src(ns);
-      for (; s < nk; ++s) sync(s);
-    } else {
-      Frags F0, F1;
-      sync0();
-      read(F0, 0, 0);
-      // The scheduling barriers keep each MFMA batch between the reads it is
-      // meant to overlap; the steady-state body is branch-free so that the
-      // compiler cannot sink the first batch into a join block.
-      int s = 0;
-      for (; s + 3 < nk; ++s) {
-        read(F1, s, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(F0);  // k-step 0 of step s
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<6>();    // this wave's DMA of step s+1 has landed
-        ring_barrier();  // also waits for the reads into F1
-        issue(cs, s + 3, slot(s + 3));
-        read(F0, s + 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(F1);  // k-step 1 of step s
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (nk > 2) finish_src(ns);
-      for (; s < nk; ++s) {  // the last (up to three) steps
-        read(F1, s, 1);
-        mma(F0);
-        if (s + 1 < nk) {
-          sync(s + 1);
-          read(F0, s + 1, 0);
-        }
-        mma(F1);
-      }
+    int s = 0;
+    for (; s + 4 < nk; s += 2) {  // steps loading this item's steps (nk is even)
+      body(F0, F1, s, cs, std::integral_constant<int, 0>{});
+      body(F1, F0, s + 1, cs, std::integral_constant<int, 1>{});
     }
-  };
+    if (!has_next) ns = cs;  // dummy source after the last item (valid addresses, never read)
+    finish_src(ns);          // the next item's token ids are needed from here on
+    for (; s + 2 < nk; s += 2) {  // steps loading the next item's first steps
+      body(F0, F1, s, src_of(s + 4), std::integral_constant<int, 2>{});
+      body(F1, F0, s + 1, src_of(s + 5), std::integral_constant<int, 3>{});
+    }
+    // last two steps: step nk-2 reads step nk-1 and loads the next item's
+    // step 2; step nk-1 only multiplies
+    body(F0, F1, nk - 2, ns, std::integral_constant<int, 4>{});
+    mma(F1);
 
-  while (true) {
-    const bool live0 = brow0 < cur.ntok, live1 = brow0 + 32 < cur.ntok;  // 32-token sub-tiles that hold tokens
-    if (live1)
-      kloop(std::integral_constant<int, 2>{});
-    else if (live0)
-      kloop(std::integral_constant<int, 1>{});
-    else
-      kloop(std::integral_constant<int, 0>{});
+    // The accumulators stay in AGPRs until the epilogue reads them tile by
+    // tile (otherwise the last MFMAs write all of them to VGPRs at once).
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // metadata of the item after the next, waited for at its first use
-    PfItem nn = nxt;
-    bool has_nn = false;
     if (has_next) {
       L += stride;
       has_nn = pf_next(a, nb, L, stride, nn);
     }
 
-    // epilogue (no LDS: the next item's first loads are landing in the ring)
+    // epilogue (no LDS: the next item's first loads are landing in the ring);
+    // one tile at a time, so that few accumulators are out of AGPRs at once
     if (MODE == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = brow0 + 32 * j + col;
+      for (int j = 0; j < NJ; ++j) {
+        const int t = 32 * j + col;
         if (t < cur.ntok) {
           const int f = cs.f[j];
-          const int fbase = cur.tile * 128 + 32 * wr;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float hv[4];
+          for (int i = 0; i < 2; ++i) {
+            const int fbase = cur.tile * 256 + 64 * wave + 32 * i;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float gt = acc[0][j][4 * g + q] * deq;
-              const float up = acc[1][j][4 * g + q] * deq;
-              hv[q] = gt / (1.0f + expf(-gt)) * up;
-              hmax = fmaxf(hmax, fabsf(hv[q]));
+            for (int g = 0; g < 4; ++g) {
+              float hv[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float gt = acc[i][j][4 * g + q] * deq;
+                const float up = acc[i + 2][j][4 * g + q] * deq;
+                hv[q] = silu_fast(gt) * up;
+                hmax = fmaxf(hmax, fabsf(hv[q]));
+              }
+              const int64_t idx = (int64_t)f * a.I + fbase + 8 * g + rq;
+              if (HDYN) {  // fp32, so that h is rounded once, to e4m3, after the amax is known
+                *(f32x4*)(a.out + idx * 4) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+              } else {
+                *(unsigned*)(a.out + idx) = pack_e4m3x4(hv[0] * rhs, hv[1] * rhs, hv[2] * rhs, hv[3] * rhs);
+              }
             }
-            const int64_t idx = (int64_t)f * a.I + fbase + 8 * g + rq;
-            if (HDYN) {
-              u32x2 o = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-              *(u32x2*)(a.out + idx * 2) = o;
-            } else {
-              *(unsigned*)(a.out + idx) = pack_e4m3x4(hv[0] * rhs, hv[1] * rhs, hv[2] * rhs, hv[3] * rhs);
-            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = brow0 + 32 * j + col;
+      for (int j = 0; j < NJ; ++j) {
+        const int t = 32 * j + col;
         if (t < cur.ntok) {
-          uint16_t* dst = (uint16_t*)a.out + (int64_t)cs.f[j] * a.H + (int64_t)cur.tile * kPfRows + 64 * wr;
+          uint16_t* dst = (uint16_t*)a.out + (int64_t)cs.f[j] * a.H + (int64_t)cur.tile * kPfRows + 128 * wave;
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const f32x16& c = acc[i][j];
-              u32x2 o = {pack_bf16x2(c[4 * g] * deq, c[4 * g + 1] * deq), pack_bf16x2(c[4 * g + 2] * deq, c[4 * g + 3] * deq)};
+              u32x2 o = {pack_bf16x2(c[4 * g] * deq, c[4 * g + 1] * deq),
+                         pack_bf16x2(c[4 * g + 2] * deq, c[4 * g + 3] * deq)};
               *(u32x2*)(dst + 32 * i + 8 * g + rq) = o;
             }
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  };
 
+  while (true) {
+    const int nj = (cur.ntok + 31) >> 5;  // 32-token tiles holding tokens (1..4)
+    if (nj == 4)
+      item(std::integral_constant<int, 4>{});
+    else if (nj == 3)
+      item(std::integral_constant<int, 3>{});
+    else if (nj == 2)
+      item(std::integral_constant<int, 2>{});
+    else
+      item(std::integral_constant<int, 1>{});
     if (!has_next) break;
     cur = nxt;
     cs = ns;
     nxt = nn;
     has_next = has_nn;
+    has_nn = false;
     slot0 = (slot0 + nk) % kPfStages;
   }
+  wait_vm<0>();  // the dummy loads after the last item
   if (MODE == 0 && HDYN) {
     hmax = wave_max(hmax);
     if (lane == 0) atomicMax(a.h_amax_out, __float_as_uint(hmax));
   }
 }
 
-// h (bf16, [P][I]) -> e4m3 with the dynamic scale amax/448; 16 per thread.
-__global__ __launch_bounds__(256) void prefill_quant_h_kernel(const uint16_t* __restrict__ h, int64_t n,
+// h (fp32, [P][I]) -> e4m3 with the dynamic scale amax/448; 16 per thread.
+__global__ __launch_bounds__(256) void prefill_quant_h_kernel(const float* __restrict__ h, int64_t n,
                                                               const unsigned* __restrict__ h_amax,
                                                               uint8_t* __restrict__ hq) {
   const float r = 1.0f / scale_from_amax(__uint_as_float(*h_amax));
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
   if (i >= n) return;
-  const u32x4 v0 = *(const u32x4*)(h + i), v1 = *(const u32x4*)(h + i + 8);
-  u32x4 o = {pack_e4m3x4(bf16_lo(v0[0]) * r, bf16_hi(v0[0]) * r, bf16_lo(v0[1]) * r, bf16_hi(v0[1]) * r),
-             pack_e4m3x4(bf16_lo(v0[2]) * r, bf16_hi(v0[2]) * r, bf16_lo(v0[3]) * r, bf16_hi(v0[3]) * r),
-             pack_e4m3x4(bf16_lo(v1[0]) * r, bf16_hi(v1[0]) * r, bf16_lo(v1[1]) * r, bf16_hi(v1[1]) * r),
-             pack_e4m3x4(bf16_lo(v1[2]) * r, bf16_hi(v1[2]) * r, bf16_lo(v1[3]) * r, bf16_hi(v1[3]) * r)};
+  const f32x4* src = (const f32x4*)(h + i);
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = src[q];
+    o[q] = pack_e4m3x4(v[0] * r, v[1] * r, v[2] * r, v[3] * r);
+  }
   *(u32x4*)(hq + i) = o;
 }
 

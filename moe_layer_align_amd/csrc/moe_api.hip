@@ -21,12 +21,14 @@ constexpr int kAlignBlockFused = 16;   // token tile of the decode products' B o
 constexpr int kPrefillMinPairs = 8192; // fp8 layers with at least this many pairs take the prefill products
 
 // fp8 layers with many pairs use the tiled prefill products (token block 128,
-// weight tiles of 256 rows: H a multiple of 256; at least two 128-byte
-// K-steps in both products).  Their operand loads take 32-bit byte offsets
-// into one expert's weights and into the activations.
+// weight tiles of 512 rows: H a multiple of 512 for the down product, I a
+// multiple of 256 for the gate/up product, whose tiles hold 256 gate and 256
+// up rows; both then have at least four 64-byte K-steps).  Their operand
+// loads take 32-bit byte offsets into one expert's weights and into the
+// activations.
 bool use_prefill(int M, int k, moe_dtype_t dt, int H, int I) {
   const int64_t P = (int64_t)M * k, lim = INT32_MAX;
-  return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0 && I >= 2 * kPfBK &&
+  return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0 && I % (kPfRows / 2) == 0 &&
          2 * (int64_t)I * H <= lim && (int64_t)M * H <= lim && P * I <= lim;
 }
 int align_block(int M, int k, moe_dtype_t dt, int H, int I) {
@@ -109,7 +111,8 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
   L.h_amax = take(4);
   const bool fp8 = dt == MOE_DTYPE_FP8_E4M3;
   L.xq = take(fp8 ? (size_t)M * H : 0);
-  L.h = take((size_t)P * I * (fp8 ? 4 : 2));
+  // h: bf16 (bf16 layers), fp32 (fp8 decode), fp32 + its e4m3 copy (fp8 prefill)
+  L.h = take((size_t)P * I * (fp8 ? (use_prefill(M, k, dt, H, I) ? 5 : 4) : 2));
   L.part = take((size_t)down_ksplit_cap(P, H, I, dt == MOE_DTYPE_FP8_E4M3) * (size_t)P * H * 4);
   L.total = off;
   return L;
@@ -442,19 +445,16 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   if ((rc = launch_status()) != MOE_OK) return rc;
 
   const PrefillSeg seg{o.sorted_ids, o.block_expert, o.offsets, o.counts, o.num_padded};
-  uint8_t* hq = hdyn ? h + (size_t)P * I * 2 : h;  // e4m3 h read by the down product
-  // work items: 8 XCDs x the raster groups that the largest possible block count needs
-  auto prefill_items = [&](int T) {
-    const int nbx = (int)cdiv(L.n_blocks, 8);
-    const int groups = (int)(cdiv(T, kPfGT) * cdiv(nbx, kPfGB));
-    return 8 * groups * kPfGT * kPfGB;
-  };
+  uint8_t* hq = hdyn ? h + (size_t)P * I * 4 : h;  // e4m3 h read by the down product (after the fp32 h)
+  // bound on the linear item index: 8 XCDs x tiles x the blocks per XCD that
+  // the largest possible block count gives
+  auto prefill_items = [&](int T) { return 8 * T * (int)cdiv(L.n_blocks, 8); };
   // persistent workgroups: one per CU, a multiple of 8 (one XCD each)
   int wgs = 0;
   if ((rc = persistent_wgs(&wgs)) != MOE_OK) return rc;
   rec(4);
   {
-    const int T = I / 128;  // 256-row tiles of W13: 128 gate + 128 up rows
+    const int T = I / (kPfRows / 2);  // 512-row tiles of W13: 256 gate + 256 up rows
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
                   a->h_scale, h, h_amax};
@@ -469,7 +469,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   {
     if (hdyn) {
       const int64_t n = P * I;
-      prefill_quant_h_kernel<<<(unsigned)cdiv(n, 4096), 256, 0, st>>>((const uint16_t*)h, n, h_amax, hq);
+      prefill_quant_h_kernel<<<(unsigned)cdiv(n, 4096), 256, 0, st>>>((const float*)h, n, h_amax, hq);
       if ((rc = launch_status()) != MOE_OK) return rc;
     }
     const int T = H / kPfRows;

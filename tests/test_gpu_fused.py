@@ -180,23 +180,24 @@ def prefill_w():
 # Tiled prefill products (fp8 with at least 8192 pairs) at sizes the oracle
 # evaluates quickly: Zipf routing leaves experts empty and blocks partial.
 def test_prefill_path_dynamic_scales_all_tokens():
-    # two 128-byte K-steps in both products: the shortest prefill K-loop
-    cfg = MoEConfig("pf_small", E=16, k=8, H=256, I=256, dtype="fp8", ms=(1100,), logits="zipf")
+    # smallest prefill shapes: one 512-row tile per product, four 64-byte
+    # K-steps in the down product
+    cfg = MoEConfig("pf_small", E=16, k=8, H=512, I=256, dtype="fp8", ms=(1100,), logits="zipf")
     compare(cfg, 1100, seed=11)
 
 
-def test_prefill_path_three_k_steps():
-    # down product with three K-steps: the next item's first loads are issued
-    # from the first tail step
-    cfg = MoEConfig("pf_k3", E=16, k=8, H=768, I=384, dtype="fp8", ms=(1100,), logits="zipf")
+def test_prefill_path_shortest_down_k():
+    # down product of four K-steps (no steady-state iteration: every step is
+    # a tail step that may load the next item), gate/up of 24
+    cfg = MoEConfig("pf_k4", E=16, k=8, H=1536, I=256, dtype="fp8", ms=(1100,), logits="zipf")
     compare(cfg, 1100, seed=13, tokens=[0, 1, 2, 3, 400, 401, 777, 1098, 1099])
 
 
 def test_prefill_path_many_items_per_workgroup():
-    # several hundred (tile, block) items per product: every persistent
-    # workgroup walks several of them with the LDS ring running across items
-    cfg = MoEConfig("pf_items", E=8, k=2, H=1024, I=1024, dtype="fp8", ms=(4096,), logits="zipf")
-    compare(cfg, 4096, seed=14, tokens=[0, 1, 2, 3, 100, 1000, 2047, 2048, 3000, 4093, 4094, 4095])
+    # several hundred (tile, block) items in both products: every persistent
+    # workgroup walks more than one with the LDS ring running across items
+    cfg = MoEConfig("pf_items", E=8, k=2, H=1024, I=1024, dtype="fp8", ms=(8192,), logits="zipf")
+    compare(cfg, 8192, seed=14, tokens=[0, 1, 2, 3, 100, 1000, 2047, 4096, 6000, 8189, 8190, 8191])
 
 
 def test_prefill_path_static_scales_long_k():
