@@ -14,15 +14,16 @@ would leave the caches full of dirty lines whose write-back then competes
 with the layer's reads, which no real model step does: the previous layers
 mostly read weights.)  The layer's time is the span
 between HIP events recorded on the launch stream right before its first
-kernel and right after its last one; the flush is outside the span.
+kernel and right after its last one, with no event in between (each adds a
+few microseconds); the flush is outside the span.
 
 value = expert-weight bytes of the experts that received tokens, summed over
 the sweep, divided by the summed layer spans (GB/s); for the prefill
 workload, real-pair flops 6*M*k*H*I over the span (TFLOP/s).  The roofline
 object covers the dominant kernel (the gate/up product): its algorithmic
-bytes (or flops) over its launch durations, both from HIP events around that
-launch inside the timed region.  The CPU oracle is timed on a bounded sample
-of the same workload.
+bytes (or flops) over its launch durations, from HIP events around that
+launch in a second timed pass of the same steps.  The CPU oracle is timed on
+a bounded sample of the same workload.
 
 Other workloads (--config qwen3|deepseek|prefill|tiny) print the same line
 for that layer; they are measurement aids, not the headline.
@@ -147,34 +148,39 @@ def main() -> int:
             run(c)
     torch.cuda.synchronize()
 
-    # Timed region: events only at the layer's start and end and around the
-    # gate/up launch (slots 0, 4, 5 and 9 of the library's stage events).
+    # Two timed passes of the same steps.  Pass A times the layer: events only
+    # at its start and end (slots 0 and 9 of the library's stage events; an
+    # event recorded between two kernels adds a few microseconds to the span).
+    # Pass B times the dominant kernel for the roofline: events only around
+    # the gate/up launch (slots 4 and 5).
     ns = moe.NUM_STAGES
-    timed_slots = (0, 4, 5, 2 * ns - 1)
-    evs = [[{i: torch.cuda.Event(enable_timing=True) for i in timed_slots} for _ in calls] for _ in range(args.steps)]
-    for step in evs:  # materialise the hipEvent_t handles
-        for per_call in step:
-            for e in per_call.values():
-                e.record(stream)
-    torch.cuda.synchronize()
-    handles = [[[per_call[i].cuda_event if i in per_call else None for i in range(2 * ns)] for per_call in step]
-               for step in evs]
 
-    log("timing %d steps" % args.steps)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        for j, c in enumerate(calls):
-            flush(s + j)
-            run(c, handles[s][j])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = t_start.elapsed_time(t_end)
+    def timed_pass(slots, label):
+        evs = [[{i: torch.cuda.Event(enable_timing=True) for i in slots} for _ in calls] for _ in range(args.steps)]
+        for step in evs:  # materialise the hipEvent_t handles
+            for per_call in step:
+                for e in per_call.values():
+                    e.record(stream)
+        torch.cuda.synchronize()
+        handles = [[[per_call[i].cuda_event if i in per_call else None for i in range(2 * ns)] for per_call in step]
+                   for step in evs]
+        log("timing %d steps (%s)" % (args.steps, label))
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(args.steps):
+            for j, c in enumerate(calls):
+                flush(s + j)
+                run(c, handles[s][j])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        a, b = slots
+        ms = [[evs[s][j][a].elapsed_time(evs[s][j][b]) for s in range(args.steps)] for j in range(len(calls))]
+        return ms, t0.elapsed_time(t1)
 
-    span_ms = [[evs[s][j][0].elapsed_time(evs[s][j][2 * ns - 1]) for s in range(args.steps)] for j in range(len(calls))]
-    g1_ms = [[evs[s][j][4].elapsed_time(evs[s][j][5]) for s in range(args.steps)] for j in range(len(calls))]
+    span_ms, wall_ms = timed_pass((0, 2 * ns - 1), "layer spans")
+    g1_ms, _ = timed_pass((4, 5), "gate/up launches")
     layer_ms_per_step = sum(sum(v) for v in span_ms) / args.steps
 
     # Per-stage breakdown, outside the timed region (all ten events per call).
