@@ -37,7 +37,8 @@ class MoEError(RuntimeError):
 class Tuning(ctypes.Structure):
     _fields_ = [("gemm1_ksplit", ctypes.c_int32), ("gemm2_ksplit", ctypes.c_int32),
                 ("token_tiles", ctypes.c_int32), ("unroll", ctypes.c_int32),
-                ("gemm2_wave_ksplit", ctypes.c_int32)]
+                ("gemm2_wave_ksplit", ctypes.c_int32), ("gemm1_stream_tiles", ctypes.c_int32),
+                ("gemm2_stream_tiles", ctypes.c_int32)]
 
 
 class _FusedArgs(ctypes.Structure):

@@ -261,6 +261,162 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
 }
 
 // --------------------------------------------------------------------------
+// Long-stream pipeline shared by the long-stream variants of both products.
+//
+// A wave walks T tiles of one expert over the same K range; tile j's A rows
+// start at pa[i] + j * tstride and the token operand (B) is the same for all
+// tiles.  The K loop of a tile has S stages of U MFMA k-steps; the stages of
+// all tiles form one flat sequence through a ring of NS register stages
+// (NS-1 stages of loads in flight while one is computed), so the first loads
+// of tile j+1 are in flight while tile j finishes and the pipeline ramps once
+// per T tiles.  Past the last stage the loads repeat the first stage (in
+// range, never used).  epi(j, acc) consumes and clears the accumulators of
+// tile j.
+// --------------------------------------------------------------------------
+template <int U>
+constexpr int stream_stages() { return U == 1 ? 4 : 3; }
+
+template <bool FP8, int NB, int U, int SB, typename Epi>
+__device__ __forceinline__ void stream_tiles(const uint8_t* const (&pa)[2], int64_t tstride, const uint8_t* const* pb,
+                                             int ntiles, int S, f32x4 (&acc)[2][NB], Epi&& epi) {
+  constexpr int SS = U * SB;
+  constexpr int NS = stream_stages<U>();
+  const int G = ntiles * S;
+  StageRegs<FP8, 2, NB, U> sr[NS];
+  int lj = 0, ls = 0;  // next stage to load
+  auto load_next = [&](StageRegs<FP8, 2, NB, U>& r) {
+    const bool in = lj < ntiles;
+    const int64_t ao = in ? (int64_t)lj * tstride + (int64_t)ls * SS : 0;
+    const int bo = in ? ls * SS : 0;
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      load_frag<FP8>(r.a[q][0], pa[0] + ao + q * SB);
+      load_frag<FP8>(r.a[q][1], pa[1] + ao + q * SB);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) load_frag<FP8>(r.b[q][t], pb[t] + bo + q * SB);
+    }
+    if (++ls == S) {
+      ls = 0;
+      ++lj;
+    }
+  };
+  int cj = 0, cs = 0;  // stage being computed
+  auto compute = [&](const StageRegs<FP8, 2, NB, U>& r) {
+    stage_mma<FP8, 2, NB, U>(r, acc);
+    if (++cs == S) {
+      epi(cj, acc);
+      cs = 0;
+      ++cj;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) load_next(sr[p]);
+  for (int g = 0; g < G; g += NS) {
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      load_next(sr[(p + NS - 1) % NS]);  // stage g + p + NS - 1
+      __builtin_amdgcn_sched_barrier(0);
+      if (p == 0 || g + p < G) compute(sr[p]);  // stage g + p
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Gate/up product, long-stream variant.  Wave w of the workgroup walks tw
+// feature tiles (tile f: gate rows 16f.. and up rows I+16f.. of W13[e])
+// ft0 + 4j, ft0 = 4*tw*blockIdx.x + w, over the whole K = H, so that the four
+// waves read 64 adjacent gate rows and their up partners at each point of the
+// stream.  Token rows and output slots are read once per wave.  No K split,
+// no LDS, no barrier.
+template <bool FP8, int HFMT, int NB, int U>
+__device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int seg, int cnt, int pass0, int tw) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int KSTEP = FP8 ? 128 : 32;
+  constexpr int LB = FP8 ? 32 : 16;
+  constexpr int SB = KSTEP * ESZ;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int ftiles = a.I >> 4;
+  const int ft0 = blockIdx.x * 4 * tw + wave;
+  if (ft0 >= ftiles) return;
+  const int ntw = min(tw, (ftiles - ft0 + 3) >> 2);
+
+  const int64_t rowb = (int64_t)a.H * ESZ;
+  const uint8_t* pa[2];
+  pa[0] = a.w13 + ((int64_t)e * 2 * a.I + ft0 * 16 + r16) * rowb + kq * LB;  // gate rows
+  pa[1] = pa[0] + (int64_t)a.I * rowb;                                        // up rows
+  const uint8_t* pb[NB];
+  int fo[NB];  // pair of the lane's token column, -1 past the expert's count
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const int slot = pass0 + t * 16 + r16;
+    const int f = a.seg.sorted_ids[seg + min(slot, cnt - 1)];
+    pb[t] = a.act + (int64_t)(f / a.top_k) * rowb + kq * LB;
+    fo[t] = slot < cnt ? f : -1;
+  }
+
+  const float deq = FP8 ? (*a.x_scale) * (*a.w_scale) : 1.0f;
+  float rh = 1.0f;
+  if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
+  float hmax = 0.0f;
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto epi = [&](int j, f32x4 (&c)[2][NB]) {
+    const int i0 = (ft0 + 4 * j) * 16;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      if (fo[t] >= 0) {
+        float hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = c[0][t][r] * deq;
+          const float u = c[1][t][r] * deq;
+          hv[r] = g / (1.0f + expf(-g)) * u;
+          hmax = fmaxf(hmax, fabsf(hv[r]));
+        }
+        const int64_t idx = (int64_t)fo[t] * a.I + i0 + kq * 4;
+        if constexpr (HFMT == H_BF16) {
+          u32x2 o = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+          *(u32x2*)(a.h + idx * 2) = o;
+        } else if constexpr (HFMT == H_F32) {
+          *(f32x4*)(a.h + idx * 4) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+        } else {
+          *(unsigned*)(a.h + idx) = pack_e4m3x4(hv[0] * rh, hv[1] * rh, hv[2] * rh, hv[3] * rh);
+        }
+      }
+      c[0][t] = c[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  stream_tiles<FP8, NB, U, SB>(pa, 64 * rowb, pb, ntw, a.H / KSTEP / U, acc, epi);
+  if constexpr (HFMT == H_F32) {
+    hmax = wave_max(hmax);
+    if (lane == 0) atomicMax(a.h_amax, __float_as_uint(hmax));
+  }
+}
+
+// Grid: x = chunks of 4*tw feature tiles, y = active expert, z = token pass.
+template <bool FP8, int HFMT, int NT, int U>
+__global__ __launch_bounds__(256) void gemm1_stream_kernel(Gemm1Args a, int tw) {
+  const int s = blockIdx.y;
+  if (s >= *a.seg.num_active) return;
+  const int e = a.seg.active[s];
+  const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
+  const int pass0 = blockIdx.z * NT * 16;
+  if (pass0 >= cnt) return;
+  const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
+  if constexpr (NT >= 4)
+    if (ntile == 4) return gemm1_stream_body<FP8, HFMT, 4, U>(a, e, seg, cnt, pass0, tw);
+  if constexpr (NT >= 3)
+    if (ntile == 3) return gemm1_stream_body<FP8, HFMT, 3, U>(a, e, seg, cnt, pass0, tw);
+  if constexpr (NT >= 2)
+    if (ntile == 2) return gemm1_stream_body<FP8, HFMT, 2, U>(a, e, seg, cnt, pass0, tw);
+  gemm1_stream_body<FP8, HFMT, 1, U>(a, e, seg, cnt, pass0, tw);
+}
+
+// --------------------------------------------------------------------------
 // Down product.
 //
 // Wave tile: 32 output rows (two 16-row MFMA tiles of W2[e]) over one K
@@ -295,6 +451,30 @@ struct Gemm2Args {
 // that the 16 token rows read by one instruction fall in different banks.
 __host__ __device__ constexpr int gemm2_lds_stride(int kw_bytes) { return kw_bytes + 16; }
 
+// Quantise the workgroup's token slice of fp32 h into LDS: NB*16 rows (token
+// slots pass0.., clamped to the expert's count) of Kw e4m3 bytes from column
+// kbeg, row stride gemm2_lds_stride(Kw).  All 256 threads take part; the
+// caller synchronises.
+template <int NB>
+__device__ __forceinline__ void stage_h_e4m3(const Gemm2Args& a, uint8_t* s_tok, int seg, int cnt, int pass0, int kbeg,
+                                             int Kw, float rh) {
+  const int stride = gemm2_lds_stride(Kw);
+  const int per_row = Kw / 16;  // 16 elements per thread-step
+  for (int idx = threadIdx.x; idx < NB * 16 * per_row; idx += 256) {
+    const int row = idx / per_row, c = (idx - row * per_row) * 16;
+    const int slot = min(pass0 + row, cnt - 1);
+    const int f = a.seg.sorted_ids[seg + slot];
+    const float* src = (const float*)a.h + (int64_t)f * a.I + kbeg + c;
+    const f32x4 v0 = *(const f32x4*)(src), v1 = *(const f32x4*)(src + 4);
+    const f32x4 v2 = *(const f32x4*)(src + 8), v3 = *(const f32x4*)(src + 12);
+    u32x4 q = {pack_e4m3x4(v0[0] * rh, v0[1] * rh, v0[2] * rh, v0[3] * rh),
+               pack_e4m3x4(v1[0] * rh, v1[1] * rh, v1[2] * rh, v1[3] * rh),
+               pack_e4m3x4(v2[0] * rh, v2[1] * rh, v2[2] * rh, v2[3] * rh),
+               pack_e4m3x4(v3[0] * rh, v3[1] * rh, v3[2] * rh, v3[3] * rh)};
+    *(u32x4*)(s_tok + row * stride + c) = q;
+  }
+}
+
 // Body for NB (<= NT) token tiles.  WKS waves of the workgroup split the
 // slice's K range and are summed through LDS (s_red); 4/WKS groups of 32 rows
 // per workgroup.
@@ -323,23 +503,7 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
     const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
     deq = sh * (*a.w_scale);
     if constexpr (QH) {
-      // quantise the workgroup's token slice into LDS: NB*16 rows of Kw bytes
-      const float rh = 1.0f / sh;
-      const int stride = gemm2_lds_stride(Kw);
-      const int per_row = Kw / 16;  // 16 elements per thread-step
-      for (int idx = threadIdx.x; idx < NB * 16 * per_row; idx += 256) {
-        const int row = idx / per_row, c = (idx - row * per_row) * 16;
-        const int slot = min(pass0 + row, cnt - 1);
-        const int f = a.seg.sorted_ids[seg + slot];
-        const float* src = (const float*)a.h + (int64_t)f * a.I + kbeg + c;
-        const f32x4 v0 = *(const f32x4*)(src), v1 = *(const f32x4*)(src + 4);
-        const f32x4 v2 = *(const f32x4*)(src + 8), v3 = *(const f32x4*)(src + 12);
-        u32x4 q = {pack_e4m3x4(v0[0] * rh, v0[1] * rh, v0[2] * rh, v0[3] * rh),
-                   pack_e4m3x4(v1[0] * rh, v1[1] * rh, v1[2] * rh, v1[3] * rh),
-                   pack_e4m3x4(v2[0] * rh, v2[1] * rh, v2[2] * rh, v2[3] * rh),
-                   pack_e4m3x4(v3[0] * rh, v3[1] * rh, v3[2] * rh, v3[3] * rh)};
-        *(u32x4*)(s_tok + row * stride + c) = q;
-      }
+      stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
       __syncthreads();
     }
   }
@@ -422,6 +586,99 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   if constexpr (NT >= 2)
     if (ntile == 2) return gemm2_body<FP8, HFMT, NT, 2, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
   gemm2_body<FP8, HFMT, NT, 1, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+}
+
+// Down product, long-stream variant.  Wave w of the workgroup walks tw tiles
+// of 32 output rows of W2[e] (tile rt0 + 4j, rt0 = 4*tw*blockIdx.x + w) over
+// the workgroup's K slice, the pipeline running on from tile to tile; the
+// token slice (quantised into LDS once per workgroup with a dynamic fp8 h
+// scale, else read from global memory) serves all of them.
+template <bool FP8, int HFMT, int NB, int U>
+__device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s_tok, int e, int seg, int cnt,
+                                                  int pass0, int kslice, int tw) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int KSTEP = FP8 ? 128 : 32;
+  constexpr int LB = FP8 ? 32 : 16;
+  constexpr int SB = KSTEP * ESZ;
+  constexpr int HSZ = HFMT == H_BF16 ? 2 : (HFMT == H_F32 ? 4 : 1);
+  constexpr bool QH = FP8 && HFMT == H_F32;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int Kw = a.I / a.ksplit;
+  const int kbeg = kslice * Kw;
+
+  float deq = 1.0f;
+  if constexpr (FP8) {
+    const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
+    deq = sh * (*a.w_scale);
+    if constexpr (QH) {
+      stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
+      __syncthreads();
+    }
+  }
+  const int rtiles = a.H >> 5;
+  const int rt0 = blockIdx.x * 4 * tw + wave;
+  if (rt0 >= rtiles) return;  // after the workgroup's only barrier
+  const int ntw = min(tw, (rtiles - rt0 + 3) >> 2);
+
+  const int64_t rowb = (int64_t)a.I * ESZ;
+  const uint8_t* pa[2];
+  pa[0] = a.w2 + ((int64_t)e * a.H + rt0 * 32 + r16) * rowb + (int64_t)kbeg * ESZ + kq * LB;
+  pa[1] = pa[0] + 16 * rowb;
+  const uint8_t* pb[NB];
+  int fo[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const int slot = pass0 + t * 16 + r16;
+    const int f = a.seg.sorted_ids[seg + min(slot, cnt - 1)];
+    fo[t] = slot < cnt ? f : -1;
+    if constexpr (QH)
+      pb[t] = s_tok + (t * 16 + r16) * gemm2_lds_stride(Kw) + kq * LB;
+    else
+      pb[t] = a.h + ((int64_t)f * a.I + kbeg) * HSZ + kq * LB;
+  }
+
+  float* part = a.part + (int64_t)kslice * a.P * a.H;
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto epi = [&](int j, f32x4 (&c)[2][NB]) {
+    const int n0 = (rt0 + 4 * j) * 32;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      if (fo[t] >= 0) {
+        float* dst = part + (int64_t)fo[t] * a.H + n0 + kq * 4;
+        *(f32x4*)dst = c[0][t] * deq;
+        *(f32x4*)(dst + 16) = c[1][t] * deq;
+      }
+      c[0][t] = c[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  stream_tiles<FP8, NB, U, SB>(pa, 128 * rowb, pb, ntw, Kw / KSTEP / U, acc, epi);
+}
+
+// Grid: x = chunks of 4*tw row tiles, y = active expert, z = K slice +
+// ksplit * token pass.
+template <bool FP8, int HFMT, int NT, int U>
+__global__ __launch_bounds__(256) void gemm2_stream_kernel(Gemm2Args a, int tw) {
+  extern __shared__ __align__(16) uint8_t s_tok[];
+  const int s = blockIdx.y;
+  if (s >= *a.seg.num_active) return;
+  const int e = a.seg.active[s];
+  const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
+  const int kslice = blockIdx.z % a.ksplit;
+  const int pass0 = (blockIdx.z / a.ksplit) * NT * 16;
+  if (pass0 >= cnt) return;
+  const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
+  if constexpr (NT >= 4)
+    if (ntile == 4) return gemm2_stream_body<FP8, HFMT, 4, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+  if constexpr (NT >= 3)
+    if (ntile == 3) return gemm2_stream_body<FP8, HFMT, 3, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+  if constexpr (NT >= 2)
+    if (ntile == 2) return gemm2_stream_body<FP8, HFMT, 2, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+  gemm2_stream_body<FP8, HFMT, 1, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
 }
 
 // LDS of a down-product workgroup: the K-split reduction buffer.

@@ -96,7 +96,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
   const int B = align_block(M, k, dt, H, I);
   L.capacity = align_capacity(P, E, B);
   L.n_blocks = (int)(L.capacity / B);
-  L.n_route_wg = (int)cdiv(M, 4);
+  L.n_route_wg = route_grid(M, dt == MOE_DTYPE_FP8_E4M3 ? (int64_t)M * H : 0);
   L.ids = take(P * 4);
   L.wts = take(P * 4);
   L.counts = take((size_t)E * 4);
@@ -125,8 +125,8 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
 // 4-token-tile variants keep a workgroup's registers high on purpose) over
 // high occupancy.
 struct Plan {
-  int nt1, passes1, u1, ks1;               // gate/up
-  int nt2, passes2, u2, ks2, wks2, lds2;   // down
+  int nt1, passes1, u1, ks1, tw1;          // gate/up (tw1 > 0: long-stream variant)
+  int nt2, passes2, u2, ks2, wks2, lds2, tw2;  // down (tw2 > 0: long-stream variant)
 };
 
 bool valid_u(bool fp8, int u) { return fp8 ? (u == 1 || u == 2) : (u == 2 || u == 4); }
@@ -136,6 +136,15 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, con
   const int kstep = fp8 ? 128 : 32;
   const int64_t P = (int64_t)M * k;
   const int n_act = (int)std::min<int64_t>(E, P);  // upper bound on experts with tokens
+  // long-stream variants: one wave per SIMD walking tiles*n_act/1024 tiles,
+  // taken when that is at most 8 (short K ranges, few tiles); otherwise the
+  // K-split variants, whose many short workgroups are as fast
+  const int ftiles = I / 16, rtiles = H / 32;
+  auto stream_tiles = [&](int tiles) {
+    const int64_t t = ((int64_t)n_act * tiles + 512) / 1024;
+    return t > 8 ? 0 : (int)std::max<int64_t>(1, t);
+  };
+  p->tw1 = p->tw2 = 0;
   if (fp8) {
     p->nt1 = M >= 8 ? 4 : 1;
     p->u1 = (p->nt1 == 4 && H < 4096) ? 1 : 2;
@@ -143,6 +152,10 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, con
     p->nt2 = 1;
     p->u2 = 1;
     p->wks2 = 1;
+    if (M >= 8) {
+      p->tw1 = stream_tiles(ftiles);
+      p->tw2 = stream_tiles(rtiles);
+    }
   } else {
     p->nt1 = p->nt2 = 2;
     p->u1 = p->u2 = 4;
@@ -167,6 +180,16 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, con
     if (!valid_wsplit(t->gemm2_wave_ksplit)) return MOE_ERR_UNSUPPORTED;
     p->wks2 = t->gemm2_wave_ksplit;
   }
+  for (int* tw : {&p->tw1, &p->tw2}) {
+    const int v = tw == &p->tw1 ? (t ? t->gemm1_stream_tiles : 0) : (t ? t->gemm2_stream_tiles : 0);
+    if (v > 16 || (v > 0 && !fp8)) return MOE_ERR_UNSUPPORTED;
+    if (v != 0) *tw = v > 0 ? v : 0;
+  }
+  if (p->tw1 > 0 && (H / kstep) % p->u1 != 0) {  // whole stages per row
+    if (t && t->unroll > 0) return MOE_ERR_UNSUPPORTED;
+    p->u1 = 1;
+  }
+  if (p->tw2 > 0) p->wks2 = 1;  // the long-stream down product does not split K over waves
   if ((H / p->ks1) % kstep != 0) return MOE_ERR_UNSUPPORTED;
   p->passes1 = (int)cdiv(M, p->nt1 * 16);
   p->passes2 = (int)cdiv(M, p->nt2 * 16);
@@ -174,20 +197,24 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, con
   // down: K slices in separate workgroups; each slice's K range must split
   // evenly over wks2 waves, and with a dynamic fp8 h scale the quantised
   // token slice must fit the workgroup's LDS.  Default: the fewest slices
-  // that give at least 1024 workgroups (4 per CU).
+  // that give at least 1024 workgroups (4 per CU), or 256 (one per CU) for
+  // the long-stream variant.
   const int nsteps2 = I / kstep;
   auto fits = [&](int ks) {
     if (nsteps2 % (ks * p->wks2) != 0) return false;
+    if (p->tw2 > 0 && (nsteps2 / ks) % p->u2 != 0) return false;
     const int64_t lds = (qh ? (int64_t)p->nt2 * 16 * gemm2_lds_stride(I / ks) : 0) + gemm2_red_bytes(p->nt2, p->wks2);
     return lds <= kDownLdsMax;
   };
   const int ks_cap = down_ksplit_cap(P, H, I, fp8);
-  const int64_t wgs_per_slice = (int64_t)(H / (32 * (4 / p->wks2))) * n_act * p->passes2;
+  const int64_t groups2 = p->tw2 > 0 ? cdiv(rtiles, 4 * p->tw2) : H / (32 * (4 / p->wks2));
+  const int64_t wgs_per_slice = groups2 * n_act * p->passes2;
   p->ks2 = 0;
+  const int64_t wgs_target = p->tw2 > 0 ? 256 : 1024;
   for (int ks = 1; ks <= ks_cap; ++ks) {
     if (!fits(ks)) continue;
     p->ks2 = ks;
-    if (wgs_per_slice * ks >= 1024) break;
+    if (wgs_per_slice * ks >= wgs_target) break;
   }
   if (t && t->gemm2_ksplit > 0) {
     const int ks = t->gemm2_ksplit;
@@ -237,6 +264,43 @@ bool g1_nt(int nt, int u, int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
   return false;
 }
 
+// long-stream variants (fp8)
+template <int HF, int NT>
+bool g1s_u(int u, int tw, dim3 g, hipStream_t st, const Gemm1Args& a) {
+  if (u == 1) gemm1_stream_kernel<true, HF, NT, 1><<<g, 256, 0, st>>>(a, tw);
+  else if (u == 2) gemm1_stream_kernel<true, HF, NT, 2><<<g, 256, 0, st>>>(a, tw);
+  else return false;
+  return true;
+}
+
+template <int HF>
+bool g1s_nt(int nt, int u, int tw, dim3 g, hipStream_t st, const Gemm1Args& a) {
+  switch (nt) {
+    case 1: return g1s_u<HF, 1>(u, tw, g, st, a);
+    case 2: return g1s_u<HF, 2>(u, tw, g, st, a);
+    case 4: return g1s_u<HF, 4>(u, tw, g, st, a);
+  }
+  return false;
+}
+
+template <int HF, int NT>
+bool g2s_u(int u, int tw, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+  if (u == 1) gemm2_stream_kernel<true, HF, NT, 1><<<g, 256, lds, st>>>(a, tw);
+  else if (u == 2) gemm2_stream_kernel<true, HF, NT, 2><<<g, 256, lds, st>>>(a, tw);
+  else return false;
+  return true;
+}
+
+template <int HF>
+bool g2s_nt(int nt, int u, int tw, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
+  switch (nt) {
+    case 1: return g2s_u<HF, 1>(u, tw, g, lds, st, a);
+    case 2: return g2s_u<HF, 2>(u, tw, g, lds, st, a);
+    case 4: return g2s_u<HF, 4>(u, tw, g, lds, st, a);
+  }
+  return false;
+}
+
 template <bool FP8, int HF, int NT, int U, int WKS>
 void launch_g2(dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
   gemm2_decode_kernel<FP8, HF, NT, U, WKS><<<g, 256, lds, st>>>(a);
@@ -276,16 +340,18 @@ bool g2_nt(int nt, int u, int wks, dim3 g, size_t lds, hipStream_t st, const Gem
 
 bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float* wts, const RouteFusedArgs& fa,
                   hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(M, 4));
-  const int npl = (int)cdiv(E, 64);
-  if (npl <= 1)
-    route_topk_kernel<1><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
-  else if (npl <= 2)
-    route_topk_kernel<2><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
-  else if (npl <= 4)
-    route_topk_kernel<4><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
-  else
-    route_topk_kernel<8><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+  const dim3 grid((unsigned)route_grid(M, fa.x_amax_part ? (int64_t)M * fa.H : 0));
+  switch ((int)cdiv(E, 16)) {  // keys per lane, rounded up to a power of two
+    case 1: route_topk_kernel<1><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
+    case 2: route_topk_kernel<2><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
+    case 3: case 4: route_topk_kernel<4><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
+    case 5: case 6: case 7: case 8: route_topk_kernel<8><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
+    default:
+      if (E <= 256)
+        route_topk_kernel<16><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+      else
+        route_topk_kernel<32><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+  }
   return true;
 }
 
@@ -323,15 +389,18 @@ void launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
 
 void launch_prologue_small(const float* logits, int M, int E, int k, int32_t* ids, float* wts, int B,
                            const AlignOut& o, const SmallQuant& q, hipStream_t st) {
-  const int npl = (int)cdiv(E, 64), lb = log2i(B), ib = log2i(E);
-  if (npl <= 1)
-    prologue_small_kernel<1><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
-  else if (npl <= 2)
-    prologue_small_kernel<2><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
-  else if (npl <= 4)
-    prologue_small_kernel<4><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
-  else
-    prologue_small_kernel<8><<<1, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+  const int lb = log2i(B), ib = log2i(E);
+  const dim3 grid(1 + (q.xq ? (unsigned)cdiv((int64_t)M * q.H, kSmallQuantPerWg) : 0u));
+  switch ((int)cdiv(E, 16)) {
+    case 1: prologue_small_kernel<1><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q); break;
+    case 2: prologue_small_kernel<2><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q); break;
+    case 3: case 4: prologue_small_kernel<4><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q); break;
+    case 5: case 6: case 7: case 8:
+      prologue_small_kernel<8><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+      break;
+    default:  // E <= kSmallMaxExperts
+      prologue_small_kernel<16><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+  }
 }
 
 void launch_align(const int32_t* ids, int64_t P, int E, int B, const AlignOut& o, const QuantXArgs& q, int n_quant_wg,
@@ -362,7 +431,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -546,7 +615,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
              num_active, L.n_blocks};
   if (prefill)
     return prefill_forward(a, st, ev, L, ws, ids, wts, o, xamax_part, scale_slot, h_amax, xq, h, part, hdyn);
-  const bool small = P <= kSmallPairs && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
+  const bool small = P <= kSmallPairs && E <= kSmallMaxExperts && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
   if (small) {
     // 1+2. routing, align (and fp8 activation quantisation) in one workgroup
     rec(0);
@@ -579,7 +648,12 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
       q.scale_slot = scale_slot;
       n_quant = (int)cdiv(q.n, 256 * 16);
     }
-    launch_align(ids, P, E, kAlignBlockFused, o, q, n_quant, st);
+    if (P <= kSmallPairs) {  // one 1024-thread align workgroup, 16K-element quantising workgroups
+      const unsigned g = 1 + (fp8 ? (unsigned)cdiv(q.n, kSmallQuantPerWg) : 0u);
+      align_small_kernel<<<g, 1024, 0, st>>>(ids, (int)P, E, log2i(kAlignBlockFused), log2i(E), o, q);
+    } else {
+      launch_align(ids, P, E, kAlignBlockFused, o, q, n_quant, st);
+    }
     rec(3);
     if ((rc = launch_status()) != MOE_OK) return rc;
   }
@@ -595,7 +669,11 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     const int tpw = 4 / plan.ks1;
     const dim3 grid((unsigned)(I / 16 / tpw), (unsigned)n_act, (unsigned)plan.passes1);
     bool ok;
-    if (!fp8)
+    if (plan.tw1 > 0) {
+      const dim3 gs((unsigned)cdiv(I / 16, 4 * plan.tw1), (unsigned)n_act, (unsigned)plan.passes1);
+      ok = hdyn ? g1s_nt<H_F32>(plan.nt1, plan.u1, plan.tw1, gs, st, g)
+                : g1s_nt<H_E4M3>(plan.nt1, plan.u1, plan.tw1, gs, st, g);
+    } else if (!fp8)
       ok = g1_nt<false, H_BF16>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
     else if (hdyn)
       ok = g1_nt<true, H_F32>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
@@ -613,7 +691,11 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
                 (int)P};
     const dim3 grid((unsigned)(H / (32 * (4 / plan.wks2))), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
     bool ok;
-    if (hf == H_BF16)
+    if (plan.tw2 > 0) {
+      const dim3 gs((unsigned)cdiv(H / 32, 4 * plan.tw2), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
+      ok = hf == H_F32 ? g2s_nt<H_F32>(plan.nt2, plan.u2, plan.tw2, gs, plan.lds2, st, g)
+                       : g2s_nt<H_E4M3>(plan.nt2, plan.u2, plan.tw2, gs, 0, st, g);
+    } else if (hf == H_BF16)
       ok = g2_nt<false, H_BF16>(plan.nt2, plan.u2, plan.wks2, grid, 0, st, g);
     else if (hf == H_F32)
       ok = g2_nt<true, H_F32>(plan.nt2, plan.u2, plan.wks2, grid, plan.lds2, st, g);

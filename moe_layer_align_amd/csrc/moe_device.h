@@ -61,27 +61,71 @@ __device__ __forceinline__ unsigned pack_e4m3x4(float a, float b, float c, float
 __device__ __forceinline__ float scale_from_amax(float amax) { return amax > 0.0f ? amax / kE4m3Max : 1.0f; }
 
 // ---------------------------------------------------------------- reductions
+// Wavefront reductions by DPP lane moves (gfx9 controls): two quad
+// permutations, the half-row and row mirrors leave every lane of a 16-lane row
+// with the row's result; the two row broadcasts fold rows 0+1 into row 1 and
+// rows 0..3 into row 3, so lane 63 ends with the wave's result, which
+// readlane makes uniform.  Each step is a VALU operation on the same lane
+// (a few cycles), where a ds_bpermute shuffle costs an LDS round trip.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i of each 8-lane half-row <- lane 7-i
+constexpr int kDppMirror = 0x140;     // lane i of each row <- lane 15-i
+constexpr int kDppBcast15 = 0x142;    // rows 1 and 3 <- lane 15 of rows 0 and 2 (row mask 0xA)
+constexpr int kDppBcast31 = 0x143;    // rows 2 and 3 <- lane 31 (row mask 0xC)
+
+// Lanes outside ROWS keep their own value.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ unsigned dpp_u32(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ float lane63_f32(float v) {
+  return __uint_as_float((unsigned)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppBcast15, 0xA>(v));
+  v = fmaxf(v, dpp_f32<kDppBcast31, 0xC>(v));
+  return lane63_f32(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  v += dpp_f32<kDppBcast15, 0xA>(v);
+  v += dpp_f32<kDppBcast31, 0xC>(v);
+  return lane63_f32(v);
+}
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ unsigned long long max_dpp_u64(unsigned long long k) {
+  const unsigned lo = dpp_u32<CTRL, ROWS>((unsigned)k), hi = dpp_u32<CTRL, ROWS>((unsigned)(k >> 32));
+  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+  return o > k ? o : k;
 }
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    unsigned lo = __shfl_xor((unsigned)k, off);
-    unsigned hi = __shfl_xor((unsigned)(k >> 32), off);
-    unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    k = o > k ? o : k;
-  }
-  return k;
+  k = max_dpp_u64<kDppXor1>(k);
+  k = max_dpp_u64<kDppXor2>(k);
+  k = max_dpp_u64<kDppHalfMirror>(k);
+  k = max_dpp_u64<kDppMirror>(k);
+  k = max_dpp_u64<kDppBcast15, 0xA>(k);
+  k = max_dpp_u64<kDppBcast31, 0xC>(k);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)k, 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(k >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -7,15 +7,17 @@
 namespace moe {
 
 // --------------------------------------------------------------------------
-// Router: one wavefront per token.
+// Router: four tokens per wavefront, one per 16-lane row.
 //
-// Each lane holds NPL logits (experts lane, lane+64, ...).  A logit becomes a
-// 64-bit key: high word = order-preserving image of the float (with -0.0
-// mapped to +0.0 first), low word = ~expert, so the largest key is the
-// largest logit and, among equal logits, the lowest expert.  k rounds of a
-// wavefront max-reduction pick the top-k in decreasing order; the winner's
-// key is cleared after each round.  Keys of absent experts are 0, below every
-// finite logit.
+// Lane l of a row holds the logits of experts l, l+16, ... of the row's
+// token as 64-bit keys: high word = order-preserving image of the float (with
+// -0.0 mapped to +0.0 first), low word = ~expert, so the largest key is the
+// largest logit and, among equal logits, the lowest expert.  Each of the k
+// rounds takes the row's largest key with four DPP steps that stay inside the
+// row (every lane of the row ends with it), records it and clears it; k
+// rounds give the top-k in decreasing order.  Keys of absent experts are 0,
+// below every finite logit.  Rows serve independent tokens, so one wave
+// routes four tokens with the instructions of one.
 // --------------------------------------------------------------------------
 __device__ __forceinline__ unsigned float_order_key(float v) {
   unsigned u = (v == 0.0f) ? 0u : __float_as_uint(v);
@@ -27,6 +29,8 @@ __device__ __forceinline__ float float_from_order_key(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+constexpr int kRouteRows = 4;  // tokens per wave (16-lane rows)
+
 struct RouteFusedArgs {
   const uint16_t* x;     // [M,H] bf16, for the activation amax (may be null)
   int H;
@@ -34,87 +38,96 @@ struct RouteFusedArgs {
   unsigned* h_amax;      // global amax of |h| to clear (may be null)
 };
 
-// Top-k of one token by the 64 lanes of a wave, from the lane's NPL logits
-// (experts lane, lane+64, ...; absent experts hold any value and are masked
-// by E); lane j < K returns the j-th expert in *e_out and its softmax weight
-// in *w_out.
+// Top-k of the token whose logits row is `row` (null for a row without a
+// token: its keys are all 0 and its results are meaningless).  l16 is the
+// lane's index in its row; lane j < K of the row returns the j-th expert in
+// *e_out and its softmax weight (over the k selected logits) in *w_out.
+// NPL = ceil(E/16) keys per lane.  All 64 lanes must be active.
 template <int NPL>
-__device__ __forceinline__ void route_select(const float (&v)[NPL], int E, int K, int lane, int* e_out, float* w_out) {
+__device__ __forceinline__ void route_row(const float* __restrict__ row, int E, int K, int l16, int* e_out,
+                                          float* w_out) {
   unsigned long long key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? (((unsigned long long)float_order_key(v[i]) << 32) | (unsigned)(~(unsigned)e)) : 0ull;
+    const int e = l16 + 16 * i;
+    key[i] = (row && e < E) ? (((unsigned long long)float_order_key(row[e]) << 32) | (unsigned)(~(unsigned)e)) : 0ull;
   }
   int my_e = 0;
-  float my_v = 0.0f;
-  float top_v = 0.0f;
+  float my_v = 0.0f, top_v = 0.0f;
   for (int j = 0; j < K; ++j) {
     unsigned long long best = key[0];
 #pragma unroll
     for (int i = 1; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
+    best = max_dpp_u64<kDppXor1>(best);
+    best = max_dpp_u64<kDppXor2>(best);
+    best = max_dpp_u64<kDppHalfMirror>(best);
+    best = max_dpp_u64<kDppMirror>(best);
     const int e = (int)(~(unsigned)best);
     const float val = float_from_order_key((unsigned)(best >> 32));  // no dependent memory access
     if (j == 0) top_v = val;
-    if (lane == j) {
+    if (l16 == j) {
       my_e = e;
       my_v = val;
     }
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + 64 * i == e) key[i] = 0ull;
+      if (l16 + 16 * i == e) key[i] = 0ull;
   }
-  const float ex = (lane < K) ? expf(my_v - top_v) : 0.0f;
-  const float sum = wave_sum(ex);
+  float ex = (l16 < K) ? expf(my_v - top_v) : 0.0f;
+  float sum = ex;
+  sum += dpp_f32<kDppXor1>(sum);
+  sum += dpp_f32<kDppXor2>(sum);
+  sum += dpp_f32<kDppHalfMirror>(sum);
+  sum += dpp_f32<kDppMirror>(sum);
   *e_out = my_e;
   *w_out = ex / sum;
 }
 
-template <int NPL>
-__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[NPL]) {
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) v[i] = (lane + 64 * i < E) ? row[lane + 64 * i] : 0.0f;
-}
+// Workgroup b routes tokens [16b, 16b+16) (when below M) and, with
+// fa.x_amax_part, takes the amax of |x| over elements
+// [b*kRouteAmaxChunk, (b+1)*kRouteAmaxChunk) of x, eight 16-byte loads in
+// flight per thread; the grid covers both ranges (route_grid).
+constexpr int kRouteAmaxChunk = 256 * 8 * 8;
 
-template <int NPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int K, int lane, int* e_out,
-                                            float* w_out) {
-  float v[NPL];
-  load_logits<NPL>(row, E, lane, v);
-  route_select<NPL>(v, E, K, lane, e_out, w_out);
+__host__ __device__ inline int route_grid(int M, int64_t x_elems) {
+  const int64_t r = (M + 4 * kRouteRows - 1) / (4 * kRouteRows);
+  const int64_t q = (x_elems + kRouteAmaxChunk - 1) / kRouteAmaxChunk;
+  return (int)(r > q ? r : q);
 }
 
 template <int NPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int M, int E, int K,
                                                          int32_t* __restrict__ ids, float* __restrict__ wts,
                                                          RouteFusedArgs fa) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int m = blockIdx.x * 4 + wave;
-  __shared__ float s_amax[4];
-  float amax = 0.0f;
-  if (m < M) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int m0 = blockIdx.x * (4 * kRouteRows);
+  if (m0 < M) {  // uniform over the workgroup
+    const int m = m0 + wave * kRouteRows + (lane >> 4);
     int e;
     float w;
-    route_token<NPL>(logits + (int64_t)m * E, E, K, lane, &e, &w);
-    if (lane < K) {
-      ids[(int64_t)m * K + lane] = e;
-      wts[(int64_t)m * K + lane] = w;
-    }
-    if (fa.x_amax_part) {
-      const uint16_t* xr = fa.x + (int64_t)m * fa.H;
-      for (int t = lane * 8; t < fa.H; t += 64 * 8) {
-        u32x4 v = *(const u32x4*)(xr + t);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          amax = fmaxf(amax, fabsf(bf16_lo(v[q])));
-          amax = fmaxf(amax, fabsf(bf16_hi(v[q])));
-        }
-      }
+    route_row<NPL>(m < M ? logits + (int64_t)m * E : nullptr, E, K, l16, &e, &w);
+    if (m < M && l16 < K) {
+      ids[(int64_t)m * K + l16] = e;
+      wts[(int64_t)m * K + l16] = w;
     }
   }
   if (fa.x_amax_part) {
+    __shared__ float s_amax[4];
+    const int64_t n = (int64_t)M * fa.H;  // multiple of 8
+    const int64_t base = (int64_t)blockIdx.x * kRouteAmaxChunk + threadIdx.x * 8;
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = base + u * 256 * 8;
+      v[u] = *(const u32x4*)(fa.x + (i < n ? i : 0));  // in-range address; counted only when i < n
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (base + u * 256 * 8 < n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[u][q])), fabsf(bf16_hi(v[u][q]))));
     amax = wave_max(amax);
     if (lane == 0) s_amax[wave] = amax;
     __syncthreads();
@@ -162,34 +175,41 @@ struct QuantXArgs {
   int first_wg;              // first workgroup index of the quantisation part
 };
 
-// x -> e4m3 with the per-tensor scale (static, or amax/448 from the router's
-// per-workgroup partial maxima).  16 elements per thread.
-__device__ void quant_x_part(const QuantXArgs& q, int wg) {
-  __shared__ float s_red[4];
-  float s;
-  if (q.static_scale) {
-    s = *q.static_scale;
-  } else {
-    float a = 0.0f;
-    for (int i = threadIdx.x; i < q.n_part; i += 256) a = fmaxf(a, q.amax_part[i]);
-    a = wave_max(a);
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = a;
-    __syncthreads();
-    a = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    s = scale_from_amax(a);
-  }
-  if (wg == 0 && threadIdx.x == 0) *q.scale_slot = s;
-  const float r = 1.0f / s;
-  const int64_t i = ((int64_t)wg * 256 + threadIdx.x) * 16;
-  if (i >= q.n) return;
-  u32x4 a0 = *(const u32x4*)(q.x + i);
-  u32x4 a1 = *(const u32x4*)(q.x + i + 8);
+// Sixteen bf16 (two 16-byte words) -> sixteen e4m3 bytes, scaled by r.
+__device__ __forceinline__ u32x4 quant16_e4m3(const u32x4& a0, const u32x4& a1, float r) {
   u32x4 o;
   o[0] = pack_e4m3x4(bf16_lo(a0[0]) * r, bf16_hi(a0[0]) * r, bf16_lo(a0[1]) * r, bf16_hi(a0[1]) * r);
   o[1] = pack_e4m3x4(bf16_lo(a0[2]) * r, bf16_hi(a0[2]) * r, bf16_lo(a0[3]) * r, bf16_hi(a0[3]) * r);
   o[2] = pack_e4m3x4(bf16_lo(a1[0]) * r, bf16_hi(a1[0]) * r, bf16_lo(a1[1]) * r, bf16_hi(a1[1]) * r);
   o[3] = pack_e4m3x4(bf16_lo(a1[2]) * r, bf16_hi(a1[2]) * r, bf16_lo(a1[3]) * r, bf16_hi(a1[3]) * r);
-  *(u32x4*)(q.xq + i) = o;
+  return o;
+}
+
+// x -> e4m3 with the per-tensor scale (static, or amax/448 from the router's
+// per-workgroup partial maxima), by a workgroup of NT threads, 16 elements
+// per thread.
+template <int NT>
+__device__ void quant_x_part(const QuantXArgs& q, int wg) {
+  __shared__ float s_red[NT / 64];
+  float s;
+  if (q.static_scale) {
+    s = *q.static_scale;
+  } else {
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < q.n_part; i += NT) a = fmaxf(a, q.amax_part[i]);
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) a = fmaxf(a, s_red[w]);
+    s = scale_from_amax(a);
+  }
+  if (wg == 0 && threadIdx.x == 0) *q.scale_slot = s;
+  const float r = 1.0f / s;
+  const int64_t i = ((int64_t)wg * NT + threadIdx.x) * 16;
+  if (i >= q.n) return;
+  *(u32x4*)(q.xq + i) = quant16_e4m3(*(const u32x4*)(q.x + i), *(const u32x4*)(q.x + i + 8), r);
 }
 
 // Exclusive scan of v over up to 512 entries held two per thread (256 threads).
@@ -210,7 +230,7 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
                                                     int log2B, int id_bits, int n_align_wgs, AlignOut o,
                                                     QuantXArgs q) {
   if ((int)blockIdx.x >= n_align_wgs) {
-    quant_x_part(q, blockIdx.x - n_align_wgs);
+    quant_x_part<256>(q, blockIdx.x - n_align_wgs);
     return;
   }
   __shared__ int s_total[kMaxExperts];
@@ -334,11 +354,14 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
 
 
 // --------------------------------------------------------------------------
-// Decode prologue in one workgroup of 1024 threads (16 waves), for token
-// counts whose pairs fit one workgroup (M*K <= 1024): routing, the stable
-// sort-and-pad by expert (block 16) and, in fp8 mode, the per-tensor
-// activation scale and the e4m3 quantisation of x.  One launch replaces the
-// router and align launches; no workgroup waits for another.
+// Decode prologue: one launch of 1024-thread workgroups for token counts
+// whose pairs fit one workgroup (M*K <= 1024) and at most 256 experts.  Workgroup 0 routes the tokens
+// and does the stable sort-and-pad by expert (block 16); in fp8 mode
+// workgroups 1..Q quantise x to e4m3, 16K elements each.  Each quantising
+// workgroup first takes the per-tensor amax over all of x by itself (packed
+// 16-bit maxima of the bf16 magnitudes, a short read of at most
+// kSmallQuantElems elements that the first workgroup brings into L2), so no
+// workgroup waits for another.
 //
 // Align here: wave w owns the pairs [64w, 64w+64).  A match over the bits of
 // the expert id gives each pair its rank among the wave's pairs of the same
@@ -346,8 +369,9 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
 // scan over experts of the padded counts give every pair its position.
 // --------------------------------------------------------------------------
 constexpr int kSmallPairs = 1024;
-constexpr int kSmallQuantChunks = 8;                                 // 8-element chunks of x per thread
-constexpr int64_t kSmallQuantElems = 1024LL * 8 * kSmallQuantChunks;  // largest M*H quantised here
+constexpr int kSmallMaxExperts = 256;            // 16 keys per lane of the 1024-thread workgroup
+constexpr int kSmallQuantPerWg = 1024 * 16;        // elements quantised per workgroup
+constexpr int64_t kSmallQuantElems = 1LL << 17;    // largest M*H of this path (amax read per workgroup)
 
 struct SmallQuant {
   const uint16_t* x;          // [M,H] bf16
@@ -358,91 +382,78 @@ struct SmallQuant {
   unsigned* h_amax;           // cleared when non-null
 };
 
-template <int NPL>
-__global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __restrict__ logits, int M, int E, int K,
-                                                              int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                              int log2B, int id_bits, AlignOut o, SmallQuant q) {
-  __shared__ int s_ids[kSmallPairs];
-  __shared__ int s_wc[16][kMaxExperts];   // per (wave, expert): group size, then start within the expert
-  __shared__ int s_tot[kMaxExperts];
-  __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_act[kMaxExperts + 1];
-  __shared__ int s_scan[16];
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Quantising workgroup qb of the prologue (1024 threads).
+__device__ __forceinline__ void prologue_quant(const SmallQuant& q, int64_t nx, int qb) {
   __shared__ float s_red[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int P = M * K;
+  float s;
+  if (q.static_scale) {
+    s = *q.static_scale;
+  } else {
+    // |bf16| ordering is the ordering of the low 15 bits as integers
+    u16x2 m2 = {0, 0};
+    for (int64_t i0 = (int64_t)tid * 8; i0 < nx; i0 += 4 * 8192) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u * 8192;
+        v[u] = *(const u32x4*)(q.x + (i < nx ? i : 0));  // in-range address; counted only when i < nx
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const unsigned keep = (i0 + u * 8192 < nx) ? 0x7fff7fffu : 0u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, v[u][c] & keep));
+      }
+    }
+    float a = __uint_as_float((unsigned)max(m2[0], m2[1]) << 16);
+    a = wave_max(a);
+    if (lane == 0) s_red[wave] = a;
+    __syncthreads();
+    a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) a = fmaxf(a, s_red[w]);
+    s = scale_from_amax(a);
+  }
+  if (qb == 0 && tid == 0) *q.scale_slot = s;
+  const float r = 1.0f / s;
+  const int64_t i = (int64_t)qb * kSmallQuantPerWg + (int64_t)tid * 16;
+  if (i >= nx) return;
+  *(u32x4*)(q.xq + i) = quant16_e4m3(*(const u32x4*)(q.x + i), *(const u32x4*)(q.x + i + 8), r);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: row shifts by
+// 1, 2, 4 and 8 (lanes without a source add 0) scan each 16-lane row, then
+// the two row broadcasts carry the totals of rows 0, 0+1 and 2 forward.
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast31, 0xC, 0xF, false);
+  return v;
+}
+
+// LDS of the one-workgroup align.
+struct SmallAlignLds {
+  int wc[16][kMaxExperts];  // per (wave, expert): group size, then start within the expert
+  int tot[kMaxExperts];
+  int off[kMaxExperts + 1];
+  int act[kMaxExperts + 1];
+  int scan[16];
+};
+
+// Stable sort-and-pad of P <= 1024 pairs with valid expert ids by one
+// 1024-thread workgroup.  Requires L.wc zeroed and ids[0..P) in LDS, both
+// before a barrier.
+__device__ __forceinline__ void small_align(const int* s_ids, int P, int E, int log2B, int id_bits, const AlignOut& o,
+                                            SmallAlignLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = 1 << log2B;
-
-  // fp8: x is read once into registers (at most kSmallQuantChunks 8-element
-  // chunks per thread), before the routing so that the loads overlap it
-  constexpr int QC = kSmallQuantChunks;
-  u32x4 xv[QC];
-  const int64_t nx = q.xq ? (int64_t)M * q.H : 0;
-#pragma unroll
-  for (int c = 0; c < QC; ++c) {
-    const int64_t i = ((int64_t)c * 1024 + tid) * 8;
-    xv[c] = i < nx ? *(const u32x4*)(q.x + i) : u32x4{0u, 0u, 0u, 0u};
-  }
-  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&s_wc[0][0])[i] = 0;
-  // routing: all of the wave's logits rows are loaded before the first top-k
-  {
-    for (int m0 = wave; m0 < M; m0 += 16 * 4) {
-      float rows[4][NPL];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int m = m0 + 16 * t;
-        if (m < M) load_logits<NPL>(logits + (int64_t)m * E, E, lane, rows[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int m = m0 + 16 * t;
-        if (m < M) {
-          int e;
-          float w;
-          route_select<NPL>(rows[t], E, K, lane, &e, &w);
-          if (lane < K) {
-            ids[m * K + lane] = e;
-            wts[m * K + lane] = w;
-            s_ids[m * K + lane] = e;
-          }
-        }
-      }
-    }
-  }
-  if (q.xq) {
-    float s;
-    if (q.static_scale) {
-      s = *q.static_scale;
-    } else {
-      float a = 0.0f;
-#pragma unroll
-      for (int c = 0; c < QC; ++c)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) a = fmaxf(a, fmaxf(fabsf(bf16_lo(xv[c][h])), fabsf(bf16_hi(xv[c][h]))));
-      a = wave_max(a);
-      if (lane == 0) s_red[wave] = a;
-      __syncthreads();
-      a = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) a = fmaxf(a, s_red[w]);
-      s = scale_from_amax(a);
-    }
-    if (tid == 0) *q.scale_slot = s;
-    const float r = 1.0f / s;
-#pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      const int64_t i = ((int64_t)c * 1024 + tid) * 8;
-      if (i < nx) {
-        const u32x4 v = xv[c];
-        u32x2 out = {pack_e4m3x4(bf16_lo(v[0]) * r, bf16_hi(v[0]) * r, bf16_lo(v[1]) * r, bf16_hi(v[1]) * r),
-                     pack_e4m3x4(bf16_lo(v[2]) * r, bf16_hi(v[2]) * r, bf16_lo(v[3]) * r, bf16_hi(v[3]) * r)};
-        *(u32x2*)(q.xq + i) = out;
-      }
-    }
-  }
-  if (q.h_amax && tid == 0) *q.h_amax = 0u;
-  __syncthreads();
-
   // rank of each pair among its wave's pairs of the same expert
   const int f = tid;
   const bool valid = f < P;
@@ -454,70 +465,106 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __res
     match &= bit ? m1 : ~m1;
   }
   const int rank = valid ? __popcll(match & lanemask_lt(lane)) : 0;
-  if (valid && rank == __popcll(match) - 1) s_wc[wave][e] = rank + 1;
+  if (valid && rank == __popcll(match) - 1) L.wc[wave][e] = rank + 1;
   __syncthreads();
   // per expert: total, and the start of each wave's group within the expert
   for (int x = tid; x < E; x += 1024) {
     int run = 0;
 #pragma unroll
     for (int w = 0; w < 16; ++w) {
-      const int c = s_wc[w][x];
-      s_wc[w][x] = run;
+      const int c = L.wc[w][x];
+      L.wc[w][x] = run;
       run += c;
     }
-    s_tot[x] = run;
+    L.tot[x] = run;
   }
   __syncthreads();
   // exclusive scan over experts of the padded sizes and of the active flags
   {
     const int x = tid;
-    const int c = x < E ? s_tot[x] : 0;
+    const int c = x < E ? L.tot[x] : 0;
     const int pad = ((c + B - 1) >> log2B) << log2B;
     const int v = pad | ((c > 0) << 20);  // padded size < 2^20 (P <= 1024, B <= 256)
-    const int incl = wave_incl_scan(v, lane);
-    if (lane == 63) s_scan[wave] = incl;
+    const int incl = wave_incl_scan_dpp(v);
+    if (lane == 63) L.scan[wave] = incl;
     __syncthreads();
     int before = 0;
-    for (int w = 0; w < wave; ++w) before += s_scan[w];
+    for (int w = 0; w < wave; ++w) before += L.scan[w];
     const int excl = before + incl - v;
     if (x < E) {
-      s_off[x] = excl & 0xfffff;
-      s_act[x] = excl >> 20;
+      L.off[x] = excl & 0xfffff;
+      L.act[x] = excl >> 20;
     }
     if (x == E - 1) {
-      s_off[E] = (excl + v) & 0xfffff;
-      s_act[E] = (excl + v) >> 20;
+      L.off[E] = (excl + v) & 0xfffff;
+      L.act[E] = (excl + v) >> 20;
     }
   }
   __syncthreads();
-  if (valid) o.sorted_ids[s_off[e] + s_wc[wave][e] + rank] = f;
+  if (valid) o.sorted_ids[L.off[e] + L.wc[wave][e] + rank] = f;
+  const int total = L.off[E];
   for (int x = tid; x < E; x += 1024) {
-    o.counts[x] = s_tot[x];
-    o.offsets[x] = s_off[x];
-    for (int p = s_off[x] + s_tot[x]; p < s_off[x + 1]; ++p) o.sorted_ids[p] = P;
-    if (o.active && s_tot[x] > 0) o.active[s_act[x]] = x;
+    const int beg = L.off[x], end = L.off[x + 1];
+    o.counts[x] = L.tot[x];
+    o.offsets[x] = beg;
+    for (int p = beg + L.tot[x]; p < end; ++p) o.sorted_ids[p] = P;
+    for (int p = beg; p < end; p += B) o.block_expert[p >> log2B] = x;  // the expert's blocks
+    if (o.active && L.tot[x] > 0) o.active[L.act[x]] = x;
   }
+  for (int b = (total >> log2B) + tid; b < o.n_blocks; b += 1024) o.block_expert[b] = -1;  // blocks past the end
   if (tid == 0) {
-    o.offsets[E] = s_off[E];
-    *o.num_padded = s_off[E];
-    if (o.num_active) *o.num_active = s_act[E];
+    o.offsets[E] = total;
+    *o.num_padded = total;
+    if (o.num_active) *o.num_active = L.act[E];
   }
-  for (int b = tid; b < o.n_blocks; b += 1024) {
-    const int pos = b << log2B;
-    int ex = -1;
-    if (pos < s_off[E]) {
-      int lo = 0, hi = E - 1;  // largest x with s_off[x] <= pos
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= pos)
-          lo = mid;
-        else
-          hi = mid - 1;
-      }
-      ex = lo;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __restrict__ logits, int M, int E, int K,
+                                                              int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                              int log2B, int id_bits, AlignOut o, SmallQuant q) {
+  if (blockIdx.x > 0) {
+    prologue_quant(q, (int64_t)M * q.H, blockIdx.x - 1);
+    return;
+  }
+  __shared__ int s_ids[kSmallPairs];
+  __shared__ SmallAlignLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15;
+  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&L.wc[0][0])[i] = 0;
+  // routing: four tokens per wave, 64 per pass of the 16 waves
+  for (int mb = wave * kRouteRows; mb < M; mb += 16 * kRouteRows) {
+    const int m = mb + (lane >> 4);
+    int e;
+    float w;
+    route_row<NPL>(m < M ? logits + (int64_t)m * E : nullptr, E, K, l16, &e, &w);
+    if (m < M && l16 < K) {
+      ids[m * K + l16] = e;
+      wts[m * K + l16] = w;
+      s_ids[m * K + l16] = e;
     }
-    o.block_expert[b] = ex;
   }
+  if (q.h_amax && tid == 0) *q.h_amax = 0u;
+  __syncthreads();
+  small_align(s_ids, M * K, E, log2B, id_bits, o, L);
+}
+
+// Align of P <= 1024 router-produced pairs (valid ids) in workgroup 0 of
+// 1024 threads; workgroups 1.. quantise x (16K elements each) from the
+// router's partial maxima.
+__global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __restrict__ ids, int P, int E, int log2B,
+                                                           int id_bits, AlignOut o, QuantXArgs q) {
+  if (blockIdx.x > 0) {
+    quant_x_part<1024>(q, blockIdx.x - 1);
+    return;
+  }
+  __shared__ int s_ids[kSmallPairs];
+  __shared__ SmallAlignLds L;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&L.wc[0][0])[i] = 0;
+  if (tid < P) s_ids[tid] = ids[tid];
+  __syncthreads();
+  small_align(s_ids, P, E, log2B, id_bits, o, L);
 }
 
 }  // namespace moe

@@ -75,6 +75,13 @@ def test_tuning_variants_agree():
               moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=4, token_tiles=4, unroll=1, gemm2_wave_ksplit=1)]:
         compare(cfg8, 33, seed=7, weights=w8, tuning=t)
         compare(cfg8, 33, seed=7, weights=w8, tuning=t, x_scale=0.03, h_scale=0.02)
+    # long-stream variants (fp8): tile counts that leave partial chunks and idle waves, K slices, unrolls
+    for t in [moe.Tuning(gemm1_stream_tiles=1, gemm2_stream_tiles=1, token_tiles=1, unroll=1),
+              moe.Tuning(gemm1_stream_tiles=3, gemm2_stream_tiles=5, token_tiles=2, unroll=2, gemm2_ksplit=2),
+              moe.Tuning(gemm1_stream_tiles=16, gemm2_stream_tiles=16, token_tiles=4, unroll=1, gemm2_ksplit=4),
+              moe.Tuning(gemm1_stream_tiles=-1, gemm2_stream_tiles=-1, token_tiles=4)]:
+        compare(cfg8, 33, seed=7, weights=w8, tuning=t)
+        compare(cfg8, 33, seed=7, weights=w8, tuning=t, x_scale=0.03, h_scale=0.02)
 
 
 def test_m0_is_noop():
