@@ -69,15 +69,15 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 constexpr int kPfTok = 128;                      // tokens per work item (the align block)
-constexpr int kPfRows = 512;                     // weight rows per work item
-constexpr int kPfBK = 64;                        // K bytes per step: one MFMA k-step
-constexpr int kPfStages = 4;                     // LDS ring depth: loads run three steps ahead
+constexpr int kPfRows = 256;                     // weight rows per work item
+constexpr int kPfBK = 128;                       // K bytes per step: two MFMA k-steps, one cache line per row
+constexpr int kPfStages = 3;                     // LDS ring depth: loads run two steps ahead
 constexpr int kPfStageA = kPfRows * kPfBK;       // 32 KB
-constexpr int kPfStageB = kPfTok * kPfBK;        // 8 KB
-constexpr int kPfStage = kPfStageA + kPfStageB;  // 40 KB
-constexpr int kPfLds = kPfStages * kPfStage;     // 160 KB: the whole LDS, one workgroup per CU
+constexpr int kPfStageB = kPfTok * kPfBK;        // 16 KB
+constexpr int kPfStage = kPfStageA + kPfStageB;  // 48 KB
+constexpr int kPfLds = kPfStages * kPfStage;     // 144 KB: one workgroup per CU
 constexpr int kPfThreads = 256;                  // four waves
-constexpr int kPfDma = 10;                       // DMA instructions per wave per step: 8 A + 2 B
+constexpr int kPfDma = 12;                       // DMA instructions per wave per step: 8 A + 4 B
 // third descriptor word of a raw byte buffer resource on CDNA (32-bit data
 // format, no swizzle, no index stride)
 constexpr int kBufferWord3 = 0x00020000;
@@ -90,12 +90,14 @@ struct PrefillSeg {
   const int32_t* num_padded;    // [1]
 };
 
-// LDS layout of an operand tile in one stage: rows of 64 bytes, the four
-// 16-byte chunks of row r stored at chunk position c ^ ((r >> 1) & 3).  Eight
-// consecutive rows with the same logical chunk then fall on the eight
-// different 16-byte bank groups of a 128-byte line, so the MFMA fragment reads
-// (32 rows, same chunk) are free of bank conflicts.
-__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// LDS layout of an operand tile in one stage: rows of 128 bytes (a whole
+// cache line of the row per step, so a 1 KB load covers 8 lines rather than
+// 16 half lines, which halves its texture-address work), the eight 16-byte
+// chunks of row r stored at chunk position c ^ (r & 7).  Eight consecutive
+// rows with the same logical chunk then fall on eight different 16-byte bank
+// groups, so the MFMA fragment reads (32 rows, same chunk) are free of bank
+// conflicts.
+__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ (row & 7)) << 4); }
 
 // Work item -> (weight tile, token block), XCD-aware.  Workgroups are handed
 // to the eight XCDs round robin by linear id, and item L belongs to XCD L % 8.
@@ -131,7 +133,7 @@ struct PrefillArgs {
   const uint8_t* act;      // gate/up: xq [M][H]; down: hq [P][I], e4m3
   PrefillSeg seg;
   int H, I, top_k, P;
-  int tiles;               // weight tiles: 2I/512 or H/512
+  int tiles;               // weight tiles: I/128 (128 gate + 128 up rows each) or H/256
   int items;               // bound on the linear item index: 8 x tiles x blocks per XCD (largest case)
   const float* w_scale;    // s_w13 or s_w2
   const float* a_scale;    // gate/up: s_x in effect; down: static s_h (null = dynamic)
@@ -146,9 +148,9 @@ struct PrefillArgs {
 // pass silently drops the kernel's launch stub.
 struct PfSrc {
   const uint8_t* wa;  // the expert's weight matrix (a buffer resource is made from it at issue)
-  int offA;     // byte offset of this lane's first A row (row q adds 16*q rows)
-  int offB[2];  // byte offsets of this lane's two B rows
-  int fb[2];    // pair ids of this lane's B rows, until finish_src turns them into offB
+  int offA;     // byte offset of this lane's first A row (load q adds 8*q rows)
+  int offB[4];  // byte offsets of this lane's four B rows
+  int fb[4];    // pair ids of this lane's B rows, until finish_src turns them into offB
   int f[4];     // pair ids of this lane's epilogue tokens 32*j + lane%32 (clamped)
 };
 
@@ -201,33 +203,33 @@ __device__ __forceinline__ void pf_interleave() {
   }
 }
 
-// MODE 0: gate/up product, tile rows = 256 gate + 256 up rows of the same 256
+// MODE 0: gate/up product, tile rows = 128 gate + 128 up rows of the same 128
 //   features, epilogue SiLU(g)*u -> h.  HDYN: h stored as fp32 with a running
 //   amax (quantised by prefill_quant_h_kernel), else as e4m3 with the static
 //   scale.
-// MODE 1: down product, tile rows = 512 output features, epilogue
+// MODE 1: down product, tile rows = 256 output features, epilogue
 //   s_h * s_w2 * acc -> bf16 part[pair][feature] (the routing weight is
 //   applied when the pairs of a token are summed).
 //
 // Persistent: one workgroup per CU walks the work items L = blockIdx.x,
 // blockIdx.x + gridDim.x, ... (gridDim.x a multiple of 8 keeps every
 // workgroup on the XCD that pf_map assigns its items to).  The LDS ring runs
-// on across items: the last three K-steps of an item load the first three of
-// the next, whose metadata was fetched one item earlier, so an item's epilogue
-// overlaps the next item's first loads and no workgroup start or metadata
-// latency sits between items.
+// on across items: the last two K-steps of an item that load anything load
+// the first two of the next, whose metadata was fetched one item earlier, so
+// an item's epilogue overlaps the next item's first loads and no workgroup
+// start or metadata latency sits between items.
 //
-// Wave w owns weight rows 128w..128w+127 of the tile (MODE 0: gate and up
-// rows of features 64w..64w+63) and all 128 tokens.  Each 64-byte K-step every
-// wave DMA-loads 128 rows of the A tile and 32 rows of the B tile (ten 1 KB
-// load instructions, lane i filling bytes 16i..16i+15 of a 16-row block).
+// Wave w multiplies 64 weight rows of the tile (MODE 0: gate rows 32w.. and
+// the up rows of the same 32 features; MODE 1: rows 64w..64w+63) by all 128
+// tokens.  Each 128-byte K-step (two MFMA k-steps) every wave DMA-loads rows
+// 64w..64w+63 of the A tile and 32w..32w+31 of the B tile (twelve 1 KB load
+// instructions, lane i filling bytes 16i..16i+15 of an 8-row block).
 //
 // Wait accounting: the waits count vector-memory operations, which complete
 // in issue order.  Before the barrier that precedes the reads of step s+1 a
-// wave waits until at most ten are outstanding: the loads of step s+2, issued
-// after those of step s+1.  Any other vector-memory operation (token ids,
-// epilogue stores) only makes that wait stricter.  When no load follows step
-// s+1 (the end of the last item) the wait is for zero.
+// wave waits until at most twelve are outstanding: the loads of step s+2,
+// issued after those of step s+1.  Any other vector-memory operation (token
+// ids, epilogue stores) only makes that wait stricter.
 template <int MODE, bool HDYN>
 __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -244,14 +246,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the wave's branches scalar
   const int K = MODE == 0 ? a.H : a.I;                        // contraction length (bytes)
-  const int nk = K / kPfBK;                                   // >= 4 (host)
+  const int nk = K / kPfBK;                                   // even, >= 4 (host)
   const int wrows = MODE == 0 ? 2 * a.I : a.H;                // rows of one expert's weight
-  const int drow = lane >> 2, dchunk = lane & 3;              // DMA: row in a 16-row block, chunk position
+  const int drow = lane >> 3, dchunk = lane & 7;              // DMA: row in an 8-row block, chunk position
   const int col = lane & 31, rq = (lane >> 5) * 4;
 
-  // DMA sources of an item for this lane: A rows 128*wave + 16*q + lane/4
-  // (q < 8), B rows 32*wave + 16*q + lane/4 (q < 2), logical chunk
-  // (lane%4) ^ ((row >> 1) & 3).  The loads go through buffer resources (the
+  // DMA sources of an item for this lane: A rows 64*wave + 8*q + lane/8
+  // (q < 8), B rows 32*wave + 8*q + lane/8 (q < 4), logical chunk
+  // (lane%8) ^ (lane/8) (the row's low three bits are lane/8).  The loads go through buffer resources (the
   // expert's weight matrix and the activation matrix, byte offsets below
   // 2^31, checked by the host) rather than flat-global addresses: the
   // compiler's wait-count model treats a flat-global load into LDS as a
@@ -260,23 +262,22 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   auto make_src = [&](const PfItem& it, PfSrc& sr) {
     sr.wa = a.w + (int64_t)it.e * wrows * K;
     {
-      // rows 128*wave + 16*q + lane/4: in MODE 0 waves 0, 1 hold gate rows and
-      // waves 2, 3 the up rows of the same features; the swizzle depends on
-      // lane/4 only
-      const int row = 128 * wave + drow;
+      // rows 64*wave + 8*q + lane/8: in MODE 0 waves 0, 1 load gate rows and
+      // waves 2, 3 the up rows of the same features
+      const int row = 64 * wave + drow;
       int wrow;
       if (MODE == 0) {
-        const int f0 = it.tile * 256;
-        wrow = row < 256 ? f0 + row : a.I + f0 + (row - 256);
+        const int f0 = it.tile * (kPfRows / 2);
+        wrow = row < kPfRows / 2 ? f0 + row : a.I + f0 + (row - kPfRows / 2);
       } else {
         wrow = it.tile * kPfRows + row;
       }
-      sr.offA = wrow * K + ((dchunk ^ ((drow >> 1) & 3)) << 4);
+      sr.offA = wrow * K + ((dchunk ^ drow) << 4);
     }
     // token ids: padding slots read the block's last token (their results are dropped)
     const int32_t* ids = a.seg.sorted_ids + it.blk * kPfTok;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) sr.fb[q] = ids[min(32 * wave + 16 * q + drow, it.ntok - 1)];
+    for (int q = 0; q < 4; ++q) sr.fb[q] = ids[min(32 * wave + 8 * q + drow, it.ntok - 1)];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sr.f[j] = ids[min(32 * j + col, it.ntok - 1)];
   };
@@ -286,27 +287,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   // loads, waiting for them there)
   auto finish_src = [&](PfSrc& sr) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = 32 * wave + 16 * q + drow;
+    for (int q = 0; q < 4; ++q) {
       int f = sr.fb[q];
       asm volatile("" : "+v"(f));
       const int brow = MODE == 0 ? f / a.top_k : f;
-      sr.offB[q] = brow * K + ((dchunk ^ ((row >> 1) & 3)) << 4);
+      sr.offB[q] = brow * K + ((dchunk ^ drow) << 4);  // row 32*wave + 8*q + drow: low bits drow
     }
-  };
-  // element-wise choice between two sources (a choice of struct address
-  // would force both structs into scratch memory)
-  auto pick = [](bool first, const PfSrc& x, const PfSrc& y) {
-    PfSrc r;
-    r.wa = first ? x.wa : y.wa;
-    r.offA = first ? x.offA : y.offA;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) r.offB[q] = first ? x.offB[q] : y.offB[q];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) r.fb[q] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.f[j] = 0;
-    return r;
   };
   const __amdgpu_buffer_rsrc_t rsrcB =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, 0x7fffffff, kBufferWord3);
@@ -317,30 +303,33 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (void __attribute__((address_space(3)))*)(base + (128 * wave + 16 * q) * kPfBK), 16, sr.offA,
-          kb + 16 * q * K, 0, 0);
+          ra, (void __attribute__((address_space(3)))*)(base + (64 * wave + 8 * q) * kPfBK), 16, sr.offA,
+          kb + 8 * q * K, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 4; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrcB, (void __attribute__((address_space(3)))*)(base + kPfStageA + (32 * wave + 16 * q) * kPfBK), 16,
+          rsrcB, (void __attribute__((address_space(3)))*)(base + kPfStageA + (32 * wave + 8 * q) * kPfBK), 16,
           sr.offB[q], kb, 0, 0);
   };
 
-  // fragment addresses within a stage: A tile i rows arow(i) + lane%32, B tile
-  // j rows 32*j + lane%32, chunks 2*(lane/32) + c.  Tiles differ by whole
-  // 32-row multiples, which leave the chunk swizzle unchanged, so a tile is a
-  // constant byte offset from the c-th base.
+  // fragment addresses within a stage: A tile i rows arow0 + arow_off(i) +
+  // lane%32, B tile j rows 32*j + lane%32; MFMA k-step ks of the step uses
+  // chunks 4*ks + 2*(lane/32) + c.  Tiles differ by whole 32-row multiples,
+  // which leave the chunk swizzle unchanged, so a tile is a constant byte
+  // offset from the (ks, c) base.
   const int fr = lane & 31, fc = (lane >> 5) * 2;
-  const int arow0 = MODE == 0 ? 64 * wave : 128 * wave;
-  int baseA[2], baseB[2];
+  const int arow0 = MODE == 0 ? 32 * wave : 64 * wave;
+  int baseA[2][2], baseB[2][2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    baseA[c] = pf_swz(arow0 + fr, fc + c);
-    baseB[c] = kPfStageA + pf_swz(fr, fc + c);
-  }
-  // row offset of A tile i from arow0 (MODE 0: tiles 0, 1 gate, 2, 3 the up
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      baseA[ks][c] = pf_swz(arow0 + fr, 4 * ks + fc + c);
+      baseB[ks][c] = kPfStageA + pf_swz(fr, 4 * ks + fc + c);
+    }
+  // row offset of A tile i from arow0 (MODE 0: tile 0 gate, tile 1 the up
   // rows of the same features)
-  auto arow_off = [](int i) { return MODE == 0 ? (i & 1) * 32 + (i >> 1) * 256 : 32 * i; };
+  auto arow_off = [](int i) { return MODE == 0 ? i * (kPfRows / 2) : 32 * i; };
 
   // epilogue constants
   const float deq = MODE == 0 ? (*a.a_scale) * (*a.w_scale)
@@ -352,30 +341,30 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   make_src(cur, cs);
   finish_src(cs);
   int slot0 = 0;  // ring slot of the current item's first K-step
-  issue(cs, 0, 0);  // steps 0..2 (each item's start issues its step 3)
+  issue(cs, 0, 0);  // steps 0, 1 (each item's start issues its step 2)
   issue(cs, 1, 1);
-  issue(cs, 2, 2);
 
-  // Fragments of one K-step: the wave's four A tiles and up to four B tiles.
+  // Fragments of one K-step (two MFMA k-steps): the wave's two A tiles and up
+  // to four B tiles.
   struct Frags {
-    u32x4 a[4][2], b[4][2];
+    u32x4 a[2][2][2], b[2][4][2];  // [k-step][tile][chunk]
   };
   PfItem nn = nxt;  // the item after the next (fetched during each item)
   bool has_nn = false;
   // One item with its NJ (1..4) 32-token tiles multiplied; one version per NJ
   // so that the K-step body has no branches, each with its own accumulators
-  // and epilogue (a join of the versions' 256 accumulators would be copied
-  // out of AGPRs).  Fragments are double-buffered: the reads of step k+1 run
-  // while the MFMAs of step k do.  Each step's barrier follows this wave's
-  // wait for its loads of step k+1 (those of k+2 and k+3 may still be in
-  // flight); then step k+4 is loaded into the slot of step k, whose reads the
-  // barrier has just drained.
+  // and epilogue (a join of the versions' accumulators would be copied out of
+  // AGPRs).  Fragments are double-buffered: the reads of step k+1 run while
+  // the MFMAs of step k do.  Each step's barrier follows this wave's wait for
+  // its loads of step k+1 (those of k+2 may still be in flight); then step
+  // k+3 is loaded into the slot of step k, whose reads the barrier has just
+  // drained.
   auto item = [&](auto nj_tag) {
     constexpr int NJ = decltype(nj_tag)::value;
-    constexpr int NMF = 4 * NJ, NDS = 8 + 2 * NJ;
-    f32x16 acc[4][NJ];
+    constexpr int NMF = 4 * NJ, NDS = 8 + 4 * NJ;
+    f32x16 acc[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -384,67 +373,71 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
     auto read = [&](Frags& F, int k) {
       const lds_u8* st = smem + slot(k) * kPfStage;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          F.a[i][c] = *(const __attribute__((address_space(3))) u32x4*)(st + baseA[c] + arow_off(i) * kPfBK);
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          F.b[j][c] = *(const __attribute__((address_space(3))) u32x4*)(st + baseB[c] + 32 * j * kPfBK);
-      }
+          for (int i = 0; i < 2; ++i)
+            F.a[ks][i][c] =
+                *(const __attribute__((address_space(3))) u32x4*)(st + baseA[ks][c] + arow_off(i) * kPfBK);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            F.b[ks][j][c] = *(const __attribute__((address_space(3))) u32x4*)(st + baseB[ks][c] + 32 * j * kPfBK);
+        }
     };
     auto mma = [&](const Frags& F) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32_fp8(F.a[i][0], F.a[i][1], F.b[j][0], F.b[j][1], acc[i][j]);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = mfma32_fp8(F.a[ks][i][0], F.a[ks][i][1], F.b[ks][j][0], F.b[ks][j][1], acc[i][j]);
     };
-    // Every K-step loads step k+3 of the ring: this item's, the next item's
-    // or, after the last item, a dummy copy of this item's first steps into
-    // a slot nothing reads again; so every wait is the same (the loads of the
-    // two following steps may be in flight) and every step has the same
-    // interleaved body.  The kernel drains these loads before it ends.
-    auto src_of = [&](int k) -> PfSrc { return pick(k < nk, cs, ns); };
-    auto kstep_of = [&](int k) { return k < nk ? k : k - nk; };
+    // Every K-step but the last loads step k+3 of the ring: this item's, the
+    // next item's or, after the last item, a dummy copy of this item's first
+    // steps into a slot nothing reads again; so every wait is the same (the
+    // loads of the following step may be in flight) and every step has the
+    // same interleaved body.  The kernel drains these loads before it ends.
     Frags F0, F1;
-    // item start: step 0 landed, load step 3 (of this item: nk >= 4)
-    wait_vm<2 * kPfDma>();
+    // item start: step 0 landed, load step 2 (of this item: nk >= 4)
+    wait_vm<kPfDma>();
     ring_barrier();
-    issue(cs, 3, slot(3));
+    issue(cs, 2, slot(2));
     make_src(nxt, ns);  // next item's token ids (unconditional: a conditional load would be copied at the join, waiting for it)
     read(F0, 0);
-    // one K-step: multiply step k, read step k+1, load step k+4
-    auto body = [&](Frags& Fc, Frags& Fn, int k, const PfSrc& src, auto id_tag) {
+    // one K-step: multiply step k, read step k+1, load K-step `kstep` of src
+    // into the slot of step k (step k+3 of the ring)
+    auto body = [&](Frags& Fc, Frags& Fn, int k, const PfSrc& src, int kstep, auto id_tag) {
       constexpr int ID = decltype(id_tag)::value;
-      wait_vm<2 * kPfDma>();  // step k+1 landed; k+2 and k+3 may be in flight
+      wait_vm<kPfDma>();  // step k+1 landed; k+2 may be in flight
       ring_barrier();
       __builtin_amdgcn_sched_barrier(0);
       read(Fn, k + 1);
-      issue(src, kstep_of(k + 4), slot(k + 4));
+      issue(src, kstep, slot(k + 3));
       mma(Fc);
       pf_interleave<0, NMF, NDS, kPfDma, ID>();
       __builtin_amdgcn_sched_barrier(0);
     };
     int s = 0;
     for (; s + 4 < nk; s += 2) {  // steps loading this item's steps (nk is even)
-      body(F0, F1, s, cs, std::integral_constant<int, 0>{});
-      body(F1, F0, s + 1, cs, std::integral_constant<int, 1>{});
+      body(F0, F1, s, cs, s + 3, std::integral_constant<int, 0>{});
+      body(F1, F0, s + 1, cs, s + 4, std::integral_constant<int, 1>{});
     }
+    // s = nk - 4: its step loads this item's last step
+    body(F0, F1, nk - 4, cs, nk - 1, std::integral_constant<int, 2>{});
     if (!has_next) ns = cs;  // dummy source after the last item (valid addresses, never read)
     finish_src(ns);          // the next item's token ids are needed from here on
-    for (; s + 2 < nk; s += 2) {  // steps loading the next item's first steps
-      body(F0, F1, s, src_of(s + 4), std::integral_constant<int, 2>{});
-      body(F1, F0, s + 1, src_of(s + 5), std::integral_constant<int, 3>{});
-    }
-    // last two steps: step nk-2 reads step nk-1 and loads the next item's
-    // step 2; step nk-1 only multiplies
-    body(F0, F1, nk - 2, ns, std::integral_constant<int, 4>{});
+    // steps nk-3 and nk-2 load the next item's steps 0 and 1; step nk-1 only
+    // multiplies
+    body(F1, F0, nk - 3, ns, 0, std::integral_constant<int, 3>{});
+    body(F0, F1, nk - 2, ns, 1, std::integral_constant<int, 4>{});
     mma(F1);
 
     // The accumulators stay in AGPRs until the epilogue reads them tile by
     // tile (otherwise the last MFMAs write all of them to VGPRs at once).
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
 
@@ -462,28 +455,25 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
         const int t = 32 * j + col;
         if (t < cur.ntok) {
           const int f = cs.f[j];
+          const int fbase = cur.tile * (kPfRows / 2) + 32 * wave;
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int fbase = cur.tile * 256 + 64 * wave + 32 * i;
+          for (int g = 0; g < 4; ++g) {
+            float hv[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              float hv[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float gt = acc[i][j][4 * g + q] * deq;
-                const float up = acc[i + 2][j][4 * g + q] * deq;
-                hv[q] = silu_fast(gt) * up;
-                hmax = fmaxf(hmax, fabsf(hv[q]));
-              }
-              const int64_t idx = (int64_t)f * a.I + fbase + 8 * g + rq;
-              if (HDYN) {  // fp32, so that h is rounded once, to e4m3, after the amax is known
-                *(f32x4*)(a.out + idx * 4) = f32x4{hv[0], hv[1], hv[2], hv[3]};
-              } else {
-                *(unsigned*)(a.out + idx) = pack_e4m3x4(hv[0] * rhs, hv[1] * rhs, hv[2] * rhs, hv[3] * rhs);
-              }
+            for (int q = 0; q < 4; ++q) {
+              const float gt = acc[0][j][4 * g + q] * deq;
+              const float up = acc[1][j][4 * g + q] * deq;
+              hv[q] = silu_fast(gt) * up;
+              hmax = fmaxf(hmax, fabsf(hv[q]));
             }
-            __builtin_amdgcn_sched_barrier(0);
+            const int64_t idx = (int64_t)f * a.I + fbase + 8 * g + rq;
+            if (HDYN) {  // fp32, so that h is rounded once, to e4m3, after the amax is known
+              *(f32x4*)(a.out + idx * 4) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+            } else {
+              *(unsigned*)(a.out + idx) = pack_e4m3x4(hv[0] * rhs, hv[1] * rhs, hv[2] * rhs, hv[3] * rhs);
+            }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
@@ -491,9 +481,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
       for (int j = 0; j < NJ; ++j) {
         const int t = 32 * j + col;
         if (t < cur.ntok) {
-          uint16_t* dst = (uint16_t*)a.out + (int64_t)cs.f[j] * a.H + (int64_t)cur.tile * kPfRows + 128 * wave;
+          uint16_t* dst = (uint16_t*)a.out + (int64_t)cs.f[j] * a.H + (int64_t)cur.tile * kPfRows + 64 * wave;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const f32x16& c = acc[i][j];

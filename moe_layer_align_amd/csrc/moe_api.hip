@@ -21,15 +21,16 @@ constexpr int kAlignBlockFused = 16;   // token tile of the decode products' B o
 constexpr int kPrefillMinPairs = 8192; // fp8 layers with at least this many pairs take the prefill products
 
 // fp8 layers with many pairs use the tiled prefill products (token block 128,
-// weight tiles of 512 rows: H a multiple of 512 for the down product, I a
-// multiple of 256 for the gate/up product, whose tiles hold 256 gate and 256
-// up rows; both then have at least four 64-byte K-steps).  Their operand
+// weight tiles of 256 rows: 256 rows of H for the down product, 128 gate and
+// 128 up rows for the gate/up product).  Both contraction lengths (H and I)
+// must be an even number, at least four, of 128-byte K-steps.  The operand
 // loads take 32-bit byte offsets into one expert's weights and into the
 // activations.
 bool use_prefill(int M, int k, moe_dtype_t dt, int H, int I) {
   const int64_t P = (int64_t)M * k, lim = INT32_MAX;
+  auto steps_ok = [](int K) { return K % (2 * kPfBK) == 0 && K >= 4 * kPfBK; };
   return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0 && I % (kPfRows / 2) == 0 &&
-         2 * (int64_t)I * H <= lim && (int64_t)M * H <= lim && P * I <= lim;
+         steps_ok(H) && steps_ok(I) && 2 * (int64_t)I * H <= lim && (int64_t)M * H <= lim && P * I <= lim;
 }
 int align_block(int M, int k, moe_dtype_t dt, int H, int I) {
   return use_prefill(M, k, dt, H, I) ? kPfTok : kAlignBlockFused;
@@ -523,7 +524,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   if ((rc = persistent_wgs(&wgs)) != MOE_OK) return rc;
   rec(4);
   {
-    const int T = I / (kPfRows / 2);  // 512-row tiles of W13: 256 gate + 256 up rows
+    const int T = I / (kPfRows / 2);  // 256-row tiles of W13: 128 gate + 128 up rows
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
                   a->h_scale, h, h_amax};

@@ -128,13 +128,16 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: row shifts by
+// 1, 2, 4 and 8 (lanes without a source add 0) scan each 16-lane row, then
+// the two row broadcasts carry the totals of rows 0, 0+1 and 2 forward.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast31, 0xC, 0xF, false);
   return v;
 }
 

@@ -216,7 +216,7 @@ __device__ void quant_x_part(const QuantXArgs& q, int wg) {
 // Returns the exclusive prefix for entry 2t; *total receives the sum.
 __device__ __forceinline__ int block_excl_scan_pair(int v0, int v1, int* s_wtot, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v0 + v1, lane);
+  const int incl = wave_incl_scan(v0 + v1);
   if (lane == 63) s_wtot[wave] = incl;
   __syncthreads();
   int before = 0;
@@ -252,17 +252,30 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  for (int f = tid; f < P; f += 256) {
-    const int e = ids[f];
-    if ((unsigned)e >= (unsigned)E) {
-      s_bad = 1;
-      continue;
+  // histogram of all P ids, 16 loads in flight per thread
+  constexpr int kHistBatch = 16;
+  for (int f0 = tid; f0 < P; f0 += 256 * kHistBatch) {
+    int ev[kHistBatch];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      const int f = f0 + 256 * u;
+      ev[u] = f < P ? ids[f] : 0;
     }
-    atomicAdd(&s_total[e], 1);
-    if (f < cb)
-      atomicAdd(&s_before[e], 1);
-    else if (f < ce)
-      atomicAdd(&s_wave[(f - cb) >> 8][e], 1);
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      const int f = f0 + 256 * u;
+      const int e = ev[u];
+      if (f >= P) break;
+      if ((unsigned)e >= (unsigned)E) {
+        s_bad = 1;
+        continue;
+      }
+      atomicAdd(&s_total[e], 1);
+      if (f < cb)
+        atomicAdd(&s_before[e], 1);
+      else if (f < ce)
+        atomicAdd(&s_wave[(f - cb) >> 8][e], 1);
+    }
   }
   __syncthreads();
 
@@ -326,9 +339,10 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
   for (int e = tid; e < E; e += 256) {
     o.counts[e] = s_total[e];
     o.offsets[e] = s_off[e];
-    for (int p = s_off[e] + s_total[e]; p < s_off[e + 1]; ++p) o.sorted_ids[p] = P;
     if (o.active && s_total[e] > 0) o.active[s_act[e]] = e;
   }
+  for (int e = wave; e < E; e += 4)  // sentinels: the lanes of a wave fill one expert's padding
+    for (int p = s_off[e] + s_total[e] + lane; p < s_off[e + 1]; p += 64) o.sorted_ids[p] = P;
   if (tid == 0) {
     o.offsets[E] = total;
     *o.num_padded = s_bad ? -1 : total;
@@ -425,19 +439,6 @@ __device__ __forceinline__ void prologue_quant(const SmallQuant& q, int64_t nx, 
   *(u32x4*)(q.xq + i) = quant16_e4m3(*(const u32x4*)(q.x + i), *(const u32x4*)(q.x + i + 8), r);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave by DPP: row shifts by
-// 1, 2, 4 and 8 (lanes without a source add 0) scan each 16-lane row, then
-// the two row broadcasts carry the totals of rows 0, 0+1 and 2 forward.
-__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast15, 0xA, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast31, 0xC, 0xF, false);
-  return v;
-}
-
 // LDS of the one-workgroup align.
 struct SmallAlignLds {
   int wc[16][kMaxExperts];  // per (wave, expert): group size, then start within the expert
@@ -485,7 +486,7 @@ __device__ __forceinline__ void small_align(const int* s_ids, int P, int E, int 
     const int c = x < E ? L.tot[x] : 0;
     const int pad = ((c + B - 1) >> log2B) << log2B;
     const int v = pad | ((c > 0) << 20);  // padded size < 2^20 (P <= 1024, B <= 256)
-    const int incl = wave_incl_scan_dpp(v);
+    const int incl = wave_incl_scan(v);
     if (lane == 63) L.scan[wave] = incl;
     __syncthreads();
     int before = 0;

@@ -187,16 +187,16 @@ def prefill_w():
 # Tiled prefill products (fp8 with at least 8192 pairs) at sizes the oracle
 # evaluates quickly: Zipf routing leaves experts empty and blocks partial.
 def test_prefill_path_dynamic_scales_all_tokens():
-    # smallest prefill shapes: one 512-row tile per product, four 64-byte
-    # K-steps in the down product
-    cfg = MoEConfig("pf_small", E=16, k=8, H=512, I=256, dtype="fp8", ms=(1100,), logits="zipf")
+    # smallest prefill shapes: four 128-byte K-steps in both products, two
+    # 256-row tiles in the down product
+    cfg = MoEConfig("pf_small", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf")
     compare(cfg, 1100, seed=11)
 
 
 def test_prefill_path_shortest_down_k():
     # down product of four K-steps (no steady-state iteration: every step is
-    # a tail step that may load the next item), gate/up of 24
-    cfg = MoEConfig("pf_k4", E=16, k=8, H=1536, I=256, dtype="fp8", ms=(1100,), logits="zipf")
+    # a tail step that may load the next item), gate/up of 12
+    cfg = MoEConfig("pf_k4", E=16, k=8, H=1536, I=512, dtype="fp8", ms=(1100,), logits="zipf")
     compare(cfg, 1100, seed=13, tokens=[0, 1, 2, 3, 400, 401, 777, 1098, 1099])
 
 
