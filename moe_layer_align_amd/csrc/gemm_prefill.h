@@ -174,6 +174,35 @@ __device__ __forceinline__ bool pf_next(const PrefillArgs& a, int nb, int& L, in
   return true;
 }
 
+// The same lookup in three phases for use inside the K-loop, each phase's
+// loads issued before a K-step's loads and consumed after the next K-step's
+// wait (which covers them), so that no wait of its own drains the ring.
+// Loads are unconditional, at index 0 when there is no item.
+struct PfFetch {
+  bool ok;
+  int tile, blk, e, off, cnt;
+};
+__device__ __forceinline__ void pf_fetch_a(const PrefillArgs& a, int nb, int L, bool want, PfFetch& f) {
+  f.tile = 0;
+  f.blk = 0;
+  f.ok = want && L < a.items && pf_map(L, a.tiles, nb, &f.tile, &f.blk);
+  f.e = a.seg.block_expert[f.ok ? f.blk : 0];
+}
+__device__ __forceinline__ void pf_fetch_b(const PrefillArgs& a, PfFetch& f) {
+  const int e = f.ok ? __builtin_amdgcn_readfirstlane(f.e) : 0;
+  f.e = e;
+  f.off = a.seg.offsets[e];
+  f.cnt = a.seg.counts[e];
+}
+__device__ __forceinline__ bool pf_fetch_c(const PfFetch& f, PfItem& it) {
+  if (!f.ok) return false;
+  it.tile = f.tile;
+  it.blk = f.blk;
+  it.e = f.e;
+  it.ntok = min(kPfTok, __builtin_amdgcn_readfirstlane(f.off + f.cnt) - f.blk * kPfTok);
+  return true;
+}
+
 // SiLU(x) = x / (1 + e^-x) with the hardware exp2 and reciprocal (about one
 // ulp each in fp32, far below the e4m3 / bf16 rounding that follows): the
 // libm exp and the IEEE division cost several times more, and with one wave
@@ -407,11 +436,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
     make_src(nxt, ns);  // next item's token ids (unconditional: a conditional load would be copied at the join, waiting for it)
     read(F0, 0);
     // one K-step: multiply step k, read step k+1, load K-step `kstep` of src
-    // into the slot of step k (step k+3 of the ring)
-    auto body = [&](Frags& Fc, Frags& Fn, int k, const PfSrc& src, int kstep, auto id_tag) {
+    // into the slot of step k (step k+3 of the ring); `pre` runs first (its
+    // loads precede the step's)
+    auto body = [&](Frags& Fc, Frags& Fn, int k, const PfSrc& src, int kstep, auto id_tag, auto&& pre) {
       constexpr int ID = decltype(id_tag)::value;
       wait_vm<kPfDma>();  // step k+1 landed; k+2 may be in flight
       ring_barrier();
+      pre();
       __builtin_amdgcn_sched_barrier(0);
       read(Fn, k + 1);
       issue(src, kstep, slot(k + 3));
@@ -419,19 +450,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
       pf_interleave<0, NMF, NDS, kPfDma, ID>();
       __builtin_amdgcn_sched_barrier(0);
     };
+    auto none = [] {};
     int s = 0;
     for (; s + 4 < nk; s += 2) {  // steps loading this item's steps (nk is even)
-      body(F0, F1, s, cs, s + 3, std::integral_constant<int, 0>{});
-      body(F1, F0, s + 1, cs, s + 4, std::integral_constant<int, 1>{});
+      body(F0, F1, s, cs, s + 3, std::integral_constant<int, 0>{}, none);
+      body(F1, F0, s + 1, cs, s + 4, std::integral_constant<int, 1>{}, none);
     }
-    // s = nk - 4: its step loads this item's last step
-    body(F0, F1, nk - 4, cs, nk - 1, std::integral_constant<int, 2>{});
+    // s = nk - 4: its step loads this item's last step; the metadata of the
+    // item after the next is fetched across the last three steps
+    PfFetch fnn;
+    body(F0, F1, nk - 4, cs, nk - 1, std::integral_constant<int, 2>{},
+         [&] { pf_fetch_a(a, nb, L + stride, has_next, fnn); });
     if (!has_next) ns = cs;  // dummy source after the last item (valid addresses, never read)
     finish_src(ns);          // the next item's token ids are needed from here on
     // steps nk-3 and nk-2 load the next item's steps 0 and 1; step nk-1 only
     // multiplies
-    body(F1, F0, nk - 3, ns, 0, std::integral_constant<int, 3>{});
-    body(F0, F1, nk - 2, ns, 1, std::integral_constant<int, 4>{});
+    body(F1, F0, nk - 3, ns, 0, std::integral_constant<int, 3>{}, [&] { pf_fetch_b(a, fnn); });
+    body(F0, F1, nk - 2, ns, 1, std::integral_constant<int, 4>{}, none);
     mma(F1);
 
     // The accumulators stay in AGPRs until the epilogue reads them tile by
@@ -441,10 +476,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
 
-    // metadata of the item after the next, waited for at its first use
+    // metadata of the item after the next (its loads completed under the
+    // waits of the last steps)
     if (has_next) {
       L += stride;
-      has_nn = pf_next(a, nb, L, stride, nn);
+      has_nn = pf_fetch_c(fnn, nn);
     }
 
     // epilogue (no LDS: the next item's first loads are landing in the ring);
