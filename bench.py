@@ -51,11 +51,16 @@ FLUSH_BYTES = 1 << 30
 # HBM bytes per launch of the gate/up product, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs of this script (scaled by the reading of a 1 GiB copy), and
 # the SHA-256 of the kernel sources they were taken on.  The figure is
-# reported only while the sources are unchanged.
-KERNEL_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
+# reported only while those sources are unchanged.
+DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
+PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "22810c16e41098c9950a917962baa512449b935ffc4818aba96670a5fe3f57a9",
-                "bytes_per_launch": 1510020804},
+    "mixtral": {"src_sha256": "94eab15d189c8070e5d81afd5826fcaad8434265d20eca846d4aa778a7bc701c",
+                "bytes_per_launch": 1510116716},
+    "qwen3": {"src_sha256": "94eab15d189c8070e5d81afd5826fcaad8434265d20eca846d4aa778a7bc701c",
+              "bytes_per_launch": 241727958},
+    "prefill": {"src_sha256": "7a15c971a6748887ffc9bf615e3d170adcf60890ffdfee2111f1b88dc57eb790",
+                "bytes_per_launch": 2763971872},
 }
 
 
@@ -64,9 +69,9 @@ def log(msg: str):
     sys.stderr.flush()
 
 
-def kernel_sources_sha256() -> str:
+def kernel_sources_sha256(sources) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -225,11 +230,13 @@ def main() -> int:
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = round(ach / roof["peak"], 4)
     tr = TRAFFIC.get(cfg.name)
-    roof["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256()
+    sources = PREFILL_SOURCES if cfg.name == "prefill" else DECODE_SOURCES
+    roof["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256(sources)
                                                  and not args.no_flush) else None
     roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
     roof["kernel"] = ("prefill_gemm_kernel<0, *> (tiled gate/up product + SiLU*up)" if cfg.name == "prefill"
-                      else "gemm1_decode_kernel (gate/up product + SiLU*up)")
+                      else "gate/up product + SiLU*up (gemm1_decode_kernel, or gemm1_stream_kernel for fp8 "
+                           "layers whose plan takes the long-stream variant)")
     roof["avg_launch_us"] = round(g1_total_ms * 1e3 / n_g1, 2)
     roof["launches"] = n_g1
 

@@ -2,19 +2,21 @@
 //
 // At prefill every active expert holds hundreds to thousands of tokens, so the
 // products are compute-bound and both operands are reused: a work item is a
-// 512 x 128 tile (512 weight rows x 128 tokens of one expert) whose operands
+// 256 x 128 tile (256 weight rows x 128 tokens of one expert) whose operands
 // are staged through LDS, K-step by K-step.  The token dimension is grouped by
 // the align step with a block of 128: block b holds tokens of expert
 // block_expert[b] only, padded with the sentinel, so an item's tokens share
 // one expert.  Weight rows stay the MFMA's A operand and tokens the B operand,
 // as in the decode kernels; the 32x32x64 fp8 MFMA is used.
 //
-// Four waves, one per SIMD, each own 128 weight rows x all 128 tokens (4 x 4
-// MFMA tiles, accumulators in AGPRs).  That shape needs the fewest LDS bytes
-// per MFMA: per 64-byte K-step a CU reads 64 KB of fragments and writes 40 KB
-// of operands into LDS against 16 MFMAs per SIMD, which keeps the LDS port
-// (128 bytes per clock) below the matrix pipes.  With one wave per SIMD there
-// is no second wave to fill the matrix pipe, so every LDS read and DMA is
+// Four waves, one per SIMD, each own 64 weight rows x all 128 tokens (2 x 4
+// MFMA tiles, accumulators in AGPRs).  A K-step is 128 bytes (two MFMA
+// k-steps), so every 1 KB direct-to-LDS load covers eight whole cache lines of
+// eight rows: the texture units, not the LDS port or the matrix pipes, are the
+// busiest part of the CU here, and a load of sixteen half lines costs them
+// twice as much.  Per K-step a CU reads 96 KB of fragments and writes 48 KB of
+// operands into LDS against 16 MFMAs per SIMD.  With one wave per SIMD there is
+// no second wave to fill the matrix pipe, so every LDS read and DMA is
 // interleaved between MFMAs (sched_group_barrier) instead of being issued as a
 // block.
 //
@@ -23,9 +25,9 @@
 // share operands in that XCD's L2 (pf_map); one persistent workgroup per CU
 // walks them.
 //
-// Pipeline: both operand tiles of each 64-byte K-step are loaded from global
-// memory straight into a four-deep LDS ring (direct-to-LDS loads, no staging
-// registers), three steps ahead of the MFMAs, with one barrier per step.
+// Pipeline: both operand tiles of each K-step are loaded from global memory
+// straight into a three-deep LDS ring (direct-to-LDS loads, no staging
+// registers), two steps ahead of the MFMAs, with one barrier per step.
 #pragma once
 
 #include <type_traits>
