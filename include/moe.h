@@ -117,9 +117,9 @@ moe_status_t moe_quant_e4m3(const float* in, int64_t n, const float* scale, uint
  *
  * Each product of the decode path (fewer than 8192 pairs, or bf16) has two
  * variants: the K-split variant (one 16-feature or 32-row tile per wave, K
- * split over the waves of a workgroup) and, in fp8 mode, the long-stream
- * variant (each wave walks several tiles over the whole K range, its load
- * pipeline running from tile to tile).
+ * split over the waves of a workgroup) and the long-stream variant (each wave
+ * walks several tiles over the whole K range, its load pipeline running from
+ * tile to tile).
  */
 typedef struct {
   int32_t gemm1_ksplit;      /* K-split gate/up: waves of a workgroup splitting K: 1, 2 or 4 */
@@ -128,10 +128,10 @@ typedef struct {
   int32_t token_tiles;       /* 16-token tiles held per pass, both products: 1..4 */
   int32_t unroll;            /* MFMA K-steps per pipeline stage, both products: bf16 2 or 4, fp8 1 or 2 */
   int32_t gemm2_wave_ksplit; /* K-split down: waves of a workgroup splitting K: 1, 2 or 4 */
-  int32_t gemm1_stream_tiles; /* fp8 gate/up: > 0 long-stream variant with this many feature tiles per
-                                 wave (1..16), < 0 K-split variant */
-  int32_t gemm2_stream_tiles; /* fp8 down: > 0 long-stream variant with this many row tiles per wave
+  int32_t gemm1_stream_tiles; /* gate/up: > 0 long-stream variant with this many feature tiles per wave
                                  (1..16), < 0 K-split variant */
+  int32_t gemm2_stream_tiles; /* down: > 0 long-stream variant with this many row tiles per wave (1..16),
+                                 < 0 K-split variant */
 } moe_tuning_t;
 
 /*

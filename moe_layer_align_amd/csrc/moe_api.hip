@@ -183,7 +183,7 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, con
   }
   for (int* tw : {&p->tw1, &p->tw2}) {
     const int v = tw == &p->tw1 ? (t ? t->gemm1_stream_tiles : 0) : (t ? t->gemm2_stream_tiles : 0);
-    if (v > 16 || (v > 0 && !fp8)) return MOE_ERR_UNSUPPORTED;
+    if (v > 16) return MOE_ERR_UNSUPPORTED;
     if (v != 0) *tw = v > 0 ? v : 0;
   }
   if (p->tw1 > 0 && (H / kstep) % p->u1 != 0) {  // whole stages per row
@@ -265,39 +265,41 @@ bool g1_nt(int nt, int u, int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
   return false;
 }
 
-// long-stream variants (fp8)
-template <int HF, int NT>
+// long-stream variants
+template <bool FP8, int HF, int NT>
 bool g1s_u(int u, int tw, dim3 g, hipStream_t st, const Gemm1Args& a) {
-  if (u == 1) gemm1_stream_kernel<true, HF, NT, 1><<<g, 256, 0, st>>>(a, tw);
-  else if (u == 2) gemm1_stream_kernel<true, HF, NT, 2><<<g, 256, 0, st>>>(a, tw);
+  constexpr int U0 = FP8 ? 1 : 2;  // the two unrolls of the dtype: U0 and 2*U0
+  if (u == U0) gemm1_stream_kernel<FP8, HF, NT, U0><<<g, 256, 0, st>>>(a, tw);
+  else if (u == 2 * U0) gemm1_stream_kernel<FP8, HF, NT, 2 * U0><<<g, 256, 0, st>>>(a, tw);
   else return false;
   return true;
 }
 
-template <int HF>
+template <bool FP8, int HF>
 bool g1s_nt(int nt, int u, int tw, dim3 g, hipStream_t st, const Gemm1Args& a) {
   switch (nt) {
-    case 1: return g1s_u<HF, 1>(u, tw, g, st, a);
-    case 2: return g1s_u<HF, 2>(u, tw, g, st, a);
-    case 4: return g1s_u<HF, 4>(u, tw, g, st, a);
+    case 1: return g1s_u<FP8, HF, 1>(u, tw, g, st, a);
+    case 2: return g1s_u<FP8, HF, 2>(u, tw, g, st, a);
+    case 4: return g1s_u<FP8, HF, 4>(u, tw, g, st, a);
   }
   return false;
 }
 
-template <int HF, int NT>
+template <bool FP8, int HF, int NT>
 bool g2s_u(int u, int tw, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  if (u == 1) gemm2_stream_kernel<true, HF, NT, 1><<<g, 256, lds, st>>>(a, tw);
-  else if (u == 2) gemm2_stream_kernel<true, HF, NT, 2><<<g, 256, lds, st>>>(a, tw);
+  constexpr int U0 = FP8 ? 1 : 2;
+  if (u == U0) gemm2_stream_kernel<FP8, HF, NT, U0><<<g, 256, lds, st>>>(a, tw);
+  else if (u == 2 * U0) gemm2_stream_kernel<FP8, HF, NT, 2 * U0><<<g, 256, lds, st>>>(a, tw);
   else return false;
   return true;
 }
 
-template <int HF>
+template <bool FP8, int HF>
 bool g2s_nt(int nt, int u, int tw, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
   switch (nt) {
-    case 1: return g2s_u<HF, 1>(u, tw, g, lds, st, a);
-    case 2: return g2s_u<HF, 2>(u, tw, g, lds, st, a);
-    case 4: return g2s_u<HF, 4>(u, tw, g, lds, st, a);
+    case 1: return g2s_u<FP8, HF, 1>(u, tw, g, lds, st, a);
+    case 2: return g2s_u<FP8, HF, 2>(u, tw, g, lds, st, a);
+    case 4: return g2s_u<FP8, HF, 4>(u, tw, g, lds, st, a);
   }
   return false;
 }
@@ -672,8 +674,9 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     bool ok;
     if (plan.tw1 > 0) {
       const dim3 gs((unsigned)cdiv(I / 16, 4 * plan.tw1), (unsigned)n_act, (unsigned)plan.passes1);
-      ok = hdyn ? g1s_nt<H_F32>(plan.nt1, plan.u1, plan.tw1, gs, st, g)
-                : g1s_nt<H_E4M3>(plan.nt1, plan.u1, plan.tw1, gs, st, g);
+      ok = !fp8  ? g1s_nt<false, H_BF16>(plan.nt1, plan.u1, plan.tw1, gs, st, g)
+           : hdyn ? g1s_nt<true, H_F32>(plan.nt1, plan.u1, plan.tw1, gs, st, g)
+                  : g1s_nt<true, H_E4M3>(plan.nt1, plan.u1, plan.tw1, gs, st, g);
     } else if (!fp8)
       ok = g1_nt<false, H_BF16>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
     else if (hdyn)
@@ -694,8 +697,9 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     bool ok;
     if (plan.tw2 > 0) {
       const dim3 gs((unsigned)cdiv(H / 32, 4 * plan.tw2), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
-      ok = hf == H_F32 ? g2s_nt<H_F32>(plan.nt2, plan.u2, plan.tw2, gs, plan.lds2, st, g)
-                       : g2s_nt<H_E4M3>(plan.nt2, plan.u2, plan.tw2, gs, 0, st, g);
+      ok = hf == H_BF16 ? g2s_nt<false, H_BF16>(plan.nt2, plan.u2, plan.tw2, gs, 0, st, g)
+           : hf == H_F32 ? g2s_nt<true, H_F32>(plan.nt2, plan.u2, plan.tw2, gs, plan.lds2, st, g)
+                         : g2s_nt<true, H_E4M3>(plan.nt2, plan.u2, plan.tw2, gs, 0, st, g);
     } else if (hf == H_BF16)
       ok = g2_nt<false, H_BF16>(plan.nt2, plan.u2, plan.wks2, grid, 0, st, g);
     else if (hf == H_F32)

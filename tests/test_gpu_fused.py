@@ -66,7 +66,10 @@ def test_tuning_variants_agree():
     for t in [moe.Tuning(gemm1_ksplit=1, gemm2_ksplit=1, token_tiles=1, unroll=2, gemm2_wave_ksplit=4),
               moe.Tuning(gemm1_ksplit=2, gemm2_ksplit=4, token_tiles=2, unroll=4, gemm2_wave_ksplit=2),
               moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=16, token_tiles=4, unroll=2, gemm2_wave_ksplit=1),
-              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=2, token_tiles=3, unroll=2, gemm2_wave_ksplit=4)]:
+              moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=2, token_tiles=3, unroll=2, gemm2_wave_ksplit=4),
+              # long-stream variants in bf16
+              moe.Tuning(gemm1_stream_tiles=3, gemm2_stream_tiles=5, token_tiles=2, unroll=2),
+              moe.Tuning(gemm1_stream_tiles=1, gemm2_stream_tiles=16, token_tiles=4, unroll=4, gemm2_ksplit=4)]:
         compare(cfg, 33, seed=7, weights=w, tuning=t)
     cfg8 = cfg_of("fp8", 8, 2, 1024, 512)
     w8 = gen_weights(cfg8, 7, device=DEV)
