@@ -37,6 +37,23 @@ def test_small_layer(dtype, xs, hs, M):
     compare(cfg, M, seed=M, x_scale=xs, h_scale=hs)
 
 
+# Routing inside the fused call: the one-workgroup prologue holds ceil(E/16)
+# logits per lane (1, 2, 4, 8 or 16 keys, E <= 256), beyond that the
+# multi-workgroup router; M spans several 64-token routing passes and ends
+# with a partial wave of token rows.
+@pytest.mark.parametrize("E,k", [(17, 3), (33, 5), (64, 8), (65, 2), (200, 8), (256, 16), (300, 4)])
+def test_fused_routing_key_widths(E, k):
+    compare(cfg_of("bf16", E, k, 256, 128), 61, seed=E)
+
+
+def test_fused_one_workgroup_align_with_router():
+    # fp8 with M*H above the prologue's quantisation limit but M*k <= 1024:
+    # multi-workgroup router (x amax in fixed chunks), one-workgroup align
+    # whose other workgroups quantise x
+    compare(cfg_of("fp8", 64, 4, 4096, 128), 40, seed=21)
+    compare(cfg_of("fp8", 64, 4, 4096, 128), 40, seed=22, x_scale=0.02, h_scale=0.02)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_single_expert_top1(dtype):
     compare(cfg_of(dtype, 1, 1, 256, 256), 9, seed=3)
