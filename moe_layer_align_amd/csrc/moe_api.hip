@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -363,31 +364,42 @@ bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float*
 // on XCD b % 8 while it walks items b, b + wgs, ...  Cached per device.
 moe_status_t persistent_wgs(int* wgs) {
   constexpr int kMaxDevices = 64;
-  static int cached[kMaxDevices] = {};
+  static std::atomic<int> cached[kMaxDevices];  // 0 until queried; callers may race, all store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_DEVICE;
-  if (dev < kMaxDevices && cached[dev] > 0) {
-    *wgs = cached[dev];
-    return MOE_OK;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *wgs = c;
+      return MOE_OK;
+    }
   }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
     return MOE_ERR_DEVICE;
   const int n = cus / 8 * 8;
-  if (dev < kMaxDevices) cached[dev] = n;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   *wgs = n;
   return MOE_OK;
 }
 
+// The dynamic LDS ceiling of a prefill kernel is raised once per kernel and
+// device (the current device, as for the launch that follows); a failure to
+// raise it is reported as MOE_ERR_DEVICE.
 template <int MODE, bool HDYN>
-void launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
-  static bool lds_set = false;  // the dynamic LDS ceiling is raised once per kernel
-  if (!lds_set) {
-    (void)hipFuncSetAttribute((const void*)prefill_gemm_kernel<MODE, HDYN>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds);
-    lds_set = true;
+moe_status_t launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> lds_set[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_DEVICE;
+  if (dev >= kMaxDevices || !lds_set[dev].load(std::memory_order_acquire)) {
+    if (hipFuncSetAttribute((const void*)prefill_gemm_kernel<MODE, HDYN>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds) != hipSuccess)
+      return MOE_ERR_DEVICE;
+    if (dev < kMaxDevices) lds_set[dev].store(true, std::memory_order_release);
   }
   prefill_gemm_kernel<MODE, HDYN><<<wgs, kPfThreads, kPfLds, st>>>(g);
+  return MOE_OK;
 }
 
 void launch_prologue_small(const float* logits, int M, int E, int k, int32_t* ids, float* wts, int B,
@@ -530,10 +542,9 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
                   a->h_scale, h, h_amax};
-    if (hdyn)
-      launch_prefill<0, true>(std::min(wgs, items), st, g);
-    else
-      launch_prefill<0, false>(std::min(wgs, items), st, g);
+    rc = hdyn ? launch_prefill<0, true>(std::min(wgs, items), st, g)
+              : launch_prefill<0, false>(std::min(wgs, items), st, g);
+    if (rc != MOE_OK) return rc;
   }
   rec(5);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -548,10 +559,9 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w2, hq, seg, H, I, k, (int)P, T, items, a->w2_scale, a->h_scale, h_amax, nullptr,
                   (uint8_t*)part, nullptr};
-    if (hdyn)
-      launch_prefill<1, true>(std::min(wgs, items), st, g);
-    else
-      launch_prefill<1, false>(std::min(wgs, items), st, g);
+    rc = hdyn ? launch_prefill<1, true>(std::min(wgs, items), st, g)
+              : launch_prefill<1, false>(std::min(wgs, items), st, g);
+    if (rc != MOE_OK) return rc;
   }
   rec(7);
   if ((rc = launch_status()) != MOE_OK) return rc;
