@@ -81,7 +81,7 @@ int64_t align_capacity(int64_t P, int E, int B) {
 // ---------------------------------------------------------------- workspace
 struct Layout {
   size_t ids, wts, counts, offsets, sorted, block_expert, num_padded, active, num_active;
-  size_t xamax_part, scale_slot, h_amax, xq, h, part, total;
+  size_t xamax_part, scale_slot, h_amax, hist, xq, h, part, total;
   int64_t capacity;
   int n_blocks, n_route_wg;
 };
@@ -111,6 +111,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
   L.xamax_part = take((size_t)L.n_route_wg * 4);
   L.scale_slot = take(4);
   L.h_amax = take(4);
+  L.hist = take((size_t)cdiv(M, 4 * kRouteRows) * E * 4);
   const bool fp8 = dt == MOE_DTYPE_FP8_E4M3;
   L.xq = take(fp8 ? (size_t)M * H : 0);
   // h: bf16 (bf16 layers), fp32 (fp8 decode), fp32 + its e4m3 copy (fp8 prefill)
@@ -418,10 +419,15 @@ void launch_prologue_small(const float* logits, int M, int E, int k, int32_t* id
   }
 }
 
+// The router's per-workgroup expert counts serve the align step when its
+// workgroups hold a whole number of routing workgroups' pairs (k a power of
+// two up to 16).
+bool hist_usable(int k) { return is_pow2(k) && k <= 16; }
+
 void launch_align(const int32_t* ids, int64_t P, int E, int B, const AlignOut& o, const QuantXArgs& q, int n_quant_wg,
-                  hipStream_t st) {
+                  hipStream_t st, const AlignHist& hist = AlignHist{nullptr, 0, 0}) {
   const int n_align = (int)std::max<int64_t>(1, cdiv(P, kAlignChunk));
-  align_kernel<<<n_align + n_quant_wg, 256, 0, st>>>(ids, (int)P, E, B, log2i(B), log2i(E), n_align, o, q);
+  align_kernel<<<n_align + n_quant_wg, 256, 0, st>>>(ids, (int)P, E, B, log2i(B), log2i(E), n_align, o, q, hist);
 }
 
 moe_status_t check_shape(int M, int E, int k) {
@@ -509,9 +515,11 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   };
   moe_status_t rc;
   const int M = a->M, E = a->E, H = a->H, I = a->I, k = a->top_k;
+  int32_t* hist_buf = (int32_t*)(ws + L.hist);
   const int64_t P = (int64_t)M * k;
   rec(0);
-  RouteFusedArgs fa{(const uint16_t*)a->x, H, a->x_scale ? nullptr : xamax_part, hdyn ? h_amax : nullptr};
+  int32_t* hist = hist_usable(k) ? hist_buf : nullptr;
+  RouteFusedArgs fa{(const uint16_t*)a->x, H, a->x_scale ? nullptr : xamax_part, hdyn ? h_amax : nullptr, hist};
   launch_route(a->logits, M, E, k, ids, wts, fa, st);
   rec(1);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -524,7 +532,8 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   q.static_scale = a->x_scale;
   q.xq = xq;
   q.scale_slot = scale_slot;
-  launch_align(ids, P, E, kPfTok, o, q, (int)cdiv(q.n, 256 * 16), st);
+  launch_align(ids, P, E, kPfTok, o, q, (int)cdiv(q.n, 256 * 16), st,
+               AlignHist{hist, (int)cdiv(M, 4 * kRouteRows), hist ? 16 / k : 0});
   rec(3);
   if ((rc = launch_status()) != MOE_OK) return rc;
 
@@ -641,8 +650,10 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   } else {
     // 1. routing (+ per-workgroup amax of x)
     rec(0);
+    // the routing workgroups' expert counts serve the multi-workgroup align
+    int32_t* hist = (P > kSmallPairs && hist_usable(k)) ? (int32_t*)(ws + L.hist) : nullptr;
     RouteFusedArgs fa{(const uint16_t*)a->x, H, (fp8 && !a->x_scale) ? xamax_part : nullptr,
-                      hdyn ? h_amax : nullptr};
+                      hdyn ? h_amax : nullptr, hist};
     launch_route(a->logits, M, E, k, ids, wts, fa, st);
     rec(1);
     if ((rc = launch_status()) != MOE_OK) return rc;
@@ -665,7 +676,8 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
       const unsigned g = 1 + (fp8 ? (unsigned)cdiv(q.n, kSmallQuantPerWg) : 0u);
       align_small_kernel<<<g, 1024, 0, st>>>(ids, (int)P, E, log2i(kAlignBlockFused), log2i(E), o, q);
     } else {
-      launch_align(ids, P, E, kAlignBlockFused, o, q, n_quant, st);
+      launch_align(ids, P, E, kAlignBlockFused, o, q, n_quant, st,
+                   AlignHist{hist, (int)cdiv(M, 4 * kRouteRows), hist ? 16 / k : 0});
     }
     rec(3);
     if ((rc = launch_status()) != MOE_OK) return rc;

@@ -36,6 +36,7 @@ struct RouteFusedArgs {
   int H;
   float* x_amax_part;    // [gridDim.x] per-workgroup amax of |x| (may be null)
   unsigned* h_amax;      // global amax of |h| to clear (may be null)
+  int32_t* hist;         // [ceil(M/16)][E] expert counts of each routing workgroup's pairs (may be null)
 };
 
 // Top-k of the token whose logits row is `row` (null for a row without a
@@ -107,9 +108,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     int e;
     float w;
     route_row<NPL>(m < M ? logits + (int64_t)m * E : nullptr, E, K, l16, &e, &w);
-    if (m < M && l16 < K) {
+    const bool pair = m < M && l16 < K;
+    if (pair) {
       ids[(int64_t)m * K + l16] = e;
       wts[(int64_t)m * K + l16] = w;
+    }
+    if (fa.hist) {  // this workgroup's expert counts, for the align step
+      __shared__ int s_hist[kMaxExperts];
+      for (int i = threadIdx.x; i < E; i += 256) s_hist[i] = 0;
+      __syncthreads();
+      if (pair) atomicAdd(&s_hist[e], 1);
+      __syncthreads();
+      for (int i = threadIdx.x; i < E; i += 256) fa.hist[(int64_t)blockIdx.x * E + i] = s_hist[i];
     }
   }
   if (fa.x_amax_part) {
@@ -226,9 +236,18 @@ __device__ __forceinline__ int block_excl_scan_pair(int v0, int v1, int* s_wtot,
   return before + incl - (v0 + v1);
 }
 
+// Per-routing-workgroup expert counts (from route_topk_kernel), usable when
+// a routing workgroup's 16 tokens hold a whole number of pairs per 256 (k a
+// power of two up to 16): rows r cover pairs [16k*r, 16k*(r+1)).
+struct AlignHist {
+  const int32_t* counts;  // [rows][E], or null: count the ids themselves
+  int rows;
+  int rows_per_wave;      // 256 / (16 k)
+};
+
 __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ ids, int P, int E, int B,
                                                     int log2B, int id_bits, int n_align_wgs, AlignOut o,
-                                                    QuantXArgs q) {
+                                                    QuantXArgs q, AlignHist hist) {
   if ((int)blockIdx.x >= n_align_wgs) {
     quant_x_part<256>(q, blockIdx.x - n_align_wgs);
     return;
@@ -252,8 +271,46 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // histogram of all P ids, 16 loads in flight per thread
   constexpr int kHistBatch = 16;
+  if (hist.counts) {
+    // the routing workgroups' counts: every row adds to the totals, rows
+    // before the chunk to s_before, the chunk's rows to their wave
+    // thread t sums column e = t % E of rows t/E, t/E + rstep, ... in
+    // registers (no division in the loop, one LDS atomic per column and
+    // thread at the end)
+    const int rw = hist.rows_per_wave;
+    const int r0 = blockIdx.x * 4 * rw;
+    const int rstep = E < 256 ? 256 / E : 1;
+    for (int e0 = 0; e0 < E; e0 += 256) {
+      const int e = e0 + (E < 256 ? tid % E : tid);
+      const int rfirst = E < 256 ? tid / E : 0;
+      if (e < E && rfirst < rstep) {
+        int tot = 0, before = 0, wv[4] = {0, 0, 0, 0};
+        for (int rb = rfirst; rb < hist.rows; rb += rstep * kHistBatch) {
+          int cv[kHistBatch];
+#pragma unroll
+          for (int u = 0; u < kHistBatch; ++u) {
+            const int r = rb + rstep * u;
+            cv[u] = r < hist.rows ? hist.counts[(int64_t)r * E + e] : 0;
+          }
+#pragma unroll
+          for (int u = 0; u < kHistBatch; ++u) {
+            const int r = rb + rstep * u;
+            tot += cv[u];
+            if (r < r0) before += cv[u];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              if (r >= r0 + w * rw && r < r0 + (w + 1) * rw) wv[w] += cv[u];
+          }
+        }
+        atomicAdd(&s_total[e], tot);
+        atomicAdd(&s_before[e], before);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) atomicAdd(&s_wave[w][e], wv[w]);
+      }
+    }
+  } else {
+  // histogram of all P ids, 16 loads in flight per thread
   for (int f0 = tid; f0 < P; f0 += 256 * kHistBatch) {
     int ev[kHistBatch];
 #pragma unroll
@@ -276,6 +333,7 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
       else if (f < ce)
         atomicAdd(&s_wave[(f - cb) >> 8][e], 1);
     }
+  }
   }
   __syncthreads();
 
