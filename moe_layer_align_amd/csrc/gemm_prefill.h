@@ -121,15 +121,24 @@ __device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK +
 // experts cut by a range boundary have their weights read by two XCDs) and
 // all weight tiles for them.  Inside an XCD the items are numbered densely
 // (no holes, so the workgroups walking them round robin get equal shares):
-// by groups of kPfGB blocks, within a block group by groups of kPfGT tiles,
-// the last group of either kind possibly smaller.  A full group of kPfGT x
-// kPfGB items is about one per CU of an XCD, so workgroups running together
-// share weight tiles and token blocks in that XCD's L2.  Returns false past
-// the XCD's last item (all later indices of that XCD are past it too).
-constexpr int kPfGT = 4;  // weight tiles per raster group
-constexpr int kPfGB = 8;  // token blocks per raster group
+// by groups of GB blocks, within a block group by groups of GT tiles, the
+// last group of either kind possibly smaller.  A full group of GT x GB items
+// is about one per CU of an XCD, so workgroups running together share weight
+// tiles and token blocks in that XCD's L2.  Returns false past the XCD's last
+// item (all later indices of that XCD are past it too).  Group shapes, from a
+// sweep of (GT, GB) over {2,4,8} x {4,8,16} on the E=128 top-8 H=4096 I=1536
+// M=4096 layer: 2 x 16 for the gate/up product (12 tiles of 128 features,
+// 2 % faster than 4 x 8), 8 x 4 for the down product (16 tiles of 256 output
+// rows, 3 % faster).
+template <int MODE>
+struct PfRaster {
+  static constexpr int GT = MODE == 0 ? 2 : 8;   // weight tiles per raster group
+  static constexpr int GB = MODE == 0 ? 16 : 4;  // token blocks per raster group
+};
 
+template <int MODE>
 __device__ __forceinline__ bool pf_map(int L, int T, int nb, int* tile, int* blk) {
+  constexpr int kPfGT = PfRaster<MODE>::GT, kPfGB = PfRaster<MODE>::GB;
   const int c = L & 7, j = L >> 3;
   const int nbx = (nb + 7) >> 3;                    // blocks per XCD
   const int nbc = max(0, min(nbx, nb - c * nbx));  // blocks of XCD c
@@ -178,9 +187,10 @@ struct PfItem {
 // The work item at linear index L, or false when the workgroup has none left
 // (stride, a multiple of 8, keeps L on one XCD).  Uniform across the
 // workgroup; the loads are waited for where their values are first used.
+template <int MODE>
 __device__ __forceinline__ bool pf_next(const PrefillArgs& a, int nb, int& L, int stride, PfItem& it) {
   int tile = 0, blk = 0;
-  if (L >= a.items || !pf_map(L, a.tiles, nb, &tile, &blk)) return false;  // later indices of this XCD are past its items too
+  if (L >= a.items || !pf_map<MODE>(L, a.tiles, nb, &tile, &blk)) return false;  // later indices of this XCD are past its items too
   const int e = a.seg.block_expert[blk];  // every block below num_padded belongs to an expert
   it.tile = tile;
   it.blk = blk;
@@ -197,10 +207,11 @@ struct PfFetch {
   bool ok;
   int tile, blk, e, off, cnt;
 };
+template <int MODE>
 __device__ __forceinline__ void pf_fetch_a(const PrefillArgs& a, int nb, int L, bool want, PfFetch& f) {
   f.tile = 0;
   f.blk = 0;
-  f.ok = want && L < a.items && pf_map(L, a.tiles, nb, &f.tile, &f.blk);
+  f.ok = want && L < a.items && pf_map<MODE>(L, a.tiles, nb, &f.tile, &f.blk);
   f.e = a.seg.block_expert[f.ok ? f.blk : 0];
 }
 __device__ __forceinline__ void pf_fetch_b(const PrefillArgs& a, PfFetch& f) {
@@ -282,10 +293,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   const int stride = gridDim.x;
   int L = blockIdx.x;
   PfItem cur;
-  if (!pf_next(a, nb, L, stride, cur)) return;
+  if (!pf_next<MODE>(a, nb, L, stride, cur)) return;
   PfItem nxt = cur;  // stays a valid item when there is no next one (its loads are then unused)
   L += stride;
-  bool has_next = pf_next(a, nb, L, stride, nxt);
+  bool has_next = pf_next<MODE>(a, nb, L, stride, nxt);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the wave's branches scalar
@@ -475,7 +486,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
     // item after the next is fetched across the last three steps
     PfFetch fnn;
     body(F0, F1, nk - 4, cs, nk - 1, std::integral_constant<int, 2>{},
-         [&] { pf_fetch_a(a, nb, L + stride, has_next, fnn); });
+         [&] { pf_fetch_a<MODE>(a, nb, L + stride, has_next, fnn); });
     if (!has_next) ns = cs;  // dummy source after the last item (valid addresses, never read)
     finish_src(ns);          // the next item's token ids are needed from here on
     // steps nk-3 and nk-2 load the next item's steps 0 and 1; step nk-1 only
