@@ -630,14 +630,26 @@ __global__ __launch_bounds__(256) void prefill_finalize_kernel(const uint16_t* _
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= (int64_t)M * H) return;
   const int64_t m = i / H, n = i - m * H;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < top_k; ++j) {
-    const float w = topk_w[m * top_k + j];
-    const u32x4 v = *(const u32x4*)(part + (m * top_k + j) * H + n);
+  // all k partial rows are loaded before the sum (k loads in flight per
+  // thread), then summed with j ascending
+  u32x4 v[kMaxTopK];
+  float w[kMaxTopK];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += w * bf16_lo(v[q]);
-      acc[2 * q + 1] += w * bf16_hi(v[q]);
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < top_k) {
+      v[j] = *(const u32x4*)(part + (m * top_k + j) * H + n);
+      w[j] = topk_w[m * top_k + j];
+    }
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < top_k) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += w[j] * bf16_lo(v[j][q]);
+        acc[2 * q + 1] += w[j] * bf16_hi(v[j][q]);
+      }
     }
   }
   u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
