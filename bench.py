@@ -59,8 +59,8 @@ TRAFFIC = {
                 "bytes_per_launch": 1510116716},
     "qwen3": {"src_sha256": "94eab15d189c8070e5d81afd5826fcaad8434265d20eca846d4aa778a7bc701c",
               "bytes_per_launch": 241727958},
-    "prefill": {"src_sha256": "7a15c971a6748887ffc9bf615e3d170adcf60890ffdfee2111f1b88dc57eb790",
-                "bytes_per_launch": 2763971872},
+    "prefill": {"src_sha256": "7d6b8ed93b9685961c4e075082acb34757988fefebc65bdd28f4a2d5d4a431a9",
+                "bytes_per_launch": 3062722821},
 }
 
 
