@@ -532,7 +532,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   q.static_scale = a->x_scale;
   q.xq = xq;
   q.scale_slot = scale_slot;
-  launch_align(ids, P, E, kPfTok, o, q, (int)cdiv(q.n, 256 * 16), st,
+  launch_align(ids, P, E, kPfTok, o, q, (int)cdiv(q.n, kAlignQuantPerWg), st,
                AlignHist{hist, (int)cdiv(M, 4 * kRouteRows), hist ? 16 / k : 0});
   rec(3);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -670,7 +670,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
       q.static_scale = a->x_scale;
       q.xq = xq;
       q.scale_slot = scale_slot;
-      n_quant = (int)cdiv(q.n, 256 * 16);
+      n_quant = (int)cdiv(q.n, kAlignQuantPerWg);
     }
     if (P <= kSmallPairs) {  // one 1024-thread align workgroup, 16K-element quantising workgroups
       const unsigned g = 1 + (fp8 ? (unsigned)cdiv(q.n, kSmallQuantPerWg) : 0u);

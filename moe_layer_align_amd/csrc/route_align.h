@@ -196,9 +196,11 @@ __device__ __forceinline__ u32x4 quant16_e4m3(const u32x4& a0, const u32x4& a1, 
 }
 
 // x -> e4m3 with the per-tensor scale (static, or amax/448 from the router's
-// per-workgroup partial maxima), by a workgroup of NT threads, 16 elements
-// per thread.
-template <int NT>
+// per-workgroup partial maxima), by a workgroup of NT threads, PER groups of
+// 16 elements per thread (NT*16 apart, all loads issued before the first
+// conversion): every workgroup first reduces the partial maxima, so a
+// workgroup quantises enough elements to amortise that.
+template <int NT, int PER = 1>
 __device__ void quant_x_part(const QuantXArgs& q, int wg) {
   __shared__ float s_red[NT / 64];
   float s;
@@ -217,10 +219,26 @@ __device__ void quant_x_part(const QuantXArgs& q, int wg) {
   }
   if (wg == 0 && threadIdx.x == 0) *q.scale_slot = s;
   const float r = 1.0f / s;
-  const int64_t i = ((int64_t)wg * NT + threadIdx.x) * 16;
-  if (i >= q.n) return;
-  *(u32x4*)(q.xq + i) = quant16_e4m3(*(const u32x4*)(q.x + i), *(const u32x4*)(q.x + i + 8), r);
+  const int64_t i0 = ((int64_t)wg * NT * PER + threadIdx.x) * 16;
+  u32x4 lo[PER], hi[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int64_t i = i0 + (int64_t)p * NT * 16;
+    if (i < q.n) {
+      lo[p] = *(const u32x4*)(q.x + i);
+      hi[p] = *(const u32x4*)(q.x + i + 8);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int64_t i = i0 + (int64_t)p * NT * 16;
+    if (i < q.n) *(u32x4*)(q.xq + i) = quant16_e4m3(lo[p], hi[p], r);
+  }
 }
+
+// elements quantised by one quantising workgroup of align_kernel
+constexpr int kAlignQuantPer = 4;
+constexpr int kAlignQuantPerWg = 256 * 16 * kAlignQuantPer;
 
 // Exclusive scan of v over up to 512 entries held two per thread (256 threads).
 // Returns the exclusive prefix for entry 2t; *total receives the sum.
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ 
                                                     int log2B, int id_bits, int n_align_wgs, AlignOut o,
                                                     QuantXArgs q, AlignHist hist) {
   if ((int)blockIdx.x >= n_align_wgs) {
-    quant_x_part<256>(q, blockIdx.x - n_align_wgs);
+    quant_x_part<256, kAlignQuantPer>(q, blockIdx.x - n_align_wgs);
     return;
   }
   __shared__ int s_total[kMaxExperts];
