@@ -315,9 +315,11 @@ def cpu_baseline(cfg, calls, weights, budget_s, unit, min_s=10.0):
     sec_per_pair = None
     while rounds == 0 or (spent < min(min_s, budget_s) and all(p.endswith(":all") for p in parts)):
         rounds += 1
-        for c in sorted(calls, key=lambda c: c["M"]):
+        ordered = sorted(calls, key=lambda c: c["M"])
+        for idx, c in enumerate(ordered):
             M = c["M"]
-            left = budget_s / len(calls) if sec_per_pair is None else (budget_s - spent) / len(calls)
+            # the budget left is shared by the points of this pass not yet run
+            left = budget_s / len(calls) if sec_per_pair is None else (budget_s - spent) / (len(ordered) - idx)
             n_tok = M if sec_per_pair is None else int(max(1, min(M, left / (sec_per_pair * cfg.k))))
             if sec_per_pair is None and M * cfg.k > 256:
                 n_tok = max(1, 256 // cfg.k)  # probe the rate first
