@@ -238,5 +238,30 @@ def test_prefill_full_static_scales(prefill_w):
     compare(CONFIGS["prefill"], M, seed=0, weights=prefill_w, tokens=toks, x_scale=0.011, h_scale=0.02)
 
 
+def test_prefill_full_dynamic_scales(prefill_w):
+    # the measured launch: M = 4096 with dynamic x and h scales; the oracle
+    # takes s_h over all 32768 pairs and y on sampled tokens
+    M = 4096
+    compare(CONFIGS["prefill"], M, seed=0, weights=prefill_w, tokens=[0, 1, 2, 1023, 2048, 3001, 4094, 4095])
+
+
+def test_prefill_path_repeat_calls_bitwise():
+    # persistent products, LDS-transposed down epilogue and the fixed-order
+    # combine: repeated calls on a stale workspace give the same bits
+    cfg = MoEConfig("pf_rep", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf")
+    w = gen_weights(cfg, 15, device=DEV)
+    x = gen_x(cfg.H, 1100, 15, sub=1100).to(DEV)
+    lg = gen_logits(cfg, 1100, 15, sub=1100).to(DEV)
+    ws = torch.empty(moe.workspace_size(1100, cfg.E, cfg.H, cfg.I, cfg.k, "fp8"), dtype=torch.uint8, device=DEV)
+    ws.fill_(0x7F)
+    s13 = torch.tensor([w[2]], device=DEV)
+    s2 = torch.tensor([w[3]], device=DEV)
+    ys = [moe.fused_forward(x, lg, w[0], w[1], cfg.k, "fp8", s13, s2, workspace=ws).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert bool(ys[0].float().isfinite().all())
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+
+
 def test_prefill_dynamic_scales(prefill_w):
     compare(CONFIGS["prefill"], 256, seed=0, weights=prefill_w, tokens=[0, 5, 100, 255])
