@@ -146,7 +146,14 @@ typedef struct {
  * fp8 mode: a_m = e4m3(x[m] / s_x) and hq = e4m3(h / s_h) (moe_quant_e4m3's
  * rounding); the products are rescaled by s_x*s_w13 and s_h*s_w2.  s_x and
  * s_h are the caller's static scales when given, else amax/448 over all of x
- * and over h of all pairs (1.0 when the amax is 0).
+ * and over h of all pairs (1.0 when the amax is 0).  The weight scales are
+ * one per tensor, or with weight_scale_per_channel one per weight row (output
+ * channel): row n of W13[e] (gate or up feature) is rescaled by
+ * w13_scale[e*2I + n] and row n of W2[e] (output feature) by w2_scale[e*H + n]
+ * (the pages name tensor-quantised FP8 experts and routing among
+ * quantisation schemes: "Fused MoE on Hopper, ...", TL;DR; ZICQ, "AWS Unveils
+ * MoE Kernel Optimizations ...", §Triton Backend Routing for FP8
+ * Quantization).
  * The expert products put expert-weight rows in the wide MFMA operand and
  * the few tokens in the narrow one; at decode sizes this is the orientation
  * the pages call Swap-AB (B^T A^T instead of A B, "Fused MoE on Hopper, ..."
@@ -159,8 +166,8 @@ typedef struct {
   const float* logits;     /* [M,E] fp32 router logits */
   const void* w13;         /* [E,2I,H] bf16 or e4m3; rows [0,I) gate, [I,2I) up */
   const void* w2;          /* [E,H,I] bf16 or e4m3 */
-  const float* w13_scale;  /* fp8: device fp32[1]; bf16: NULL */
-  const float* w2_scale;   /* fp8: device fp32[1]; bf16: NULL */
+  const float* w13_scale;  /* fp8: device fp32[1], or fp32[E*2I] per channel (16-byte aligned); bf16: NULL */
+  const float* w2_scale;   /* fp8: device fp32[1], or fp32[E*H] per channel (16-byte aligned); bf16: NULL */
   const float* x_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
   const float* h_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
   void* y;                 /* [M,H] bf16 output (overwritten) */
@@ -171,6 +178,8 @@ typedef struct {
   void* workspace;         /* device scratch, 256-byte aligned */
   size_t workspace_bytes;
   const moe_tuning_t* tuning; /* host pointer or NULL */
+  int32_t weight_scale_per_channel; /* fp8: 0 = one scale per weight tensor, 1 = one per weight row;
+                                       any other value, or non-zero in bf16 mode: MOE_ERR_INVALID_ARG */
 } moe_fused_args_t;
 
 /* Host-only: workspace bytes needed by moe_fused_forward for these sizes. */

@@ -51,6 +51,7 @@ class _FusedArgs(ctypes.Structure):
         ("topk_weights", ctypes.c_void_p), ("expert_counts", ctypes.c_void_p), ("scales_out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("tuning", ctypes.POINTER(Tuning)),
+        ("weight_scale_per_channel", ctypes.c_int32),
     ]
 
 
@@ -178,8 +179,10 @@ def fused_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: 
     """The fused layer (moe_fused_forward).
 
     x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
-    (dtype "bf16") or uint8 e4m3fn codes (dtype "fp8") with fp32 [1] device
-    scales; x_scale/h_scale: static fp8 activation scales or None (dynamic).
+    (dtype "bf16") or uint8 e4m3fn codes (dtype "fp8") with fp32 device
+    scales, either one per tensor ([1] each) or one per weight row (w13_scale
+    [E,2I], w2_scale [E,H]); x_scale/h_scale: static fp8 activation scales or
+    None (dynamic).
     events: optional list of 2*NUM_STAGES hipEvent_t handles (ints) recorded
     around the stages on the stream.
     """
@@ -192,7 +195,14 @@ def fused_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: 
     _need(logits, "logits", torch.float32, (M, E))
     _need(w13, "w13", wdt, (E, 2 * I, H))
     _need(w2, "w2", wdt, (E, H, I))
-    for name, s in (("w13_scale", w13_scale), ("w2_scale", w2_scale), ("x_scale", x_scale), ("h_scale", h_scale)):
+    per_channel = w13_scale is not None and w13_scale.dim() == 2
+    if per_channel:
+        if w2_scale is None:
+            raise ValueError("per-channel w13_scale needs a per-channel w2_scale")
+        _need(w13_scale, "w13_scale", torch.float32, (E, 2 * I))
+        _need(w2_scale, "w2_scale", torch.float32, (E, H))
+    for name, s in (("w13_scale", None if per_channel else w13_scale), ("w2_scale", None if per_channel else w2_scale),
+                    ("x_scale", x_scale), ("h_scale", h_scale)):
         if s is not None:
             _need(s, name, torch.float32, (1,))
     if out is None:
@@ -220,6 +230,7 @@ def fused_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: 
         expert_counts=_ptr(expert_counts), scales_out=_ptr(scales_out),
         workspace=_ptr(workspace), workspace_bytes=workspace.numel(),
         tuning=ctypes.pointer(tuning) if tuning is not None else None,
+        weight_scale_per_channel=int(per_channel),
     )
     if events is None:
         _check("moe_fused_forward", lib.moe_fused_forward(ctypes.byref(args), _stream(stream)))

@@ -143,12 +143,23 @@ struct Gemm1Args {
   const uint8_t* act;        // bf16 x [M][H] or e4m3 xq [M][H]
   Segments seg;
   int H, I, top_k;
-  const float* w_scale;      // fp8: s_w13
+  const float* w_scale;      // fp8: s_w13, one per tensor or one per W13 row ([E][2I], w_cs = 1)
   const float* x_scale;      // fp8: s_x in effect
   const float* h_scale;      // fp8 static h: s_h
   uint8_t* h;                // [P][I] in HFMT
   unsigned* h_amax;          // fp8 dynamic: running max of |h| (float bits)
+  int w_cs = 0;              // fp8: 1 = w_scale holds one scale per weight row, 0 = one per tensor
 };
+
+// fp8 dequantisation factors s_x * s_w of the four weight rows row0..row0+3
+// of expert e (rows_e rows per expert); with one scale per tensor (cs = 0)
+// every row reads w_scale[0].
+__device__ __forceinline__ void row_deq4(const float* w_scale, int cs, int e, int rows_e, int row0, float sa,
+                                         float (&d)[4]) {
+  const float* ws = w_scale + (int64_t)e * rows_e * cs;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[r] = sa * ws[(row0 + r) * cs];
+}
 
 // Body for NB (<= NT) token tiles; the kernel picks NB from the workgroup's
 // token count so that tiles with no token issue no loads and no MFMAs.
@@ -206,7 +217,12 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
     }
   }
 
-  const float deq = FP8 ? (*a.x_scale) * (*a.w_scale) : 1.0f;
+  // dequantisation of this lane's rows: gate rows i0+4kq.., up rows I+i0+4kq..
+  float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if constexpr (FP8) {
+    row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, i0 + kq * 4, *a.x_scale, dg);
+    row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, a.I + i0 + kq * 4, *a.x_scale, du);
+  }
   float rh = 1.0f;
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
   float hmax = 0.0f;
@@ -218,8 +234,8 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
       float hv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float g = acc[0][t][r] * deq;
-        const float u = acc[1][t][r] * deq;
+        const float g = acc[0][t][r] * dg[r];
+        const float u = acc[1][t][r] * du[r];
         hv[r] = g / (1.0f + expf(-g)) * u;
         hmax = fmaxf(hmax, fabsf(hv[r]));
       }
@@ -357,7 +373,7 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
     fo[t] = slot < cnt ? f : -1;
   }
 
-  const float deq = FP8 ? (*a.x_scale) * (*a.w_scale) : 1.0f;
+  const float sx = FP8 ? *a.x_scale : 1.0f;
   float rh = 1.0f;
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
   float hmax = 0.0f;
@@ -366,14 +382,19 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
   for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto epi = [&](int j, f32x4 (&c)[2][NB]) {
     const int i0 = (ft0 + 4 * j) * 16;
+    float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (FP8) {
+      row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, i0 + kq * 4, sx, dg);
+      row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, a.I + i0 + kq * 4, sx, du);
+    }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       if (fo[t] >= 0) {
         float hv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float g = c[0][t][r] * deq;
-          const float u = c[1][t][r] * deq;
+          const float g = c[0][t][r] * dg[r];
+          const float u = c[1][t][r] * du[r];
           hv[r] = g / (1.0f + expf(-g)) * u;
           hmax = fmaxf(hmax, fabsf(hv[r]));
         }
@@ -440,11 +461,12 @@ struct Gemm2Args {
   Segments seg;
   const float* topk_w;       // [P]
   int H, I, top_k, ksplit;
-  const float* w_scale;      // fp8: s_w2
+  const float* w_scale;      // fp8: s_w2, one per tensor or one per W2 row ([E][H], w_cs = 1)
   const float* h_scale;      // fp8 static: s_h
   const unsigned* h_amax;    // fp8 dynamic: max |h| (float bits)
   float* part;               // [ksplit][P][H] partial outputs
   int P;
+  int w_cs = 0;              // fp8: 1 = one scale per weight row, 0 = one per tensor
 };
 
 // LDS row stride (bytes) of the quantised token slice: Kw plus 16 bytes so
@@ -498,10 +520,12 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
   const int Kp = Kw / WKS;             // K range of the wave
   const int koff = kpart * Kp;
 
-  float deq = 1.0f;
+  // dequantisation of this lane's rows n0+4kq.. and n0+16+4kq..
+  float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (FP8) {
     const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
-    deq = sh * (*a.w_scale);
+    row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + kq * 4, sh, d0);
+    row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + 16 + kq * 4, sh, d1);
     if constexpr (QH) {
       stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
       __syncthreads();
@@ -558,8 +582,8 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
     if (slot < cnt) {
       const int f = a.seg.sorted_ids[seg + slot];
       float* dst = part + (int64_t)f * a.H + n0 + kq * 4;
-      *(f32x4*)dst = acc[0][t] * deq;
-      *(f32x4*)(dst + 16) = acc[1][t] * deq;
+      *(f32x4*)dst = acc[0][t] * f32x4{d0[0], d0[1], d0[2], d0[3]};
+      *(f32x4*)(dst + 16) = acc[1][t] * f32x4{d1[0], d1[1], d1[2], d1[3]};
     }
   }
 }
@@ -609,10 +633,9 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
   const int Kw = a.I / a.ksplit;
   const int kbeg = kslice * Kw;
 
-  float deq = 1.0f;
+  float sh = 1.0f;
   if constexpr (FP8) {
-    const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
-    deq = sh * (*a.w_scale);
+    sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
     if constexpr (QH) {
       stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
       __syncthreads();
@@ -646,12 +669,17 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
   for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto epi = [&](int j, f32x4 (&c)[2][NB]) {
     const int n0 = (rt0 + 4 * j) * 32;
+    float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (FP8) {
+      row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + kq * 4, sh, d0);
+      row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + 16 + kq * 4, sh, d1);
+    }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       if (fo[t] >= 0) {
         float* dst = part + (int64_t)fo[t] * a.H + n0 + kq * 4;
-        *(f32x4*)dst = c[0][t] * deq;
-        *(f32x4*)(dst + 16) = c[1][t] * deq;
+        *(f32x4*)dst = c[0][t] * f32x4{d0[0], d0[1], d0[2], d0[3]};
+        *(f32x4*)(dst + 16) = c[1][t] * f32x4{d1[0], d1[1], d1[2], d1[3]};
       }
       c[0][t] = c[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }

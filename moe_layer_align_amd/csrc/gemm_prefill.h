@@ -159,7 +159,7 @@ struct PrefillArgs {
   int H, I, top_k, P;
   int tiles;               // weight tiles: I/128 (128 gate + 128 up rows each) or H/256
   int items;               // bound on the linear item index: 8 x tiles x blocks per XCD (largest case)
-  const float* w_scale;    // s_w13 or s_w2
+  const float* w_scale;    // s_w13 or s_w2: one per tensor, or one per weight row ([E][2I] / [E][H], PC)
   const float* a_scale;    // gate/up: s_x in effect; down: static s_h (null = dynamic)
   const unsigned* h_amax;  // down with dynamic scale: max |h| (float bits)
   const float* h_scale;    // gate/up: static s_h (null = dynamic: h written as bf16)
@@ -262,6 +262,9 @@ __device__ __forceinline__ void pf_interleave() {
 //   features, epilogue SiLU(g)*u -> h.  HDYN: h stored as fp32 with a running
 //   amax (quantised by prefill_quant_h_kernel), else as e4m3 with the static
 //   scale.
+// PC: the weight scale is one fp32 per weight row (output channel) instead of
+//   one per tensor; the epilogue reads the lane's 16 (MODE 0: 16 gate + 16 up)
+//   row scales once per item.
 // MODE 1: down product, tile rows = 256 output features, epilogue
 //   s_h * s_w2 * acc -> bf16 part[pair][feature] (the routing weight is
 //   applied when the pairs of a token are summed).
@@ -285,7 +288,7 @@ __device__ __forceinline__ void pf_interleave() {
 // wave waits until at most twelve are outstanding: the loads of step s+2,
 // issued after those of step s+1.  Any other vector-memory operation (token
 // ids, epilogue stores) only makes that wait stricter.
-template <int MODE, bool HDYN>
+template <int MODE, bool HDYN, bool PC>
 __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
@@ -387,8 +390,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
   auto arow_off = [](int i) { return MODE == 0 ? i * (kPfRows / 2) : 32 * i; };
 
   // epilogue constants
-  const float deq = MODE == 0 ? (*a.a_scale) * (*a.w_scale)
-                              : (HDYN ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.a_scale) * (*a.w_scale);
+  const float sa = MODE == 0 ? *a.a_scale : (HDYN ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.a_scale);
+  const float deq = sa * (*a.w_scale);  // one weight scale per tensor (!PC)
   const float rhs = (MODE == 0 && !HDYN) ? 1.0f / *a.h_scale : 1.0f;
   float hmax = 0.0f;
 
@@ -519,19 +522,29 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
     auto ep_at = [&](int t, int c) { return ep + t * 128 + ((c ^ (t & 7)) << 4); };
     const int rt = lane >> 3, rc = lane & 7;  // read-back: token rt + 8*rr, chunk rc
     if (MODE == 0) {
+      const int fbase = cur.tile * (kPfRows / 2) + 32 * wave;
+      // per-row dequantisation of features fbase+8g+rq.. (gate) and I+.. (up)
+      f32x4 dg4[4], du4[4];
+      if constexpr (PC) {
+        const float* ws = a.w_scale + (int64_t)cur.e * 2 * a.I;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          dg4[g] = sa * *(const f32x4*)(ws + fbase + 8 * g + rq);
+          du4[g] = sa * *(const f32x4*)(ws + a.I + fbase + 8 * g + rq);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int t = 32 * j + col;
         if (t < cur.ntok) {
           const int f = cs.f[j];
-          const int fbase = cur.tile * (kPfRows / 2) + 32 * wave;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float hv[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float gt = acc[0][j][4 * g + q] * deq;
-              const float up = acc[1][j][4 * g + q] * deq;
+              const float gt = acc[0][j][4 * g + q] * (PC ? dg4[g][q] : deq);
+              const float up = acc[1][j][4 * g + q] * (PC ? du4[g][q] : deq);
               hv[q] = silu_fast(gt) * up;
               hmax = fmaxf(hmax, fabsf(hv[q]));
             }
@@ -549,6 +562,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
       // bf16 partial sums: rows 64*wave.. of token t are its 128-byte row;
       // rows 32i+8g+rq.. are bytes 16*(4i+g) + 2*rq of it
       const int64_t obase = (int64_t)cur.tile * kPfRows + 64 * wave;
+      // per-row dequantisation of rows obase+32i+8g+rq..
+      f32x4 dd[2][4];
+      if constexpr (PC) {
+        const float* ws = a.w_scale + (int64_t)cur.e * a.H + obase;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) dd[i][g] = sa * *(const f32x4*)(ws + 32 * i + 8 * g + rq);
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -556,8 +578,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x16& c = acc[i][j];
-            u32x2 o = {pack_bf16x2(c[4 * g] * deq, c[4 * g + 1] * deq),
-                       pack_bf16x2(c[4 * g + 2] * deq, c[4 * g + 3] * deq)};
+            const f32x4 d = PC ? dd[i][g] : f32x4{deq, deq, deq, deq};
+            u32x2 o = {pack_bf16x2(c[4 * g] * d[0], c[4 * g + 1] * d[1]),
+                       pack_bf16x2(c[4 * g + 2] * d[2], c[4 * g + 3] * d[3])};
             *(__attribute__((address_space(3))) u32x2*)(ep_at(col, 4 * i + g) + 2 * rq) = o;
           }
           __builtin_amdgcn_sched_barrier(0);

@@ -387,19 +387,19 @@ moe_status_t persistent_wgs(int* wgs) {
 // The dynamic LDS ceiling of a prefill kernel is raised once per kernel and
 // device (the current device, as for the launch that follows); a failure to
 // raise it is reported as MOE_ERR_DEVICE.
-template <int MODE, bool HDYN>
+template <int MODE, bool HDYN, bool PC>
 moe_status_t launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> lds_set[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_DEVICE;
   if (dev >= kMaxDevices || !lds_set[dev].load(std::memory_order_acquire)) {
-    if (hipFuncSetAttribute((const void*)prefill_gemm_kernel<MODE, HDYN>,
+    if (hipFuncSetAttribute((const void*)prefill_gemm_kernel<MODE, HDYN, PC>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds) != hipSuccess)
       return MOE_ERR_DEVICE;
     if (dev < kMaxDevices) lds_set[dev].store(true, std::memory_order_release);
   }
-  prefill_gemm_kernel<MODE, HDYN><<<wgs, kPfThreads, kPfLds, st>>>(g);
+  prefill_gemm_kernel<MODE, HDYN, PC><<<wgs, kPfThreads, kPfLds, st>>>(g);
   return MOE_OK;
 }
 
@@ -452,7 +452,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -510,6 +510,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
                                     uint8_t* ws, int32_t* ids, float* wts, const AlignOut& o, float* xamax_part,
                                     float* scale_slot, unsigned* h_amax, uint8_t* xq, uint8_t* h, float* part,
                                     bool hdyn) {
+  const bool pc = a->weight_scale_per_channel == 1;
   auto rec = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
   };
@@ -551,8 +552,9 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
                   a->h_scale, h, h_amax};
-    rc = hdyn ? launch_prefill<0, true>(std::min(wgs, items), st, g)
-              : launch_prefill<0, false>(std::min(wgs, items), st, g);
+    const int n = std::min(wgs, items);
+    rc = pc ? (hdyn ? launch_prefill<0, true, true>(n, st, g) : launch_prefill<0, false, true>(n, st, g))
+            : (hdyn ? launch_prefill<0, true, false>(n, st, g) : launch_prefill<0, false, false>(n, st, g));
     if (rc != MOE_OK) return rc;
   }
   rec(5);
@@ -568,8 +570,9 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w2, hq, seg, H, I, k, (int)P, T, items, a->w2_scale, a->h_scale, h_amax, nullptr,
                   (uint8_t*)part, nullptr};
-    rc = hdyn ? launch_prefill<1, true>(std::min(wgs, items), st, g)
-              : launch_prefill<1, false>(std::min(wgs, items), st, g);
+    const int n = std::min(wgs, items);
+    rc = pc ? (hdyn ? launch_prefill<1, true, true>(n, st, g) : launch_prefill<1, false, true>(n, st, g))
+            : (hdyn ? launch_prefill<1, true, false>(n, st, g) : launch_prefill<1, false, false>(n, st, g));
     if (rc != MOE_OK) return rc;
   }
   rec(7);
@@ -594,6 +597,9 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const int M = a->M, E = a->E, H = a->H, I = a->I, k = a->top_k;
   if (!fp8 && (a->w13_scale || a->w2_scale || a->x_scale || a->h_scale)) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (a->weight_scale_per_channel != 0 && (a->weight_scale_per_channel != 1 || !fp8)) return MOE_ERR_INVALID_ARG;
+  const bool pc = a->weight_scale_per_channel == 1;
+  if (pc && (!aligned(a->w13_scale, 16) || !aligned(a->w2_scale, 16))) return MOE_ERR_INVALID_ARG;
   if (M == 0) {
     if (ev)
       for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) rec(i);
@@ -691,6 +697,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   {
     Gemm1Args g{(const uint8_t*)a->w13, fp8 ? xq : (const uint8_t*)a->x, segs, H, I, k, a->w13_scale, scale_slot,
                 a->h_scale, h, h_amax};
+    g.w_cs = pc ? 1 : 0;
     const int tpw = 4 / plan.ks1;
     const dim3 grid((unsigned)(I / 16 / tpw), (unsigned)n_act, (unsigned)plan.passes1);
     bool ok;
@@ -715,6 +722,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   {
     Gemm2Args g{(const uint8_t*)a->w2, h, segs, wts, H, I, k, plan.ks2, a->w2_scale, a->h_scale, h_amax, part,
                 (int)P};
+    g.w_cs = pc ? 1 : 0;
     const dim3 grid((unsigned)(H / (32 * (4 / plan.wks2))), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
     bool ok;
     if (plan.tw2 > 0) {

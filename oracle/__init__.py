@@ -61,7 +61,12 @@ class _LayerArgs(ctypes.Structure):
         ("s_x_out", ctypes.c_void_p),
         ("s_h_out", ctypes.c_void_p),
         ("all_pairs_h", ctypes.c_int32),
+        ("w13_scale_rows", ctypes.c_void_p),
+        ("w2_scale_rows", ctypes.c_void_p),
     ]
+
+
+_ABI = 2  # oracle_abi_version() of moe_oracle.c that this binding matches
 
 
 def _load():
@@ -71,6 +76,10 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         build(force=False)
     lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_abi_version.restype = ctypes.c_int
+    if lib.oracle_abi_version() != _ABI:
+        raise RuntimeError("oracle/liboracle.so is a stale build (ABI %d, expected %d): run oracle.build()"
+                           % (lib.oracle_abi_version(), _ABI))
     lib.oracle_bf16_decode.restype = ctypes.c_double
     lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_encode.restype = ctypes.c_uint16
@@ -192,7 +201,8 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
 
     x: bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] / w2 [E,H,I] (bf16 or e4m3
     codes), or None together with `experts`, a dict e -> (w13_e, w2_e) holding
-    only the experts that are needed.  x_scale/h_scale: static fp8 activation
+    only the experts that are needed.  w13_scale/w2_scale (fp8): one float per
+    tensor, or arrays [E,2I] / [E,H] with one scale per weight row.  x_scale/h_scale: static fp8 activation
     scales, None = dynamic amax/448.  tokens: rows of y to produce (default all).
     Returns dict(y=float64 [T,H], ids, weights, s_x, s_h).
     """
@@ -236,16 +246,32 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
     sh = np.zeros(1, dtype=np.float32)
     if all_pairs_h is None:
         all_pairs_h = fp8 and h_scale is None
+
+    def scale_rows(sc, rows):
+        # one scale per weight row: E pointers to that expert's fp32 row scales
+        if sc is None or np.ndim(_np(sc)) == 0 or np.size(_np(sc)) == 1:
+            return None
+        arr = np.ascontiguousarray(_np(sc), dtype=np.float32)
+        if arr.shape != (E, rows):
+            raise ValueError("per-row scales must have shape %s, got %s" % ((E, rows), arr.shape))
+        keep.append(arr)
+        ptrs = (ctypes.c_void_p * E)(*[arr[e].ctypes.data for e in range(E)])
+        keep.append(ptrs)
+        return ctypes.cast(ptrs, ctypes.c_void_p)
+
+    rows13 = scale_rows(w13_scale, 2 * I) if fp8 else None
+    rows2 = scale_rows(w2_scale, H) if fp8 else None
     args = _LayerArgs(
         M=M, E=E, H=H, I=I, k=k, dtype=DTYPE_E4M3 if fp8 else DTYPE_BF16,
         x=_ptr(xa), logits=_ptr(lg),
         w13=ctypes.cast(p13, ctypes.c_void_p), w2=ctypes.cast(p2, ctypes.c_void_p),
-        w13_scale=float(w13_scale or 0.0), w2_scale=float(w2_scale or 0.0),
+        w13_scale=0.0 if rows13 else float(w13_scale or 0.0), w2_scale=0.0 if rows2 else float(w2_scale or 0.0),
         x_scale_static=int(x_scale is not None), x_scale=float(x_scale or 0.0),
         h_scale_static=int(h_scale is not None), h_scale=float(h_scale or 0.0),
         tokens=_ptr(tok) if tok.size else None, n_tokens=tok.size,
         y=_ptr(y) if y.size else None, ids=_ptr(ids) if ids.size else None, weights=_ptr(w) if w.size else None,
         s_x_out=_ptr(sx), s_h_out=_ptr(sh), all_pairs_h=int(bool(all_pairs_h)),
+        w13_scale_rows=rows13, w2_scale_rows=rows2,
     )
     rc = lib.oracle_layer(ctypes.byref(args))
     if rc:

@@ -235,6 +235,11 @@ typedef struct {
   float* s_x_out;               /* fp8 out (may be NULL) */
   float* s_h_out;               /* fp8 out (may be NULL) */
   int32_t all_pairs_h;          /* 1: evaluate h for all pairs (needed for a dynamic h scale) */
+  /* fp8, one scale per weight row (output channel) instead of w13_scale /
+   * w2_scale: E pointers, each [2I] (row n of W13[e]) resp. [H] (row n of
+   * W2[e]); NULL = one scale per tensor */
+  const float* const* w13_scale_rows;
+  const float* const* w2_scale_rows;
 } oracle_layer_args;
 
 /* e4m3 code -> value, filled from oracle_e4m3_decode before any parallel
@@ -254,18 +259,30 @@ static double weight_at(int32_t dtype, const void* base, int64_t idx) {
 
 static double silu(double g) { return g / (1.0 + exp(-g)); }
 
+/* Weight scale of row `row` of W13[e] / W2[e]: its own, or the tensor's. */
+static double w13_scale_of(const oracle_layer_args* A, int32_t e, int64_t row) {
+  return A->w13_scale_rows ? (double)A->w13_scale_rows[e][row] : (double)A->w13_scale;
+}
+static double w2_scale_of(const oracle_layer_args* A, int32_t e, int64_t row) {
+  return A->w2_scale_rows ? (double)A->w2_scale_rows[e][row] : (double)A->w2_scale;
+}
+
 /* h for one pair (token m, expert e), in fp32 as the value the next step
  * rounds from.  a: the token's activation row in double (x, or its e4m3
- * codes decoded), deq: fp8 dequantisation factor (1 for bf16). */
-static void expert_up(const oracle_layer_args* A, int32_t e, const double* a, double deq, float* h) {
+ * codes decoded); s_a: the activation scale (fp8); the products of row n
+ * are rescaled by s_a times that row's weight scale (fp8 only). */
+static void expert_up(const oracle_layer_args* A, int32_t e, const double* a, double s_a, float* h) {
   const void* w = A->w13[e];
+  const int fp8 = A->dtype == ORC_DTYPE_E4M3;
   int64_t H = A->H, I = A->I;
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int64_t t = 0; t < H; ++t) g += a[t] * weight_at(A->dtype, w, n * H + t);
     for (int64_t t = 0; t < H; ++t) u += a[t] * weight_at(A->dtype, w, (I + n) * H + t);
-    g *= deq;
-    u *= deq;
+    if (fp8) {
+      g *= s_a * w13_scale_of(A, e, n);
+      u *= s_a * w13_scale_of(A, e, I + n);
+    }
     h[n] = (float)(silu(g) * u);
   }
 }
@@ -318,7 +335,6 @@ int oracle_layer(oracle_layer_args* A) {
     if (A->s_x_out) *A->s_x_out = s_x;
   }
   const float r_x = 1.0f / s_x;
-  const double deq1 = fp8 ? (double)s_x * (double)A->w13_scale : 1.0;
 
   /* h for every needed pair, fp32 */
   float* h = (float*)malloc(sizeof(float) * (size_t)P * (size_t)I);
@@ -333,7 +349,7 @@ int oracle_layer(oracle_layer_args* A) {
         float xv = (float)oracle_bf16_decode(A->x[m * H + t]);
         a[t] = fp8 ? oracle_e4m3_decode(quant_e4m3(xv, r_x)) : (double)xv;
       }
-      expert_up(A, A->ids[p], a, deq1, h + p * (int64_t)I);
+      expert_up(A, A->ids[p], a, (double)s_x, h + p * (int64_t)I);
     }
     free(a);
   }
@@ -357,7 +373,6 @@ int oracle_layer(oracle_layer_args* A) {
     if (A->s_h_out) *A->s_h_out = s_h;
   }
   const float r_h = 1.0f / s_h;
-  const double deq2 = fp8 ? (double)s_h * (double)A->w2_scale : 1.0;
 
   double* hq = (double*)malloc(sizeof(double) * (size_t)P * (size_t)I);
   for (int64_t p = 0; p < P; ++p) {
@@ -379,7 +394,7 @@ int oracle_layer(oracle_layer_args* A) {
         const void* w = A->w2[A->ids[p]];
         double o = 0.0;
         for (int64_t t = 0; t < I; ++t) o += hq[p * I + t] * weight_at(A->dtype, w, n * (int64_t)I + t);
-        o *= deq2;
+        if (fp8) o *= (double)s_h * w2_scale_of(A, A->ids[p], n);
         acc += (double)A->weights[p] * o;
       }
       A->y[i * H + n] = acc;
@@ -399,4 +414,4 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 int oracle_num_threads(void) { return 1; }
 #endif
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }

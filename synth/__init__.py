@@ -147,6 +147,32 @@ def gen_weights(cfg: MoEConfig, seed: int = 0, device="cpu", H: Optional[int] = 
     return w13, w2, s13, s2
 
 
+def gen_weights_per_channel(cfg: MoEConfig, seed: int = 0, device="cpu"):
+    """fp8 expert weights with one scale per weight row (output channel).
+
+    The same normal draws as gen_weights; row n of W13[e] and of W2[e] is
+    stored as e4m3fn codes of W/s with s = amax(|row|)/448 (1.0 for an all-zero
+    row).  Returns (w13, w2, s13, s2): uint8 codes and fp32 tensors s13 [E,2I],
+    s2 [E,H] on `device`.
+    """
+    if cfg.dtype != "fp8":
+        raise ValueError("per-channel scales are for fp8 layers")
+    E, H, I = cfg.E, cfg.H, cfg.I
+    s13_std, s2_std = 1.0 / math.sqrt(H), 1.0 / math.sqrt(I)
+    w13 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
+    w2 = torch.empty(E, H, I, dtype=torch.uint8, device=device)
+    s13 = torch.empty(E, 2 * I, dtype=torch.float32, device=device)
+    s2 = torch.empty(E, H, dtype=torch.float32, device=device)
+    for e in range(E):
+        for w, s, t, rows, cols, std in ((w13, s13, _T_W13, 2 * I, H, s13_std), (w2, s2, _T_W2, H, I, s2_std)):
+            v = _expert_normal(seed, t, e, rows, cols, std, device)
+            a = v.abs().amax(dim=1)
+            sc = torch.where(a > 0, a / E4M3_MAX, torch.ones_like(a))
+            s[e] = sc
+            w[e] = (v / sc[:, None]).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return w13, w2, s13, s2
+
+
 @dataclasses.dataclass
 class LayerInputs:
     cfg: MoEConfig

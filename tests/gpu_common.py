@@ -31,7 +31,10 @@ def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuni
     w13, w2, s13, s2 = weights
     M = x.shape[0]
     fp8 = cfg.dtype == "fp8"
-    sc = lambda v: None if v is None else torch.tensor([v], dtype=torch.float32, device=DEV)
+    # activation scales and per-tensor weight scales are floats; per-row
+    # weight scales are [E,rows] tensors, passed as they are
+    sc = lambda v: (None if v is None else v.to(DEV, torch.float32).contiguous() if isinstance(v, torch.Tensor)
+                    else torch.tensor([v], dtype=torch.float32, device=DEV))
     ids = torch.full((M, cfg.k), -1, dtype=torch.int32, device=DEV)
     wts = torch.zeros((M, cfg.k), dtype=torch.float32, device=DEV)
     counts = torch.full((cfg.E,), -1, dtype=torch.int32, device=DEV)

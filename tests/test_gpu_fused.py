@@ -19,7 +19,7 @@ import torch
 
 import moe_layer_align_amd as moe
 from gpu_common import DEV, TOL, compare, run_gpu, say
-from synth import CONFIGS, MoEConfig, gen_logits, gen_weights, gen_x
+from synth import CONFIGS, MoEConfig, gen_logits, gen_weights, gen_weights_per_channel, gen_x
 
 pytestmark = pytest.mark.gpu
 
@@ -261,6 +261,57 @@ def test_prefill_path_repeat_calls_bitwise():
     assert bool(ys[0].float().isfinite().all())
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
+
+
+# ---------------------------------------------------------------- one weight scale per row
+@pytest.mark.parametrize("variant", ["ksplit", "stream"])
+@pytest.mark.parametrize("xs,hs", [(None, None), (0.015, 0.004)])
+@pytest.mark.parametrize("M", [5, 40])
+def test_per_channel_small_layer(variant, xs, hs, M):
+    cfg = cfg_of("fp8", 16, 4, 512, 384)
+    w = gen_weights_per_channel(cfg, 21, device=DEV)
+    t = moe.Tuning(gemm1_stream_tiles=-1, gemm2_stream_tiles=-1) if variant == "ksplit" else \
+        moe.Tuning(gemm1_stream_tiles=2, gemm2_stream_tiles=2)
+    compare(cfg, M, seed=21, weights=w, x_scale=xs, h_scale=hs, tuning=t)
+
+
+def test_per_channel_equal_rows_match_per_tensor():
+    # per-row scales all equal to the tensor's scale: the same bits as one
+    # scale per tensor, on the decode and on the prefill path
+    for cfg, M in ((cfg_of("fp8", 16, 4, 512, 384), 40),
+                   (MoEConfig("pf_pc", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf"), 1100)):
+        w13, w2, s13, s2 = gen_weights(cfg, 22, device=DEV)
+        x = gen_x(cfg.H, M, 22, sub=M).to(DEV)
+        lg = gen_logits(cfg, M, 22, sub=M).to(DEV)
+        t13 = torch.tensor([s13], device=DEV)
+        t2 = torch.tensor([s2], device=DEV)
+        r13 = torch.full((cfg.E, 2 * cfg.I), s13, dtype=torch.float32, device=DEV)
+        r2 = torch.full((cfg.E, cfg.H), s2, dtype=torch.float32, device=DEV)
+        a = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", t13, t2)
+        b = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", r13, r2)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), cfg.name
+
+
+def test_per_channel_qwen3_shape():
+    cfg = CONFIGS["qwen3"]
+    w = gen_weights_per_channel(cfg, 0, device=DEV)
+    compare(cfg, 32, seed=0, weights=w)
+
+
+@pytest.mark.parametrize("xs,hs", [(None, None), (0.012, 0.003)])
+def test_per_channel_prefill_path(xs, hs):
+    cfg = MoEConfig("pf_pc", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf")
+    w = gen_weights_per_channel(cfg, 23, device=DEV)
+    compare(cfg, 1100, seed=23, weights=w, x_scale=xs, h_scale=hs)
+
+
+def test_per_channel_prefill_full_static_scales():
+    cfg = CONFIGS["prefill"]
+    w = gen_weights_per_channel(cfg, 0, device=DEV)
+    compare(cfg, 4096, seed=0, weights=w, tokens=[0, 1, 1500, 4095], x_scale=0.011, h_scale=0.02)
+    del w
+    torch.cuda.empty_cache()
 
 
 def test_prefill_dynamic_scales(prefill_w):

@@ -9,6 +9,11 @@
   expert MLPs, with the weights from the closed form.
 * A token repeated M times gives identical rows.
 * The dynamic fp8 scales are amax/448 of x and of h.
+* One weight scale per row (output channel): E=1, k=1 against the same
+  float64 SwiGLU with per-row rescaling; per-row scales all equal to the
+  tensor's scale give the per-tensor result bit for bit; with several experts
+  each pair uses its own expert's rows (static activation scales, dense
+  per-token sum of per-expert MLPs).
 * A hand-derived fixture in tests/golden.
 Plausible mistakes (gate and up swapped, a sign in SiLU, a transposed W2, a
 dropped routing weight, the scale applied twice) each fail one of these.
@@ -22,7 +27,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, MoEConfig, gen_weights, gen_x
+from synth import CONFIGS, MoEConfig, gen_weights, gen_weights_per_channel, gen_x
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -101,6 +106,47 @@ def test_single_expert_is_swiglu_fp8_static():
     ref, _, _ = mlp_ref_fp8(x, w13[0], w2[0], s13, s2, sx=0.01, sh=0.002)
     assert out["s_x"] == np.float32(0.01) and out["s_h"] == np.float32(0.002)
     assert rel_err(out["y"], ref.numpy()) < 1e-12
+
+
+@pytest.mark.parametrize("static", [False, True])
+def test_single_expert_is_swiglu_fp8_per_channel(static):
+    cfg = small_cfg("fp8", 1, 1)
+    x = gen_x(cfg.H, 7, seed=4)
+    w13, w2, s13, s2 = gen_weights_per_channel(cfg, seed=4)
+    assert len(set(s13[0].tolist())) > cfg.I and len(set(s2[0].tolist())) > cfg.H // 2  # rows differ
+    xs, hs = (0.01, 0.002) if static else (None, None)
+    out = oracle.layer(x, torch.zeros(7, 1), w13, w2, 1, "fp8", s13, s2, x_scale=xs, h_scale=hs)
+    ref, sx, sh = mlp_ref_fp8(x, w13[0], w2[0], s13[0].double(), s2[0].double(), sx=xs, sh=hs)
+    assert out["s_x"] == np.float32(sx) and out["s_h"] == np.float32(sh)
+    assert rel_err(out["y"], ref.numpy()) < 1e-12
+
+
+def test_per_channel_equal_rows_is_per_tensor():
+    cfg = small_cfg("fp8", 4, 2)
+    x = gen_x(cfg.H, 9, seed=5)
+    lg = torch.randn(9, 4, generator=torch.Generator().manual_seed(5))
+    w13, w2, s13, s2 = gen_weights(cfg, seed=5)
+    r13 = torch.full((4, 2 * cfg.I), s13, dtype=torch.float32)
+    r2 = torch.full((4, cfg.H), s2, dtype=torch.float32)
+    a = oracle.layer(x, lg, w13, w2, 2, "fp8", s13, s2)
+    b = oracle.layer(x, lg, w13, w2, 2, "fp8", r13, r2)
+    assert np.array_equal(a["y"], b["y"]) and a["s_h"] == b["s_h"]
+
+
+def test_per_channel_rows_follow_each_pairs_expert():
+    cfg = small_cfg("fp8", 4, 2)
+    M = 6
+    x = gen_x(cfg.H, M, seed=6)
+    lg = torch.randn(M, 4, generator=torch.Generator().manual_seed(6))
+    w13, w2, s13, s2 = gen_weights_per_channel(cfg, seed=6)
+    out = oracle.layer(x, lg, w13, w2, 2, "fp8", s13, s2, x_scale=0.02, h_scale=0.004)
+    ref = np.zeros((M, cfg.H))
+    for m in range(M):
+        for j in range(2):
+            e = int(out["ids"][m, j])
+            o, _, _ = mlp_ref_fp8(x[m:m + 1], w13[e], w2[e], s13[e].double(), s2[e].double(), sx=0.02, sh=0.004)
+            ref[m] += float(out["weights"][m, j]) * o[0].numpy()
+    assert rel_err(out["y"], ref) < 1e-12
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
