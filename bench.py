@@ -84,6 +84,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="mixtral", choices=["mixtral", "qwen3", "deepseek", "prefill", "tiny"])
     ap.add_argument("--no-flush", action="store_true", help="hot-cache numbers: skip the cache flush before each call")
+    ap.add_argument("--per-channel", action="store_true",
+                    help="fp8 workloads: one weight scale per weight row instead of one per tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -97,7 +99,7 @@ def main() -> int:
 
     import torch
     import moe_layer_align_amd as moe
-    from synth import CONFIGS, gen_logits, gen_weights, gen_x
+    from synth import CONFIGS, gen_logits, gen_weights, gen_weights_per_channel, gen_x
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -110,9 +112,16 @@ def main() -> int:
     fp8 = cfg.dtype == "fp8"
     esz = 1 if fp8 else 2
     log("generating %s weights on the GPU" % cfg.name)
-    w13, w2, s13, s2 = gen_weights(cfg, 0, device=dev)
-    s13_t = torch.tensor([s13], device=dev) if fp8 else None
-    s2_t = torch.tensor([s2], device=dev) if fp8 else None
+    if args.per_channel and not fp8:
+        print("--per-channel applies to fp8 workloads only", file=sys.stderr)
+        return 2
+    if args.per_channel:
+        w13, w2, s13_t, s2_t = gen_weights_per_channel(cfg, 0, device=dev)
+        s13, s2 = s13_t, s2_t
+    else:
+        w13, w2, s13, s2 = gen_weights(cfg, 0, device=dev)
+        s13_t = torch.tensor([s13], device=dev) if fp8 else None
+        s2_t = torch.tensor([s2], device=dev) if fp8 else None
 
     calls = []
     for M in cfg.ms:
@@ -264,6 +273,7 @@ def main() -> int:
             "workload": "%s-shaped %s layer E=%d top-%d H=%d I=%d, M in {%s}" % (cfg.name, cfg.dtype, cfg.E, cfg.k,
                                                                                cfg.H, cfg.I, ms_str),
             "E": cfg.E, "top_k": cfg.k, "H": cfg.H, "I": cfg.I, "M_sweep": list(cfg.ms), "router_logits": cfg.logits,
+            "weight_scales": ("per channel" if args.per_channel else "per tensor") if fp8 else None,
         },
         "per_m": per_m,
         "roofline": roof,

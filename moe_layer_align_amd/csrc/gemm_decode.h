@@ -22,6 +22,8 @@
 // pairs, so no host readback is needed and surplus workgroups exit at once.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -151,19 +153,27 @@ struct Gemm1Args {
   int w_cs = 0;              // fp8: 1 = w_scale holds one scale per weight row, 0 = one per tensor
 };
 
-// fp8 dequantisation factors s_x * s_w of the four weight rows row0..row0+3
-// of expert e (rows_e rows per expert); with one scale per tensor (cs = 0)
-// every row reads w_scale[0].
-__device__ __forceinline__ void row_deq4(const float* w_scale, int cs, int e, int rows_e, int row0, float sa,
-                                         float (&d)[4]) {
-  const float* ws = w_scale + (int64_t)e * rows_e * cs;
+// fp8 dequantisation factors s_a * s_w: with one scale per weight row (PC)
+// those of the four rows row0..row0+3 of expert e (rows_e rows per expert),
+// else the tensor's one scale for all four.  The kernels branch on w_cs once,
+// at entry, into bodies specialised on PC, so the per-tensor bodies carry no
+// per-row work.
+template <bool PC>
+__device__ __forceinline__ void row_deq4(const float* w_scale, int e, int rows_e, int row0, float sa, float (&d)[4]) {
+  if constexpr (PC) {
+    const float* ws = w_scale + (int64_t)e * rows_e;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) d[r] = sa * ws[(row0 + r) * cs];
+    for (int r = 0; r < 4; ++r) d[r] = sa * ws[row0 + r];
+  } else {
+    const float v = sa * w_scale[0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = v;
+  }
 }
 
 // Body for NB (<= NT) token tiles; the kernel picks NB from the workgroup's
 // token count so that tiles with no token issue no loads and no MFMAs.
-template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT>
+template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT, bool PC>
 __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int e, int seg, int cnt, int pass0) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;   // k per MFMA
@@ -220,8 +230,8 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
   // dequantisation of this lane's rows: gate rows i0+4kq.., up rows I+i0+4kq..
   float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (FP8) {
-    row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, i0 + kq * 4, *a.x_scale, dg);
-    row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, a.I + i0 + kq * 4, *a.x_scale, du);
+    row_deq4<PC>(a.w_scale, e, 2 * a.I, i0 + kq * 4, *a.x_scale, dg);
+    row_deq4<PC>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, *a.x_scale, du);
   }
   float rh = 1.0f;
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
@@ -267,13 +277,19 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
   const int pass0 = blockIdx.z * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
-  if constexpr (NT >= 4)
-    if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
-  if constexpr (NT >= 3)
-    if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
-  if constexpr (NT >= 2)
-    if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
-  gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT>(a, s_red, e, seg, cnt, pass0);
+  auto run = [&](auto pc_tag) {
+    constexpr bool PC = decltype(pc_tag)::value;
+    if constexpr (NT >= 4)
+      if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
+    if constexpr (NT >= 3)
+      if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
+    if constexpr (NT >= 2)
+      if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
+    gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
+  };
+  if constexpr (FP8)
+    if (a.w_cs) return run(std::true_type{});  // one weight scale per row
+  run(std::false_type{});
 }
 
 // --------------------------------------------------------------------------
@@ -344,7 +360,7 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const (&pa)[2], int6
 // waves read 64 adjacent gate rows and their up partners at each point of the
 // stream.  Token rows and output slots are read once per wave.  No K split,
 // no LDS, no barrier.
-template <bool FP8, int HFMT, int NB, int U>
+template <bool FP8, int HFMT, int NB, int U, bool PC>
 __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int seg, int cnt, int pass0, int tw) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;
@@ -374,6 +390,11 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
   }
 
   const float sx = FP8 ? *a.x_scale : 1.0f;
+  float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if constexpr (FP8 && !PC) {  // one scale per tensor: the same factors for every tile
+    row_deq4<false>(a.w_scale, e, 0, 0, sx, dg);
+    row_deq4<false>(a.w_scale, e, 0, 0, sx, du);
+  }
   float rh = 1.0f;
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
   float hmax = 0.0f;
@@ -382,10 +403,9 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
   for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto epi = [&](int j, f32x4 (&c)[2][NB]) {
     const int i0 = (ft0 + 4 * j) * 16;
-    float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (FP8) {
-      row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, i0 + kq * 4, sx, dg);
-      row_deq4(a.w_scale, a.w_cs, e, 2 * a.I, a.I + i0 + kq * 4, sx, du);
+    if constexpr (FP8 && PC) {
+      row_deq4<true>(a.w_scale, e, 2 * a.I, i0 + kq * 4, sx, dg);
+      row_deq4<true>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, sx, du);
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
@@ -428,13 +448,19 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(Gemm1Args a, int tw) 
   const int pass0 = blockIdx.z * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
-  if constexpr (NT >= 4)
-    if (ntile == 4) return gemm1_stream_body<FP8, HFMT, 4, U>(a, e, seg, cnt, pass0, tw);
-  if constexpr (NT >= 3)
-    if (ntile == 3) return gemm1_stream_body<FP8, HFMT, 3, U>(a, e, seg, cnt, pass0, tw);
-  if constexpr (NT >= 2)
-    if (ntile == 2) return gemm1_stream_body<FP8, HFMT, 2, U>(a, e, seg, cnt, pass0, tw);
-  gemm1_stream_body<FP8, HFMT, 1, U>(a, e, seg, cnt, pass0, tw);
+  auto run = [&](auto pc_tag) {
+    constexpr bool PC = decltype(pc_tag)::value;
+    if constexpr (NT >= 4)
+      if (ntile == 4) return gemm1_stream_body<FP8, HFMT, 4, U, PC>(a, e, seg, cnt, pass0, tw);
+    if constexpr (NT >= 3)
+      if (ntile == 3) return gemm1_stream_body<FP8, HFMT, 3, U, PC>(a, e, seg, cnt, pass0, tw);
+    if constexpr (NT >= 2)
+      if (ntile == 2) return gemm1_stream_body<FP8, HFMT, 2, U, PC>(a, e, seg, cnt, pass0, tw);
+    gemm1_stream_body<FP8, HFMT, 1, U, PC>(a, e, seg, cnt, pass0, tw);
+  };
+  if constexpr (FP8)
+    if (a.w_cs) return run(std::true_type{});  // one weight scale per row
+  run(std::false_type{});
 }
 
 // --------------------------------------------------------------------------
@@ -500,7 +526,7 @@ __device__ __forceinline__ void stage_h_e4m3(const Gemm2Args& a, uint8_t* s_tok,
 // Body for NB (<= NT) token tiles.  WKS waves of the workgroup split the
 // slice's K range and are summed through LDS (s_red); 4/WKS groups of 32 rows
 // per workgroup.
-template <bool FP8, int HFMT, int NT, int NB, int U, int WKS>
+template <bool FP8, int HFMT, int NT, int NB, int U, int WKS, bool PC>
 __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f32x4* s_red, int e, int seg, int cnt,
                                            int pass0, int kslice) {
   constexpr int ESZ = FP8 ? 1 : 2;
@@ -524,8 +550,8 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
   float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (FP8) {
     const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
-    row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + kq * 4, sh, d0);
-    row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + 16 + kq * 4, sh, d1);
+    row_deq4<PC>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0);
+    row_deq4<PC>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1);
     if constexpr (QH) {
       stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
       __syncthreads();
@@ -603,13 +629,19 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   const int pass0 = (blockIdx.z / a.ksplit) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
-  if constexpr (NT >= 4)
-    if (ntile == 4) return gemm2_body<FP8, HFMT, NT, 4, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
-  if constexpr (NT >= 3)
-    if (ntile == 3) return gemm2_body<FP8, HFMT, NT, 3, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
-  if constexpr (NT >= 2)
-    if (ntile == 2) return gemm2_body<FP8, HFMT, NT, 2, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
-  gemm2_body<FP8, HFMT, NT, 1, U, WKS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+  auto run = [&](auto pc_tag) {
+    constexpr bool PC = decltype(pc_tag)::value;
+    if constexpr (NT >= 4)
+      if (ntile == 4) return gemm2_body<FP8, HFMT, NT, 4, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+    if constexpr (NT >= 3)
+      if (ntile == 3) return gemm2_body<FP8, HFMT, NT, 3, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+    if constexpr (NT >= 2)
+      if (ntile == 2) return gemm2_body<FP8, HFMT, NT, 2, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+    gemm2_body<FP8, HFMT, NT, 1, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+  };
+  if constexpr (FP8)
+    if (a.w_cs) return run(std::true_type{});  // one weight scale per row
+  run(std::false_type{});
 }
 
 // Down product, long-stream variant.  Wave w of the workgroup walks tw tiles
@@ -617,7 +649,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
 // the workgroup's K slice, the pipeline running on from tile to tile; the
 // token slice (quantised into LDS once per workgroup with a dynamic fp8 h
 // scale, else read from global memory) serves all of them.
-template <bool FP8, int HFMT, int NB, int U>
+template <bool FP8, int HFMT, int NB, int U, bool PC>
 __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s_tok, int e, int seg, int cnt,
                                                   int pass0, int kslice, int tw) {
   constexpr int ESZ = FP8 ? 1 : 2;
@@ -634,8 +666,13 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
   const int kbeg = kslice * Kw;
 
   float sh = 1.0f;
+  float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (FP8) {
     sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
+    if constexpr (!PC) {  // one scale per tensor: the same factors for every tile
+      row_deq4<false>(a.w_scale, e, 0, 0, sh, d0);
+      row_deq4<false>(a.w_scale, e, 0, 0, sh, d1);
+    }
     if constexpr (QH) {
       stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
       __syncthreads();
@@ -669,10 +706,9 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
   for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto epi = [&](int j, f32x4 (&c)[2][NB]) {
     const int n0 = (rt0 + 4 * j) * 32;
-    float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (FP8) {
-      row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + kq * 4, sh, d0);
-      row_deq4(a.w_scale, a.w_cs, e, a.H, n0 + 16 + kq * 4, sh, d1);
+    if constexpr (FP8 && PC) {
+      row_deq4<true>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0);
+      row_deq4<true>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1);
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
@@ -700,13 +736,19 @@ __global__ __launch_bounds__(256) void gemm2_stream_kernel(Gemm2Args a, int tw) 
   const int pass0 = (blockIdx.z / a.ksplit) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
-  if constexpr (NT >= 4)
-    if (ntile == 4) return gemm2_stream_body<FP8, HFMT, 4, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
-  if constexpr (NT >= 3)
-    if (ntile == 3) return gemm2_stream_body<FP8, HFMT, 3, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
-  if constexpr (NT >= 2)
-    if (ntile == 2) return gemm2_stream_body<FP8, HFMT, 2, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
-  gemm2_stream_body<FP8, HFMT, 1, U>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+  auto run = [&](auto pc_tag) {
+    constexpr bool PC = decltype(pc_tag)::value;
+    if constexpr (NT >= 4)
+      if (ntile == 4) return gemm2_stream_body<FP8, HFMT, 4, U, PC>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+    if constexpr (NT >= 3)
+      if (ntile == 3) return gemm2_stream_body<FP8, HFMT, 3, U, PC>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+    if constexpr (NT >= 2)
+      if (ntile == 2) return gemm2_stream_body<FP8, HFMT, 2, U, PC>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+    gemm2_stream_body<FP8, HFMT, 1, U, PC>(a, s_tok, e, seg, cnt, pass0, kslice, tw);
+  };
+  if constexpr (FP8)
+    if (a.w_cs) return run(std::true_type{});  // one weight scale per row
+  run(std::false_type{});
 }
 
 // LDS of a down-product workgroup: the K-split reduction buffer.
