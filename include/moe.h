@@ -111,6 +111,23 @@ moe_status_t moe_align(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_
 moe_status_t moe_quant_e4m3(const float* in, int64_t n, const float* scale, uint8_t* out, void* stream);
 
 /*
+ * Router logits, the step before routing: logits[m,e] = sum_t x[m,t] *
+ * router_w[e,t] with fp32 accumulation in a fixed order (the same bits on
+ * every call and for every M).  The pages' fused operation starts from the
+ * tokens: routing, data movement and expert computation in one batched GPU
+ * operation (wagnersolution page, "AWS describes a fused MoE optimization for
+ * the NVIDIA Hopper architecture", body).
+ *   x         [M,H] bf16, 16-byte aligned
+ *   router_w  [E,H] bf16, 16-byte aligned
+ *   logits    [M,E] fp32 out
+ * H a multiple of 128, E <= 512.  M = 0 is a no-op.  Errors: MOE_ERR_INVALID_ARG
+ * (null or misaligned pointers, M < 0, E < 1), MOE_ERR_UNSUPPORTED (E > 512,
+ * H not a multiple of 128).
+ */
+moe_status_t moe_router_logits(const void* x, const void* router_w, int32_t M, int32_t E, int32_t H, float* logits,
+                               void* stream);
+
+/*
  * Optional tuning of the fused forward; NULL selects the built-in table.
  * Any field 0 keeps its default; negative values are invalid except where
  * stated.  Values outside the supported set return MOE_ERR_UNSUPPORTED.
@@ -163,7 +180,7 @@ typedef struct {
   int32_t M, E, H, I, top_k;
   moe_dtype_t dtype;
   const void* x;           /* [M,H] bf16 hidden states */
-  const float* logits;     /* [M,E] fp32 router logits */
+  const float* logits;     /* [M,E] fp32 router logits, or NULL with router_w */
   const void* w13;         /* [E,2I,H] bf16 or e4m3; rows [0,I) gate, [I,2I) up */
   const void* w2;          /* [E,H,I] bf16 or e4m3 */
   const float* w13_scale;  /* fp8: device fp32[1], or fp32[E*2I] per channel (16-byte aligned); bf16: NULL */
@@ -180,6 +197,11 @@ typedef struct {
   const moe_tuning_t* tuning; /* host pointer or NULL */
   int32_t weight_scale_per_channel; /* fp8: 0 = one scale per weight tensor, 1 = one per weight row;
                                        any other value, or non-zero in bf16 mode: MOE_ERR_INVALID_ARG */
+  const void* router_w;    /* bf16 [E,H] router weights, 16-byte aligned, or NULL.  Exactly one of logits and
+                              router_w is non-NULL (else MOE_ERR_INVALID_ARG); with router_w the layer first
+                              computes logits = x . router_w^T as moe_router_logits does and routes on them */
+  float* logits_out;       /* optional out [M,E]: the logits computed from router_w (NULL = kept in the
+                              workspace); must be NULL when logits is given */
 } moe_fused_args_t;
 
 /* Host-only: workspace bytes needed by moe_fused_forward for these sizes. */
@@ -191,7 +213,8 @@ moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream);
  * Profiling support: when `events` (host array of hipEvent_t, passed as
  * void*) is non-NULL, moe_fused_forward_profiled records events[2*s] before
  * and events[2*s+1] after each of its MOE_NUM_STAGES launches on `stream`
- * (stage order: route, align, gate/up product, down product, finalize).
+ * (stage order: route (preceded by the router logits product when router_w is
+ * given), align, gate/up product, down product, finalize).
  * A stage that is not launched still records both events back to back.
  * NULL entries of `events` are skipped, so a caller can time only the stages
  * it needs without adding markers between the others.

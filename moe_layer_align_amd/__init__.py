@@ -52,6 +52,7 @@ class _FusedArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("tuning", ctypes.POINTER(Tuning)),
         ("weight_scale_per_channel", ctypes.c_int32),
+        ("router_w", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
     ]
 
 
@@ -76,6 +77,8 @@ def load():
     lib.moe_align_capacity.argtypes = [i32, i32, i32, i32]
     lib.moe_align.restype = ctypes.c_int
     lib.moe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.moe_router_logits.restype = ctypes.c_int
+    lib.moe_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.moe_quant_e4m3.restype = ctypes.c_int
     lib.moe_quant_e4m3.argtypes = [vp, i64, vp, vp, vp]
     lib.moe_fused_workspace_size.restype = sz
@@ -120,7 +123,12 @@ def route_topk(logits: torch.Tensor, top_k: int, ids: Optional[torch.Tensor] = N
                weights: Optional[torch.Tensor] = None, stream=None):
     """Top-k experts per token and their softmax weights (moe_route_topk)."""
     M, E = logits.shape
-    _need(logits, "logits", torch.float32, (M, E))
+    if logits is not None:
+        _need(logits, "logits", torch.float32, (M, E))
+    else:
+        _need(router_w, "router_w", torch.bfloat16, (E, H))
+        if logits_out is not None:
+            _need(logits_out, "logits_out", torch.float32, (M, E))
     if ids is None:
         ids = torch.empty(M, top_k, dtype=torch.int32, device=logits.device)
     if weights is None:
@@ -130,6 +138,20 @@ def route_topk(logits: torch.Tensor, top_k: int, ids: Optional[torch.Tensor] = N
     _check("moe_route_topk", load().moe_route_topk(_ptr(logits), M, E, top_k, _ptr(ids), _ptr(weights),
                                                    _stream(stream)))
     return ids, weights
+
+
+def router_logits(x: torch.Tensor, router_w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """logits = x . router_w^T (moe_router_logits): x bf16 [M,H], router_w bf16
+    [E,H] -> fp32 [M,E]."""
+    M, H = x.shape
+    E = router_w.shape[0]
+    _need(x, "x", torch.bfloat16, (M, H))
+    _need(router_w, "router_w", torch.bfloat16, (E, H))
+    if out is None:
+        out = torch.empty(M, E, dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (M, E))
+    _check("moe_router_logits", load().moe_router_logits(_ptr(x), _ptr(router_w), M, E, H, _ptr(out), _stream(stream)))
+    return out
 
 
 def align_capacity(M: int, top_k: int, E: int, block: int) -> int:
@@ -168,31 +190,40 @@ def workspace_size(M: int, E: int, H: int, I: int, top_k: int, dtype: str) -> in
     return int(load().moe_fused_workspace_size(M, E, H, I, top_k, DTYPE_FP8 if dtype == "fp8" else DTYPE_BF16))
 
 
-def fused_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: int,
+def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Tensor, w2: torch.Tensor, top_k: int,
                   dtype: str = "bf16", w13_scale: Optional[torch.Tensor] = None,
                   w2_scale: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None,
                   h_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
                   topk_weights: Optional[torch.Tensor] = None, expert_counts: Optional[torch.Tensor] = None,
                   scales_out: Optional[torch.Tensor] = None, tuning: Optional[Tuning] = None, stream=None,
-                  events=None) -> torch.Tensor:
+                  events=None, router_w: Optional[torch.Tensor] = None,
+                  logits_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The fused layer (moe_fused_forward).
 
     x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
     (dtype "bf16") or uint8 e4m3fn codes (dtype "fp8") with fp32 device
     scales, either one per tensor ([1] each) or one per weight row (w13_scale
     [E,2I], w2_scale [E,H]); x_scale/h_scale: static fp8 activation scales or
-    None (dynamic).
+    None (dynamic).  logits may be None when router_w (bf16 [E,H]) is given:
+    the layer then computes them (into logits_out fp32 [M,E] when given).
     events: optional list of 2*NUM_STAGES hipEvent_t handles (ints) recorded
     around the stages on the stream.
     """
     M, H = x.shape
-    E = logits.shape[1]
+    if (logits is None) == (router_w is None):
+        raise ValueError("give exactly one of logits and router_w")
+    E = logits.shape[1] if logits is not None else router_w.shape[0]
     fp8 = dtype == "fp8"
     I = w2.shape[2]
     wdt = torch.uint8 if fp8 else torch.bfloat16
     _need(x, "x", torch.bfloat16, (M, H))
-    _need(logits, "logits", torch.float32, (M, E))
+    if logits is not None:
+        _need(logits, "logits", torch.float32, (M, E))
+    else:
+        _need(router_w, "router_w", torch.bfloat16, (E, H))
+        if logits_out is not None:
+            _need(logits_out, "logits_out", torch.float32, (M, E))
     _need(w13, "w13", wdt, (E, 2 * I, H))
     _need(w2, "w2", wdt, (E, H, I))
     per_channel = w13_scale is not None and w13_scale.dim() == 2
@@ -231,6 +262,7 @@ def fused_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: 
         workspace=_ptr(workspace), workspace_bytes=workspace.numel(),
         tuning=ctypes.pointer(tuning) if tuning is not None else None,
         weight_scale_per_channel=int(per_channel),
+        router_w=_ptr(router_w), logits_out=_ptr(logits_out),
     )
     if events is None:
         _check("moe_fused_forward", lib.moe_fused_forward(ctypes.byref(args), _stream(stream)))

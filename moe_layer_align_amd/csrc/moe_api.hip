@@ -81,7 +81,7 @@ int64_t align_capacity(int64_t P, int E, int B) {
 // ---------------------------------------------------------------- workspace
 struct Layout {
   size_t ids, wts, counts, offsets, sorted, block_expert, num_padded, active, num_active;
-  size_t xamax_part, scale_slot, h_amax, hist, xq, h, part, total;
+  size_t xamax_part, scale_slot, h_amax, hist, logits, xq, h, part, total;
   int64_t capacity;
   int n_blocks, n_route_wg;
 };
@@ -112,6 +112,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
   L.scale_slot = take(4);
   L.h_amax = take(4);
   L.hist = take((size_t)cdiv(M, 4 * kRouteRows) * E * 4);
+  L.logits = take((size_t)M * E * 4);  // router logits computed by the layer (router_w given)
   const bool fp8 = dt == MOE_DTYPE_FP8_E4M3;
   L.xq = take(fp8 ? (size_t)M * H : 0);
   // h: bf16 (bf16 layers), fp32 (fp8 decode), fp32 + its e4m3 copy (fp8 prefill)
@@ -430,6 +431,11 @@ void launch_align(const int32_t* ids, int64_t P, int E, int B, const AlignOut& o
   align_kernel<<<n_align + n_quant_wg, 256, 0, st>>>(ids, (int)P, E, B, log2i(B), log2i(E), n_align, o, q, hist);
 }
 
+void launch_router_logits(const void* x, const void* w, int M, int E, int H, float* logits, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(E, 16), (unsigned)cdiv(M, 16));
+  router_logits_kernel<<<grid, 1024, 0, st>>>((const uint16_t*)x, (const uint16_t*)w, M, E, H, logits);
+}
+
 moe_status_t check_shape(int M, int E, int k) {
   if (M < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (E > kMaxExperts || k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
@@ -452,7 +458,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -462,6 +468,17 @@ moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t t
   if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4)) return MOE_ERR_INVALID_ARG;
   launch_route(logits, M, E, top_k, topk_ids, topk_weights, RouteFusedArgs{}, (hipStream_t)stream);
+  return launch_status();
+}
+
+moe_status_t moe_router_logits(const void* x, const void* router_w, int32_t M, int32_t E, int32_t H, float* logits,
+                               void* stream) {
+  if (M < 0 || E < 1 || E > kMaxExperts) return M < 0 || E < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
+  if (H < 128 || H % 128) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (!x || !router_w || !logits) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
+  launch_router_logits(x, router_w, M, E, H, logits, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -605,8 +622,13 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
       for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) rec(i);
     return MOE_OK;
   }
-  if (!a->x || !a->logits || !a->w13 || !a->w2 || !a->y || !a->workspace) return MOE_ERR_INVALID_ARG;
-  for (const void* p : {a->x, a->w13, a->w2, (const void*)a->y}) if (!aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+  if (!a->x || !a->w13 || !a->w2 || !a->y || !a->workspace) return MOE_ERR_INVALID_ARG;
+  // logits: given, or computed from the router weights (exactly one of the two)
+  if ((a->logits == nullptr) == (a->router_w == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (a->logits_out && !a->router_w) return MOE_ERR_INVALID_ARG;
+  for (const void* p : {a->x, a->w13, a->w2, (const void*)a->y, a->router_w})
+    if (!aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(a->logits_out, 4)) return MOE_ERR_INVALID_ARG;
   if (!aligned(a->workspace, 256)) return MOE_ERR_INVALID_ARG;
   for (const void* p : {(const void*)a->logits, (const void*)a->w13_scale, (const void*)a->w2_scale,
                         (const void*)a->x_scale, (const void*)a->h_scale, (const void*)a->topk_ids,
@@ -623,6 +645,24 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   }
 
   uint8_t* ws = (uint8_t*)a->workspace;
+  // router logits from the hidden states (the step before routing), inside
+  // the route stage: its start event is recorded here and not again
+  moe_fused_args_t with_logits;
+  void* ev_rest[2 * MOE_NUM_STAGES];
+  if (a->router_w) {
+    float* lo = a->logits_out ? a->logits_out : (float*)(ws + L.logits);
+    rec(0);
+    launch_router_logits(a->x, a->router_w, M, E, H, lo, st);
+    if ((rc = launch_status()) != MOE_OK) return rc;
+    with_logits = *a;
+    with_logits.logits = lo;
+    a = &with_logits;
+    if (ev) {
+      for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) ev_rest[i] = ev[i];
+      ev_rest[0] = nullptr;
+      ev = ev_rest;
+    }
+  }
   int32_t* ids = a->topk_ids ? a->topk_ids : (int32_t*)(ws + L.ids);
   float* wts = a->topk_weights ? a->topk_weights : (float*)(ws + L.wts);
   int32_t* counts = a->expert_counts ? a->expert_counts : (int32_t*)(ws + L.counts);

@@ -66,7 +66,7 @@ class _LayerArgs(ctypes.Structure):
     ]
 
 
-_ABI = 2  # oracle_abi_version() of moe_oracle.c that this binding matches
+_ABI = 3  # oracle_abi_version() of moe_oracle.c that this binding matches
 
 
 def _load():
@@ -100,6 +100,9 @@ def _load():
     lib.oracle_layer.restype = ctypes.c_int
     lib.oracle_layer.argtypes = [ctypes.POINTER(_LayerArgs)]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_router_logits.restype = ctypes.c_int
+    lib.oracle_router_logits.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -194,6 +197,24 @@ def align(ids, E: int, B: int, capacity: Optional[int] = None):
 
 
 # ---------------------------------------------------------------- layer
+def router_logits(x, w) -> np.ndarray:
+    """Router logits x . w^T for bf16 x [M,H] and bf16 router weights w [E,H]:
+    fp32 [M,E], each a double sum over t ascending rounded once."""
+    lib = _load()
+    xa, wa = _np(x), _np(w)
+    if xa.dtype != np.uint16 or wa.dtype != np.uint16:
+        raise TypeError("x and w must be bf16")
+    M, H = xa.shape
+    E = wa.shape[0]
+    if wa.shape[1] != H:
+        raise ValueError("w must be [E,H]")
+    out = np.zeros((M, E), dtype=np.float32)
+    rc = lib.oracle_router_logits(_ptr(xa) if xa.size else None, _ptr(wa), M, E, H, _ptr(out) if out.size else None)
+    if rc:
+        raise ValueError("oracle_router_logits failed with code %d" % rc)
+    return out
+
+
 def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = None,
           w2_scale: Optional[float] = None, x_scale: Optional[float] = None, h_scale: Optional[float] = None,
           tokens: Optional[Sequence[int]] = None, experts: Optional[dict] = None, all_pairs_h: Optional[bool] = None):

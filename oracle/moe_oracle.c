@@ -406,6 +406,25 @@ int oracle_layer(oracle_layer_args* A) {
   return ORC_OK;
 }
 
+/* Router logits, the step before routing: logits[m,e] = sum_t x[m,t] *
+ * w[e,t] for bf16 x [M,H] and router weights w [E,H], summed in double with
+ * t ascending and rounded once to fp32 (wagnersolution page, "AWS describes a
+ * fused MoE optimization for the NVIDIA Hopper architecture", body: the fused
+ * operation starts from the tokens' routing). */
+int oracle_router_logits(const uint16_t* x, const uint16_t* w, int64_t M, int32_t E, int32_t H, float* logits) {
+  if (M < 0 || E < 1 || H < 1) return ORC_ERR_ARG;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int32_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int32_t t = 0; t < H; ++t)
+        acc += oracle_bf16_decode(x[m * H + t]) * oracle_bf16_decode(w[(int64_t)e * H + t]);
+      logits[m * E + e] = (float)acc;
+    }
+  }
+  return ORC_OK;
+}
+
 /* Threads the parallel loops use (OpenMP's default team size). */
 #ifdef _OPENMP
 #include <omp.h>
@@ -414,4 +433,4 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 int oracle_num_threads(void) { return 1; }
 #endif
 
-int oracle_abi_version(void) { return 2; }
+int oracle_abi_version(void) { return 3; }

@@ -61,7 +61,7 @@ CONFIGS: Dict[str, MoEConfig] = {
     "prefill": MoEConfig("prefill", E=128, k=8, H=4096, I=1536, dtype="fp8", ms=(4096,), logits="zipf"),
 }
 
-_T_X, _T_LOGITS, _T_BIAS, _T_PERM, _T_W13, _T_W2 = 1, 2, 3, 4, 5, 6
+_T_X, _T_LOGITS, _T_BIAS, _T_PERM, _T_W13, _T_W2, _T_WG = 1, 2, 3, 4, 5, 6, 7
 E4M3_MAX = 448.0
 
 
@@ -145,6 +145,14 @@ def gen_weights(cfg: MoEConfig, seed: int = 0, device="cpu", H: Optional[int] = 
         q = (_expert_normal(seed, _T_W2, e, H, I, s2_std, device) / r2).clamp_(-E4M3_MAX, E4M3_MAX)
         w2[e] = q.to(torch.float8_e4m3fn).view(torch.uint8)
     return w13, w2, s13, s2
+
+
+def gen_router_weights(E: int, H: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Router weights W_g [E,H] bf16 ~ N(0, 1/H): logits x . W_g^T of N(0,1)
+    hidden states are then about N(0,1), the law of the given-logit workloads."""
+    g = _gen(seed, _T_WG, 0, device)
+    w = torch.randn(E, H, generator=g, dtype=torch.float32, device=device) / math.sqrt(H)
+    return w.to(torch.bfloat16).contiguous()
 
 
 def gen_weights_per_channel(cfg: MoEConfig, seed: int = 0, device="cpu"):

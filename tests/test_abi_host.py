@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("moe_route_topk", "moe_align", "moe_fused_forward", "moe_align_capacity",
-              "moe_fused_workspace_size", "moe_status_string", "moe_quant_e4m3"):
+              "moe_fused_workspace_size", "moe_status_string", "moe_quant_e4m3", "moe_router_logits"):
         assert n in names
 
 
@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def capacity_formula(M, k, E, B):
@@ -136,10 +136,24 @@ def fused_args(**kw):
     (dict(weight_scale_per_channel=1), 1),                   # per-channel weight scales in bf16 mode
     (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_per_channel=2), 1),  # unknown scale mode
     (dict(dtype=1, w13_scale=FAKE + 4, w2_scale=FAKE, weight_scale_per_channel=1), 1),  # rows need 16-byte alignment
+    (dict(router_w=FAKE), 1),                                # both logits and router weights
+    (dict(logits=None), 1),                                  # neither
+    (dict(logits_out=FAKE), 1),                              # logits out without router weights
+    (dict(logits=None, router_w=FAKE + 8), 1),               # misaligned router weights
 ])
 def test_fused_validation(lib, kw, code):
     args = fused_args(**kw)
     assert lib.moe_fused_forward(ctypes.byref(args), None) == code
+
+
+def test_router_logits_validation(lib):
+    r = lib.moe_router_logits
+    assert r(FAKE, FAKE, -1, 8, 256, FAKE, None) == 1
+    assert r(None, FAKE, 4, 8, 256, FAKE, None) == 1
+    assert r(FAKE, FAKE + 8, 4, 8, 256, FAKE, None) == 1   # 16-byte alignment
+    assert r(FAKE, FAKE, 4, 8, 200, FAKE, None) == 2       # H not a multiple of 128
+    assert r(FAKE, FAKE, 4, 1024, 256, FAKE, None) == 2    # E above 512
+    assert r(None, None, 0, 8, 256, None, None) == 0       # M = 0
 
 
 def test_fused_tuning_validation(lib):

@@ -18,8 +18,9 @@ import pytest
 import torch
 
 import moe_layer_align_amd as moe
+import oracle
 from gpu_common import DEV, TOL, compare, run_gpu, say
-from synth import CONFIGS, MoEConfig, gen_logits, gen_weights, gen_weights_per_channel, gen_x
+from synth import CONFIGS, MoEConfig, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel, gen_x
 
 pytestmark = pytest.mark.gpu
 
@@ -312,6 +313,40 @@ def test_per_channel_prefill_full_static_scales():
     compare(cfg, 4096, seed=0, weights=w, tokens=[0, 1, 1500, 4095], x_scale=0.011, h_scale=0.02)
     del w
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- router logits inside the layer
+@pytest.mark.parametrize("cfg,M", [
+    (MoEConfig("r_bf16", E=8, k=2, H=256, I=512, dtype="bf16", ms=(4,), logits="normal"), 4),
+    (CONFIGS["qwen3"], 8),
+    (MoEConfig("r_pf", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="normal"), 1100),
+])
+def test_fused_with_router_weights(cfg, M):
+    # the layer computes the logits itself: they agree with the oracle's
+    # within fp32 summation error, the routing taken on them is the oracle's
+    # bit for bit, and y is the oracle's layer on those logits
+    say("fused with router weights %s M=%d" % (cfg.name, M))
+    w = gen_weights(cfg, 24, device=DEV)
+    x = gen_x(cfg.H, M, 24, sub=M)
+    wg = gen_router_weights(cfg.E, cfg.H, 24)
+    fp8 = cfg.dtype == "fp8"
+    lo = torch.empty(M, cfg.E, dtype=torch.float32, device=DEV)
+    ids = torch.empty(M, cfg.k, dtype=torch.int32, device=DEV)
+    sc = (lambda v: torch.tensor([v], device=DEV)) if fp8 else (lambda v: None)
+    y = moe.fused_forward(x.to(DEV), None, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]), topk_ids=ids,
+                          router_w=wg.to(DEV), logits_out=lo)
+    torch.cuda.synchronize()
+    lg = lo.cpu()
+    ref_lg = oracle.router_logits(x, wg)
+    assert np.abs(lg.numpy() - ref_lg).max() <= 1e-5 * np.abs(ref_lg).max() + 1e-6
+    ref_ids, _ = oracle.route(lg, cfg.k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    toks = None if M <= 64 else [0, 1, M // 2, M - 1]
+    e, _, _ = compare(cfg, M, seed=24, weights=w, logits=lg, x=x, tokens=toks)
+    # the same layer on the given logits gives the same bits
+    y2 = moe.fused_forward(x.to(DEV), lo, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
 
 
 def test_prefill_dynamic_scales(prefill_w):

@@ -1,6 +1,7 @@
 """GPU parity of the single-step entry points against the CPU oracle:
-e4m3 quantisation (bit-exact codes), router top-k (bit-exact ids), align
-(bit-exact counts, offsets, sorted ids, block map)."""
+e4m3 quantisation (bit-exact codes), router logits (within fp32 summation
+error, bitwise the same for a token in any batch), router top-k (bit-exact
+ids), align (bit-exact counts, offsets, sorted ids, block map)."""
 import numpy as np
 import pytest
 import torch
@@ -8,7 +9,7 @@ import torch
 import moe_layer_align_amd as moe
 import oracle
 from gpu_common import DEV, say
-from synth import CONFIGS, gen_logits
+from synth import CONFIGS, gen_logits, gen_router_weights, gen_x
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +132,20 @@ def test_align_out_of_range_ids_flagged():
     torch.cuda.synchronize()
     assert int(dev["num_padded"].item()) == -1
     assert dev["counts"].cpu().numpy().tolist() == [1, 1, 1, 1, 0, 0, 0, 0]
+
+
+# ------------------------------------------------------------------ router logits
+@pytest.mark.parametrize("M,E,H", [(1, 8, 4096), (5, 128, 2048), (63, 256, 7168), (300, 128, 4096), (17, 7, 256),
+                                   (4096, 128, 4096)])
+def test_router_logits(M, E, H):
+    say("router logits M=%d E=%d H=%d" % (M, E, H))
+    x = gen_x(H, M, 40 + E, sub=M)
+    w = gen_router_weights(E, H, 40 + E)
+    out = moe.router_logits(x.to(DEV), w.to(DEV)).cpu().numpy()
+    ref = oracle.router_logits(x, w)
+    # fp32 sums of H bf16 products in another order: far below 1e-5 of the
+    # logits' scale
+    assert np.abs(out - ref).max() <= 1e-5 * np.abs(ref).max() + 1e-6
+    # a token's logits do not depend on the batch it is in
+    one = moe.router_logits(x[:1].to(DEV), w.to(DEV)).cpu().numpy()
+    assert np.array_equal(one[0], out[0])
