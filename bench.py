@@ -84,6 +84,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="mixtral", choices=["mixtral", "qwen3", "deepseek", "prefill", "tiny"])
     ap.add_argument("--no-flush", action="store_true", help="hot-cache numbers: skip the cache flush before each call")
+    ap.add_argument("--router-gemm", action="store_true",
+                    help="the layer computes its router logits from the hidden states and N(0,1/H) router "
+                         "weights [E,H] (inside the timed span) instead of taking the workload's logits")
     ap.add_argument("--per-channel", action="store_true",
                     help="fp8 workloads: one weight scale per weight row instead of one per tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -99,7 +102,7 @@ def main() -> int:
 
     import torch
     import moe_layer_align_amd as moe
-    from synth import CONFIGS, gen_logits, gen_weights, gen_weights_per_channel, gen_x
+    from synth import CONFIGS, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel, gen_x
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -135,9 +138,12 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     flush_buf = None if args.no_flush else torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
 
+    router_w = gen_router_weights(cfg.E, cfg.H, 0, device=dev) if args.router_gemm else None
+
     def run(c, events=None):
-        moe.fused_forward(c["x"], c["lg"], w13, w2, cfg.k, cfg.dtype, s13_t, s2_t, out=c["y"], workspace=c["ws"],
-                          expert_counts=c["counts"], stream=stream, events=events)
+        moe.fused_forward(c["x"], None if args.router_gemm else c["lg"], w13, w2, cfg.k, cfg.dtype, s13_t, s2_t,
+                          out=c["y"], workspace=c["ws"], expert_counts=c["counts"], stream=stream, events=events,
+                          router_w=router_w)
 
     def flush(i):
         if flush_buf is not None:
@@ -250,7 +256,7 @@ def main() -> int:
     roof["launches"] = n_g1
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.router_gemm:  # the oracle sample takes the workload's logits
         cpu = cpu_baseline(cfg, calls, (w13, w2, s13, s2), args.cpu_seconds, unit)
 
     ms_str = ",".join(str(m) for m in cfg.ms)
@@ -274,6 +280,7 @@ def main() -> int:
                                                                                cfg.H, cfg.I, ms_str),
             "E": cfg.E, "top_k": cfg.k, "H": cfg.H, "I": cfg.I, "M_sweep": list(cfg.ms), "router_logits": cfg.logits,
             "weight_scales": ("per channel" if args.per_channel else "per tensor") if fp8 else None,
+            "router_logits": "computed in the layer from router weights" if args.router_gemm else "given",
         },
         "per_m": per_m,
         "roofline": roof,
