@@ -55,12 +55,14 @@ FLUSH_BYTES = 1 << 30
 DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "94eab15d189c8070e5d81afd5826fcaad8434265d20eca846d4aa778a7bc701c",
-                "bytes_per_launch": 1510116716},
-    "qwen3": {"src_sha256": "94eab15d189c8070e5d81afd5826fcaad8434265d20eca846d4aa778a7bc701c",
-              "bytes_per_launch": 241727958},
-    "prefill": {"src_sha256": "7d6b8ed93b9685961c4e075082acb34757988fefebc65bdd28f4a2d5d4a431a9",
-                "bytes_per_launch": 3062722821},
+    "mixtral": {"src_sha256": "c282e47f9c3ef4e3ea088f3b663ca0d12522109553665fac205ebde59a98b0de",
+                "bytes_per_launch": 1510012782},
+    "qwen3": {"src_sha256": "c282e47f9c3ef4e3ea088f3b663ca0d12522109553665fac205ebde59a98b0de",
+              "bytes_per_launch": 241749200},
+    "deepseek": {"src_sha256": "c282e47f9c3ef4e3ea088f3b663ca0d12522109553665fac205ebde59a98b0de",
+                 "bytes_per_launch": 3292509242},
+    "prefill": {"src_sha256": "b34f5ee278f37292ae1b8562f7b83f3ac3d9e94ea862026e7242b2bbdd9067bc",
+                "bytes_per_launch": 3056562960},
 }
 
 
@@ -246,8 +248,11 @@ def main() -> int:
     roof["frac"] = round(ach / roof["peak"], 4)
     tr = TRAFFIC.get(cfg.name)
     sources = PREFILL_SOURCES if cfg.name == "prefill" else DECODE_SOURCES
+    # the counters were taken on the default inputs (cold cache, given logits,
+    # per-tensor scales) of these kernel sources
     roof["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256(sources)
-                                                 and not args.no_flush) else None
+                                                 and not (args.no_flush or args.per_channel or args.router_gemm)) \
+        else None
     roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
     roof["kernel"] = ("prefill_gemm_kernel<0, *> (tiled gate/up product + SiLU*up)" if cfg.name == "prefill"
                       else "gate/up product + SiLU*up (gemm1_decode_kernel, or gemm1_stream_kernel for fp8 "
