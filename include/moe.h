@@ -28,8 +28,8 @@
  *    in [1, 256], M*top_k < 2^31).
  *    MOE_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the required size.
  *    MOE_ERR_DEVICE: a launch failed (hipGetLastError after the launch).
- *  - M = 0 is valid: route and the fused forward enqueue nothing; align
- *    writes the empty layout.
+ *  - M = 0 is valid: route, router logits and the fused forward enqueue
+ *    nothing; align writes the empty layout.
  *  - Kernels are compiled ahead of time for gfx950; no argument value
  *    (token count included) triggers a compilation.
  */
