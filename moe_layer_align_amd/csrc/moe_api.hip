@@ -431,9 +431,16 @@ void launch_align(const int32_t* ids, int64_t P, int E, int B, const AlignOut& o
   align_kernel<<<n_align + n_quant_wg, 256, 0, st>>>(ids, (int)P, E, B, log2i(B), log2i(E), n_align, o, q, hist);
 }
 
+// Router logits: 16 experts x 16 tokens per workgroup at decode sizes, x 64
+// tokens beyond (the same per-tile sums, fewer reads of the router rows).
 void launch_router_logits(const void* x, const void* w, int M, int E, int H, float* logits, hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(E, 16), (unsigned)cdiv(M, 16));
-  router_logits_kernel<<<grid, 1024, 0, st>>>((const uint16_t*)x, (const uint16_t*)w, M, E, H, logits);
+  const uint16_t* xx = (const uint16_t*)x;
+  const uint16_t* ww = (const uint16_t*)w;
+  if (M <= 64) {
+    router_logits_kernel<1><<<dim3((unsigned)cdiv(E, 16), (unsigned)cdiv(M, 16)), 1024, 0, st>>>(xx, ww, M, E, H, logits);
+  } else {
+    router_logits_kernel<4><<<dim3((unsigned)cdiv(E, 16), (unsigned)cdiv(M, 64)), 1024, 0, st>>>(xx, ww, M, E, H, logits);
+  }
 }
 
 moe_status_t check_shape(int M, int E, int k) {

@@ -115,43 +115,59 @@ __host__ __device__ inline int route_grid(int M, int64_t x_elems) {
 // fp32 accumulation.  The pages' fused operation starts from the tokens
 // (routing, data movement and expert products in one batched GPU operation:
 // wagnersolution page, "AWS describes a fused MoE optimization ...", body).
-// A workgroup computes 16 experts x 16 tokens with the 16x16x32 bf16 MFMA
+// A workgroup computes 16 experts x 16*T tokens with the 16x16x32 bf16 MFMA
 // (router rows are the A operand, tokens the B operand, as in the expert
 // products); its 16 waves take the 32-element K-steps s = wave, wave+16, ...
-// and the wave sums are added in wave order through LDS, so every logit is
-// the same fixed-order sum on every call and for every M.
+// and the wave sums are added in wave order through LDS.  Every 16 x 16 tile
+// is summed in that same order whatever T is, so a token's logits are the
+// same bits on every call and in every batch; T = 4 (large M) reads each
+// router row once per 64 tokens instead of once per 16.
+template <int T>
 __global__ __launch_bounds__(1024) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                              const uint16_t* __restrict__ wg, int M, int E, int H,
                                                              float* __restrict__ logits) {
-  __shared__ f32x4 s_part[16][64];
+  __shared__ f32x4 s_part[16][T][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int e0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const int e0 = blockIdx.x * 16, m0 = blockIdx.y * 16 * T;
   // rows past E or M read the last valid row (their results are not stored)
   const uint16_t* pa = wg + (int64_t)min(e0 + r16, E - 1) * H + kq * 8;
-  const uint16_t* pb = x + (int64_t)min(m0 + r16, M - 1) * H + kq * 8;
+  const uint16_t* pb[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) pb[t] = x + (int64_t)min(m0 + 16 * t + r16, M - 1) * H + kq * 8;
   const int nsteps = H >> 5;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = wave;
   for (; s + 48 < nsteps; s += 64) {  // four steps of loads in flight
-    u32x4 a[4], b[4];
+    u32x4 a[4], b[4][T];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       a[u] = *(const u32x4*)(pa + (s + 16 * u) * 32);
-      b[u] = *(const u32x4*)(pb + (s + 16 * u) * 32);
+#pragma unroll
+      for (int t = 0; t < T; ++t) b[u][t] = *(const u32x4*)(pb[t] + (s + 16 * u) * 32);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = mfma_bf16(a[u], b[u], acc);
-  }
-  for (; s < nsteps; s += 16) acc = mfma_bf16(*(const u32x4*)(pa + s * 32), *(const u32x4*)(pb + s * 32), acc);
-  s_part[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-  f32x4 sum = s_part[0][lane];
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-  for (int w = 1; w < 16; ++w) sum += s_part[w][lane];
-  // lane holds experts e0 + 4*kq + 0..3 of token m0 + r16
-  const int m = m0 + r16;
+      for (int t = 0; t < T; ++t) acc[t] = mfma_bf16(a[u], b[u][t], acc[t]);
+  }
+  for (; s < nsteps; s += 16) {
+    const u32x4 a = *(const u32x4*)(pa + s * 32);
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = mfma_bf16(a, *(const u32x4*)(pb[t] + s * 32), acc[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) s_part[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (wave >= T) return;
+  // wave t adds the 16 wave sums of token tile t, in wave order
+  f32x4 sum = s_part[0][wave][lane];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) sum += s_part[w][wave][lane];
+  // lane holds experts e0 + 4*kq + 0..3 of token m0 + 16*wave + r16
+  const int m = m0 + 16 * wave + r16;
   if (m < M) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
