@@ -285,7 +285,7 @@ def main() -> int:
                                                                                cfg.H, cfg.I, ms_str),
             "E": cfg.E, "top_k": cfg.k, "H": cfg.H, "I": cfg.I, "M_sweep": list(cfg.ms), "router_logits": cfg.logits,
             "weight_scales": ("per channel" if args.per_channel else "per tensor") if fp8 else None,
-            "router_logits": "computed in the layer from router weights" if args.router_gemm else "given",
+            "logits_source": "computed in the layer from router weights" if args.router_gemm else "given",
         },
         "per_m": per_m,
         "roofline": roof,
