@@ -758,11 +758,14 @@ __host__ __device__ constexpr int gemm2_red_bytes(int nt, int wks) {
 
 // Top-k combine and output rounding:
 //   y[m,n] = bf16( sum_j w[m,j] * (sum_s part[s][m*k+j][n]) )
-// One lane per (group of four outputs, expert slot j): the lane loads its
-// K slices all at once (s ascending), scales by w[m,j], and the KP lanes of a
+// One lane per (G groups of four outputs, expert slot j): the lane loads its
+// K slices (s ascending), scales by w[m,j], and the KP lanes of a
 // group (KP = k rounded up to a power of two) add their terms by a fixed
 // xor-butterfly, so the result does not depend on scheduling and every call
-// gives the same bits.  Also reports the fp8 scales in effect.
+// gives the same bits.  G = 4 at large M keeps four groups' loads in flight
+// per lane with a quarter of the workgroups; every output is the same sum.
+// Also reports the fp8 scales in effect.
+template <int G>
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, const float* __restrict__ topk_w,
                                                        uint16_t* __restrict__ y, int M, int H, int top_k, int log2kp,
                                                        int ksplit, const float* x_scale, const unsigned* h_amax,
@@ -772,32 +775,51 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
     scales_out[1] = h_scale ? *h_scale : scale_from_amax(__uint_as_float(*h_amax));
   }
   const int kp = 1 << log2kp;
-  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> log2kp;  // output group
+  const int64_t g = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> log2kp) * G;  // first output group
   const int j = threadIdx.x & (kp - 1);
-  const int64_t i = g * 4;
+  const int64_t i = g * 4;  // G groups of 4 outputs, one row (H is a multiple of 4*G)
   const bool live = i < (int64_t)M * H;
   const int m = live ? (int)(i / H) : 0, n = live ? (int)(i - (int64_t)m * H) : 0;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (live && j < top_k) {
     const int64_t f = (int64_t)m * top_k + j;
     const int64_t slice = (int64_t)M * top_k * H;
     const float* p = part + f * H + n;
-    f32x4 v[16];
+    const float w = topk_w[f];
+    if constexpr (G == 1) {  // every slice in flight at once
+      f32x4 v[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) v[s] = s < ksplit ? *(const f32x4*)(p + s * slice) : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 o = v[0];
+      for (int s = 0; s < 16; ++s) v[s] = s < ksplit ? *(const f32x4*)(p + s * slice) : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 o = v[0];
 #pragma unroll
-    for (int s = 1; s < 16; ++s)
-      if (s < ksplit) o += v[s];
-    acc = o * topk_w[f];
+      for (int s = 1; s < 16; ++s)
+        if (s < ksplit) o += v[s];
+      acc[0] = o * w;
+    } else {  // the G groups of a slice in flight at once, slices in order
+      f32x4 o[G];
+#pragma unroll
+      for (int q = 0; q < G; ++q) o[q] = *(const f32x4*)(p + 4 * q);
+      for (int s = 1; s < ksplit; ++s)
+#pragma unroll
+        for (int q = 0; q < G; ++q) o[q] += *(const f32x4*)(p + s * slice + 4 * q);
+#pragma unroll
+      for (int q = 0; q < G; ++q) acc[q] = o[q] * w;
+    }
   }
-  for (int off = 1; off < kp; off <<= 1) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
-  }
+  for (int q = 0; q < G; ++q)
+    for (int off = 1; off < kp; off <<= 1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[q][c] += __shfl_xor(acc[q][c], off);
+    }
   if (live && j == 0) {
-    uint2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    *(uint2*)(y + i) = out;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      uint2 out = {pack_bf16x2(acc[q][0], acc[q][1]), pack_bf16x2(acc[q][2], acc[q][3])};
+      *(uint2*)(y + i + 4 * q) = out;
+    }
   }
 }
 

@@ -793,9 +793,14 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   {
     const int64_t groups = (int64_t)M * H / 4;
     const int lkp = log2i(k);
-    finalize_kernel<<<(unsigned)cdiv(groups << lkp, 256), 256, 0, st>>>(part, wts, (uint16_t*)a->y, M, H, k, lkp,
-                                                                        plan.ks2, scale_slot, h_amax, a->h_scale,
-                                                                        fp8 ? a->scales_out : nullptr);
+    float* so = fp8 ? a->scales_out : nullptr;
+    // four groups per lane once that still leaves at least 256 workgroups
+    if ((groups << lkp) >= (int64_t)4 * 256 * 256)
+      finalize_kernel<4><<<(unsigned)cdiv((groups / 4) << lkp, 256), 256, 0, st>>>(
+          part, wts, (uint16_t*)a->y, M, H, k, lkp, plan.ks2, scale_slot, h_amax, a->h_scale, so);
+    else
+      finalize_kernel<1><<<(unsigned)cdiv(groups << lkp, 256), 256, 0, st>>>(
+          part, wts, (uint16_t*)a->y, M, H, k, lkp, plan.ks2, scale_slot, h_amax, a->h_scale, so);
   }
   rec(9);
   return launch_status();
