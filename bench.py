@@ -55,12 +55,12 @@ FLUSH_BYTES = 1 << 30
 DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "c282e47f9c3ef4e3ea088f3b663ca0d12522109553665fac205ebde59a98b0de",
-                "bytes_per_launch": 1510012782},
-    "qwen3": {"src_sha256": "c282e47f9c3ef4e3ea088f3b663ca0d12522109553665fac205ebde59a98b0de",
-              "bytes_per_launch": 241749200},
-    "deepseek": {"src_sha256": "c282e47f9c3ef4e3ea088f3b663ca0d12522109553665fac205ebde59a98b0de",
-                 "bytes_per_launch": 3292509242},
+    "mixtral": {"src_sha256": "1413612ebdc9810764a97a7d9212bf2a655dc60383e4e3f5bf5877ad8bde6c07",
+                "bytes_per_launch": 1510104077},
+    "qwen3": {"src_sha256": "1413612ebdc9810764a97a7d9212bf2a655dc60383e4e3f5bf5877ad8bde6c07",
+              "bytes_per_launch": 241752044},
+    "deepseek": {"src_sha256": "1413612ebdc9810764a97a7d9212bf2a655dc60383e4e3f5bf5877ad8bde6c07",
+                 "bytes_per_launch": 3292493968},
     "prefill": {"src_sha256": "b34f5ee278f37292ae1b8562f7b83f3ac3d9e94ea862026e7242b2bbdd9067bc",
                 "bytes_per_launch": 3056562960},
 }
