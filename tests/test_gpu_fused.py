@@ -349,5 +349,23 @@ def test_fused_with_router_weights(cfg, M):
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("M", [6, 1100])
+def test_router_weights_with_per_channel_scales(M):
+    # the two optional inputs together, on the decode and on the prefill path:
+    # logits from router weights, one weight scale per row, static x scale
+    cfg = MoEConfig("r_pc", E=16, k=8, H=512, I=512, dtype="fp8", ms=(M,), logits="normal")
+    w = gen_weights_per_channel(cfg, 25, device=DEV)
+    x = gen_x(cfg.H, M, 25, sub=M)
+    wg = gen_router_weights(cfg.E, cfg.H, 25)
+    lo = torch.empty(M, cfg.E, dtype=torch.float32, device=DEV)
+    xs = torch.tensor([0.013], device=DEV)
+    y = moe.fused_forward(x.to(DEV), None, w[0], w[1], cfg.k, "fp8", w[2], w[3], x_scale=xs, router_w=wg.to(DEV),
+                          logits_out=lo)
+    torch.cuda.synchronize()
+    toks = None if M <= 64 else [0, 7, M // 2, M - 1]
+    _, gpu, _ = compare(cfg, M, seed=25, weights=w, logits=lo.cpu(), x=x, x_scale=0.013, tokens=toks)
+    assert torch.equal(y.float().cpu(), torch.from_numpy(gpu["y"]).float())
+
+
 def test_prefill_dynamic_scales(prefill_w):
     compare(CONFIGS["prefill"], 256, seed=0, weights=prefill_w, tokens=[0, 5, 100, 255])
