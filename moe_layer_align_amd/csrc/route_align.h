@@ -677,6 +677,66 @@ __device__ __forceinline__ void small_align(const int* s_ids, int P, int E, int 
   }
 }
 
+// The same sort-and-pad for P <= 64 pairs by one wave (wave 0 of the
+// workgroup): a pair per lane, per-expert sums and the scan over experts in
+// the wave's own LDS, so no workgroup barrier follows the routing barrier.
+// The outputs are those of small_align bit for bit.  Requires ids[0..P) in
+// LDS before a barrier.
+__device__ __forceinline__ void wave_align(const int* s_ids, int P, int E, int log2B, int id_bits, const AlignOut& o,
+                                           SmallAlignLds& L) {
+  const int lane = threadIdx.x & 63;
+  const int B = 1 << log2B;
+  const bool valid = lane < P;
+  const int e = valid ? s_ids[lane] : 0;
+  unsigned long long match = __ballot(valid);
+  for (int b = 0; b < id_bits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const unsigned long long m1 = __ballot(bit);
+    match &= bit ? m1 : ~m1;
+  }
+  const int rank = valid ? __popcll(match & lanemask_lt(lane)) : 0;
+  for (int x = lane; x < E; x += 64) L.tot[x] = 0;
+  if (valid && rank == 0) L.tot[e] = __popcll(match);
+  // exclusive scan over experts of the padded sizes and active flags: lane
+  // l takes experts [l*npe, (l+1)*npe)
+  const int npe = (E + 63) >> 6;
+  const int x0 = lane * npe;
+  int pad_sum = 0, act_sum = 0;
+  for (int x = x0; x < min(x0 + npe, E); ++x) {
+    const int c = L.tot[x];
+    pad_sum += ((c + B - 1) >> log2B) << log2B;
+    act_sum += c > 0;
+  }
+  const int v = pad_sum | (act_sum << 20);  // padded total < 2^20 (P <= 64)
+  int run = wave_incl_scan(v) - v;
+  for (int x = x0; x < min(x0 + npe, E); ++x) {
+    const int c = L.tot[x];
+    L.off[x] = run & 0xfffff;
+    L.act[x] = run >> 20;
+    run += (((c + B - 1) >> log2B) << log2B) | ((c > 0) << 20);
+  }
+  if (x0 < E && x0 + npe >= E) {  // the lane holding the last expert
+    L.off[E] = run & 0xfffff;
+    L.act[E] = run >> 20;
+  }
+  if (valid) o.sorted_ids[L.off[e] + rank] = lane;
+  const int total = L.off[E];
+  for (int x = lane; x < E; x += 64) {
+    const int beg = L.off[x], end = L.off[x + 1];
+    o.counts[x] = L.tot[x];
+    o.offsets[x] = beg;
+    for (int p = beg + L.tot[x]; p < end; ++p) o.sorted_ids[p] = P;
+    for (int p = beg; p < end; p += B) o.block_expert[p >> log2B] = x;
+    if (o.active && L.tot[x] > 0) o.active[L.act[x]] = x;
+  }
+  for (int b = (total >> log2B) + lane; b < o.n_blocks; b += 64) o.block_expert[b] = -1;
+  if (lane == 0) {
+    o.offsets[E] = total;
+    *o.num_padded = total;
+    if (o.num_active) *o.num_active = L.act[E];
+  }
+}
+
 template <int NPL>
 __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __restrict__ logits, int M, int E, int K,
                                                               int32_t* __restrict__ ids, float* __restrict__ wts,
@@ -689,7 +749,8 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __res
   __shared__ SmallAlignLds L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15;
-  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&L.wc[0][0])[i] = 0;
+  if (M * K > 64)  // the per-wave tables of small_align (wave_align needs none)
+    for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&L.wc[0][0])[i] = 0;
   // routing: four tokens per wave, 64 per pass of the 16 waves
   for (int mb = wave * kRouteRows; mb < M; mb += 16 * kRouteRows) {
     const int m = mb + (lane >> 4);
@@ -704,6 +765,10 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __res
   }
   if (q.h_amax && tid == 0) *q.h_amax = 0u;
   __syncthreads();
+  if (M * K <= 64) {
+    if (wave == 0) wave_align(s_ids, M * K, E, log2B, id_bits, o, L);
+    return;
+  }
   small_align(s_ids, M * K, E, log2B, id_bits, o, L);
 }
 
