@@ -63,10 +63,11 @@ class _LayerArgs(ctypes.Structure):
         ("all_pairs_h", ctypes.c_int32),
         ("w13_scale_rows", ctypes.c_void_p),
         ("w2_scale_rows", ctypes.c_void_p),
+        ("n_shared", ctypes.c_int32),
     ]
 
 
-_ABI = 3  # oracle_abi_version() of moe_oracle.c that this binding matches
+_ABI = 4  # oracle_abi_version() of moe_oracle.c that this binding matches
 
 
 def _load():
@@ -217,7 +218,8 @@ def router_logits(x, w) -> np.ndarray:
 
 def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = None,
           w2_scale: Optional[float] = None, x_scale: Optional[float] = None, h_scale: Optional[float] = None,
-          tokens: Optional[Sequence[int]] = None, experts: Optional[dict] = None, all_pairs_h: Optional[bool] = None):
+          tokens: Optional[Sequence[int]] = None, experts: Optional[dict] = None, all_pairs_h: Optional[bool] = None,
+          n_shared: int = 0):
     """Reference output of the layer.
 
     x: bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] / w2 [E,H,I] (bf16 or e4m3
@@ -225,6 +227,8 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
     only the experts that are needed.  w13_scale/w2_scale (fp8): one float per
     tensor, or arrays [E,2I] / [E,H] with one scale per weight row.  x_scale/h_scale: static fp8 activation
     scales, None = dynamic amax/448.  tokens: rows of y to produce (default all).
+    n_shared: shared experts stacked after the E routed ones (w13 [E+n_shared,2I,H],
+    per-row scales [E+n_shared,..]); every token passes through each with weight one.
     Returns dict(y=float64 [T,H], ids, weights, s_x, s_h).
     """
     lib = _load()
@@ -235,19 +239,22 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
     M, H = xa.shape
     E = lg.shape[1]
     fp8 = dtype == "fp8"
+    EW = E + n_shared  # expert weight sets: routed, then shared
     keep = []  # keep numpy buffers alive
-    p13 = (ctypes.c_void_p * E)()
-    p2 = (ctypes.c_void_p * E)()
+    p13 = (ctypes.c_void_p * EW)()
+    p2 = (ctypes.c_void_p * EW)()
     I = None
     if experts is None:
         a13, a2 = _np(w13), _np(w2)
         keep += [a13, a2]
+        if a13.shape[0] != EW or a2.shape[0] != EW:
+            raise ValueError("w13/w2 must hold E + n_shared = %d experts" % EW)
         I = a13.shape[1] // 2
-        for e in range(E):
+        for e in range(EW):
             p13[e] = a13[e].ctypes.data
             p2[e] = a2[e].ctypes.data
     else:
-        for e in range(E):
+        for e in range(EW):
             if e in experts:
                 a13, a2 = _np(experts[e][0]), _np(experts[e][1])
                 keep += [a13, a2]
@@ -273,10 +280,10 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
         if sc is None or np.ndim(_np(sc)) == 0 or np.size(_np(sc)) == 1:
             return None
         arr = np.ascontiguousarray(_np(sc), dtype=np.float32)
-        if arr.shape != (E, rows):
-            raise ValueError("per-row scales must have shape %s, got %s" % ((E, rows), arr.shape))
+        if arr.shape != (EW, rows):
+            raise ValueError("per-row scales must have shape %s, got %s" % ((EW, rows), arr.shape))
         keep.append(arr)
-        ptrs = (ctypes.c_void_p * E)(*[arr[e].ctypes.data for e in range(E)])
+        ptrs = (ctypes.c_void_p * EW)(*[arr[e].ctypes.data for e in range(EW)])
         keep.append(ptrs)
         return ctypes.cast(ptrs, ctypes.c_void_p)
 
@@ -292,7 +299,7 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
         tokens=_ptr(tok) if tok.size else None, n_tokens=tok.size,
         y=_ptr(y) if y.size else None, ids=_ptr(ids) if ids.size else None, weights=_ptr(w) if w.size else None,
         s_x_out=_ptr(sx), s_h_out=_ptr(sh), all_pairs_h=int(bool(all_pairs_h)),
-        w13_scale_rows=rows13, w2_scale_rows=rows2,
+        w13_scale_rows=rows13, w2_scale_rows=rows2, n_shared=int(n_shared),
     )
     rc = lib.oracle_layer(ctypes.byref(args))
     if rc:

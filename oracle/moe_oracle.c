@@ -220,7 +220,7 @@ typedef struct {
   int32_t E, H, I, k, dtype;
   const uint16_t* x;            /* [M,H] bf16 */
   const float* logits;          /* [M,E] */
-  const void* const* w13;       /* E pointers, each [2I,H] bf16|e4m3; NULL = not provided */
+  const void* const* w13;       /* E + n_shared pointers, each [2I,H] bf16|e4m3; NULL = not provided */
   const void* const* w2;        /* E pointers, each [H,I] */
   float w13_scale, w2_scale;    /* fp8 only */
   int32_t x_scale_static;       /* fp8: 1 = use x_scale, 0 = amax/448 */
@@ -240,6 +240,9 @@ typedef struct {
    * W2[e]); NULL = one scale per tensor */
   const float* const* w13_scale_rows;
   const float* const* w2_scale_rows;
+  /* shared experts: every token also passes through experts E..E+n_shared-1
+   * (entries E.. of w13/w2 and of the row-scale arrays) with weight one */
+  int32_t n_shared;
 } oracle_layer_args;
 
 /* e4m3 code -> value, filled from oracle_e4m3_decode before any parallel
@@ -289,8 +292,8 @@ static void expert_up(const oracle_layer_args* A, int32_t e, const double* a, do
 
 int oracle_layer(oracle_layer_args* A) {
   const int64_t M = A->M;
-  const int32_t E = A->E, H = A->H, I = A->I, k = A->k;
-  if (M < 0 || E < 1 || k < 1 || k > E || H < 1 || I < 1) return ORC_ERR_ARG;
+  const int32_t E = A->E, H = A->H, I = A->I, k = A->k, S = A->n_shared;
+  if (M < 0 || E < 1 || k < 1 || k > E || H < 1 || I < 1 || S < 0) return ORC_ERR_ARG;
   if (A->dtype != ORC_DTYPE_BF16 && A->dtype != ORC_DTYPE_E4M3) return ORC_ERR_ARG;
   const int fp8 = A->dtype == ORC_DTYPE_E4M3;
   fill_e4m3_value();
@@ -298,7 +301,19 @@ int oracle_layer(oracle_layer_args* A) {
   int rc = oracle_route(A->logits, M, E, k, A->ids, A->weights);
   if (rc) return rc;
   if (M == 0) return ORC_OK;
-  const int64_t P = M * k;
+
+  /* The pairs of token m: its k routed experts with their routing weights,
+   * then each shared expert E+s (s < S) with weight one. */
+  const int32_t kk = k + S;
+  const int64_t P = M * kk;
+  int32_t* pid = (int32_t*)malloc(sizeof(int32_t) * (size_t)P);
+  double* pw = (double*)malloc(sizeof(double) * (size_t)P);
+  for (int64_t m = 0; m < M; ++m) {
+    for (int32_t j = 0; j < kk; ++j) {
+      pid[m * kk + j] = j < k ? A->ids[m * k + j] : E + (j - k);
+      pw[m * kk + j] = j < k ? (double)A->weights[m * k + j] : 1.0;
+    }
+  }
 
   /* which pairs need h */
   unsigned char* need = (unsigned char*)calloc((size_t)P, 1);
@@ -306,15 +321,19 @@ int oracle_layer(oracle_layer_args* A) {
     int64_t m = A->tokens[i];
     if (m < 0 || m >= M) {
       free(need);
+      free(pid);
+      free(pw);
       return ORC_ERR_ARG;
     }
-    for (int32_t j = 0; j < k; ++j) need[m * k + j] = 1;
+    for (int32_t j = 0; j < kk; ++j) need[m * kk + j] = 1;
   }
   if (A->all_pairs_h)
     for (int64_t p = 0; p < P; ++p) need[p] = 1;
   for (int64_t p = 0; p < P; ++p) {
-    if (need[p] && (A->w13[A->ids[p]] == NULL || A->w2[A->ids[p]] == NULL)) {
+    if (need[p] && (A->w13[pid[p]] == NULL || A->w2[pid[p]] == NULL)) {
       free(need);
+      free(pid);
+      free(pw);
       return ORC_ERR_MISSING_EXPERT;
     }
   }
@@ -344,12 +363,12 @@ int oracle_layer(oracle_layer_args* A) {
 #pragma omp for schedule(dynamic, 1)
     for (int64_t p = 0; p < P; ++p) {
       if (!need[p]) continue;
-      int64_t m = p / k;
+      int64_t m = p / kk;
       for (int64_t t = 0; t < H; ++t) {
         float xv = (float)oracle_bf16_decode(A->x[m * H + t]);
         a[t] = fp8 ? oracle_e4m3_decode(quant_e4m3(xv, r_x)) : (double)xv;
       }
-      expert_up(A, A->ids[p], a, (double)s_x, h + p * (int64_t)I);
+      expert_up(A, pid[p], a, (double)s_x, h + p * (int64_t)I);
     }
     free(a);
   }
@@ -389,13 +408,13 @@ int oracle_layer(oracle_layer_args* A) {
     for (int64_t n = 0; n < H; ++n) {
       int64_t m = A->tokens[i];
       double acc = 0.0;
-      for (int32_t j = 0; j < k; ++j) {
-        int64_t p = m * k + j;
-        const void* w = A->w2[A->ids[p]];
+      for (int32_t j = 0; j < kk; ++j) {
+        int64_t p = m * kk + j;
+        const void* w = A->w2[pid[p]];
         double o = 0.0;
         for (int64_t t = 0; t < I; ++t) o += hq[p * I + t] * weight_at(A->dtype, w, n * (int64_t)I + t);
-        if (fp8) o *= (double)s_h * w2_scale_of(A, A->ids[p], n);
-        acc += (double)A->weights[p] * o;
+        if (fp8) o *= (double)s_h * w2_scale_of(A, pid[p], n);
+        acc += pw[p] * o;
       }
       A->y[i * H + n] = acc;
     }
@@ -403,6 +422,8 @@ int oracle_layer(oracle_layer_args* A) {
   free(hq);
   free(h);
   free(need);
+  free(pid);
+  free(pw);
   return ORC_OK;
 }
 
@@ -433,4 +454,4 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 int oracle_num_threads(void) { return 1; }
 #endif
 
-int oracle_abi_version(void) { return 3; }
+int oracle_abi_version(void) { return 4; }

@@ -14,6 +14,11 @@
   tensor's scale give the per-tensor result bit for bit; with several experts
   each pair uses its own expert's rows (static activation scales, dense
   per-token sum of per-expert MLPs).
+* Shared experts (experts E.. that every token passes through with weight
+  one): with the routed down weights zeroed, y is the shared expert's SwiGLU
+  (float64 torch); with S shared experts, y equals the routed-only layer plus
+  each shared expert run alone as an E=1, k=1 layer, bit for bit; a dynamic h
+  scale is the larger of the routed-only and the shared-only scales.
 * A hand-derived fixture in tests/golden.
 Plausible mistakes (gate and up swapped, a sign in SiLU, a transposed W2, a
 dropped routing weight, the scale applied twice) each fail one of these.
@@ -214,3 +219,51 @@ def test_golden_hand_example():
     out = oracle.layer(x, lg, w13, w2, g["k"], "bf16")
     assert out["ids"].tolist() == g["ids"]
     assert np.array_equal(out["y"], np.array(g["y"], dtype=np.float64))
+
+
+def test_shared_expert_alone_is_swiglu_bf16():
+    cfg = small_cfg("bf16", 4, 2)
+    M = 5
+    x = gen_x(cfg.H, M, seed=11)
+    w13, w2, _, _ = gen_weights(cfg, seed=11, E=5)
+    w2[:4] = 0  # routed experts contribute exactly zero
+    lg = torch.randn(M, 4, generator=torch.Generator().manual_seed(11))
+    out = oracle.layer(x, lg, w13, w2, 2, "bf16", n_shared=1)
+    assert out["ids"].shape == (M, 2) and (out["ids"] < 4).all()
+    assert rel_err(out["y"], mlp_ref_bf16(x, w13[4], w2[4]).numpy()) < 1e-12
+
+
+@pytest.mark.parametrize("dtype,S", [("bf16", 1), ("bf16", 2), ("fp8", 1), ("fp8", 2)])
+def test_shared_experts_add_to_routed_output(dtype, S):
+    cfg = small_cfg(dtype, 4, 2)
+    M = 7
+    x = gen_x(cfg.H, M, seed=12)
+    w13, w2, s13, s2 = gen_weights(cfg, seed=12, E=4 + S)
+    lg = torch.randn(M, 4, generator=torch.Generator().manual_seed(12))
+    kw = dict(x_scale=0.02, h_scale=0.004) if dtype == "fp8" else {}
+    full = oracle.layer(x, lg, w13, w2, 2, dtype, s13, s2, n_shared=S, **kw)
+    ref = oracle.layer(x, lg, w13[:4], w2[:4], 2, dtype, s13, s2, **kw)
+    assert np.array_equal(full["ids"], ref["ids"]) and np.array_equal(full["weights"], ref["weights"])
+    y = ref["y"]
+    for s in range(S):
+        alone = oracle.layer(x, torch.zeros(M, 1), w13[4 + s:5 + s], w2[4 + s:5 + s], 1, dtype, s13, s2, **kw)
+        y = y + alone["y"]
+    assert np.array_equal(full["y"], y)
+
+
+def test_dynamic_h_scale_covers_shared_pairs():
+    cfg = small_cfg("fp8", 4, 2)
+    M = 6
+    x = gen_x(cfg.H, M, seed=13)
+    w13, w2, s13, s2 = gen_weights_per_channel(cfg, seed=13)
+    w13s, w2s, s13s, s2s = gen_weights_per_channel(cfg, seed=14)
+    w13 = torch.cat([w13, w13s[:1]])
+    w2 = torch.cat([w2, w2s[:1]])
+    r13 = torch.cat([s13, s13s[:1] * 8])  # the shared expert's h dominates
+    r2 = torch.cat([s2, s2s[:1]])
+    lg = torch.randn(M, 4, generator=torch.Generator().manual_seed(13))
+    full = oracle.layer(x, lg, w13, w2, 2, "fp8", r13, r2, n_shared=1)
+    routed = oracle.layer(x, lg, w13[:4], w2[:4], 2, "fp8", r13[:4], r2[:4])
+    alone = oracle.layer(x, torch.zeros(M, 1), w13[4:], w2[4:], 1, "fp8", r13[4:], r2[4:])
+    assert alone["s_h"] > routed["s_h"]
+    assert full["s_h"] == alone["s_h"] and full["s_x"] == routed["s_x"]
