@@ -171,6 +171,15 @@ typedef struct {
  * quantisation schemes: "Fused MoE on Hopper, ...", TL;DR; ZICQ, "AWS Unveils
  * MoE Kernel Optimizations ...", §Triton Backend Routing for FP8
  * Quantization).
+ * Shared experts (n_shared = S > 0; the pages do not describe them, and here
+ * they are the plain form): every token also passes through experts
+ * E..E+S-1, stacked after the routed ones in w13/w2 (and in per-row scales),
+ * with weight one.  From the routing on they are S more experts and S more
+ * slots per token: the sums above run over j < top_k+S, slot top_k+s of
+ * token m holds expert E+s with weight 1, s_h covers their h too, and
+ * topk_ids/topk_weights are [M,top_k+S], expert_counts [E+S].  Size the
+ * workspace with moe_fused_workspace_size(M, E+S, H, I, top_k+S, dtype).
+ * top_k+S <= 16 and E+S <= 512, else MOE_ERR_UNSUPPORTED.
  * The expert products put expert-weight rows in the wide MFMA operand and
  * the few tokens in the narrow one; at decode sizes this is the orientation
  * the pages call Swap-AB (B^T A^T instead of A B, "Fused MoE on Hopper, ..."
@@ -181,16 +190,16 @@ typedef struct {
   moe_dtype_t dtype;
   const void* x;           /* [M,H] bf16 hidden states */
   const float* logits;     /* [M,E] fp32 router logits, or NULL with router_w */
-  const void* w13;         /* [E,2I,H] bf16 or e4m3; rows [0,I) gate, [I,2I) up */
-  const void* w2;          /* [E,H,I] bf16 or e4m3 */
-  const float* w13_scale;  /* fp8: device fp32[1], or fp32[E*2I] per channel (16-byte aligned); bf16: NULL */
-  const float* w2_scale;   /* fp8: device fp32[1], or fp32[E*H] per channel (16-byte aligned); bf16: NULL */
+  const void* w13;         /* [E+S,2I,H] bf16 or e4m3; rows [0,I) gate, [I,2I) up */
+  const void* w2;          /* [E+S,H,I] bf16 or e4m3 */
+  const float* w13_scale;  /* fp8: device fp32[1], or fp32[(E+S)*2I] per channel (16-byte aligned); bf16: NULL */
+  const float* w2_scale;   /* fp8: device fp32[1], or fp32[(E+S)*H] per channel (16-byte aligned); bf16: NULL */
   const float* x_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
   const float* h_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
   void* y;                 /* [M,H] bf16 output (overwritten) */
-  int32_t* topk_ids;       /* optional out [M,top_k]; NULL = kept in the workspace */
-  float* topk_weights;     /* optional out [M,top_k] */
-  int32_t* expert_counts;  /* optional out [E] */
+  int32_t* topk_ids;       /* optional out [M,top_k+S]; NULL = kept in the workspace */
+  float* topk_weights;     /* optional out [M,top_k+S] */
+  int32_t* expert_counts;  /* optional out [E+S] */
   float* scales_out;       /* optional out fp32[2]: s_x, s_h used (fp8 only) */
   void* workspace;         /* device scratch, 256-byte aligned */
   size_t workspace_bytes;
@@ -202,6 +211,7 @@ typedef struct {
                               computes logits = x . router_w^T as moe_router_logits does and routes on them */
   float* logits_out;       /* optional out [M,E]: the logits computed from router_w (NULL = kept in the
                               workspace); must be NULL when logits is given */
+  int32_t n_shared;        /* S >= 0 shared experts after the E routed ones (see above); < 0: INVALID_ARG */
 } moe_fused_args_t;
 
 /* Host-only: workspace bytes needed by moe_fused_forward for these sizes. */

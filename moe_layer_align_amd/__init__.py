@@ -53,10 +53,12 @@ class _FusedArgs(ctypes.Structure):
         ("tuning", ctypes.POINTER(Tuning)),
         ("weight_scale_per_channel", ctypes.c_int32),
         ("router_w", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
+        ("n_shared", ctypes.c_int32),
     ]
 
 
 _lib = None
+_ABI = 6  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():
@@ -87,6 +89,9 @@ def load():
     lib.moe_fused_forward.argtypes = [ctypes.POINTER(_FusedArgs), vp]
     lib.moe_fused_forward_profiled.restype = ctypes.c_int
     lib.moe_fused_forward_profiled.argtypes = [ctypes.POINTER(_FusedArgs), vp, vp]
+    if lib.moe_abi_version() != _ABI:
+        raise RuntimeError("libmoe_mi355x.so has ABI version %d, this binding expects %d: rebuild it"
+                           % (lib.moe_abi_version(), _ABI))
     _lib = lib
     return lib
 
@@ -198,7 +203,7 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
                   topk_weights: Optional[torch.Tensor] = None, expert_counts: Optional[torch.Tensor] = None,
                   scales_out: Optional[torch.Tensor] = None, tuning: Optional[Tuning] = None, stream=None,
                   events=None, router_w: Optional[torch.Tensor] = None,
-                  logits_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  logits_out: Optional[torch.Tensor] = None, n_shared: int = 0) -> torch.Tensor:
     """The fused layer (moe_fused_forward).
 
     x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
@@ -207,6 +212,9 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
     [E,2I], w2_scale [E,H]); x_scale/h_scale: static fp8 activation scales or
     None (dynamic).  logits may be None when router_w (bf16 [E,H]) is given:
     the layer then computes them (into logits_out fp32 [M,E] when given).
+    n_shared: S shared experts stacked after the E routed ones (w13 [E+S,2I,H],
+    w2 [E+S,H,I], per-row scales [E+S,..]), each taken by every token with
+    weight one; topk_ids/topk_weights are then [M,top_k+S], expert_counts [E+S].
     events: optional list of 2*NUM_STAGES hipEvent_t handles (ints) recorded
     around the stages on the stream.
     """
@@ -216,6 +224,8 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
     E = logits.shape[1] if logits is not None else router_w.shape[0]
     fp8 = dtype == "fp8"
     I = w2.shape[2]
+    S = int(n_shared)
+    ES, KS = E + S, top_k + S
     wdt = torch.uint8 if fp8 else torch.bfloat16
     _need(x, "x", torch.bfloat16, (M, H))
     if logits is not None:
@@ -224,14 +234,14 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         _need(router_w, "router_w", torch.bfloat16, (E, H))
         if logits_out is not None:
             _need(logits_out, "logits_out", torch.float32, (M, E))
-    _need(w13, "w13", wdt, (E, 2 * I, H))
-    _need(w2, "w2", wdt, (E, H, I))
+    _need(w13, "w13", wdt, (ES, 2 * I, H))
+    _need(w2, "w2", wdt, (ES, H, I))
     per_channel = w13_scale is not None and w13_scale.dim() == 2
     if per_channel:
         if w2_scale is None:
             raise ValueError("per-channel w13_scale needs a per-channel w2_scale")
-        _need(w13_scale, "w13_scale", torch.float32, (E, 2 * I))
-        _need(w2_scale, "w2_scale", torch.float32, (E, H))
+        _need(w13_scale, "w13_scale", torch.float32, (ES, 2 * I))
+        _need(w2_scale, "w2_scale", torch.float32, (ES, H))
     for name, s in (("w13_scale", None if per_channel else w13_scale), ("w2_scale", None if per_channel else w2_scale),
                     ("x_scale", x_scale), ("h_scale", h_scale)):
         if s is not None:
@@ -240,15 +250,15 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         out = torch.empty(M, H, dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, (M, H))
     if topk_ids is not None:
-        _need(topk_ids, "topk_ids", torch.int32, (M, top_k))
+        _need(topk_ids, "topk_ids", torch.int32, (M, KS))
     if topk_weights is not None:
-        _need(topk_weights, "topk_weights", torch.float32, (M, top_k))
+        _need(topk_weights, "topk_weights", torch.float32, (M, KS))
     if expert_counts is not None:
-        _need(expert_counts, "expert_counts", torch.int32, (E,))
+        _need(expert_counts, "expert_counts", torch.int32, (ES,))
     if scales_out is not None:
         _need(scales_out, "scales_out", torch.float32, (2,))
     lib = load()
-    need = int(lib.moe_fused_workspace_size(M, E, H, I, top_k, DTYPE_FP8 if fp8 else DTYPE_BF16))
+    need = int(lib.moe_fused_workspace_size(M, ES, H, I, KS, DTYPE_FP8 if fp8 else DTYPE_BF16))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
@@ -262,7 +272,7 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         workspace=_ptr(workspace), workspace_bytes=workspace.numel(),
         tuning=ctypes.pointer(tuning) if tuning is not None else None,
         weight_scale_per_channel=int(per_channel),
-        router_w=_ptr(router_w), logits_out=_ptr(logits_out),
+        router_w=_ptr(router_w), logits_out=_ptr(logits_out), n_shared=S,
     )
     if events is None:
         _check("moe_fused_forward", lib.moe_fused_forward(ctypes.byref(args), _stream(stream)))

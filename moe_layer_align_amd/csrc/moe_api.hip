@@ -344,19 +344,19 @@ bool g2_nt(int nt, int u, int wks, dim3 g, size_t lds, hipStream_t st, const Gem
   return false;
 }
 
-bool launch_route(const float* logits, int M, int E, int k, int32_t* ids, float* wts, const RouteFusedArgs& fa,
+bool launch_route(const float* logits, int M, int E, int k, int S, int32_t* ids, float* wts, const RouteFusedArgs& fa,
                   hipStream_t st) {
   const dim3 grid((unsigned)route_grid(M, fa.x_amax_part ? (int64_t)M * fa.H : 0));
   switch ((int)cdiv(E, 16)) {  // keys per lane, rounded up to a power of two
-    case 1: route_topk_kernel<1><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
-    case 2: route_topk_kernel<2><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
-    case 3: case 4: route_topk_kernel<4><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
-    case 5: case 6: case 7: case 8: route_topk_kernel<8><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa); break;
+    case 1: route_topk_kernel<1><<<grid, 256, 0, st>>>(logits, M, E, k, S, ids, wts, fa); break;
+    case 2: route_topk_kernel<2><<<grid, 256, 0, st>>>(logits, M, E, k, S, ids, wts, fa); break;
+    case 3: case 4: route_topk_kernel<4><<<grid, 256, 0, st>>>(logits, M, E, k, S, ids, wts, fa); break;
+    case 5: case 6: case 7: case 8: route_topk_kernel<8><<<grid, 256, 0, st>>>(logits, M, E, k, S, ids, wts, fa); break;
     default:
       if (E <= 256)
-        route_topk_kernel<16><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+        route_topk_kernel<16><<<grid, 256, 0, st>>>(logits, M, E, k, S, ids, wts, fa);
       else
-        route_topk_kernel<32><<<grid, 256, 0, st>>>(logits, M, E, k, ids, wts, fa);
+        route_topk_kernel<32><<<grid, 256, 0, st>>>(logits, M, E, k, S, ids, wts, fa);
   }
   return true;
 }
@@ -404,19 +404,19 @@ moe_status_t launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
   return MOE_OK;
 }
 
-void launch_prologue_small(const float* logits, int M, int E, int k, int32_t* ids, float* wts, int B,
+void launch_prologue_small(const float* logits, int M, int E, int k, int S, int32_t* ids, float* wts, int B,
                            const AlignOut& o, const SmallQuant& q, hipStream_t st) {
-  const int lb = log2i(B), ib = log2i(E);
+  const int lb = log2i(B), ib = log2i(E + S);
   const dim3 grid(1 + (q.xq ? (unsigned)cdiv((int64_t)M * q.H, kSmallQuantPerWg) : 0u));
   switch ((int)cdiv(E, 16)) {
-    case 1: prologue_small_kernel<1><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q); break;
-    case 2: prologue_small_kernel<2><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q); break;
-    case 3: case 4: prologue_small_kernel<4><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q); break;
+    case 1: prologue_small_kernel<1><<<grid, 1024, 0, st>>>(logits, M, E, k, S, ids, wts, lb, ib, o, q); break;
+    case 2: prologue_small_kernel<2><<<grid, 1024, 0, st>>>(logits, M, E, k, S, ids, wts, lb, ib, o, q); break;
+    case 3: case 4: prologue_small_kernel<4><<<grid, 1024, 0, st>>>(logits, M, E, k, S, ids, wts, lb, ib, o, q); break;
     case 5: case 6: case 7: case 8:
-      prologue_small_kernel<8><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+      prologue_small_kernel<8><<<grid, 1024, 0, st>>>(logits, M, E, k, S, ids, wts, lb, ib, o, q);
       break;
     default:  // E <= kSmallMaxExperts
-      prologue_small_kernel<16><<<grid, 1024, 0, st>>>(logits, M, E, k, ids, wts, lb, ib, o, q);
+      prologue_small_kernel<16><<<grid, 1024, 0, st>>>(logits, M, E, k, S, ids, wts, lb, ib, o, q);
   }
 }
 
@@ -465,7 +465,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 5; }
+int32_t moe_abi_version(void) { return 6; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -474,7 +474,7 @@ moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t t
   if (M == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4)) return MOE_ERR_INVALID_ARG;
-  launch_route(logits, M, E, top_k, topk_ids, topk_weights, RouteFusedArgs{}, (hipStream_t)stream);
+  launch_route(logits, M, E, top_k, 0, topk_ids, topk_weights, RouteFusedArgs{}, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -533,7 +533,7 @@ size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int3
 static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev, const Layout& L,
                                     uint8_t* ws, int32_t* ids, float* wts, const AlignOut& o, float* xamax_part,
                                     float* scale_slot, unsigned* h_amax, uint8_t* xq, uint8_t* h, float* part,
-                                    bool hdyn) {
+                                    bool hdyn, int S) {
   const bool pc = a->weight_scale_per_channel == 1;
   auto rec = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
@@ -545,7 +545,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   rec(0);
   int32_t* hist = hist_usable(k) ? hist_buf : nullptr;
   RouteFusedArgs fa{(const uint16_t*)a->x, H, a->x_scale ? nullptr : xamax_part, hdyn ? h_amax : nullptr, hist};
-  launch_route(a->logits, M, E, k, ids, wts, fa, st);
+  launch_route(a->logits, M, E - S, k - S, S, ids, wts, fa, st);
   rec(1);
   if ((rc = launch_status()) != MOE_OK) return rc;
   rec(2);
@@ -615,10 +615,17 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   };
   moe_status_t rc = check_shape(a->M, a->E, a->top_k);
   if (rc != MOE_OK) return rc;
+  // shared experts: every token also passes through experts E..E+S-1 with
+  // weight one; from the routing on they are S more experts and S more slots
+  // per token
+  const int S = a->n_shared;
+  if (S < 0) return MOE_ERR_INVALID_ARG;
+  if ((rc = check_shape(a->M, a->E + S, a->top_k + S)) != MOE_OK) return rc;
   if (a->dtype != MOE_DTYPE_BF16 && a->dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (a->H < 128 || a->I < 128 || a->H % 128 || a->I % 128) return MOE_ERR_UNSUPPORTED;
   const bool fp8 = a->dtype == MOE_DTYPE_FP8_E4M3;
-  const int M = a->M, E = a->E, H = a->H, I = a->I, k = a->top_k;
+  const int Er = a->E, kr = a->top_k;  // the routed experts and slots
+  const int M = a->M, E = Er + S, H = a->H, I = a->I, k = kr + S;
   if (!fp8 && (a->w13_scale || a->w2_scale || a->x_scale || a->h_scale)) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_INVALID_ARG;
   if (a->weight_scale_per_channel != 0 && (a->weight_scale_per_channel != 1 || !fp8)) return MOE_ERR_INVALID_ARG;
@@ -654,22 +661,23 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   uint8_t* ws = (uint8_t*)a->workspace;
   // router logits from the hidden states (the step before routing), inside
   // the route stage: its start event is recorded here and not again
-  moe_fused_args_t with_logits;
+  moe_fused_args_t ax = *a;  // the layer as the steps after routing see it
+  ax.E = E;
+  ax.top_k = k;
   void* ev_rest[2 * MOE_NUM_STAGES];
   if (a->router_w) {
     float* lo = a->logits_out ? a->logits_out : (float*)(ws + L.logits);
     rec(0);
-    launch_router_logits(a->x, a->router_w, M, E, H, lo, st);
+    launch_router_logits(a->x, a->router_w, M, Er, H, lo, st);
     if ((rc = launch_status()) != MOE_OK) return rc;
-    with_logits = *a;
-    with_logits.logits = lo;
-    a = &with_logits;
+    ax.logits = lo;
     if (ev) {
       for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) ev_rest[i] = ev[i];
       ev_rest[0] = nullptr;
       ev = ev_rest;
     }
   }
+  a = &ax;
   int32_t* ids = a->topk_ids ? a->topk_ids : (int32_t*)(ws + L.ids);
   float* wts = a->topk_weights ? a->topk_weights : (float*)(ws + L.wts);
   int32_t* counts = a->expert_counts ? a->expert_counts : (int32_t*)(ws + L.counts);
@@ -689,13 +697,13 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   AlignOut o{counts, offsets, sorted, (int32_t*)(ws + L.block_expert), (int32_t*)(ws + L.num_padded), active,
              num_active, L.n_blocks};
   if (prefill)
-    return prefill_forward(a, st, ev, L, ws, ids, wts, o, xamax_part, scale_slot, h_amax, xq, h, part, hdyn);
+    return prefill_forward(a, st, ev, L, ws, ids, wts, o, xamax_part, scale_slot, h_amax, xq, h, part, hdyn, S);
   const bool small = P <= kSmallPairs && E <= kSmallMaxExperts && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
   if (small) {
     // 1+2. routing, align (and fp8 activation quantisation) in one workgroup
     rec(0);
     SmallQuant q{(const uint16_t*)a->x, H, a->x_scale, fp8 ? xq : nullptr, scale_slot, hdyn ? h_amax : nullptr};
-    launch_prologue_small(a->logits, M, E, k, ids, wts, kAlignBlockFused, o, q, st);
+    launch_prologue_small(a->logits, M, Er, kr, S, ids, wts, kAlignBlockFused, o, q, st);
     rec(1);
     rec(2);
     rec(3);
@@ -707,7 +715,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     int32_t* hist = (P > kSmallPairs && hist_usable(k)) ? (int32_t*)(ws + L.hist) : nullptr;
     RouteFusedArgs fa{(const uint16_t*)a->x, H, (fp8 && !a->x_scale) ? xamax_part : nullptr,
                       hdyn ? h_amax : nullptr, hist};
-    launch_route(a->logits, M, E, k, ids, wts, fa, st);
+    launch_route(a->logits, M, Er, kr, S, ids, wts, fa, st);
     rec(1);
     if ((rc = launch_status()) != MOE_OK) return rc;
 

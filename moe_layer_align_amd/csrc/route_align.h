@@ -177,8 +177,11 @@ __global__ __launch_bounds__(1024) void router_logits_kernel(const uint16_t* __r
   }
 }
 
+// S shared experts follow the E routed ones: slots K..K+S-1 of each token's
+// row of ids/wts (stride K+S) name experts E..E+S-1 with weight one, and the
+// expert counts cover all E+S.
 template <int NPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int M, int E, int K,
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int M, int E, int K, int S,
                                                          int32_t* __restrict__ ids, float* __restrict__ wts,
                                                          RouteFusedArgs fa) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -189,18 +192,23 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     int e;
     float w;
     route_row<NPL>(logits + (int64_t)min(m, M - 1) * E, m < M, E, K, l16, &e, &w);
-    const bool pair = m < M && l16 < K;
+    if (l16 >= K) {  // a shared expert's slot
+      e = E + (l16 - K);
+      w = 1.0f;
+    }
+    const int KS = K + S, ES = E + S;
+    const bool pair = m < M && l16 < KS;
     if (pair) {
-      ids[(int64_t)m * K + l16] = e;
-      wts[(int64_t)m * K + l16] = w;
+      ids[(int64_t)m * KS + l16] = e;
+      wts[(int64_t)m * KS + l16] = w;
     }
     if (fa.hist) {  // this workgroup's expert counts, for the align step
       __shared__ int s_hist[kMaxExperts];
-      for (int i = threadIdx.x; i < E; i += 256) s_hist[i] = 0;
+      for (int i = threadIdx.x; i < ES; i += 256) s_hist[i] = 0;
       __syncthreads();
       if (pair) atomicAdd(&s_hist[e], 1);
       __syncthreads();
-      for (int i = threadIdx.x; i < E; i += 256) fa.hist[(int64_t)blockIdx.x * E + i] = s_hist[i];
+      for (int i = threadIdx.x; i < ES; i += 256) fa.hist[(int64_t)blockIdx.x * ES + i] = s_hist[i];
     }
   }
   if (fa.x_amax_part) {
@@ -739,7 +747,7 @@ __device__ __forceinline__ void wave_align(const int* s_ids, int P, int E, int l
 
 template <int NPL>
 __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __restrict__ logits, int M, int E, int K,
-                                                              int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                              int S, int32_t* __restrict__ ids, float* __restrict__ wts,
                                                               int log2B, int id_bits, AlignOut o, SmallQuant q) {
   if (blockIdx.x > 0) {
     prologue_quant(q, (int64_t)M * q.H, blockIdx.x - 1);
@@ -749,7 +757,8 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __res
   __shared__ SmallAlignLds L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15;
-  if (M * K > 64)  // the per-wave tables of small_align (wave_align needs none)
+  const int KS = K + S, P = M * KS;  // routed slots, then the shared experts' (as in route_topk_kernel)
+  if (P > 64)  // the per-wave tables of small_align (wave_align needs none)
     for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&L.wc[0][0])[i] = 0;
   // routing: four tokens per wave, 64 per pass of the 16 waves
   for (int mb = wave * kRouteRows; mb < M; mb += 16 * kRouteRows) {
@@ -757,19 +766,23 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __res
     int e;
     float w;
     route_row<NPL>(logits + (int64_t)min(m, M - 1) * E, m < M, E, K, l16, &e, &w);
-    if (m < M && l16 < K) {
-      ids[m * K + l16] = e;
-      wts[m * K + l16] = w;
-      s_ids[m * K + l16] = e;
+    if (l16 >= K) {
+      e = E + (l16 - K);
+      w = 1.0f;
+    }
+    if (m < M && l16 < KS) {
+      ids[m * KS + l16] = e;
+      wts[m * KS + l16] = w;
+      s_ids[m * KS + l16] = e;
     }
   }
   if (q.h_amax && tid == 0) *q.h_amax = 0u;
   __syncthreads();
-  if (M * K <= 64) {
-    if (wave == 0) wave_align(s_ids, M * K, E, log2B, id_bits, o, L);
+  if (P <= 64) {
+    if (wave == 0) wave_align(s_ids, P, E + S, log2B, id_bits, o, L);
     return;
   }
-  small_align(s_ids, M * K, E, log2B, id_bits, o, L);
+  small_align(s_ids, P, E + S, log2B, id_bits, o, L);
 }
 
 // Align of P <= 1024 router-produced pairs (valid ids) in workgroup 0 of

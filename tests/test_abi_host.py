@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def capacity_formula(M, k, E, B):
@@ -140,6 +140,9 @@ def fused_args(**kw):
     (dict(logits=None), 1),                                  # neither
     (dict(logits_out=FAKE), 1),                              # logits out without router weights
     (dict(logits=None, router_w=FAKE + 8), 1),               # misaligned router weights
+    (dict(n_shared=-1), 1),                                  # negative shared-expert count
+    (dict(n_shared=15), 2),                                  # top_k + shared above 16
+    (dict(E=500, n_shared=13), 2),                           # E + shared above 512
 ])
 def test_fused_validation(lib, kw, code):
     args = fused_args(**kw)

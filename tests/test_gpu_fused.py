@@ -369,3 +369,42 @@ def test_router_weights_with_per_channel_scales(M):
 
 def test_prefill_dynamic_scales(prefill_w):
     compare(CONFIGS["prefill"], 256, seed=0, weights=prefill_w, tokens=[0, 5, 100, 255])
+
+
+# ---------------------------------------------------------------- shared experts
+# Every token also passes through the S experts stacked after the E routed
+# ones, with weight one: slots k..k+S-1 of the routing.  The cases cover the
+# one-wave align (M*(k+S) <= 64), the one-workgroup align, the router + align
+# launches with (k+S a power of two) and without the router's histograms, and
+# the tiled prefill products.
+@pytest.mark.parametrize("dtype,xs,hs", [("bf16", None, None), ("fp8", None, None), ("fp8", 0.02, 0.004)])
+@pytest.mark.parametrize("M,S", [(5, 1), (40, 1), (40, 2), (600, 1), (600, 2)])
+def test_shared_experts_small_layer(dtype, xs, hs, M, S):
+    compare(cfg_of(dtype, 6, 2, 512, 384), M, seed=30 + M + S, x_scale=xs, h_scale=hs, n_shared=S)
+
+
+def test_shared_expert_qwen3_shape():
+    compare(CONFIGS["qwen3"], 16, seed=31, n_shared=1)
+
+
+@pytest.mark.parametrize("k,S", [(8, 1), (7, 1)])
+def test_shared_expert_prefill_path(k, S):
+    cfg = MoEConfig("pf_shared", E=16, k=k, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf")
+    compare(cfg, 1100, seed=32 + k, tokens=[0, 1, 2, 3, 500, 777, 1098, 1099], n_shared=S)
+
+
+def test_shared_expert_per_channel_with_router_weights():
+    # per-row weight scales (the shared expert's rows after the routed ones)
+    # and logits computed from router weights inside the call; the same layer
+    # on those logits, given, gives the same bits and the oracle's output
+    cfg = cfg_of("fp8", 16, 4, 512, 384)
+    M, S = 24, 1
+    w13, w2, s13, s2 = gen_weights_per_channel(cfg_of("fp8", 16 + S, 4, 512, 384), 33, device=DEV)
+    x = gen_x(cfg.H, M, 33, sub=M)
+    rw = gen_router_weights(cfg.E, cfg.H, 33, device=DEV)
+    lo = torch.empty(M, cfg.E, dtype=torch.float32, device=DEV)
+    b = moe.fused_forward(x.to(DEV), None, w13, w2, cfg.k, "fp8", s13, s2, router_w=rw, logits_out=lo, n_shared=S)
+    a = moe.fused_forward(x.to(DEV), lo, w13, w2, cfg.k, "fp8", s13, s2, n_shared=S)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    compare(cfg, M, seed=33, weights=(w13, w2, s13, s2), x=x, logits=lo.cpu(), n_shared=S)
