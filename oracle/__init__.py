@@ -225,7 +225,8 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
     x: bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] / w2 [E,H,I] (bf16 or e4m3
     codes), or None together with `experts`, a dict e -> (w13_e, w2_e) holding
     only the experts that are needed.  w13_scale/w2_scale (fp8): one float per
-    tensor, or arrays [E,2I] / [E,H] with one scale per weight row.  x_scale/h_scale: static fp8 activation
+    tensor, arrays [E,2I] / [E,H] with one scale per weight row, or arrays
+    [E] with one per expert.  x_scale/h_scale: static fp8 activation
     scales, None = dynamic amax/448.  tokens: rows of y to produce (default all).
     n_shared: shared experts stacked after the E routed ones (w13 [E+n_shared,2I,H],
     per-row scales [E+n_shared,..]); every token passes through each with weight one.
@@ -276,10 +277,13 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
         all_pairs_h = fp8 and h_scale is None
 
     def scale_rows(sc, rows):
-        # one scale per weight row: E pointers to that expert's fp32 row scales
+        # one scale per weight row: E pointers to that expert's fp32 row scales;
+        # one scale per expert ([E], E > 1) is every row of that expert at it
         if sc is None or np.ndim(_np(sc)) == 0 or np.size(_np(sc)) == 1:
             return None
         arr = np.ascontiguousarray(_np(sc), dtype=np.float32)
+        if arr.shape == (EW,):
+            arr = np.ascontiguousarray(np.repeat(arr[:, None], rows, axis=1))
         if arr.shape != (EW, rows):
             raise ValueError("per-row scales must have shape %s, got %s" % ((EW, rows), arr.shape))
         keep.append(arr)

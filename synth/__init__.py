@@ -181,6 +181,34 @@ def gen_weights_per_channel(cfg: MoEConfig, seed: int = 0, device="cpu"):
     return w13, w2, s13, s2
 
 
+def gen_weights_per_expert(cfg: MoEConfig, seed: int = 0, device="cpu", E: Optional[int] = None):
+    """fp8 expert weights with one scale per expert and weight tensor.
+
+    The normal draws of gen_weights with expert e's standard deviation
+    multiplied by 0.5 * (1 + e % 4), so that the experts' scales differ by up
+    to 4x; W13[e] and W2[e] are stored as e4m3fn codes of W/s with
+    s = amax(|W|)/448 over that expert's tensor.  Returns (w13, w2, s13, s2):
+    uint8 codes and fp32 tensors s13 [E], s2 [E] on `device`.
+    """
+    if cfg.dtype != "fp8":
+        raise ValueError("per-expert scales are for fp8 layers")
+    E = cfg.E if E is None else E
+    H, I = cfg.H, cfg.I
+    w13 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
+    w2 = torch.empty(E, H, I, dtype=torch.uint8, device=device)
+    s13 = torch.empty(E, dtype=torch.float32, device=device)
+    s2 = torch.empty(E, dtype=torch.float32, device=device)
+    for e in range(E):
+        f = 0.5 * (1 + e % 4)
+        for w, s, t, rows, cols, std in ((w13, s13, _T_W13, 2 * I, H, f / math.sqrt(H)),
+                                         (w2, s2, _T_W2, H, I, f / math.sqrt(I))):
+            v = _expert_normal(seed, t, e, rows, cols, std, device)
+            sc = v.abs().amax() / E4M3_MAX
+            s[e] = sc
+            w[e] = (v / sc).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return w13, w2, s13, s2
+
+
 @dataclasses.dataclass
 class LayerInputs:
     cfg: MoEConfig

@@ -14,6 +14,9 @@
   tensor's scale give the per-tensor result bit for bit; with several experts
   each pair uses its own expert's rows (static activation scales, dense
   per-token sum of per-expert MLPs).
+* One weight scale per expert: scales all equal to the tensor's give the
+  per-tensor output bit for bit; unequal scales (up to 4x apart): the dense
+  per-token sum of float64 per-expert MLPs, each with its expert's scales.
 * Shared experts (experts E.. that every token passes through with weight
   one): with the routed down weights zeroed, y is the shared expert's SwiGLU
   (float64 torch); with S shared experts, y equals the routed-only layer plus
@@ -32,7 +35,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, MoEConfig, gen_weights, gen_weights_per_channel, gen_x
+from synth import CONFIGS, MoEConfig, gen_weights, gen_weights_per_channel, gen_weights_per_expert, gen_x
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -267,3 +270,34 @@ def test_dynamic_h_scale_covers_shared_pairs():
     alone = oracle.layer(x, torch.zeros(M, 1), w13[4:], w2[4:], 1, "fp8", r13[4:], r2[4:])
     assert alone["s_h"] > routed["s_h"]
     assert full["s_h"] == alone["s_h"] and full["s_x"] == routed["s_x"]
+
+
+def test_per_expert_equal_scales_is_per_tensor():
+    cfg = small_cfg("fp8", 4, 2)
+    x = gen_x(cfg.H, 9, seed=15)
+    lg = torch.randn(9, 4, generator=torch.Generator().manual_seed(15))
+    w13, w2, s13, s2 = gen_weights(cfg, seed=15)
+    a = oracle.layer(x, lg, w13, w2, 2, "fp8", s13, s2)
+    b = oracle.layer(x, lg, w13, w2, 2, "fp8", torch.full((4,), s13), torch.full((4,), s2))
+    assert np.array_equal(a["y"], b["y"]) and a["s_h"] == b["s_h"]
+
+
+@pytest.mark.parametrize("static", [False, True])
+def test_per_expert_scales_follow_each_pairs_expert(static):
+    cfg = small_cfg("fp8", 4, 2)
+    M = 6
+    x = gen_x(cfg.H, M, seed=16)
+    lg = torch.randn(M, 4, generator=torch.Generator().manual_seed(16))
+    w13, w2, s13, s2 = gen_weights_per_expert(cfg, seed=16)
+    assert float(s13.max() / s13.min()) > 3
+    xs, hs = (0.02, 0.004) if static else (None, None)
+    out = oracle.layer(x, lg, w13, w2, 2, "fp8", s13, s2, x_scale=xs, h_scale=hs)
+    if not static:  # the scales the oracle took, checked on their own by the E = 1 pins
+        xs, hs = out["s_x"], out["s_h"]
+    ref = np.zeros((M, cfg.H))
+    for m in range(M):
+        for j in range(2):
+            e = int(out["ids"][m, j])
+            o, _, _ = mlp_ref_fp8(x[m:m + 1], w13[e], w2[e], float(s13[e]), float(s2[e]), sx=xs, sh=hs)
+            ref[m] += float(out["weights"][m, j]) * o[0].numpy()
+    assert rel_err(out["y"], ref) < 1e-12
