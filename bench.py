@@ -55,14 +55,14 @@ FLUSH_BYTES = 1 << 30
 DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "1413612ebdc9810764a97a7d9212bf2a655dc60383e4e3f5bf5877ad8bde6c07",
-                "bytes_per_launch": 1510104077},
-    "qwen3": {"src_sha256": "1413612ebdc9810764a97a7d9212bf2a655dc60383e4e3f5bf5877ad8bde6c07",
-              "bytes_per_launch": 241752044},
-    "deepseek": {"src_sha256": "1413612ebdc9810764a97a7d9212bf2a655dc60383e4e3f5bf5877ad8bde6c07",
-                 "bytes_per_launch": 3292493968},
-    "prefill": {"src_sha256": "b34f5ee278f37292ae1b8562f7b83f3ac3d9e94ea862026e7242b2bbdd9067bc",
-                "bytes_per_launch": 3056562960},
+    "mixtral": {"src_sha256": "62a62d77bce3fe6f8b4dec368dcaf03b9bb2b68f92ade3139c8add043047c99f",
+                "bytes_per_launch": 1510074290},
+    "qwen3": {"src_sha256": "62a62d77bce3fe6f8b4dec368dcaf03b9bb2b68f92ade3139c8add043047c99f",
+              "bytes_per_launch": 241755112},
+    "deepseek": {"src_sha256": "62a62d77bce3fe6f8b4dec368dcaf03b9bb2b68f92ade3139c8add043047c99f",
+                 "bytes_per_launch": 3292474268},
+    "prefill": {"src_sha256": "f621dc48fc397a5fb03f177e419476c47058ec661e022bb55320c5f0a2d23658",
+                "bytes_per_launch": 3025681692},
 }
 
 

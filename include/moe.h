@@ -163,11 +163,12 @@ typedef struct {
  * fp8 mode: a_m = e4m3(x[m] / s_x) and hq = e4m3(h / s_h) (moe_quant_e4m3's
  * rounding); the products are rescaled by s_x*s_w13 and s_h*s_w2.  s_x and
  * s_h are the caller's static scales when given, else amax/448 over all of x
- * and over h of all pairs (1.0 when the amax is 0).  The weight scales are
- * one per tensor, or with weight_scale_per_channel one per weight row (output
- * channel): row n of W13[e] (gate or up feature) is rescaled by
- * w13_scale[e*2I + n] and row n of W2[e] (output feature) by w2_scale[e*H + n]
- * (the pages name tensor-quantised FP8 experts and routing among
+ * and over h of all pairs (1.0 when the amax is 0).  The weight scales
+ * (weight_scale_mode) are one per tensor (0: s_w13 = w13_scale[0]), one per
+ * weight row (1, output channel: row n of W13[e], a gate or up feature, is
+ * rescaled by w13_scale[e*2I + n] and row n of W2[e], an output feature, by
+ * w2_scale[e*H + n]) or one per expert (2: every row of W13[e] by
+ * w13_scale[e], of W2[e] by w2_scale[e]) (the pages name tensor-quantised FP8 experts and routing among
  * quantisation schemes: "Fused MoE on Hopper, ...", TL;DR; ZICQ, "AWS Unveils
  * MoE Kernel Optimizations ...", §Triton Backend Routing for FP8
  * Quantization).
@@ -192,8 +193,10 @@ typedef struct {
   const float* logits;     /* [M,E] fp32 router logits, or NULL with router_w */
   const void* w13;         /* [E+S,2I,H] bf16 or e4m3; rows [0,I) gate, [I,2I) up */
   const void* w2;          /* [E+S,H,I] bf16 or e4m3 */
-  const float* w13_scale;  /* fp8: device fp32[1], or fp32[(E+S)*2I] per channel (16-byte aligned); bf16: NULL */
-  const float* w2_scale;   /* fp8: device fp32[1], or fp32[(E+S)*H] per channel (16-byte aligned); bf16: NULL */
+  const float* w13_scale;  /* fp8: device fp32[1], fp32[(E+S)*2I] per row (16-byte aligned) or fp32[E+S] per
+                              expert; bf16: NULL */
+  const float* w2_scale;   /* fp8: device fp32[1], fp32[(E+S)*H] per row (16-byte aligned) or fp32[E+S] per
+                              expert; bf16: NULL */
   const float* x_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
   const float* h_scale;    /* fp8: NULL = dynamic, else device fp32[1]; bf16: NULL */
   void* y;                 /* [M,H] bf16 output (overwritten) */
@@ -204,8 +207,8 @@ typedef struct {
   void* workspace;         /* device scratch, 256-byte aligned */
   size_t workspace_bytes;
   const moe_tuning_t* tuning; /* host pointer or NULL */
-  int32_t weight_scale_per_channel; /* fp8: 0 = one scale per weight tensor, 1 = one per weight row;
-                                       any other value, or non-zero in bf16 mode: MOE_ERR_INVALID_ARG */
+  int32_t weight_scale_mode; /* fp8: 0 = one scale per weight tensor, 1 = one per weight row, 2 = one per
+                                expert; any other value, or non-zero in bf16 mode: MOE_ERR_INVALID_ARG */
   const void* router_w;    /* bf16 [E,H] router weights, 16-byte aligned, or NULL.  Exactly one of logits and
                               router_w is non-NULL (else MOE_ERR_INVALID_ARG); with router_w the layer first
                               computes logits = x . router_w^T as moe_router_logits does and routes on them */

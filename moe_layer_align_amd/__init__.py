@@ -51,14 +51,14 @@ class _FusedArgs(ctypes.Structure):
         ("topk_weights", ctypes.c_void_p), ("expert_counts", ctypes.c_void_p), ("scales_out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("tuning", ctypes.POINTER(Tuning)),
-        ("weight_scale_per_channel", ctypes.c_int32),
+        ("weight_scale_mode", ctypes.c_int32),
         ("router_w", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
         ("n_shared", ctypes.c_int32),
     ]
 
 
 _lib = None
-_ABI = 6  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
+_ABI = 7  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():
@@ -208,8 +208,8 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
 
     x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
     (dtype "bf16") or uint8 e4m3fn codes (dtype "fp8") with fp32 device
-    scales, either one per tensor ([1] each) or one per weight row (w13_scale
-    [E,2I], w2_scale [E,H]); x_scale/h_scale: static fp8 activation scales or
+    scales, either one per tensor ([1] each), one per weight row (w13_scale
+    [E,2I], w2_scale [E,H]) or one per expert ([E] each); x_scale/h_scale: static fp8 activation scales or
     None (dynamic).  logits may be None when router_w (bf16 [E,H]) is given:
     the layer then computes them (into logits_out fp32 [M,E] when given).
     n_shared: S shared experts stacked after the E routed ones (w13 [E+S,2I,H],
@@ -236,13 +236,18 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
             _need(logits_out, "logits_out", torch.float32, (M, E))
     _need(w13, "w13", wdt, (ES, 2 * I, H))
     _need(w2, "w2", wdt, (ES, H, I))
-    per_channel = w13_scale is not None and w13_scale.dim() == 2
-    if per_channel:
-        if w2_scale is None:
-            raise ValueError("per-channel w13_scale needs a per-channel w2_scale")
+    # weight scale mode from the scale shapes: [E+S,rows] one per row (1),
+    # [E+S] with E+S > 1 one per expert (2), [1] one per tensor (0)
+    mode = 0
+    if w13_scale is not None and w13_scale.dim() == 2:
+        mode = 1
         _need(w13_scale, "w13_scale", torch.float32, (ES, 2 * I))
         _need(w2_scale, "w2_scale", torch.float32, (ES, H))
-    for name, s in (("w13_scale", None if per_channel else w13_scale), ("w2_scale", None if per_channel else w2_scale),
+    elif w13_scale is not None and ES > 1 and w13_scale.numel() == ES:
+        mode = 2
+        _need(w13_scale, "w13_scale", torch.float32, (ES,))
+        _need(w2_scale, "w2_scale", torch.float32, (ES,))
+    for name, s in (("w13_scale", None if mode else w13_scale), ("w2_scale", None if mode else w2_scale),
                     ("x_scale", x_scale), ("h_scale", h_scale)):
         if s is not None:
             _need(s, name, torch.float32, (1,))
@@ -271,7 +276,7 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         expert_counts=_ptr(expert_counts), scales_out=_ptr(scales_out),
         workspace=_ptr(workspace), workspace_bytes=workspace.numel(),
         tuning=ctypes.pointer(tuning) if tuning is not None else None,
-        weight_scale_per_channel=int(per_channel),
+        weight_scale_mode=mode,
         router_w=_ptr(router_w), logits_out=_ptr(logits_out), n_shared=S,
     )
     if events is None:

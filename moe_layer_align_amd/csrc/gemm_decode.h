@@ -151,21 +151,24 @@ struct Gemm1Args {
   uint8_t* h;                // [P][I] in HFMT
   unsigned* h_amax;          // fp8 dynamic: running max of |h| (float bits)
   int w_cs = 0;              // fp8: 1 = w_scale holds one scale per weight row, 0 = one per tensor
+  int w_es = 0;              // fp8 without w_cs: 1 = one scale per expert (w_scale[e]), 0 = w_scale[0]
 };
 
 // fp8 dequantisation factors s_a * s_w: with one scale per weight row (PC)
 // those of the four rows row0..row0+3 of expert e (rows_e rows per expert),
-// else the tensor's one scale for all four.  The kernels branch on w_cs once,
+// else the one scale of expert e (es = 1) or of the tensor (es = 0) for all
+// four.  The kernels branch on w_cs once,
 // at entry, into bodies specialised on PC, so the per-tensor bodies carry no
 // per-row work.
 template <bool PC>
-__device__ __forceinline__ void row_deq4(const float* w_scale, int e, int rows_e, int row0, float sa, float (&d)[4]) {
+__device__ __forceinline__ void row_deq4(const float* w_scale, int e, int rows_e, int row0, float sa, float (&d)[4],
+                                         int es) {
   if constexpr (PC) {
     const float* ws = w_scale + (int64_t)e * rows_e;
 #pragma unroll
     for (int r = 0; r < 4; ++r) d[r] = sa * ws[row0 + r];
   } else {
-    const float v = sa * w_scale[0];
+    const float v = sa * w_scale[(int64_t)e * es];
 #pragma unroll
     for (int r = 0; r < 4; ++r) d[r] = v;
   }
@@ -230,8 +233,8 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
   // dequantisation of this lane's rows: gate rows i0+4kq.., up rows I+i0+4kq..
   float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (FP8) {
-    row_deq4<PC>(a.w_scale, e, 2 * a.I, i0 + kq * 4, *a.x_scale, dg);
-    row_deq4<PC>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, *a.x_scale, du);
+    row_deq4<PC>(a.w_scale, e, 2 * a.I, i0 + kq * 4, *a.x_scale, dg, a.w_es);
+    row_deq4<PC>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, *a.x_scale, du, a.w_es);
   }
   float rh = 1.0f;
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
@@ -392,8 +395,8 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
   const float sx = FP8 ? *a.x_scale : 1.0f;
   float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (FP8 && !PC) {  // one scale per tensor: the same factors for every tile
-    row_deq4<false>(a.w_scale, e, 0, 0, sx, dg);
-    row_deq4<false>(a.w_scale, e, 0, 0, sx, du);
+    row_deq4<false>(a.w_scale, e, 0, 0, sx, dg, a.w_es);
+    row_deq4<false>(a.w_scale, e, 0, 0, sx, du, a.w_es);
   }
   float rh = 1.0f;
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
@@ -404,8 +407,8 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
   auto epi = [&](int j, f32x4 (&c)[2][NB]) {
     const int i0 = (ft0 + 4 * j) * 16;
     if constexpr (FP8 && PC) {
-      row_deq4<true>(a.w_scale, e, 2 * a.I, i0 + kq * 4, sx, dg);
-      row_deq4<true>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, sx, du);
+      row_deq4<true>(a.w_scale, e, 2 * a.I, i0 + kq * 4, sx, dg, a.w_es);
+      row_deq4<true>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, sx, du, a.w_es);
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
@@ -493,6 +496,7 @@ struct Gemm2Args {
   float* part;               // [ksplit][P][H] partial outputs
   int P;
   int w_cs = 0;              // fp8: 1 = one scale per weight row, 0 = one per tensor
+  int w_es = 0;              // fp8 without w_cs: 1 = one scale per expert (w_scale[e]), 0 = w_scale[0]
 };
 
 // LDS row stride (bytes) of the quantised token slice: Kw plus 16 bytes so
@@ -550,8 +554,8 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
   float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (FP8) {
     const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
-    row_deq4<PC>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0);
-    row_deq4<PC>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1);
+    row_deq4<PC>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0, a.w_es);
+    row_deq4<PC>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1, a.w_es);
     if constexpr (QH) {
       stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
       __syncthreads();
@@ -670,8 +674,8 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
   if constexpr (FP8) {
     sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
     if constexpr (!PC) {  // one scale per tensor: the same factors for every tile
-      row_deq4<false>(a.w_scale, e, 0, 0, sh, d0);
-      row_deq4<false>(a.w_scale, e, 0, 0, sh, d1);
+      row_deq4<false>(a.w_scale, e, 0, 0, sh, d0, a.w_es);
+      row_deq4<false>(a.w_scale, e, 0, 0, sh, d1, a.w_es);
     }
     if constexpr (QH) {
       stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
@@ -707,8 +711,8 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
   auto epi = [&](int j, f32x4 (&c)[2][NB]) {
     const int n0 = (rt0 + 4 * j) * 32;
     if constexpr (FP8 && PC) {
-      row_deq4<true>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0);
-      row_deq4<true>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1);
+      row_deq4<true>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0, a.w_es);
+      row_deq4<true>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1, a.w_es);
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {

@@ -159,12 +159,14 @@ struct PrefillArgs {
   int H, I, top_k, P;
   int tiles;               // weight tiles: I/128 (128 gate + 128 up rows each) or H/256
   int items;               // bound on the linear item index: 8 x tiles x blocks per XCD (largest case)
-  const float* w_scale;    // s_w13 or s_w2: one per tensor, or one per weight row ([E][2I] / [E][H], PC)
+  const float* w_scale;    // s_w13 or s_w2: one per tensor, per expert ([E], w_es = 1) or per weight row
+                           // ([E][2I] / [E][H], PC)
   const float* a_scale;    // gate/up: s_x in effect; down: static s_h (null = dynamic)
   const unsigned* h_amax;  // down with dynamic scale: max |h| (float bits)
   const float* h_scale;    // gate/up: static s_h (null = dynamic: h written as bf16)
   uint8_t* out;            // gate/up: h (fp32 or e4m3); down: part [P][H] bf16
   unsigned* h_amax_out;    // gate/up with dynamic scale
+  int w_es = 0;            // without PC: 1 = one weight scale per expert (w_scale[e]), 0 = w_scale[0]
 };
 
 // DMA sources of one work item for one lane (see prefill_gemm_kernel).  At
@@ -391,7 +393,6 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
 
   // epilogue constants
   const float sa = MODE == 0 ? *a.a_scale : (HDYN ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.a_scale);
-  const float deq = sa * (*a.w_scale);  // one weight scale per tensor (!PC)
   const float rhs = (MODE == 0 && !HDYN) ? 1.0f / *a.h_scale : 1.0f;
   float hmax = 0.0f;
 
@@ -521,6 +522,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
     lds_u8* ep = smem + kPfRing + wave * kPfEpiWave;
     auto ep_at = [&](int t, int c) { return ep + t * 128 + ((c ^ (t & 7)) << 4); };
     const int rt = lane >> 3, rc = lane & 7;  // read-back: token rt + 8*rr, chunk rc
+    const float deq = PC ? 0.0f : sa * a.w_scale[(int64_t)cur.e * a.w_es];  // the expert's or tensor's scale
     if (MODE == 0) {
       const int fbase = cur.tile * (kPfRows / 2) + 32 * wave;
       // per-row dequantisation of features fbase+8g+rq.. (gate) and I+.. (up)

@@ -465,7 +465,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 6; }
+int32_t moe_abi_version(void) { return 7; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -534,7 +534,8 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
                                     uint8_t* ws, int32_t* ids, float* wts, const AlignOut& o, float* xamax_part,
                                     float* scale_slot, unsigned* h_amax, uint8_t* xq, uint8_t* h, float* part,
                                     bool hdyn, int S) {
-  const bool pc = a->weight_scale_per_channel == 1;
+  const bool pc = a->weight_scale_mode == 1;
+  const int es = a->weight_scale_mode == 2 ? 1 : 0;  // one weight scale per expert
   auto rec = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
   };
@@ -575,7 +576,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int T = I / (kPfRows / 2);  // 256-row tiles of W13: 128 gate + 128 up rows
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
-                  a->h_scale, h, h_amax};
+                  a->h_scale, h, h_amax, es};
     const int n = std::min(wgs, items);
     rc = pc ? (hdyn ? launch_prefill<0, true, true>(n, st, g) : launch_prefill<0, false, true>(n, st, g))
             : (hdyn ? launch_prefill<0, true, false>(n, st, g) : launch_prefill<0, false, false>(n, st, g));
@@ -593,7 +594,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int T = H / kPfRows;
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w2, hq, seg, H, I, k, (int)P, T, items, a->w2_scale, a->h_scale, h_amax, nullptr,
-                  (uint8_t*)part, nullptr};
+                  (uint8_t*)part, nullptr, es};
     const int n = std::min(wgs, items);
     rc = pc ? (hdyn ? launch_prefill<1, true, true>(n, st, g) : launch_prefill<1, false, true>(n, st, g))
             : (hdyn ? launch_prefill<1, true, false>(n, st, g) : launch_prefill<1, false, false>(n, st, g));
@@ -628,8 +629,9 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const int M = a->M, E = Er + S, H = a->H, I = a->I, k = kr + S;
   if (!fp8 && (a->w13_scale || a->w2_scale || a->x_scale || a->h_scale)) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_INVALID_ARG;
-  if (a->weight_scale_per_channel != 0 && (a->weight_scale_per_channel != 1 || !fp8)) return MOE_ERR_INVALID_ARG;
-  const bool pc = a->weight_scale_per_channel == 1;
+  if (a->weight_scale_mode != 0 && (a->weight_scale_mode < 0 || a->weight_scale_mode > 2 || !fp8))
+    return MOE_ERR_INVALID_ARG;
+  const bool pc = a->weight_scale_mode == 1;
   if (pc && (!aligned(a->w13_scale, 16) || !aligned(a->w2_scale, 16))) return MOE_ERR_INVALID_ARG;
   if (M == 0) {
     if (ev)
@@ -753,6 +755,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     Gemm1Args g{(const uint8_t*)a->w13, fp8 ? xq : (const uint8_t*)a->x, segs, H, I, k, a->w13_scale, scale_slot,
                 a->h_scale, h, h_amax};
     g.w_cs = pc ? 1 : 0;
+    g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
     const int tpw = 4 / plan.ks1;
     const dim3 grid((unsigned)(I / 16 / tpw), (unsigned)n_act, (unsigned)plan.passes1);
     bool ok;
@@ -778,6 +781,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     Gemm2Args g{(const uint8_t*)a->w2, h, segs, wts, H, I, k, plan.ks2, a->w2_scale, a->h_scale, h_amax, part,
                 (int)P};
     g.w_cs = pc ? 1 : 0;
+    g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
     const dim3 grid((unsigned)(H / (32 * (4 / plan.wks2))), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
     bool ok;
     if (plan.tw2 > 0) {

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 def capacity_formula(M, k, E, B):
@@ -133,9 +133,11 @@ def fused_args(**kw):
     (dict(w13_scale=FAKE), 1),           # a scale in bf16 mode
     (dict(dtype=1), 1),                  # fp8 without weight scales
     (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE + 1), 1),  # misaligned scale
-    (dict(weight_scale_per_channel=1), 1),                   # per-channel weight scales in bf16 mode
-    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_per_channel=2), 1),  # unknown scale mode
-    (dict(dtype=1, w13_scale=FAKE + 4, w2_scale=FAKE, weight_scale_per_channel=1), 1),  # rows need 16-byte alignment
+    (dict(weight_scale_mode=1), 1),                   # per-channel weight scales in bf16 mode
+    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_mode=3), 1),  # unknown scale mode
+    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_mode=-1), 1),  # unknown scale mode
+    (dict(weight_scale_mode=2), 1),                          # per-expert weight scales in bf16 mode
+    (dict(dtype=1, w13_scale=FAKE + 4, w2_scale=FAKE, weight_scale_mode=1), 1),  # rows need 16-byte alignment
     (dict(router_w=FAKE), 1),                                # both logits and router weights
     (dict(logits=None), 1),                                  # neither
     (dict(logits_out=FAKE), 1),                              # logits out without router weights

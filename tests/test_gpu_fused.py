@@ -20,7 +20,8 @@ import torch
 import moe_layer_align_amd as moe
 import oracle
 from gpu_common import DEV, TOL, compare, run_gpu, say
-from synth import CONFIGS, MoEConfig, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel, gen_x
+from synth import (CONFIGS, MoEConfig, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel,
+                   gen_weights_per_expert, gen_x)
 
 pytestmark = pytest.mark.gpu
 
@@ -408,3 +409,49 @@ def test_shared_expert_per_channel_with_router_weights():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     compare(cfg, M, seed=33, weights=(w13, w2, s13, s2), x=x, logits=lo.cpu(), n_shared=S)
+
+
+
+# ---------------------------------------------------------------- one weight scale per expert
+# Experts' scales up to 4x apart, so that a wrong expert's scale fails the
+# tolerance; both decode variants, the prefill path, and with shared experts.
+@pytest.mark.parametrize("variant", ["ksplit", "stream"])
+@pytest.mark.parametrize("xs,hs", [(None, None), (0.015, 0.004)])
+@pytest.mark.parametrize("M", [5, 40])
+def test_per_expert_small_layer(variant, xs, hs, M):
+    cfg = cfg_of("fp8", 16, 4, 512, 384)
+    w = gen_weights_per_expert(cfg, 41, device=DEV)
+    t = moe.Tuning(gemm1_stream_tiles=-1, gemm2_stream_tiles=-1) if variant == "ksplit" else \
+        moe.Tuning(gemm1_stream_tiles=2, gemm2_stream_tiles=2)
+    compare(cfg, M, seed=41, weights=w, x_scale=xs, h_scale=hs, tuning=t)
+
+
+@pytest.mark.parametrize("xs,hs", [(None, None), (0.012, 0.003)])
+def test_per_expert_prefill_path(xs, hs):
+    cfg = MoEConfig("pf_pe", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf")
+    w = gen_weights_per_expert(cfg, 42, device=DEV)
+    compare(cfg, 1100, seed=42, weights=w, tokens=[0, 1, 2, 3, 500, 777, 1098, 1099], x_scale=xs, h_scale=hs)
+
+
+def test_per_expert_equal_scales_match_per_tensor():
+    # per-expert scales all equal to the tensor's: the same bits as one scale
+    # per tensor, on the decode and on the prefill path
+    for cfg, M in ((cfg_of("fp8", 16, 4, 512, 384), 40),
+                   (MoEConfig("pf_pe", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf"), 1100)):
+        w13, w2, s13, s2 = gen_weights(cfg, 43, device=DEV)
+        x = gen_x(cfg.H, M, 43, sub=M).to(DEV)
+        lg = gen_logits(cfg, M, 43, sub=M).to(DEV)
+        a = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", torch.tensor([s13], device=DEV),
+                              torch.tensor([s2], device=DEV))
+        b = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", torch.full((cfg.E,), s13, device=DEV),
+                              torch.full((cfg.E,), s2, device=DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), cfg.name
+
+
+@pytest.mark.parametrize("M", [24, 1100])
+def test_per_expert_scales_with_shared_expert(M):
+    cfg = MoEConfig("pe_shared", E=16, k=7, H=512, I=512, dtype="fp8", ms=(M,), logits="zipf")
+    w = gen_weights_per_expert(cfg, 44, device=DEV, E=17)
+    toks = None if M <= 64 else [0, 1, 2, 500, 1099]
+    compare(cfg, M, seed=44, weights=w, tokens=toks, n_shared=1)
