@@ -55,14 +55,14 @@ FLUSH_BYTES = 1 << 30
 DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "62a62d77bce3fe6f8b4dec368dcaf03b9bb2b68f92ade3139c8add043047c99f",
-                "bytes_per_launch": 1510074290},
-    "qwen3": {"src_sha256": "62a62d77bce3fe6f8b4dec368dcaf03b9bb2b68f92ade3139c8add043047c99f",
-              "bytes_per_launch": 241755112},
-    "deepseek": {"src_sha256": "62a62d77bce3fe6f8b4dec368dcaf03b9bb2b68f92ade3139c8add043047c99f",
-                 "bytes_per_launch": 3292474268},
+    "mixtral": {"src_sha256": "ad7e9e2edeb1f13c73d6cb7b97e2731285f19d4fcd87be37127a938ea0ca37a0",
+                "bytes_per_launch": 1510150625},
+    "qwen3": {"src_sha256": "ad7e9e2edeb1f13c73d6cb7b97e2731285f19d4fcd87be37127a938ea0ca37a0",
+              "bytes_per_launch": 241755050},
+    "deepseek": {"src_sha256": "ad7e9e2edeb1f13c73d6cb7b97e2731285f19d4fcd87be37127a938ea0ca37a0",
+                 "bytes_per_launch": 3292560799},
     "prefill": {"src_sha256": "f621dc48fc397a5fb03f177e419476c47058ec661e022bb55320c5f0a2d23658",
-                "bytes_per_launch": 3025681692},
+                "bytes_per_launch": 3049336194},
 }
 
 
@@ -91,6 +91,10 @@ def main() -> int:
                          "weights [E,H] (inside the timed span) instead of taking the workload's logits")
     ap.add_argument("--per-channel", action="store_true",
                     help="fp8 workloads: one weight scale per weight row instead of one per tensor")
+    ap.add_argument("--per-expert", action="store_true",
+                    help="fp8 workloads: one weight scale per expert instead of one per tensor")
+    ap.add_argument("--shared", type=int, default=0, metavar="S",
+                    help="S shared experts (every token also passes through them, weight one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -104,7 +108,8 @@ def main() -> int:
 
     import torch
     import moe_layer_align_amd as moe
-    from synth import CONFIGS, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel, gen_x
+    from synth import (CONFIGS, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel,
+                       gen_weights_per_expert, gen_x)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -117,14 +122,20 @@ def main() -> int:
     fp8 = cfg.dtype == "fp8"
     esz = 1 if fp8 else 2
     log("generating %s weights on the GPU" % cfg.name)
-    if args.per_channel and not fp8:
-        print("--per-channel applies to fp8 workloads only", file=sys.stderr)
+    if (args.per_channel or args.per_expert) and not fp8:
+        print("--per-channel and --per-expert apply to fp8 workloads only", file=sys.stderr)
         return 2
-    if args.per_channel:
-        w13, w2, s13_t, s2_t = gen_weights_per_channel(cfg, 0, device=dev)
+    if args.per_channel and args.per_expert or args.shared < 0:
+        print("give at most one of --per-channel and --per-expert, and --shared >= 0", file=sys.stderr)
+        return 2
+    S = args.shared
+    ES, KS = cfg.E + S, cfg.k + S  # experts and slots per token with the shared experts
+    if args.per_channel or args.per_expert:
+        gen = gen_weights_per_channel if args.per_channel else gen_weights_per_expert
+        w13, w2, s13_t, s2_t = gen(cfg, 0, device=dev, E=ES)
         s13, s2 = s13_t, s2_t
     else:
-        w13, w2, s13, s2 = gen_weights(cfg, 0, device=dev)
+        w13, w2, s13, s2 = gen_weights(cfg, 0, device=dev, E=ES)
         s13_t = torch.tensor([s13], device=dev) if fp8 else None
         s2_t = torch.tensor([s2], device=dev) if fp8 else None
 
@@ -132,9 +143,9 @@ def main() -> int:
     for M in cfg.ms:
         x = gen_x(cfg.H, M, 0, sub=M).to(dev)
         lg = gen_logits(cfg, M, 0, sub=M).to(dev)
-        ws = torch.empty(moe.workspace_size(M, cfg.E, cfg.H, cfg.I, cfg.k, cfg.dtype), dtype=torch.uint8, device=dev)
+        ws = torch.empty(moe.workspace_size(M, ES, cfg.H, cfg.I, KS, cfg.dtype), dtype=torch.uint8, device=dev)
         y = torch.empty(M, cfg.H, dtype=torch.bfloat16, device=dev)
-        counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+        counts = torch.empty(ES, dtype=torch.int32, device=dev)
         calls.append(dict(M=M, x=x, lg=lg, ws=ws, y=y, counts=counts))
 
     stream = torch.cuda.current_stream()
@@ -145,7 +156,7 @@ def main() -> int:
     def run(c, events=None):
         moe.fused_forward(c["x"], None if args.router_gemm else c["lg"], w13, w2, cfg.k, cfg.dtype, s13_t, s2_t,
                           out=c["y"], workspace=c["ws"], expert_counts=c["counts"], stream=stream, events=events,
-                          router_w=router_w)
+                          router_w=router_w, n_shared=S)
 
     def flush(i):
         if flush_buf is not None:
@@ -160,8 +171,8 @@ def main() -> int:
         c["active"] = int((cnt > 0).sum())
         c["w_bytes"] = c["active"] * 3 * cfg.H * cfg.I * esz
         c["g1_bytes"] = c["active"] * 2 * cfg.H * cfg.I * esz
-        c["flops"] = 6.0 * c["M"] * cfg.k * cfg.H * cfg.I
-        c["g1_flops"] = 4.0 * c["M"] * cfg.k * cfg.H * cfg.I
+        c["flops"] = 6.0 * c["M"] * KS * cfg.H * cfg.I
+        c["g1_flops"] = 4.0 * c["M"] * KS * cfg.H * cfg.I
 
     log("warmup %d steps" % args.warmup)
     for s in range(args.warmup):
@@ -251,7 +262,8 @@ def main() -> int:
     # the counters were taken on the default inputs (cold cache, given logits,
     # per-tensor scales) of these kernel sources
     roof["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256(sources)
-                                                 and not (args.no_flush or args.per_channel or args.router_gemm)) \
+                                                 and not (args.no_flush or args.per_channel or args.per_expert
+                                                          or args.shared or args.router_gemm)) \
         else None
     roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
     roof["kernel"] = ("prefill_gemm_kernel<0, *> (tiled gate/up product + SiLU*up)" if cfg.name == "prefill"
@@ -262,7 +274,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline and not args.router_gemm:  # the oracle sample takes the workload's logits
-        cpu = cpu_baseline(cfg, calls, (w13, w2, s13, s2), args.cpu_seconds, unit)
+        cpu = cpu_baseline(cfg, calls, (w13, w2, s13, s2), args.cpu_seconds, unit, n_shared=S)
 
     ms_str = ",".join(str(m) for m in cfg.ms)
     line = {
@@ -281,10 +293,12 @@ def main() -> int:
         "dtype": "f8e4m3" if fp8 else "bf16",
         "data": "synthetic: seeded N(0,1) hidden states, N(0,1/fan_in) expert weights, router logits per workload",
         "config": {
-            "workload": "%s-shaped %s layer E=%d top-%d H=%d I=%d, M in {%s}" % (cfg.name, cfg.dtype, cfg.E, cfg.k,
-                                                                               cfg.H, cfg.I, ms_str),
+            "workload": "%s-shaped %s layer E=%d top-%d H=%d I=%d%s, M in {%s}" % (
+                cfg.name, cfg.dtype, cfg.E, cfg.k, cfg.H, cfg.I, " +%d shared" % S if S else "", ms_str),
             "E": cfg.E, "top_k": cfg.k, "H": cfg.H, "I": cfg.I, "M_sweep": list(cfg.ms), "router_logits": cfg.logits,
-            "weight_scales": ("per channel" if args.per_channel else "per tensor") if fp8 else None,
+            "weight_scales": ("per channel" if args.per_channel else "per expert" if args.per_expert
+                              else "per tensor") if fp8 else None,
+            "shared_experts": S,
             "logits_source": "computed in the layer from router weights" if args.router_gemm else "given",
         },
         "per_m": per_m,
@@ -318,7 +332,7 @@ def calibrate_copy(mib: int) -> int:
     return 0
 
 
-def cpu_baseline(cfg, calls, weights, budget_s, unit, min_s=10.0):
+def cpu_baseline(cfg, calls, weights, budget_s, unit, min_s=10.0, n_shared=0):
     """The CPU oracle on the same inputs, timed on a bounded sample.
 
     The oracle evaluates every (token, expert) pair with dense loops, so its
@@ -331,6 +345,7 @@ def cpu_baseline(cfg, calls, weights, budget_s, unit, min_s=10.0):
     import oracle
 
     w13, w2, s13, s2 = weights
+    kk = cfg.k + n_shared  # pairs per token
     log("cpu baseline: copying weights to the host")
     w13h, w2h = w13.cpu(), w2.cpu()
     work_sum, secs_sum, spent, parts, rounds = 0.0, 0.0, 0.0, [], 0
@@ -342,21 +357,21 @@ def cpu_baseline(cfg, calls, weights, budget_s, unit, min_s=10.0):
             M = c["M"]
             # the budget left is shared by the points of this pass not yet run
             left = budget_s / len(calls) if sec_per_pair is None else (budget_s - spent) / (len(ordered) - idx)
-            n_tok = M if sec_per_pair is None else int(max(1, min(M, left / (sec_per_pair * cfg.k))))
-            if sec_per_pair is None and M * cfg.k > 256:
-                n_tok = max(1, 256 // cfg.k)  # probe the rate first
+            n_tok = M if sec_per_pair is None else int(max(1, min(M, left / (sec_per_pair * kk))))
+            if sec_per_pair is None and M * kk > 256:
+                n_tok = max(1, 256 // kk)  # probe the rate first
             toks = sorted({int(round(i * (M - 1) / max(n_tok - 1, 1))) for i in range(n_tok)}) if n_tok < M else None
             log("cpu baseline: oracle at M=%d on %s tokens" % (M, M if toks is None else len(toks)))
             x, lg = c["x"].cpu(), c["lg"].cpu()
             t0 = time.perf_counter()
             oracle.layer(x, lg, w13h, w2h, cfg.k, cfg.dtype, s13, s2, tokens=toks,
-                         all_pairs_h=False if toks is not None else None)
+                         all_pairs_h=False if toks is not None else None, n_shared=n_shared)
             dt = time.perf_counter() - t0
             spent += dt
-            n_pairs = (M if toks is None else len(toks)) * cfg.k
+            n_pairs = (M if toks is None else len(toks)) * kk
             sec_per_pair = dt / n_pairs
             work_sum += c["w_bytes"] if unit == "GB/s" else c["flops"]
-            secs_sum += sec_per_pair * M * cfg.k
+            secs_sum += sec_per_pair * M * kk
             if rounds == 1:
                 parts.append("M=%d:%s" % (M, "all" if toks is None else "%d/%d tokens" % (len(toks), M)))
             if spent > budget_s:

@@ -149,6 +149,10 @@ typedef struct {
                                  (1..16), < 0 K-split variant */
   int32_t gemm2_stream_tiles; /* down: > 0 long-stream variant with this many row tiles per wave (1..16),
                                  < 0 K-split variant */
+  int32_t reverse_order;     /* both products: 1 = take the grid's expert and token-pass indices in reverse
+                                (the last experts' and late passes' workgroups first), -1 = in order;
+                                default: reversed with shared experts, which then also take the K-split
+                                variants unless the stream fields say otherwise */
 } moe_tuning_t;
 
 /*

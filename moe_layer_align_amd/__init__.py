@@ -38,7 +38,7 @@ class Tuning(ctypes.Structure):
     _fields_ = [("gemm1_ksplit", ctypes.c_int32), ("gemm2_ksplit", ctypes.c_int32),
                 ("token_tiles", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("gemm2_wave_ksplit", ctypes.c_int32), ("gemm1_stream_tiles", ctypes.c_int32),
-                ("gemm2_stream_tiles", ctypes.c_int32)]
+                ("gemm2_stream_tiles", ctypes.c_int32), ("reverse_order", ctypes.c_int32)]
 
 
 class _FusedArgs(ctypes.Structure):
@@ -58,7 +58,7 @@ class _FusedArgs(ctypes.Structure):
 
 
 _lib = None
-_ABI = 7  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
+_ABI = 8  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():

@@ -36,7 +36,16 @@ struct Segments {
   const int32_t* counts;
   const int32_t* active;
   const int32_t* num_active;
+  // 1: the products take their grid's y (active expert) and z (token pass)
+  // indices in reverse, so that the workgroups of the last experts and of the
+  // late token passes are dispatched first.  Set when a few experts hold many
+  // more tokens than the rest (shared experts take every token): their long
+  // workgroups then start first instead of running alone at the end.
+  int rev;
 };
+
+__device__ __forceinline__ int grid_y(const Segments& g) { return g.rev ? gridDim.y - 1 - blockIdx.y : blockIdx.y; }
+__device__ __forceinline__ int grid_z(const Segments& g) { return g.rev ? gridDim.z - 1 - blockIdx.z : blockIdx.z; }
 
 // One MFMA step's operand fragment for one 16-row (or 16-token) tile.
 template <bool FP8>
@@ -273,11 +282,11 @@ template <bool FP8, int HFMT, int NT, int U, int KSPLIT>
 __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
   constexpr int TPW = 4 / KSPLIT;
   __shared__ f32x4 s_red[KSPLIT > 1 ? (KSPLIT - 1) * TPW * 2 * NT * 64 : 1];
-  const int s = blockIdx.y;
+  const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
   const int e = a.seg.active[s];
   const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
-  const int pass0 = blockIdx.z * NT * 16;
+  const int pass0 = grid_z(a.seg) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
   auto run = [&](auto pc_tag) {
@@ -444,11 +453,11 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
 // Grid: x = chunks of 4*tw feature tiles, y = active expert, z = token pass.
 template <bool FP8, int HFMT, int NT, int U>
 __global__ __launch_bounds__(256) void gemm1_stream_kernel(Gemm1Args a, int tw) {
-  const int s = blockIdx.y;
+  const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
   const int e = a.seg.active[s];
   const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
-  const int pass0 = blockIdx.z * NT * 16;
+  const int pass0 = grid_z(a.seg) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
   auto run = [&](auto pc_tag) {
@@ -625,12 +634,12 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   extern __shared__ __align__(16) uint8_t s_tok[];
   constexpr int TPW = 4 / WKS;
   __shared__ f32x4 s_red[WKS > 1 ? (WKS - 1) * TPW * 2 * NT * 64 : 1];
-  const int s = blockIdx.y;
+  const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
   const int e = a.seg.active[s];
   const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
-  const int kslice = blockIdx.z % a.ksplit;
-  const int pass0 = (blockIdx.z / a.ksplit) * NT * 16;
+  const int z = grid_z(a.seg), kslice = z % a.ksplit;
+  const int pass0 = (z / a.ksplit) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
   auto run = [&](auto pc_tag) {
@@ -732,12 +741,12 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
 template <bool FP8, int HFMT, int NT, int U>
 __global__ __launch_bounds__(256) void gemm2_stream_kernel(Gemm2Args a, int tw) {
   extern __shared__ __align__(16) uint8_t s_tok[];
-  const int s = blockIdx.y;
+  const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
   const int e = a.seg.active[s];
   const int seg = a.seg.offsets[e], cnt = a.seg.counts[e];
-  const int kslice = blockIdx.z % a.ksplit;
-  const int pass0 = (blockIdx.z / a.ksplit) * NT * 16;
+  const int z = grid_z(a.seg), kslice = z % a.ksplit;
+  const int pass0 = (z / a.ksplit) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
   auto run = [&](auto pc_tag) {

@@ -131,12 +131,14 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
 struct Plan {
   int nt1, passes1, u1, ks1, tw1;          // gate/up (tw1 > 0: long-stream variant)
   int nt2, passes2, u2, ks2, wks2, lds2, tw2;  // down (tw2 > 0: long-stream variant)
+  int rev;                                  // reversed grid order (Segments::rev)
 };
 
 bool valid_u(bool fp8, int u) { return fp8 ? (u == 1 || u == 2) : (u == 2 || u == 4); }
 bool valid_wsplit(int ks) { return ks == 1 || ks == 2 || ks == 4; }
 
-moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, const moe_tuning_t* t, Plan* p) {
+moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool qh, const moe_tuning_t* t,
+                       Plan* p) {
   const int kstep = fp8 ? 128 : 32;
   const int64_t P = (int64_t)M * k;
   const int n_act = (int)std::min<int64_t>(E, P);  // upper bound on experts with tokens
@@ -165,6 +167,15 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, bool fp8, bool qh, con
     p->u1 = p->u2 = 4;
     p->ks1 = 4;
     p->wks2 = 4;
+  }
+  // Shared experts (S > 0) hold every token, the routed ones a few each: the
+  // K-split variants' many short workgroups absorb the shared experts' long
+  // ones, which the reversed grid order starts first.
+  p->rev = S > 0 ? 1 : 0;
+  if (S > 0) p->tw1 = p->tw2 = 0;
+  if (t && t->reverse_order != 0) {
+    if (t->reverse_order != 1 && t->reverse_order != -1) return MOE_ERR_UNSUPPORTED;
+    p->rev = t->reverse_order > 0 ? 1 : 0;
   }
   if (t && t->token_tiles > 0) {
     if (t->token_tiles > 4) return MOE_ERR_UNSUPPORTED;
@@ -465,7 +476,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 7; }
+int32_t moe_abi_version(void) { return 8; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -656,7 +667,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const bool prefill = use_prefill(M, k, a->dtype, a->H, a->I);
   Plan plan{};
   if (!prefill) {
-    rc = make_plan(M, E, H, I, k, fp8, hdyn, a->tuning, &plan);
+    rc = make_plan(M, E, H, I, k, S, fp8, hdyn, a->tuning, &plan);
     if (rc != MOE_OK) return rc;
   }
 
@@ -746,7 +757,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     if ((rc = launch_status()) != MOE_OK) return rc;
   }
 
-  const Segments segs{sorted, offsets, counts, active, num_active};
+  const Segments segs{sorted, offsets, counts, active, num_active, plan.rev};
   const int hf = !fp8 ? H_BF16 : (hdyn ? H_F32 : H_E4M3);
 
   // 3. gate/up product + SiLU(gate)*up

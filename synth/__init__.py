@@ -155,7 +155,7 @@ def gen_router_weights(E: int, H: int, seed: int = 0, device="cpu") -> torch.Ten
     return w.to(torch.bfloat16).contiguous()
 
 
-def gen_weights_per_channel(cfg: MoEConfig, seed: int = 0, device="cpu"):
+def gen_weights_per_channel(cfg: MoEConfig, seed: int = 0, device="cpu", E: Optional[int] = None):
     """fp8 expert weights with one scale per weight row (output channel).
 
     The same normal draws as gen_weights; row n of W13[e] and of W2[e] is
@@ -165,7 +165,8 @@ def gen_weights_per_channel(cfg: MoEConfig, seed: int = 0, device="cpu"):
     """
     if cfg.dtype != "fp8":
         raise ValueError("per-channel scales are for fp8 layers")
-    E, H, I = cfg.E, cfg.H, cfg.I
+    E = cfg.E if E is None else E
+    H, I = cfg.H, cfg.I
     s13_std, s2_std = 1.0 / math.sqrt(H), 1.0 / math.sqrt(I)
     w13 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
     w2 = torch.empty(E, H, I, dtype=torch.uint8, device=device)

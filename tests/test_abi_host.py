@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 def capacity_formula(M, k, E, B):
@@ -164,7 +164,7 @@ def test_router_logits_validation(lib):
 def test_fused_tuning_validation(lib):
     import moe_layer_align_amd as m
     for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17),
-              m.Tuning(gemm2_wave_ksplit=3)):
+              m.Tuning(gemm2_wave_ksplit=3), m.Tuning(reverse_order=2)):
         args = fused_args(tuning=ctypes.pointer(t))
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 

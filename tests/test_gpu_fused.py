@@ -455,3 +455,26 @@ def test_per_expert_scales_with_shared_expert(M):
     w = gen_weights_per_expert(cfg, 44, device=DEV, E=17)
     toks = None if M <= 64 else [0, 1, 2, 500, 1099]
     compare(cfg, M, seed=44, weights=w, tokens=toks, n_shared=1)
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_reverse_grid_order_is_bitwise_neutral(S):
+    # the workgroup order of the products does not enter the arithmetic: the
+    # reversed and the in-order grid give the same bits, in both variants
+    cfg = CONFIGS["qwen3"]
+    M = 40
+    w13, w2, s13, s2 = gen_weights(cfg, 45, device=DEV, E=cfg.E + S)
+    x = gen_x(cfg.H, M, 45, sub=M).to(DEV)
+    lg = gen_logits(cfg, M, 45, sub=M).to(DEV)
+    t13, t2 = torch.tensor([s13], device=DEV), torch.tensor([s2], device=DEV)
+    for st in (-1, 2):
+        ys = [moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", t13, t2, n_shared=S,
+                                tuning=moe.Tuning(reverse_order=r, gemm1_stream_tiles=st, gemm2_stream_tiles=st))
+              for r in (1, -1)]
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0], ys[1]), st
+
+
+def test_shared_expert_stream_variants():
+    t = moe.Tuning(gemm1_stream_tiles=2, gemm2_stream_tiles=2)
+    compare(CONFIGS["qwen3"], 40, seed=46, n_shared=1, tuning=t)
