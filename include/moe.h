@@ -43,15 +43,26 @@
 extern "C" {
 #endif
 
+/* The *_RANGE_ enumerators are not values of their type: they give each
+ * enumeration the range of int32_t, so that any int a C caller passes is a
+ * valid value of the type on the C++ side (the library rejects unknown ones
+ * with MOE_ERR_INVALID_ARG). */
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,
   MOE_ERR_UNSUPPORTED = 2,
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,
-  MOE_ERR_DEVICE = 4
+  MOE_ERR_DEVICE = 4,
+  MOE_STATUS_RANGE_LO_ = -2147483647 - 1,
+  MOE_STATUS_RANGE_HI_ = 2147483647
 } moe_status_t;
 
-typedef enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3 = 1 } moe_dtype_t;
+typedef enum {
+  MOE_DTYPE_BF16 = 0,
+  MOE_DTYPE_FP8_E4M3 = 1,
+  MOE_DTYPE_RANGE_LO_ = -2147483647 - 1,
+  MOE_DTYPE_RANGE_HI_ = 2147483647
+} moe_dtype_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status_t status);
@@ -219,10 +230,44 @@ typedef struct {
   float* logits_out;       /* optional out [M,E]: the logits computed from router_w (NULL = kept in the
                               workspace); must be NULL when logits is given */
   int32_t n_shared;        /* S >= 0 shared experts after the E routed ones (see above); < 0: INVALID_ARG */
+  /* Optional outputs of the call's sort-and-pad step (NULL = kept in the
+   * workspace), in moe_align's layout for the block and capacity that
+   * moe_fused_align_shape reports for the call (E and top_k counting the
+   * shared experts): expert_offsets [E+S+1], sorted_ids [capacity] (entries
+   * at or beyond *num_padded unspecified), block_expert [capacity/block],
+   * num_padded [1].  The layer reads them back, so they must not alias any
+   * other argument. */
+  int32_t* expert_offsets;
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* num_padded;
+  /* 1 = deterministic mode: a token's outputs (routing, weights and y) are
+   * the same bits whatever the batch it is in and its position there, on
+   * every call and in every process (the pages report a serving process and
+   * a separate rescoring process agreeing to the bit once the kernel
+   * configurations were pinned: "Fused MoE on Hopper, ...", TL;DR and key
+   * points).  The order of every sum is then fixed by the shape alone:
+   * the decode products run at every M (no switch to the prefill products),
+   * with the gate/up K split over a fixed number of waves and the down
+   * product in one K slice.  fp8 layers need static activation scales
+   * (x_scale and h_scale non-NULL; a dynamic scale is an amax over the
+   * batch), else MOE_ERR_INVALID_ARG; so do tunings that set a K split or a
+   * long-stream variant whose sum order differs.  0 = default. */
+  int32_t deterministic;
 } moe_fused_args_t;
 
-/* Host-only: workspace bytes needed by moe_fused_forward for these sizes. */
+/* Host-only: workspace bytes needed by moe_fused_forward for these sizes (in
+ * either mode). */
 size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype);
+
+/* Host-only: block size and sorted_ids capacity of the sort-and-pad step of
+ * moe_fused_forward for these sizes and mode (E and top_k counting shared
+ * experts, as for moe_fused_workspace_size): block 128 on the prefill path
+ * (fp8, M*top_k >= 8192, default mode), else 16; capacity as
+ * moe_align_capacity.  Errors as moe_fused_forward's shape checks, and
+ * MOE_ERR_INVALID_ARG for NULL outputs. */
+moe_status_t moe_fused_align_shape(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype,
+                                   int32_t deterministic, int32_t* block, int64_t* capacity);
 
 moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream);
 

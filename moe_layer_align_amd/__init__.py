@@ -15,8 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "MoEError", "load", "LIB_PATH", "route_topk", "align_capacity", "align", "quant_e4m3",
-    "workspace_size", "fused_forward", "Tuning", "STATUS", "NUM_STAGES", "STAGE_NAMES",
+    "MoEError", "load", "LIB_PATH", "route_topk", "router_logits", "align_capacity", "align", "quant_e4m3",
+    "workspace_size", "fused_align_shape", "fused_forward", "Tuning", "STATUS", "NUM_STAGES", "STAGE_NAMES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -54,11 +54,14 @@ class _FusedArgs(ctypes.Structure):
         ("weight_scale_mode", ctypes.c_int32),
         ("router_w", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
         ("n_shared", ctypes.c_int32),
+        ("expert_offsets", ctypes.c_void_p), ("sorted_ids", ctypes.c_void_p), ("block_expert", ctypes.c_void_p),
+        ("num_padded", ctypes.c_void_p),
+        ("deterministic", ctypes.c_int32),
     ]
 
 
 _lib = None
-_ABI = 8  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
+_ABI = 9  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():
@@ -85,6 +88,8 @@ def load():
     lib.moe_quant_e4m3.argtypes = [vp, i64, vp, vp, vp]
     lib.moe_fused_workspace_size.restype = sz
     lib.moe_fused_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.moe_fused_align_shape.restype = ctypes.c_int
+    lib.moe_fused_align_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, i32, vp, vp]
     lib.moe_fused_forward.restype = ctypes.c_int
     lib.moe_fused_forward.argtypes = [ctypes.POINTER(_FusedArgs), vp]
     lib.moe_fused_forward_profiled.restype = ctypes.c_int
@@ -128,12 +133,7 @@ def route_topk(logits: torch.Tensor, top_k: int, ids: Optional[torch.Tensor] = N
                weights: Optional[torch.Tensor] = None, stream=None):
     """Top-k experts per token and their softmax weights (moe_route_topk)."""
     M, E = logits.shape
-    if logits is not None:
-        _need(logits, "logits", torch.float32, (M, E))
-    else:
-        _need(router_w, "router_w", torch.bfloat16, (E, H))
-        if logits_out is not None:
-            _need(logits_out, "logits_out", torch.float32, (M, E))
+    _need(logits, "logits", torch.float32, (M, E))
     if ids is None:
         ids = torch.empty(M, top_k, dtype=torch.int32, device=logits.device)
     if weights is None:
@@ -195,6 +195,16 @@ def workspace_size(M: int, E: int, H: int, I: int, top_k: int, dtype: str) -> in
     return int(load().moe_fused_workspace_size(M, E, H, I, top_k, DTYPE_FP8 if dtype == "fp8" else DTYPE_BF16))
 
 
+def fused_align_shape(M: int, E: int, H: int, I: int, top_k: int, dtype: str, deterministic: bool = False):
+    """(block, capacity) of the fused call's sort-and-pad step
+    (moe_fused_align_shape); E and top_k count the shared experts."""
+    b, c = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check("moe_fused_align_shape", load().moe_fused_align_shape(
+        M, E, H, I, top_k, DTYPE_FP8 if dtype == "fp8" else DTYPE_BF16, int(bool(deterministic)),
+        ctypes.byref(b), ctypes.byref(c)))
+    return int(b.value), int(c.value)
+
+
 def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Tensor, w2: torch.Tensor, top_k: int,
                   dtype: str = "bf16", w13_scale: Optional[torch.Tensor] = None,
                   w2_scale: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None,
@@ -203,7 +213,8 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
                   topk_weights: Optional[torch.Tensor] = None, expert_counts: Optional[torch.Tensor] = None,
                   scales_out: Optional[torch.Tensor] = None, tuning: Optional[Tuning] = None, stream=None,
                   events=None, router_w: Optional[torch.Tensor] = None,
-                  logits_out: Optional[torch.Tensor] = None, n_shared: int = 0) -> torch.Tensor:
+                  logits_out: Optional[torch.Tensor] = None, n_shared: int = 0,
+                  align_out: Optional[dict] = None, deterministic: bool = False) -> torch.Tensor:
     """The fused layer (moe_fused_forward).
 
     x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
@@ -217,6 +228,11 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
     weight one; topk_ids/topk_weights are then [M,top_k+S], expert_counts [E+S].
     events: optional list of 2*NUM_STAGES hipEvent_t handles (ints) recorded
     around the stages on the stream.
+    align_out: optional dict of int32 GPU tensors receiving the call's
+    sort-and-pad outputs: "offsets" [E+S+1], "sorted_ids" [capacity],
+    "block_expert" [capacity/block], "num_padded" [1] (block and capacity
+    from fused_align_shape; any subset of the keys).
+    deterministic: batch-invariant mode (fp8 needs x_scale and h_scale).
     """
     M, H = x.shape
     if (logits is None) == (router_w is None):
@@ -262,6 +278,16 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         _need(expert_counts, "expert_counts", torch.int32, (ES,))
     if scales_out is not None:
         _need(scales_out, "scales_out", torch.float32, (2,))
+    al = dict(align_out or {})
+    if set(al) - {"offsets", "sorted_ids", "block_expert", "num_padded"}:
+        raise ValueError("unknown align_out keys: %s" % sorted(set(al) - {"offsets", "sorted_ids", "block_expert",
+                                                                            "num_padded"}))
+    if al:
+        blk, cap = fused_align_shape(M, ES, H, I, KS, dtype, deterministic)
+        for key, shape in (("offsets", (ES + 1,)), ("sorted_ids", (cap,)), ("block_expert", (cap // blk,)),
+                           ("num_padded", (1,))):
+            if key in al:
+                _need(al[key], "align_out[%s]" % key, torch.int32, shape)
     lib = load()
     need = int(lib.moe_fused_workspace_size(M, ES, H, I, KS, DTYPE_FP8 if fp8 else DTYPE_BF16))
     if workspace is None:
@@ -278,6 +304,9 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         tuning=ctypes.pointer(tuning) if tuning is not None else None,
         weight_scale_mode=mode,
         router_w=_ptr(router_w), logits_out=_ptr(logits_out), n_shared=S,
+        expert_offsets=_ptr(al.get("offsets")), sorted_ids=_ptr(al.get("sorted_ids")),
+        block_expert=_ptr(al.get("block_expert")), num_padded=_ptr(al.get("num_padded")),
+        deterministic=int(bool(deterministic)),
     )
     if events is None:
         _check("moe_fused_forward", lib.moe_fused_forward(ctypes.byref(args), _stream(stream)))

@@ -1,18 +1,23 @@
 """Ahead-of-time build of the gfx950 HIP library (libmoe_mi355x.so).
 
-Compiles moe_layer_align_amd/csrc/moe_api.hip with hipcc for gfx950 into the
-package directory.  Packed-fp32 instructions are disabled (the compiler may
-otherwise fuse fp32 pairs into v_pk_* forms).
+Compiles the translation units under moe_layer_align_amd/csrc with hipcc for
+gfx950, in parallel, and links them into the package directory.  Every unit
+carries its own code object (no relocatable device code).  Packed-fp32
+instructions are disabled (the compiler may otherwise fuse fp32 pairs into
+v_pk_* forms).
 """
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "moe_api.hip")
+CSRC = os.path.join(PKG, "csrc")
+UNITS = ["moe_api.hip", "launch_decode_bf16.hip", "launch_decode_fp8.hip", "launch_decode_fp8_static.hip",
+         "launch_prefill.hip"]
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -21,7 +26,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-munsafe-fp-atomics",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -29,18 +33,41 @@ FLAGS = [
 ]
 
 
+def _clean(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l)
+
+
 def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"), SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        sys.stderr.write(err + "\n")
-        raise RuntimeError("hipcc failed (%d)" % res.returncode)
-    if verbose and err.strip():
-        sys.stderr.write(err + "\n")
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpdir:
+        procs = []
+        for unit in UNITS:
+            obj = os.path.join(tmpdir, unit.replace(".hip", ".o"))
+            cmd = [HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, unit), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((unit, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                      text=True)))
+        objs, failed = [], []
+        for unit, obj, p in procs:
+            _, err = p.communicate()
+            err = _clean(err)
+            if p.returncode != 0:
+                failed.append(unit)
+                sys.stderr.write(err + "\n")
+            elif verbose and err.strip():
+                sys.stderr.write(err + "\n")
+            objs.append(obj)
+        if failed:
+            raise RuntimeError("hipcc failed on %s" % ", ".join(failed))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(_clean(res.stderr) + "\n")
+            raise RuntimeError("hipcc link failed (%d)" % res.returncode)
     os.replace(tmp, LIB)
     return LIB
 

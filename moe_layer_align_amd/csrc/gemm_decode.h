@@ -279,7 +279,7 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
 }
 
 template <bool FP8, int HFMT, int NT, int U, int KSPLIT>
-__global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
+static __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
   constexpr int TPW = 4 / KSPLIT;
   __shared__ f32x4 s_red[KSPLIT > 1 ? (KSPLIT - 1) * TPW * 2 * NT * 64 : 1];
   const int s = grid_y(a.seg);
@@ -452,7 +452,7 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
 
 // Grid: x = chunks of 4*tw feature tiles, y = active expert, z = token pass.
 template <bool FP8, int HFMT, int NT, int U>
-__global__ __launch_bounds__(256) void gemm1_stream_kernel(Gemm1Args a, int tw) {
+static __global__ __launch_bounds__(256) void gemm1_stream_kernel(Gemm1Args a, int tw) {
   const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
   const int e = a.seg.active[s];
@@ -630,7 +630,7 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
 // Grid: x = groups of 32*(4/WKS) output rows, y = active expert, z = K slice
 // + ksplit * token pass.
 template <bool FP8, int HFMT, int NT, int U, int WKS>
-__global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
+static __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   extern __shared__ __align__(16) uint8_t s_tok[];
   constexpr int TPW = 4 / WKS;
   __shared__ f32x4 s_red[WKS > 1 ? (WKS - 1) * TPW * 2 * NT * 64 : 1];
@@ -739,7 +739,7 @@ __device__ __forceinline__ void gemm2_stream_body(const Gemm2Args& a, uint8_t* s
 // Grid: x = chunks of 4*tw row tiles, y = active expert, z = K slice +
 // ksplit * token pass.
 template <bool FP8, int HFMT, int NT, int U>
-__global__ __launch_bounds__(256) void gemm2_stream_kernel(Gemm2Args a, int tw) {
+static __global__ __launch_bounds__(256) void gemm2_stream_kernel(Gemm2Args a, int tw) {
   extern __shared__ __align__(16) uint8_t s_tok[];
   const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
@@ -779,7 +779,7 @@ __host__ __device__ constexpr int gemm2_red_bytes(int nt, int wks) {
 // per lane with a quarter of the workgroups; every output is the same sum.
 // Also reports the fp8 scales in effect.
 template <int G>
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, const float* __restrict__ topk_w,
+static __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, const float* __restrict__ topk_w,
                                                        uint16_t* __restrict__ y, int M, int H, int top_k, int log2kp,
                                                        int ksplit, const float* x_scale, const unsigned* h_amax,
                                                        const float* h_scale, float* scales_out) {
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
 }
 
 // Stand-alone per-tensor e4m3 quantisation of fp32 data with a given scale.
-__global__ __launch_bounds__(256) void quant_f32_kernel(const float* __restrict__ in, int64_t n,
+static __global__ __launch_bounds__(256) void quant_f32_kernel(const float* __restrict__ in, int64_t n,
                                                         const float* __restrict__ scale, uint8_t* __restrict__ out) {
   const float r = 1.0f / *scale;
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;

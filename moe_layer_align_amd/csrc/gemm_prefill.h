@@ -291,7 +291,7 @@ __device__ __forceinline__ void pf_interleave() {
 // issued after those of step s+1.  Any other vector-memory operation (token
 // ids, epilogue stores) only makes that wait stricter.
 template <int MODE, bool HDYN, bool PC>
-__global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
+static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
   const int nb = *a.seg.num_padded / kPfTok;
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a)
 }
 
 // h (fp32, [P][I]) -> e4m3 with the dynamic scale amax/448; 16 per thread.
-__global__ __launch_bounds__(256) void prefill_quant_h_kernel(const float* __restrict__ h, int64_t n,
+static __global__ __launch_bounds__(256) void prefill_quant_h_kernel(const float* __restrict__ h, int64_t n,
                                                               const unsigned* __restrict__ h_amax,
                                                               uint8_t* __restrict__ hq) {
   const float r = 1.0f / scale_from_amax(__uint_as_float(*h_amax));
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(256) void prefill_quant_h_kernel(const float* __res
 
 // y[m,n] = bf16( sum_j w[m*k+j] * part[m*k+j][n] ), j ascending, fp32 sum;
 // 8 outputs per thread.
-__global__ __launch_bounds__(256) void prefill_finalize_kernel(const uint16_t* __restrict__ part,
+static __global__ __launch_bounds__(256) void prefill_finalize_kernel(const uint16_t* __restrict__ part,
                                                                const float* __restrict__ topk_w,
                                                                uint16_t* __restrict__ y, int M, int H, int top_k,
                                                                const float* x_scale, const unsigned* h_amax,

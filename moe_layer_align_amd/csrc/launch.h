@@ -1,0 +1,40 @@
+// Host launchers of the expert products, one translation unit per family of
+// kernel instantiations (so that the library's kernels compile in parallel):
+//   launch_decode_bf16.hip, launch_decode_fp8.hip  decode products
+//   launch_prefill.hip                              prefill products
+// Each launcher picks the template instance for the run-time variant and
+// enqueues it on the stream; it returns false when the variant is not built.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_decode.h"
+#include "gemm_prefill.h"
+
+namespace moe {
+
+// Launch shape of the two decode products (see make_plan in moe_api.hip).
+struct DecodeShape {
+  int nt, u;  // 16-token tiles per pass; MFMA k-steps per pipeline stage
+  int ks;     // gate/up: waves splitting K; down: waves splitting a K slice
+  int tw;     // > 0: long-stream variant with tw tiles per wave
+  dim3 grid;  // grid of the chosen variant
+  size_t lds; // dynamic LDS (down product, dynamic fp8 h scale)
+};
+
+bool launch_gemm1_bf16(const DecodeShape& s, hipStream_t st, const Gemm1Args& a);
+bool launch_gemm2_bf16(const DecodeShape& s, hipStream_t st, const Gemm2Args& a);
+// hf: H_F32 (dynamic h scale) or H_E4M3 (static)
+bool launch_gemm1_fp8(int hf, const DecodeShape& s, hipStream_t st, const Gemm1Args& a);
+bool launch_gemm2_fp8(int hf, const DecodeShape& s, hipStream_t st, const Gemm2Args& a);
+
+// Persistent prefill product: mode 0 gate/up, 1 down; hdyn: dynamic h
+// scale; pc: one weight scale per row.  The kernel's dynamic LDS ceiling is
+// raised once per kernel and device; false when that fails.
+bool launch_prefill_gemm(int mode, bool hdyn, bool pc, int wgs, hipStream_t st, const PrefillArgs& g);
+void launch_prefill_quant_h(const float* h, int64_t n, const unsigned* h_amax, uint8_t* hq, hipStream_t st);
+void launch_prefill_finalize(const uint16_t* part, const float* wts, uint16_t* y, int M, int H, int k,
+                             const float* x_scale, const unsigned* h_amax, const float* h_scale, float* scales_out,
+                             hipStream_t st);
+
+}  // namespace moe

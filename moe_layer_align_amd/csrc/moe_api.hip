@@ -9,8 +9,7 @@
 #include <type_traits>
 
 #include "moe.h"
-#include "gemm_decode.h"
-#include "gemm_prefill.h"
+#include "launch.h"
 #include "moe_device.h"
 #include "route_align.h"
 
@@ -33,8 +32,10 @@ bool use_prefill(int M, int k, moe_dtype_t dt, int H, int I) {
   return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0 && I % (kPfRows / 2) == 0 &&
          steps_ok(H) && steps_ok(I) && 2 * (int64_t)I * H <= lim && (int64_t)M * H <= lim && P * I <= lim;
 }
-int align_block(int M, int k, moe_dtype_t dt, int H, int I) {
-  return use_prefill(M, k, dt, H, I) ? kPfTok : kAlignBlockFused;
+// Align block of the fused call: 128 on the prefill path, else 16 (the
+// deterministic mode always takes the decode path).
+int align_block(int M, int k, moe_dtype_t dt, int H, int I, bool det) {
+  return !det && use_prefill(M, k, dt, H, I) ? kPfTok : kAlignBlockFused;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -83,10 +84,14 @@ struct Layout {
   size_t ids, wts, counts, offsets, sorted, block_expert, num_padded, active, num_active;
   size_t xamax_part, scale_slot, h_amax, hist, logits, xq, h, part, total;
   int64_t capacity;
-  int n_blocks, n_route_wg;
+  int block, n_blocks, n_route_wg;
 };
 
-Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
+// The workspace serves both modes of a shape (the default one and the
+// deterministic one, whose align block may differ): the sort-and-pad arrays
+// are sized for the larger of the two blocks' needs.  capacity and n_blocks
+// are those of the call's own block.
+Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det = false) {
   Layout L{};
   const int64_t P = (int64_t)M * k;
   size_t off = 0;
@@ -95,16 +100,22 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt) {
     off += round_up(std::max<size_t>(bytes, 4), 256);
     return o;
   };
-  const int B = align_block(M, k, dt, H, I);
+  const int B = align_block(M, k, dt, H, I, det);
+  L.block = B;
   L.capacity = align_capacity(P, E, B);
   L.n_blocks = (int)(L.capacity / B);
+  int64_t cap_max = 0, blocks_max = 0;
+  for (const int b : {align_block(M, k, dt, H, I, false), align_block(M, k, dt, H, I, true)}) {
+    cap_max = std::max(cap_max, align_capacity(P, E, b));
+    blocks_max = std::max(blocks_max, align_capacity(P, E, b) / b);
+  }
   L.n_route_wg = route_grid(M, dt == MOE_DTYPE_FP8_E4M3 ? (int64_t)M * H : 0);
   L.ids = take(P * 4);
   L.wts = take(P * 4);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
-  L.sorted = take(L.capacity * 4);
-  L.block_expert = take((size_t)L.n_blocks * 4);
+  L.sorted = take((size_t)cap_max * 4);
+  L.block_expert = take((size_t)blocks_max * 4);
   L.num_padded = take(4);
   L.active = take((size_t)E * 4);
   L.num_active = take(4);
@@ -137,7 +148,7 @@ struct Plan {
 bool valid_u(bool fp8, int u) { return fp8 ? (u == 1 || u == 2) : (u == 2 || u == 4); }
 bool valid_wsplit(int ks) { return ks == 1 || ks == 2 || ks == 4; }
 
-moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool qh, const moe_tuning_t* t,
+moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool qh, const moe_tuning_t* t, bool det,
                        Plan* p) {
   const int kstep = fp8 ? 128 : 32;
   const int64_t P = (int64_t)M * k;
@@ -205,6 +216,22 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
     p->u1 = 1;
   }
   if (p->tw2 > 0) p->wks2 = 1;  // the long-stream down product does not split K over waves
+  if (det) {
+    // Deterministic mode: the order of every output's sums is fixed by the
+    // shape alone, never by M.  Gate/up: K split over ks1 waves (fp8 1, bf16
+    // 4), the long-stream variant only with ks1 = 1, whose one chain of
+    // k-steps is the K-split variant's with one wave; down: one K slice split
+    // over wks2 waves (fp8 1, bf16 4), the long-stream variant only with
+    // wks2 = 1.  Tunings that change those orders are refused.
+    if (t && (t->gemm1_ksplit > 0 || t->gemm2_ksplit > 0 || t->gemm2_wave_ksplit > 0)) return MOE_ERR_INVALID_ARG;
+    p->ks1 = fp8 ? 1 : 4;
+    const int wks = fp8 ? 1 : 4;
+    if ((t && t->gemm1_stream_tiles > 0 && p->ks1 > 1) || (t && t->gemm2_stream_tiles > 0 && wks > 1))
+      return MOE_ERR_INVALID_ARG;
+    if (p->ks1 > 1) p->tw1 = 0;
+    if (wks > 1) p->tw2 = 0;
+    p->wks2 = wks;
+  }
   if ((H / p->ks1) % kstep != 0) return MOE_ERR_UNSUPPORTED;
   p->passes1 = (int)cdiv(M, p->nt1 * 16);
   p->passes2 = (int)cdiv(M, p->nt2 * 16);
@@ -226,7 +253,7 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
   const int64_t wgs_per_slice = groups2 * n_act * p->passes2;
   p->ks2 = 0;
   const int64_t wgs_target = p->tw2 > 0 ? 256 : 1024;
-  for (int ks = 1; ks <= ks_cap; ++ks) {
+  for (int ks = 1; ks <= (det ? 1 : ks_cap); ++ks) {
     if (!fits(ks)) continue;
     p->ks2 = ks;
     if (wgs_per_slice * ks >= wgs_target) break;
@@ -241,120 +268,7 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
   return MOE_OK;
 }
 
-// ---------------------------------------------------------------- dispatch
-template <bool FP8, int HF, int NT, int U, int KS>
-void launch_g1(dim3 g, hipStream_t st, const Gemm1Args& a) {
-  gemm1_decode_kernel<FP8, HF, NT, U, KS><<<g, 256, 0, st>>>(a);
-}
-
-template <bool FP8, int HF, int NT, int U>
-bool g1_ks(int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
-  switch (ks) {
-    case 1: launch_g1<FP8, HF, NT, U, 1>(g, st, a); return true;
-    case 2: launch_g1<FP8, HF, NT, U, 2>(g, st, a); return true;
-    case 4: launch_g1<FP8, HF, NT, U, 4>(g, st, a); return true;
-  }
-  return false;
-}
-
-template <bool FP8, int HF, int NT>
-bool g1_u(int u, int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
-  if constexpr (FP8) {
-    if (u == 1) return g1_ks<FP8, HF, NT, 1>(ks, g, st, a);
-    if (u == 2) return g1_ks<FP8, HF, NT, 2>(ks, g, st, a);
-  } else {
-    if (u == 2) return g1_ks<FP8, HF, NT, 2>(ks, g, st, a);
-    if (u == 4) return g1_ks<FP8, HF, NT, 4>(ks, g, st, a);
-  }
-  return false;
-}
-
-template <bool FP8, int HF>
-bool g1_nt(int nt, int u, int ks, dim3 g, hipStream_t st, const Gemm1Args& a) {
-  switch (nt) {
-    case 1: return g1_u<FP8, HF, 1>(u, ks, g, st, a);
-    case 2: return g1_u<FP8, HF, 2>(u, ks, g, st, a);
-    case 4: return g1_u<FP8, HF, 4>(u, ks, g, st, a);
-  }
-  return false;
-}
-
-// long-stream variants
-template <bool FP8, int HF, int NT>
-bool g1s_u(int u, int tw, dim3 g, hipStream_t st, const Gemm1Args& a) {
-  constexpr int U0 = FP8 ? 1 : 2;  // the two unrolls of the dtype: U0 and 2*U0
-  if (u == U0) gemm1_stream_kernel<FP8, HF, NT, U0><<<g, 256, 0, st>>>(a, tw);
-  else if (u == 2 * U0) gemm1_stream_kernel<FP8, HF, NT, 2 * U0><<<g, 256, 0, st>>>(a, tw);
-  else return false;
-  return true;
-}
-
-template <bool FP8, int HF>
-bool g1s_nt(int nt, int u, int tw, dim3 g, hipStream_t st, const Gemm1Args& a) {
-  switch (nt) {
-    case 1: return g1s_u<FP8, HF, 1>(u, tw, g, st, a);
-    case 2: return g1s_u<FP8, HF, 2>(u, tw, g, st, a);
-    case 4: return g1s_u<FP8, HF, 4>(u, tw, g, st, a);
-  }
-  return false;
-}
-
-template <bool FP8, int HF, int NT>
-bool g2s_u(int u, int tw, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  constexpr int U0 = FP8 ? 1 : 2;
-  if (u == U0) gemm2_stream_kernel<FP8, HF, NT, U0><<<g, 256, lds, st>>>(a, tw);
-  else if (u == 2 * U0) gemm2_stream_kernel<FP8, HF, NT, 2 * U0><<<g, 256, lds, st>>>(a, tw);
-  else return false;
-  return true;
-}
-
-template <bool FP8, int HF>
-bool g2s_nt(int nt, int u, int tw, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  switch (nt) {
-    case 1: return g2s_u<FP8, HF, 1>(u, tw, g, lds, st, a);
-    case 2: return g2s_u<FP8, HF, 2>(u, tw, g, lds, st, a);
-    case 4: return g2s_u<FP8, HF, 4>(u, tw, g, lds, st, a);
-  }
-  return false;
-}
-
-template <bool FP8, int HF, int NT, int U, int WKS>
-void launch_g2(dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  gemm2_decode_kernel<FP8, HF, NT, U, WKS><<<g, 256, lds, st>>>(a);
-}
-
-template <bool FP8, int HF, int NT, int U>
-bool g2_wks(int wks, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  switch (wks) {
-    case 1: launch_g2<FP8, HF, NT, U, 1>(g, lds, st, a); return true;
-    case 2: launch_g2<FP8, HF, NT, U, 2>(g, lds, st, a); return true;
-    case 4: launch_g2<FP8, HF, NT, U, 4>(g, lds, st, a); return true;
-  }
-  return false;
-}
-
-template <bool FP8, int HF, int NT>
-bool g2_u(int u, int wks, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  if constexpr (FP8) {
-    if (u == 1) return g2_wks<FP8, HF, NT, 1>(wks, g, lds, st, a);
-    if (u == 2) return g2_wks<FP8, HF, NT, 2>(wks, g, lds, st, a);
-  } else {
-    if (u == 2) return g2_wks<FP8, HF, NT, 2>(wks, g, lds, st, a);
-    if (u == 4) return g2_wks<FP8, HF, NT, 4>(wks, g, lds, st, a);
-  }
-  return false;
-}
-
-template <bool FP8, int HF>
-bool g2_nt(int nt, int u, int wks, dim3 g, size_t lds, hipStream_t st, const Gemm2Args& a) {
-  switch (nt) {
-    case 1: return g2_u<FP8, HF, 1>(u, wks, g, lds, st, a);
-    case 2: return g2_u<FP8, HF, 2>(u, wks, g, lds, st, a);
-    case 4: return g2_u<FP8, HF, 4>(u, wks, g, lds, st, a);
-  }
-  return false;
-}
-
+// ---------------------------------------------------------------- launches
 bool launch_route(const float* logits, int M, int E, int k, int S, int32_t* ids, float* wts, const RouteFusedArgs& fa,
                   hipStream_t st) {
   const dim3 grid((unsigned)route_grid(M, fa.x_amax_part ? (int64_t)M * fa.H : 0));
@@ -393,25 +307,6 @@ moe_status_t persistent_wgs(int* wgs) {
   const int n = cus / 8 * 8;
   if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   *wgs = n;
-  return MOE_OK;
-}
-
-// The dynamic LDS ceiling of a prefill kernel is raised once per kernel and
-// device (the current device, as for the launch that follows); a failure to
-// raise it is reported as MOE_ERR_DEVICE.
-template <int MODE, bool HDYN, bool PC>
-moe_status_t launch_prefill(int wgs, hipStream_t st, const PrefillArgs& g) {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<bool> lds_set[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_DEVICE;
-  if (dev >= kMaxDevices || !lds_set[dev].load(std::memory_order_acquire)) {
-    if (hipFuncSetAttribute((const void*)prefill_gemm_kernel<MODE, HDYN, PC>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds) != hipSuccess)
-      return MOE_ERR_DEVICE;
-    if (dev < kMaxDevices) lds_set[dev].store(true, std::memory_order_release);
-  }
-  prefill_gemm_kernel<MODE, HDYN, PC><<<wgs, kPfThreads, kPfLds, st>>>(g);
   return MOE_OK;
 }
 
@@ -472,11 +367,12 @@ const char* moe_status_string(moe_status_t s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
     case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    default: break;
   }
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 8; }
+int32_t moe_abi_version(void) { return 9; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -539,6 +435,20 @@ size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int3
   return make_layout(M, E, H, I, top_k, dtype).total;
 }
 
+moe_status_t moe_fused_align_shape(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype,
+                                   int32_t deterministic, int32_t* block, int64_t* capacity) {
+  moe_status_t rc = check_shape(M, E, top_k);
+  if (rc != MOE_OK) return rc;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (deterministic != 0 && deterministic != 1) return MOE_ERR_INVALID_ARG;
+  if (!block || !capacity) return MOE_ERR_INVALID_ARG;
+  if (H < 128 || I < 128 || H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
+  const Layout L = make_layout(M, E, H, I, top_k, dtype, deterministic == 1);
+  *block = L.block;
+  *capacity = L.capacity;
+  return MOE_OK;
+}
+
 // fp8 prefill: router, align (block 128) with the activation quantisation,
 // the two tiled products and the per-token combine.
 static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev, const Layout& L,
@@ -588,10 +498,7 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
                   a->h_scale, h, h_amax, es};
-    const int n = std::min(wgs, items);
-    rc = pc ? (hdyn ? launch_prefill<0, true, true>(n, st, g) : launch_prefill<0, false, true>(n, st, g))
-            : (hdyn ? launch_prefill<0, true, false>(n, st, g) : launch_prefill<0, false, false>(n, st, g));
-    if (rc != MOE_OK) return rc;
+    if (!launch_prefill_gemm(0, hdyn, pc, std::min(wgs, items), st, g)) return MOE_ERR_DEVICE;
   }
   rec(5);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -599,23 +506,20 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   {
     if (hdyn) {
       const int64_t n = P * I;
-      prefill_quant_h_kernel<<<(unsigned)cdiv(n, 4096), 256, 0, st>>>((const float*)h, n, h_amax, hq);
+      launch_prefill_quant_h((const float*)h, n, h_amax, hq, st);
       if ((rc = launch_status()) != MOE_OK) return rc;
     }
     const int T = H / kPfRows;
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w2, hq, seg, H, I, k, (int)P, T, items, a->w2_scale, a->h_scale, h_amax, nullptr,
                   (uint8_t*)part, nullptr, es};
-    const int n = std::min(wgs, items);
-    rc = pc ? (hdyn ? launch_prefill<1, true, true>(n, st, g) : launch_prefill<1, false, true>(n, st, g))
-            : (hdyn ? launch_prefill<1, true, false>(n, st, g) : launch_prefill<1, false, false>(n, st, g));
-    if (rc != MOE_OK) return rc;
+    if (!launch_prefill_gemm(1, hdyn, pc, std::min(wgs, items), st, g)) return MOE_ERR_DEVICE;
   }
   rec(7);
   if ((rc = launch_status()) != MOE_OK) return rc;
   rec(8);
-  prefill_finalize_kernel<<<(unsigned)cdiv((int64_t)M * H, 2048), 256, 0, st>>>(
-      (const uint16_t*)part, wts, (uint16_t*)a->y, M, H, k, scale_slot, h_amax, a->h_scale, a->scales_out);
+  launch_prefill_finalize((const uint16_t*)part, wts, (uint16_t*)a->y, M, H, k, scale_slot, h_amax, a->h_scale,
+                          a->scales_out, st);
   rec(9);
   return launch_status();
 }
@@ -659,15 +563,22 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   if (!aligned(a->workspace, 256)) return MOE_ERR_INVALID_ARG;
   for (const void* p : {(const void*)a->logits, (const void*)a->w13_scale, (const void*)a->w2_scale,
                         (const void*)a->x_scale, (const void*)a->h_scale, (const void*)a->topk_ids,
-                        (const void*)a->topk_weights, (const void*)a->expert_counts, (const void*)a->scales_out})
+                        (const void*)a->topk_weights, (const void*)a->expert_counts, (const void*)a->scales_out,
+                        (const void*)a->expert_offsets, (const void*)a->sorted_ids, (const void*)a->block_expert,
+                        (const void*)a->num_padded})
     if (!aligned(p, 4)) return MOE_ERR_INVALID_ARG;
-  const Layout L = make_layout(M, E, H, I, k, a->dtype);
+  // deterministic mode: batch-invariant only with per-tensor activation
+  // scales fixed by the caller (a dynamic scale is an amax over the batch)
+  if (a->deterministic != 0 && a->deterministic != 1) return MOE_ERR_INVALID_ARG;
+  const bool det = a->deterministic == 1;
+  if (det && fp8 && (!a->x_scale || !a->h_scale)) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(M, E, H, I, k, a->dtype, det);
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const bool hdyn = fp8 && !a->h_scale;
-  const bool prefill = use_prefill(M, k, a->dtype, a->H, a->I);
+  const bool prefill = !det && use_prefill(M, k, a->dtype, a->H, a->I);
   Plan plan{};
   if (!prefill) {
-    rc = make_plan(M, E, H, I, k, S, fp8, hdyn, a->tuning, &plan);
+    rc = make_plan(M, E, H, I, k, S, fp8, hdyn, a->tuning, det, &plan);
     if (rc != MOE_OK) return rc;
   }
 
@@ -694,8 +605,10 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   int32_t* ids = a->topk_ids ? a->topk_ids : (int32_t*)(ws + L.ids);
   float* wts = a->topk_weights ? a->topk_weights : (float*)(ws + L.wts);
   int32_t* counts = a->expert_counts ? a->expert_counts : (int32_t*)(ws + L.counts);
-  int32_t* offsets = (int32_t*)(ws + L.offsets);
-  int32_t* sorted = (int32_t*)(ws + L.sorted);
+  int32_t* offsets = a->expert_offsets ? a->expert_offsets : (int32_t*)(ws + L.offsets);
+  int32_t* sorted = a->sorted_ids ? a->sorted_ids : (int32_t*)(ws + L.sorted);
+  int32_t* block_expert = a->block_expert ? a->block_expert : (int32_t*)(ws + L.block_expert);
+  int32_t* num_padded = a->num_padded ? a->num_padded : (int32_t*)(ws + L.num_padded);
   int32_t* active = (int32_t*)(ws + L.active);
   int32_t* num_active = (int32_t*)(ws + L.num_active);
   float* xamax_part = (float*)(ws + L.xamax_part);
@@ -707,8 +620,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const int64_t P = (int64_t)M * k;
   const int n_act = (int)std::min<int64_t>(E, P);
 
-  AlignOut o{counts, offsets, sorted, (int32_t*)(ws + L.block_expert), (int32_t*)(ws + L.num_padded), active,
-             num_active, L.n_blocks};
+  AlignOut o{counts, offsets, sorted, block_expert, num_padded, active, num_active, L.n_blocks};
   if (prefill)
     return prefill_forward(a, st, ev, L, ws, ids, wts, o, xamax_part, scale_slot, h_amax, xq, h, part, hdyn, S);
   const bool small = P <= kSmallPairs && E <= kSmallMaxExperts && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
@@ -767,20 +679,10 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
                 a->h_scale, h, h_amax};
     g.w_cs = pc ? 1 : 0;
     g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
-    const int tpw = 4 / plan.ks1;
-    const dim3 grid((unsigned)(I / 16 / tpw), (unsigned)n_act, (unsigned)plan.passes1);
-    bool ok;
-    if (plan.tw1 > 0) {
-      const dim3 gs((unsigned)cdiv(I / 16, 4 * plan.tw1), (unsigned)n_act, (unsigned)plan.passes1);
-      ok = !fp8  ? g1s_nt<false, H_BF16>(plan.nt1, plan.u1, plan.tw1, gs, st, g)
-           : hdyn ? g1s_nt<true, H_F32>(plan.nt1, plan.u1, plan.tw1, gs, st, g)
-                  : g1s_nt<true, H_E4M3>(plan.nt1, plan.u1, plan.tw1, gs, st, g);
-    } else if (!fp8)
-      ok = g1_nt<false, H_BF16>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
-    else if (hdyn)
-      ok = g1_nt<true, H_F32>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
-    else
-      ok = g1_nt<true, H_E4M3>(plan.nt1, plan.u1, plan.ks1, grid, st, g);
+    DecodeShape sh{plan.nt1, plan.u1, plan.ks1, plan.tw1, dim3(), 0};
+    sh.grid = plan.tw1 > 0 ? dim3((unsigned)cdiv(I / 16, 4 * plan.tw1), (unsigned)n_act, (unsigned)plan.passes1)
+                           : dim3((unsigned)(I / 16 / (4 / plan.ks1)), (unsigned)n_act, (unsigned)plan.passes1);
+    const bool ok = fp8 ? launch_gemm1_fp8(hdyn ? H_F32 : H_E4M3, sh, st, g) : launch_gemm1_bf16(sh, st, g);
     if (!ok) return MOE_ERR_UNSUPPORTED;
   }
   rec(5);
@@ -793,19 +695,11 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
                 (int)P};
     g.w_cs = pc ? 1 : 0;
     g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
-    const dim3 grid((unsigned)(H / (32 * (4 / plan.wks2))), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
-    bool ok;
-    if (plan.tw2 > 0) {
-      const dim3 gs((unsigned)cdiv(H / 32, 4 * plan.tw2), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
-      ok = hf == H_BF16 ? g2s_nt<false, H_BF16>(plan.nt2, plan.u2, plan.tw2, gs, 0, st, g)
-           : hf == H_F32 ? g2s_nt<true, H_F32>(plan.nt2, plan.u2, plan.tw2, gs, plan.lds2, st, g)
-                         : g2s_nt<true, H_E4M3>(plan.nt2, plan.u2, plan.tw2, gs, 0, st, g);
-    } else if (hf == H_BF16)
-      ok = g2_nt<false, H_BF16>(plan.nt2, plan.u2, plan.wks2, grid, 0, st, g);
-    else if (hf == H_F32)
-      ok = g2_nt<true, H_F32>(plan.nt2, plan.u2, plan.wks2, grid, plan.lds2, st, g);
-    else
-      ok = g2_nt<true, H_E4M3>(plan.nt2, plan.u2, plan.wks2, grid, 0, st, g);
+    DecodeShape sh{plan.nt2, plan.u2, plan.wks2, plan.tw2, dim3(), (size_t)(hf == H_F32 ? plan.lds2 : 0)};
+    sh.grid = plan.tw2 > 0
+                  ? dim3((unsigned)cdiv(H / 32, 4 * plan.tw2), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2))
+                  : dim3((unsigned)(H / (32 * (4 / plan.wks2))), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
+    const bool ok = fp8 ? launch_gemm2_fp8(hf, sh, st, g) : launch_gemm2_bf16(sh, st, g);
     if (!ok) return MOE_ERR_UNSUPPORTED;
   }
   rec(7);

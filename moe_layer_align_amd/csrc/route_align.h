@@ -123,7 +123,7 @@ __host__ __device__ inline int route_grid(int M, int64_t x_elems) {
 // same bits on every call and in every batch; T = 4 (large M) reads each
 // router row once per 64 tokens instead of once per 16.
 template <int T>
-__global__ __launch_bounds__(1024) void router_logits_kernel(const uint16_t* __restrict__ x,
+static __global__ __launch_bounds__(1024) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                              const uint16_t* __restrict__ wg, int M, int E, int H,
                                                              float* __restrict__ logits) {
   __shared__ f32x4 s_part[16][T][64];
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(1024) void router_logits_kernel(const uint16_t* __r
 // row of ids/wts (stride K+S) name experts E..E+S-1 with weight one, and the
 // expert counts cover all E+S.
 template <int NPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int M, int E, int K, int S,
+static __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int M, int E, int K, int S,
                                                          int32_t* __restrict__ ids, float* __restrict__ wts,
                                                          RouteFusedArgs fa) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -352,7 +352,7 @@ struct AlignHist {
   int rows_per_wave;      // 256 / (16 k)
 };
 
-__global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ ids, int P, int E, int B,
+static __global__ __launch_bounds__(256) void align_kernel(const int32_t* __restrict__ ids, int P, int E, int B,
                                                     int log2B, int id_bits, int n_align_wgs, AlignOut o,
                                                     QuantXArgs q, AlignHist hist) {
   if ((int)blockIdx.x >= n_align_wgs) {
@@ -746,7 +746,7 @@ __device__ __forceinline__ void wave_align(const int* s_ids, int P, int E, int l
 }
 
 template <int NPL>
-__global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __restrict__ logits, int M, int E, int K,
+static __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __restrict__ logits, int M, int E, int K,
                                                               int S, int32_t* __restrict__ ids, float* __restrict__ wts,
                                                               int log2B, int id_bits, AlignOut o, SmallQuant q) {
   if (blockIdx.x > 0) {
@@ -788,7 +788,7 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(const float* __res
 // Align of P <= 1024 router-produced pairs (valid ids) in workgroup 0 of
 // 1024 threads; workgroups 1.. quantise x (16K elements each) from the
 // router's partial maxima.
-__global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __restrict__ ids, int P, int E, int log2B,
+static __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __restrict__ ids, int P, int E, int log2B,
                                                            int id_bits, AlignOut o, QuantXArgs q) {
   if (blockIdx.x > 0) {
     quant_x_part<1024>(q, blockIdx.x - 1);

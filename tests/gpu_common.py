@@ -14,6 +14,26 @@ from synth import MoEConfig, gen_logits, gen_weights, gen_x
 
 DEV = torch.device("cuda:0")
 TOL = {"bf16": 1e-2, "fp8": 3e-2}
+GUARD = 64  # canary elements before and after every caller-visible output
+
+
+class Guarded:
+    """A GPU output with GUARD canary elements on both sides.  The interior is
+    pre-filled with the same pattern, so every element the call must write
+    is checked to have been written (by the comparisons that follow) and
+    nothing past either end may change."""
+
+    def __init__(self, shape, dtype, pattern: int):
+        n = int(np.prod(shape))
+        raw = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.int32: torch.int32}[dtype]
+        self.n, self.pattern = n, pattern
+        self.buf = torch.full((n + 2 * GUARD,), pattern, dtype=raw, device=DEV)
+        self.t = self.buf[GUARD:GUARD + n].view(dtype).view(*shape)
+
+    def check(self, name: str):
+        b = self.buf.cpu()
+        assert bool((b[:GUARD] == self.pattern).all()), "%s: canary before the output overwritten" % name
+        assert bool((b[GUARD + self.n:] == self.pattern).all()), "%s: canary after the output overwritten" % name
 
 
 def say(msg: str):
@@ -26,27 +46,65 @@ def err_norm(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
     return float(np.abs(y_gpu - y_ref).max() / max(np.abs(y_ref).max(), 1e-30))
 
 
-def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuning=None, n_shared=0):
+def err_rows(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
+    """The same figure per token, max over tokens of max_n |dy_m| / max_n |y_ref_m|,
+    so that rows of small magnitude are held to the same bound."""
+    num = np.abs(y_gpu - y_ref).max(axis=1)
+    den = np.maximum(np.abs(y_ref).max(axis=1), 1e-30)
+    return float((num / den).max()) if num.size else 0.0
+
+
+def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuning=None, n_shared=0,
+            deterministic=False):
     """One fused forward on the GPU; returns host copies of y and intermediates
-    (ids/weights [M,k+n_shared], counts [E+n_shared])."""
+    (ids/weights [M,k+n_shared], counts [E+n_shared], the sort-and-pad
+    outputs).  Every output sits between canaries, checked after the call."""
     w13, w2, s13, s2 = weights
     M = x.shape[0]
     fp8 = cfg.dtype == "fp8"
+    ES, KS = cfg.E + n_shared, cfg.k + n_shared
     # activation scales and per-tensor weight scales are floats; per-row
     # weight scales are [E,rows] tensors, passed as they are
     sc = lambda v: (None if v is None else v.to(DEV, torch.float32).contiguous() if isinstance(v, torch.Tensor)
                     else torch.tensor([v], dtype=torch.float32, device=DEV))
-    ids = torch.full((M, cfg.k + n_shared), -1, dtype=torch.int32, device=DEV)
-    wts = torch.zeros((M, cfg.k + n_shared), dtype=torch.float32, device=DEV)
-    counts = torch.full((cfg.E + n_shared,), -1, dtype=torch.int32, device=DEV)
-    scales = torch.zeros(2, dtype=torch.float32, device=DEV) if fp8 else None
+    blk, cap = moe.fused_align_shape(M, ES, cfg.H, cfg.I, KS, cfg.dtype, deterministic)
+    out = dict(y=Guarded((M, cfg.H), torch.bfloat16, 0x7FC1), ids=Guarded((M, KS), torch.int32, -7),
+               weights=Guarded((M, KS), torch.float32, 0x7FC00007), counts=Guarded((ES,), torch.int32, -7),
+               offsets=Guarded((ES + 1,), torch.int32, -7), sorted_ids=Guarded((cap,), torch.int32, -7),
+               block_expert=Guarded((cap // blk,), torch.int32, -7), num_padded=Guarded((1,), torch.int32, -7))
+    if fp8:
+        out["scales"] = Guarded((2,), torch.float32, 0x7FC00007)
     y = moe.fused_forward(x.to(DEV), logits.to(DEV), w13, w2, cfg.k, cfg.dtype,
                           w13_scale=sc(s13) if fp8 else None, w2_scale=sc(s2) if fp8 else None,
-                          x_scale=sc(x_scale), h_scale=sc(h_scale), topk_ids=ids, topk_weights=wts,
-                          expert_counts=counts, scales_out=scales, tuning=tuning, n_shared=n_shared)
+                          x_scale=sc(x_scale), h_scale=sc(h_scale), out=out["y"].t, topk_ids=out["ids"].t,
+                          topk_weights=out["weights"].t, expert_counts=out["counts"].t,
+                          scales_out=out["scales"].t if fp8 else None, tuning=tuning, n_shared=n_shared,
+                          align_out={key: out[key].t for key in ("offsets", "sorted_ids", "block_expert",
+                                                                  "num_padded")},
+                          deterministic=deterministic)
     torch.cuda.synchronize()
-    return dict(y=y.float().cpu().numpy().astype(np.float64), ids=ids.cpu().numpy(), weights=wts.cpu().numpy(),
-                counts=counts.cpu().numpy(), scales=None if scales is None else scales.cpu().numpy())
+    assert y.data_ptr() == out["y"].t.data_ptr()
+    for name, g in out.items():
+        g.check(name)
+    res = {name: g.t.cpu().numpy() for name, g in out.items() if name != "y"}
+    res["y"] = out["y"].t.float().cpu().numpy().astype(np.float64)
+    res["y_bits"] = out["y"].t.view(torch.int16).cpu().numpy()
+    res.setdefault("scales", None)
+    res["block"] = blk
+    return res
+
+
+def check_align(gpu: dict, ids_full: np.ndarray, E: int):
+    """The fused call's sort-and-pad outputs equal the oracle's for its block
+    size, bit for bit (entries of sorted_ids past the padded total are
+    unspecified and not compared)."""
+    ref = oracle.align(ids_full, E, gpu["block"])
+    n = int(gpu["num_padded"][0])
+    assert n == ref["num_padded"], (n, ref["num_padded"])
+    assert np.array_equal(gpu["counts"], ref["counts"]), "expert counts differ"
+    assert np.array_equal(gpu["offsets"], ref["offsets"]), "expert offsets differ"
+    assert np.array_equal(gpu["sorted_ids"][:n], ref["sorted_ids"][:n]), "sorted ids differ"
+    assert np.array_equal(gpu["block_expert"], ref["block_expert"]), "block map differs"
 
 
 def run_oracle(cfg: MoEConfig, x, logits, weights, tokens=None, x_scale=None, h_scale=None, n_shared=0):
@@ -68,7 +126,7 @@ def run_oracle(cfg: MoEConfig, x, logits, weights, tokens=None, x_scale=None, h_
 
 
 def compare(cfg: MoEConfig, M: int, seed: int = 0, weights=None, tokens=None, x_scale=None, h_scale=None,
-            tuning=None, logits=None, x=None, n_shared=0):
+            tuning=None, logits=None, x=None, n_shared=0, deterministic=False):
     """Full parity check of one layer call; returns (err, gpu, ref).  With
     n_shared, `weights` (default: drawn for E+n_shared experts) hold the shared
     experts after the routed ones."""
@@ -79,24 +137,30 @@ def compare(cfg: MoEConfig, M: int, seed: int = 0, weights=None, tokens=None, x_
     if weights is None:
         weights = gen_weights(cfg, seed, device=DEV, E=cfg.E + n_shared)
     say("%s M=%d dtype=%s xs=%s hs=%s shared=%d" % (cfg.name, M, cfg.dtype, x_scale, h_scale, n_shared))
-    gpu = run_gpu(cfg, x, logits, weights, x_scale, h_scale, tuning, n_shared)
+    gpu = run_gpu(cfg, x, logits, weights, x_scale, h_scale, tuning, n_shared, deterministic)
     ref = run_oracle(cfg, x, logits, weights, tokens, x_scale, h_scale, n_shared)
     # routing: bit-exact ids and counts; the shared slots name E+s with weight one
     k = cfg.k
     assert np.array_equal(gpu["ids"][:, :k], ref["ids"]), "topk ids differ"
     counts = np.bincount(ref["ids"].ravel(), minlength=cfg.E)
+    ids_full = ref["ids"]
     if n_shared:
         assert (gpu["ids"][:, k:] == cfg.E + np.arange(n_shared)).all(), "shared slots differ"
         assert (gpu["weights"][:, k:] == 1.0).all(), "shared weights differ"
         counts = np.concatenate([counts, np.full(n_shared, M)])
+        ids_full = np.concatenate([ref["ids"], np.tile(cfg.E + np.arange(n_shared, dtype=np.int32), (M, 1))], axis=1)
     assert np.array_equal(gpu["counts"], counts), "expert counts differ"
+    check_align(gpu, np.ascontiguousarray(ids_full, dtype=np.int32), cfg.E + n_shared)
     assert np.allclose(gpu["weights"][:, :k], ref["weights"], rtol=1e-6, atol=1e-6), "topk weights differ"
     if cfg.dtype == "fp8":
         assert gpu["scales"][0] == np.float32(ref["s_x"]), (gpu["scales"][0], ref["s_x"])
         assert abs(gpu["scales"][1] / ref["s_h"] - 1) < 1e-4, (gpu["scales"][1], ref["s_h"])
     rows = list(range(M)) if tokens is None else list(tokens)
     e = err_norm(gpu["y"][rows], ref["y"])
-    say("  err=%.3e (tol %.0e) oracle %.1fs" % (e, TOL[cfg.dtype], ref["seconds"]))
+    er = err_rows(gpu["y"][rows], ref["y"])
+    say("  err=%.3e per-token %.3e (tol %.0e) on %s tokens, oracle %.1fs"
+        % (e, er, TOL[cfg.dtype], "all" if tokens is None else len(rows), ref["seconds"]))
     assert np.isfinite(gpu["y"]).all()
     assert e <= TOL[cfg.dtype], "output error %.3e above %.0e" % (e, TOL[cfg.dtype])
+    assert er <= TOL[cfg.dtype], "per-token output error %.3e above %.0e" % (er, TOL[cfg.dtype])
     return e, gpu, ref

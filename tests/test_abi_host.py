@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("moe_route_topk", "moe_align", "moe_fused_forward", "moe_align_capacity",
-              "moe_fused_workspace_size", "moe_status_string", "moe_quant_e4m3", "moe_router_logits"):
+              "moe_fused_workspace_size", "moe_status_string", "moe_quant_e4m3", "moe_router_logits",
+              "moe_fused_align_shape"):
         assert n in names
 
 
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 8
+    assert lib.moe_abi_version() == 9
 
 
 def capacity_formula(M, k, E, B):
@@ -76,6 +77,36 @@ def test_workspace_size(lib):
     assert bf >= 8 * 256 * 4 + 8 * 512 * 2
     assert lib.moe_fused_workspace_size(4, 8, 200, 512, 2, 0) == 0  # H not a multiple of 128
     assert lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 7) == 0  # unknown dtype
+
+
+def align_shape(lib, M, E, H, I, k, dtype, det=0):
+    b, c = ctypes.c_int32(-1), ctypes.c_int64(-1)
+    rc = lib.moe_fused_align_shape(M, E, H, I, k, dtype, det, ctypes.byref(b), ctypes.byref(c))
+    return rc, b.value, c.value
+
+
+@pytest.mark.parametrize("M,E,H,I,k,dtype,det,block", [
+    (4, 8, 256, 512, 2, 0, 0, 16),          # decode
+    (4096, 128, 4096, 1536, 8, 1, 0, 128),  # fp8 with 32768 pairs: prefill path
+    (4096, 128, 4096, 1536, 8, 1, 1, 16),   # deterministic mode: decode path at every M
+    (4096, 128, 4096, 1536, 8, 0, 0, 16),   # bf16: decode path at every M
+    (1023, 8, 512, 512, 8, 1, 0, 16),       # 8184 pairs: below the prefill threshold
+    (1024, 8, 512, 512, 8, 1, 0, 128),      # 8192 pairs
+])
+def test_fused_align_shape(lib, M, E, H, I, k, dtype, det, block):
+    rc, b, c = align_shape(lib, M, E, H, I, k, dtype, det)
+    assert rc == 0 and b == block and c == capacity_formula(M, k, E, block)
+    # the workspace holds the sort-and-pad arrays of both modes
+    assert lib.moe_fused_workspace_size(M, E, H, I, k, dtype) >= 4 * c + 4 * (c // b)
+
+
+def test_fused_align_shape_invalid(lib):
+    assert align_shape(lib, 4, 8, 256, 512, 9, 0)[0] == 1     # k > E
+    assert align_shape(lib, 4, 8, 256, 512, 2, 3)[0] == 1     # unknown dtype
+    assert align_shape(lib, 4, 8, 256, 512, 2, 0, 2)[0] == 1  # unknown mode
+    assert align_shape(lib, 4, 8, 200, 512, 2, 0)[0] == 2     # H not a multiple of 128
+    b = ctypes.c_int32(0)
+    assert lib.moe_fused_align_shape(4, 8, 256, 512, 2, 0, 0, ctypes.byref(b), None) == 1
 
 
 FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on these paths
@@ -145,6 +176,11 @@ def fused_args(**kw):
     (dict(n_shared=-1), 1),                                  # negative shared-expert count
     (dict(n_shared=15), 2),                                  # top_k + shared above 16
     (dict(E=500, n_shared=13), 2),                           # E + shared above 512
+    (dict(sorted_ids=FAKE + 2), 1),                          # misaligned align output
+    (dict(num_padded=FAKE + 1), 1),                          # misaligned align output
+    (dict(deterministic=2), 1),                              # unknown mode
+    (dict(deterministic=1, dtype=1, w13_scale=FAKE, w2_scale=FAKE), 1),                # fp8: dynamic scales
+    (dict(deterministic=1, dtype=1, w13_scale=FAKE, w2_scale=FAKE, x_scale=FAKE), 1),  # fp8: dynamic h scale
 ])
 def test_fused_validation(lib, kw, code):
     args = fused_args(**kw)
@@ -167,6 +203,16 @@ def test_fused_tuning_validation(lib):
               m.Tuning(gemm2_wave_ksplit=3), m.Tuning(reverse_order=2)):
         args = fused_args(tuning=ctypes.pointer(t))
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
+
+
+def test_fused_deterministic_refuses_order_changing_tunings(lib):
+    import moe_layer_align_amd as m
+    for dt, t in ((0, m.Tuning(gemm1_ksplit=2)), (0, m.Tuning(gemm2_ksplit=2)), (0, m.Tuning(gemm2_wave_ksplit=1)),
+                  (0, m.Tuning(gemm1_stream_tiles=2)), (0, m.Tuning(gemm2_stream_tiles=2)),
+                  (1, m.Tuning(gemm2_ksplit=1))):
+        kw = dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, x_scale=FAKE, h_scale=FAKE) if dt else {}
+        args = fused_args(deterministic=1, tuning=ctypes.pointer(t), **kw)
+        assert lib.moe_fused_forward(ctypes.byref(args), None) == 1, (dt, t)
 
 
 def test_fused_m0_is_noop(lib):

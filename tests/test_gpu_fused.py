@@ -6,12 +6,16 @@ within 1e-6, the fp8 activation scale s_x bit-exact and s_h within 1e-4
 max|y - y_ref| / max|y_ref| <= 1e-2 (bf16) or 3e-2 (fp8), y_ref being the
 oracle's output before bf16 rounding.
 
+Every case also checks the call's sort-and-pad outputs (counts, offsets,
+sorted ids, block map, padded total) bit-exact against the oracle's align for
+the call's block size, the output per token (max |dy_m| / max |y_ref_m|)
+against the same bound, and canaries on both sides of every output.
+
 Shapes: small layers that span several weight tiles, token tiles and token
-passes with ragged tails (the oracle evaluates them whole), the tiny
-workload, and the four full-size workloads at every token count of their
-sweeps; the fp8 prefill layer at M=4096 is compared on sampled tokens with
-static activation scales (the dynamic h scale needs h of all 32768 pairs),
-and with dynamic scales at M=256.
+passes with ragged tails, the tiny workload, and the four full-size workloads
+at every token count of their sweeps.  Every output element of every case is
+compared (the oracle evaluates all tokens, the M=4096 prefill layer
+included).
 """
 import numpy as np
 import pytest
@@ -194,8 +198,7 @@ def deepseek_w():
 
 @pytest.mark.parametrize("M", CONFIGS["deepseek"].ms)
 def test_deepseek(deepseek_w, M):
-    toks = None if M <= 16 else sorted({0, 1, M // 3, M // 2, M - 2, M - 1})
-    compare(CONFIGS["deepseek"], M, seed=0, weights=deepseek_w, tokens=toks)
+    compare(CONFIGS["deepseek"], M, seed=0, weights=deepseek_w)
 
 
 @pytest.fixture(scope="module")
@@ -219,32 +222,33 @@ def test_prefill_path_shortest_down_k():
     # down product of four K-steps (no steady-state iteration: every step is
     # a tail step that may load the next item), gate/up of 12
     cfg = MoEConfig("pf_k4", E=16, k=8, H=1536, I=512, dtype="fp8", ms=(1100,), logits="zipf")
-    compare(cfg, 1100, seed=13, tokens=[0, 1, 2, 3, 400, 401, 777, 1098, 1099])
+    compare(cfg, 1100, seed=13)
 
 
 def test_prefill_path_many_items_per_workgroup():
     # several hundred (tile, block) items in both products: every persistent
     # workgroup walks more than one with the LDS ring running across items
     cfg = MoEConfig("pf_items", E=8, k=2, H=1024, I=1024, dtype="fp8", ms=(8192,), logits="zipf")
-    compare(cfg, 8192, seed=14, tokens=[0, 1, 2, 3, 100, 1000, 2047, 4096, 6000, 8189, 8190, 8191])
+    compare(cfg, 8192, seed=14)
 
 
 def test_prefill_path_static_scales_long_k():
     cfg = MoEConfig("pf_long", E=16, k=8, H=1024, I=512, dtype="fp8", ms=(1100,), logits="zipf")
-    compare(cfg, 1100, seed=12, tokens=[0, 1, 2, 500, 777, 1098, 1099], x_scale=0.012, h_scale=0.01)
+    compare(cfg, 1100, seed=12, x_scale=0.012, h_scale=0.01)
 
 
+@pytest.mark.timeout(900)
 def test_prefill_full_static_scales(prefill_w):
     M = 4096
-    toks = [0, 1, 777, 2048, 3000, 4095]
-    compare(CONFIGS["prefill"], M, seed=0, weights=prefill_w, tokens=toks, x_scale=0.011, h_scale=0.02)
+    compare(CONFIGS["prefill"], M, seed=0, weights=prefill_w, x_scale=0.011, h_scale=0.02)
 
 
+@pytest.mark.timeout(900)
 def test_prefill_full_dynamic_scales(prefill_w):
     # the measured launch: M = 4096 with dynamic x and h scales; the oracle
-    # takes s_h over all 32768 pairs and y on sampled tokens
+    # takes s_h over all 32768 pairs and y of every token
     M = 4096
-    compare(CONFIGS["prefill"], M, seed=0, weights=prefill_w, tokens=[0, 1, 2, 1023, 2048, 3001, 4094, 4095])
+    compare(CONFIGS["prefill"], M, seed=0, weights=prefill_w)
 
 
 def test_prefill_path_repeat_calls_bitwise():
@@ -308,10 +312,11 @@ def test_per_channel_prefill_path(xs, hs):
     compare(cfg, 1100, seed=23, weights=w, x_scale=xs, h_scale=hs)
 
 
+@pytest.mark.timeout(900)
 def test_per_channel_prefill_full_static_scales():
     cfg = CONFIGS["prefill"]
     w = gen_weights_per_channel(cfg, 0, device=DEV)
-    compare(cfg, 4096, seed=0, weights=w, tokens=[0, 1, 1500, 4095], x_scale=0.011, h_scale=0.02)
+    compare(cfg, 4096, seed=0, weights=w, x_scale=0.011, h_scale=0.02)
     del w
     torch.cuda.empty_cache()
 
@@ -342,8 +347,7 @@ def test_fused_with_router_weights(cfg, M):
     assert np.abs(lg.numpy() - ref_lg).max() <= 1e-5 * np.abs(ref_lg).max() + 1e-6
     ref_ids, _ = oracle.route(lg, cfg.k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
-    toks = None if M <= 64 else [0, 1, M // 2, M - 1]
-    e, _, _ = compare(cfg, M, seed=24, weights=w, logits=lg, x=x, tokens=toks)
+    e, _, _ = compare(cfg, M, seed=24, weights=w, logits=lg, x=x)
     # the same layer on the given logits gives the same bits
     y2 = moe.fused_forward(x.to(DEV), lo, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]))
     torch.cuda.synchronize()
@@ -363,13 +367,12 @@ def test_router_weights_with_per_channel_scales(M):
     y = moe.fused_forward(x.to(DEV), None, w[0], w[1], cfg.k, "fp8", w[2], w[3], x_scale=xs, router_w=wg.to(DEV),
                           logits_out=lo)
     torch.cuda.synchronize()
-    toks = None if M <= 64 else [0, 7, M // 2, M - 1]
-    _, gpu, _ = compare(cfg, M, seed=25, weights=w, logits=lo.cpu(), x=x, x_scale=0.013, tokens=toks)
+    _, gpu, _ = compare(cfg, M, seed=25, weights=w, logits=lo.cpu(), x=x, x_scale=0.013)
     assert torch.equal(y.float().cpu(), torch.from_numpy(gpu["y"]).float())
 
 
 def test_prefill_dynamic_scales(prefill_w):
-    compare(CONFIGS["prefill"], 256, seed=0, weights=prefill_w, tokens=[0, 5, 100, 255])
+    compare(CONFIGS["prefill"], 256, seed=0, weights=prefill_w)
 
 
 # ---------------------------------------------------------------- shared experts
@@ -391,7 +394,7 @@ def test_shared_expert_qwen3_shape():
 @pytest.mark.parametrize("k,S", [(8, 1), (7, 1)])
 def test_shared_expert_prefill_path(k, S):
     cfg = MoEConfig("pf_shared", E=16, k=k, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf")
-    compare(cfg, 1100, seed=32 + k, tokens=[0, 1, 2, 3, 500, 777, 1098, 1099], n_shared=S)
+    compare(cfg, 1100, seed=32 + k, n_shared=S)
 
 
 def test_shared_expert_per_channel_with_router_weights():
@@ -430,7 +433,7 @@ def test_per_expert_small_layer(variant, xs, hs, M):
 def test_per_expert_prefill_path(xs, hs):
     cfg = MoEConfig("pf_pe", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="zipf")
     w = gen_weights_per_expert(cfg, 42, device=DEV)
-    compare(cfg, 1100, seed=42, weights=w, tokens=[0, 1, 2, 3, 500, 777, 1098, 1099], x_scale=xs, h_scale=hs)
+    compare(cfg, 1100, seed=42, weights=w, x_scale=xs, h_scale=hs)
 
 
 def test_per_expert_equal_scales_match_per_tensor():
@@ -453,8 +456,7 @@ def test_per_expert_equal_scales_match_per_tensor():
 def test_per_expert_scales_with_shared_expert(M):
     cfg = MoEConfig("pe_shared", E=16, k=7, H=512, I=512, dtype="fp8", ms=(M,), logits="zipf")
     w = gen_weights_per_expert(cfg, 44, device=DEV, E=17)
-    toks = None if M <= 64 else [0, 1, 2, 500, 1099]
-    compare(cfg, M, seed=44, weights=w, tokens=toks, n_shared=1)
+    compare(cfg, M, seed=44, weights=w, n_shared=1)
 
 
 @pytest.mark.parametrize("S", [0, 1])

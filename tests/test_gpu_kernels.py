@@ -120,7 +120,7 @@ def test_align_deterministic():
     t = torch.from_numpy(ids).to(DEV)
     a = moe.align(t, 64, 16)
     n = int(a["num_padded"].item())
-    for _ in range(20):
+    for _ in range(100):
         b = moe.align(t, 64, 16)
         assert int(b["num_padded"].item()) == n
         assert torch.equal(a["sorted_ids"][:n], b["sorted_ids"][:n])  # entries past num_padded are unspecified
