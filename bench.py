@@ -25,8 +25,12 @@ bytes (or flops) over its launch durations, from HIP events around that
 launch in a second timed pass of the same steps.  The CPU oracle is timed on
 a bounded sample of the same workload.
 
-Other workloads (--config qwen3|deepseek|prefill|tiny) print the same line
-for that layer; they are measurement aids, not the headline.
+The default run then times the other workloads the metric names, each with
+its own roofline object and CPU baseline, under "workloads": the fp8
+prefill layer (E=128, top-8, H=4096, I=1536, M=4096; TFLOP/s against the
+fp8 MFMA peak), the Qwen3-shaped fp8 sweep and the DeepSeek-V3-shaped fp8
+sweep (GB/s against HBM).  --config X times workload X alone and prints its
+line with X as the headline.
 """
 from __future__ import annotations
 
@@ -84,7 +88,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="mixtral", choices=["mixtral", "qwen3", "deepseek", "prefill", "tiny"])
+    ap.add_argument("--config", default=None, choices=["mixtral", "qwen3", "deepseek", "prefill", "tiny"],
+                    help="time this workload only (default: the Mixtral headline, then the prefill, Qwen3 and "
+                         "DeepSeek workloads under 'workloads')")
     ap.add_argument("--no-flush", action="store_true", help="hot-cache numbers: skip the cache flush before each call")
     ap.add_argument("--router-gemm", action="store_true",
                     help="the layer computes its router logits from the hidden states and N(0,1/H) router "
@@ -108,8 +114,6 @@ def main() -> int:
 
     import torch
     import moe_layer_align_amd as moe
-    from synth import (CONFIGS, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel,
-                       gen_weights_per_expert, gen_x)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -117,21 +121,47 @@ def main() -> int:
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
     moe.load()  # fails loudly when the HIP library is missing
+    if (args.per_channel or args.per_expert) and args.config in (None, "mixtral", "tiny"):
+        print("--per-channel and --per-expert apply to the fp8 workloads: give --config qwen3|deepseek|prefill",
+              file=sys.stderr)
+        return 2
+    if args.config is not None:
+        line = measure(args.config, args)
+    else:
+        line = measure("mixtral", args)
+        extra = {}
+        for name in ("prefill", "qwen3", "deepseek"):
+            sub = measure(name, args, cpu_seconds=args.cpu_seconds / 2)
+            extra[name] = dict(value=sub["metric_value"], **{key: sub[key] for key in (
+                "unit", "ms_per_step", "dtype", "config", "per_m", "roofline", "cpu_baseline")})
+            torch.cuda.empty_cache()
+        line["workloads"] = extra
+    for key in ("metric_value",):
+        line.pop(key, None)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def measure(config: str, args, cpu_seconds=None) -> dict:
+    """Time one workload's sweep; returns its JSON line (as a dict)."""
+    import torch
+    import moe_layer_align_amd as moe
+    from synth import (CONFIGS, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel,
+                       gen_weights_per_expert, gen_x)
+
     dev = torch.device("cuda:0")
-    cfg = CONFIGS[args.config]
+    cfg = CONFIGS[config]
     fp8 = cfg.dtype == "fp8"
     esz = 1 if fp8 else 2
     log("generating %s weights on the GPU" % cfg.name)
-    if (args.per_channel or args.per_expert) and not fp8:
-        print("--per-channel and --per-expert apply to fp8 workloads only", file=sys.stderr)
-        return 2
     if args.per_channel and args.per_expert or args.shared < 0:
-        print("give at most one of --per-channel and --per-expert, and --shared >= 0", file=sys.stderr)
-        return 2
+        raise SystemExit("give at most one of --per-channel and --per-expert, and --shared >= 0")
     S = args.shared
+    per_channel = args.per_channel and fp8
+    per_expert = args.per_expert and fp8
     ES, KS = cfg.E + S, cfg.k + S  # experts and slots per token with the shared experts
-    if args.per_channel or args.per_expert:
-        gen = gen_weights_per_channel if args.per_channel else gen_weights_per_expert
+    if per_channel or per_expert:
+        gen = gen_weights_per_channel if per_channel else gen_weights_per_expert
         w13, w2, s13_t, s2_t = gen(cfg, 0, device=dev, E=ES)
         s13, s2 = s13_t, s2_t
     else:
@@ -262,7 +292,7 @@ def main() -> int:
     # the counters were taken on the default inputs (cold cache, given logits,
     # per-tensor scales) of these kernel sources
     roof["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256(sources)
-                                                 and not (args.no_flush or args.per_channel or args.per_expert
+                                                 and not (args.no_flush or per_channel or per_expert
                                                           or args.shared or args.router_gemm)) \
         else None
     roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
@@ -274,7 +304,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline and not args.router_gemm:  # the oracle sample takes the workload's logits
-        cpu = cpu_baseline(cfg, calls, (w13, w2, s13, s2), args.cpu_seconds, unit, n_shared=S)
+        cpu = cpu_baseline(cfg, calls, (w13, w2, s13, s2), cpu_seconds or args.cpu_seconds, unit, n_shared=S,
+                           min_s=min(10.0, cpu_seconds or args.cpu_seconds))
 
     ms_str = ",".join(str(m) for m in cfg.ms)
     line = {
@@ -296,7 +327,7 @@ def main() -> int:
             "workload": "%s-shaped %s layer E=%d top-%d H=%d I=%d%s, M in {%s}" % (
                 cfg.name, cfg.dtype, cfg.E, cfg.k, cfg.H, cfg.I, " +%d shared" % S if S else "", ms_str),
             "E": cfg.E, "top_k": cfg.k, "H": cfg.H, "I": cfg.I, "M_sweep": list(cfg.ms), "router_logits": cfg.logits,
-            "weight_scales": ("per channel" if args.per_channel else "per expert" if args.per_expert
+            "weight_scales": ("per channel" if per_channel else "per expert" if per_expert
                               else "per tensor") if fp8 else None,
             "shared_experts": S,
             "logits_source": "computed in the layer from router weights" if args.router_gemm else "given",
@@ -304,9 +335,10 @@ def main() -> int:
         "per_m": per_m,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "metric_value": round(value, 2),
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    del w13, w2, calls, flush_buf
+    return line
 
 
 def _materialise(events, stream):
