@@ -284,6 +284,29 @@ moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream);
 #define MOE_NUM_STAGES 5
 moe_status_t moe_fused_forward_profiled(const moe_fused_args_t* args, void* stream, void* const* events);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the fused
+ * layer exactly as moe_fused_forward computes it (same kernels, same plan,
+ * same bits), with the workspace taken from a scratch array that the library
+ * holds on each GPU it runs on, MOE_NOALLOC_SCRATCH_BYTES bytes, from the
+ * first call on that GPU until the process ends.  args->workspace must be
+ * NULL and args->workspace_bytes 0 (else MOE_ERR_INVALID_ARG); the caller
+ * still passes every input and output.  Calls whose workspace would exceed
+ * the array (the down product's partial sums are sized here for the plan's
+ * K slices only; decode-sized layers fit, the fp8 prefill layer of 4096
+ * tokens does not) return MOE_ERR_UNSUPPORTED before anything is enqueued.
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  The first call on a GPU looks up the array's device address
+ * (hipGetSymbolAddress); a failure there is MOE_ERR_DEVICE.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; nothing in it needs to start at zero.  Calls that overlap on one
+ * GPU (other streams, other threads) race on the array: the caller must
+ * order them, e.g. on one stream.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_fused_forward_noalloc(const moe_fused_args_t* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

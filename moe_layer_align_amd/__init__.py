@@ -17,6 +17,7 @@ import torch
 __all__ = [
     "MoEError", "load", "LIB_PATH", "route_topk", "router_logits", "align_capacity", "align", "quant_e4m3",
     "workspace_size", "fused_align_shape", "fused_forward", "Tuning", "STATUS", "NUM_STAGES", "STAGE_NAMES",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -25,6 +26,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
           4: "MOE_ERR_DEVICE"}
 DTYPE_BF16, DTYPE_FP8 = 0, 1
 NUM_STAGES = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAGE_NAMES = ("route", "align", "gate_up", "down", "finalize")
 
 
@@ -94,6 +96,8 @@ def load():
     lib.moe_fused_forward.argtypes = [ctypes.POINTER(_FusedArgs), vp]
     lib.moe_fused_forward_profiled.restype = ctypes.c_int
     lib.moe_fused_forward_profiled.argtypes = [ctypes.POINTER(_FusedArgs), vp, vp]
+    lib.moe_fused_forward_noalloc.restype = ctypes.c_int
+    lib.moe_fused_forward_noalloc.argtypes = [ctypes.POINTER(_FusedArgs), vp]
     if lib.moe_abi_version() != _ABI:
         raise RuntimeError("libmoe_mi355x.so has ABI version %d, this binding expects %d: rebuild it"
                            % (lib.moe_abi_version(), _ABI))
@@ -214,7 +218,8 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
                   scales_out: Optional[torch.Tensor] = None, tuning: Optional[Tuning] = None, stream=None,
                   events=None, router_w: Optional[torch.Tensor] = None,
                   logits_out: Optional[torch.Tensor] = None, n_shared: int = 0,
-                  align_out: Optional[dict] = None, deterministic: bool = False) -> torch.Tensor:
+                  align_out: Optional[dict] = None, deterministic: bool = False,
+                  noalloc: bool = False) -> torch.Tensor:
     """The fused layer (moe_fused_forward).
 
     x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
@@ -233,6 +238,9 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
     "block_expert" [capacity/block], "num_padded" [1] (block and capacity
     from fused_align_shape; any subset of the keys).
     deterministic: batch-invariant mode (fp8 needs x_scale and h_scale).
+    noalloc: call moe_fused_forward_noalloc, whose workspace is the library's
+    own scratch array (no workspace may be given; `out` must be given, so
+    that the call allocates nothing here either).
     """
     M, H = x.shape
     if (logits is None) == (router_w is None):
@@ -268,6 +276,8 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         if s is not None:
             _need(s, name, torch.float32, (1,))
     if out is None:
+        if noalloc:
+            raise ValueError("the no-alloc call needs `out`")
         out = torch.empty(M, H, dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, (M, H))
     if topk_ids is not None:
@@ -289,18 +299,22 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
             if key in al:
                 _need(al[key], "align_out[%s]" % key, torch.int32, shape)
     lib = load()
-    need = int(lib.moe_fused_workspace_size(M, ES, H, I, KS, DTYPE_FP8 if fp8 else DTYPE_BF16))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
-    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("the no-alloc call takes no workspace")
+    else:
+        need = int(lib.moe_fused_workspace_size(M, ES, H, I, KS, DTYPE_FP8 if fp8 else DTYPE_BF16))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
     args = _FusedArgs(
         M=M, E=E, H=H, I=I, top_k=top_k, dtype=DTYPE_FP8 if fp8 else DTYPE_BF16,
         x=_ptr(x), logits=_ptr(logits), w13=_ptr(w13), w2=_ptr(w2),
         w13_scale=_ptr(w13_scale), w2_scale=_ptr(w2_scale), x_scale=_ptr(x_scale), h_scale=_ptr(h_scale),
         y=_ptr(out), topk_ids=_ptr(topk_ids), topk_weights=_ptr(topk_weights),
         expert_counts=_ptr(expert_counts), scales_out=_ptr(scales_out),
-        workspace=_ptr(workspace), workspace_bytes=workspace.numel(),
+        workspace=_ptr(workspace), workspace_bytes=0 if workspace is None else workspace.numel(),
         tuning=ctypes.pointer(tuning) if tuning is not None else None,
         weight_scale_mode=mode,
         router_w=_ptr(router_w), logits_out=_ptr(logits_out), n_shared=S,
@@ -308,7 +322,11 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         block_expert=_ptr(al.get("block_expert")), num_padded=_ptr(al.get("num_padded")),
         deterministic=int(bool(deterministic)),
     )
-    if events is None:
+    if noalloc:
+        if events is not None:
+            raise ValueError("the no-alloc call records no stage events")
+        _check("moe_fused_forward_noalloc", lib.moe_fused_forward_noalloc(ctypes.byref(args), _stream(stream)))
+    elif events is None:
         _check("moe_fused_forward", lib.moe_fused_forward(ctypes.byref(args), _stream(stream)))
     else:
         if len(events) != 2 * NUM_STAGES:

@@ -91,7 +91,9 @@ struct Layout {
 // deterministic one, whose align block may differ): the sort-and-pad arrays
 // are sized for the larger of the two blocks' needs.  capacity and n_blocks
 // are those of the call's own block.
-Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det = false) {
+// part_slices: K slices of fp32 partial sums the layout holds for the down
+// product (0: as many as any plan of the shape may take, down_ksplit_cap).
+Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det = false, int part_slices = 0) {
   Layout L{};
   const int64_t P = (int64_t)M * k;
   size_t off = 0;
@@ -128,7 +130,9 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det =
   L.xq = take(fp8 ? (size_t)M * H : 0);
   // h: bf16 (bf16 layers), fp32 (fp8 decode), fp32 + its e4m3 copy (fp8 prefill)
   L.h = take((size_t)P * I * (fp8 ? (use_prefill(M, k, dt, H, I) ? 5 : 4) : 2));
-  L.part = take((size_t)down_ksplit_cap(P, H, I, dt == MOE_DTYPE_FP8_E4M3) * (size_t)P * H * 4);
+  const int slices = part_slices > 0 ? part_slices : down_ksplit_cap(P, H, I, dt == MOE_DTYPE_FP8_E4M3);
+  // decode: [slices][P][H] fp32; prefill: [P][H] bf16 (never more)
+  L.part = take((size_t)slices * (size_t)P * H * 4);
   L.total = off;
   return L;
 }
@@ -356,6 +360,30 @@ moe_status_t check_shape(int M, int E, int k) {
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- no-alloc scratch
+// Workspace of moe_fused_forward_noalloc: one array per GPU, held by the
+// loaded code object until the process ends.  Its name is a host-side
+// stand-in in host code: the device address comes from hipGetSymbolAddress,
+// taken once per device (with that device current) and cached.
+constexpr size_t kNoallocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+moe_status_t noalloc_scratch(uint8_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<uint8_t*> cached[kMaxDevices];  // null until taken; racing first calls store the same address
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  uint8_t* p = cached[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return MOE_ERR_DEVICE;
+    p = (uint8_t*)addr;
+    cached[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -524,8 +552,11 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   return launch_status();
 }
 
-static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev) {
+// noalloc: the workspace is the library's scratch array (the caller passes
+// none), its partial-sum region sized for the plan's K slices only.
+static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev, bool noalloc = false) {
   if (!a) return MOE_ERR_INVALID_ARG;
+  if (noalloc && (a->workspace || a->workspace_bytes)) return MOE_ERR_INVALID_ARG;
   auto rec = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
   };
@@ -553,7 +584,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
       for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) rec(i);
     return MOE_OK;
   }
-  if (!a->x || !a->w13 || !a->w2 || !a->y || !a->workspace) return MOE_ERR_INVALID_ARG;
+  if (!a->x || !a->w13 || !a->w2 || !a->y || (!noalloc && !a->workspace)) return MOE_ERR_INVALID_ARG;
   // logits: given, or computed from the router weights (exactly one of the two)
   if ((a->logits == nullptr) == (a->router_w == nullptr)) return MOE_ERR_INVALID_ARG;
   if (a->logits_out && !a->router_w) return MOE_ERR_INVALID_ARG;
@@ -572,8 +603,6 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   if (a->deterministic != 0 && a->deterministic != 1) return MOE_ERR_INVALID_ARG;
   const bool det = a->deterministic == 1;
   if (det && fp8 && (!a->x_scale || !a->h_scale)) return MOE_ERR_INVALID_ARG;
-  const Layout L = make_layout(M, E, H, I, k, a->dtype, det);
-  if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const bool hdyn = fp8 && !a->h_scale;
   const bool prefill = !det && use_prefill(M, k, a->dtype, a->H, a->I);
   Plan plan{};
@@ -581,8 +610,15 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     rc = make_plan(M, E, H, I, k, S, fp8, hdyn, a->tuning, det, &plan);
     if (rc != MOE_OK) return rc;
   }
-
+  // the scratch array holds the partial sums of the plan's K slices only
+  const Layout L = make_layout(M, E, H, I, k, a->dtype, det, noalloc && !prefill ? plan.ks2 : 0);
   uint8_t* ws = (uint8_t*)a->workspace;
+  if (noalloc) {
+    if (L.total > kNoallocScratchBytes) return MOE_ERR_UNSUPPORTED;
+    if ((rc = noalloc_scratch(&ws)) != MOE_OK) return rc;
+  } else if (a->workspace_bytes < L.total) {
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
   // router logits from the hidden states (the step before routing), inside
   // the route stage: its start event is recorded here and not again
   moe_fused_args_t ax = *a;  // the layer as the steps after routing see it
@@ -729,6 +765,10 @@ moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream) {
 
 moe_status_t moe_fused_forward_profiled(const moe_fused_args_t* args, void* stream, void* const* events) {
   return fused_forward(args, (hipStream_t)stream, events);
+}
+
+moe_status_t moe_fused_forward_noalloc(const moe_fused_args_t* args, void* stream) {
+  return fused_forward(args, (hipStream_t)stream, nullptr, true);
 }
 
 }  // extern "C"

@@ -215,6 +215,18 @@ def test_fused_deterministic_refuses_order_changing_tunings(lib):
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 1, (dt, t)
 
 
+def test_fused_noalloc_validation(lib):
+    # a workspace given, and a layer beyond the scratch array (fp32 h of
+    # 32768 pairs x 1024 features alone is 128 MB): refused before any launch
+    args = fused_args()
+    assert lib.moe_fused_forward_noalloc(ctypes.byref(args), None) == 1
+    args = fused_args(workspace=None, workspace_bytes=0, M=4096, E=16, top_k=8, H=1024, I=1024, dtype=1,
+                      w13_scale=FAKE, w2_scale=FAKE)
+    assert lib.moe_fused_forward_noalloc(ctypes.byref(args), None) == 2
+    args = fused_args(workspace=None, workspace_bytes=0, top_k=9)
+    assert lib.moe_fused_forward_noalloc(ctypes.byref(args), None) == 1
+
+
 def test_fused_m0_is_noop(lib):
     args = fused_args(M=0, x=None, logits=None, y=None, workspace=None, workspace_bytes=0)
     assert lib.moe_fused_forward(ctypes.byref(args), None) == 0
