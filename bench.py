@@ -57,6 +57,8 @@ FLUSH_BYTES = 1 << 30
 # the SHA-256 of the kernel sources they were taken on.  The figure is
 # reported only while those sources are unchanged.
 DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
+SINGLE_SOURCES = ("moe_layer_align_amd/csrc/layer_small.h", "moe_layer_align_amd/csrc/gemm_decode.h",
+                  "moe_layer_align_amd/csrc/route_align.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
     "mixtral": {"src_sha256": "ad7e9e2edeb1f13c73d6cb7b97e2731285f19d4fcd87be37127a938ea0ca37a0",
@@ -101,6 +103,9 @@ def main() -> int:
                     help="fp8 workloads: one weight scale per expert instead of one per tensor")
     ap.add_argument("--shared", type=int, default=0, metavar="S",
                     help="S shared experts (every token also passes through them, weight one)")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="tiny token counts (at most 16 tokens and 64 pairs) run as one launch (tuning "
+                         "single_launch = 1) instead of the default multi-launch path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -183,10 +188,16 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
 
     router_w = gen_router_weights(cfg.E, cfg.H, 0, device=dev) if args.router_gemm else None
 
+    tuning = None
+    if args.single_launch:
+        small = lambda M: M <= 16 and M * KS <= 64 and cfg.E <= 256
+        tuning_for = {M: moe.Tuning(single_launch=1 if small(M) else 0) for M in cfg.ms}
+
     def run(c, events=None):
         moe.fused_forward(c["x"], None if args.router_gemm else c["lg"], w13, w2, cfg.k, cfg.dtype, s13_t, s2_t,
                           out=c["y"], workspace=c["ws"], expert_counts=c["counts"], stream=stream, events=events,
-                          router_w=router_w, n_shared=S)
+                          router_w=router_w, n_shared=S,
+                          tuning=tuning_for[c["M"]] if args.single_launch else tuning)
 
     def flush(i):
         if flush_buf is not None:
@@ -238,12 +249,22 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
                 run(c, handles[s][j])
         t1.record(stream)
         torch.cuda.synchronize()
-        a, b = slots
-        ms = [[evs[s][j][a].elapsed_time(evs[s][j][b]) for s in range(args.steps)] for j in range(len(calls))]
-        return ms, t0.elapsed_time(t1)
 
-    span_ms, wall_ms = timed_pass((0, 2 * ns - 1), "layer spans")
-    g1_ms, _ = timed_pass((4, 5), "gate/up launches")
+        def between(a, b):
+            return [[evs[s][j][a].elapsed_time(evs[s][j][b]) for s in range(args.steps)] for j in range(len(calls))]
+        return between, t0.elapsed_time(t1)
+
+    between, wall_ms = timed_pass((0, 2 * ns - 1), "layer spans")
+    span_ms = between(0, 2 * ns - 1)
+    # Pass B: the launches of the dominant kernels.  A call that takes the
+    # multi-launch path runs its gate/up product between events 4 and 5; one
+    # that takes the single-launch layer runs that one kernel between events 0
+    # and 1 (the library then records events 1..9 back to back after it).
+    between, _ = timed_pass((0, 1, 4, 5), "dominant-kernel launches")
+    first_ms, g1_ms = between(0, 1), between(4, 5)
+    for j, c in enumerate(calls):
+        c["single"] = cfg.name != "prefill" and statistics.median(g1_ms[j]) < 0.25 * statistics.median(first_ms[j])
+        c["kern_ms"] = first_ms[j] if c["single"] else g1_ms[j]
     layer_ms_per_step = sum(sum(v) for v in span_ms) / args.steps
 
     # Per-stage breakdown, outside the timed region (all ten events per call).
@@ -263,44 +284,73 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
     per_m = []
     for j, c in enumerate(calls):
         us = statistics.median(span_ms[j]) * 1e3
+        kern_us = statistics.median(c["kern_ms"]) * 1e3
         entry = dict(M=c["M"], us=round(us, 2), active_experts=c["active"], weight_bytes=c["w_bytes"],
                      gbps=round(c["w_bytes"] / us / 1e3, 1), hbm_frac=round(c["w_bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
-                     tflops=round(c["flops"] / us / 1e6, 2),
-                     gate_up_gbps=round(c["g1_bytes"] / (statistics.median(g1_ms[j]) * 1e3) / 1e3, 1))
+                     tflops=round(c["flops"] / us / 1e6, 2), path="single launch" if c["single"] else "multi launch")
+        if c["single"]:
+            entry["single_launch_kernel_us"] = round(kern_us, 2)
+        else:
+            entry["gate_up_gbps"] = round(c["g1_bytes"] / kern_us / 1e3, 1)
         for q, name in enumerate(moe.STAGE_NAMES):
             entry["%s_us" % name] = round(stage_ms[j][q] * 1e3, 2)
         per_m.append(entry)
 
     total_bytes = sum(c["w_bytes"] for c in calls)
     total_flops = sum(c["flops"] for c in calls)
-    g1_total_ms = sum(sum(v) for v in g1_ms)
-    n_g1 = args.steps * len(calls)
     if cfg.name == "prefill":
         value = total_flops / (layer_ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-        ach = sum(c["g1_flops"] for c in calls) * args.steps / (g1_total_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(ach, 1), peak=FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS,
-                    unit="TFLOP/s")
     else:
         value = total_bytes / (layer_ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
-        ach = sum(c["g1_bytes"] for c in calls) * args.steps / (g1_total_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s")
-    roof["frac"] = round(ach / roof["peak"], 4)
-    tr = TRAFFIC.get(cfg.name)
-    sources = PREFILL_SOURCES if cfg.name == "prefill" else DECODE_SOURCES
-    # the counters were taken on the default inputs (cold cache, given logits,
-    # per-tensor scales) of these kernel sources
-    roof["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256(sources)
-                                                 and not (args.no_flush or per_channel or per_expert
-                                                          or args.shared or args.router_gemm)) \
-        else None
-    roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
-    roof["kernel"] = ("prefill_gemm_kernel<0, *> (tiled gate/up product + SiLU*up)" if cfg.name == "prefill"
-                      else "gate/up product + SiLU*up (gemm1_decode_kernel, or gemm1_stream_kernel for fp8 "
-                           "layers whose plan takes the long-stream variant)")
-    roof["avg_launch_us"] = round(g1_total_ms * 1e3 / n_g1, 2)
-    roof["launches"] = n_g1
+
+    # Roofline of the kernel that takes the most time over the sweep: the
+    # gate/up product of the multi-launch calls (algorithmic bytes: W13 of the
+    # experts with tokens; prefill: 4*M*k*H*I flops) or the single-launch
+    # layer (bytes: W13 and W2 of those experts); the other kind, when the
+    # sweep has both, is reported beside it.
+    def roofline(single: bool):
+        sel = [c for c in calls if c["single"] == single]
+        if not sel:
+            return None
+        kern_ms = sum(sum(c["kern_ms"]) for c in sel)
+        n = args.steps * len(sel)
+        if cfg.name == "prefill":
+            ach = sum(c["g1_flops"] for c in sel) * args.steps / (kern_ms * 1e-3) / 1e12
+            r = dict(bound="mfma", achieved=round(ach, 1), peak=FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS,
+                     unit="TFLOP/s")
+        else:
+            work = sum((c["w_bytes"] if single else c["g1_bytes"]) for c in sel)
+            ach = work * args.steps / (kern_ms * 1e-3) / 1e9
+            r = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s")
+        r["frac"] = round(ach / r["peak"], 4)
+        tr = TRAFFIC.get(cfg.name + ("_single" if single else ""))
+        srcs = PREFILL_SOURCES if cfg.name == "prefill" else (SINGLE_SOURCES if single else DECODE_SOURCES)
+        # the counters were taken on the default inputs (cold cache, given
+        # logits, per-tensor scales) of these kernel sources
+        r["traffic"] = tr["bytes_per_launch"] if (tr and tr["src_sha256"] == kernel_sources_sha256(srcs)
+                                                  and not (args.no_flush or per_channel or per_expert
+                                                           or args.shared or args.router_gemm)) else None
+        r["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
+        r["kernel"] = ("prefill_gemm_kernel<0, *> (tiled gate/up product + SiLU*up)" if cfg.name == "prefill"
+                       else "layer1_kernel (the whole layer in one cooperative launch) at M = %s"
+                       % ",".join(str(c["M"]) for c in sel) if single
+                       else "gate/up product + SiLU*up (gemm1_decode_kernel, or gemm1_stream_kernel for fp8 "
+                            "layers whose plan takes the long-stream variant) at M = %s"
+                            % ",".join(str(c["M"]) for c in sel))
+        r["avg_launch_us"] = round(kern_ms * 1e3 / n, 2)
+        r["launches"] = n
+        r["kernel_ms_total"] = kern_ms
+        return r
+
+    roofs = [r for r in (roofline(False), roofline(True)) if r is not None]
+    roofs.sort(key=lambda r: -r["kernel_ms_total"])
+    for r in roofs:
+        del r["kernel_ms_total"]
+    roof = roofs[0]
+    if len(roofs) > 1:
+        roof["other_kernel"] = roofs[1]
 
     cpu = None
     if not args.no_cpu_baseline and not args.router_gemm:  # the oracle sample takes the workload's logits
@@ -331,6 +381,7 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
                               else "per tensor") if fp8 else None,
             "shared_experts": S,
             "logits_source": "computed in the layer from router weights" if args.router_gemm else "given",
+            "single_launch": "at M <= 16 with at most 64 pairs" if args.single_launch else "off",
         },
         "per_m": per_m,
         "roofline": roof,

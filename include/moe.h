@@ -164,6 +164,12 @@ typedef struct {
                                 (the last experts' and late passes' workgroups first), -1 = in order;
                                 default: reversed with shared experts, which then also take the K-split
                                 variants unless the stream fields say otherwise */
+  int32_t single_launch;     /* 1 = the whole layer in one launch (tiny token counts: at most 16 tokens
+                                and 64 pairs, at most 256 routed experts, given logits, default mode;
+                                MOE_ERR_UNSUPPORTED where it does not fit); 0 or -1 = the multi-launch
+                                path (default: on MI355X a grid barrier costs about as much as the kernel
+                                boundary it replaces).  Single-launch calls on one GPU must not overlap
+                                (they share the barrier's device counters) */
 } moe_tuning_t;
 
 /*

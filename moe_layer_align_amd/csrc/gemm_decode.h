@@ -184,9 +184,13 @@ __device__ __forceinline__ void row_deq4(const float* w_scale, int e, int rows_e
 }
 
 // Body for NB (<= NT) token tiles; the kernel picks NB from the workgroup's
-// token count so that tiles with no token issue no loads and no MFMAs.
+// token count so that tiles with no token issue no loads and no MFMAs.  bx:
+// the workgroup's group of 4/KSPLIT feature tiles.  Returns the lane's
+// largest |h| (0 in lanes that store nothing), which the caller reduces
+// when the h scale is dynamic.
 template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT, bool PC>
-__device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int e, int seg, int cnt, int pass0) {
+__device__ __forceinline__ float gemm1_body(const Gemm1Args& a, f32x4* s_red, int e, int seg, int cnt, int pass0,
+                                            int bx) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;   // k per MFMA
   constexpr int LB = FP8 ? 32 : 16;       // bytes per lane per operand per step
@@ -196,7 +200,7 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KSPLIT, tile = wave / KSPLIT;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int i0 = (blockIdx.x * TPW + tile) * 16;
+  const int i0 = (bx * TPW + tile) * 16;
   const int Kw = a.H / KSPLIT;
   const int kbeg = kpart * Kw;
 
@@ -227,7 +231,7 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
       }
     }
     __syncthreads();
-    if (kpart > 0) return;
+    if (kpart > 0) return 0.0f;
 #pragma unroll
     for (int p = 0; p < KSPLIT - 1; ++p) {
       const f32x4* src = s_red + ((p * TPW + tile) * 2 * NT) * 64 + lane;
@@ -272,10 +276,7 @@ __device__ __forceinline__ void gemm1_body(const Gemm1Args& a, f32x4* s_red, int
       }
     }
   }
-  if constexpr (HFMT == H_F32) {
-    hmax = wave_max(hmax);
-    if (lane == 0) atomicMax(a.h_amax, __float_as_uint(hmax));
-  }
+  return hmax;
 }
 
 template <bool FP8, int HFMT, int NT, int U, int KSPLIT>
@@ -291,17 +292,26 @@ static __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
   auto run = [&](auto pc_tag) {
     constexpr bool PC = decltype(pc_tag)::value;
+    const int bx = blockIdx.x;
     if constexpr (NT >= 4)
-      if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
+      if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
     if constexpr (NT >= 3)
-      if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
+      if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
     if constexpr (NT >= 2)
-      if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
-    gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0);
+      if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
+    return gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
   };
+  float hmax;
   if constexpr (FP8)
-    if (a.w_cs) return run(std::true_type{});  // one weight scale per row
-  run(std::false_type{});
+    hmax = a.w_cs ? run(std::true_type{}) : run(std::false_type{});  // one weight scale per row, or not
+  else
+    hmax = run(std::false_type{});
+  if constexpr (HFMT == H_F32) {
+    // one device-scope atomic per wave that stored h (same-address atomics
+    // serialise: an atomic from every wave cost 8-25 us on the M = 1 layers)
+    hmax = wave_max(hmax);
+    if ((threadIdx.x & 63) == 0 && hmax > 0.0f) atomicMax(a.h_amax, __float_as_uint(hmax));
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -446,7 +456,7 @@ __device__ __forceinline__ void gemm1_stream_body(const Gemm1Args& a, int e, int
   stream_tiles<FP8, NB, U, SB>(pa, 64 * rowb, pb, ntw, a.H / KSTEP / U, acc, epi);
   if constexpr (HFMT == H_F32) {
     hmax = wave_max(hmax);
-    if (lane == 0) atomicMax(a.h_amax, __float_as_uint(hmax));
+    if (lane == 0 && hmax > 0.0f) atomicMax(a.h_amax, __float_as_uint(hmax));
   }
 }
 
@@ -541,7 +551,7 @@ __device__ __forceinline__ void stage_h_e4m3(const Gemm2Args& a, uint8_t* s_tok,
 // per workgroup.
 template <bool FP8, int HFMT, int NT, int NB, int U, int WKS, bool PC>
 __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f32x4* s_red, int e, int seg, int cnt,
-                                           int pass0, int kslice) {
+                                           int pass0, int kslice, int bx) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;
   constexpr int LB = FP8 ? 32 : 16;
@@ -553,7 +563,7 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % WKS, tile = wave / WKS;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int n0 = (blockIdx.x * TPW + tile) * 32;
+  const int n0 = (bx * TPW + tile) * 32;
   const int Kw = a.I / a.ksplit;       // K range of the workgroup
   const int kbeg = kslice * Kw;
   const int Kp = Kw / WKS;             // K range of the wave
@@ -645,12 +655,15 @@ static __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   auto run = [&](auto pc_tag) {
     constexpr bool PC = decltype(pc_tag)::value;
     if constexpr (NT >= 4)
-      if (ntile == 4) return gemm2_body<FP8, HFMT, NT, 4, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+      if (ntile == 4)
+        return gemm2_body<FP8, HFMT, NT, 4, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
     if constexpr (NT >= 3)
-      if (ntile == 3) return gemm2_body<FP8, HFMT, NT, 3, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+      if (ntile == 3)
+        return gemm2_body<FP8, HFMT, NT, 3, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
     if constexpr (NT >= 2)
-      if (ntile == 2) return gemm2_body<FP8, HFMT, NT, 2, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
-    gemm2_body<FP8, HFMT, NT, 1, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice);
+      if (ntile == 2)
+        return gemm2_body<FP8, HFMT, NT, 2, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+    gemm2_body<FP8, HFMT, NT, 1, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
   };
   if constexpr (FP8)
     if (a.w_cs) return run(std::true_type{});  // one weight scale per row

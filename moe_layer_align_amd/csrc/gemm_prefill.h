@@ -619,8 +619,17 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
   }
   wait_vm<0>();  // the dummy loads after the last item
   if (MODE == 0 && HDYN) {
+    // one device-scope atomic per workgroup: same-address atomics serialise,
+    // and every workgroup finishes at about the same time
     hmax = wave_max(hmax);
-    if (lane == 0) atomicMax(a.h_amax_out, __float_as_uint(hmax));
+    __syncthreads();  // the epilogue areas are no longer read
+    float* red = (float*)(smem_raw + kPfRing);
+    if (lane == 0) red[wave] = hmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (m > 0.0f) atomicMax(a.h_amax_out, __float_as_uint(m));
+    }
   }
 }
 

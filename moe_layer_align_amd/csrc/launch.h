@@ -37,4 +37,10 @@ void launch_prefill_finalize(const uint16_t* part, const float* wts, uint16_t* y
                              const float* x_scale, const unsigned* h_amax, const float* h_scale, float* scales_out,
                              hipStream_t st);
 
+// The single-launch layer for tiny token counts (layer_small.h): a launch of
+// `grid` workgroups, refused (hipErrorInvalidConfiguration) when they could
+// not all be resident at once; otherwise the launch's own status.
+struct Layer1Args;
+hipError_t launch_layer1(bool fp8, int hf, int wks, int grid, size_t lds, hipStream_t st, const Layer1Args& a);
+
 }  // namespace moe

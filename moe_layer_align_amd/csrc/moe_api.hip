@@ -10,6 +10,7 @@
 
 #include "moe.h"
 #include "launch.h"
+#include "layer_small.h"
 #include "moe_device.h"
 #include "route_align.h"
 
@@ -82,7 +83,7 @@ int64_t align_capacity(int64_t P, int E, int B) {
 // ---------------------------------------------------------------- workspace
 struct Layout {
   size_t ids, wts, counts, offsets, sorted, block_expert, num_padded, active, num_active;
-  size_t xamax_part, scale_slot, h_amax, hist, logits, xq, h, part, total;
+  size_t xamax_part, scale_slot, h_amax, hist, logits, wg_hmax, xq, h, part, total;
   int64_t capacity;
   int block, n_blocks, n_route_wg;
 };
@@ -126,6 +127,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det =
   L.h_amax = take(4);
   L.hist = take((size_t)cdiv(M, 4 * kRouteRows) * E * 4);
   L.logits = take((size_t)M * E * 4);  // router logits computed by the layer (router_w given)
+  L.wg_hmax = take((size_t)kLayer1MaxGrid * 4);  // single-launch layer: largest |h| of each workgroup
   const bool fp8 = dt == MOE_DTYPE_FP8_E4M3;
   L.xq = take(fp8 ? (size_t)M * H : 0);
   // h: bf16 (bf16 layers), fp32 (fp8 decode), fp32 + its e4m3 copy (fp8 prefill)
@@ -360,6 +362,21 @@ moe_status_t check_shape(int M, int E, int k) {
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- single-launch layer
+// The single-launch layer's wave split of the down product (4, 2 or 1: the
+// most that divides I's K-steps), or 0 when the layer does not fit it: more
+// than 16 tokens or 64 pairs, more than 256 routed experts, a gate/up K that
+// four waves cannot split into whole MFMA k-steps, or (dynamic fp8 h scale)
+// a down-product token slice beyond the workgroup's LDS.
+int layer1_wks(int M, int Er, int k, int H, int I, bool fp8, bool hdyn) {
+  const int kstep = fp8 ? 128 : 32;
+  if (M > kLayer1Tokens || (int64_t)M * k > kLayer1Pairs || Er > kLayer1Experts) return 0;
+  if ((H / 4) % kstep != 0) return 0;
+  if (hdyn && 16 * gemm2_lds_stride(I) > kLayer1LdsMax - 24 * 1024) return 0;  // static LDS is under 24 KB
+  const int nsteps = I / kstep;
+  return nsteps % 4 == 0 ? 4 : nsteps % 2 == 0 ? 2 : 1;
+}
+
 // ---------------------------------------------------------------- no-alloc scratch
 // Workspace of moe_fused_forward_noalloc: one array per GPU, held by the
 // loaded code object until the process ends.  Its name is a host-side
@@ -400,7 +417,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 9; }
+int32_t moe_abi_version(void) { return 10; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -610,6 +627,18 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     rc = make_plan(M, E, H, I, k, S, fp8, hdyn, a->tuning, det, &plan);
     if (rc != MOE_OK) return rc;
   }
+  // the single-launch layer for tiny token counts, on request (never with
+  // router weights, whose product is a launch of its own, nor in the
+  // deterministic mode, whose K order it does not keep)
+  int l1_wks = 0;
+  if (!prefill) {
+    const int mode = a->tuning ? a->tuning->single_launch : 0;
+    if (mode < -1 || mode > 1) return MOE_ERR_UNSUPPORTED;
+    if (mode == 1) {
+      if (!det && !a->router_w) l1_wks = layer1_wks(M, Er, k, H, I, fp8, hdyn);
+      if (!l1_wks) return MOE_ERR_UNSUPPORTED;
+    }
+  }
   // the scratch array holds the partial sums of the plan's K slices only
   const Layout L = make_layout(M, E, H, I, k, a->dtype, det, noalloc && !prefill ? plan.ks2 : 0);
   uint8_t* ws = (uint8_t*)a->workspace;
@@ -659,6 +688,51 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   AlignOut o{counts, offsets, sorted, block_expert, num_padded, active, num_active, L.n_blocks};
   if (prefill)
     return prefill_forward(a, st, ev, L, ws, ids, wts, o, xamax_part, scale_slot, h_amax, xq, h, part, hdyn, S);
+  if (l1_wks) {
+    int cus = 0;
+    if ((rc = persistent_wgs(&cus)) != MOE_OK) return rc;
+    // one workgroup per item of the larger product, at most one per CU (two
+    // per CU measured slower: the barrier's cost grows with its workgroups)
+    const int64_t items = (int64_t)n_act * std::max(I / 16, H / (32 * (4 / l1_wks)));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(cus, kLayer1MaxGrid), items));
+    Layer1Args la{};
+    la.logits = a->logits;
+    la.x = (const uint16_t*)a->x;
+    la.M = M;
+    la.E = Er;
+    la.K = kr;
+    la.S = S;
+    la.H = H;
+    la.I = I;
+    la.w13 = (const uint8_t*)a->w13;
+    la.w2 = (const uint8_t*)a->w2;
+    la.w13_scale = a->w13_scale;
+    la.w2_scale = a->w2_scale;
+    la.w_cs = pc ? 1 : 0;
+    la.w_es = a->weight_scale_mode == 2 ? 1 : 0;
+    la.x_scale = a->x_scale;
+    la.h_scale = a->h_scale;
+    la.xq = xq;
+    la.h = h;
+    la.part = part;
+    la.wg_hmax = (float*)(ws + L.wg_hmax);
+    la.y = (uint16_t*)a->y;
+    la.n_blocks = L.n_blocks;
+    la.ids_out = a->topk_ids;
+    la.wts_out = a->topk_weights;
+    la.align_out = AlignOut{a->expert_counts, a->expert_offsets, a->sorted_ids, a->block_expert, a->num_padded,
+                            nullptr, nullptr, L.n_blocks};
+    la.scales_out = fp8 ? a->scales_out : nullptr;
+    const int hf1 = !fp8 ? H_BF16 : (hdyn ? H_F32 : H_E4M3);
+    rec(0);
+    const hipError_t err = launch_layer1(fp8, hf1, l1_wks, grid, hdyn ? 16 * gemm2_lds_stride(I) : 0, st, la);
+    for (int i = 1; i < 2 * MOE_NUM_STAGES; ++i) rec(i);
+    if (err != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ERR_DEVICE;
+    }
+    return launch_status();
+  }
   const bool small = P <= kSmallPairs && E <= kSmallMaxExperts && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
   if (small) {
     // 1+2. routing, align (and fp8 activation quantisation) in one workgroup

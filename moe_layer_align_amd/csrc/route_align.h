@@ -604,6 +604,13 @@ __device__ __forceinline__ void prologue_quant(const SmallQuant& q, int64_t nx, 
   *(u32x4*)(q.xq + i) = quant16_e4m3(*(const u32x4*)(q.x + i), *(const u32x4*)(q.x + i + 8), r);
 }
 
+// LDS of the one-wave align alone (wave_align).
+struct WaveAlignLds {
+  int tot[kMaxExperts];
+  int off[kMaxExperts + 1];
+  int act[kMaxExperts + 1];
+};
+
 // LDS of the one-workgroup align.
 struct SmallAlignLds {
   int wc[16][kMaxExperts];  // per (wave, expert): group size, then start within the expert
@@ -690,8 +697,9 @@ __device__ __forceinline__ void small_align(const int* s_ids, int P, int E, int 
 // the wave's own LDS, so no workgroup barrier follows the routing barrier.
 // The outputs are those of small_align bit for bit.  Requires ids[0..P) in
 // LDS before a barrier.
+template <class Lds>  // SmallAlignLds, or any LDS struct with the same tot, off and act arrays
 __device__ __forceinline__ void wave_align(const int* s_ids, int P, int E, int log2B, int id_bits, const AlignOut& o,
-                                           SmallAlignLds& L) {
+                                           Lds& L) {
   const int lane = threadIdx.x & 63;
   const int B = 1 << log2B;
   const bool valid = lane < P;

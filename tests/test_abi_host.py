@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 9
+    assert lib.moe_abi_version() == 10
 
 
 def capacity_formula(M, k, E, B):
@@ -200,7 +200,8 @@ def test_router_logits_validation(lib):
 def test_fused_tuning_validation(lib):
     import moe_layer_align_amd as m
     for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17),
-              m.Tuning(gemm2_wave_ksplit=3), m.Tuning(reverse_order=2)):
+              m.Tuning(gemm2_wave_ksplit=3), m.Tuning(reverse_order=2), m.Tuning(single_launch=2),
+              m.Tuning(single_launch=-2)):
         args = fused_args(tuning=ctypes.pointer(t))
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 
@@ -225,6 +226,19 @@ def test_fused_noalloc_validation(lib):
     assert lib.moe_fused_forward_noalloc(ctypes.byref(args), None) == 2
     args = fused_args(workspace=None, workspace_bytes=0, top_k=9)
     assert lib.moe_fused_forward_noalloc(ctypes.byref(args), None) == 1
+
+
+def test_fused_single_launch_required_where_it_does_not_fit(lib):
+    import moe_layer_align_amd as m
+    t = m.Tuning(single_launch=1)
+    for kw in (dict(M=17), dict(M=40, top_k=2), dict(M=8, top_k=9, E=16), dict(E=300, top_k=2, M=2)):
+        args = fused_args(tuning=ctypes.pointer(t), **kw)
+        assert lib.moe_fused_forward(ctypes.byref(args), None) == 2, kw
+    # never with router weights or in the deterministic mode
+    args = fused_args(tuning=ctypes.pointer(t), logits=None, router_w=FAKE)
+    assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
+    args = fused_args(tuning=ctypes.pointer(t), deterministic=1)
+    assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 
 
 def test_fused_m0_is_noop(lib):

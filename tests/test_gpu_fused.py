@@ -142,7 +142,7 @@ def test_bf16_batch_invariance_with_fixed_splits():
     # at two positions of batches of 17 and 64 other tokens, gives the same bits.
     cfg = cfg_of("bf16", 8, 2, 512, 384)
     w13, w2, _, _ = gen_weights(cfg, 9, device=DEV)
-    t = moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=3, gemm2_wave_ksplit=4, token_tiles=2)
+    t = moe.Tuning(gemm1_ksplit=4, gemm2_ksplit=3, gemm2_wave_ksplit=4, token_tiles=2, single_launch=-1)
     x1 = gen_x(cfg.H, 1, 9, sub=1)
     lg1 = gen_logits(cfg, 1, 9, sub=1)
     y1 = moe.fused_forward(x1.to(DEV), lg1.to(DEV), w13, w2, cfg.k, tuning=t)
@@ -156,10 +156,73 @@ def test_bf16_batch_invariance_with_fixed_splits():
         assert torch.equal(y[pos], y1[0]), (M, pos)
 
 
+# ---------------------------------------------------------------- the single-launch layer
+# At most 16 tokens and 64 pairs the layer can run as one launch (tuning
+# single_launch = 1, which fails rather than falls back where it does not
+# fit); the default (0) and -1 take the multi-launch path, which the cases
+# below also run at the same sizes.
+ONE = moe.Tuning(single_launch=1)
+MULTI = moe.Tuning(single_launch=-1)
+
+
+@pytest.mark.parametrize("dtype,xs,hs", [("bf16", None, None), ("fp8", None, None), ("fp8", 0.02, 0.02)])
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("path", ["single", "multi"])
+def test_small_layer_both_paths(dtype, xs, hs, M, path):
+    cfg = cfg_of(dtype, 6, 2, 512, 384)
+    compare(cfg, M, seed=60 + M, x_scale=xs, h_scale=hs, tuning=ONE if path == "single" else MULTI)
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_single_launch_shared_experts(S):
+    for dtype, xs, hs in (("bf16", None, None), ("fp8", None, None), ("fp8", 0.02, 0.004)):
+        compare(cfg_of(dtype, 6, 2, 512, 384), 7, seed=61 + S, x_scale=xs, h_scale=hs, n_shared=S, tuning=ONE)
+
+
+def test_single_launch_weight_scale_modes():
+    cfg = cfg_of("fp8", 16, 4, 512, 384)
+    compare(cfg, 9, seed=62, weights=gen_weights_per_channel(cfg, 62, device=DEV), tuning=ONE)
+    compare(cfg, 9, seed=63, weights=gen_weights_per_expert(cfg, 63, device=DEV), tuning=ONE)
+    compare(cfg, 9, seed=63, weights=gen_weights_per_expert(cfg, 63, device=DEV), tuning=ONE, x_scale=0.015,
+            h_scale=0.004)
+
+
+def test_single_launch_down_wave_splits():
+    # I of 3, 2 and 4 fp8 K-steps: the down product split over 1, 2 and 4 waves
+    for I in (384, 256, 512):
+        compare(cfg_of("fp8", 8, 2, 512, I), 6, seed=64 + I, tuning=ONE)
+
+
+def test_single_launch_refused_where_it_does_not_fit():
+    cfg = cfg_of("bf16", 8, 2, 256, 256)
+    w13, w2, _, _ = gen_weights(cfg, 65, device=DEV)
+    for M in (17, 40):  # more than 16 tokens, more than 64 pairs
+        x = gen_x(cfg.H, M, 65, sub=M).to(DEV)
+        lg = gen_logits(cfg, M, 65, sub=M).to(DEV)
+        with pytest.raises(moe.MoEError) as e:
+            moe.fused_forward(x, lg, w13, w2, cfg.k, tuning=ONE)
+        assert e.value.code == 2
+
+
+def test_single_launch_repeat_calls_bitwise():
+    cfg = cfg_of("fp8", 16, 4, 512, 256)
+    w = gen_weights(cfg, 66, device=DEV)
+    x = gen_x(cfg.H, 12, 66, sub=12).to(DEV)
+    lg = gen_logits(cfg, 12, 66, sub=12).to(DEV)
+    ws = torch.empty(moe.workspace_size(12, 16, 512, 256, 4, "fp8"), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xFF)  # stale contents must not matter
+    s13, s2 = torch.tensor([w[2]], device=DEV), torch.tensor([w[3]], device=DEV)
+    ys = [moe.fused_forward(x, lg, w[0], w[1], 4, "fp8", s13, s2, workspace=ws, tuning=ONE).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+
+
 # ---------------------------------------------------------------- the workloads
 def test_tiny():
     cfg = CONFIGS["tiny"]
     compare(cfg, 4, seed=0)
+    compare(cfg, 4, seed=0, tuning=ONE)
 
 
 @pytest.fixture(scope="module")
@@ -173,6 +236,8 @@ def mixtral_w():
 @pytest.mark.parametrize("M", CONFIGS["mixtral"].ms)
 def test_mixtral(mixtral_w, M):
     compare(CONFIGS["mixtral"], M, seed=0, weights=mixtral_w)
+    if M <= 16:  # the single-launch layer too
+        compare(CONFIGS["mixtral"], M, seed=0, weights=mixtral_w, tuning=ONE)
 
 
 @pytest.fixture(scope="module")
@@ -188,6 +253,12 @@ def test_qwen3(qwen3_w, M):
     compare(CONFIGS["qwen3"], M, seed=0, weights=qwen3_w)
 
 
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_qwen3_single_launch(qwen3_w, M):
+    compare(CONFIGS["qwen3"], M, seed=0, weights=qwen3_w, tuning=ONE)
+    compare(CONFIGS["qwen3"], M, seed=0, weights=qwen3_w, tuning=ONE, x_scale=0.02, h_scale=0.01)
+
+
 @pytest.fixture(scope="module")
 def deepseek_w():
     w = gen_weights(CONFIGS["deepseek"], 0, device=DEV)
@@ -199,6 +270,11 @@ def deepseek_w():
 @pytest.mark.parametrize("M", CONFIGS["deepseek"].ms)
 def test_deepseek(deepseek_w, M):
     compare(CONFIGS["deepseek"], M, seed=0, weights=deepseek_w)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_deepseek_single_launch(deepseek_w, M):
+    compare(CONFIGS["deepseek"], M, seed=0, weights=deepseek_w, tuning=ONE)
 
 
 @pytest.fixture(scope="module")
@@ -348,8 +424,9 @@ def test_fused_with_router_weights(cfg, M):
     ref_ids, _ = oracle.route(lg, cfg.k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     e, _, _ = compare(cfg, M, seed=24, weights=w, logits=lg, x=x)
-    # the same layer on the given logits gives the same bits
-    y2 = moe.fused_forward(x.to(DEV), lo, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]))
+    # the same layer on the given logits gives the same bits (on the same
+    # path: with router weights the layer never takes the single launch)
+    y2 = moe.fused_forward(x.to(DEV), lo, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]), tuning=MULTI)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
 
@@ -367,7 +444,7 @@ def test_router_weights_with_per_channel_scales(M):
     y = moe.fused_forward(x.to(DEV), None, w[0], w[1], cfg.k, "fp8", w[2], w[3], x_scale=xs, router_w=wg.to(DEV),
                           logits_out=lo)
     torch.cuda.synchronize()
-    _, gpu, _ = compare(cfg, M, seed=25, weights=w, logits=lo.cpu(), x=x, x_scale=0.013)
+    _, gpu, _ = compare(cfg, M, seed=25, weights=w, logits=lo.cpu(), x=x, x_scale=0.013, tuning=MULTI)
     assert torch.equal(y.float().cpu(), torch.from_numpy(gpu["y"]).float())
 
 
