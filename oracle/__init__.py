@@ -64,10 +64,13 @@ class _LayerArgs(ctypes.Structure):
         ("w13_scale_rows", ctypes.c_void_p),
         ("w2_scale_rows", ctypes.c_void_p),
         ("n_shared", ctypes.c_int32),
+        ("block_scaled", ctypes.c_int32),
+        ("w13_block", ctypes.c_void_p),
+        ("w2_block", ctypes.c_void_p),
     ]
 
 
-_ABI = 4  # oracle_abi_version() of moe_oracle.c that this binding matches
+_ABI = 5  # oracle_abi_version() of moe_oracle.c that this binding matches
 
 
 def _load():
@@ -91,6 +94,10 @@ def _load():
     lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
     lib.oracle_scale_from_amax.restype = ctypes.c_float
     lib.oracle_scale_from_amax.argtypes = [ctypes.c_float]
+    lib.oracle_e8m0_value.restype = ctypes.c_double
+    lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_block_quant.restype = ctypes.c_uint8
+    lib.oracle_block_quant.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.oracle_route.restype = ctypes.c_int
     lib.oracle_route.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_void_p]
@@ -147,6 +154,23 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
 def e4m3_decode(c: np.ndarray) -> np.ndarray:
     lib = _load()
     return np.array([lib.oracle_e4m3_decode(int(a)) for a in np.ravel(c)], dtype=np.float64)
+
+
+def e8m0_value(c: int) -> float:
+    """Value of an E8M0 scale code: 2^(c-127) (NaN for 255)."""
+    return float(_load().oracle_e8m0_value(int(c)))
+
+
+def block_quant(v: np.ndarray):
+    """Block quantisation of up to 128 fp32 values sharing one power-of-two
+    scale (oracle_block_quant): returns (e4m3 codes uint8 [n], scale code)."""
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    if not 1 <= v.size <= 128:
+        raise ValueError("a block holds 1..128 values")
+    codes = np.zeros(v.size, dtype=np.uint8)
+    c = lib.oracle_block_quant(_ptr(v), v.size, _ptr(codes))
+    return codes, int(c)
 
 
 def num_threads() -> int:
@@ -219,7 +243,7 @@ def router_logits(x, w) -> np.ndarray:
 def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = None,
           w2_scale: Optional[float] = None, x_scale: Optional[float] = None, h_scale: Optional[float] = None,
           tokens: Optional[Sequence[int]] = None, experts: Optional[dict] = None, all_pairs_h: Optional[bool] = None,
-          n_shared: int = 0):
+          n_shared: int = 0, w13_block=None, w2_block=None):
     """Reference output of the layer.
 
     x: bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] / w2 [E,H,I] (bf16 or e4m3
@@ -230,6 +254,10 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
     scales, None = dynamic amax/448.  tokens: rows of y to produce (default all).
     n_shared: shared experts stacked after the E routed ones (w13 [E+n_shared,2I,H],
     per-row scales [E+n_shared,..]); every token passes through each with weight one.
+    w13_block/w2_block (fp8, block-scaled mode, instead of w13_scale/w2_scale):
+    uint8 E8M0 codes [E+n_shared, 2I/128, H/128] and [E+n_shared, H/128, I/128],
+    one per 128 x 128 weight block; activations are then quantised per 128
+    elements (block_quant) and s_x, s_h are reported as 0.
     Returns dict(y=float64 [T,H], ids, weights, s_x, s_h).
     """
     lib = _load()
@@ -274,7 +302,7 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
     sx = np.zeros(1, dtype=np.float32)
     sh = np.zeros(1, dtype=np.float32)
     if all_pairs_h is None:
-        all_pairs_h = fp8 and h_scale is None
+        all_pairs_h = fp8 and h_scale is None and w13_block is None
 
     def scale_rows(sc, rows):
         # one scale per weight row: E pointers to that expert's fp32 row scales;
@@ -291,8 +319,23 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
         keep.append(ptrs)
         return ctypes.cast(ptrs, ctypes.c_void_p)
 
-    rows13 = scale_rows(w13_scale, 2 * I) if fp8 else None
-    rows2 = scale_rows(w2_scale, H) if fp8 else None
+    blk = w13_block is not None
+    if blk != (w2_block is not None) or (blk and not fp8):
+        raise ValueError("block scales need both w13_block and w2_block, in fp8 mode")
+    rows13 = scale_rows(w13_scale, 2 * I) if fp8 and not blk else None
+    rows2 = scale_rows(w2_scale, H) if fp8 and not blk else None
+
+    def block_ptrs(b, shape):
+        arr = np.ascontiguousarray(_np(b), dtype=np.uint8)
+        if arr.shape != (EW,) + shape:
+            raise ValueError("block scales must have shape %s, got %s" % ((EW,) + shape, arr.shape))
+        keep.append(arr)
+        ptrs = (ctypes.c_void_p * EW)(*[arr[e].ctypes.data for e in range(EW)])
+        keep.append(ptrs)
+        return ctypes.cast(ptrs, ctypes.c_void_p)
+
+    b13 = block_ptrs(w13_block, (2 * I // 128, H // 128)) if blk else None
+    b2 = block_ptrs(w2_block, (H // 128, I // 128)) if blk else None
     args = _LayerArgs(
         M=M, E=E, H=H, I=I, k=k, dtype=DTYPE_E4M3 if fp8 else DTYPE_BF16,
         x=_ptr(xa), logits=_ptr(lg),
@@ -304,6 +347,7 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
         y=_ptr(y) if y.size else None, ids=_ptr(ids) if ids.size else None, weights=_ptr(w) if w.size else None,
         s_x_out=_ptr(sx), s_h_out=_ptr(sh), all_pairs_h=int(bool(all_pairs_h)),
         w13_scale_rows=rows13, w2_scale_rows=rows2, n_shared=int(n_shared),
+        block_scaled=int(blk), w13_block=b13, w2_block=b2,
     )
     rc = lib.oracle_layer(ctypes.byref(args))
     if rc:

@@ -30,7 +30,11 @@
  * and alignment, closed forms for the softmax weights, the E=1/k=1 case
  * against a float64 library matmul, the all-equal-logit case against the mean
  * of expert outputs, the e4m3/bf16 codecs against the framework's casts, and
- * hand-derived fixtures in tests/golden/.
+ * hand-derived fixtures in tests/golden/.  Block-scaled mode: block
+ * quantisation by brute force over all E4M3 codes and by its exponent window
+ * and shift invariance, the E=1/k=1 layer against float64 library matmuls of
+ * the dequantised operands, and per-token independence (tests/
+ * test_oracle_block.py).
  */
 #include <math.h>
 #include <stdint.h>
@@ -116,6 +120,35 @@ uint8_t oracle_e4m3_encode(float f) {
 float oracle_scale_from_amax(float amax) {
   if (!(amax > 0.0f)) return 1.0f;
   return amax / 448.0f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-scaled FP8: power-of-two scales per block                           */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an E8M0 scale code (OCP MX scale format: 2^(c-127); 255 is NaN). */
+double oracle_e8m0_value(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
+
+/* Block quantisation of n consecutive fp32 values (n <= 128) sharing one
+ * scale, the OCP MX rule for an E4M3 element format: the shared exponent is
+ * floor(log2(amax)) minus 8, the exponent of the format's largest power of
+ * two (448 = 1.75 * 2^8), clamped to the code range; each element is
+ * divided by the scale and rounded to E4M3 (nearest even, saturating at 448).
+ * With amax read as a biased binary32 exponent field f, the scale code is
+ * max(f - 8, 0) (the smallest scale, 2^-127, for amax below 2^-118: zero,
+ * subnormal or tiny blocks).  Dividing by a power of two is exact here: the
+ * quotients stay below 512.  Returns the scale code. */
+uint8_t oracle_block_quant(const float* v, int n, uint8_t* codes) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i)
+    if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+  uint32_t bits;
+  memcpy(&bits, &amax, sizeof bits);
+  const int f = (int)((bits >> 23) & 0xff);
+  const int c = f > 8 ? f - 8 : 0;
+  const float r = ldexpf(1.0f, 127 - c); /* 1/scale, a power of two between 2^-119 and 2^127 */
+  for (int i = 0; i < n; ++i) codes[i] = oracle_e4m3_encode(v[i] * r);
+  return (uint8_t)c;
 }
 
 /* Quantise an fp32 value with the fp32 reciprocal of the scale. */
@@ -243,6 +276,15 @@ typedef struct {
   /* shared experts: every token also passes through experts E..E+n_shared-1
    * (entries E.. of w13/w2 and of the row-scale arrays) with weight one */
   int32_t n_shared;
+  /* fp8, block-scaled mode (1) instead of the scales above: weights carry one
+   * power-of-two scale per 128 x 128 block (E pointers to uint8 E8M0 codes,
+   * [2I/128][H/128] for W13[e], [H/128][I/128] for W2[e]); activations are
+   * quantised per 128 consecutive elements of a token's x row or of a
+   * pair's h row, each group with its own power-of-two scale
+   * (oracle_block_quant).  H and I multiples of 128. */
+  int32_t block_scaled;
+  const uint8_t* const* w13_block;
+  const uint8_t* const* w2_block;
 } oracle_layer_args;
 
 /* e4m3 code -> value, filled from oracle_e4m3_decode before any parallel
@@ -262,6 +304,15 @@ static double weight_at(int32_t dtype, const void* base, int64_t idx) {
 
 static double silu(double g) { return g / (1.0 + exp(-g)); }
 
+/* Power-of-two scale of element (row, col) of W13[e] / W2[e] in block mode:
+ * the code of its 128 x 128 block. */
+static double w13_block_of(const oracle_layer_args* A, int32_t e, int64_t row, int64_t col) {
+  return oracle_e8m0_value(A->w13_block[e][(row / 128) * (A->H / 128) + col / 128]);
+}
+static double w2_block_of(const oracle_layer_args* A, int32_t e, int64_t row, int64_t col) {
+  return oracle_e8m0_value(A->w2_block[e][(row / 128) * (A->I / 128) + col / 128]);
+}
+
 /* Weight scale of row `row` of W13[e] / W2[e]: its own, or the tensor's. */
 static double w13_scale_of(const oracle_layer_args* A, int32_t e, int64_t row) {
   return A->w13_scale_rows ? (double)A->w13_scale_rows[e][row] : (double)A->w13_scale;
@@ -280,6 +331,13 @@ static void expert_up(const oracle_layer_args* A, int32_t e, const double* a, do
   int64_t H = A->H, I = A->I;
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
+    if (A->block_scaled) { /* a holds dequantised activations; each weight times its block's scale */
+      for (int64_t t = 0; t < H; ++t) g += a[t] * (weight_at(A->dtype, w, n * H + t) * w13_block_of(A, e, n, t));
+      for (int64_t t = 0; t < H; ++t)
+        u += a[t] * (weight_at(A->dtype, w, (I + n) * H + t) * w13_block_of(A, e, I + n, t));
+      h[n] = (float)(silu(g) * u);
+      continue;
+    }
     for (int64_t t = 0; t < H; ++t) g += a[t] * weight_at(A->dtype, w, n * H + t);
     for (int64_t t = 0; t < H; ++t) u += a[t] * weight_at(A->dtype, w, (I + n) * H + t);
     if (fp8) {
@@ -296,6 +354,8 @@ int oracle_layer(oracle_layer_args* A) {
   if (M < 0 || E < 1 || k < 1 || k > E || H < 1 || I < 1 || S < 0) return ORC_ERR_ARG;
   if (A->dtype != ORC_DTYPE_BF16 && A->dtype != ORC_DTYPE_E4M3) return ORC_ERR_ARG;
   const int fp8 = A->dtype == ORC_DTYPE_E4M3;
+  const int blk = A->block_scaled != 0;
+  if (blk && (!fp8 || H % 128 || I % 128 || !A->w13_block || !A->w2_block)) return ORC_ERR_ARG;
   fill_e4m3_value();
 
   int rc = oracle_route(A->logits, M, E, k, A->ids, A->weights);
@@ -338,9 +398,21 @@ int oracle_layer(oracle_layer_args* A) {
     }
   }
 
-  /* activation operand of the first product */
+  for (int64_t p = 0; blk && p < P; ++p) {
+    if (need[p] && (A->w13_block[pid[p]] == NULL || A->w2_block[pid[p]] == NULL)) {
+      free(need);
+      free(pid);
+      free(pw);
+      return ORC_ERR_MISSING_EXPERT;
+    }
+  }
+
+  /* activation operand of the first product (block mode: per 128-element
+   * group of the token's row, below) */
   float s_x = 1.0f;
-  if (fp8) {
+  if (blk) {
+    if (A->s_x_out) *A->s_x_out = 0.0f;
+  } else if (fp8) {
     if (A->x_scale_static) {
       s_x = A->x_scale;
     } else {
@@ -364,18 +436,31 @@ int oracle_layer(oracle_layer_args* A) {
     for (int64_t p = 0; p < P; ++p) {
       if (!need[p]) continue;
       int64_t m = p / kk;
-      for (int64_t t = 0; t < H; ++t) {
-        float xv = (float)oracle_bf16_decode(A->x[m * H + t]);
-        a[t] = fp8 ? oracle_e4m3_decode(quant_e4m3(xv, r_x)) : (double)xv;
+      if (blk) {
+        float v[128];
+        uint8_t q[128];
+        for (int64_t g = 0; g < H; g += 128) {
+          for (int i = 0; i < 128; ++i) v[i] = (float)oracle_bf16_decode(A->x[m * H + g + i]);
+          const double sc = oracle_e8m0_value(oracle_block_quant(v, 128, q));
+          for (int i = 0; i < 128; ++i) a[g + i] = oracle_e4m3_decode(q[i]) * sc;
+        }
+      } else {
+        for (int64_t t = 0; t < H; ++t) {
+          float xv = (float)oracle_bf16_decode(A->x[m * H + t]);
+          a[t] = fp8 ? oracle_e4m3_decode(quant_e4m3(xv, r_x)) : (double)xv;
+        }
       }
       expert_up(A, pid[p], a, (double)s_x, h + p * (int64_t)I);
     }
     free(a);
   }
 
-  /* activation operand of the second product */
+  /* activation operand of the second product (block mode: per 128-element
+   * group of each pair's h row) */
   float s_h = 1.0f;
-  if (fp8) {
+  if (blk) {
+    if (A->s_h_out) *A->s_h_out = 0.0f;
+  } else if (fp8) {
     if (A->h_scale_static) {
       s_h = A->h_scale;
     } else {
@@ -396,6 +481,14 @@ int oracle_layer(oracle_layer_args* A) {
   double* hq = (double*)malloc(sizeof(double) * (size_t)P * (size_t)I);
   for (int64_t p = 0; p < P; ++p) {
     if (!need[p]) continue;
+    if (blk) {
+      uint8_t q[128];
+      for (int64_t g = 0; g < I; g += 128) {
+        const double sc = oracle_e8m0_value(oracle_block_quant(h + p * I + g, 128, q));
+        for (int i = 0; i < 128; ++i) hq[p * I + g + i] = oracle_e4m3_decode(q[i]) * sc;
+      }
+      continue;
+    }
     for (int64_t n = 0; n < I; ++n) {
       float v = h[p * I + n];
       hq[p * I + n] = fp8 ? oracle_e4m3_decode(quant_e4m3(v, r_h)) : oracle_bf16_decode(oracle_bf16_encode(v));
@@ -412,8 +505,13 @@ int oracle_layer(oracle_layer_args* A) {
         int64_t p = m * kk + j;
         const void* w = A->w2[pid[p]];
         double o = 0.0;
-        for (int64_t t = 0; t < I; ++t) o += hq[p * I + t] * weight_at(A->dtype, w, n * (int64_t)I + t);
-        if (fp8) o *= (double)s_h * w2_scale_of(A, pid[p], n);
+        if (blk) {
+          for (int64_t t = 0; t < I; ++t)
+            o += hq[p * I + t] * (weight_at(A->dtype, w, n * (int64_t)I + t) * w2_block_of(A, pid[p], n, t));
+        } else {
+          for (int64_t t = 0; t < I; ++t) o += hq[p * I + t] * weight_at(A->dtype, w, n * (int64_t)I + t);
+          if (fp8) o *= (double)s_h * w2_scale_of(A, pid[p], n);
+        }
         acc += pw[p] * o;
       }
       A->y[i * H + n] = acc;
@@ -454,4 +552,4 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 int oracle_num_threads(void) { return 1; }
 #endif
 
-int oracle_abi_version(void) { return 4; }
+int oracle_abi_version(void) { return 5; }

@@ -46,7 +46,12 @@ typedef struct {
   const float* const* w13_scale_rows;
   const float* const* w2_scale_rows;
   int32_t n_shared;
+  int32_t block_scaled;
+  const uint8_t* const* w13_block;
+  const uint8_t* const* w2_block;
 } layer_args;
+uint8_t oracle_block_quant(const float* v, int n, uint8_t* codes);
+double oracle_e8m0_value(uint8_t c);
 int oracle_layer(layer_args* A);
 
 static int failures = 0;
@@ -116,8 +121,8 @@ static void routing_and_align(void) {
   free(lg);
 }
 
-static void layer(int fp8, int xs, int hs, int rows, int S, int subset) {
-  const int M = 9, E = 5, H = 32, I = 48, k = 2, EW = E + S;
+static void layer(int fp8, int xs, int hs, int rows, int S, int subset, int blk) {
+  const int M = 9, E = 5, H = blk ? 256 : 32, I = blk ? 128 : 48, k = 2, EW = E + S;
   uint16_t* x = malloc(sizeof(uint16_t) * M * H);
   float* lg = malloc(sizeof(float) * M * E);
   for (int i = 0; i < M * H; ++i) x[i] = oracle_bf16_encode(normal());
@@ -126,6 +131,8 @@ static void layer(int fp8, int xs, int hs, int rows, int S, int subset) {
   void* w2[8];
   float* r13[8];
   float* r2[8];
+  uint8_t* b13[8];
+  uint8_t* b2[8];
   for (int e = 0; e < EW; ++e) {
     const size_t n13 = (size_t)2 * I * H, n2 = (size_t)H * I, esz = fp8 ? 1 : 2;
     w13[e] = malloc(n13 * esz);
@@ -144,6 +151,10 @@ static void layer(int fp8, int xs, int hs, int rows, int S, int subset) {
     r2[e] = malloc(sizeof(float) * H);
     for (int i = 0; i < 2 * I; ++i) r13[e][i] = 0.01f * (1 + i % 3);
     for (int i = 0; i < H; ++i) r2[e][i] = 0.01f * (1 + i % 4);
+    b13[e] = malloc((size_t)(2 * I / 128) * (H / 128) + 1);
+    b2[e] = malloc((size_t)(H / 128) * (I / 128) + 1);
+    for (int i = 0; i < (2 * I / 128) * (H / 128); ++i) b13[e][i] = (uint8_t)(118 + i % 5);
+    for (int i = 0; i < (H / 128) * (I / 128); ++i) b2[e][i] = (uint8_t)(119 + i % 3);
   }
   int64_t tokens[9];
   int64_t nt = 0;
@@ -163,6 +174,9 @@ static void layer(int fp8, int xs, int hs, int rows, int S, int subset) {
   A.w13_scale_rows = rows ? (const float* const*)r13 : NULL;
   A.w2_scale_rows = rows ? (const float* const*)r2 : NULL;
   A.n_shared = S;
+  A.block_scaled = blk;
+  A.w13_block = (const uint8_t* const*)b13;
+  A.w2_block = (const uint8_t* const*)b2;
   CHECK(oracle_layer(&A) == 0);
   for (int64_t i = 0; i < nt * H; ++i) CHECK(isfinite(y[i]));
   /* a missing expert is reported, not dereferenced */
@@ -180,6 +194,8 @@ static void layer(int fp8, int xs, int hs, int rows, int S, int subset) {
     free(w2[e]);
     free(r13[e]);
     free(r2[e]);
+    free(b13[e]);
+    free(b2[e]);
   }
   free(x);
   free(lg);
@@ -210,8 +226,19 @@ int main(void) {
           for (int S = 0; S < 3; S += 2)
             for (int subset = 0; subset < 2; ++subset) {
               if (!fp8 && (xs || hs || rows)) continue;
-              layer(fp8, xs, hs, rows, S, subset);
+              layer(fp8, xs, hs, rows, S, subset, 0);
             }
+  for (int S = 0; S < 3; S += 2)
+    for (int subset = 0; subset < 2; ++subset) layer(1, 0, 0, 0, S, subset, 1);
+  {
+    float v[128];
+    uint8_t q[128];
+    for (int i = 0; i < 128; ++i) v[i] = normal() * 1e-39f;
+    (void)oracle_block_quant(v, 128, q);
+    for (int i = 0; i < 128; ++i) v[i] = normal() * 1e30f;
+    (void)oracle_block_quant(v, 128, q);
+    for (int c = 0; c < 256; ++c) (void)oracle_e8m0_value((uint8_t)c);
+  }
   router();
   if (failures) {
     fprintf(stderr, "%d checks failed\n", failures);
