@@ -67,11 +67,10 @@ class _LayerArgs(ctypes.Structure):
         ("block_scaled", ctypes.c_int32),
         ("w13_block", ctypes.c_void_p),
         ("w2_block", ctypes.c_void_p),
-        ("h_margin", ctypes.c_void_p),
     ]
 
 
-_ABI = 6  # oracle_abi_version() of moe_oracle.c that this binding matches
+_ABI = 5  # oracle_abi_version() of moe_oracle.c that this binding matches
 
 
 def _load():
@@ -97,8 +96,6 @@ def _load():
     lib.oracle_scale_from_amax.argtypes = [ctypes.c_float]
     lib.oracle_e8m0_value.restype = ctypes.c_double
     lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
-    lib.oracle_pow2_margin.restype = ctypes.c_double
-    lib.oracle_pow2_margin.argtypes = [ctypes.c_float]
     lib.oracle_block_quant.restype = ctypes.c_uint8
     lib.oracle_block_quant.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.oracle_route.restype = ctypes.c_int
@@ -162,12 +159,6 @@ def e4m3_decode(c: np.ndarray) -> np.ndarray:
 def e8m0_value(c: int) -> float:
     """Value of an E8M0 scale code: 2^(c-127) (NaN for 255)."""
     return float(_load().oracle_e8m0_value(int(c)))
-
-
-def pow2_margin(amax: float) -> float:
-    """Distance of amax from the nearest power of two in log2 units, in [0, 1/2]
-    (1 for zero or non-finite): where a block's scale code changes."""
-    return float(_load().oracle_pow2_margin(float(amax)))
 
 
 def block_quant(v: np.ndarray):
@@ -266,10 +257,8 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
     w13_block/w2_block (fp8, block-scaled mode, instead of w13_scale/w2_scale):
     uint8 E8M0 codes [E+n_shared, 2I/128, H/128] and [E+n_shared, H/128, I/128],
     one per 128 x 128 weight block; activations are then quantised per 128
-    elements (block_quant) and s_x, s_h are reported as 0, and the result
-    also holds h_margin, float64 [M, k+n_shared]: per pair the smallest
-    pow2_margin of its h groups' amax (1 where h was not evaluated).
-    Returns dict(y=float64 [T,H], ids, weights, s_x, s_h[, h_margin]).
+    elements (block_quant) and s_x, s_h are reported as 0.
+    Returns dict(y=float64 [T,H], ids, weights, s_x, s_h).
     """
     lib = _load()
     xa = _np(x)
@@ -345,7 +334,6 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
         keep.append(ptrs)
         return ctypes.cast(ptrs, ctypes.c_void_p)
 
-    margin = np.ones((M, k + n_shared), dtype=np.float64) if blk else None
     b13 = block_ptrs(w13_block, (2 * I // 128, H // 128)) if blk else None
     b2 = block_ptrs(w2_block, (H // 128, I // 128)) if blk else None
     args = _LayerArgs(
@@ -360,12 +348,8 @@ def layer(x, logits, w13, w2, k: int, dtype: str, w13_scale: Optional[float] = N
         s_x_out=_ptr(sx), s_h_out=_ptr(sh), all_pairs_h=int(bool(all_pairs_h)),
         w13_scale_rows=rows13, w2_scale_rows=rows2, n_shared=int(n_shared),
         block_scaled=int(blk), w13_block=b13, w2_block=b2,
-        h_margin=_ptr(margin) if blk and margin.size else None,
     )
     rc = lib.oracle_layer(ctypes.byref(args))
     if rc:
         raise ValueError("oracle_layer failed with code %d" % rc)
-    out = dict(y=y, ids=ids, weights=w, s_x=float(sx[0]), s_h=float(sh[0]))
-    if blk:
-        out["h_margin"] = margin
-    return out
+    return dict(y=y, ids=ids, weights=w, s_x=float(sx[0]), s_h=float(sh[0]))

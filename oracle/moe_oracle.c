@@ -151,19 +151,6 @@ uint8_t oracle_block_quant(const float* v, int n, uint8_t* codes) {
   return (uint8_t)c;
 }
 
-/* Distance, in binary orders of magnitude, from amax to the nearest power of
- * two: min(d, 1 - d) for d the fractional part of log2(amax), in [0, 1/2];
- * 1 for amax zero or not finite.  The block scale code (oracle_block_quant)
- * changes exactly where amax crosses a power of two, and with it the step of
- * every element of the block and whether the largest one saturates at 448: a
- * small margin marks a block whose code rests on the last bits of amax. */
-double oracle_pow2_margin(float amax) {
-  if (!(amax > 0.0f) || !isfinite(amax)) return 1.0;
-  const double l = log2((double)amax);
-  const double d = l - floor(l);
-  return d < 1.0 - d ? d : 1.0 - d;
-}
-
 /* Quantise an fp32 value with the fp32 reciprocal of the scale. */
 static uint8_t quant_e4m3(float v, float recip) {
   float t = v * recip; /* fp32 product, rounded once */
@@ -298,12 +285,6 @@ typedef struct {
   int32_t block_scaled;
   const uint8_t* const* w13_block;
   const uint8_t* const* w2_block;
-  /* block mode out (may be NULL): [M*(k+n_shared)], per pair the smallest
-   * oracle_pow2_margin over the 128-element groups of its h row (1 for pairs
-   * whose h was not evaluated).  A group near a power of two is one whose
-   * scale code an fp32 h computed in another summation order may take one
-   * higher or lower. */
-  double* h_margin;
 } oracle_layer_args;
 
 /* e4m3 code -> value, filled from oracle_e4m3_decode before any parallel
@@ -498,8 +479,6 @@ int oracle_layer(oracle_layer_args* A) {
   const float r_h = 1.0f / s_h;
 
   double* hq = (double*)malloc(sizeof(double) * (size_t)P * (size_t)I);
-  if (blk && A->h_margin)
-    for (int64_t p = 0; p < P; ++p) A->h_margin[p] = 1.0;
   for (int64_t p = 0; p < P; ++p) {
     if (!need[p]) continue;
     if (blk) {
@@ -507,12 +486,6 @@ int oracle_layer(oracle_layer_args* A) {
       for (int64_t g = 0; g < I; g += 128) {
         const double sc = oracle_e8m0_value(oracle_block_quant(h + p * I + g, 128, q));
         for (int i = 0; i < 128; ++i) hq[p * I + g + i] = oracle_e4m3_decode(q[i]) * sc;
-        if (A->h_margin) {
-          float amax = 0.0f;
-          for (int i = 0; i < 128; ++i) amax = fmaxf(amax, fabsf(h[p * I + g + i]));
-          const double mg = oracle_pow2_margin(amax);
-          if (mg < A->h_margin[p]) A->h_margin[p] = mg;
-        }
       }
       continue;
     }
@@ -579,4 +552,4 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 int oracle_num_threads(void) { return 1; }
 #endif
 
-int oracle_abi_version(void) { return 6; }
+int oracle_abi_version(void) { return 5; }

@@ -49,11 +49,9 @@ typedef struct {
   int32_t block_scaled;
   const uint8_t* const* w13_block;
   const uint8_t* const* w2_block;
-  double* h_margin;
 } layer_args;
 uint8_t oracle_block_quant(const float* v, int n, uint8_t* codes);
 double oracle_e8m0_value(uint8_t c);
-double oracle_pow2_margin(float amax);
 int oracle_layer(layer_args* A);
 
 static int failures = 0;
@@ -179,11 +177,8 @@ static void layer(int fp8, int xs, int hs, int rows, int S, int subset, int blk)
   A.block_scaled = blk;
   A.w13_block = (const uint8_t* const*)b13;
   A.w2_block = (const uint8_t* const*)b2;
-  double margin[9 * 4];
-  A.h_margin = blk ? margin : NULL;
   CHECK(oracle_layer(&A) == 0);
   for (int64_t i = 0; i < nt * H; ++i) CHECK(isfinite(y[i]));
-  for (int p = 0; blk && p < M * (k + S); ++p) CHECK(margin[p] >= 0.0 && margin[p] <= 1.0);
   /* a missing expert is reported, not dereferenced */
   void* keep = w13[ids[0]];
   w13[ids[0]] = NULL;
@@ -243,7 +238,6 @@ int main(void) {
     for (int i = 0; i < 128; ++i) v[i] = normal() * 1e30f;
     (void)oracle_block_quant(v, 128, q);
     for (int c = 0; c < 256; ++c) (void)oracle_e8m0_value((uint8_t)c);
-    CHECK(oracle_pow2_margin(0.0f) == 1.0 && oracle_pow2_margin(INFINITY) == 1.0 && oracle_pow2_margin(4.0f) == 0.0);
   }
   router();
   if (failures) {
