@@ -193,6 +193,21 @@ typedef struct {
  * quantisation schemes: "Fused MoE on Hopper, ...", TL;DR; ZICQ, "AWS Unveils
  * MoE Kernel Optimizations ...", §Triton Backend Routing for FP8
  * Quantization).
+ * Block-scaled fp8 (weight_scale_mode 3; the pages name routing among
+ * quantisation schemes, ZICQ page, §Triton Backend Routing for FP8
+ * Quantization): w13_scale and w2_scale then point to uint8 E8M0 codes (the
+ * OCP microscaling scale format, value 2^(c-127)), one per 128 x 128 block:
+ * [E+S][2I/128][H/128] for W13 and [E+S][H/128][I/128] for W2; every weight
+ * is its e4m3 value times its block's scale.  Activations take one
+ * power-of-two scale per 128 consecutive elements of a token's x row and of
+ * a pair's h row, chosen by the OCP microscaling rule for E4M3 elements
+ * (code = max(biased exponent of the group's amax - 8, 0)), each element
+ * rounded to e4m3 after division by it; x_scale and h_scale must be NULL
+ * (else MOE_ERR_INVALID_ARG) and scales_out reports 0, 0.  The scales go
+ * into the scaled MFMA with the operands.  The decode products serve every M
+ * in this mode (the K-split variants; tunings asking for a long-stream
+ * variant return MOE_ERR_UNSUPPORTED); a token's output does not depend on
+ * the rest of its batch.
  * Shared experts (n_shared = S > 0; the pages do not describe them, and here
  * they are the plain form): every token also passes through experts
  * E..E+S-1, stacked after the routed ones in w13/w2 (and in per-row scales),
@@ -229,7 +244,8 @@ typedef struct {
   size_t workspace_bytes;
   const moe_tuning_t* tuning; /* host pointer or NULL */
   int32_t weight_scale_mode; /* fp8: 0 = one scale per weight tensor, 1 = one per weight row, 2 = one per
-                                expert; any other value, or non-zero in bf16 mode: MOE_ERR_INVALID_ARG */
+                                expert, 3 = block-scaled (below); any other value, or non-zero in bf16
+                                mode: MOE_ERR_INVALID_ARG */
   const void* router_w;    /* bf16 [E,H] router weights, 16-byte aligned, or NULL.  Exactly one of logits and
                               router_w is non-NULL (else MOE_ERR_INVALID_ARG); with router_w the layer first
                               computes logits = x . router_w^T as moe_router_logits does and routes on them */
@@ -267,13 +283,15 @@ typedef struct {
 size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype);
 
 /* Host-only: block size and sorted_ids capacity of the sort-and-pad step of
- * moe_fused_forward for these sizes and mode (E and top_k counting shared
- * experts, as for moe_fused_workspace_size): block 128 on the prefill path
- * (fp8, M*top_k >= 8192, default mode), else 16; capacity as
- * moe_align_capacity.  Errors as moe_fused_forward's shape checks, and
- * MOE_ERR_INVALID_ARG for NULL outputs. */
+ * moe_fused_forward for these sizes and modes (E and top_k counting shared
+ * experts, as for moe_fused_workspace_size; deterministic and
+ * weight_scale_mode as in moe_fused_args_t): block 128 on the prefill path
+ * (fp8, M*top_k >= 8192, not deterministic, not block-scaled), else 16;
+ * capacity as moe_align_capacity.  Errors as moe_fused_forward's shape
+ * checks, and MOE_ERR_INVALID_ARG for unknown modes or NULL outputs. */
 moe_status_t moe_fused_align_shape(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype,
-                                   int32_t deterministic, int32_t* block, int64_t* capacity);
+                                   int32_t deterministic, int32_t weight_scale_mode, int32_t* block,
+                                   int64_t* capacity);
 
 moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream);
 

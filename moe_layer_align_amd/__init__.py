@@ -64,7 +64,7 @@ class _FusedArgs(ctypes.Structure):
 
 
 _lib = None
-_ABI = 10  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
+_ABI = 11  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():
@@ -92,7 +92,7 @@ def load():
     lib.moe_fused_workspace_size.restype = sz
     lib.moe_fused_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.moe_fused_align_shape.restype = ctypes.c_int
-    lib.moe_fused_align_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, i32, vp, vp]
+    lib.moe_fused_align_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, i32, i32, vp, vp]
     lib.moe_fused_forward.restype = ctypes.c_int
     lib.moe_fused_forward.argtypes = [ctypes.POINTER(_FusedArgs), vp]
     lib.moe_fused_forward_profiled.restype = ctypes.c_int
@@ -200,13 +200,14 @@ def workspace_size(M: int, E: int, H: int, I: int, top_k: int, dtype: str) -> in
     return int(load().moe_fused_workspace_size(M, E, H, I, top_k, DTYPE_FP8 if dtype == "fp8" else DTYPE_BF16))
 
 
-def fused_align_shape(M: int, E: int, H: int, I: int, top_k: int, dtype: str, deterministic: bool = False):
+def fused_align_shape(M: int, E: int, H: int, I: int, top_k: int, dtype: str, deterministic: bool = False,
+                      weight_scale_mode: int = 0):
     """(block, capacity) of the fused call's sort-and-pad step
     (moe_fused_align_shape); E and top_k count the shared experts."""
     b, c = ctypes.c_int32(0), ctypes.c_int64(0)
     _check("moe_fused_align_shape", load().moe_fused_align_shape(
         M, E, H, I, top_k, DTYPE_FP8 if dtype == "fp8" else DTYPE_BF16, int(bool(deterministic)),
-        ctypes.byref(b), ctypes.byref(c)))
+        int(weight_scale_mode), ctypes.byref(b), ctypes.byref(c)))
     return int(b.value), int(c.value)
 
 
@@ -226,8 +227,10 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
     x bf16 [M,H]; logits fp32 [M,E]; w13 [E,2I,H] and w2 [E,H,I] as bf16
     (dtype "bf16") or uint8 e4m3fn codes (dtype "fp8") with fp32 device
     scales, either one per tensor ([1] each), one per weight row (w13_scale
-    [E,2I], w2_scale [E,H]) or one per expert ([E] each); x_scale/h_scale: static fp8 activation scales or
-    None (dynamic).  logits may be None when router_w (bf16 [E,H]) is given:
+    [E,2I], w2_scale [E,H]) or one per expert ([E] each), or uint8 E8M0 codes
+    one per 128 x 128 block (w13_scale [E,2I/128,H/128], w2_scale
+    [E,H/128,I/128]: block-scaled mode, activations scaled per 128 elements);
+    x_scale/h_scale: static fp8 activation scales or None (dynamic).  logits may be None when router_w (bf16 [E,H]) is given:
     the layer then computes them (into logits_out fp32 [M,E] when given).
     n_shared: S shared experts stacked after the E routed ones (w13 [E+S,2I,H],
     w2 [E+S,H,I], per-row scales [E+S,..]), each taken by every token with
@@ -261,10 +264,15 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
             _need(logits_out, "logits_out", torch.float32, (M, E))
     _need(w13, "w13", wdt, (ES, 2 * I, H))
     _need(w2, "w2", wdt, (ES, H, I))
-    # weight scale mode from the scale shapes: [E+S,rows] one per row (1),
-    # [E+S] with E+S > 1 one per expert (2), [1] one per tensor (0)
+    # weight scale mode from the scale shapes: uint8 E8M0 codes
+    # [E+S,2I/128,H/128] one per 128 x 128 block (3), [E+S,rows] one per row
+    # (1), [E+S] with E+S > 1 one per expert (2), [1] one per tensor (0)
     mode = 0
-    if w13_scale is not None and w13_scale.dim() == 2:
+    if w13_scale is not None and w13_scale.dtype == torch.uint8:
+        mode = 3
+        _need(w13_scale, "w13_scale", torch.uint8, (ES, 2 * I // 128, H // 128))
+        _need(w2_scale, "w2_scale", torch.uint8, (ES, H // 128, I // 128))
+    elif w13_scale is not None and w13_scale.dim() == 2:
         mode = 1
         _need(w13_scale, "w13_scale", torch.float32, (ES, 2 * I))
         _need(w2_scale, "w2_scale", torch.float32, (ES, H))
@@ -294,7 +302,7 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         raise ValueError("unknown align_out keys: %s" % sorted(set(al) - {"offsets", "sorted_ids", "block_expert",
                                                                             "num_padded"}))
     if al:
-        blk, cap = fused_align_shape(M, ES, H, I, KS, dtype, deterministic)
+        blk, cap = fused_align_shape(M, ES, H, I, KS, dtype, deterministic, mode)
         for key, shape in (("offsets", (ES + 1,)), ("sorted_ids", (cap,)), ("block_expert", (cap // blk,)),
                            ("num_padded", (1,))):
             if key in al:

@@ -76,67 +76,89 @@ __device__ __forceinline__ f32x4 mma(const Frag<FP8>& a, const Frag<FP8>& b, f32
 // while the wave computes.  pa[i] / pb[t] point at the lane's first bytes;
 // consecutive k-steps are SB bytes apart.
 // --------------------------------------------------------------------------
-template <bool FP8, int NA, int NB, int U>
+// BS (block-scaled fp8): every k-step also carries the E8M0 block scales of
+// its operands, one per A tile (qa[i][step], the same for every lane of the
+// tile: a 16-row tile and a 128-element k-step lie in one 128 x 128 weight
+// block) and one per token column (qb[t][step]: the token's 128-element
+// group), loaded with the stage and fed to the scaled MFMA.
+template <bool FP8, int NA, int NB, int U, bool BS = false>
 struct StageRegs {
   Frag<FP8> a[U][NA];
   Frag<FP8> b[U][NB];
+  int sa[BS ? U : 1][NA];
+  int sb[BS ? U : 1][NB];
 };
 
-template <bool FP8, int NA, int NB, int U, int SB>
-__device__ __forceinline__ void stage_load(StageRegs<FP8, NA, NB, U>& s, const uint8_t* const* pa,
-                                           const uint8_t* const* pb, int64_t off) {
+template <bool FP8, int NA, int NB, int U, int SB, bool BS = false>
+__device__ __forceinline__ void stage_load(StageRegs<FP8, NA, NB, U, BS>& s, const uint8_t* const* pa,
+                                           const uint8_t* const* pb, int64_t off, const uint8_t* const* qa = nullptr,
+                                           const uint8_t* const* qb = nullptr, int step = 0) {
 #pragma unroll
   for (int q = 0; q < U; ++q) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) load_frag<FP8>(s.a[q][i], pa[i] + off + q * SB);
 #pragma unroll
     for (int t = 0; t < NB; ++t) load_frag<FP8>(s.b[q][t], pb[t] + off + q * SB);
+    if constexpr (BS) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) s.sa[q][i] = qa[i][step + q];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) s.sb[q][t] = qb[t][step + q];
+    }
   }
 }
 
-template <bool FP8, int NA, int NB, int U>
-__device__ __forceinline__ void stage_mma(const StageRegs<FP8, NA, NB, U>& s, f32x4 (&acc)[NA][NB]) {
+template <bool FP8, int NA, int NB, int U, bool BS = false>
+__device__ __forceinline__ void stage_mma(const StageRegs<FP8, NA, NB, U, BS>& s, f32x4 (&acc)[NA][NB]) {
 #pragma unroll
   for (int q = 0; q < U; ++q)
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
-      for (int i = 0; i < NA; ++i) acc[i][t] = mma<FP8>(s.a[q][i], s.b[q][t], acc[i][t]);
+      for (int i = 0; i < NA; ++i) {
+        if constexpr (BS)
+          acc[i][t] = mfma_fp8_scaled(s.a[q][i].v[0], s.a[q][i].v[1], s.b[q][t].v[0], s.b[q][t].v[1], acc[i][t],
+                                      s.sa[q][i], s.sb[q][t]);
+        else
+          acc[i][t] = mma<FP8>(s.a[q][i], s.b[q][t], acc[i][t]);
+      }
 }
 
-// acc += sum over nsteps k-steps of A_i . B_t
-template <bool FP8, int NA, int NB, int U, int SB>
+// acc += sum over nsteps k-steps of A_i . B_t (BS: with the k-steps' block
+// scales from qa, qb)
+template <bool FP8, int NA, int NB, int U, int SB, bool BS = false>
 __device__ __forceinline__ void stream_k(const uint8_t* const* pa, const uint8_t* const* pb, int nsteps,
-                                         f32x4 (&acc)[NA][NB]) {
+                                         f32x4 (&acc)[NA][NB], const uint8_t* const* qa = nullptr,
+                                         const uint8_t* const* qb = nullptr) {
   constexpr int SS = U * SB;  // bytes per row per stage
   const int nfull = nsteps / U;
   if (nfull > 0) {
-    StageRegs<FP8, NA, NB, U> s0, s1;
-    stage_load<FP8, NA, NB, U, SB>(s0, pa, pb, 0);
+    StageRegs<FP8, NA, NB, U, BS> s0, s1;
+    stage_load<FP8, NA, NB, U, SB, BS>(s0, pa, pb, 0, qa, qb, 0);
     int it = 0;
     for (; it + 2 < nfull; it += 2) {
-      stage_load<FP8, NA, NB, U, SB>(s1, pa, pb, (int64_t)(it + 1) * SS);
+      stage_load<FP8, NA, NB, U, SB, BS>(s1, pa, pb, (int64_t)(it + 1) * SS, qa, qb, (it + 1) * U);
       __builtin_amdgcn_sched_barrier(0);  // keep the whole stage's loads ahead of the MFMAs
-      stage_mma<FP8, NA, NB, U>(s0, acc);
+      stage_mma<FP8, NA, NB, U, BS>(s0, acc);
       __builtin_amdgcn_sched_barrier(0);
-      stage_load<FP8, NA, NB, U, SB>(s0, pa, pb, (int64_t)(it + 2) * SS);
+      stage_load<FP8, NA, NB, U, SB, BS>(s0, pa, pb, (int64_t)(it + 2) * SS, qa, qb, (it + 2) * U);
       __builtin_amdgcn_sched_barrier(0);
-      stage_mma<FP8, NA, NB, U>(s1, acc);
+      stage_mma<FP8, NA, NB, U, BS>(s1, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (it + 1 < nfull) {
-      stage_load<FP8, NA, NB, U, SB>(s1, pa, pb, (int64_t)(it + 1) * SS);
+      stage_load<FP8, NA, NB, U, SB, BS>(s1, pa, pb, (int64_t)(it + 1) * SS, qa, qb, (it + 1) * U);
       __builtin_amdgcn_sched_barrier(0);
-      stage_mma<FP8, NA, NB, U>(s0, acc);
-      stage_mma<FP8, NA, NB, U>(s1, acc);
+      stage_mma<FP8, NA, NB, U, BS>(s0, acc);
+      stage_mma<FP8, NA, NB, U, BS>(s1, acc);
     } else {
-      stage_mma<FP8, NA, NB, U>(s0, acc);
+      stage_mma<FP8, NA, NB, U, BS>(s0, acc);
     }
   }
   for (int st = nfull * U; st < nsteps; ++st) {
-    StageRegs<FP8, NA, NB, 1> s;
-    stage_load<FP8, NA, NB, 1, SB>(s, pa, pb, (int64_t)st * SB);
-    stage_mma<FP8, NA, NB, 1>(s, acc);
+    StageRegs<FP8, NA, NB, 1, BS> s;
+    stage_load<FP8, NA, NB, 1, SB, BS>(s, pa, pb, (int64_t)st * SB, qa, qb, st);
+    stage_mma<FP8, NA, NB, 1, BS>(s, acc);
   }
 }
 
@@ -161,7 +183,15 @@ struct Gemm1Args {
   unsigned* h_amax;          // fp8 dynamic: running max of |h| (float bits)
   int w_cs = 0;              // fp8: 1 = w_scale holds one scale per weight row, 0 = one per tensor
   int w_es = 0;              // fp8 without w_cs: 1 = one scale per expert (w_scale[e]), 0 = w_scale[0]
+  int w_bs = 0;              // fp8: 1 = block-scaled (w_block, x_block; h written as fp32)
+  const uint8_t* w_block;    // block-scaled: E8M0 codes [E][2I/128][H/128], one per 128 x 128 block of W13
+  const uint8_t* x_block;    // block-scaled: E8M0 codes [M][H/128] of the activations' 128-element groups
 };
+
+// Weight-scale kinds of the fp8 bodies (template parameter WS): one scale per
+// tensor or per expert (0), per weight row (1), or per 128 x 128 block, with
+// the activations' per-128-element scales, fed to the scaled MFMA (2).
+constexpr int kWsTensor = 0, kWsRow = 1, kWsBlock = 2;
 
 // fp8 dequantisation factors s_a * s_w: with one scale per weight row (PC)
 // those of the four rows row0..row0+3 of expert e (rows_e rows per expert),
@@ -188,9 +218,10 @@ __device__ __forceinline__ void row_deq4(const float* w_scale, int e, int rows_e
 // the workgroup's group of 4/KSPLIT feature tiles.  Returns the lane's
 // largest |h| (0 in lanes that store nothing), which the caller reduces
 // when the h scale is dynamic.
-template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT, bool PC>
+template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT, int WS>
 __device__ __forceinline__ float gemm1_body(const Gemm1Args& a, f32x4* s_red, int e, int seg, int cnt, int pass0,
                                             int bx) {
+  constexpr bool PC = WS == kWsRow, BS = FP8 && WS == kWsBlock;
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;   // k per MFMA
   constexpr int LB = FP8 ? 32 : 16;       // bytes per lane per operand per step
@@ -209,17 +240,28 @@ __device__ __forceinline__ float gemm1_body(const Gemm1Args& a, f32x4* s_red, in
   pa[0] = a.w13 + ((int64_t)e * 2 * a.I + i0 + r16) * rowb + (int64_t)kbeg * ESZ + kq * LB;  // gate rows
   pa[1] = pa[0] + (int64_t)a.I * rowb;                                                         // up rows
   const uint8_t* pb[NB];
+  const uint8_t* qb[NB];  // block-scaled: the lane's token's group scales from kbeg on
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const int slot = min(pass0 + t * 16 + r16, cnt - 1);
     const int m = a.seg.sorted_ids[seg + slot] / a.top_k;
     pb[t] = a.act + (int64_t)m * rowb + (int64_t)kbeg * ESZ + kq * LB;
+    if constexpr (BS) qb[t] = a.x_block + (int64_t)m * (a.H / 128) + kbeg / 128;
   }
 
   f32x4 acc[2][NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<FP8, 2, NB, U, SB>(pa, pb, Kw / KSTEP, acc);
+  if constexpr (BS) {
+    // the gate and up tiles' 128 x 128 weight blocks: rows i0/128 and (I+i0)/128
+    const uint8_t* qa[2];
+    const int kg = a.H / 128;
+    qa[0] = a.w_block + ((int64_t)e * (2 * a.I / 128) + i0 / 128) * kg + kbeg / 128;
+    qa[1] = a.w_block + ((int64_t)e * (2 * a.I / 128) + (a.I + i0) / 128) * kg + kbeg / 128;
+    stream_k<FP8, 2, NB, U, SB, true>(pa, pb, Kw / KSTEP, acc, qa, qb);
+  } else {
+    stream_k<FP8, 2, NB, U, SB>(pa, pb, Kw / KSTEP, acc);
+  }
 
   if constexpr (KSPLIT > 1) {
     if (kpart > 0) {
@@ -245,7 +287,7 @@ __device__ __forceinline__ float gemm1_body(const Gemm1Args& a, f32x4* s_red, in
 
   // dequantisation of this lane's rows: gate rows i0+4kq.., up rows I+i0+4kq..
   float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-  if constexpr (FP8) {
+  if constexpr (FP8 && !BS) {  // block-scaled: the MFMA applied the scales
     row_deq4<PC>(a.w_scale, e, 2 * a.I, i0 + kq * 4, *a.x_scale, dg, a.w_es);
     row_deq4<PC>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, *a.x_scale, du, a.w_es);
   }
@@ -290,22 +332,28 @@ static __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
   const int pass0 = grid_z(a.seg) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
-  auto run = [&](auto pc_tag) {
-    constexpr bool PC = decltype(pc_tag)::value;
+  auto run = [&](auto ws_tag) {
+    constexpr int WS = decltype(ws_tag)::value;
     const int bx = blockIdx.x;
     if constexpr (NT >= 4)
-      if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
+      if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
     if constexpr (NT >= 3)
-      if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
+      if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
     if constexpr (NT >= 2)
-      if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
-    return gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT, PC>(a, s_red, e, seg, cnt, pass0, bx);
+      if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
+    return gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
   };
   float hmax;
-  if constexpr (FP8)
-    hmax = a.w_cs ? run(std::true_type{}) : run(std::false_type{});  // one weight scale per row, or not
+  if constexpr (FP8 && HFMT == H_F32) {
+    if (a.w_bs) {  // block-scaled: h is quantised per block later, no tensor amax
+      run(std::integral_constant<int, kWsBlock>{});
+      return;
+    }
+  }
+  if constexpr (FP8)  // one weight scale per row, or per tensor / expert
+    hmax = a.w_cs ? run(std::integral_constant<int, kWsRow>{}) : run(std::integral_constant<int, kWsTensor>{});
   else
-    hmax = run(std::false_type{});
+    hmax = run(std::integral_constant<int, kWsTensor>{});
   if constexpr (HFMT == H_F32) {
     // one device-scope atomic per wave that stored h (same-address atomics
     // serialise: an atomic from every wave cost 8-25 us on the M = 1 layers)
@@ -516,6 +564,8 @@ struct Gemm2Args {
   int P;
   int w_cs = 0;              // fp8: 1 = one scale per weight row, 0 = one per tensor
   int w_es = 0;              // fp8 without w_cs: 1 = one scale per expert (w_scale[e]), 0 = w_scale[0]
+  int w_bs = 0;              // fp8: 1 = block-scaled (w_block; h, fp32, quantised per 128-element group)
+  const uint8_t* w_block;    // block-scaled: E8M0 codes [E][H/128][I/128], one per 128 x 128 block of W2
 };
 
 // LDS row stride (bytes) of the quantised token slice: Kw plus 16 bytes so
@@ -546,12 +596,56 @@ __device__ __forceinline__ void stage_h_e4m3(const Gemm2Args& a, uint8_t* s_tok,
   }
 }
 
+// Block-scaled variant: each 128-element group of a token row gets its own
+// power-of-two scale (OCP MX rule, block_scale_code), whose E8M0 code goes to
+// the byte array after the NB*16 token rows, Kw/128 codes per row.  Eight
+// consecutive threads take one group (16 elements each) and share its amax
+// through DPP, so every thread runs every round (rows past the slice take
+// part with zeros).
+__host__ __device__ constexpr int gemm2_block_scale_bytes(int rows, int kw_bytes) { return rows * (kw_bytes / 128); }
+
+template <int NB>
+__device__ __forceinline__ void stage_h_block(const Gemm2Args& a, uint8_t* s_tok, int seg, int cnt, int pass0,
+                                              int kbeg, int Kw) {
+  const int stride = gemm2_lds_stride(Kw);
+  const int per_row = Kw / 16;  // 16 elements per thread-step, 8 steps per group
+  const int total = NB * 16 * per_row;
+  uint8_t* s_scale = s_tok + NB * 16 * stride;
+  for (int base = 0; base < total; base += 256) {
+    const int idx = base + threadIdx.x;
+    const bool live = idx < total;  // whole groups are live or not: total is a multiple of 128
+    const int j = live ? idx : 0;
+    const int row = j / per_row, c = (j - row * per_row) * 16;
+    const int slot = min(pass0 + row, cnt - 1);
+    const int f = a.seg.sorted_ids[seg + slot];
+    const float* src = (const float*)a.h + (int64_t)f * a.I + kbeg + c;
+    const f32x4 v0 = *(const f32x4*)(src), v1 = *(const f32x4*)(src + 4);
+    const f32x4 v2 = *(const f32x4*)(src + 8), v3 = *(const f32x4*)(src + 12);
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v0[q]), fabsf(v1[q])), fmaxf(fabsf(v2[q]), fabsf(v3[q]))));
+    m = max8(live ? m : 0.0f);
+    const int code = block_scale_code(m);
+    const float r = block_scale_recip(code);
+    if (live) {
+      u32x4 q = {pack_e4m3x4(v0[0] * r, v0[1] * r, v0[2] * r, v0[3] * r),
+                 pack_e4m3x4(v1[0] * r, v1[1] * r, v1[2] * r, v1[3] * r),
+                 pack_e4m3x4(v2[0] * r, v2[1] * r, v2[2] * r, v2[3] * r),
+                 pack_e4m3x4(v3[0] * r, v3[1] * r, v3[2] * r, v3[3] * r)};
+      *(u32x4*)(s_tok + row * stride + c) = q;
+      if ((idx & 7) == 0) s_scale[row * (Kw / 128) + c / 128] = (uint8_t)code;
+    }
+  }
+}
+
 // Body for NB (<= NT) token tiles.  WKS waves of the workgroup split the
 // slice's K range and are summed through LDS (s_red); 4/WKS groups of 32 rows
 // per workgroup.
-template <bool FP8, int HFMT, int NT, int NB, int U, int WKS, bool PC>
+template <bool FP8, int HFMT, int NT, int NB, int U, int WKS, int WS>
 __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f32x4* s_red, int e, int seg, int cnt,
                                            int pass0, int kslice, int bx) {
+  constexpr bool PC = WS == kWsRow, BS = FP8 && HFMT == H_F32 && WS == kWsBlock;
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 128 : 32;
   constexpr int LB = FP8 ? 32 : 16;
@@ -571,7 +665,10 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
 
   // dequantisation of this lane's rows n0+4kq.. and n0+16+4kq..
   float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-  if constexpr (FP8) {
+  if constexpr (BS) {  // the MFMA applies the scales
+    stage_h_block<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw);
+    __syncthreads();
+  } else if constexpr (FP8) {
     const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
     row_deq4<PC>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0, a.w_es);
     row_deq4<PC>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1, a.w_es);
@@ -600,7 +697,19 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
   f32x4 acc[2][NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<FP8, 2, NB, U, SB>(pa, pb, Kp / KSTEP, acc);
+  if constexpr (BS) {
+    // both 16-row tiles lie in the 128 x 128 block of rows n0/128; the token
+    // rows' group scales follow the staged slice
+    const uint8_t* qa[2];
+    qa[0] = qa[1] = a.w_block + ((int64_t)e * (a.H / 128) + n0 / 128) * (a.I / 128) + (kbeg + koff) / 128;
+    const uint8_t* qb[NB];
+    const uint8_t* s_scale = s_tok + NB * 16 * gemm2_lds_stride(Kw);
+#pragma unroll
+    for (int t = 0; t < NB; ++t) qb[t] = s_scale + (t * 16 + r16) * (Kw / 128) + koff / 128;
+    stream_k<FP8, 2, NB, U, SB, true>(pa, pb, Kp / KSTEP, acc, qa, qb);
+  } else {
+    stream_k<FP8, 2, NB, U, SB>(pa, pb, Kp / KSTEP, acc);
+  }
 
   if constexpr (WKS > 1) {
     if (kpart > 0) {
@@ -652,22 +761,24 @@ static __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   const int pass0 = (z / a.ksplit) * NT * 16;
   if (pass0 >= cnt) return;
   const int ntile = min(NT, (cnt - pass0 + 15) >> 4);  // uniform over the workgroup
-  auto run = [&](auto pc_tag) {
-    constexpr bool PC = decltype(pc_tag)::value;
+  auto run = [&](auto ws_tag) {
+    constexpr int WS = decltype(ws_tag)::value;
     if constexpr (NT >= 4)
       if (ntile == 4)
-        return gemm2_body<FP8, HFMT, NT, 4, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+        return gemm2_body<FP8, HFMT, NT, 4, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
     if constexpr (NT >= 3)
       if (ntile == 3)
-        return gemm2_body<FP8, HFMT, NT, 3, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+        return gemm2_body<FP8, HFMT, NT, 3, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
     if constexpr (NT >= 2)
       if (ntile == 2)
-        return gemm2_body<FP8, HFMT, NT, 2, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
-    gemm2_body<FP8, HFMT, NT, 1, U, WKS, PC>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+        return gemm2_body<FP8, HFMT, NT, 2, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+    gemm2_body<FP8, HFMT, NT, 1, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
   };
+  if constexpr (FP8 && HFMT == H_F32)
+    if (a.w_bs) return run(std::integral_constant<int, kWsBlock>{});  // block-scaled
   if constexpr (FP8)
-    if (a.w_cs) return run(std::true_type{});  // one weight scale per row
-  run(std::false_type{});
+    if (a.w_cs) return run(std::integral_constant<int, kWsRow>{});  // one weight scale per row
+  run(std::integral_constant<int, kWsTensor>{});
 }
 
 // Down product, long-stream variant.  Wave w of the workgroup walks tw tiles

@@ -220,7 +220,7 @@ static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
   auto grid_barrier = [&] { layer1_barrier(a.sync); };
 
   auto layer = [&](auto pc_tag) {
-    constexpr bool PC = decltype(pc_tag)::value;
+    constexpr int WS = decltype(pc_tag)::value ? kWsRow : kWsTensor;
     // ---- phase 1: gate/up items (expert, 16-feature tile)
     Gemm1Args g1{a.w13, FP8 ? a.xq : (const uint8_t*)a.x, seg, H, I, KS, a.w13_scale, &s_sx, a.h_scale, a.h,
                  nullptr};
@@ -231,7 +231,7 @@ static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
     for (int it = blockIdx.x; it < nact * t1; it += gridDim.x) {
       __syncthreads();  // the previous item's reduction tiles are consumed
       const int e = s_active[it / t1];
-      hmax = fmaxf(hmax, gemm1_body<FP8, HFMT, 1, 1, U1, 4, PC>(g1, s_red, e, s_offsets[e], s_counts[e], 0,
+      hmax = fmaxf(hmax, gemm1_body<FP8, HFMT, 1, 1, U1, 4, WS>(g1, s_red, e, s_offsets[e], s_counts[e], 0,
                                                                  it % t1));
     }
     if constexpr (HFMT == H_F32) {
@@ -265,7 +265,7 @@ static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
     for (int it = blockIdx.x; it < nact * t2; it += gridDim.x) {
       __syncthreads();  // the previous item's token slice and reduction tiles are consumed
       const int e = s_active[it / t2];
-      gemm2_body<FP8, HFMT, 1, 1, U2, WKS, PC>(g2, s_tok, s_red, e, s_offsets[e], s_counts[e], 0, 0, it % t2);
+      gemm2_body<FP8, HFMT, 1, 1, U2, WKS, WS>(g2, s_tok, s_red, e, s_offsets[e], s_counts[e], 0, 0, it % t2);
     }
     grid_barrier();
   };

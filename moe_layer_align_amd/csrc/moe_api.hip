@@ -33,10 +33,11 @@ bool use_prefill(int M, int k, moe_dtype_t dt, int H, int I) {
   return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0 && I % (kPfRows / 2) == 0 &&
          steps_ok(H) && steps_ok(I) && 2 * (int64_t)I * H <= lim && (int64_t)M * H <= lim && P * I <= lim;
 }
-// Align block of the fused call: 128 on the prefill path, else 16 (the
-// deterministic mode always takes the decode path).
-int align_block(int M, int k, moe_dtype_t dt, int H, int I, bool det) {
-  return !det && use_prefill(M, k, dt, H, I) ? kPfTok : kAlignBlockFused;
+// Align block of the fused call: 128 on the prefill path, else 16.
+// decode_only: the deterministic and block-scaled modes take the decode path
+// at every M.
+int align_block(int M, int k, moe_dtype_t dt, int H, int I, bool decode_only) {
+  return !decode_only && use_prefill(M, k, dt, H, I) ? kPfTok : kAlignBlockFused;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -83,18 +84,18 @@ int64_t align_capacity(int64_t P, int E, int B) {
 // ---------------------------------------------------------------- workspace
 struct Layout {
   size_t ids, wts, counts, offsets, sorted, block_expert, num_padded, active, num_active;
-  size_t xamax_part, scale_slot, h_amax, hist, logits, wg_hmax, xq, h, part, total;
+  size_t xamax_part, scale_slot, h_amax, hist, logits, wg_hmax, xs_blk, xq, h, part, total;
   int64_t capacity;
   int block, n_blocks, n_route_wg;
 };
 
-// The workspace serves both modes of a shape (the default one and the
-// deterministic one, whose align block may differ): the sort-and-pad arrays
-// are sized for the larger of the two blocks' needs.  capacity and n_blocks
-// are those of the call's own block.
+// The workspace serves every mode of a shape (the default one and those that
+// take the decode path at every M, whose align block may differ): the
+// sort-and-pad arrays are sized for the larger of the two blocks' needs.
+// capacity and n_blocks are those of the call's own block.
 // part_slices: K slices of fp32 partial sums the layout holds for the down
 // product (0: as many as any plan of the shape may take, down_ksplit_cap).
-Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det = false, int part_slices = 0) {
+Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool decode_only = false, int part_slices = 0) {
   Layout L{};
   const int64_t P = (int64_t)M * k;
   size_t off = 0;
@@ -103,7 +104,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det =
     off += round_up(std::max<size_t>(bytes, 4), 256);
     return o;
   };
-  const int B = align_block(M, k, dt, H, I, det);
+  const int B = align_block(M, k, dt, H, I, decode_only);
   L.block = B;
   L.capacity = align_capacity(P, E, B);
   L.n_blocks = (int)(L.capacity / B);
@@ -129,6 +130,7 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool det =
   L.logits = take((size_t)M * E * 4);  // router logits computed by the layer (router_w given)
   L.wg_hmax = take((size_t)kLayer1MaxGrid * 4);  // single-launch layer: largest |h| of each workgroup
   const bool fp8 = dt == MOE_DTYPE_FP8_E4M3;
+  L.xs_blk = take(fp8 ? (size_t)M * H / 128 : 0);  // block-scaled fp8: x's group scales
   L.xq = take(fp8 ? (size_t)M * H : 0);
   // h: bf16 (bf16 layers), fp32 (fp8 decode), fp32 + its e4m3 copy (fp8 prefill)
   L.h = take((size_t)P * I * (fp8 ? (use_prefill(M, k, dt, H, I) ? 5 : 4) : 2));
@@ -154,8 +156,10 @@ struct Plan {
 bool valid_u(bool fp8, int u) { return fp8 ? (u == 1 || u == 2) : (u == 2 || u == 4); }
 bool valid_wsplit(int ks) { return ks == 1 || ks == 2 || ks == 4; }
 
+// blk: block-scaled fp8 (K-split variants only; h staged with its group
+// scales in the down product's LDS, as for a dynamic h scale).
 moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool qh, const moe_tuning_t* t, bool det,
-                       Plan* p) {
+                       bool blk, Plan* p) {
   const int kstep = fp8 ? 128 : 32;
   const int64_t P = (int64_t)M * k;
   const int n_act = (int)std::min<int64_t>(E, P);  // upper bound on experts with tokens
@@ -217,6 +221,10 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
     if (v > 16) return MOE_ERR_UNSUPPORTED;
     if (v != 0) *tw = v > 0 ? v : 0;
   }
+  if (blk) {  // block-scaled fp8: the K-split variants only
+    if (t && (t->gemm1_stream_tiles > 0 || t->gemm2_stream_tiles > 0)) return MOE_ERR_UNSUPPORTED;
+    p->tw1 = p->tw2 = 0;
+  }
   if (p->tw1 > 0 && (H / kstep) % p->u1 != 0) {  // whole stages per row
     if (t && t->unroll > 0) return MOE_ERR_UNSUPPORTED;
     p->u1 = 1;
@@ -251,7 +259,8 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
   auto fits = [&](int ks) {
     if (nsteps2 % (ks * p->wks2) != 0) return false;
     if (p->tw2 > 0 && (nsteps2 / ks) % p->u2 != 0) return false;
-    const int64_t lds = (qh ? (int64_t)p->nt2 * 16 * gemm2_lds_stride(I / ks) : 0) + gemm2_red_bytes(p->nt2, p->wks2);
+    const int64_t lds = (qh ? (int64_t)p->nt2 * 16 * gemm2_lds_stride(I / ks) : 0) +
+                        (blk ? gemm2_block_scale_bytes(p->nt2 * 16, I / ks) : 0) + gemm2_red_bytes(p->nt2, p->wks2);
     return lds <= kDownLdsMax;
   };
   const int ks_cap = down_ksplit_cap(P, H, I, fp8);
@@ -270,7 +279,8 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
     p->ks2 = ks;
   }
   if (p->ks2 == 0) return MOE_ERR_UNSUPPORTED;
-  p->lds2 = qh ? p->nt2 * 16 * gemm2_lds_stride(I / p->ks2) : 0;
+  p->lds2 = (qh ? p->nt2 * 16 * gemm2_lds_stride(I / p->ks2) : 0) +
+            (blk ? gemm2_block_scale_bytes(p->nt2 * 16, I / p->ks2) : 0);
   return MOE_OK;
 }
 
@@ -417,7 +427,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 10; }
+int32_t moe_abi_version(void) { return 11; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -481,14 +491,17 @@ size_t moe_fused_workspace_size(int32_t M, int32_t E, int32_t H, int32_t I, int3
 }
 
 moe_status_t moe_fused_align_shape(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, moe_dtype_t dtype,
-                                   int32_t deterministic, int32_t* block, int64_t* capacity) {
+                                   int32_t deterministic, int32_t weight_scale_mode, int32_t* block,
+                                   int64_t* capacity) {
   moe_status_t rc = check_shape(M, E, top_k);
   if (rc != MOE_OK) return rc;
   if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (deterministic != 0 && deterministic != 1) return MOE_ERR_INVALID_ARG;
+  if (weight_scale_mode < 0 || weight_scale_mode > 3 || (weight_scale_mode != 0 && dtype != MOE_DTYPE_FP8_E4M3))
+    return MOE_ERR_INVALID_ARG;
   if (!block || !capacity) return MOE_ERR_INVALID_ARG;
   if (H < 128 || I < 128 || H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
-  const Layout L = make_layout(M, E, H, I, top_k, dtype, deterministic == 1);
+  const Layout L = make_layout(M, E, H, I, top_k, dtype, deterministic == 1 || weight_scale_mode == 3);
   *block = L.block;
   *capacity = L.capacity;
   return MOE_OK;
@@ -592,8 +605,12 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const int M = a->M, E = Er + S, H = a->H, I = a->I, k = kr + S;
   if (!fp8 && (a->w13_scale || a->w2_scale || a->x_scale || a->h_scale)) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_INVALID_ARG;
-  if (a->weight_scale_mode != 0 && (a->weight_scale_mode < 0 || a->weight_scale_mode > 2 || !fp8))
+  if (a->weight_scale_mode != 0 && (a->weight_scale_mode < 0 || a->weight_scale_mode > 3 || !fp8))
     return MOE_ERR_INVALID_ARG;
+  // block-scaled: per-block weight scales, activations scaled per 128-element
+  // group in the layer (no tensor scales to give)
+  const bool blk = a->weight_scale_mode == 3;
+  if (blk && (a->x_scale || a->h_scale)) return MOE_ERR_INVALID_ARG;
   const bool pc = a->weight_scale_mode == 1;
   if (pc && (!aligned(a->w13_scale, 16) || !aligned(a->w2_scale, 16))) return MOE_ERR_INVALID_ARG;
   if (M == 0) {
@@ -619,12 +636,12 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   // scales fixed by the caller (a dynamic scale is an amax over the batch)
   if (a->deterministic != 0 && a->deterministic != 1) return MOE_ERR_INVALID_ARG;
   const bool det = a->deterministic == 1;
-  if (det && fp8 && (!a->x_scale || !a->h_scale)) return MOE_ERR_INVALID_ARG;
+  if (det && fp8 && !blk && (!a->x_scale || !a->h_scale)) return MOE_ERR_INVALID_ARG;
   const bool hdyn = fp8 && !a->h_scale;
-  const bool prefill = !det && use_prefill(M, k, a->dtype, a->H, a->I);
+  const bool prefill = !det && !blk && use_prefill(M, k, a->dtype, a->H, a->I);
   Plan plan{};
   if (!prefill) {
-    rc = make_plan(M, E, H, I, k, S, fp8, hdyn, a->tuning, det, &plan);
+    rc = make_plan(M, E, H, I, k, S, fp8, hdyn, a->tuning, det, blk, &plan);
     if (rc != MOE_OK) return rc;
   }
   // the single-launch layer for tiny token counts, on request (never with
@@ -635,12 +652,12 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     const int mode = a->tuning ? a->tuning->single_launch : 0;
     if (mode < -1 || mode > 1) return MOE_ERR_UNSUPPORTED;
     if (mode == 1) {
-      if (!det && !a->router_w) l1_wks = layer1_wks(M, Er, k, H, I, fp8, hdyn);
+      if (!det && !blk && !a->router_w) l1_wks = layer1_wks(M, Er, k, H, I, fp8, hdyn);
       if (!l1_wks) return MOE_ERR_UNSUPPORTED;
     }
   }
   // the scratch array holds the partial sums of the plan's K slices only
-  const Layout L = make_layout(M, E, H, I, k, a->dtype, det, noalloc && !prefill ? plan.ks2 : 0);
+  const Layout L = make_layout(M, E, H, I, k, a->dtype, det || blk, noalloc && !prefill ? plan.ks2 : 0);
   uint8_t* ws = (uint8_t*)a->workspace;
   if (noalloc) {
     if (L.total > kNoallocScratchBytes) return MOE_ERR_UNSUPPORTED;
@@ -680,6 +697,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   float* scale_slot = (float*)(ws + L.scale_slot);
   unsigned* h_amax = (unsigned*)(ws + L.h_amax);
   uint8_t* xq = ws + L.xq;
+  uint8_t* xs_blk = ws + L.xs_blk;
   uint8_t* h = ws + L.h;
   float* part = (float*)(ws + L.part);
   const int64_t P = (int64_t)M * k;
@@ -737,7 +755,8 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   if (small) {
     // 1+2. routing, align (and fp8 activation quantisation) in one workgroup
     rec(0);
-    SmallQuant q{(const uint16_t*)a->x, H, a->x_scale, fp8 ? xq : nullptr, scale_slot, hdyn ? h_amax : nullptr};
+    SmallQuant q{(const uint16_t*)a->x, H, a->x_scale, fp8 ? xq : nullptr, scale_slot, hdyn ? h_amax : nullptr,
+                 blk ? xs_blk : nullptr};
     launch_prologue_small(a->logits, M, Er, kr, S, ids, wts, kAlignBlockFused, o, q, st);
     rec(1);
     rec(2);
@@ -748,7 +767,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     rec(0);
     // the routing workgroups' expert counts serve the multi-workgroup align
     int32_t* hist = (P > kSmallPairs && hist_usable(k)) ? (int32_t*)(ws + L.hist) : nullptr;
-    RouteFusedArgs fa{(const uint16_t*)a->x, H, (fp8 && !a->x_scale) ? xamax_part : nullptr,
+    RouteFusedArgs fa{(const uint16_t*)a->x, H, (fp8 && !blk && !a->x_scale) ? xamax_part : nullptr,
                       hdyn ? h_amax : nullptr, hist};
     launch_route(a->logits, M, Er, kr, S, ids, wts, fa, st);
     rec(1);
@@ -766,6 +785,7 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
       q.static_scale = a->x_scale;
       q.xq = xq;
       q.scale_slot = scale_slot;
+      q.xs = blk ? xs_blk : nullptr;
       n_quant = (int)cdiv(q.n, kAlignQuantPerWg);
     }
     if (P <= kSmallPairs) {  // one 1024-thread align workgroup, 16K-element quantising workgroups
@@ -789,6 +809,9 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
                 a->h_scale, h, h_amax};
     g.w_cs = pc ? 1 : 0;
     g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
+    g.w_bs = blk ? 1 : 0;
+    g.w_block = blk ? (const uint8_t*)a->w13_scale : nullptr;
+    g.x_block = xs_blk;
     DecodeShape sh{plan.nt1, plan.u1, plan.ks1, plan.tw1, dim3(), 0};
     sh.grid = plan.tw1 > 0 ? dim3((unsigned)cdiv(I / 16, 4 * plan.tw1), (unsigned)n_act, (unsigned)plan.passes1)
                            : dim3((unsigned)(I / 16 / (4 / plan.ks1)), (unsigned)n_act, (unsigned)plan.passes1);
@@ -805,6 +828,8 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
                 (int)P};
     g.w_cs = pc ? 1 : 0;
     g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
+    g.w_bs = blk ? 1 : 0;
+    g.w_block = blk ? (const uint8_t*)a->w2_scale : nullptr;
     DecodeShape sh{plan.nt2, plan.u2, plan.wks2, plan.tw2, dim3(), (size_t)(hf == H_F32 ? plan.lds2 : 0)};
     sh.grid = plan.tw2 > 0
                   ? dim3((unsigned)cdiv(H / 32, 4 * plan.tw2), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2))
@@ -821,13 +846,16 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     const int64_t groups = (int64_t)M * H / 4;
     const int lkp = log2i(k);
     float* so = fp8 ? a->scales_out : nullptr;
+    // block-scaled: no tensor scales; both reported scales read the slot
+    // that the quantisation set to 0
+    const float* hs = blk ? scale_slot : a->h_scale;
     // four groups per lane once that still leaves at least 256 workgroups
     if ((groups << lkp) >= (int64_t)4 * 256 * 256)
       finalize_kernel<4><<<(unsigned)cdiv((groups / 4) << lkp, 256), 256, 0, st>>>(
-          part, wts, (uint16_t*)a->y, M, H, k, lkp, plan.ks2, scale_slot, h_amax, a->h_scale, so);
+          part, wts, (uint16_t*)a->y, M, H, k, lkp, plan.ks2, scale_slot, h_amax, hs, so);
     else
       finalize_kernel<1><<<(unsigned)cdiv(groups << lkp, 256), 256, 0, st>>>(
-          part, wts, (uint16_t*)a->y, M, H, k, lkp, plan.ks2, scale_slot, h_amax, a->h_scale, so);
+          part, wts, (uint16_t*)a->y, M, H, k, lkp, plan.ks2, scale_slot, h_amax, hs, so);
   }
   rec(9);
   return launch_status();

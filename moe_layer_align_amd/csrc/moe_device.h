@@ -37,6 +37,16 @@ __device__ __forceinline__ f32x4 mfma_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// The same product with per-lane E8M0 block scales (2^(s-127)): sa applies to
+// this lane's 32 bytes of A, sb to its 32 bytes of B (lanes holding the same
+// row of A, or the same column of B, at the same k positions pass the same
+// scale).
+__device__ __forceinline__ f32x4 mfma_fp8_scaled(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c, int sa, int sb) {
+  i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // ---------------------------------------------------------------- formats
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
@@ -59,6 +69,15 @@ __device__ __forceinline__ unsigned pack_e4m3x4(float a, float b, float c, float
 
 // Scale from an amax: amax/448, or 1 when amax is 0.
 __device__ __forceinline__ float scale_from_amax(float amax) { return amax > 0.0f ? amax / kE4m3Max : 1.0f; }
+
+// Block scaling (OCP MX rule for E4M3 elements): the E8M0 code of a block
+// whose largest magnitude is amax, max(biased exponent of amax - 8, 0), and
+// the reciprocal of its scale, 2^(127 - code), an exact power of two.
+__device__ __forceinline__ int block_scale_code(float amax) {
+  const int f = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  return f > 8 ? f - 8 : 0;
+}
+__device__ __forceinline__ float block_scale_recip(int code) { return __uint_as_float((unsigned)(254 - code) << 23); }
 
 // ---------------------------------------------------------------- reductions
 // Wavefront reductions by DPP lane moves (gfx9 controls): two quad
@@ -87,6 +106,14 @@ __device__ __forceinline__ float dpp_f32(float v) {
 
 __device__ __forceinline__ float lane63_f32(float v) {
   return __uint_as_float((unsigned)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
+// Largest value over each aligned group of 8 lanes (two quad permutations
+// and the half-row mirror), in all 8 of them.  All lanes must be active.
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  return fmaxf(v, dpp_f32<kDppHalfMirror>(v));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -270,8 +270,9 @@ struct QuantXArgs {
   int n_part;
   const float* static_scale; // device fp32 or null
   uint8_t* xq;               // [n] e4m3
-  float* scale_slot;         // s_x used
+  float* scale_slot;         // s_x used (0 in block mode)
   int first_wg;              // first workgroup index of the quantisation part
+  uint8_t* xs;               // block mode: E8M0 code of each 128-element group [n/128]; null = per tensor
 };
 
 // Sixteen bf16 (two 16-byte words) -> sixteen e4m3 bytes, scaled by r.
@@ -284,6 +285,25 @@ __device__ __forceinline__ u32x4 quant16_e4m3(const u32x4& a0, const u32x4& a1, 
   return o;
 }
 
+// Sixteen bf16 of a 128-element group whose other 112 elements the seven
+// neighbouring lanes of an aligned 8-lane group hold -> sixteen e4m3 bytes
+// with the group's power-of-two scale (OCP MX rule, block_scale_code); the
+// group's first lane stores the scale code.  Every lane of the wave takes part
+// (live: this lane's group is in range; whole groups are live or not).
+__device__ __forceinline__ void quant16_block(const u32x4& a0, const u32x4& a1, bool live, uint8_t* dst,
+                                              uint8_t* scale_dst, bool store_scale) {
+  unsigned m = 0;  // |bf16| order is the order of the low 15 bits
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    m = max(m, max(max(a0[c] & 0x7fffu, (a0[c] >> 16) & 0x7fffu), max(a1[c] & 0x7fffu, (a1[c] >> 16) & 0x7fffu)));
+  const float amax = max8(live ? __uint_as_float(m << 16) : 0.0f);
+  const int code = block_scale_code(amax);
+  if (live) {
+    *(u32x4*)dst = quant16_e4m3(a0, a1, block_scale_recip(code));
+    if (store_scale) *scale_dst = (uint8_t)code;
+  }
+}
+
 // x -> e4m3 with the per-tensor scale (static, or amax/448 from the router's
 // per-workgroup partial maxima), by a workgroup of NT threads, PER groups of
 // 16 elements per thread (NT*16 apart, all loads issued before the first
@@ -292,6 +312,19 @@ __device__ __forceinline__ u32x4 quant16_e4m3(const u32x4& a0, const u32x4& a1, 
 template <int NT, int PER = 1>
 __device__ void quant_x_part(const QuantXArgs& q, int wg) {
   __shared__ float s_red[NT / 64];
+  if (q.xs) {  // block mode: each 128-element group with its own scale, eight consecutive threads per group
+    if (wg == 0 && threadIdx.x == 0) *q.scale_slot = 0.0f;
+    const int64_t i0 = ((int64_t)wg * NT * PER + threadIdx.x) * 16;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int64_t i = i0 + (int64_t)p * NT * 16;
+      const bool live = i < q.n;
+      const int64_t src = live ? i : 0;
+      quant16_block(*(const u32x4*)(q.x + src), *(const u32x4*)(q.x + src + 8), live, q.xq + i, q.xs + (i >> 7),
+                    (threadIdx.x & 7) == 0);
+    }
+    return;
+  }
   float s;
   if (q.static_scale) {
     s = *q.static_scale;
@@ -557,8 +590,9 @@ struct SmallQuant {
   int H;
   const float* static_scale;  // device fp32 or null (dynamic amax/448)
   uint8_t* xq;                // [M,H] e4m3, null in bf16 mode
-  float* scale_slot;          // s_x used
+  float* scale_slot;          // s_x used (0 in block mode)
   unsigned* h_amax;           // cleared when non-null
+  uint8_t* xs;                // block mode: E8M0 codes [M*H/128]; null = per tensor
 };
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -567,6 +601,15 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void prologue_quant(const SmallQuant& q, int64_t nx, int qb) {
   __shared__ float s_red[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (q.xs) {  // block mode: each 128-element group with its own scale
+    if (qb == 0 && tid == 0) *q.scale_slot = 0.0f;
+    const int64_t i = (int64_t)qb * kSmallQuantPerWg + (int64_t)tid * 16;
+    const bool live = i < nx;
+    const int64_t src = live ? i : 0;
+    quant16_block(*(const u32x4*)(q.x + src), *(const u32x4*)(q.x + src + 8), live, q.xq + i, q.xs + (i >> 7),
+                  (tid & 7) == 0);
+    return;
+  }
   float s;
   if (q.static_scale) {
     s = *q.static_scale;

@@ -37,7 +37,8 @@ from typing import Dict, Iterable, List, Optional, Tuple
 
 import torch
 
-__all__ = ["MoEConfig", "CONFIGS", "gen_x", "gen_logits", "gen_weights", "LayerInputs", "make_layer"]
+__all__ = ["MoEConfig", "CONFIGS", "gen_x", "gen_logits", "gen_weights", "gen_weights_block", "gen_x_varied",
+           "LayerInputs", "make_layer"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -208,6 +209,56 @@ def gen_weights_per_expert(cfg: MoEConfig, seed: int = 0, device="cpu", E: Optio
             s[e] = sc
             w[e] = (v / sc).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
     return w13, w2, s13, s2
+
+
+_T_BLK, _T_XV = 8, 9
+
+
+def gen_weights_block(cfg: MoEConfig, seed: int = 0, device="cpu", E: Optional[int] = None):
+    """fp8 expert weights with one power-of-two (E8M0) scale per 128 x 128 block.
+
+    The normal draws of gen_weights, each 128 x 128 block multiplied by 2^r
+    with r drawn uniformly from -3..3 per block (so neighbouring blocks'
+    scales differ by up to 64x and a scale taken from a wrong block shows);
+    the block's E8M0 code is c = max(floor(log2 amax) + 127 - 8, 0) and its
+    values are stored as e4m3fn codes of W * 2^(127 - c) (below 512, clamped
+    to 448).  Returns (w13, w2, b13, b2): uint8 codes [E,2I,H] / [E,H,I] and
+    uint8 E8M0 codes [E,2I/128,H/128] / [E,H/128,I/128] on `device`.
+    """
+    if cfg.dtype != "fp8":
+        raise ValueError("block scales are for fp8 layers")
+    E = cfg.E if E is None else E
+    H, I = cfg.H, cfg.I
+    w13 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
+    w2 = torch.empty(E, H, I, dtype=torch.uint8, device=device)
+    b13 = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.uint8, device=device)
+    b2 = torch.empty(E, H // 128, I // 128, dtype=torch.uint8, device=device)
+    for e in range(E):
+        for w, b, t, rows, cols, std in ((w13, b13, _T_W13, 2 * I, H, 1.0 / math.sqrt(H)),
+                                         (w2, b2, _T_W2, H, I, 1.0 / math.sqrt(I))):
+            v = _expert_normal(seed, t, e, rows, cols, std, device)
+            gr = _gen(seed, _T_BLK, e * 2 + (t == _T_W2), device)
+            r = torch.randint(-3, 4, (rows // 128, cols // 128), generator=gr, device=device).to(torch.float32)
+            blocks = v.view(rows // 128, 128, cols // 128, 128) * torch.exp2(r)[:, None, :, None]
+            amax = blocks.abs().amax(dim=(1, 3))
+            _, ex = torch.frexp(amax)  # amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+            c = torch.clamp(ex - 1 + 127 - 8, 0, 254)
+            b[e] = c.to(torch.uint8)
+            q = blocks * torch.exp2((127 - c).to(torch.float32))[:, None, :, None]
+            w[e] = q.clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8).view(rows, cols)
+    return w13, w2, b13, b2
+
+
+def gen_x_varied(H: int, M: int, seed: int = 0, sub: int = 0) -> torch.Tensor:
+    """Hidden states whose tokens and 128-element groups differ in magnitude:
+    N(0,1) times 2^a per token and 2^b per group, a and b drawn from -4..4, so
+    that per-group activation scales differ.  bf16 [M, H] on the host."""
+    x = gen_x(H, M, seed, sub).to(torch.float32)
+    g = _gen(seed, _T_XV, sub, "cpu")
+    a = torch.randint(-4, 5, (M, 1), generator=g).to(torch.float32)
+    b = torch.randint(-4, 5, (M, H // 128), generator=g).to(torch.float32)
+    f = torch.exp2(a + torch.repeat_interleave(b, 128, dim=1))
+    return (x * f).to(torch.bfloat16)
 
 
 @dataclasses.dataclass

@@ -46,12 +46,27 @@ def err_norm(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
     return float(np.abs(y_gpu - y_ref).max() / max(np.abs(y_ref).max(), 1e-30))
 
 
-def err_rows(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
-    """The same figure per token, max over tokens of max_n |dy_m| / max_n |y_ref_m|,
-    so that rows of small magnitude are held to the same bound."""
+def row_errs(y_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Per token max_n |dy_m| / max_n |y_ref_m|, so that rows of small
+    magnitude are held to the same bound."""
     num = np.abs(y_gpu - y_ref).max(axis=1)
     den = np.maximum(np.abs(y_ref).max(axis=1), 1e-30)
-    return float((num / den).max()) if num.size else 0.0
+    return num / den
+
+
+# Per-token bound of the block-scaled fp8 mode.  The fp8 matrix instructions
+# of gfx950 do not sum their products at fp32 precision: against exact sums
+# of random e4m3 operands spread over the format's range, their results are
+# off by up to about 2^-13 of the sum of |products| (both the 16x16x128 and
+# the 16x16x32 forms; narrow-range operands and the fp32 accumulator add are
+# exact).  So the kernel's fp32 h differs from the definition's by ~1e-4 of
+# its row and some of h's e4m3 rounding decisions come out on the other side
+# of a midpoint.  Block scaling puts every 128-element group's largest
+# values in the format's top binade, where a step is 1/8 to 1/16 of the value,
+# and the per-token maximum of those moves grows with the token count: about
+# 1.3e-2 at 600 tokens, 2.4e-2 at 1100 and 3.0e-2 at 4096.  The whole-output
+# bound TOL holds for every token in every mode.
+TOL_TOKEN_BLOCK = 5e-2
 
 
 def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuning=None, n_shared=0,
@@ -65,9 +80,12 @@ def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuni
     ES, KS = cfg.E + n_shared, cfg.k + n_shared
     # activation scales and per-tensor weight scales are floats; per-row
     # weight scales are [E,rows] tensors, passed as they are
-    sc = lambda v: (None if v is None else v.to(DEV, torch.float32).contiguous() if isinstance(v, torch.Tensor)
+    # (uint8 block-scale codes pass unchanged)
+    sc = lambda v: (None if v is None else v.to(DEV).contiguous() if isinstance(v, torch.Tensor) and
+                    v.dtype == torch.uint8 else v.to(DEV, torch.float32).contiguous() if isinstance(v, torch.Tensor)
                     else torch.tensor([v], dtype=torch.float32, device=DEV))
-    blk, cap = moe.fused_align_shape(M, ES, cfg.H, cfg.I, KS, cfg.dtype, deterministic)
+    block_scaled = isinstance(s13, torch.Tensor) and s13.dtype == torch.uint8
+    blk, cap = moe.fused_align_shape(M, ES, cfg.H, cfg.I, KS, cfg.dtype, deterministic, 3 if block_scaled else 0)
     out = dict(y=Guarded((M, cfg.H), torch.bfloat16, 0x7FC1), ids=Guarded((M, KS), torch.int32, -7),
                weights=Guarded((M, KS), torch.float32, 0x7FC00007), counts=Guarded((ES,), torch.int32, -7),
                offsets=Guarded((ES + 1,), torch.int32, -7), sorted_ids=Guarded((cap,), torch.int32, -7),
@@ -114,13 +132,20 @@ def run_oracle(cfg: MoEConfig, x, logits, weights, tokens=None, x_scale=None, h_
     if tokens is None:
         tokens = list(range(x.shape[0]))
     fp8 = cfg.dtype == "fp8"
-    all_h = fp8 and h_scale is None
+    # uint8 weight scales: E8M0 codes of 128 x 128 blocks (block-scaled mode),
+    # whose activation scales are per group (no h amax over all pairs)
+    blk = isinstance(s13, torch.Tensor) and s13.dtype == torch.uint8
+    all_h = fp8 and h_scale is None and not blk
     need = sorted(set(ids.ravel().tolist()) if all_h else set(ids[tokens].ravel().tolist()))
     need += [cfg.E + s for s in range(n_shared)]
     experts = {e: (w13[e].cpu(), w2[e].cpu()) for e in need}
     t0 = time.time()
-    out = oracle.layer(x, logits, None, None, cfg.k, cfg.dtype, s13, s2, x_scale=x_scale, h_scale=h_scale,
-                       tokens=tokens, experts=experts, n_shared=n_shared)
+    if blk:
+        out = oracle.layer(x, logits, None, None, cfg.k, cfg.dtype, x_scale=x_scale, h_scale=h_scale, tokens=tokens,
+                           experts=experts, n_shared=n_shared, w13_block=s13.cpu(), w2_block=s2.cpu())
+    else:
+        out = oracle.layer(x, logits, None, None, cfg.k, cfg.dtype, s13, s2, x_scale=x_scale, h_scale=h_scale,
+                           tokens=tokens, experts=experts, n_shared=n_shared)
     out["seconds"] = time.time() - t0
     return out
 
@@ -154,13 +179,18 @@ def compare(cfg: MoEConfig, M: int, seed: int = 0, weights=None, tokens=None, x_
     assert np.allclose(gpu["weights"][:, :k], ref["weights"], rtol=1e-6, atol=1e-6), "topk weights differ"
     if cfg.dtype == "fp8":
         assert gpu["scales"][0] == np.float32(ref["s_x"]), (gpu["scales"][0], ref["s_x"])
-        assert abs(gpu["scales"][1] / ref["s_h"] - 1) < 1e-4, (gpu["scales"][1], ref["s_h"])
+        if ref["s_h"] == 0.0:  # block-scaled: no tensor scales, both reported as 0
+            assert gpu["scales"][1] == 0.0, gpu["scales"][1]
+        else:
+            assert abs(gpu["scales"][1] / ref["s_h"] - 1) < 1e-4, (gpu["scales"][1], ref["s_h"])
     rows = list(range(M)) if tokens is None else list(tokens)
     e = err_norm(gpu["y"][rows], ref["y"])
-    er = err_rows(gpu["y"][rows], ref["y"])
-    say("  err=%.3e per-token %.3e (tol %.0e) on %s tokens, oracle %.1fs"
-        % (e, er, TOL[cfg.dtype], "all" if tokens is None else len(rows), ref["seconds"]))
+    er = float(row_errs(gpu["y"][rows], ref["y"]).max()) if rows else 0.0
+    block_scaled = isinstance(weights[2], torch.Tensor) and weights[2].dtype == torch.uint8
+    tol_tok = TOL_TOKEN_BLOCK if block_scaled else TOL[cfg.dtype]
+    say("  err=%.3e per-token %.3e (tol %.0e, per token %.0e) on %s tokens, oracle %.1fs"
+        % (e, er, TOL[cfg.dtype], tol_tok, "all" if tokens is None else len(rows), ref["seconds"]))
     assert np.isfinite(gpu["y"]).all()
     assert e <= TOL[cfg.dtype], "output error %.3e above %.0e" % (e, TOL[cfg.dtype])
-    assert er <= TOL[cfg.dtype], "per-token output error %.3e above %.0e" % (er, TOL[cfg.dtype])
+    assert er <= tol_tok, "per-token output error %.3e above %.0e" % (er, tol_tok)
     return e, gpu, ref

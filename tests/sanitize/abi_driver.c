@@ -55,12 +55,13 @@ static void helpers(void) {
           for (int dt = 0; dt < 3; ++dt) {
             const int M = Ms[a], E = Es[b], k = ks[c], H = HIs[d], I = HIs[(d + 3) % 7];
             (void)moe_fused_workspace_size(M, E, H, I, k, (moe_dtype_t)dt);
-            for (int det = 0; det < 3; ++det) {
-              int32_t blk = 0;
-              int64_t cap = 0;
-              moe_status_t rc = moe_fused_align_shape(M, E, H, I, k, (moe_dtype_t)dt, det, &blk, &cap);
-              if (rc == MOE_OK) CHECK(blk == 16 || blk == 128);
-            }
+            for (int det = 0; det < 3; ++det)
+              for (int ws = -1; ws < 5; ++ws) {
+                int32_t blk = 0;
+                int64_t cap = 0;
+                moe_status_t rc = moe_fused_align_shape(M, E, H, I, k, (moe_dtype_t)dt, det, ws, &blk, &cap);
+                if (rc == MOE_OK) CHECK(blk == 16 || blk == 128);
+              }
             for (int B = 1; B <= 512; B *= 2) (void)moe_align_capacity(M, k, E, B);
           }
   for (int s = -1; s < 6; ++s) CHECK(moe_status_string((moe_status_t)s) != NULL);

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 10
+    assert lib.moe_abi_version() == 11
 
 
 def capacity_formula(M, k, E, B):
@@ -79,22 +79,24 @@ def test_workspace_size(lib):
     assert lib.moe_fused_workspace_size(4, 8, 256, 512, 2, 7) == 0  # unknown dtype
 
 
-def align_shape(lib, M, E, H, I, k, dtype, det=0):
+def align_shape(lib, M, E, H, I, k, dtype, det=0, mode=0):
     b, c = ctypes.c_int32(-1), ctypes.c_int64(-1)
-    rc = lib.moe_fused_align_shape(M, E, H, I, k, dtype, det, ctypes.byref(b), ctypes.byref(c))
+    rc = lib.moe_fused_align_shape(M, E, H, I, k, dtype, det, mode, ctypes.byref(b), ctypes.byref(c))
     return rc, b.value, c.value
 
 
-@pytest.mark.parametrize("M,E,H,I,k,dtype,det,block", [
-    (4, 8, 256, 512, 2, 0, 0, 16),          # decode
-    (4096, 128, 4096, 1536, 8, 1, 0, 128),  # fp8 with 32768 pairs: prefill path
-    (4096, 128, 4096, 1536, 8, 1, 1, 16),   # deterministic mode: decode path at every M
-    (4096, 128, 4096, 1536, 8, 0, 0, 16),   # bf16: decode path at every M
-    (1023, 8, 512, 512, 8, 1, 0, 16),       # 8184 pairs: below the prefill threshold
-    (1024, 8, 512, 512, 8, 1, 0, 128),      # 8192 pairs
+@pytest.mark.parametrize("M,E,H,I,k,dtype,det,mode,block", [
+    (4, 8, 256, 512, 2, 0, 0, 0, 16),          # decode
+    (4096, 128, 4096, 1536, 8, 1, 0, 0, 128),  # fp8 with 32768 pairs: prefill path
+    (4096, 128, 4096, 1536, 8, 1, 1, 0, 16),   # deterministic mode: decode path at every M
+    (4096, 128, 4096, 1536, 8, 1, 0, 3, 16),   # block-scaled: decode path at every M
+    (4096, 128, 4096, 1536, 8, 1, 0, 1, 128),  # per-row scales: prefill path
+    (4096, 128, 4096, 1536, 8, 0, 0, 0, 16),   # bf16: decode path at every M
+    (1023, 8, 512, 512, 8, 1, 0, 0, 16),       # 8184 pairs: below the prefill threshold
+    (1024, 8, 512, 512, 8, 1, 0, 0, 128),      # 8192 pairs
 ])
-def test_fused_align_shape(lib, M, E, H, I, k, dtype, det, block):
-    rc, b, c = align_shape(lib, M, E, H, I, k, dtype, det)
+def test_fused_align_shape(lib, M, E, H, I, k, dtype, det, mode, block):
+    rc, b, c = align_shape(lib, M, E, H, I, k, dtype, det, mode)
     assert rc == 0 and b == block and c == capacity_formula(M, k, E, block)
     # the workspace holds the sort-and-pad arrays of both modes
     assert lib.moe_fused_workspace_size(M, E, H, I, k, dtype) >= 4 * c + 4 * (c // b)
@@ -104,9 +106,11 @@ def test_fused_align_shape_invalid(lib):
     assert align_shape(lib, 4, 8, 256, 512, 9, 0)[0] == 1     # k > E
     assert align_shape(lib, 4, 8, 256, 512, 2, 3)[0] == 1     # unknown dtype
     assert align_shape(lib, 4, 8, 256, 512, 2, 0, 2)[0] == 1  # unknown mode
+    assert align_shape(lib, 4, 8, 256, 512, 2, 1, 0, 4)[0] == 1  # unknown weight scale mode
+    assert align_shape(lib, 4, 8, 256, 512, 2, 0, 0, 3)[0] == 1  # block-scaled bf16
     assert align_shape(lib, 4, 8, 200, 512, 2, 0)[0] == 2     # H not a multiple of 128
     b = ctypes.c_int32(0)
-    assert lib.moe_fused_align_shape(4, 8, 256, 512, 2, 0, 0, ctypes.byref(b), None) == 1
+    assert lib.moe_fused_align_shape(4, 8, 256, 512, 2, 0, 0, 0, ctypes.byref(b), None) == 1
 
 
 FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on these paths
@@ -165,7 +169,10 @@ def fused_args(**kw):
     (dict(dtype=1), 1),                  # fp8 without weight scales
     (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE + 1), 1),  # misaligned scale
     (dict(weight_scale_mode=1), 1),                   # per-channel weight scales in bf16 mode
-    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_mode=3), 1),  # unknown scale mode
+    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_mode=4), 1),  # unknown scale mode
+    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_mode=3, x_scale=FAKE), 1),  # block: static x scale
+    (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_mode=3, h_scale=FAKE), 1),  # block: static h scale
+    (dict(weight_scale_mode=3), 1),                                           # block-scaled in bf16 mode
     (dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE, weight_scale_mode=-1), 1),  # unknown scale mode
     (dict(weight_scale_mode=2), 1),                          # per-expert weight scales in bf16 mode
     (dict(dtype=1, w13_scale=FAKE + 4, w2_scale=FAKE, weight_scale_mode=1), 1),  # rows need 16-byte alignment
