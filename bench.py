@@ -130,6 +130,7 @@ def main() -> int:
         print("--per-channel and --per-expert apply to the fp8 workloads: give --config qwen3|deepseek|prefill",
               file=sys.stderr)
         return 2
+    peaks = achieved_peaks()
     if args.config is not None:
         line = measure(args.config, args)
     else:
@@ -143,8 +144,60 @@ def main() -> int:
         line["workloads"] = extra
     for key in ("metric_value",):
         line.pop(key, None)
+    line["achieved_peaks"] = peaks
+    for roof in [line["roofline"]] + [w["roofline"] for w in line.get("workloads", {}).values()]:
+        for r in (roof, roof.get("other_kernel")):
+            if r:
+                ceil = peaks["hbm_read_gbs"] if r["bound"] == "hbm" else peaks["fp8_mfma_tflops"]
+                r["frac_of_achieved_peak"] = round(r["achieved"] / ceil, 4) if (
+                    r["bound"] == "hbm" or r["peak"] == FP8_PEAK_TFLOPS) else None
     print(json.dumps(line), flush=True)
     return 0
+
+
+def achieved_peaks(reps: int = 5) -> dict:
+    """What this GPU delivers, from the probes of libmoe_probes.so, timed
+    with HIP events on the launch stream: the read bandwidth of a 4 GiB
+    streaming read (16 times the last-level cache, so HBM) and the issue
+    rate of independent 32x32x64 fp8 MFMAs on all compute units; the best of
+    `reps` calls each."""
+    import torch
+    from moe_layer_align_amd import probes
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    grid_r = 8192
+    sink = torch.empty(grid_r, dtype=torch.int32, device=dev)
+    grid_m, iters = 512, 2000
+    out = torch.empty(grid_m * 16, dtype=torch.float32, device=dev)
+
+    def best(fn):
+        fn()  # warm
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    t_read = best(lambda: probes.hbm_read(buf, sink, grid_r, stream))
+    t_mfma = best(lambda: probes.mfma_fp8_loop(out, grid_m, iters, stream))
+    torch.cuda.synchronize()
+    if not torch.all(out == 64.0 * iters):
+        raise RuntimeError("MFMA probe returned wrong sums")
+    flops = grid_m * 4 * iters * 4 * 2.0 * 32 * 32 * 64
+    res = dict(hbm_read_gbs=round(nbytes / t_read / 1e9, 1), fp8_mfma_tflops=round(flops / t_mfma / 1e12, 1),
+               how="best of %d: streaming read of 4 GiB by %d workgroups; %d workgroups x 4 waves x %d rounds of "
+                   "4 independent 32x32x64 fp8 MFMAs (libmoe_probes.so)" % (reps, grid_r, grid_m, iters))
+    log("achieved peaks: %s" % res)
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def measure(config: str, args, cpu_seconds=None) -> dict:

@@ -1,0 +1,68 @@
+/*
+ * moe_probes.h -- C ABI of the measurement probes (libmoe_probes.so).
+ *
+ * Not part of the layer: three small kernels that measure what an MI355X
+ * delivers for the resources the fused MoE layer is bound by, so that its
+ * roofline fractions can be read against achieved as well as nameplate
+ * ceilings, and the summation precision of the fp8 matrix instructions that
+ * the fp8 layer's tolerance rests on.  The layer's decode products stream
+ * expert weights from HBM and its prefill products run on the fp8 matrix
+ * cores (wagnersolution, "AWS describes a fused MoE optimization for the
+ * NVIDIA Hopper architecture", body: the fused kernel's throughput and
+ * latency goals; "Fused MoE on Hopper, ...", TL;DR: FP8 experts).
+ *
+ * Conventions as in moe.h: device pointers owned by the caller, `stream` a
+ * hipStream_t as void* (NULL = default stream), arguments checked on the
+ * host before anything is enqueued (MOE_ERR_INVALID_ARG, nothing enqueued),
+ * MOE_ERR_DEVICE when the launch fails.  The caller times a probe with HIP
+ * events recorded on the same stream around the call.
+ */
+#ifndef MOE_MI355X_PROBES_H
+#define MOE_MI355X_PROBES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ABI version of this header. */
+int32_t moe_probes_abi_version(void);
+
+/* Streaming read of `bytes` bytes at `buf` (16-byte aligned, bytes a
+ * multiple of 16) by `grid` workgroups of 256 threads (1..2^20), each thread
+ * reading 16-byte words with four loads in flight, grid-stride.  Writes
+ * sink[g] (uint32 [grid]) = XOR of all 32-bit words that workgroup g read,
+ * so every load is live; the XOR of sink over all g is the XOR of the whole
+ * buffer.  Achieved read bandwidth = bytes / the call's duration; a buffer
+ * well above the 256 MB last-level cache measures HBM. */
+moe_status_t moe_probe_hbm_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, void* stream);
+
+/* fp8 matrix-core issue rate: `grid` workgroups of four waves (1..2^20),
+ * every wave running `iters` rounds (1..2^20) of four independent
+ * 32x32x64 e4m3 MFMAs (the prefill products' instruction) on register
+ * operands of 1.0 with unit scales.  Each round adds 64 to every element of
+ * the four accumulators; lane 0 of wave w writes out[4w + j] = the first
+ * element of accumulator j, which is 64 * iters (exact up to 2^24).
+ * out: fp32 [grid * 4 * 4].  Achieved rate = grid * 4 waves * iters * 4 *
+ * 2*32*32*64 flops / the call's duration. */
+moe_status_t moe_probe_mfma_fp8_loop(float* out, int32_t grid, int32_t iters, void* stream);
+
+/* One wave: C[r][c] = c0 + 2^(sa-127) * 2^(sb-127) * sum over k < 128 of
+ * A[r][k] * B[c][k], for e4m3 codes A, B [16][128] row-major (16-byte
+ * aligned) and fp32 C [16][16], as the fp8 matrix instructions compute it:
+ * form 0 = one 16x16x128 block-scaled MFMA (sa, sb: E8M0 codes 0..254);
+ * form 1 = four 16x16x32 MFMAs accumulating in order (unit scales only, sa
+ * and sb must be 127).  Comparing C with the exact sum shows the
+ * instructions' own summation precision. */
+moe_status_t moe_probe_fp8_dot(const uint8_t* A, const uint8_t* B, float* C, int32_t sa, int32_t sb, float c0,
+                               int32_t form, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_PROBES_H */

@@ -1,4 +1,5 @@
-"""Ahead-of-time build of the gfx950 HIP library (libmoe_mi355x.so).
+"""Ahead-of-time build of the gfx950 HIP libraries: the layer
+(libmoe_mi355x.so) and the measurement probes (libmoe_probes.so).
 
 Compiles the translation units under moe_layer_align_amd/csrc with hipcc for
 gfx950, in parallel, and links them into the package directory.  Every unit
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 UNITS = ["moe_api.hip", "launch_decode_bf16.hip", "launch_decode_fp8.hip", "launch_decode_fp8_static.hip",
          "launch_prefill.hip", "launch_layer1.hip"]
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
+PROBE_UNITS = ["probes.hip"]
+PROBE_LIB = os.path.join(PKG, "libmoe_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -37,17 +40,18 @@ def _clean(stderr: str) -> str:
     return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l)
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpdir:
-        procs = []
-        for unit in UNITS:
-            obj = os.path.join(tmpdir, unit.replace(".hip", ".o"))
-            cmd = [HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, unit), "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            procs.append((unit, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
-                                                      text=True)))
+def _compile_link(units, lib, inc, verbose, extra, tmpdir, tag):
+    """Start the compiles of `units`; returns a function that waits for them
+    and links `lib`."""
+    procs = []
+    for unit in units:
+        obj = os.path.join(tmpdir, tag + "_" + unit.replace(".hip", ".o"))
+        cmd = [HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, unit), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((unit, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+
+    def finish():
         objs, failed = [], []
         for unit, obj, p in procs:
             _, err = p.communicate()
@@ -60,7 +64,7 @@ def build(verbose: bool = False, extra=()) -> str:
             objs.append(obj)
         if failed:
             raise RuntimeError("hipcc failed on %s" % ", ".join(failed))
-        tmp = LIB + ".tmp%d" % os.getpid()
+        tmp = lib + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -68,7 +72,19 @@ def build(verbose: bool = False, extra=()) -> str:
         if res.returncode != 0:
             sys.stderr.write(_clean(res.stderr) + "\n")
             raise RuntimeError("hipcc link failed (%d)" % res.returncode)
-    os.replace(tmp, LIB)
+        os.replace(tmp, lib)
+    return finish
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Build both libraries (all units compile in parallel); returns the
+    layer library's path."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpdir:
+        layer = _compile_link(UNITS, LIB, inc, verbose, extra, tmpdir, "layer")
+        probes = _compile_link(PROBE_UNITS, PROBE_LIB, inc, verbose, extra, tmpdir, "probes")
+        layer()
+        probes()
     return LIB
 
 

@@ -23,8 +23,8 @@ def lib():
     return m.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -41,6 +41,28 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for n in declared_functions():
         assert hasattr(lib, n), n
+
+
+def test_probe_library_exports_its_header():
+    # the measurement probes' library (include/moe_probes.h): loads on the
+    # CPU, exports every declared function, and rejects bad arguments before
+    # any launch
+    from moe_layer_align_amd import probes
+    if not os.path.exists(probes.LIB_PATH):
+        pytest.fail("libmoe_probes.so is not built; run __graft_entry__.build()")
+    plib = probes.load()
+    names = declared_functions(os.path.join(ROOT, "include", "moe_probes.h"))
+    assert set(names) >= {"moe_probes_abi_version", "moe_probe_hbm_read", "moe_probe_mfma_fp8_loop",
+                          "moe_probe_fp8_dot"}
+    for n in names:
+        assert hasattr(plib, n), n
+    assert plib.moe_probe_hbm_read(None, 16, 1, 16, None) == 1
+    assert plib.moe_probe_hbm_read(16, 15, 1, 16, None) == 1       # size not a multiple of 16
+    assert plib.moe_probe_hbm_read(16, 16, 0, 16, None) == 1       # empty grid
+    assert plib.moe_probe_mfma_fp8_loop(16, 1, 0, None) == 1        # no iterations
+    assert plib.moe_probe_fp8_dot(16, 16, 16, 255, 127, 0.0, 0, None) == 1  # NaN scale code
+    assert plib.moe_probe_fp8_dot(16, 16, 16, 120, 127, 0.0, 1, None) == 1  # form 1 has no scales
+    assert plib.moe_probe_fp8_dot(16, 16, 16, 127, 127, 0.0, 2, None) == 1  # unknown form
 
 
 def test_status_strings(lib):
