@@ -1,6 +1,6 @@
-"""Spacing between the fp8 matrix instructions and the first reads of their
-results, in the gfx950 assembly of every unit of both libraries (CPU only:
-hipcc -S, no GPU).
+"""Checks on the gfx950 assembly of every unit of both libraries (CPU only:
+hipcc -S, no GPU): the spacing between the fp8 matrix instructions and the
+first reads of their results, and that no kernel spills to scratch memory.
 
 The hardware does not hold back an instruction that reads an MFMA's result
 registers before the MFMA has written them: the compiler must put enough
@@ -14,6 +14,12 @@ This test follows every control-flow path from every scaled MFMA to the
 first instruction that reads its destination registers and fails if any
 path is shorter than those spacings, so that such a miss cannot reach a
 product kernel unnoticed.
+
+Scratch: every kernel keeps its state in registers and LDS (private segment
+size 0).  A build of the prefill product whose registers spilled to scratch
+faulted the GPU on its first run (its code was never kept, so the fault was
+not traced); a kernel that spills is therefore not run before its scratch
+accesses have been checked.
 """
 import collections
 import heapq
@@ -191,3 +197,13 @@ def test_every_scaled_mfma_read_is_spaced(assembly):
                     short.append((unit, func["name"][:80], label, kind, dist))
     assert counts["16x16x128"] > 0 and counts["32x32x64"] > 0  # the scan saw the fp8 products
     assert not short, short[:10]
+
+
+def test_no_kernel_uses_scratch(assembly):
+    spill = []
+    for unit, text in assembly.items():
+        names = re.findall(r"^\s*\.name:\s+(\S+)", text, flags=re.M)
+        sizes = [int(v) for v in re.findall(r"^\s*\.private_segment_fixed_size:\s+(\d+)", text, flags=re.M)]
+        assert len(sizes) >= 1 and len(names) >= len(sizes), unit
+        spill += [(unit, n) for n, v in zip(names, sizes) if v != 0]
+    assert not spill, spill[:10]
