@@ -44,12 +44,17 @@ moe_status_t moe_probe_hbm_read(const void* buf, size_t bytes, int32_t grid, uin
 /* fp8 matrix-core issue rate: `grid` workgroups of four waves (1..2^20),
  * every wave running `iters` rounds (1..2^20) of four independent
  * 32x32x64 e4m3 MFMAs (the prefill products' instruction) on register
- * operands of 1.0 with unit scales.  Each round adds 64 to every element of
- * the four accumulators; lane 0 of wave w writes out[4w + j] = the first
- * element of accumulator j, which is 64 * iters (exact up to 2^24).
- * out: fp32 [grid * 4 * 4].  Achieved rate = grid * 4 waves * iters * 4 *
- * 2*32*32*64 flops / the call's duration. */
-moe_status_t moe_probe_mfma_fp8_loop(float* out, int32_t grid, int32_t iters, void* stream);
+ * operands with unit scales.  random_operands 0: every operand 1.0, so each
+ * round adds 64 to every accumulator element; 1: fixed pseudo-random e4m3
+ * bytes per lane (no NaN codes), the same every round, whose bit switching
+ * draws power as real data does (the clock the hardware then holds is lower).
+ * Lane 0 of wave w writes out[4w + j] = the first element of accumulator j:
+ * 64 * iters (exact up to 2^24) with operands 1.0, else iters times the
+ * one-round value up to fp32 accumulation.  out: fp32 [grid * 4 * 4].
+ * Other random_operands values: MOE_ERR_INVALID_ARG.  Achieved rate =
+ * grid * 4 waves * iters * 4 * 2*32*32*64 flops / the call's duration. */
+moe_status_t moe_probe_mfma_fp8_loop(float* out, int32_t grid, int32_t iters, int32_t random_operands,
+                                     void* stream);
 
 /* One wave: C[r][c] = c0 + 2^(sa-127) * 2^(sb-127) * sum over k < 128 of
  * A[r][k] * B[c][k], for e4m3 codes A, B [16][128] row-major (16-byte

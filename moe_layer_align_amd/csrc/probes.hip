@@ -48,13 +48,29 @@ __global__ __launch_bounds__(kReadThreads) void hbm_read_kernel(const u32x4* __r
 
 // fp8 matrix-core issue rate: every wave runs `iters` rounds of four
 // independent 32x32x64 e4m3 MFMAs (the prefill tile's instruction) on
-// register operands holding 1.0 (code 0x38) with unit scales, so each round
-// adds 64 to every accumulator element; lane 0 of each wave stores its four
-// accumulators' first elements.
-__global__ __launch_bounds__(256) void mfma_fp8_loop_kernel(float* __restrict__ out, int iters) {
+// register operands with unit scales, and lane 0 of each wave stores its four
+// accumulators' first elements.  Operands: 1.0 everywhere (code 0x38, so each
+// round adds 64 to every accumulator element), or, with `random_ops`, bytes
+// of a per-lane integer hash with the lowest mantissa bit cleared (never the
+// NaN codes 0x7F / 0xFF), whose switching draws power the way real weights and
+// activations do; the hardware then holds a lower clock.
+__device__ __forceinline__ unsigned probe_hash(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(256) void mfma_fp8_loop_kernel(float* __restrict__ out, int iters, int random_ops) {
   i32x8 a, b;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = b[i] = 0x38383838;
+  for (int i = 0; i < 8; ++i) {
+    const unsigned seed = (threadIdx.x * 16u + (unsigned)i) * 2u;
+    a[i] = random_ops ? (int)(probe_hash(seed) & 0xFEFEFEFEu) : 0x38383838;
+    b[i] = random_ops ? (int)(probe_hash(seed + 1u) & 0xFEFEFEFEu) : 0x38383838;
+  }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int it = 0; it < iters; ++it) {
     c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
@@ -114,7 +130,7 @@ moe_status_t launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK :
 
 extern "C" {
 
-int32_t moe_probes_abi_version(void) { return 1; }
+int32_t moe_probes_abi_version(void) { return 2; }
 
 moe_status_t moe_probe_hbm_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || grid < 1 || grid > (1 << 20)) return MOE_ERR_INVALID_ARG;
@@ -123,9 +139,11 @@ moe_status_t moe_probe_hbm_read(const void* buf, size_t bytes, int32_t grid, uin
   return launch_status();
 }
 
-moe_status_t moe_probe_mfma_fp8_loop(float* out, int32_t grid, int32_t iters, void* stream) {
+moe_status_t moe_probe_mfma_fp8_loop(float* out, int32_t grid, int32_t iters, int32_t random_operands,
+                                     void* stream) {
   if (!out || grid < 1 || grid > (1 << 20) || iters < 1 || iters > (1 << 20)) return MOE_ERR_INVALID_ARG;
-  mfma_fp8_loop_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(out, iters);
+  if (random_operands != 0 && random_operands != 1) return MOE_ERR_INVALID_ARG;
+  mfma_fp8_loop_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(out, iters, random_operands);
   return launch_status();
 }
 

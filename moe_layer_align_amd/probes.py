@@ -14,7 +14,7 @@ from . import MoEError, _stream
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_probes.so")
-_ABI = 1
+_ABI = 2
 _lib = None
 
 
@@ -34,7 +34,7 @@ def load():
     lib.moe_probe_hbm_read.restype = ctypes.c_int
     lib.moe_probe_hbm_read.argtypes = [vp, sz, i32, vp, vp]
     lib.moe_probe_mfma_fp8_loop.restype = ctypes.c_int
-    lib.moe_probe_mfma_fp8_loop.argtypes = [vp, i32, i32, vp]
+    lib.moe_probe_mfma_fp8_loop.argtypes = [vp, i32, i32, i32, vp]
     lib.moe_probe_fp8_dot.restype = ctypes.c_int
     lib.moe_probe_fp8_dot.argtypes = [vp, vp, vp, i32, i32, ctypes.c_float, i32, vp]
     _lib = lib
@@ -58,12 +58,15 @@ def hbm_read(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream: Optional[
            "moe_probe_hbm_read")
 
 
-def mfma_fp8_loop(out: torch.Tensor, grid: int, iters: int, stream: Optional[torch.cuda.Stream] = None):
-    """fp8 MFMA issue loop; out: float32 GPU tensor of at least grid*16 elements."""
+def mfma_fp8_loop(out: torch.Tensor, grid: int, iters: int, random_operands: bool = False,
+                  stream: Optional[torch.cuda.Stream] = None):
+    """fp8 MFMA issue loop (operands 1.0, or fixed pseudo-random bytes);
+    out: float32 GPU tensor of at least grid*16 elements."""
     if not (out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= grid * 16):
         raise ValueError("out: contiguous float32 GPU tensor of at least grid*16 elements")
     s = _stream(stream)
-    _raise(load().moe_probe_mfma_fp8_loop(out.data_ptr(), grid, iters, s), "moe_probe_mfma_fp8_loop")
+    _raise(load().moe_probe_mfma_fp8_loop(out.data_ptr(), grid, iters, int(bool(random_operands)), s),
+           "moe_probe_mfma_fp8_loop")
 
 
 def fp8_dot(A: torch.Tensor, B: torch.Tensor, sa: int = 127, sb: int = 127, c0: float = 0.0, form: int = 0,

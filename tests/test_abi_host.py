@@ -59,7 +59,8 @@ def test_probe_library_exports_its_header():
     assert plib.moe_probe_hbm_read(None, 16, 1, 16, None) == 1
     assert plib.moe_probe_hbm_read(16, 15, 1, 16, None) == 1       # size not a multiple of 16
     assert plib.moe_probe_hbm_read(16, 16, 0, 16, None) == 1       # empty grid
-    assert plib.moe_probe_mfma_fp8_loop(16, 1, 0, None) == 1        # no iterations
+    assert plib.moe_probe_mfma_fp8_loop(16, 1, 0, 0, None) == 1     # no iterations
+    assert plib.moe_probe_mfma_fp8_loop(16, 1, 1, 2, None) == 1     # unknown operand mode
     assert plib.moe_probe_fp8_dot(16, 16, 16, 255, 127, 0.0, 0, None) == 1  # NaN scale code
     assert plib.moe_probe_fp8_dot(16, 16, 16, 120, 127, 0.0, 1, None) == 1  # form 1 has no scales
     assert plib.moe_probe_fp8_dot(16, 16, 16, 127, 127, 0.0, 2, None) == 1  # unknown form

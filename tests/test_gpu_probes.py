@@ -3,7 +3,8 @@
 Each probe's result is checked against what it must compute, so that the
 figures bench.py reports from them measure real work: the streaming read's
 per-workgroup XORs fold to the XOR of the buffer; the MFMA loop's
-accumulators hold 64 * iters; the fp8 dot agrees with exact sums where the
+accumulators hold 64 * iters (operands 1.0), or iters times one round
+(pseudo-random operands); the fp8 dot agrees with exact sums where the
 instructions are exact (operands of one binade, power-of-two scales, the
 fp32 accumulator add) and stays within 2^-12 of the sum of |products| for
 operands spread over the whole e4m3 range, where the instructions' own
@@ -57,6 +58,21 @@ def test_mfma_loop_accumulates():
     probes.mfma_fp8_loop(out, grid, iters)
     torch.cuda.synchronize()
     assert torch.all(out == 64.0 * iters)
+
+
+def test_mfma_loop_random_operands_accumulate():
+    # the same product every round: iters rounds give iters times one round
+    grid = 40
+    one = torch.empty(grid * 16, dtype=torch.float32, device=DEV)
+    many = torch.empty_like(one)
+    probes.mfma_fp8_loop(one, grid, 1, random_operands=True)
+    probes.mfma_fp8_loop(many, grid, 64, random_operands=True)
+    torch.cuda.synchronize()
+    o1, o64 = one.cpu().double(), many.cpu().double()
+    assert torch.all(torch.isfinite(o1)) and o1.abs().max() > 0
+    assert torch.allclose(o64, 64 * o1, rtol=1e-5, atol=1e-6 * float(o1.abs().max()))
+    # every wave holds the same operands, so its four accumulators agree
+    assert torch.all(o1.view(-1, 4) == o1.view(-1, 4)[:, :1])
 
 
 @pytest.mark.parametrize("form", [0, 1])
