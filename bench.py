@@ -106,6 +106,10 @@ def main() -> int:
     ap.add_argument("--single-launch", action="store_true",
                     help="tiny token counts (at most 16 tokens and 64 pairs) run as one launch (tuning "
                          "single_launch = 1) instead of the default multi-launch path")
+    ap.add_argument("--down", choices=["auto", "token", "expert"], default="auto",
+                    help="down product of layers with at most 64 pairs: auto (default: per token, with the "
+                         "combine in the same launch), token (required), expert (per-expert down product and a "
+                         "separate finalize)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -245,16 +249,16 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
 
     router_w = gen_router_weights(cfg.E, cfg.H, 0, device=dev) if args.router_gemm else None
 
-    tuning = None
-    if args.single_launch:
-        small = lambda M: M <= 16 and M * KS <= 64 and cfg.E <= 256
-        tuning_for = {M: moe.Tuning(single_launch=1 if small(M) else 0) for M in cfg.ms}
+    down = {"auto": 0, "token": 1, "expert": -1}[args.down]
+    small = lambda M: M <= 16 and M * KS <= 64 and cfg.E <= 256
+    tok_ok = lambda M: M * KS <= 64
+    tuning_for = {M: moe.Tuning(single_launch=1 if (args.single_launch and small(M)) else 0,
+                                down_per_token=down if (down != 1 or tok_ok(M)) else 0) for M in cfg.ms}
 
     def run(c, events=None):
         moe.fused_forward(c["x"], None if args.router_gemm else c["lg"], w13, w2, cfg.k, cfg.dtype, s13_t, s2_t,
                           out=c["y"], workspace=c["ws"], expert_counts=c["counts"], stream=stream, events=events,
-                          router_w=router_w, n_shared=S,
-                          tuning=tuning_for[c["M"]] if args.single_launch else tuning)
+                          router_w=router_w, n_shared=S, tuning=tuning_for[c["M"]])
 
     def flush(i):
         if flush_buf is not None:
@@ -439,6 +443,9 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
             "shared_experts": S,
             "logits_source": "computed in the layer from router weights" if args.router_gemm else "given",
             "single_launch": "at M <= 16 with at most 64 pairs" if args.single_launch else "off",
+            "down_product": {"auto": "per token with the combine at <= 64 pairs, else per expert + finalize",
+                             "token": "per token with the combine where it fits",
+                             "expert": "per expert + finalize"}[args.down],
         },
         "per_m": per_m,
         "roofline": roof,

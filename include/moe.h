@@ -170,6 +170,15 @@ typedef struct {
                                 path (default: on MI355X a grid barrier costs about as much as the kernel
                                 boundary it replaces).  Single-launch calls on one GPU must not overlap
                                 (they share the barrier's device counters) */
+  int32_t down_per_token;    /* layers of at most 64 pairs M*(top_k+S): 1 = the down product and the
+                                weighted combine as one launch, a workgroup per (16 output rows, token)
+                                summing the token's pairs in a fixed order (MOE_ERR_UNSUPPORTED where it
+                                does not fit: deterministic or block-scaled mode, more pairs, or a dynamic
+                                fp8 h scale with (top_k+S)*I above 64 KB); -1 = the per-expert down
+                                product and the finalize; 0 = default: per token where it fits and the
+                                tokens that share an expert would not re-read much of its W2 (always at
+                                M = 1; small experts up to 64 pairs), unless a down-product field above
+                                (gemm2_ksplit, gemm2_wave_ksplit, gemm2_stream_tiles) is set */
 } moe_tuning_t;
 
 /*

@@ -41,7 +41,7 @@ class Tuning(ctypes.Structure):
                 ("token_tiles", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("gemm2_wave_ksplit", ctypes.c_int32), ("gemm1_stream_tiles", ctypes.c_int32),
                 ("gemm2_stream_tiles", ctypes.c_int32), ("reverse_order", ctypes.c_int32),
-                ("single_launch", ctypes.c_int32)]
+                ("single_launch", ctypes.c_int32), ("down_per_token", ctypes.c_int32)]
 
 
 class _FusedArgs(ctypes.Structure):
@@ -64,7 +64,7 @@ class _FusedArgs(ctypes.Structure):
 
 
 _lib = None
-_ABI = 11  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
+_ABI = 12  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 UNITS = ["moe_api.hip", "launch_decode_bf16.hip", "launch_decode_fp8.hip", "launch_decode_fp8_static.hip",
-         "launch_prefill.hip", "launch_layer1.hip"]
+         "launch_prefill.hip", "launch_layer1.hip", "launch_down_token.hip"]
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 PROBE_UNITS = ["probes.hip"]
 PROBE_LIB = os.path.join(PKG, "libmoe_probes.so")

@@ -960,6 +960,150 @@ static __global__ __launch_bounds__(256) void finalize_kernel(const float* __res
   }
 }
 
+// --------------------------------------------------------------------------
+// Down product with the weighted top-k combine in its epilogue, for small
+// layers (at most kTokDownPairs pairs).  One workgroup owns 16 output rows of
+// one token and computes
+//   y[m][n0..n0+15] = bf16( sum_j w_j * d_j * (W2[e_j][n0..n0+15] . h_(m,j)) )
+// over the token's pairs j itself (d_j: the pair's fp8 dequantisation
+// s_h * s_w2, 1 in bf16).  The token's pairs use different experts, so the
+// four waves split the token's units (pair j, K chunk c) of 16 weight rows:
+// wave w takes units w, w + 4, ..., two at a time (two weight tiles and two h
+// chunks in flight, the two cross products of the MFMA pair unused); every
+// MFMA's sixteen B columns hold the same h chunk and column 0's results are
+// used.  Each wave adds its units' weighted, dequantised sums in unit order,
+// and the four waves' sums are added in wave order through LDS.  So every
+// output is one workgroup's fixed sequence of operations: no partial sums in
+// HBM, no atomics, no finalize launch, repeated calls give the same bits.
+// With a dynamic fp8 h scale the workgroup first quantises its token's h
+// rows into LDS (the token's pairs m*kk..m*kk+kk-1 are consecutive rows of h).
+// --------------------------------------------------------------------------
+constexpr int kTokDownPairs = 64;     // layers with at most this many pairs M*kk
+constexpr int kTokDownLds = 65536;    // LDS of the staged e4m3 h rows of one token (dynamic scale)
+
+struct DownTokArgs {
+  const uint8_t* w2;       // [E][H][I]
+  const uint8_t* h;        // [P][I] in HFMT
+  const int32_t* ids;      // [M*kk] expert of pair m*kk+j
+  const float* topk_w;     // [M*kk] routing weight of pair m*kk+j
+  uint16_t* y;             // [M][H] bf16
+  int H, I, kk;            // kk: pairs per token (top_k + shared experts)
+  int kchunks;             // K chunks per pair's product (divides I / k-step)
+  const float* w_scale;    // fp8: s_w2 per tensor, per expert (w_es) or per row ([E][H], w_cs)
+  int w_cs = 0, w_es = 0;
+  const float* h_scale;    // fp8 static: s_h
+  const unsigned* h_amax;  // fp8 dynamic: max |h| (float bits)
+  const float* x_scale;    // fp8: s_x in effect (reported)
+  float* scales_out;       // optional fp32[2]: s_x, s_h in effect
+};
+
+// Unit u of the token: pair u / kchunks, K chunk u % kchunks of csteps
+// k-steps.  Sets the lane's weight-row and h pointers and the pair.
+template <bool FP8, int HFMT>
+__device__ __forceinline__ void tok_unit(const DownTokArgs& a, const uint8_t* s_h8, int m, int n0, int u,
+                                         int csteps, const uint8_t*& pa, const uint8_t*& pb, int& f, int& e) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int KSTEP = FP8 ? 128 : 32;
+  constexpr int LB = FP8 ? 32 : 16;
+  constexpr int HSZ = HFMT == H_BF16 ? 2 : (HFMT == H_F32 ? 4 : 1);
+  const int lane = threadIdx.x & 63, r16 = lane & 15, kq = lane >> 4;
+  const int j = u / a.kchunks, c = u - j * a.kchunks;
+  const int kbeg = c * csteps * KSTEP;
+  f = m * a.kk + j;
+  e = a.ids[f];
+  pa = a.w2 + ((int64_t)e * a.H + n0 + r16) * a.I * ESZ + (int64_t)kbeg * ESZ + kq * LB;
+  if constexpr (HFMT == H_F32)
+    pb = s_h8 + j * a.I + kbeg + kq * LB;  // e4m3 in LDS
+  else
+    pb = a.h + ((int64_t)f * a.I + kbeg) * HSZ + kq * LB;
+}
+
+// The unit's sum for this lane's rows n0+4kq.., dequantised and weighted,
+// added to ysum in place.
+template <bool FP8>
+__device__ __forceinline__ void tok_add(const DownTokArgs& a, f32x4& ysum, const f32x4& acc, int f, int e, int n0,
+                                        float sh) {
+  const int kq = (threadIdx.x & 63) >> 4;
+  const float w = a.topk_w[f];
+  float d[4] = {w, w, w, w};
+  if constexpr (FP8) {
+    if (a.w_cs) {
+      const float* ws = a.w_scale + (int64_t)e * a.H + n0 + kq * 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[r] = w * (sh * ws[r]);
+    } else {
+      const float v = w * (sh * a.w_scale[(int64_t)e * a.w_es]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[r] = v;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ysum[r] += acc[r] * d[r];
+}
+
+// Grid: x = 16-row tiles of H, y = tokens.
+template <bool FP8, int HFMT, int U>
+static __global__ __launch_bounds__(256) void down_token_kernel(DownTokArgs a) {
+  extern __shared__ __align__(16) uint8_t s_h8[];  // dynamic fp8 h: the token's [kk][I] e4m3 rows
+  __shared__ f32x4 s_sum[4][4];                     // wave, row quad
+  constexpr int KSTEP = FP8 ? 128 : 32;
+  constexpr int SB = KSTEP * (FP8 ? 1 : 2);
+  const int m = blockIdx.y, n0 = blockIdx.x * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float sh = 1.0f;
+  if constexpr (FP8) sh = HFMT == H_F32 ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
+  if (FP8 && a.scales_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    a.scales_out[0] = *a.x_scale;
+    a.scales_out[1] = sh;
+  }
+  if constexpr (HFMT == H_F32) {
+    const float rh = 1.0f / sh;
+    const int n = a.kk * a.I;  // a multiple of 128
+    const float* src = (const float*)a.h + (int64_t)m * n;
+    for (int i = threadIdx.x * 16; i < n; i += 256 * 16) {
+      const f32x4 v0 = *(const f32x4*)(src + i), v1 = *(const f32x4*)(src + i + 4);
+      const f32x4 v2 = *(const f32x4*)(src + i + 8), v3 = *(const f32x4*)(src + i + 12);
+      *(u32x4*)(s_h8 + i) = u32x4{pack_e4m3x4(v0[0] * rh, v0[1] * rh, v0[2] * rh, v0[3] * rh),
+                                  pack_e4m3x4(v1[0] * rh, v1[1] * rh, v1[2] * rh, v1[3] * rh),
+                                  pack_e4m3x4(v2[0] * rh, v2[1] * rh, v2[2] * rh, v2[3] * rh),
+                                  pack_e4m3x4(v3[0] * rh, v3[1] * rh, v3[2] * rh, v3[3] * rh)};
+    }
+    __syncthreads();
+  }
+  const int csteps = a.I / KSTEP / a.kchunks;
+  const int units = a.kk * a.kchunks;
+  f32x4 ysum = {0.f, 0.f, 0.f, 0.f};
+  int u = wave;
+  for (; u + 4 < units; u += 8) {  // units u and u + 4 together
+    const uint8_t *pa[2], *pb[2];
+    int f[2], e[2];
+    tok_unit<FP8, HFMT>(a, s_h8, m, n0, u, csteps, pa[0], pb[0], f[0], e[0]);
+    tok_unit<FP8, HFMT>(a, s_h8, m, n0, u + 4, csteps, pa[1], pb[1], f[1], e[1]);
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_k<FP8, 2, 2, U, SB>(pa, pb, csteps, acc);
+    tok_add<FP8>(a, ysum, acc[0][0], f[0], e[0], n0, sh);
+    tok_add<FP8>(a, ysum, acc[1][1], f[1], e[1], n0, sh);
+  }
+  if (u < units) {
+    const uint8_t *pa[1], *pb[1];
+    int f, e;
+    tok_unit<FP8, HFMT>(a, s_h8, m, n0, u, csteps, pa[0], pb[0], f, e);
+    f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+    stream_k<FP8, 1, 1, U, SB>(pa, pb, csteps, acc);
+    tok_add<FP8>(a, ysum, acc[0][0], f, e, n0, sh);
+  }
+  if ((lane & 15) == 0) s_sum[wave][lane >> 4] = ysum;  // column 0: rows 4kq..4kq+3
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int q = threadIdx.x >> 2, r = threadIdx.x & 3;
+    const float v = ((s_sum[0][q][r] + s_sum[1][q][r]) + s_sum[2][q][r]) + s_sum[3][q][r];
+    const __bf16 b = (__bf16)v;
+    a.y[(int64_t)m * a.H + n0 + threadIdx.x] = __builtin_bit_cast(unsigned short, b);
+  }
+}
+
 // Stand-alone per-tensor e4m3 quantisation of fp32 data with a given scale.
 static __global__ __launch_bounds__(256) void quant_f32_kernel(const float* __restrict__ in, int64_t n,
                                                         const float* __restrict__ scale, uint8_t* __restrict__ out) {

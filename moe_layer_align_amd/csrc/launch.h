@@ -1,6 +1,7 @@
 // Host launchers of the expert products, one translation unit per family of
 // kernel instantiations (so that the library's kernels compile in parallel):
 //   launch_decode_bf16.hip, launch_decode_fp8.hip  decode products
+//   launch_down_token.hip                           down product + combine per token
 //   launch_prefill.hip                              prefill products
 // Each launcher picks the template instance for the run-time variant and
 // enqueues it on the stream; it returns false when the variant is not built.
@@ -27,6 +28,11 @@ bool launch_gemm2_bf16(const DecodeShape& s, hipStream_t st, const Gemm2Args& a)
 // hf: H_F32 (dynamic h scale) or H_E4M3 (static)
 bool launch_gemm1_fp8(int hf, const DecodeShape& s, hipStream_t st, const Gemm1Args& a);
 bool launch_gemm2_fp8(int hf, const DecodeShape& s, hipStream_t st, const Gemm2Args& a);
+
+// Down product with the weighted combine per token (small layers):
+// hf H_BF16 (bf16 layers), H_F32 or H_E4M3 (fp8); u: k-steps per pipeline
+// stage; lds: the staged e4m3 h rows of a token (dynamic fp8 h scale).
+bool launch_down_token(bool fp8, int hf, int u, dim3 grid, size_t lds, hipStream_t st, const DownTokArgs& a);
 
 // Persistent prefill product: mode 0 gate/up, 1 down; hdyn: dynamic h
 // scale; pc: one weight scale per row.  The kernel's dynamic LDS ceiling is

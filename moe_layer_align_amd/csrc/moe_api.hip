@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <type_traits>
 
@@ -56,6 +57,8 @@ moe_status_t launch_status() {
 }
 
 constexpr int kDownLdsMax = 65536;  // LDS of one down-product workgroup staging e4m3 h
+constexpr double kTokDownCachedW2 = 4.0 * (1 << 20);     // one XCD's L2
+constexpr double kTokDownRepeatBytes = 16.0 * (1 << 20);  // repeated W2 reads the saved launch is worth
 
 // Largest K split of the down product that the workspace holds partial sums
 // for (ksplit * P * H fp32): as many slices as fit 64 MB, at most 16, and in
@@ -151,6 +154,7 @@ struct Plan {
   int nt1, passes1, u1, ks1, tw1;          // gate/up (tw1 > 0: long-stream variant)
   int nt2, passes2, u2, ks2, wks2, lds2, tw2;  // down (tw2 > 0: long-stream variant)
   int rev;                                  // reversed grid order (Segments::rev)
+  int tok, tok_chunks;                      // down product and combine per token (down_token_kernel)
 };
 
 bool valid_u(bool fp8, int u) { return fp8 ? (u == 1 || u == 2) : (u == 2 || u == 4); }
@@ -281,6 +285,30 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
   if (p->ks2 == 0) return MOE_ERR_UNSUPPORTED;
   p->lds2 = (qh ? p->nt2 * 16 * gemm2_lds_stride(I / p->ks2) : 0) +
             (blk ? gemm2_block_scale_bytes(p->nt2 * 16, I / p->ks2) : 0);
+
+  // Down product and combine per token (small layers): K chunks per pair so
+  // that the token has at least eight units (two per wave, streamed together)
+  // where I's k-steps split evenly.  Per token, every pair of an expert after
+  // its first reads that expert's W2 again: free while W2 fits an XCD's L2
+  // (the repeats hit it), else a whole matrix from HBM.  The default takes
+  // the per-token path when the expected repeats' bytes stay below what the
+  // saved launch is worth (16 MB, about 2.5 us of HBM time): always at
+  // M = 1, and with small experts (Qwen3-like) up to 64 pairs; not with a few
+  // large experts that many tokens share (Mixtral at M >= 2 measured up to 3x
+  // slower).
+  const int mode = t ? t->down_per_token : 0;
+  if (mode < -1 || mode > 1) return MOE_ERR_UNSUPPORTED;
+  const bool pinned = t && (t->gemm2_ksplit > 0 || t->gemm2_wave_ksplit > 0 || t->gemm2_stream_tiles != 0);
+  const bool tok_fits = !det && !blk && P <= kTokDownPairs && (!qh || (int64_t)k * I <= kTokDownLds);
+  if (mode == 1 && !tok_fits) return MOE_ERR_UNSUPPORTED;
+  const int Er = E - S, kr = k - S;
+  const double distinct = Er * (1.0 - std::pow(1.0 - (double)kr / Er, (double)M));  // expected routed experts
+  const double repeats = ((double)M * kr - distinct) + (double)S * (M - 1);
+  const double w2_bytes = (double)H * I * (fp8 ? 1 : 2);
+  const bool tok_pays = w2_bytes <= kTokDownCachedW2 || repeats * w2_bytes <= kTokDownRepeatBytes;
+  p->tok = tok_fits && (mode == 1 || (mode == 0 && !pinned && tok_pays)) ? 1 : 0;
+  p->tok_chunks = 1;
+  while (k * p->tok_chunks < 8 && nsteps2 % (2 * p->tok_chunks) == 0) p->tok_chunks *= 2;
   return MOE_OK;
 }
 
@@ -427,7 +455,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 11; }
+int32_t moe_abi_version(void) { return 12; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -820,6 +848,26 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   }
   rec(5);
   if ((rc = launch_status()) != MOE_OK) return rc;
+
+  // 4+5 for small layers: the down product with the weighted combine, one
+  // workgroup per (16 output rows, token)
+  if (plan.tok) {
+    rec(6);
+    DownTokArgs g{(const uint8_t*)a->w2, h, ids, wts, (uint16_t*)a->y, H, I, k, plan.tok_chunks, a->w2_scale};
+    g.w_cs = pc ? 1 : 0;
+    g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
+    g.h_scale = a->h_scale;
+    g.h_amax = h_amax;
+    g.x_scale = scale_slot;
+    g.scales_out = fp8 ? a->scales_out : nullptr;
+    const size_t lds = hf == H_F32 ? (size_t)k * I : 0;
+    if (!launch_down_token(fp8, hf, plan.u2, dim3((unsigned)(H / 16), (unsigned)M), lds, st, g))
+      return MOE_ERR_UNSUPPORTED;
+    rec(7);
+    rec(8);
+    rec(9);
+    return launch_status();
+  }
 
   // 4. down product (partial sums per K slice)
   rec(6);

@@ -69,7 +69,7 @@ def test_probe_library_exports_its_header():
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 11
+    assert lib.moe_abi_version() == 12
 
 
 def capacity_formula(M, k, E, B):
@@ -231,7 +231,7 @@ def test_fused_tuning_validation(lib):
     import moe_layer_align_amd as m
     for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17),
               m.Tuning(gemm2_wave_ksplit=3), m.Tuning(reverse_order=2), m.Tuning(single_launch=2),
-              m.Tuning(single_launch=-2)):
+              m.Tuning(single_launch=-2), m.Tuning(down_per_token=2), m.Tuning(down_per_token=-2)):
         args = fused_args(tuning=ctypes.pointer(t))
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 
@@ -269,6 +269,18 @@ def test_fused_single_launch_required_where_it_does_not_fit(lib):
     assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
     args = fused_args(tuning=ctypes.pointer(t), deterministic=1)
     assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
+
+
+def test_fused_down_per_token_required_where_it_does_not_fit(lib):
+    # more than 64 pairs, the deterministic and the block-scaled modes, and a
+    # dynamic fp8 h scale whose token rows (top_k * I bytes) exceed 64 KB
+    import moe_layer_align_amd as m
+    t = m.Tuning(down_per_token=1)
+    fp8 = dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE)
+    for kw in (dict(M=40, top_k=2), dict(deterministic=1), dict(weight_scale_mode=3, **fp8),
+               dict(top_k=8, I=16384, **fp8)):
+        args = fused_args(tuning=ctypes.pointer(t), **kw)
+        assert lib.moe_fused_forward(ctypes.byref(args), None) == 2, kw
 
 
 def test_fused_m0_is_noop(lib):

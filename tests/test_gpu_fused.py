@@ -557,3 +557,58 @@ def test_reverse_grid_order_is_bitwise_neutral(S):
 def test_shared_expert_stream_variants():
     t = moe.Tuning(gemm1_stream_tiles=2, gemm2_stream_tiles=2)
     compare(CONFIGS["qwen3"], 40, seed=46, n_shared=1, tuning=t)
+
+
+# ---------------------------------------------------------------- down product + combine per token
+# Layers of at most 64 pairs take, by default, the down product with the
+# weighted top-k combine in one launch: a workgroup per (16 output rows,
+# token) sums the token's pairs itself (tuning down_per_token; -1 takes the
+# per-expert down product and the finalize).  Both paths against the oracle,
+# over K chunk counts with an odd number of units per wave, shared experts,
+# every weight-scale mode, and repeated calls.
+TOK = moe.Tuning(down_per_token=1, single_launch=-1)
+EXP = moe.Tuning(down_per_token=-1, single_launch=-1)
+
+
+@pytest.mark.parametrize("dtype,xs,hs", [("bf16", None, None), ("fp8", None, None), ("fp8", 0.02, 0.02)])
+@pytest.mark.parametrize("M", [1, 5, 32])
+@pytest.mark.parametrize("path", ["token", "expert"])
+def test_down_per_token_small_layers(dtype, xs, hs, M, path):
+    compare(cfg_of(dtype, 8, 2, 512, 384), M, seed=80 + M, x_scale=xs, h_scale=hs,
+            tuning=TOK if path == "token" else EXP)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("E,k,I", [(1, 1, 1024), (6, 3, 512), (16, 7, 256), (16, 16, 512)])
+def test_down_per_token_unit_splits(dtype, E, k, I):
+    # pairs per token 1..16 with the K chunks the plan picks for them: paired
+    # units and a single unit left over per wave, idle waves (k = 1: one pair
+    # in eight chunks), one unit per wave (k = 16 in fp8 gets one chunk)
+    M = max(1, 64 // k)
+    compare(cfg_of(dtype, E, k, 256, I), M, seed=90 + k, tuning=TOK)
+
+
+def test_down_per_token_shared_experts_and_scale_modes():
+    cfg = cfg_of("fp8", 16, 7, 512, 512, logits="zipf")
+    M = 8  # 8 x (7 + 1) = 64 pairs
+    compare(cfg, M, seed=95, weights=gen_weights_per_channel(cfg_of("fp8", 17, 7, 512, 512), 95, device=DEV),
+            n_shared=1, tuning=TOK)
+    compare(cfg, M, seed=96, weights=gen_weights_per_expert(cfg, 96, device=DEV, E=17), n_shared=1, tuning=TOK)
+    compare(cfg, M, seed=97, n_shared=1, x_scale=0.015, h_scale=0.004, tuning=TOK)
+
+
+def test_down_per_token_is_the_default_and_repeats_bitwise():
+    # with no tuning a 64-pair layer takes the per-token path (same bits as
+    # requiring it), and repeated calls on a stale workspace give the same bits
+    cfg = CONFIGS["qwen3"]
+    M = 8
+    w13, w2, s13, s2 = gen_weights(cfg, 98, device=DEV)
+    x = gen_x(cfg.H, M, 98, sub=M).to(DEV)
+    lg = gen_logits(cfg, M, 98, sub=M).to(DEV)
+    t13, t2 = torch.tensor([s13], device=DEV), torch.tensor([s2], device=DEV)
+    ws = torch.empty(moe.workspace_size(M, cfg.E, cfg.H, cfg.I, cfg.k, "fp8"), dtype=torch.uint8, device=DEV)
+    ys = [moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", t13, t2, workspace=ws, tuning=t)
+          for t in (None, TOK, None, TOK)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])

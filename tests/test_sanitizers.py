@@ -20,8 +20,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HERE = os.path.join(ROOT, "tests", "sanitize")
 CSRC = os.path.join(ROOT, "moe_layer_align_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-UNITS = ["moe_api", "launch_decode_bf16", "launch_decode_fp8", "launch_decode_fp8_static", "launch_prefill",
-         "launch_layer1"]
+
+
+def _layer_units():
+    import moe_layer_align_amd.build as b  # the layer library's translation units, as built
+    return [u[:-len(".hip")] for u in b.UNITS]
+
+
+UNITS = _layer_units()
 # sanitizers on the host half of each hipcc compilation only
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=all"]
