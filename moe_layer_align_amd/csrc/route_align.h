@@ -177,6 +177,25 @@ static __global__ __launch_bounds__(1024) void router_logits_kernel(const uint16
   }
 }
 
+// Slot l16 of token m (l16 < K: the j-th routed expert e with its weight w;
+// K <= l16 < K+S: shared expert E + (l16 - K) with weight one) into ids/wts
+// (row stride K+S); returns whether the lane holds a pair of a real token,
+// and its expert in *e.
+__device__ __forceinline__ bool route_store(int m, int M, int E, int K, int S, int l16, int* e, float w,
+                                            int32_t* __restrict__ ids, float* __restrict__ wts) {
+  if (l16 >= K) {  // a shared expert's slot
+    *e = E + (l16 - K);
+    w = 1.0f;
+  }
+  const int KS = K + S;
+  const bool pair = m < M && l16 < KS;
+  if (pair) {
+    ids[(int64_t)m * KS + l16] = *e;
+    wts[(int64_t)m * KS + l16] = w;
+  }
+  return pair;
+}
+
 // S shared experts follow the E routed ones: slots K..K+S-1 of each token's
 // row of ids/wts (stride K+S) name experts E..E+S-1 with weight one, and the
 // expert counts cover all E+S.
@@ -192,17 +211,9 @@ static __global__ __launch_bounds__(256) void route_topk_kernel(const float* __r
     int e;
     float w;
     route_row<NPL>(logits + (int64_t)min(m, M - 1) * E, m < M, E, K, l16, &e, &w);
-    if (l16 >= K) {  // a shared expert's slot
-      e = E + (l16 - K);
-      w = 1.0f;
-    }
-    const int KS = K + S, ES = E + S;
-    const bool pair = m < M && l16 < KS;
-    if (pair) {
-      ids[(int64_t)m * KS + l16] = e;
-      wts[(int64_t)m * KS + l16] = w;
-    }
+    const bool pair = route_store(m, M, E, K, S, l16, &e, w, ids, wts);
     if (fa.hist) {  // this workgroup's expert counts, for the align step
+      const int ES = E + S;
       __shared__ int s_hist[kMaxExperts];
       for (int i = threadIdx.x; i < ES; i += 256) s_hist[i] = 0;
       __syncthreads();

@@ -612,3 +612,37 @@ def test_down_per_token_is_the_default_and_repeats_bitwise():
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
+
+
+# ---------------------------------------------------------------- router logits at larger M
+# With router weights the layer's logits are moe_router_logits' bits (the
+# same kernel, every 16 x 16 tile summed in one fixed order), the routing is
+# the oracle's on them and y the oracle's layer, at token counts past the
+# one-workgroup prologue and not a multiple of the router's 64-token tiles:
+# E = 8..256, shared experts, fp8 with a dynamic x scale, and the prefill path.
+@pytest.mark.parametrize("cfg,M,S", [
+    (MoEConfig("rg_bf16", E=8, k=2, H=256, I=512, dtype="bf16", ms=(300,), logits="normal"), 300, 0),
+    (MoEConfig("rg_fp8", E=64, k=6, H=1024, I=512, dtype="fp8", ms=(301,), logits="normal"), 301, 1),
+    (MoEConfig("rg_e256", E=256, k=8, H=512, I=256, dtype="fp8", ms=(257,), logits="normal"), 257, 0),
+    (MoEConfig("rg_pf", E=16, k=8, H=512, I=512, dtype="fp8", ms=(1100,), logits="normal"), 1100, 0),
+])
+def test_router_logits_at_larger_token_counts(cfg, M, S):
+    say("router weights %s M=%d S=%d" % (cfg.name, M, S))
+    w = gen_weights(cfg, 26, device=DEV, E=cfg.E + S)
+    x = gen_x(cfg.H, M, 26, sub=M)
+    wg = gen_router_weights(cfg.E, cfg.H, 26)
+    fp8 = cfg.dtype == "fp8"
+    sc = (lambda v: torch.tensor([v], device=DEV)) if fp8 else (lambda v: None)
+    lo = torch.empty(M, cfg.E, dtype=torch.float32, device=DEV)
+    ids = torch.empty(M, cfg.k + S, dtype=torch.int32, device=DEV)
+    y = moe.fused_forward(x.to(DEV), None, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]), topk_ids=ids,
+                          router_w=wg.to(DEV), logits_out=lo, n_shared=S)
+    alone = moe.router_logits(x.to(DEV), wg.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(lo.view(torch.int32), alone.view(torch.int32)), "logits differ from moe_router_logits"
+    ref_ids, _ = oracle.route(lo.cpu(), cfg.k)
+    assert np.array_equal(ids[:, :cfg.k].cpu().numpy(), ref_ids)
+    compare(cfg, M, seed=26, weights=w, logits=lo.cpu(), x=x, n_shared=S)
+    y2 = moe.fused_forward(x.to(DEV), lo, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]), n_shared=S)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "the layer on its own logits, given, gives other bits"
