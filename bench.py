@@ -61,14 +61,14 @@ SINGLE_SOURCES = ("moe_layer_align_amd/csrc/layer_small.h", "moe_layer_align_amd
                   "moe_layer_align_amd/csrc/route_align.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "ad7e9e2edeb1f13c73d6cb7b97e2731285f19d4fcd87be37127a938ea0ca37a0",
-                "bytes_per_launch": 1510150625},
-    "qwen3": {"src_sha256": "ad7e9e2edeb1f13c73d6cb7b97e2731285f19d4fcd87be37127a938ea0ca37a0",
-              "bytes_per_launch": 241755050},
-    "deepseek": {"src_sha256": "ad7e9e2edeb1f13c73d6cb7b97e2731285f19d4fcd87be37127a938ea0ca37a0",
-                 "bytes_per_launch": 3292560799},
-    "prefill": {"src_sha256": "f621dc48fc397a5fb03f177e419476c47058ec661e022bb55320c5f0a2d23658",
-                "bytes_per_launch": 3049336194},
+    "mixtral": {"src_sha256": "9011ecb3585ae31e8a4b5b47ea4fdbc5332314bc1e8bc6fdd5040720d41cf9f2",
+                "bytes_per_launch": 1510121827},
+    "qwen3": {"src_sha256": "9011ecb3585ae31e8a4b5b47ea4fdbc5332314bc1e8bc6fdd5040720d41cf9f2",
+              "bytes_per_launch": 241767974},
+    "deepseek": {"src_sha256": "9011ecb3585ae31e8a4b5b47ea4fdbc5332314bc1e8bc6fdd5040720d41cf9f2",
+                 "bytes_per_launch": 3292623699},
+    "prefill": {"src_sha256": "fc1be3b6af278ceec8b86c100c8f7c58542d22e5c2ca8bcd5e6e6b4747980a1a",
+                "bytes_per_launch": 3024756279},
 }
 
 
