@@ -1,4 +1,5 @@
-// Grouped expert products for large token counts (prefill), gfx950 fp8 MFMA.
+// Grouped expert products for large token counts (prefill), gfx950 MFMA: fp8
+// (32x32x64) and bf16 (32x32x16) layers.
 //
 // At prefill every active expert holds hundreds to thousands of tokens, so the
 // products are compute-bound and both operands are reused: a work item is a
@@ -7,7 +8,9 @@
 // the align step with a block of 128: block b holds tokens of expert
 // block_expert[b] only, padded with the sentinel, so an item's tokens share
 // one expert.  Weight rows stay the MFMA's A operand and tokens the B operand,
-// as in the decode kernels; the 32x32x64 fp8 MFMA is used.
+// as in the decode kernels; the 32x32x64 fp8 MFMA is used, or for bf16
+// layers four 32x32x16 bf16 MFMAs per 128-byte K-step (the tiles, the LDS
+// ring and its byte layout are the same).
 //
 // Four waves, one per SIMD, each own 64 weight rows x all 128 tokens (2 x 4
 // MFMA tiles, accumulators in AGPRs).  A K-step is 128 bytes (two MFMA
@@ -56,6 +59,13 @@ __device__ __forceinline__ f32x16 mfma32_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4
   i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 32x32x16 bf16 -> fp32.  A: lane l holds 8 bf16 (16 bytes) of row l%32 at
+// k = 8*(l/32); B: the same k of column l%32.  C as for mfma32_fp8.
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are
@@ -154,7 +164,7 @@ __device__ __forceinline__ bool pf_map(int L, int T, int nb, int* tile, int* blk
 // ---------------------------------------------------------------- products
 struct PrefillArgs {
   const uint8_t* w;        // W13 [E][2I][H] or W2 [E][H][I], e4m3
-  const uint8_t* act;      // gate/up: xq [M][H]; down: hq [P][I], e4m3
+  const uint8_t* act;      // gate/up: xq [M][H]; down: hq [P][I], e4m3 (bf16 layers: x and h, bf16)
   PrefillSeg seg;
   int H, I, top_k, P;
   int tiles;               // weight tiles: I/128 (128 gate + 128 up rows each) or H/256
@@ -290,8 +300,12 @@ __device__ __forceinline__ void pf_interleave() {
 // wave waits until at most twelve are outstanding: the loads of step s+2,
 // issued after those of step s+1.  Any other vector-memory operation (token
 // ids, epilogue stores) only makes that wait stricter.
-template <int MODE, bool HDYN, bool PC>
+// BF: bf16 layers (weights, x and h bf16, no scales; HDYN and PC false):
+//   a 128-byte K-step holds 64 elements, four 32x32x16 bf16 MFMA k-steps, and
+//   the gate/up epilogue stores h as bf16 for the down product.
+template <int MODE, bool HDYN, bool PC, bool BF = false>
 static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(PrefillArgs a) {
+  static_assert(!BF || (!HDYN && !PC), "bf16 layers have no scales");
   extern __shared__ __align__(16) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
   const int nb = *a.seg.num_padded / kPfTok;
@@ -305,7 +319,7 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the wave's branches scalar
-  const int K = MODE == 0 ? a.H : a.I;                        // contraction length (bytes)
+  const int K = (MODE == 0 ? a.H : a.I) * (BF ? 2 : 1);       // contraction length (bytes)
   const int nk = K / kPfBK;                                   // even, >= 4 (host)
   const int wrows = MODE == 0 ? 2 * a.I : a.H;                // rows of one expert's weight
   const int drow = lane >> 3, dchunk = lane & 7;              // DMA: row in an 8-row block, chunk position
@@ -373,27 +387,31 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
   };
 
   // fragment addresses within a stage: A tile i rows arow0 + arow_off(i) +
-  // lane%32, B tile j rows 32*j + lane%32; MFMA k-step ks of the step uses
-  // chunks 4*ks + 2*(lane/32) + c.  Tiles differ by whole 32-row multiples,
+  // lane%32, B tile j rows 32*j + lane%32.  fp8: MFMA k-step ks (64 bytes)
+  // of the step uses chunks 4*ks + 2*(lane/32) + c, c = 0, 1 (32 bytes per
+  // lane); bf16: MFMA k-step 2*ks + c (32 bytes) uses chunk 4*ks + 2*c +
+  // lane/32 (16 bytes per lane).  Tiles differ by whole 32-row multiples,
   // which leave the chunk swizzle unchanged, so a tile is a constant byte
   // offset from the (ks, c) base.
-  const int fr = lane & 31, fc = (lane >> 5) * 2;
+  const int fr = lane & 31, hl = lane >> 5;
   const int arow0 = MODE == 0 ? 32 * wave : 64 * wave;
   int baseA[2][2], baseB[2][2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      baseA[ks][c] = pf_swz(arow0 + fr, 4 * ks + fc + c);
-      baseB[ks][c] = kPfStageA + pf_swz(fr, 4 * ks + fc + c);
+      const int chunk = BF ? 4 * ks + 2 * c + hl : 4 * ks + 2 * hl + c;
+      baseA[ks][c] = pf_swz(arow0 + fr, chunk);
+      baseB[ks][c] = kPfStageA + pf_swz(fr, chunk);
     }
   // row offset of A tile i from arow0 (MODE 0: tile 0 gate, tile 1 the up
   // rows of the same features)
   auto arow_off = [](int i) { return MODE == 0 ? i * (kPfRows / 2) : 32 * i; };
 
   // epilogue constants
-  const float sa = MODE == 0 ? *a.a_scale : (HDYN ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.a_scale);
-  const float rhs = (MODE == 0 && !HDYN) ? 1.0f / *a.h_scale : 1.0f;
+  const float sa = BF ? 1.0f
+                      : (MODE == 0 ? *a.a_scale : (HDYN ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.a_scale));
+  const float rhs = (MODE == 0 && !HDYN && !BF) ? 1.0f / *a.h_scale : 1.0f;
   float hmax = 0.0f;
 
   PfSrc cs, ns;
@@ -420,7 +438,7 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
   // drained.
   auto item = [&](auto nj_tag) {
     constexpr int NJ = decltype(nj_tag)::value;
-    constexpr int NMF = 4 * NJ, NDS = 8 + 4 * NJ;
+    constexpr int NMF = (BF ? 8 : 4) * NJ, NDS = 8 + 4 * NJ;
     f32x16 acc[2][NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -450,8 +468,14 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = mfma32_fp8(F.a[ks][i][0], F.a[ks][i][1], F.b[ks][j][0], F.b[ks][j][1], acc[i][j]);
+          for (int j = 0; j < NJ; ++j) {
+            if constexpr (BF) {
+              acc[i][j] = mfma32_bf16(F.a[ks][i][0], F.b[ks][j][0], acc[i][j]);
+              acc[i][j] = mfma32_bf16(F.a[ks][i][1], F.b[ks][j][1], acc[i][j]);
+            } else {
+              acc[i][j] = mfma32_fp8(F.a[ks][i][0], F.a[ks][i][1], F.b[ks][j][0], F.b[ks][j][1], acc[i][j]);
+            }
+          }
     };
     // Every K-step but the last loads step k+3 of the ring: this item's, the
     // next item's or, after the last item, a dummy copy of this item's first
@@ -522,7 +546,7 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
     lds_u8* ep = smem + kPfRing + wave * kPfEpiWave;
     auto ep_at = [&](int t, int c) { return ep + t * 128 + ((c ^ (t & 7)) << 4); };
     const int rt = lane >> 3, rc = lane & 7;  // read-back: token rt + 8*rr, chunk rc
-    const float deq = PC ? 0.0f : sa * a.w_scale[(int64_t)cur.e * a.w_es];  // the expert's or tensor's scale
+    const float deq = (PC || BF) ? (BF ? 1.0f : 0.0f) : sa * a.w_scale[(int64_t)cur.e * a.w_es];  // the expert's or tensor's scale
     if (MODE == 0) {
       const int fbase = cur.tile * (kPfRows / 2) + 32 * wave;
       // per-row dequantisation of features fbase+8g+rq.. (gate) and I+.. (up)
@@ -551,7 +575,9 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
               hmax = fmaxf(hmax, fabsf(hv[q]));
             }
             const int64_t idx = (int64_t)f * a.I + fbase + 8 * g + rq;
-            if (HDYN) {  // fp32, so that h is rounded once, to e4m3, after the amax is known
+            if (BF) {  // bf16 h, as the decode path's bf16 layers keep it
+              *(u32x2*)(a.out + idx * 2) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+            } else if (HDYN) {  // fp32, so that h is rounded once, to e4m3, after the amax is known
               *(f32x4*)(a.out + idx * 4) = f32x4{hv[0], hv[1], hv[2], hv[3]};
             } else {
               *(unsigned*)(a.out + idx) = pack_e4m3x4(hv[0] * rhs, hv[1] * rhs, hv[2] * rhs, hv[3] * rhs);

@@ -34,10 +34,11 @@ bool launch_gemm2_fp8(int hf, const DecodeShape& s, hipStream_t st, const Gemm2A
 // stage; lds: the staged e4m3 h rows of a token (dynamic fp8 h scale).
 bool launch_down_token(bool fp8, int hf, int u, dim3 grid, size_t lds, hipStream_t st, const DownTokArgs& a);
 
-// Persistent prefill product: mode 0 gate/up, 1 down; hdyn: dynamic h
-// scale; pc: one weight scale per row.  The kernel's dynamic LDS ceiling is
-// raised once per kernel and device; false when that fails.
-bool launch_prefill_gemm(int mode, bool hdyn, bool pc, int wgs, hipStream_t st, const PrefillArgs& g);
+// Persistent prefill product: mode 0 gate/up, 1 down; bf: bf16 layer (no
+// scales); hdyn: dynamic fp8 h scale; pc: one weight scale per row.  The
+// kernel's dynamic LDS ceiling is raised once per kernel and device; false
+// when that fails.
+bool launch_prefill_gemm(int mode, bool bf, bool hdyn, bool pc, int wgs, hipStream_t st, const PrefillArgs& g);
 void launch_prefill_quant_h(const float* h, int64_t n, const unsigned* h_amax, uint8_t* hq, hipStream_t st);
 void launch_prefill_finalize(const uint16_t* part, const float* wts, uint16_t* y, int M, int H, int k,
                              const float* x_scale, const unsigned* h_amax, const float* h_scale, float* scales_out,

@@ -20,19 +20,21 @@ using namespace moe;
 namespace {
 
 constexpr int kAlignBlockFused = 16;   // token tile of the decode products' B operand
-constexpr int kPrefillMinPairs = 8192; // fp8 layers with at least this many pairs take the prefill products
+constexpr int kPrefillMinPairs = 8192; // layers with at least this many pairs take the prefill products
 
-// fp8 layers with many pairs use the tiled prefill products (token block 128,
+// Layers with many pairs use the tiled prefill products (token block 128,
 // weight tiles of 256 rows: 256 rows of H for the down product, 128 gate and
-// 128 up rows for the gate/up product).  Both contraction lengths (H and I)
-// must be an even number, at least four, of 128-byte K-steps.  The operand
-// loads take 32-bit byte offsets into one expert's weights and into the
-// activations.
+// 128 up rows for the gate/up product), fp8 or bf16.  Both contraction
+// lengths (H and I, in bytes) must be an even number, at least four, of
+// 128-byte K-steps.  The operand loads take 32-bit byte offsets into one
+// expert's weights and into the activations.
 bool use_prefill(int M, int k, moe_dtype_t dt, int H, int I) {
   const int64_t P = (int64_t)M * k, lim = INT32_MAX;
-  auto steps_ok = [](int K) { return K % (2 * kPfBK) == 0 && K >= 4 * kPfBK; };
-  return dt == MOE_DTYPE_FP8_E4M3 && P >= kPrefillMinPairs && H % kPfRows == 0 && I % (kPfRows / 2) == 0 &&
-         steps_ok(H) && steps_ok(I) && 2 * (int64_t)I * H <= lim && (int64_t)M * H <= lim && P * I <= lim;
+  const int esz = dt == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
+  auto steps_ok = [](int64_t K) { return K % (2 * kPfBK) == 0 && K >= 4 * kPfBK; };
+  return (dt == MOE_DTYPE_FP8_E4M3 || dt == MOE_DTYPE_BF16) && P >= kPrefillMinPairs && H % kPfRows == 0 &&
+         I % (kPfRows / 2) == 0 && steps_ok((int64_t)H * esz) && steps_ok((int64_t)I * esz) &&
+         2 * (int64_t)I * H * esz <= lim && (int64_t)M * H * esz <= lim && P * I * esz <= lim;
 }
 // Align block of the fused call: 128 on the prefill path, else 16.
 // decode_only: the deterministic and block-scaled modes take the decode path
@@ -552,20 +554,24 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   const int64_t P = (int64_t)M * k;
   rec(0);
   int32_t* hist = hist_usable(k) ? hist_buf : nullptr;
-  RouteFusedArgs fa{(const uint16_t*)a->x, H, a->x_scale ? nullptr : xamax_part, hdyn ? h_amax : nullptr, hist};
+  const bool bf = a->dtype == MOE_DTYPE_BF16;
+  RouteFusedArgs fa{(const uint16_t*)a->x, H, (bf || a->x_scale) ? nullptr : xamax_part, hdyn ? h_amax : nullptr,
+                    hist};
   launch_route(a->logits, M, E - S, k - S, S, ids, wts, fa, st);
   rec(1);
   if ((rc = launch_status()) != MOE_OK) return rc;
   rec(2);
   QuantXArgs q{};
-  q.x = (const uint16_t*)a->x;
-  q.n = (int64_t)M * H;
-  q.amax_part = xamax_part;
-  q.n_part = L.n_route_wg;
-  q.static_scale = a->x_scale;
-  q.xq = xq;
-  q.scale_slot = scale_slot;
-  launch_align(ids, P, E, kPfTok, o, q, (int)cdiv(q.n, kAlignQuantPerWg), st,
+  if (!bf) {
+    q.x = (const uint16_t*)a->x;
+    q.n = (int64_t)M * H;
+    q.amax_part = xamax_part;
+    q.n_part = L.n_route_wg;
+    q.static_scale = a->x_scale;
+    q.xq = xq;
+    q.scale_slot = scale_slot;
+  }
+  launch_align(ids, P, E, kPfTok, o, q, bf ? 0 : (int)cdiv(q.n, kAlignQuantPerWg), st,
                AlignHist{hist, (int)cdiv(M, 4 * kRouteRows), hist ? 16 / k : 0});
   rec(3);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -582,9 +588,9 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
   {
     const int T = I / (kPfRows / 2);  // 256-row tiles of W13: 128 gate + 128 up rows
     const int items = prefill_items(T);
-    PrefillArgs g{(const uint8_t*)a->w13, xq, seg, H, I, k, (int)P, T, items, a->w13_scale, scale_slot, nullptr,
-                  a->h_scale, h, h_amax, es};
-    if (!launch_prefill_gemm(0, hdyn, pc, std::min(wgs, items), st, g)) return MOE_ERR_DEVICE;
+    PrefillArgs g{(const uint8_t*)a->w13, bf ? (const uint8_t*)a->x : xq, seg, H, I, k, (int)P, T, items,
+                  a->w13_scale, scale_slot, nullptr, a->h_scale, h, h_amax, es};
+    if (!launch_prefill_gemm(0, bf, hdyn, pc, std::min(wgs, items), st, g)) return MOE_ERR_DEVICE;
   }
   rec(5);
   if ((rc = launch_status()) != MOE_OK) return rc;
@@ -599,13 +605,13 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
     const int items = prefill_items(T);
     PrefillArgs g{(const uint8_t*)a->w2, hq, seg, H, I, k, (int)P, T, items, a->w2_scale, a->h_scale, h_amax, nullptr,
                   (uint8_t*)part, nullptr, es};
-    if (!launch_prefill_gemm(1, hdyn, pc, std::min(wgs, items), st, g)) return MOE_ERR_DEVICE;
+    if (!launch_prefill_gemm(1, bf, hdyn, pc, std::min(wgs, items), st, g)) return MOE_ERR_DEVICE;
   }
   rec(7);
   if ((rc = launch_status()) != MOE_OK) return rc;
   rec(8);
   launch_prefill_finalize((const uint16_t*)part, wts, (uint16_t*)a->y, M, H, k, scale_slot, h_amax, a->h_scale,
-                          a->scales_out, st);
+                          bf ? nullptr : a->scales_out, st);
   rec(9);
   return launch_status();
 }

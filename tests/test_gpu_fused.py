@@ -646,3 +646,33 @@ def test_router_logits_at_larger_token_counts(cfg, M, S):
     y2 = moe.fused_forward(x.to(DEV), lo, w[0], w[1], cfg.k, cfg.dtype, sc(w[2]), sc(w[3]), n_shared=S)
     torch.cuda.synchronize()
     assert torch.equal(y, y2), "the layer on its own logits, given, gives other bits"
+
+
+# ---------------------------------------------------------------- bf16 prefill path
+# bf16 layers with at least 8192 pairs take the tiled prefill products too
+# (four 32x32x16 bf16 MFMAs per 128-byte K-step, bf16 h between the products,
+# no scales).  Every token against the oracle: the smallest shapes (four
+# K-steps in both products at H = I = 256 elements), a long K, many items per
+# workgroup, shared experts, an align histogram-free top-k (k = 9), and
+# repeated calls bitwise.
+@pytest.mark.parametrize("E,k,H,I,M,S", [(16, 8, 256, 256, 1100, 0), (16, 8, 1024, 512, 1100, 0),
+                                         (8, 2, 1024, 1024, 8192, 0), (16, 7, 512, 512, 1100, 1),
+                                         (16, 9, 512, 256, 1000, 0)])
+def test_prefill_path_bf16(E, k, H, I, M, S):
+    cfg = MoEConfig("pf_bf16", E=E, k=k, H=H, I=I, dtype="bf16", ms=(M,), logits="zipf")
+    assert moe.fused_align_shape(M, E + S, H, I, k + S, "bf16")[0] == 128  # the prefill path's block
+    compare(cfg, M, seed=60 + k, n_shared=S)
+
+
+def test_prefill_path_bf16_repeat_calls_bitwise():
+    cfg = MoEConfig("pf_bf16_rep", E=16, k=8, H=512, I=512, dtype="bf16", ms=(1100,), logits="zipf")
+    w = gen_weights(cfg, 16, device=DEV)
+    x = gen_x(cfg.H, 1100, 16, sub=1100).to(DEV)
+    lg = gen_logits(cfg, 1100, 16, sub=1100).to(DEV)
+    ws = torch.empty(moe.workspace_size(1100, cfg.E, cfg.H, cfg.I, cfg.k, "bf16"), dtype=torch.uint8, device=DEV)
+    ws.fill_(0x7F)
+    ys = [moe.fused_forward(x, lg, w[0], w[1], cfg.k, "bf16", workspace=ws).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert bool(ys[0].float().isfinite().all())
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
