@@ -1,11 +1,12 @@
 /*
  * moe_probes.h -- C ABI of the measurement probes (libmoe_probes.so).
  *
- * Not part of the layer: three small kernels that measure what an MI355X
+ * Not part of the layer: small kernels that measure what an MI355X
  * delivers for the resources the fused MoE layer is bound by, so that its
  * roofline fractions can be read against achieved as well as nameplate
  * ceilings, and the summation precision of the fp8 matrix instructions that
- * the fp8 layer's tolerance rests on.  The layer's decode products stream
+ * the fp8 layer's tolerance rests on, and what publishing partial results
+ * across XCDs inside a kernel costs.  The layer's decode products stream
  * expert weights from HBM and its prefill products run on the fp8 matrix
  * cores (wagnersolution, "AWS describes a fused MoE optimization for the
  * NVIDIA Hopper architecture", body: the fused kernel's throughput and
@@ -65,6 +66,19 @@ moe_status_t moe_probe_mfma_fp8_loop(float* out, int32_t grid, int32_t iters, in
  * instructions' own summation precision. */
 moe_status_t moe_probe_fp8_dot(const uint8_t* A, const uint8_t* B, float* C, int32_t sa, int32_t sb, float c0,
                                int32_t form, void* stream);
+
+/* The cost of publishing partial results to workgroups on other XCDs inside
+ * one kernel (each XCD has its own L2, not kept coherent with the others
+ * within a kernel), as a last-arriver combine would need: `grid` workgroups
+ * (1..2^20) each write 32 KB, buf[8192*g + i] = g + i for i < 8192 (buf: fp32
+ * [grid * 8192], 16-byte aligned), and then add one to cnt[g % 1024] (cnt:
+ * uint32 [1024], caller-zeroed; after the call it holds the number of
+ * workgroups that counted themselves in at each slot).  mode 0: plain
+ * stores; 1: plain stores and an agent-scope release fence (an L2
+ * writeback) before the count; 2: write-through stores (agent-scope atomic
+ * stores) completed before the count.  Other modes: MOE_ERR_INVALID_ARG.
+ * The caller times the call with events. */
+moe_status_t moe_probe_publish(float* buf, uint32_t* cnt, int32_t grid, int32_t mode, void* stream);
 
 #ifdef __cplusplus
 }

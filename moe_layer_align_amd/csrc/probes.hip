@@ -124,13 +124,41 @@ __global__ __launch_bounds__(64) void fp8_dot32_kernel(const uint8_t* __restrict
   for (int r = 0; r < 4; ++r) C[(4 * (l / 16) + r) * 16 + (l % 16)] = c[r];
 }
 
+// Publishing partial results to other XCDs inside one kernel: every
+// workgroup writes its 32 KB slice of buf (8192 floats, value blockIdx.x + i)
+// and then counts itself in at cnt[blockIdx.x % 1024], as a last-arriver
+// combine would; mode 0: plain stores (no publication: only this kernel's end
+// makes them visible to other XCDs), 1: plain stores and an agent-scope
+// release fence (an L2 writeback) before the count, 2: write-through stores
+// (agent-scope atomic stores) completed before the count.
+template <int MODE>
+__global__ __launch_bounds__(256) void publish_kernel(float* __restrict__ buf, unsigned* __restrict__ cnt) {
+  float* p = buf + (int64_t)blockIdx.x * 8192;
+  const float v = (float)blockIdx.x;
+  for (int i = threadIdx.x; i < 2048; i += 256) {
+    const f32x4 x = {v + 4 * i, v + 4 * i + 1, v + 4 * i + 2, v + 4 * i + 3};
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) __hip_atomic_store(p + 4 * i + q, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *(f32x4*)(p + 4 * i) = x;
+    }
+  }
+  if constexpr (MODE == 2) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores are performed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if constexpr (MODE == 1) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(cnt + (blockIdx.x & 1023), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 moe_status_t launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 }  // namespace
 
 extern "C" {
 
-int32_t moe_probes_abi_version(void) { return 2; }
+int32_t moe_probes_abi_version(void) { return 3; }
 
 moe_status_t moe_probe_hbm_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || grid < 1 || grid > (1 << 20)) return MOE_ERR_INVALID_ARG;
@@ -156,6 +184,16 @@ moe_status_t moe_probe_fp8_dot(const uint8_t* A, const uint8_t* B, float* C, int
     fp8_dot128_kernel<<<1, 64, 0, (hipStream_t)stream>>>(A, B, C, sa, sb, c0);
   else
     fp8_dot32_kernel<<<1, 64, 0, (hipStream_t)stream>>>(A, B, C, c0);
+  return launch_status();
+}
+
+moe_status_t moe_probe_publish(float* buf, uint32_t* cnt, int32_t grid, int32_t mode, void* stream) {
+  if (!buf || !cnt || grid < 1 || grid > (1 << 20) || mode < 0 || mode > 2) return MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)buf % 16) != 0 || ((uintptr_t)cnt % 4) != 0) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (mode == 0) publish_kernel<0><<<grid, 256, 0, st>>>(buf, cnt);
+  if (mode == 1) publish_kernel<1><<<grid, 256, 0, st>>>(buf, cnt);
+  if (mode == 2) publish_kernel<2><<<grid, 256, 0, st>>>(buf, cnt);
   return launch_status();
 }
 

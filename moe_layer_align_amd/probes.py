@@ -14,7 +14,7 @@ from . import MoEError, _stream
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_probes.so")
-_ABI = 2
+_ABI = 3
 _lib = None
 
 
@@ -35,6 +35,8 @@ def load():
     lib.moe_probe_hbm_read.argtypes = [vp, sz, i32, vp, vp]
     lib.moe_probe_mfma_fp8_loop.restype = ctypes.c_int
     lib.moe_probe_mfma_fp8_loop.argtypes = [vp, i32, i32, i32, vp]
+    lib.moe_probe_publish.restype = ctypes.c_int
+    lib.moe_probe_publish.argtypes = [vp, vp, i32, i32, vp]
     lib.moe_probe_fp8_dot.restype = ctypes.c_int
     lib.moe_probe_fp8_dot.argtypes = [vp, vp, vp, i32, i32, ctypes.c_float, i32, vp]
     _lib = lib
@@ -82,3 +84,15 @@ def fp8_dot(A: torch.Tensor, B: torch.Tensor, sa: int = 127, sb: int = 127, c0: 
     _raise(load().moe_probe_fp8_dot(A.data_ptr(), B.data_ptr(), C.data_ptr(), sa, sb, float(c0), form, s),
            "moe_probe_fp8_dot")
     return C
+
+
+def publish(buf: torch.Tensor, cnt: torch.Tensor, grid: int, mode: int, stream: Optional[torch.cuda.Stream] = None):
+    """Every workgroup writes its 32 KB of buf (float32 GPU tensor of at least
+    grid*8192 elements) and counts itself in at cnt[g % 1024] (int32 GPU
+    tensor of 1024, caller-zeroed); mode 0 plain stores, 1 + an agent-scope
+    release fence, 2 write-through stores."""
+    if not (buf.is_cuda and buf.dtype == torch.float32 and buf.is_contiguous() and buf.numel() >= grid * 8192):
+        raise ValueError("buf: contiguous float32 GPU tensor of at least grid*8192 elements")
+    if not (cnt.is_cuda and cnt.dtype == torch.int32 and cnt.numel() >= 1024):
+        raise ValueError("cnt: int32 GPU tensor of 1024 elements")
+    _raise(load().moe_probe_publish(buf.data_ptr(), cnt.data_ptr(), grid, mode, _stream(stream)), "moe_probe_publish")

@@ -53,7 +53,7 @@ def test_probe_library_exports_its_header():
     plib = probes.load()
     names = declared_functions(os.path.join(ROOT, "include", "moe_probes.h"))
     assert set(names) >= {"moe_probes_abi_version", "moe_probe_hbm_read", "moe_probe_mfma_fp8_loop",
-                          "moe_probe_fp8_dot"}
+                          "moe_probe_fp8_dot", "moe_probe_publish"}
     for n in names:
         assert hasattr(plib, n), n
     assert plib.moe_probe_hbm_read(None, 16, 1, 16, None) == 1
@@ -64,6 +64,8 @@ def test_probe_library_exports_its_header():
     assert plib.moe_probe_fp8_dot(16, 16, 16, 255, 127, 0.0, 0, None) == 1  # NaN scale code
     assert plib.moe_probe_fp8_dot(16, 16, 16, 120, 127, 0.0, 1, None) == 1  # form 1 has no scales
     assert plib.moe_probe_fp8_dot(16, 16, 16, 127, 127, 0.0, 2, None) == 1  # unknown form
+    assert plib.moe_probe_publish(16, 16, 1, 3, None) == 1                    # unknown mode
+    assert plib.moe_probe_publish(16, 16, 0, 0, None) == 1                    # empty grid
 
 
 def test_status_strings(lib):
@@ -114,7 +116,8 @@ def align_shape(lib, M, E, H, I, k, dtype, det=0, mode=0):
     (4096, 128, 4096, 1536, 8, 1, 1, 0, 16),   # deterministic mode: decode path at every M
     (4096, 128, 4096, 1536, 8, 1, 0, 3, 16),   # block-scaled: decode path at every M
     (4096, 128, 4096, 1536, 8, 1, 0, 1, 128),  # per-row scales: prefill path
-    (4096, 128, 4096, 1536, 8, 0, 0, 0, 16),   # bf16: decode path at every M
+    (4096, 128, 4096, 1536, 8, 0, 0, 0, 128),  # bf16 with 32768 pairs: prefill path too
+    (4096, 128, 4096, 1536, 8, 0, 1, 0, 16),   # bf16, deterministic mode: decode path
     (1023, 8, 512, 512, 8, 1, 0, 0, 16),       # 8184 pairs: below the prefill threshold
     (1024, 8, 512, 512, 8, 1, 0, 0, 128),      # 8192 pairs
 ])

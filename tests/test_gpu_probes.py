@@ -4,7 +4,8 @@ Each probe's result is checked against what it must compute, so that the
 figures bench.py reports from them measure real work: the streaming read's
 per-workgroup XORs fold to the XOR of the buffer; the MFMA loop's
 accumulators hold 64 * iters (operands 1.0), or iters times one round
-(pseudo-random operands); the fp8 dot agrees with exact sums where the
+(pseudo-random operands); the publish probe writes every workgroup's values
+and counts every workgroup once in each of its modes (their timings printed); the fp8 dot agrees with exact sums where the
 instructions are exact (operands of one binade, power-of-two scales, the
 fp32 accumulator add) and stays within 2^-12 of the sum of |products| for
 operands spread over the whole e4m3 range, where the instructions' own
@@ -121,3 +122,26 @@ def test_fp8_dot_summation_precision(form):
     print("fp8 dot form %d: max |C - exact| / sum|a*b| = %.3e (2^%.1f)"
           % (form, worst, np.log2(worst) if worst > 0 else -np.inf))
     assert worst <= 2.0 ** -12
+
+
+def test_publish_probe_writes_and_counts():
+    # every mode writes the same values and counts every workgroup once; the
+    # durations (best of five calls, 2048 workgroups x 32 KB) are printed
+    grid = 2048
+    buf = torch.empty(grid * 8192, dtype=torch.float32, device=DEV)
+    want = (torch.arange(grid, dtype=torch.float64)[:, None] + torch.arange(8192, dtype=torch.float64)[None, :])
+    for mode in (0, 1, 2):
+        best = None
+        for rep in range(5):
+            cnt = torch.zeros(1024, dtype=torch.int32, device=DEV)
+            buf.fill_(-1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            probes.publish(buf, cnt, grid, mode)
+            b.record()
+            b.synchronize()
+            best = a.elapsed_time(b) if best is None else min(best, a.elapsed_time(b))
+            assert int(cnt.sum()) == grid and bool((cnt == 2).all())
+        got = buf.view(grid, 8192).double().cpu()
+        assert torch.equal(got, want.float().double()), mode
+        print("publish mode %d: %.2f us for %d workgroups x 32 KB" % (mode, best * 1e3, grid))
