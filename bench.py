@@ -56,7 +56,8 @@ FLUSH_BYTES = 1 << 30
 # WRITE_SIZE runs of this script (scaled by the reading of a 1 GiB copy), and
 # the SHA-256 of the kernel sources they were taken on.  The figure is
 # reported only while those sources are unchanged.
-DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/moe_device.h")
+DECODE_SOURCES = ("moe_layer_align_amd/csrc/gemm_decode.h", "moe_layer_align_amd/csrc/layer_small.h",
+                  "moe_layer_align_amd/csrc/route_align.h", "moe_layer_align_amd/csrc/moe_device.h")
 SINGLE_SOURCES = ("moe_layer_align_amd/csrc/layer_small.h", "moe_layer_align_amd/csrc/gemm_decode.h",
                   "moe_layer_align_amd/csrc/route_align.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
@@ -110,6 +111,10 @@ def main() -> int:
                     help="down product of layers with at most 64 pairs: auto (default: per token, with the "
                          "combine in the same launch), token (required), expert (per-expert down product and a "
                          "separate finalize)")
+    ap.add_argument("--routing", choices=["auto", "separate"], default="auto",
+                    help="tiny layers (at most 16 tokens and 64 pairs, per-token down product): auto (default: "
+                         "the routing and sort-and-pad inside the gate/up launch, the layer in two launches, "
+                         "where that fits) or separate (routing launches of their own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -253,7 +258,13 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
     small = lambda M: M <= 16 and M * KS <= 64 and cfg.E <= 256
     tok_ok = lambda M: M * KS <= 64
     tuning_for = {M: moe.Tuning(single_launch=1 if (args.single_launch and small(M)) else 0,
-                                down_per_token=down if (down != 1 or tok_ok(M)) else 0) for M in cfg.ms}
+                                down_per_token=down if (down != 1 or tok_ok(M)) else 0,
+                                routing_in_gate_up=-1 if args.routing == "separate" else 0) for M in cfg.ms}
+
+    mode = 1 if per_channel else 2 if per_expert else 0
+    for c in calls:  # the launch sequence each call takes, from the library's own plan
+        c["path"] = moe.fused_path(c["M"], cfg.E, cfg.H, cfg.I, cfg.k, cfg.dtype, n_shared=S, weight_scale_mode=mode,
+                                   router_w=args.router_gemm, tuning=tuning_for[c["M"]])
 
     def run(c, events=None):
         moe.fused_forward(c["x"], None if args.router_gemm else c["lg"], w13, w2, cfg.k, cfg.dtype, s13_t, s2_t,
@@ -318,13 +329,14 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
     between, wall_ms = timed_pass((0, 2 * ns - 1), "layer spans")
     span_ms = between(0, 2 * ns - 1)
     # Pass B: the launches of the dominant kernels.  A call that takes the
-    # multi-launch path runs its gate/up product between events 4 and 5; one
-    # that takes the single-launch layer runs that one kernel between events 0
-    # and 1 (the library then records events 1..9 back to back after it).
+    # multi-launch or the two-launch path runs its gate/up launch between
+    # events 4 and 5; one that takes the single-launch layer runs that one
+    # kernel between events 0 and 1 (the library then records events 1..9
+    # back to back after it).
     between, _ = timed_pass((0, 1, 4, 5), "dominant-kernel launches")
     first_ms, g1_ms = between(0, 1), between(4, 5)
     for j, c in enumerate(calls):
-        c["single"] = cfg.name != "prefill" and statistics.median(g1_ms[j]) < 0.25 * statistics.median(first_ms[j])
+        c["single"] = c["path"] == "single_launch"
         c["kern_ms"] = first_ms[j] if c["single"] else g1_ms[j]
     layer_ms_per_step = sum(sum(v) for v in span_ms) / args.steps
 
@@ -348,7 +360,7 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
         kern_us = statistics.median(c["kern_ms"]) * 1e3
         entry = dict(M=c["M"], us=round(us, 2), active_experts=c["active"], weight_bytes=c["w_bytes"],
                      gbps=round(c["w_bytes"] / us / 1e3, 1), hbm_frac=round(c["w_bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
-                     tflops=round(c["flops"] / us / 1e6, 2), path="single launch" if c["single"] else "multi launch")
+                     tflops=round(c["flops"] / us / 1e6, 2), path=c["path"])
         if c["single"]:
             entry["single_launch_kernel_us"] = round(kern_us, 2)
         else:
@@ -394,12 +406,16 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
                                                   and not (args.no_flush or per_channel or per_expert
                                                            or args.shared or args.router_gemm)) else None
         r["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
+        ms_of = lambda paths: ",".join(str(c["M"]) for c in sel if c["path"] in paths)
+        two, dec = ms_of(("two_launches",)), ms_of(("decode", "decode_token_down"))
         r["kernel"] = ("prefill_gemm_kernel<0, *> (tiled gate/up product + SiLU*up)" if cfg.name == "prefill"
                        else "layer1_kernel (the whole layer in one cooperative launch) at M = %s"
                        % ",".join(str(c["M"]) for c in sel) if single
-                       else "gate/up product + SiLU*up (gemm1_decode_kernel, or gemm1_stream_kernel for fp8 "
-                            "layers whose plan takes the long-stream variant) at M = %s"
-                            % ",".join(str(c["M"]) for c in sel))
+                       else "; ".join(x for x in (
+                           "tiny_gate_up_kernel (routing, sort-and-pad and the gate/up product + SiLU*up in one "
+                           "launch) at M = %s" % two if two else "",
+                           "gate/up product + SiLU*up (gemm1_decode_kernel, or gemm1_stream_kernel for fp8 layers "
+                           "whose plan takes the long-stream variant) at M = %s" % dec if dec else "") if x))
         r["avg_launch_us"] = round(kern_ms * 1e3 / n, 2)
         r["launches"] = n
         r["kernel_ms_total"] = kern_ms
@@ -443,6 +459,9 @@ def measure(config: str, args, cpu_seconds=None) -> dict:
             "shared_experts": S,
             "logits_source": "computed in the layer from router weights" if args.router_gemm else "given",
             "single_launch": "at M <= 16 with at most 64 pairs" if args.single_launch else "off",
+            "routing": {"auto": "in the gate/up launch where the layer fits two launches",
+                        "separate": "launches of its own"}[args.routing],
+            "paths": {str(c["M"]): c["path"] for c in calls},
             "down_product": {"auto": "per token with the combine at <= 64 pairs, else per expert + finalize",
                              "token": "per token with the combine where it fits",
                              "expert": "per expert + finalize"}[args.down],

@@ -179,6 +179,19 @@ typedef struct {
                                 tokens that share an expert would not re-read much of its W2 (always at
                                 M = 1; small experts up to 64 pairs), unless a down-product field above
                                 (gemm2_ksplit, gemm2_wave_ksplit, gemm2_stream_tiles) is set */
+  int32_t routing_in_gate_up; /* tiny layers taking the per-token down product (at most 16 tokens and 64
+                                pairs, at most 256 routed experts, H a multiple of 512 in fp8 or of 128 in
+                                bf16, fp8 x of at most 8192 elements, not the single-launch layer): 1 = the
+                                layer in two launches, every gate/up workgroup routing, quantising and
+                                sorting the few tokens itself before its items (MOE_ERR_UNSUPPORTED where
+                                the layer would take another path); -1 = the routing launch of its own;
+                                0 = default: two launches where it fits and the gate/up product has at
+                                most 1024 items of 16 features (min(E+S, M*(top_k+S)) * I/16), unless a
+                                gate/up field above (gemm1_ksplit, token_tiles, unroll,
+                                gemm1_stream_tiles) is set.  The
+                                outputs are those of the routing launch of its own, bit for bit, wherever
+                                that path's gate/up product splits K over four waves (bf16; fp8 below 8
+                                tokens) */
 } moe_tuning_t;
 
 /*
@@ -316,6 +329,42 @@ moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream);
  */
 #define MOE_NUM_STAGES 5
 moe_status_t moe_fused_forward_profiled(const moe_fused_args_t* args, void* stream, void* const* events);
+
+/*
+ * The launch sequence a moe_fused_forward call on `args` takes.  Its stage
+ * events (moe_fused_forward_profiled) bracket these launches:
+ *   MOE_PATH_NONE               M = 0: nothing is launched
+ *   MOE_PATH_PREFILL            tiled prefill products: route, align with the
+ *                               x quantisation, gate/up, down (preceded in its
+ *                               stage by the h quantisation with a dynamic fp8
+ *                               h scale), finalize
+ *   MOE_PATH_DECODE             route, align (one launch for both at most 1024
+ *                               pairs), gate/up, down per expert, finalize
+ *   MOE_PATH_DECODE_TOKEN_DOWN  as MOE_PATH_DECODE up to the gate/up product,
+ *                               then the down product with the weighted
+ *                               combine per token (its down stage; the
+ *                               finalize stage is empty)
+ *   MOE_PATH_TWO_LAUNCHES       the routing, sort-and-pad and gate/up product
+ *                               in one launch (the gate/up stage; route and
+ *                               align are empty), then the per-token down
+ *                               product with the combine
+ *   MOE_PATH_SINGLE_LAUNCH      the whole layer in one launch (the route
+ *                               stage; the others are empty)
+ * A given router_w adds its logits product at the start of the route stage.
+ * The call validates `args` exactly as moe_fused_forward does, except that
+ * y and the workspace may be NULL and the workspace size is not checked, and
+ * returns the status moe_fused_forward would return before enqueuing
+ * anything; *path is written on MOE_OK only.  It enqueues nothing, reads no
+ * memory through the device pointers in `args` and needs no GPU.  path NULL:
+ * MOE_ERR_INVALID_ARG.
+ */
+#define MOE_PATH_NONE 0
+#define MOE_PATH_PREFILL 1
+#define MOE_PATH_DECODE 2
+#define MOE_PATH_DECODE_TOKEN_DOWN 3
+#define MOE_PATH_TWO_LAUNCHES 4
+#define MOE_PATH_SINGLE_LAUNCH 5
+moe_status_t moe_fused_path(const moe_fused_args_t* args, int32_t* path);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "MoEError", "load", "LIB_PATH", "route_topk", "router_logits", "align_capacity", "align", "quant_e4m3",
     "workspace_size", "fused_align_shape", "fused_forward", "Tuning", "STATUS", "NUM_STAGES", "STAGE_NAMES",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "fused_path", "PATH_NAMES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -28,6 +28,8 @@ DTYPE_BF16, DTYPE_FP8 = 0, 1
 NUM_STAGES = 5
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAGE_NAMES = ("route", "align", "gate_up", "down", "finalize")
+# moe_fused_path's MOE_PATH_* values, in order
+PATH_NAMES = ("none", "prefill", "decode", "decode_token_down", "two_launches", "single_launch")
 
 
 class MoEError(RuntimeError):
@@ -41,7 +43,8 @@ class Tuning(ctypes.Structure):
                 ("token_tiles", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("gemm2_wave_ksplit", ctypes.c_int32), ("gemm1_stream_tiles", ctypes.c_int32),
                 ("gemm2_stream_tiles", ctypes.c_int32), ("reverse_order", ctypes.c_int32),
-                ("single_launch", ctypes.c_int32), ("down_per_token", ctypes.c_int32)]
+                ("single_launch", ctypes.c_int32), ("down_per_token", ctypes.c_int32),
+                ("routing_in_gate_up", ctypes.c_int32)]
 
 
 class _FusedArgs(ctypes.Structure):
@@ -64,7 +67,7 @@ class _FusedArgs(ctypes.Structure):
 
 
 _lib = None
-_ABI = 12  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
+_ABI = 14  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():
@@ -98,6 +101,8 @@ def load():
     lib.moe_fused_forward_profiled.restype = ctypes.c_int
     lib.moe_fused_forward_profiled.argtypes = [ctypes.POINTER(_FusedArgs), vp, vp]
     lib.moe_fused_forward_noalloc.restype = ctypes.c_int
+    lib.moe_fused_path.restype = ctypes.c_int
+    lib.moe_fused_path.argtypes = [ctypes.POINTER(_FusedArgs), ctypes.POINTER(i32)]
     lib.moe_fused_forward_noalloc.argtypes = [ctypes.POINTER(_FusedArgs), vp]
     if lib.moe_abi_version() != _ABI:
         raise RuntimeError("libmoe_mi355x.so has ABI version %d, this binding expects %d: rebuild it"
@@ -209,6 +214,27 @@ def fused_align_shape(M: int, E: int, H: int, I: int, top_k: int, dtype: str, de
         M, E, H, I, top_k, DTYPE_FP8 if dtype == "fp8" else DTYPE_BF16, int(bool(deterministic)),
         int(weight_scale_mode), ctypes.byref(b), ctypes.byref(c)))
     return int(b.value), int(c.value)
+
+
+def fused_path(M: int, E: int, H: int, I: int, top_k: int, dtype: str = "bf16", n_shared: int = 0,
+               weight_scale_mode: int = 0, static_x_scale: bool = False, static_h_scale: bool = False,
+               router_w: bool = False, deterministic: bool = False, tuning: Optional[Tuning] = None) -> str:
+    """Name (PATH_NAMES) of the launch sequence fused_forward takes on a call
+    of this shape (moe_fused_path; host only, no GPU needed).  E and top_k
+    count the routed experts; static_x_scale/static_h_scale: fp8 scales given
+    by the caller; router_w: logits computed in the layer."""
+    fp8 = dtype == "fp8"
+    fake = 1 << 20  # moe_fused_path reads no memory through the pointers
+    args = _FusedArgs(
+        M=M, E=E, H=H, I=I, top_k=top_k, dtype=DTYPE_FP8 if fp8 else DTYPE_BF16, x=fake, w13=fake, w2=fake,
+        logits=None if router_w else fake, router_w=fake if router_w else None,
+        w13_scale=fake if fp8 else None, w2_scale=fake if fp8 else None,
+        x_scale=fake if static_x_scale else None, h_scale=fake if static_h_scale else None,
+        tuning=ctypes.pointer(tuning) if tuning is not None else None, weight_scale_mode=int(weight_scale_mode),
+        n_shared=int(n_shared), deterministic=int(bool(deterministic)))
+    p = ctypes.c_int32(-1)
+    _check("moe_fused_path", load().moe_fused_path(ctypes.byref(args), ctypes.byref(p)))
+    return PATH_NAMES[p.value]
 
 
 def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Tensor, w2: torch.Tensor, top_k: int,

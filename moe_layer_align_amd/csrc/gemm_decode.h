@@ -995,6 +995,8 @@ struct DownTokArgs {
   const unsigned* h_amax;  // fp8 dynamic: max |h| (float bits)
   const float* x_scale;    // fp8: s_x in effect (reported)
   float* scales_out;       // optional fp32[2]: s_x, s_h in effect
+  const float* wg_hmax = nullptr;  // fp8 dynamic, instead of h_amax: the gate/up workgroups' largest |h|
+  int n_wg = 0;                    // entries of wg_hmax
 };
 
 // Unit u of the token: pair u / kchunks, K chunk u % kchunks of csteps
@@ -1051,7 +1053,21 @@ static __global__ __launch_bounds__(256) void down_token_kernel(DownTokArgs a) {
   const int m = blockIdx.y, n0 = blockIdx.x * 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float sh = 1.0f;
-  if constexpr (FP8) sh = HFMT == H_F32 ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
+  if constexpr (HFMT == H_F32) {
+    if (a.wg_hmax) {  // the largest of the gate/up workgroups' maxima
+      __shared__ float s_m[4];
+      float m = 0.0f;
+      for (int i = threadIdx.x; i < a.n_wg; i += 256) m = fmaxf(m, a.wg_hmax[i]);
+      m = wave_max(m);
+      if (lane == 0) s_m[wave] = m;
+      __syncthreads();
+      sh = scale_from_amax(fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3])));
+    } else {
+      sh = scale_from_amax(__uint_as_float(*a.h_amax));
+    }
+  } else if constexpr (FP8) {
+    sh = *a.h_scale;
+  }
   if (FP8 && a.scales_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     a.scales_out[0] = *a.x_scale;
     a.scales_out[1] = sh;

@@ -49,5 +49,9 @@ void launch_prefill_finalize(const uint16_t* part, const float* wts, uint16_t* y
 // not all be resident at once; otherwise the launch's own status.
 struct Layer1Args;
 hipError_t launch_layer1(bool fp8, int hf, int wks, int grid, size_t lds, hipStream_t st, const Layer1Args& a);
+// The first launch of the two-launch layer for tiny token counts (routing,
+// quantisation, sort-and-pad and the gate/up product); false when the
+// dtype / h format is not built.
+bool launch_tiny_gate_up(bool fp8, int hf, int grid, hipStream_t st, const Layer1Args& a);
 
 }  // namespace moe

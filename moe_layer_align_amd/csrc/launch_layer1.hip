@@ -1,5 +1,6 @@
-// The single-launch layer for tiny token counts (layer_small.h): launch of the
-// instance for the dtype, h format and down-product wave split.
+// The small layers of layer_small.h: the single-launch layer (the instance
+// for the dtype, h format and down-product wave split) and the first launch of
+// the two-launch layer.
 #include <atomic>
 
 #include "launch.h"
@@ -40,6 +41,18 @@ const void* pick_wks(int wks) {
 }
 
 }  // namespace
+
+bool launch_tiny_gate_up(bool fp8, int hf, int grid, hipStream_t st, const Layer1Args& a) {
+  if (!fp8 && hf == H_BF16)
+    tiny_gate_up_kernel<false, H_BF16><<<grid, 256, 0, st>>>(a);
+  else if (fp8 && hf == H_F32)
+    tiny_gate_up_kernel<true, H_F32><<<grid, 256, 0, st>>>(a);
+  else if (fp8 && hf == H_E4M3)
+    tiny_gate_up_kernel<true, H_E4M3><<<grid, 256, 0, st>>>(a);
+  else
+    return false;
+  return true;
+}
 
 hipError_t launch_layer1(bool fp8, int hf, int wks, int grid, size_t lds, hipStream_t st, const Layer1Args& a) {
   const void* fn = !fp8 ? (hf == H_BF16 ? pick_wks<false, H_BF16>(wks) : nullptr)

@@ -100,6 +100,7 @@ constexpr int kLayer1NPL = 16;
 constexpr int kLayer1Sorted = kLayer1Pairs * 16;  // align capacity bound: P + min(E,P)*15 <= 64*16
 constexpr int kLayer1LdsMax = 65536;   // LDS of one workgroup (static + the dynamic token slice)
 constexpr int kLayer1MaxGrid = 1024;   // slots of the per-workgroup |h| maxima
+constexpr int kTinyXElems = 8192;      // fp8 x of the two-launch layer: every gate/up workgroup's LDS copy
 
 struct Layer1Args {
   const float* logits;   // [M][E] routed experts' logits
@@ -125,6 +126,7 @@ struct Layer1Args {
   AlignOut align_out;    // counts, offsets, sorted_ids, block_expert, num_padded (each may be null)
   float* scales_out;     // fp32[2]: s_x, s_h
   unsigned* sync;        // the barrier's counters (kL1SyncWords, zero between launches)
+  float* sx_out;         // fp8: s_x in effect, for a later launch (may be null)
 };
 
 // Largest |x| over n bf16 elements by the whole workgroup (every thread gets it).
@@ -144,29 +146,31 @@ __device__ __forceinline__ float layer1_amax_bf16(const uint16_t* x, int64_t n, 
   return a;
 }
 
-template <bool FP8, int HFMT, int WKS>
-static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
-  constexpr int U1 = FP8 ? 2 : 4, U2 = FP8 ? 1 : 4;
-  constexpr int TPW2 = 4 / WKS;  // row tiles of 32 per down item
-  __shared__ int s_ids[kLayer1Pairs];
-  __shared__ float s_wts[kLayer1Pairs];
-  __shared__ int s_counts[kMaxExperts], s_offsets[kMaxExperts + 1], s_active[kMaxExperts];
-  __shared__ int s_sorted[kLayer1Sorted];
-  __shared__ int s_block_expert[kLayer1Sorted / 16];
-  __shared__ int s_num_padded, s_num_active;
-  __shared__ WaveAlignLds s_al;
-  __shared__ f32x4 s_red[3 * 2 * 64];  // three waves' partial tiles (K split over four waves, one token tile)
-  __shared__ float s_red4[4];
-  __shared__ float s_sx;
-  __shared__ unsigned s_hamax;
-  extern __shared__ __align__(16) uint8_t s_tok[];  // down product's token slice (dynamic h scale)
+// The routing and sort-and-pad state every workgroup of the small layers
+// keeps in LDS.
+struct Layer1Lds {
+  int ids[kLayer1Pairs];
+  float wts[kLayer1Pairs];
+  int counts[kMaxExperts], offsets[kMaxExperts + 1], active[kMaxExperts];
+  int sorted[kLayer1Sorted];
+  int block_expert[kLayer1Sorted / 16];
+  int num_padded, num_active;
+  WaveAlignLds al;
+  float red4[4];
+  float sx;
+};
 
+// Phase 0 of the small layers, in every workgroup: routing (token
+// 4*wave + lane/16), the activation scale and quantisation into xq (fp8:
+// a.xq, which every workgroup writes with the same bytes, or the workgroup's
+// own LDS copy), and the one-wave sort-and-pad into LDS.  The lead workgroup
+// also writes the routing, the sort-and-pad outputs that were asked for, and
+// s_x.  Ends with the workgroup synchronised.
+template <bool FP8>
+__device__ __forceinline__ void layer1_prologue(const Layer1Args& a, Layer1Lds& s, bool lead, uint8_t* xq) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15;
-  const int M = a.M, E = a.E, K = a.K, S = a.S, H = a.H, I = a.I;
+  const int M = a.M, E = a.E, K = a.K, S = a.S, H = a.H;
   const int KS = K + S, ES = E + S, P = M * KS;
-  const bool lead = blockIdx.x == 0;
-
-  // ---- phase 0: routing (token 4*wave + lane/16), activation scale and quantisation
   {
     const int m = wave * kRouteRows + (lane >> 4);
     int e;
@@ -177,52 +181,76 @@ static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
       w = 1.0f;
     }
     if (m < M && l16 < KS) {
-      s_ids[m * KS + l16] = e;
-      s_wts[m * KS + l16] = w;
+      s.ids[m * KS + l16] = e;
+      s.wts[m * KS + l16] = w;
       if (lead && a.ids_out) a.ids_out[m * KS + l16] = e;
       if (lead && a.wts_out) a.wts_out[m * KS + l16] = w;
     }
   }
   if constexpr (FP8) {
     const int64_t nx = (int64_t)M * H;
-    const float sx = a.x_scale ? *a.x_scale : scale_from_amax(layer1_amax_bf16(a.x, nx, s_red4));
+    const float sx = a.x_scale ? *a.x_scale : scale_from_amax(layer1_amax_bf16(a.x, nx, s.red4));
     const float r = 1.0f / sx;
     for (int64_t i = (int64_t)tid * 16; i < nx; i += 256 * 16)
-      *(u32x4*)(a.xq + i) = quant16_e4m3(*(const u32x4*)(a.x + i), *(const u32x4*)(a.x + i + 8), r);
-    if (tid == 0) s_sx = sx;
+      *(u32x4*)(xq + i) = quant16_e4m3(*(const u32x4*)(a.x + i), *(const u32x4*)(a.x + i + 8), r);
+    if (tid == 0) s.sx = sx;
     if (lead && tid == 0 && a.scales_out) a.scales_out[0] = sx;
+    if (lead && tid == 0 && a.sx_out) *a.sx_out = sx;
   }
   __syncthreads();
   if (wave == 0) {
     int bits = 0;
     while ((1 << bits) < ES) ++bits;
-    const AlignOut lo{s_counts, s_offsets, s_sorted, s_block_expert, &s_num_padded, s_active, &s_num_active,
+    const AlignOut lo{s.counts, s.offsets, s.sorted, s.block_expert, &s.num_padded, s.active, &s.num_active,
                       a.n_blocks};
-    wave_align(s_ids, P, ES, 4, bits, lo, s_al);
+    wave_align(s.ids, P, ES, 4, bits, lo, s.al);
   }
   __syncthreads();
   if (lead) {  // the call's sort-and-pad outputs, when asked for
     const AlignOut& o = a.align_out;
     for (int x = tid; x < ES; x += 256) {
-      if (o.counts) o.counts[x] = s_counts[x];
-      if (o.offsets) o.offsets[x] = s_offsets[x];
+      if (o.counts) o.counts[x] = s.counts[x];
+      if (o.offsets) o.offsets[x] = s.offsets[x];
     }
-    if (o.offsets && tid == 0) o.offsets[ES] = s_offsets[ES];
-    if (o.num_padded && tid == 0) *o.num_padded = s_num_padded;
+    if (o.offsets && tid == 0) o.offsets[ES] = s.offsets[ES];
+    if (o.num_padded && tid == 0) *o.num_padded = s.num_padded;
     if (o.sorted_ids)
-      for (int p = tid; p < s_num_padded; p += 256) o.sorted_ids[p] = s_sorted[p];
+      for (int p = tid; p < s.num_padded; p += 256) o.sorted_ids[p] = s.sorted[p];
     if (o.block_expert)
-      for (int b = tid; b < a.n_blocks; b += 256) o.block_expert[b] = s_block_expert[b];
+      for (int b = tid; b < a.n_blocks; b += 256) o.block_expert[b] = s.block_expert[b];
   }
+}
 
-  const Segments seg{s_sorted, s_offsets, s_counts, s_active, &s_num_active, 0};
-  const int nact = s_num_active;
+template <bool FP8, int HFMT, int WKS>
+static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
+  constexpr int U1 = FP8 ? 2 : 4, U2 = FP8 ? 1 : 4;
+  constexpr int TPW2 = 4 / WKS;  // row tiles of 32 per down item
+  __shared__ Layer1Lds s;
+  __shared__ f32x4 s_red[3 * 2 * 64];  // three waves' partial tiles (K split over four waves, one token tile)
+  __shared__ unsigned s_hamax;
+  extern __shared__ __align__(16) uint8_t s_tok[];  // down product's token slice (dynamic h scale)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = a.M, K = a.K, S = a.S, H = a.H, I = a.I;
+  const int KS = K + S, P = M * KS;
+  const bool lead = blockIdx.x == 0;
+  float* const s_red4 = s.red4;
+  const int* const s_active = s.active;
+  const int* const s_offsets = s.offsets;
+  const int* const s_counts = s.counts;
+  const float* const s_wts = s.wts;
+
+  // ---- phase 0: routing, activation scale and quantisation, sort and pad
+  layer1_prologue<FP8>(a, s, lead, a.xq);
+
+  const Segments seg{s.sorted, s.offsets, s.counts, s.active, &s.num_active, 0};
+  const int nact = s.num_active;
   auto grid_barrier = [&] { layer1_barrier(a.sync); };
 
   auto layer = [&](auto pc_tag) {
     constexpr int WS = decltype(pc_tag)::value ? kWsRow : kWsTensor;
     // ---- phase 1: gate/up items (expert, 16-feature tile)
-    Gemm1Args g1{a.w13, FP8 ? a.xq : (const uint8_t*)a.x, seg, H, I, KS, a.w13_scale, &s_sx, a.h_scale, a.h,
+    Gemm1Args g1{a.w13, FP8 ? a.xq : (const uint8_t*)a.x, seg, H, I, KS, a.w13_scale, &s.sx, a.h_scale, a.h,
                  nullptr};
     g1.w_cs = a.w_cs;
     g1.w_es = a.w_es;
@@ -285,6 +313,57 @@ static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < KS; ++j) acc += s_wts[m * KS + j] * *(const f32x4*)(a.part + (int64_t)(m * KS + j) * H + n);
     *(uint2*)(a.y + (int64_t)m * H + n) = uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  }
+}
+
+// ---------------------------------------------------------------- two launches for tiny M
+// The layer in two launches where it fits the single-launch layer's limits:
+//   1. tiny_gate_up_kernel: every workgroup runs phase 0 above (the routing,
+//      quantisation and sort-and-pad of a few tokens cost less than a launch;
+//      fp8 x is quantised into the workgroup's LDS, where its gate/up product
+//      reads it) and then takes gate/up items it = blockIdx.x, + gridDim.x, ... exactly
+//      as the single-launch layer's phase 1 does; with a dynamic h scale it
+//      writes its largest |h| to wg_hmax[blockIdx.x] (no counter to clear);
+//   2. down_token_kernel (gemm_decode.h): the down product and the weighted
+//      combine per token, reducing those maxima for s_h.
+// The kernel boundary orders the two launches, so no grid barrier is needed;
+// the arithmetic is the multi-launch path's, bit for bit.
+template <bool FP8, int HFMT>
+static __global__ __launch_bounds__(256) void tiny_gate_up_kernel(Layer1Args a) {
+  constexpr int U1 = FP8 ? 2 : 4;
+  __shared__ Layer1Lds s;
+  __shared__ f32x4 s_red[3 * 2 * 64];  // three waves' partial tiles (K split over four waves, one token tile)
+  __shared__ __align__(16) uint8_t s_xq[FP8 ? kTinyXElems : 16];  // this workgroup's e4m3 copy of x
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  layer1_prologue<FP8>(a, s, blockIdx.x == 0, s_xq);
+  const Segments seg{s.sorted, s.offsets, s.counts, s.active, &s.num_active, 0};
+  const int KS = a.K + a.S, t1 = a.I / 16, nact = s.num_active;
+  auto run = [&](auto pc_tag) {
+    constexpr int WS = decltype(pc_tag)::value ? kWsRow : kWsTensor;
+    Gemm1Args g1{a.w13, FP8 ? s_xq : (const uint8_t*)a.x, seg, a.H, a.I, KS, a.w13_scale, &s.sx, a.h_scale, a.h,
+                 nullptr};
+    g1.w_cs = a.w_cs;
+    g1.w_es = a.w_es;
+    float hmax = 0.0f;
+    for (int it = blockIdx.x; it < nact * t1; it += gridDim.x) {
+      __syncthreads();  // the previous item's reduction tiles are consumed
+      const int e = s.active[it / t1];
+      hmax = fmaxf(hmax, gemm1_body<FP8, HFMT, 1, 1, U1, 4, WS>(g1, s_red, e, s.offsets[e], s.counts[e], 0,
+                                                                 it % t1));
+    }
+    return hmax;
+  };
+  float hmax;
+  if constexpr (FP8)
+    hmax = a.w_cs ? run(std::true_type{}) : run(std::false_type{});
+  else
+    hmax = run(std::false_type{});
+  if constexpr (HFMT == H_F32) {
+    hmax = wave_max(hmax);
+    __syncthreads();
+    if (lane == 0) s.red4[wave] = hmax;
+    __syncthreads();
+    if (tid == 0) a.wg_hmax[blockIdx.x] = fmaxf(fmaxf(s.red4[0], s.red4[1]), fmaxf(s.red4[2], s.red4[3]));
   }
 }
 

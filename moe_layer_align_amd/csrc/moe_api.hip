@@ -402,6 +402,18 @@ moe_status_t check_shape(int M, int E, int k) {
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- two-launch layer
+// Grid of its gate/up launch: as many workgroups as are resident at once
+// (two per CU: the kernel's ~150 VGPRs allow two waves per SIMD), each
+// paying the routing prologue once and then looping over gate/up items; a
+// larger grid pays it again in every later round.  The default takes the two
+// launches up to 1024 items (16-feature tiles x experts with tokens): at M = 1
+// measured 1.8 us faster on the Qwen3-shaped layer (384 items) and 1 us on
+// the DeepSeek-shaped one (1024), 1 us slower on the Mixtral-shaped one
+// (1792: 3.5 items per workgroup, the pipeline drained between them).
+constexpr int kTinyGrid = 512;
+constexpr int64_t kTinyDefaultItems = 1024;
+
 // ---------------------------------------------------------------- single-launch layer
 // The single-launch layer's wave split of the down product (4, 2 or 1: the
 // most that divides I's K-steps), or 0 when the layer does not fit it: more
@@ -457,7 +469,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 12; }
+int32_t moe_abi_version(void) { return 14; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -618,7 +630,10 @@ static moe_status_t prefill_forward(const moe_fused_args_t* a, hipStream_t st, v
 
 // noalloc: the workspace is the library's scratch array (the caller passes
 // none), its partial-sum region sized for the plan's K slices only.
-static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev, bool noalloc = false) {
+// path_out: validate and plan only (y and the workspace are not required),
+// report the launch sequence in *path_out and enqueue nothing.
+static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, void* const* ev, bool noalloc = false,
+                                  int32_t* path_out = nullptr) {
   if (!a) return MOE_ERR_INVALID_ARG;
   if (noalloc && (a->workspace || a->workspace_bytes)) return MOE_ERR_INVALID_ARG;
   auto rec = [&](int i) {
@@ -648,11 +663,15 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   const bool pc = a->weight_scale_mode == 1;
   if (pc && (!aligned(a->w13_scale, 16) || !aligned(a->w2_scale, 16))) return MOE_ERR_INVALID_ARG;
   if (M == 0) {
+    if (path_out) {
+      *path_out = MOE_PATH_NONE;
+      return MOE_OK;
+    }
     if (ev)
       for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) rec(i);
     return MOE_OK;
   }
-  if (!a->x || !a->w13 || !a->w2 || !a->y || (!noalloc && !a->workspace)) return MOE_ERR_INVALID_ARG;
+  if (!a->x || !a->w13 || !a->w2 || (!path_out && (!a->y || (!noalloc && !a->workspace)))) return MOE_ERR_INVALID_ARG;
   // logits: given, or computed from the router weights (exactly one of the two)
   if ((a->logits == nullptr) == (a->router_w == nullptr)) return MOE_ERR_INVALID_ARG;
   if (a->logits_out && !a->router_w) return MOE_ERR_INVALID_ARG;
@@ -689,6 +708,27 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
       if (!det && !blk && !a->router_w) l1_wks = layer1_wks(M, Er, k, H, I, fp8, hdyn);
       if (!l1_wks) return MOE_ERR_UNSUPPORTED;
     }
+  }
+  // tiny layers in two launches: the routing, quantisation and sort-and-pad
+  // in every gate/up workgroup, the combine in the per-token down product
+  // (taken by default unless the gate/up launch shape is pinned)
+  bool tiny = false;
+  const int rmode = a->tuning ? a->tuning->routing_in_gate_up : 0;
+  if (rmode < -1 || rmode > 1) return MOE_ERR_UNSUPPORTED;
+  if (!prefill && !l1_wks) {
+    const bool g1_pinned = a->tuning && (a->tuning->gemm1_ksplit > 0 || a->tuning->token_tiles > 0 ||
+                                         a->tuning->unroll > 0 || a->tuning->gemm1_stream_tiles != 0);
+    // (gate/up K split over four waves in whole MFMA k-steps, as in the single-launch layer)
+    const bool fits = plan.tok && M <= kLayer1Tokens && (int64_t)M * k <= kLayer1Pairs && Er <= kLayer1Experts &&
+                      (H / 4) % (fp8 ? 128 : 32) == 0 && (!fp8 || (int64_t)M * H <= kTinyXElems);
+    const bool pays = (int64_t)std::min<int64_t>(Er + S, (int64_t)M * k) * (I / 16) <= kTinyDefaultItems;
+    tiny = fits && (rmode == 1 || (rmode == 0 && !g1_pinned && pays));
+  }
+  if (rmode == 1 && !tiny) return MOE_ERR_UNSUPPORTED;  // required where the layer takes another path
+  if (path_out) {
+    *path_out = prefill ? MOE_PATH_PREFILL : l1_wks ? MOE_PATH_SINGLE_LAUNCH : tiny ? MOE_PATH_TWO_LAUNCHES
+              : plan.tok ? MOE_PATH_DECODE_TOKEN_DOWN : MOE_PATH_DECODE;
+    return MOE_OK;
   }
   // the scratch array holds the partial sums of the plan's K slices only
   const Layout L = make_layout(M, E, H, I, k, a->dtype, det || blk, noalloc && !prefill ? plan.ks2 : 0);
@@ -786,6 +826,62 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     return launch_status();
   }
   const bool small = P <= kSmallPairs && E <= kSmallMaxExperts && (!fp8 || (int64_t)M * H <= kSmallQuantElems);
+  if (tiny) {
+    const int hf = !fp8 ? H_BF16 : (hdyn ? H_F32 : H_E4M3);
+    const int grid = (int)std::min<int64_t>((int64_t)n_act * (I / 16), kTinyGrid);
+    Layer1Args la{};
+    la.logits = a->logits;
+    la.x = (const uint16_t*)a->x;
+    la.M = M;
+    la.E = Er;
+    la.K = kr;
+    la.S = S;
+    la.H = H;
+    la.I = I;
+    la.w13 = (const uint8_t*)a->w13;
+    la.w2 = (const uint8_t*)a->w2;
+    la.w13_scale = a->w13_scale;
+    la.w2_scale = a->w2_scale;
+    la.w_cs = pc ? 1 : 0;
+    la.w_es = a->weight_scale_mode == 2 ? 1 : 0;
+    la.x_scale = a->x_scale;
+    la.h_scale = a->h_scale;
+    la.h = h;
+    la.wg_hmax = (float*)(ws + L.wg_hmax);
+    la.n_blocks = L.n_blocks;
+    la.ids_out = ids;
+    la.wts_out = wts;
+    la.align_out = o;
+    la.scales_out = fp8 ? a->scales_out : nullptr;
+    la.sx_out = fp8 ? scale_slot : nullptr;
+    rec(0);
+    rec(1);
+    rec(2);
+    rec(3);
+    rec(4);
+    if (!launch_tiny_gate_up(fp8, hf, grid, st, la)) return MOE_ERR_UNSUPPORTED;
+    rec(5);
+    if ((rc = launch_status()) != MOE_OK) return rc;
+    rec(6);
+    DownTokArgs g{(const uint8_t*)a->w2, h, ids, wts, (uint16_t*)a->y, H, I, k, plan.tok_chunks, a->w2_scale};
+    g.w_cs = pc ? 1 : 0;
+    g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
+    g.h_scale = a->h_scale;
+    g.h_amax = h_amax;
+    g.x_scale = scale_slot;
+    g.scales_out = fp8 ? a->scales_out : nullptr;
+    if (hf == H_F32) {
+      g.wg_hmax = (const float*)(ws + L.wg_hmax);
+      g.n_wg = grid;
+    }
+    const size_t lds = hf == H_F32 ? (size_t)k * I : 0;
+    if (!launch_down_token(fp8, hf, plan.u2, dim3((unsigned)(H / 16), (unsigned)M), lds, st, g))
+      return MOE_ERR_UNSUPPORTED;
+    rec(7);
+    rec(8);
+    rec(9);
+    return launch_status();
+  }
   if (small) {
     // 1+2. routing, align (and fp8 activation quantisation) in one workgroup
     rec(0);
@@ -921,6 +1017,11 @@ moe_status_t moe_fused_forward(const moe_fused_args_t* args, void* stream) {
 
 moe_status_t moe_fused_forward_profiled(const moe_fused_args_t* args, void* stream, void* const* events) {
   return fused_forward(args, (hipStream_t)stream, events);
+}
+
+moe_status_t moe_fused_path(const moe_fused_args_t* args, int32_t* path) {
+  if (!path) return MOE_ERR_INVALID_ARG;
+  return fused_forward(args, nullptr, nullptr, false, path);
 }
 
 moe_status_t moe_fused_forward_noalloc(const moe_fused_args_t* args, void* stream) {

@@ -71,7 +71,7 @@ def test_probe_library_exports_its_header():
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 12
+    assert lib.moe_abi_version() == 14
 
 
 def capacity_formula(M, k, E, B):
@@ -218,6 +218,66 @@ def fused_args(**kw):
 def test_fused_validation(lib, kw, code):
     args = fused_args(**kw)
     assert lib.moe_fused_forward(ctypes.byref(args), None) == code
+    # the path query validates the same way, bar the workspace size
+    p = ctypes.c_int32(-1)
+    assert lib.moe_fused_path(ctypes.byref(args), ctypes.byref(p)) == (0 if code == 3 else code)
+    assert (p.value >= 0) == (code == 3)
+
+
+# The launch sequence of each workload shape, and of the modes that change it
+# (moe_fused_path plans on the host; no GPU).
+@pytest.mark.parametrize("name,M,path", [
+    ("mixtral", 1, "decode_token_down"),  # 2 x 896 gate/up items: above the two-launch default's 1024
+    ("mixtral", 4, "decode"), ("mixtral", 63, "decode"),
+    ("qwen3", 1, "two_launches"), ("qwen3", 8, "decode_token_down"),  # 8 x 2048 fp8 x: above 8192 elements
+    ("qwen3", 64, "decode"),
+    ("deepseek", 1, "two_launches"), ("deepseek", 16, "decode"),
+    ("prefill", 4096, "prefill"), ("prefill", 0, "none"),
+])
+def test_fused_path_of_the_workloads(name, M, path):
+    import moe_layer_align_amd as m
+    from synth import CONFIGS
+    c = CONFIGS[name]
+    assert m.fused_path(M, c.E, c.H, c.I, c.k, c.dtype) == path
+
+
+def test_fused_path_modes():
+    import moe_layer_align_amd as m
+    T = m.Tuning
+    q = (1, 128, 2048, 768, 8, "fp8")  # one Qwen3-shaped token
+    assert m.fused_path(*q, tuning=T(single_launch=1)) == "single_launch"
+    assert m.fused_path(*q, tuning=T(routing_in_gate_up=-1)) == "decode_token_down"
+    assert m.fused_path(*q, tuning=T(gemm1_ksplit=2)) == "decode_token_down"  # pinned gate/up launch shape
+    assert m.fused_path(*q, tuning=T(gemm1_ksplit=2, routing_in_gate_up=1)) == "two_launches"
+    assert m.fused_path(*q, tuning=T(down_per_token=-1)) == "decode"
+    assert m.fused_path(*q, static_x_scale=True, static_h_scale=True, deterministic=True) == "decode"
+    assert m.fused_path(*q, weight_scale_mode=3) == "decode"  # block-scaled
+    assert m.fused_path(*q, weight_scale_mode=1, n_shared=1) == "two_launches"
+    assert m.fused_path(*q, router_w=True) == "two_launches"
+    assert m.fused_path(2, 16, 256, 256, 2, "fp8") == "decode_token_down"  # H/4 not whole fp8 k-steps
+    assert m.fused_path(2, 16, 512, 256, 2, "fp8") == "two_launches"
+    assert m.fused_path(2, 16, 256, 256, 2, "bf16") == "two_launches"
+    mix = (1, 8, 4096, 14336, 2, "bf16")
+    assert m.fused_path(*mix) == "decode_token_down"
+    assert m.fused_path(*mix, tuning=T(routing_in_gate_up=1)) == "two_launches"
+    for bad in (dict(tuning=T(single_launch=1, routing_in_gate_up=1)),
+                dict(tuning=T(routing_in_gate_up=1, down_per_token=-1)),
+                dict(router_w=True, tuning=T(single_launch=1))):
+        with pytest.raises(m.MoEError) as e:
+            m.fused_path(*q, **bad)
+        assert e.value.code == 2, bad
+    with pytest.raises(m.MoEError) as e:
+        m.fused_path(4096, 128, 4096, 1536, 8, "fp8", tuning=T(routing_in_gate_up=1))
+    assert e.value.code == 2
+
+
+def test_fused_path_needs_no_outputs_and_rejects_null(lib):
+    args = fused_args(y=None, workspace=None, workspace_bytes=0)
+    p = ctypes.c_int32(-1)
+    assert lib.moe_fused_path(ctypes.byref(args), ctypes.byref(p)) == 0 and p.value >= 1
+    assert lib.moe_fused_path(ctypes.byref(args), None) == 1
+    assert lib.moe_fused_path(None, ctypes.byref(p)) == 1
+    assert lib.moe_fused_forward(ctypes.byref(args), None) == 1  # the call itself needs them
 
 
 def test_router_logits_validation(lib):
@@ -234,7 +294,8 @@ def test_fused_tuning_validation(lib):
     import moe_layer_align_amd as m
     for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17),
               m.Tuning(gemm2_wave_ksplit=3), m.Tuning(reverse_order=2), m.Tuning(single_launch=2),
-              m.Tuning(single_launch=-2), m.Tuning(down_per_token=2), m.Tuning(down_per_token=-2)):
+              m.Tuning(single_launch=-2), m.Tuning(down_per_token=2), m.Tuning(down_per_token=-2),
+              m.Tuning(routing_in_gate_up=2), m.Tuning(routing_in_gate_up=-2)):
         args = fused_args(tuning=ctypes.pointer(t))
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 
@@ -284,6 +345,22 @@ def test_fused_down_per_token_required_where_it_does_not_fit(lib):
                dict(top_k=8, I=16384, **fp8)):
         args = fused_args(tuning=ctypes.pointer(t), **kw)
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2, kw
+
+
+def test_fused_routing_in_gate_up_required_where_it_does_not_fit(lib):
+    # more than 16 tokens or 64 pairs, the per-expert down product, E above
+    # 256, fp8 x above 8192 elements, a gate/up K that four waves cannot split
+    # into whole MFMA k-steps
+    import moe_layer_align_amd as m
+    fp8 = dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE)
+    for kw in (dict(M=17, top_k=2), dict(M=9, top_k=8), dict(E=300, top_k=2),
+               dict(M=2, H=8192, **fp8), dict(M=2, H=256, **fp8), dict(M=2, H=384, **fp8)):
+        t = m.Tuning(routing_in_gate_up=1)
+        args = fused_args(tuning=ctypes.pointer(t), **kw)
+        assert lib.moe_fused_forward(ctypes.byref(args), None) == 2, kw
+    t = m.Tuning(routing_in_gate_up=1, down_per_token=-1)
+    args = fused_args(tuning=ctypes.pointer(t))
+    assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 
 
 def test_fused_m0_is_noop(lib):

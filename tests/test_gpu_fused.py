@@ -676,3 +676,64 @@ def test_prefill_path_bf16_repeat_calls_bitwise():
     assert bool(ys[0].float().isfinite().all())
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
+
+
+# ---------------------------------------------------------------- two launches for tiny layers
+# At most 16 tokens and 64 pairs (fp8 x of at most 8192 elements) with the
+# per-token down product: every gate/up workgroup routes, quantises and sorts
+# the few tokens itself, so the layer is two launches.  Its arithmetic is the
+# three-launch path's: the same bits where that path's gate/up takes the same
+# plan (M < 8 in fp8; bf16), and the oracle's outputs everywhere, with the
+# call's routing and sort-and-pad outputs (checked by compare).
+TWO = moe.Tuning(routing_in_gate_up=1, single_launch=-1)
+THREE = moe.Tuning(routing_in_gate_up=-1, single_launch=-1)
+
+
+@pytest.mark.parametrize("dtype,xs,hs", [("bf16", None, None), ("fp8", None, None), ("fp8", 0.02, 0.004)])
+@pytest.mark.parametrize("M", [1, 3, 7])
+def test_two_launches_match_three(dtype, xs, hs, M):
+    cfg = cfg_of(dtype, 16, 4, 512, 384)
+    w13, w2, s13, s2 = gen_weights(cfg, 100 + M, device=DEV)
+    x = gen_x(cfg.H, M, 100 + M, sub=M).to(DEV)
+    lg = gen_logits(cfg, M, 100 + M, sub=M).to(DEV)
+    fp8 = dtype == "fp8"
+    sc = (lambda v: torch.tensor([v], device=DEV)) if fp8 else (lambda v: None)
+    kw = dict(x_scale=sc(xs) if xs else None, h_scale=sc(hs) if hs else None)
+    so = [torch.empty(2, device=DEV) if fp8 else None for _ in range(2)]
+    ys = [moe.fused_forward(x, lg, w13, w2, cfg.k, dtype, sc(s13), sc(s2), tuning=t, scales_out=so[i], **kw)
+          for i, t in enumerate((TWO, THREE))]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]), "two launches and three differ"
+    if fp8:
+        assert torch.equal(so[0], so[1])
+    compare(cfg, M, seed=100 + M, weights=(w13, w2, s13, s2), x=x.cpu(), logits=lg.cpu(), x_scale=xs, h_scale=hs,
+            tuning=TWO)
+
+
+def test_two_launches_workload_shapes(qwen3_w, deepseek_w):
+    compare(CONFIGS["qwen3"], 1, seed=0, weights=qwen3_w, tuning=TWO)
+    compare(CONFIGS["qwen3"], 4, seed=0, weights=qwen3_w, tuning=TWO)
+    compare(CONFIGS["deepseek"], 1, seed=0, weights=deepseek_w, tuning=TWO)
+    compare(CONFIGS["tiny"], 4, seed=0, tuning=TWO)
+
+
+def test_two_launches_shared_experts_and_scale_modes():
+    cfg = cfg_of("fp8", 16, 7, 512, 512, logits="zipf")
+    M = 8  # 64 pairs with the shared expert; x of 4096 elements
+    compare(cfg, M, seed=101, weights=gen_weights_per_channel(cfg_of("fp8", 17, 7, 512, 512), 101, device=DEV),
+            n_shared=1, tuning=TWO)
+    compare(cfg, M, seed=102, weights=gen_weights_per_expert(cfg, 102, device=DEV, E=17), n_shared=1, tuning=TWO)
+    compare(cfg_of("bf16", 8, 2, 512, 384), 16, seed=103, n_shared=1, tuning=TWO)
+
+
+def test_two_launches_are_the_default_for_tiny_layers():
+    cfg = CONFIGS["qwen3"]
+    w13, w2, s13, s2 = gen_weights(cfg, 104, device=DEV)
+    x = gen_x(cfg.H, 1, 104, sub=1).to(DEV)
+    lg = gen_logits(cfg, 1, 104, sub=1).to(DEV)
+    t13, t2 = torch.tensor([s13], device=DEV), torch.tensor([s2], device=DEV)
+    a = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", t13, t2)
+    b = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", t13, t2, tuning=TWO)
+    c = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", t13, t2, tuning=THREE)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
