@@ -80,6 +80,29 @@ moe_status_t moe_probe_fp8_dot(const uint8_t* A, const uint8_t* B, float* C, int
  * The caller times the call with events. */
 moe_status_t moe_probe_publish(float* buf, uint32_t* cnt, int32_t grid, int32_t mode, void* stream);
 
+/* The operand stream of the tiled prefill product without its arithmetic,
+ * to tell the load path's limits from the product's: `grid` workgroups
+ * (1..65536) of 256 threads each walk `steps` K-steps (3..2^20, a multiple
+ * of 3) of 128 bytes over 384 rows of a [bytes/4096][4096] byte matrix (256
+ * weight rows, 128 token rows; the next 384 rows every 32 steps, wrapping
+ * within the buffer), each step's 48 KB landing in a three-slot LDS ring two
+ * steps ahead of its use with one barrier per step.  mode 0: direct-to-LDS
+ * buffer loads; 1: the same loads into registers, then 16-byte LDS stores;
+ * 2: mode 0 plus the product's LDS fragment reads (24 KB per wave per step,
+ * swizzled as the product's).  Added to mode: 4 = each workgroup starts its
+ * tiles at K-step g % 32 (the operands' addresses then differ between
+ * workgroups in their low 12 bits); 8 = rows 4224 bytes apart instead of
+ * 4096; 16 = every workgroup keeps its first tile and alternates between
+ * its first two K-steps (96 KB per workgroup, re-read from L2); 32 (modes 0
+ * and 2) = 256 token rows per step (64 KB, 512 rows per tile) in a two-slot
+ * ring, loads one step ahead.  buf at least 512 * 4224 bytes.  buf: bytes a multiple of 4096, from 384*4224 to 2^30 (a buffer below the
+ * L2 size stays there; one far above the last-level cache streams from
+ * HBM).  sink: uint32 [grid * 4], each wave's XOR of what it read.  Other
+ * arguments: MOE_ERR_INVALID_ARG.  The caller times the call with events:
+ * bytes moved = grid * steps * 48 KB. */
+moe_status_t moe_probe_ring_load(const void* buf, size_t bytes, int32_t grid, int32_t steps, int32_t mode,
+                                 uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_probes.h"
 
 namespace {
@@ -152,13 +154,160 @@ __global__ __launch_bounds__(256) void publish_kernel(float* __restrict__ buf, u
   }
 }
 
+// The operand stream of the tiled prefill product without its arithmetic:
+// every workgroup walks `steps` K-steps of 128 bytes over 384 rows (256
+// weight rows and 128 token rows of a 4096-byte-row matrix, a new tile of
+// rows every 32 steps), each step's 48 KB landing in a three-slot LDS ring
+// two steps ahead of its use, one barrier per step.  MODE 0: direct-to-LDS
+// buffer loads (1 KB per instruction, eight whole rows' lines); MODE 1: the
+// same loads into registers, written to the ring with 16-byte LDS stores;
+// MODE 2: MODE 0 plus the LDS fragment reads of the product (each wave reads
+// 24 KB of every step).  Rows wrap within the buffer (nrows = bytes / 4096),
+// so a small buffer stays in L2 and a large one streams from HBM.  Every
+// load goes through a buffer resource of `bytes` records.
+constexpr int kRingRow = 4096, kRingBK = 128, kRingStage = 384 * kRingBK, kRingStages = 3;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+template <int N>
+__device__ __forceinline__ void ring_wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+}
+
+// this lane's 12 rows of step s: 8 of the weight block (rows 64w + 8q +
+// lane/8) and 4 of the token block (256 + 32w + 8q + lane/8), 16 bytes each;
+// a new tile of 384 rows every 32 steps, wrapping within nrows
+// (flags: 1 = each workgroup starts its tiles at K-step blockIdx.x % 32,
+// 2 = rows 4096 + 128 bytes apart instead of 4096, 4 = every workgroup keeps
+// its first tile and alternates between its first two K-steps: 96 KB per
+// workgroup, re-read from L2)
+// TB: token rows per step (128, or 256 with a two-slot ring)
+template <int TB = 128>
+__device__ __forceinline__ int ring_off(int s, int q, int wave, int lane, int nrows, int flags) {
+  const int tile = (flags & 4) ? blockIdx.x : blockIdx.x + (s / 32) * gridDim.x;
+  if (flags & 4) s %= 2;
+  const int r = q < 8 ? 64 * wave + 8 * q + (lane >> 3) : 256 + (TB / 4) * wave + 8 * (q - 8) + (lane >> 3);
+  const int row = (int)(((int64_t)tile * (256 + TB) + r) % nrows);
+  const int ks = (flags & 1) ? (s + blockIdx.x) % 32 : s % 32;
+  return row * (kRingRow + ((flags & 2) ? kRingBK : 0)) + ks * kRingBK + ((((lane & 7) ^ (lane >> 3)) & 7) << 4);
+}
+// LDS address of this wave's 8-row block q of a ring slot
+template <int TB = 128>
+__device__ __forceinline__ lds_u8* ring_dst(lds_u8* smem, int slot, int q, int wave) {
+  const int r = q < 8 ? 64 * wave + 8 * q : 256 + (TB / 4) * wave + 8 * (q - 8);
+  return smem + slot * (256 + TB) * kRingBK + r * kRingBK;
+}
+__device__ __forceinline__ void ring_sink(u32x4 x, uint32_t* sink, int wave, int lane) {
+  uint32_t r = x[0] ^ x[1] ^ x[2] ^ x[3];
+  for (int o = 32; o > 0; o >>= 1) r ^= (uint32_t)__shfl_xor((int)r, o, 64);
+  if (lane == 0) sink[blockIdx.x * 4 + wave] = r;
+}
+
+// modes 0 (READS false) and 2 (READS true): direct-to-LDS loads; TB 128:
+// three 48 KB slots, loads two steps ahead; TB 256: two 64 KB slots, loads
+// one step ahead
+template <bool READS, int TB>
+__global__ __launch_bounds__(256) void ring_dma_kernel(const uint8_t* __restrict__ buf, int bytes, int steps,
+                                                       uint32_t* __restrict__ sink, int flags) {
+  constexpr int NS = TB == 128 ? 3 : 2, NQ = 8 + TB / 32, SB = (256 + TB) * kRingBK;
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrows = bytes / (kRingRow + ((flags & 2) ? kRingBK : 0));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)buf, (short)0, bytes, 0x00020000);
+  auto issue = [&](int s) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      // (computed apart: a template-dependent expression as the builtin's
+      // argument drops the kernel's host stub)
+      const int o = ring_off<TB>(s, q, wave, lane, nrows, flags);
+      lds_u8* d = ring_dst<TB>(smem, s % NS, q, wave);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3)))*)d, 16, o, 0, 0, 0);
+    }
+  };
+  u32x4 x = {0u, 0u, 0u, 0u};
+  issue(0);
+  if (NS == 3) issue(1);
+  for (int s = 0; s < steps; ++s) {
+    // step s landed (three slots: s+1 may be in flight, its 12 loads); a
+    // wait count that depends on TB would drop the kernel's host stub
+    if (NS == 3)
+      ring_wait_vm<12>();
+    else
+      ring_wait_vm<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const lds_u8* st = smem + (s % NS) * SB;
+    if (READS) {
+      // the product's reads: 8 A fragments of this wave's 64 rows and 16 B
+      // fragments of all 128 token rows, 16 bytes per lane each, logical
+      // chunk c of row r at position c ^ (r & 7) (the loads above put global
+      // chunk (lane%8) ^ (lane/8) of row 8q + lane/8 at position lane%8)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = 64 * wave + (lane & 31) + 32 * (q & 1), c = (q >> 1) * 2 + (lane >> 5);
+        x ^= *(const __attribute__((address_space(3))) u32x4*)(st + r * kRingBK + ((c ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int q = 0; q < TB / 8; ++q) {
+        const int r = 256 + (lane & 31) + 32 * (q % (TB / 32)), c = (q / (TB / 32)) * 2 + (lane >> 5);
+        x ^= *(const __attribute__((address_space(3))) u32x4*)(st + r * kRingBK + ((c ^ (r & 7)) << 4));
+      }
+    } else {
+      x ^= *(const __attribute__((address_space(3))) u32x4*)(st + threadIdx.x * 16);
+    }
+    issue(s + NS - 1);  // into the slot of step s-1, which every wave has read
+  }
+  ring_wait_vm<0>();
+  ring_sink(x, sink, wave, lane);
+}
+
+// mode 1: register loads (steps s+1 and s+2 in flight in registers while
+// step s is stored), then 16-byte LDS stores
+__global__ __launch_bounds__(256) void ring_reg_kernel(const uint8_t* __restrict__ buf, int bytes, int steps,
+                                                       uint32_t* __restrict__ sink, int flags) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrows = bytes / (kRingRow + ((flags & 2) ? kRingBK : 0));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)buf, (short)0, bytes, 0x00020000);
+  constexpr int TB = 128;
+  u32x4 v[3][12];
+  auto load = [&](u32x4 (&d)[12], int s) {
+#pragma unroll
+    for (int q = 0; q < 12; ++q) d[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, ring_off<TB>(s, q, wave, lane, nrows, flags), 0, 0);
+  };
+  auto store = [&](const u32x4 (&d)[12], int slot) {
+#pragma unroll
+    for (int q = 0; q < 12; ++q)
+      *(__attribute__((address_space(3))) u32x4*)(ring_dst<128>(smem, slot, q, wave) + lane * 16) = d[q];
+  };
+  u32x4 x = {0u, 0u, 0u, 0u};
+  load(v[0], 0);
+  load(v[1], 1);
+  int s = 0;
+  auto body = [&](auto c) {
+    constexpr int C = decltype(c)::value;
+    load(v[(C + 2) % 3], s + 2);  // (the last two load steps nothing reads)
+    store(v[C], s % 3);
+    __syncthreads();
+    x ^= *(__attribute__((address_space(3))) u32x4*)(smem + (s % 3) * kRingStage + threadIdx.x * 16);
+    ++s;
+  };
+  while (s + 3 <= steps) {
+    body(std::integral_constant<int, 0>{});
+    body(std::integral_constant<int, 1>{});
+    body(std::integral_constant<int, 2>{});
+  }
+  ring_sink(x, sink, wave, lane);
+}
+
 moe_status_t launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 }  // namespace
 
 extern "C" {
 
-int32_t moe_probes_abi_version(void) { return 3; }
+int32_t moe_probes_abi_version(void) { return 4; }
 
 moe_status_t moe_probe_hbm_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || grid < 1 || grid > (1 << 20)) return MOE_ERR_INVALID_ARG;
@@ -194,6 +343,31 @@ moe_status_t moe_probe_publish(float* buf, uint32_t* cnt, int32_t grid, int32_t 
   if (mode == 0) publish_kernel<0><<<grid, 256, 0, st>>>(buf, cnt);
   if (mode == 1) publish_kernel<1><<<grid, 256, 0, st>>>(buf, cnt);
   if (mode == 2) publish_kernel<2><<<grid, 256, 0, st>>>(buf, cnt);
+  return launch_status();
+}
+
+moe_status_t moe_probe_ring_load(const void* buf, size_t bytes, int32_t grid, int32_t steps, int32_t mode,
+                                 uint32_t* sink, void* stream) {
+  const int flags = mode >> 2;
+  mode &= 3;
+  if (!buf || !sink || bytes % kRingRow != 0 || bytes < (size_t)512 * (kRingRow + kRingBK) ||
+      bytes > ((size_t)1 << 30) || grid < 1 || grid > 65536 || steps < 3 || steps > (1 << 20) || steps % 3 != 0 ||
+      mode > 2 || flags > 15 || ((flags & 8) && mode == 1))
+    return MOE_ERR_INVALID_ARG;
+  const hipStream_t st = (hipStream_t)stream;
+  const bool wide = (flags & 8) != 0;  // 256 token rows per step, two slots
+  const size_t lds = wide ? (size_t)2 * 512 * kRingBK : (size_t)kRingStages * kRingStage;
+  const void* k = mode == 1 ? (const void*)ring_reg_kernel
+                  : wide ? (mode == 0 ? (const void*)ring_dma_kernel<false, 256> : (const void*)ring_dma_kernel<true, 256>)
+                         : (mode == 0 ? (const void*)ring_dma_kernel<false, 128> : (const void*)ring_dma_kernel<true, 128>);
+  if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  const uint8_t* b = (const uint8_t*)buf;
+  if (mode == 1) ring_reg_kernel<<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
+  if (mode == 0 && !wide) ring_dma_kernel<false, 128><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
+  if (mode == 2 && !wide) ring_dma_kernel<true, 128><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
+  if (mode == 0 && wide) ring_dma_kernel<false, 256><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
+  if (mode == 2 && wide) ring_dma_kernel<true, 256><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
   return launch_status();
 }
 

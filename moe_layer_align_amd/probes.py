@@ -14,7 +14,7 @@ from . import MoEError, _stream
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_probes.so")
-_ABI = 3
+_ABI = 4
 _lib = None
 
 
@@ -39,6 +39,8 @@ def load():
     lib.moe_probe_publish.argtypes = [vp, vp, i32, i32, vp]
     lib.moe_probe_fp8_dot.restype = ctypes.c_int
     lib.moe_probe_fp8_dot.argtypes = [vp, vp, vp, i32, i32, ctypes.c_float, i32, vp]
+    lib.moe_probe_ring_load.restype = ctypes.c_int
+    lib.moe_probe_ring_load.argtypes = [vp, sz, i32, i32, i32, vp, vp]
     _lib = lib
     return lib
 
@@ -96,3 +98,20 @@ def publish(buf: torch.Tensor, cnt: torch.Tensor, grid: int, mode: int, stream: 
     if not (cnt.is_cuda and cnt.dtype == torch.int32 and cnt.numel() >= 1024):
         raise ValueError("cnt: int32 GPU tensor of 1024 elements")
     _raise(load().moe_probe_publish(buf.data_ptr(), cnt.data_ptr(), grid, mode, _stream(stream)), "moe_probe_publish")
+
+
+def ring_load(buf: torch.Tensor, sink: torch.Tensor, grid: int, steps: int, mode: int,
+              stream: Optional[torch.cuda.Stream] = None):
+    """The tiled prefill product's operand stream without its arithmetic
+    (moe_probe_ring_load): `grid` workgroups walk `steps` 48 KB K-steps of buf
+    (contiguous GPU tensor, size a multiple of 4096 bytes, 1.5 MiB..1 GiB)
+    through a three-slot LDS ring; mode 0 direct-to-LDS loads, 1 register
+    loads and LDS stores, 2 mode 0 plus the product's fragment reads, plus 4
+    (K start rotated per workgroup), 8 (rows 4224 bytes apart) and 16 (a
+    private 96 KB window per workgroup, re-read from L2).  sink:
+    int32 GPU tensor of at least grid*4 elements."""
+    if not (buf.is_cuda and buf.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+            and sink.numel() >= grid * 4):
+        raise ValueError("buf: contiguous GPU tensor; sink: int32 GPU tensor of at least grid*4 elements")
+    _raise(load().moe_probe_ring_load(buf.data_ptr(), buf.numel() * buf.element_size(), grid, steps, mode,
+                                      sink.data_ptr(), _stream(stream)), "moe_probe_ring_load")

@@ -53,7 +53,7 @@ def test_probe_library_exports_its_header():
     plib = probes.load()
     names = declared_functions(os.path.join(ROOT, "include", "moe_probes.h"))
     assert set(names) >= {"moe_probes_abi_version", "moe_probe_hbm_read", "moe_probe_mfma_fp8_loop",
-                          "moe_probe_fp8_dot", "moe_probe_publish"}
+                          "moe_probe_fp8_dot", "moe_probe_publish", "moe_probe_ring_load"}
     for n in names:
         assert hasattr(plib, n), n
     assert plib.moe_probe_hbm_read(None, 16, 1, 16, None) == 1
@@ -66,6 +66,16 @@ def test_probe_library_exports_its_header():
     assert plib.moe_probe_fp8_dot(16, 16, 16, 127, 127, 0.0, 2, None) == 1  # unknown form
     assert plib.moe_probe_publish(16, 16, 1, 3, None) == 1                    # unknown mode
     assert plib.moe_probe_publish(16, 16, 0, 0, None) == 1                    # empty grid
+    rl, MB = plib.moe_probe_ring_load, 1 << 20
+    assert rl(16, 4 * MB, 1, 3, 3, 16, None) == 1          # unknown mode
+    assert rl(16, 4 * MB, 1, 3, 64, 16, None) == 1         # unknown flag
+    assert rl(16, 4 * MB, 1, 3, 33, 16, None) == 1         # two-slot ring of register loads
+    assert rl(16, 4 * MB, 1, 4, 0, 16, None) == 1          # steps not a multiple of 3
+    assert rl(16, 4 * MB + 16, 1, 3, 0, 16, None) == 1     # size not a multiple of 4096
+    assert rl(16, 512 * 4224 - 4096, 1, 3, 0, 16, None) == 1  # below 512 padded rows
+    assert rl(16, 2048 * MB, 1, 3, 0, 16, None) == 1       # above 1 GiB
+    assert rl(16, 4 * MB, 0, 3, 0, 16, None) == 1          # empty grid
+    assert rl(None, 4 * MB, 1, 3, 0, 16, None) == 1
 
 
 def test_status_strings(lib):
