@@ -62,14 +62,14 @@ SINGLE_SOURCES = ("moe_layer_align_amd/csrc/layer_small.h", "moe_layer_align_amd
                   "moe_layer_align_amd/csrc/route_align.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "9011ecb3585ae31e8a4b5b47ea4fdbc5332314bc1e8bc6fdd5040720d41cf9f2",
-                "bytes_per_launch": 1510121827},
-    "qwen3": {"src_sha256": "9011ecb3585ae31e8a4b5b47ea4fdbc5332314bc1e8bc6fdd5040720d41cf9f2",
-              "bytes_per_launch": 241767974},
-    "deepseek": {"src_sha256": "9011ecb3585ae31e8a4b5b47ea4fdbc5332314bc1e8bc6fdd5040720d41cf9f2",
-                 "bytes_per_launch": 3292623699},
-    "prefill": {"src_sha256": "fc1be3b6af278ceec8b86c100c8f7c58542d22e5c2ca8bcd5e6e6b4747980a1a",
-                "bytes_per_launch": 3024756279},
+    "mixtral": {"src_sha256": "52554b0f49ac9036ea1c2b2eddcb63748126b7881a16ec2a859d0d2385a7f329",
+                "bytes_per_launch": 1511427704},
+    "qwen3": {"src_sha256": "52554b0f49ac9036ea1c2b2eddcb63748126b7881a16ec2a859d0d2385a7f329",
+              "bytes_per_launch": 241792566},
+    "deepseek": {"src_sha256": "52554b0f49ac9036ea1c2b2eddcb63748126b7881a16ec2a859d0d2385a7f329",
+                 "bytes_per_launch": 3292693558},
+    "prefill": {"src_sha256": "ac86f14bf7fa4ac2520e876b28bb05a559a55dcbb407601bf5acb963b45b35cc",
+                "bytes_per_launch": 3051415558},
 }
 
 
