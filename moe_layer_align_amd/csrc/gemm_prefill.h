@@ -118,11 +118,16 @@ struct PrefillSeg {
 // LDS layout of an operand tile in one stage: rows of 128 bytes (a whole
 // cache line of the row per step, so a 1 KB load covers 8 lines rather than
 // 16 half lines, which halves its texture-address work), the eight 16-byte
-// chunks of row r stored at chunk position c ^ (r & 7).  Eight consecutive
-// rows with the same logical chunk then fall on eight different 16-byte bank
-// groups, so the MFMA fragment reads (32 rows, same chunk) are free of bank
-// conflicts.
-__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ (row & 7)) << 4); }
+// chunks of row r stored at chunk position c ^ pf_mix(r).  A 16-byte LDS read
+// is served 16 lanes at a time over 64 four-byte banks (256 bytes); a 128-byte
+// row covers half of them, even rows one half and odd rows the other.  The
+// MFMA fragment reads take one logical chunk of 16 consecutive rows, so the
+// eight rows of each parity must land on eight different chunk positions:
+// pf_mix(r) = (r & 7) ^ ((r >> 3) & 1) does that (r & 7 alone repeats every
+// eight rows, a two-way conflict on every such read).  pf_mix depends on the
+// row's low four bits only, so tiles 32 rows apart share one pattern.
+__device__ __forceinline__ int pf_mix(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int pf_swz(int row, int chunk) { return row * kPfBK + ((chunk ^ pf_mix(row)) << 4); }
 
 // Work item -> (weight tile, token block), XCD-aware.  Workgroups are handed
 // to the eight XCDs round robin by linear id, and item L belongs to XCD L % 8.
@@ -327,7 +332,8 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
 
   // DMA sources of an item for this lane: A rows 64*wave + 8*q + lane/8
   // (q < 8), B rows 32*wave + 8*q + lane/8 (q < 4), logical chunk
-  // (lane%8) ^ (lane/8) (the row's low three bits are lane/8).  The loads go through buffer resources (the
+  // (lane%8) ^ pf_mix(row) = (lane%8) ^ (lane/8) ^ (q & 1): offA holds the
+  // chunk for even q, odd q flip its lowest bit (byte offset bit 4).  The loads go through buffer resources (the
   // expert's weight matrix and the activation matrix, byte offsets below
   // 2^31, checked by the host) rather than flat-global addresses: the
   // compiler's wait-count model treats a flat-global load into LDS as a
@@ -365,7 +371,7 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
       int f = sr.fb[q];
       asm volatile("" : "+v"(f));
       const int brow = MODE == 0 ? f / a.top_k : f;
-      sr.offB[q] = brow * K + ((dchunk ^ drow) << 4);  // row 32*wave + 8*q + drow: low bits drow
+      sr.offB[q] = brow * K + ((dchunk ^ drow ^ (q & 1)) << 4);  // row 32*wave + 8*q + drow
     }
   };
   const __amdgpu_buffer_rsrc_t rsrcB =
@@ -377,7 +383,8 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (void __attribute__((address_space(3)))*)(base + (64 * wave + 8 * q) * kPfBK), 16, sr.offA,
+          ra, (void __attribute__((address_space(3)))*)(base + (64 * wave + 8 * q) * kPfBK), 16,
+          (q & 1) ? (sr.offA ^ 16) : sr.offA,
           kb + 8 * q * K, 0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -391,7 +398,7 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
   // of the step uses chunks 4*ks + 2*(lane/32) + c, c = 0, 1 (32 bytes per
   // lane); bf16: MFMA k-step 2*ks + c (32 bytes) uses chunk 4*ks + 2*c +
   // lane/32 (16 bytes per lane).  Tiles differ by whole 32-row multiples,
-  // which leave the chunk swizzle unchanged, so a tile is a constant byte
+  // which leave pf_mix unchanged, so a tile is a constant byte
   // offset from the (ks, c) base.
   const int fr = lane & 31, hl = lane >> 5;
   const int arow0 = MODE == 0 ? 32 * wave : 64 * wave;
@@ -541,10 +548,10 @@ static __global__ __launch_bounds__(kPfThreads) void prefill_gemm_kernel(Prefill
     // the wave's own area past the ring is used); one 32-token tile at a time,
     // so that few accumulators are out of AGPRs at once.  Transposed tiles
     // (down product): token row t holds 16-byte chunk c at chunk position
-    // c ^ (t & 7), so that the writes (32 tokens, same chunk) and the reads
+    // c ^ pf_mix(t), so that the writes (32 tokens, same chunk) and the reads
     // (8 tokens x 8 chunks) spread evenly over the LDS banks.
     lds_u8* ep = smem + kPfRing + wave * kPfEpiWave;
-    auto ep_at = [&](int t, int c) { return ep + t * 128 + ((c ^ (t & 7)) << 4); };
+    auto ep_at = [&](int t, int c) { return ep + t * 128 + ((c ^ pf_mix(t)) << 4); };
     const int rt = lane >> 3, rc = lane & 7;  // read-back: token rt + 8*rr, chunk rc
     const float deq = (PC || BF) ? (BF ? 1.0f : 0.0f) : sa * a.w_scale[(int64_t)cur.e * a.w_es];  // the expert's or tensor's scale
     if (MODE == 0) {
