@@ -165,12 +165,32 @@ struct Layer1Lds {
 // a.xq, which every workgroup writes with the same bytes, or the workgroup's
 // own LDS copy), and the one-wave sort-and-pad into LDS.  The lead workgroup
 // also writes the routing, the sort-and-pad outputs that were asked for, and
-// s_x.  Ends with the workgroup synchronised.
+// s_x.  An fp8 x of at most 8192 elements (two 16-element chunks per
+// thread) is loaded into registers before the routing, so that its loads are
+// in flight with the logits' and x is read once.  Ends with the workgroup
+// synchronised.
+constexpr int kX2Reg = 2 * 256 * 16;
 template <bool FP8>
 __device__ __forceinline__ void layer1_prologue(const Layer1Args& a, Layer1Lds& s, bool lead, uint8_t* xq) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15;
   const int M = a.M, E = a.E, K = a.K, S = a.S, H = a.H;
   const int KS = K + S, ES = E + S, P = M * KS;
+  const int64_t nx = (int64_t)M * H;
+  const bool xreg = FP8 && nx <= kX2Reg;  // H is a multiple of 16
+  // chunk c: elements 16*(tid + 256c) .. +16, loaded from the last chunk
+  // where that is past x (no branch around the loads, so no wait for them
+  // here; a repeated chunk leaves the largest |x| unchanged)
+  u32x4 xr[4];
+  // a static s_x is read here too, beside the other loads
+  const float sx_given = (xreg && a.x_scale) ? *a.x_scale : 0.0f;
+  if (xreg) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int64_t i = min((int64_t)(tid + 256 * c) * 16, nx - 16);
+      xr[2 * c] = *(const u32x4*)(a.x + i);
+      xr[2 * c + 1] = *(const u32x4*)(a.x + i + 8);
+    }
+  }
   {
     const int m = wave * kRouteRows + (lane >> 4);
     int e;
@@ -188,11 +208,34 @@ __device__ __forceinline__ void layer1_prologue(const Layer1Args& a, Layer1Lds& 
     }
   }
   if constexpr (FP8) {
-    const int64_t nx = (int64_t)M * H;
-    const float sx = a.x_scale ? *a.x_scale : scale_from_amax(layer1_amax_bf16(a.x, nx, s.red4));
-    const float r = 1.0f / sx;
-    for (int64_t i = (int64_t)tid * 16; i < nx; i += 256 * 16)
-      *(u32x4*)(xq + i) = quant16_e4m3(*(const u32x4*)(a.x + i), *(const u32x4*)(a.x + i + 8), r);
+    float sx;
+    if (xreg) {
+      if (a.x_scale) {
+        sx = sx_given;
+      } else {  // largest |x| as layer1_amax_bf16 takes it, from the registers
+        unsigned m = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) m = max(m, max(xr[c][q] & 0x7fffu, (xr[c][q] >> 16) & 0x7fffu));
+        float am = wave_max(__uint_as_float(m << 16));
+        if (lane == 0) s.red4[wave] = am;
+        __syncthreads();
+        am = fmaxf(fmaxf(s.red4[0], s.red4[1]), fmaxf(s.red4[2], s.red4[3]));
+        sx = scale_from_amax(am);
+      }
+      const float r = 1.0f / sx;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int64_t i = (int64_t)(tid + 256 * c) * 16;
+        if (i < nx) *(u32x4*)(xq + i) = quant16_e4m3(xr[2 * c], xr[2 * c + 1], r);
+      }
+    } else {
+      sx = a.x_scale ? *a.x_scale : scale_from_amax(layer1_amax_bf16(a.x, nx, s.red4));
+      const float r = 1.0f / sx;
+      for (int64_t i = (int64_t)tid * 16; i < nx; i += 256 * 16)
+        *(u32x4*)(xq + i) = quant16_e4m3(*(const u32x4*)(a.x + i), *(const u32x4*)(a.x + i + 8), r);
+    }
     if (tid == 0) s.sx = sx;
     if (lead && tid == 0 && a.scales_out) a.scales_out[0] = sx;
     if (lead && tid == 0 && a.sx_out) *a.sx_out = sx;
