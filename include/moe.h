@@ -177,8 +177,9 @@ typedef struct {
                                 fp8 h scale with (top_k+S)*I above 64 KB); -1 = the per-expert down
                                 product and the finalize; 0 = default: per token where it fits and the
                                 tokens that share an expert would not re-read much of its W2 (always at
-                                M = 1; small experts up to 64 pairs), unless a down-product field above
-                                (gemm2_ksplit, gemm2_wave_ksplit, gemm2_stream_tiles) is set */
+                                M = 1; small experts up to 64 pairs), unless a down-product field
+                                (gemm2_ksplit, gemm2_wave_ksplit, gemm2_stream_tiles, gemm2_row_tiles) is
+                                set */
   int32_t routing_in_gate_up; /* tiny layers taking the per-token down product (at most 16 tokens and 64
                                 pairs, at most 256 routed experts, H a multiple of 512 in fp8 or of 128 in
                                 bf16, fp8 x of at most 8192 elements, not the single-launch layer): 1 = the
@@ -187,11 +188,24 @@ typedef struct {
                                 the layer would take another path); -1 = the routing launch of its own;
                                 0 = default: two launches where it fits and the gate/up product has at
                                 most 1024 items of 16 features (min(E+S, M*(top_k+S)) * I/16), unless a
-                                gate/up field above (gemm1_ksplit, token_tiles, unroll,
-                                gemm1_stream_tiles) is set.  The
+                                gate/up field (gemm1_ksplit, token_tiles, unroll, gemm1_stream_tiles,
+                                gemm1_feature_tiles) is set.  The
                                 outputs are those of the routing launch of its own, bit for bit, wherever
                                 that path's gate/up product splits K over four waves (bf16; fp8 below 8
                                 tokens) */
+  int32_t gemm1_feature_tiles; /* K-split gate/up: 16-feature groups per wave, 1 or 2 (2: the workgroup
+                                covers twice the features and reads each token row once for both, half
+                                the token-row reads per weight byte; same results bit for bit); 0 =
+                                default: 2 for bf16 layers whose gate/up grid keeps at least 2048
+                                workgroups with two (then with unroll 2 for the gate/up product unless
+                                unroll is given), else 1 */
+  int32_t gemm2_row_tiles;   /* K-split down: 32-row groups per wave, 1 or 2 (2 only where H divides into
+                                the workgroup's 32*2*4/gemm2_wave_ksplit rows and the K-split reduction
+                                buffer fits the workgroup's LDS): the same results bit for bit with the same
+                                K slices (the default slice count follows the number of workgroups, which
+                                two groups halve); 0 = default: 2 for bf16 layers with at least 12 pairs
+                                per expert that can hold tokens (M*(top_k+S) >= 12*min(E+S, M*(top_k+S))),
+                                where it fits, else 1 */
 } moe_tuning_t;
 
 /*

@@ -95,7 +95,9 @@ moe_status_t moe_probe_publish(float* buf, uint32_t* cnt, int32_t grid, int32_t 
  * 4096; 16 = every workgroup keeps its first tile and alternates between
  * its first two K-steps (96 KB per workgroup, re-read from L2); 32 (modes 0
  * and 2) = 256 token rows per step (64 KB, 512 rows per tile) in a two-slot
- * ring, loads one step ahead.  buf at least 512 * 4224 bytes.  buf: bytes a multiple of 4096, from 384*4224 to 2^30 (a buffer below the
+ * ring, loads one step ahead; 64 (modes 0 and 2, no other flag) = 256 token
+ * rows and 64-byte K-steps (32 KB, half a line of each row) in a four-slot
+ * ring, loads three steps ahead.  buf at least 512 * 4224 bytes.  buf: bytes a multiple of 4096, from 384*4224 to 2^30 (a buffer below the
  * L2 size stays there; one far above the last-level cache streams from
  * HBM).  sink: uint32 [grid * 4], each wave's XOR of what it read.  Other
  * arguments: MOE_ERR_INVALID_ARG.  The caller times the call with events:

@@ -44,7 +44,8 @@ class Tuning(ctypes.Structure):
                 ("gemm2_wave_ksplit", ctypes.c_int32), ("gemm1_stream_tiles", ctypes.c_int32),
                 ("gemm2_stream_tiles", ctypes.c_int32), ("reverse_order", ctypes.c_int32),
                 ("single_launch", ctypes.c_int32), ("down_per_token", ctypes.c_int32),
-                ("routing_in_gate_up", ctypes.c_int32)]
+                ("routing_in_gate_up", ctypes.c_int32), ("gemm1_feature_tiles", ctypes.c_int32),
+                ("gemm2_row_tiles", ctypes.c_int32)]
 
 
 class _FusedArgs(ctypes.Structure):
@@ -67,7 +68,7 @@ class _FusedArgs(ctypes.Structure):
 
 
 _lib = None
-_ABI = 14  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
+_ABI = 15  # moe_abi_version() of the library whose moe_fused_args_t _FusedArgs mirrors
 
 
 def load():

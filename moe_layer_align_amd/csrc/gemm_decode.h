@@ -165,11 +165,15 @@ __device__ __forceinline__ void stream_k(const uint8_t* const* pa, const uint8_t
 // --------------------------------------------------------------------------
 // Gate/up product with the SiLU(gate)*up epilogue.
 //
-// Wave tile: 16 output features i0..i0+15, i.e. gate rows i0.. and up rows
-// I+i0.. of W13[e] (two 16-row MFMA tiles whose accumulators land in the same
-// lanes, so the epilogue pairs gate and up without data exchange), times NT
-// 16-token tiles.  KSPLIT waves of the workgroup split K = H and are summed
-// through LDS; 4/KSPLIT feature tiles per workgroup.
+// Wave tile: FT groups of 16 output features i0+16f..i0+16f+15, i.e. gate
+// rows i0+16f.. and up rows I+i0+16f.. of W13[e] (16-row MFMA tiles whose
+// gate and up accumulators land in the same lanes, so the epilogue pairs
+// gate and up without data exchange), times NT 16-token tiles.  KSPLIT waves
+// of the workgroup split K = H and are summed through LDS; FT*4/KSPLIT
+// feature groups per workgroup.  With FT = 2 a wave's token fragments serve
+// twice the weight rows, which halves the token rows the workgroups read per
+// weight byte; every output's k-steps and K-split sum keep their order, so
+// the results are those of FT = 1, bit for bit.
 // --------------------------------------------------------------------------
 struct Gemm1Args {
   const uint8_t* w13;        // [E][2I][H]
@@ -218,7 +222,7 @@ __device__ __forceinline__ void row_deq4(const float* w_scale, int e, int rows_e
 // the workgroup's group of 4/KSPLIT feature tiles.  Returns the lane's
 // largest |h| (0 in lanes that store nothing), which the caller reduces
 // when the h scale is dynamic.
-template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT, int WS>
+template <bool FP8, int HFMT, int NT, int NB, int U, int KSPLIT, int WS, int FT = 1>
 __device__ __forceinline__ float gemm1_body(const Gemm1Args& a, f32x4* s_red, int e, int seg, int cnt, int pass0,
                                             int bx) {
   constexpr bool PC = WS == kWsRow, BS = FP8 && WS == kWsBlock;
@@ -226,19 +230,23 @@ __device__ __forceinline__ float gemm1_body(const Gemm1Args& a, f32x4* s_red, in
   constexpr int KSTEP = FP8 ? 128 : 32;   // k per MFMA
   constexpr int LB = FP8 ? 32 : 16;       // bytes per lane per operand per step
   constexpr int SB = KSTEP * ESZ;         // bytes per row per step
-  constexpr int TPW = 4 / KSPLIT;         // feature tiles per workgroup
+  constexpr int TPW = FT * 4 / KSPLIT;    // 16-feature groups per workgroup
+  constexpr int NA = 2 * FT;              // weight tiles per wave: gate, up of each group
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KSPLIT, tile = wave / KSPLIT;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int i0 = (bx * TPW + tile) * 16;
+  const int i0 = (bx * TPW + tile * FT) * 16;  // the wave's first feature
   const int Kw = a.H / KSPLIT;
   const int kbeg = kpart * Kw;
 
   const int64_t rowb = (int64_t)a.H * ESZ;
-  const uint8_t* pa[2];
-  pa[0] = a.w13 + ((int64_t)e * 2 * a.I + i0 + r16) * rowb + (int64_t)kbeg * ESZ + kq * LB;  // gate rows
-  pa[1] = pa[0] + (int64_t)a.I * rowb;                                                         // up rows
+  const uint8_t* pa[NA];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    pa[2 * f] = a.w13 + ((int64_t)e * 2 * a.I + i0 + 16 * f + r16) * rowb + (int64_t)kbeg * ESZ + kq * LB;  // gate
+    pa[2 * f + 1] = pa[2 * f] + (int64_t)a.I * rowb;                                                        // up
+  }
   const uint8_t* pb[NB];
   const uint8_t* qb[NB];  // block-scaled: the lane's token's group scales from kbeg on
 #pragma unroll
@@ -249,81 +257,97 @@ __device__ __forceinline__ float gemm1_body(const Gemm1Args& a, f32x4* s_red, in
     if constexpr (BS) qb[t] = a.x_block + (int64_t)m * (a.H / 128) + kbeg / 128;
   }
 
-  f32x4 acc[2][NB];
+  f32x4 acc[NA][NB];
 #pragma unroll
-  for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int t = 0; t < NB; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (BS) {
-    // the gate and up tiles' 128 x 128 weight blocks: rows i0/128 and (I+i0)/128
-    const uint8_t* qa[2];
+    // each gate and up tile's 128 x 128 weight block: rows (i0+16f)/128 and (I+i0+16f)/128
+    const uint8_t* qa[NA];
     const int kg = a.H / 128;
-    qa[0] = a.w_block + ((int64_t)e * (2 * a.I / 128) + i0 / 128) * kg + kbeg / 128;
-    qa[1] = a.w_block + ((int64_t)e * (2 * a.I / 128) + (a.I + i0) / 128) * kg + kbeg / 128;
-    stream_k<FP8, 2, NB, U, SB, true>(pa, pb, Kw / KSTEP, acc, qa, qb);
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      qa[2 * f] = a.w_block + ((int64_t)e * (2 * a.I / 128) + (i0 + 16 * f) / 128) * kg + kbeg / 128;
+      qa[2 * f + 1] = a.w_block + ((int64_t)e * (2 * a.I / 128) + (a.I + i0 + 16 * f) / 128) * kg + kbeg / 128;
+    }
+    stream_k<FP8, NA, NB, U, SB, true>(pa, pb, Kw / KSTEP, acc, qa, qb);
   } else {
-    stream_k<FP8, 2, NB, U, SB>(pa, pb, Kw / KSTEP, acc);
+    stream_k<FP8, NA, NB, U, SB>(pa, pb, Kw / KSTEP, acc);
   }
 
   if constexpr (KSPLIT > 1) {
+    // partial tiles of K parts 1..KSPLIT-1: group g of the workgroup, token
+    // tile t, gate (0) or up (1) at ((part-1)*TPW + g)*2*NT + 2t + (0|1)
     if (kpart > 0) {
-      f32x4* dst = s_red + (((kpart - 1) * TPW + tile) * 2 * NT) * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        dst[(2 * t) * 64] = acc[0][t];
-        dst[(2 * t + 1) * 64] = acc[1][t];
+      for (int f = 0; f < FT; ++f) {
+        f32x4* dst = s_red + (((kpart - 1) * TPW + tile * FT + f) * 2 * NT) * 64 + lane;
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          dst[(2 * t) * 64] = acc[2 * f][t];
+          dst[(2 * t + 1) * 64] = acc[2 * f + 1][t];
+        }
       }
     }
     __syncthreads();
     if (kpart > 0) return 0.0f;
 #pragma unroll
-    for (int p = 0; p < KSPLIT - 1; ++p) {
-      const f32x4* src = s_red + ((p * TPW + tile) * 2 * NT) * 64 + lane;
+    for (int p = 0; p < KSPLIT - 1; ++p)
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        acc[0][t] += src[(2 * t) * 64];
-        acc[1][t] += src[(2 * t + 1) * 64];
+      for (int f = 0; f < FT; ++f) {
+        const f32x4* src = s_red + ((p * TPW + tile * FT + f) * 2 * NT) * 64 + lane;
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          acc[2 * f][t] += src[(2 * t) * 64];
+          acc[2 * f + 1][t] += src[(2 * t + 1) * 64];
+        }
       }
-    }
   }
 
-  // dequantisation of this lane's rows: gate rows i0+4kq.., up rows I+i0+4kq..
-  float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-  if constexpr (FP8 && !BS) {  // block-scaled: the MFMA applied the scales
-    row_deq4<PC>(a.w_scale, e, 2 * a.I, i0 + kq * 4, *a.x_scale, dg, a.w_es);
-    row_deq4<PC>(a.w_scale, e, 2 * a.I, a.I + i0 + kq * 4, *a.x_scale, du, a.w_es);
-  }
   float rh = 1.0f;
   if constexpr (HFMT == H_E4M3) rh = 1.0f / *a.h_scale;
   float hmax = 0.0f;
 #pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    const int slot = pass0 + t * 16 + r16;
-    if (slot < cnt) {
-      const int f = a.seg.sorted_ids[seg + slot];
-      float hv[4];
+  for (int f = 0; f < FT; ++f) {
+    const int i0f = i0 + 16 * f;
+    // dequantisation of this lane's rows: gate rows i0f+4kq.., up rows I+i0f+4kq..
+    float dg[4] = {1.0f, 1.0f, 1.0f, 1.0f}, du[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (FP8 && !BS) {  // block-scaled: the MFMA applied the scales
+      row_deq4<PC>(a.w_scale, e, 2 * a.I, i0f + kq * 4, *a.x_scale, dg, a.w_es);
+      row_deq4<PC>(a.w_scale, e, 2 * a.I, a.I + i0f + kq * 4, *a.x_scale, du, a.w_es);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float g = acc[0][t][r] * dg[r];
-        const float u = acc[1][t][r] * du[r];
-        hv[r] = g / (1.0f + expf(-g)) * u;
-        hmax = fmaxf(hmax, fabsf(hv[r]));
-      }
-      const int64_t idx = (int64_t)f * a.I + i0 + kq * 4;
-      if constexpr (HFMT == H_BF16) {
-        u32x2 o = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-        *(u32x2*)(a.h + idx * 2) = o;
-      } else if constexpr (HFMT == H_F32) {
-        *(f32x4*)(a.h + idx * 4) = f32x4{hv[0], hv[1], hv[2], hv[3]};
-      } else {
-        *(unsigned*)(a.h + idx) = pack_e4m3x4(hv[0] * rh, hv[1] * rh, hv[2] * rh, hv[3] * rh);
+    for (int t = 0; t < NB; ++t) {
+      const int slot = pass0 + t * 16 + r16;
+      if (slot < cnt) {
+        const int pf = a.seg.sorted_ids[seg + slot];
+        float hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[2 * f][t][r] * dg[r];
+          const float u = acc[2 * f + 1][t][r] * du[r];
+          hv[r] = g / (1.0f + expf(-g)) * u;
+          hmax = fmaxf(hmax, fabsf(hv[r]));
+        }
+        const int64_t idx = (int64_t)pf * a.I + i0f + kq * 4;
+        if constexpr (HFMT == H_BF16) {
+          u32x2 o = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+          *(u32x2*)(a.h + idx * 2) = o;
+        } else if constexpr (HFMT == H_F32) {
+          *(f32x4*)(a.h + idx * 4) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+        } else {
+          *(unsigned*)(a.h + idx) = pack_e4m3x4(hv[0] * rh, hv[1] * rh, hv[2] * rh, hv[3] * rh);
+        }
       }
     }
   }
   return hmax;
 }
 
-template <bool FP8, int HFMT, int NT, int U, int KSPLIT>
+template <bool FP8, int HFMT, int NT, int U, int KSPLIT, int FT = 1>
 static __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
-  constexpr int TPW = 4 / KSPLIT;
+  constexpr int TPW = FT * 4 / KSPLIT;
   __shared__ f32x4 s_red[KSPLIT > 1 ? (KSPLIT - 1) * TPW * 2 * NT * 64 : 1];
   const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
@@ -336,12 +360,12 @@ static __global__ __launch_bounds__(256) void gemm1_decode_kernel(Gemm1Args a) {
     constexpr int WS = decltype(ws_tag)::value;
     const int bx = blockIdx.x;
     if constexpr (NT >= 4)
-      if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
+      if (ntile == 4) return gemm1_body<FP8, HFMT, NT, 4, U, KSPLIT, WS, FT>(a, s_red, e, seg, cnt, pass0, bx);
     if constexpr (NT >= 3)
-      if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
+      if (ntile == 3) return gemm1_body<FP8, HFMT, NT, 3, U, KSPLIT, WS, FT>(a, s_red, e, seg, cnt, pass0, bx);
     if constexpr (NT >= 2)
-      if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
-    return gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT, WS>(a, s_red, e, seg, cnt, pass0, bx);
+      if (ntile == 2) return gemm1_body<FP8, HFMT, NT, 2, U, KSPLIT, WS, FT>(a, s_red, e, seg, cnt, pass0, bx);
+    return gemm1_body<FP8, HFMT, NT, 1, U, KSPLIT, WS, FT>(a, s_red, e, seg, cnt, pass0, bx);
   };
   float hmax;
   if constexpr (FP8 && HFMT == H_F32) {
@@ -640,9 +664,11 @@ __device__ __forceinline__ void stage_h_block(const Gemm2Args& a, uint8_t* s_tok
 }
 
 // Body for NB (<= NT) token tiles.  WKS waves of the workgroup split the
-// slice's K range and are summed through LDS (s_red); 4/WKS groups of 32 rows
-// per workgroup.
-template <bool FP8, int HFMT, int NT, int NB, int U, int WKS, int WS>
+// slice's K range and are summed through LDS (s_red); each wave computes FR
+// groups of 32 rows, FR*4/WKS groups per workgroup (FR = 2: a wave's token
+// fragments serve twice the weight rows; every output's sums keep their
+// order, so the results are those of FR = 1, bit for bit).
+template <bool FP8, int HFMT, int NT, int NB, int U, int WKS, int WS, int FR = 1>
 __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f32x4* s_red, int e, int seg, int cnt,
                                            int pass0, int kslice, int bx) {
   constexpr bool PC = WS == kWsRow, BS = FP8 && HFMT == H_F32 && WS == kWsBlock;
@@ -652,26 +678,31 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
   constexpr int SB = KSTEP * ESZ;
   constexpr int HSZ = HFMT == H_BF16 ? 2 : (HFMT == H_F32 ? 4 : 1);
   constexpr bool QH = FP8 && HFMT == H_F32;  // token operand staged in LDS
-  constexpr int TPW = 4 / WKS;
+  constexpr int TPW = FR * 4 / WKS;          // 32-row groups per workgroup
+  constexpr int NA = 2 * FR;                 // 16-row weight tiles per wave
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % WKS, tile = wave / WKS;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int n0 = (bx * TPW + tile) * 32;
+  const int n0 = (bx * TPW + tile * FR) * 32;  // the wave's first row
   const int Kw = a.I / a.ksplit;       // K range of the workgroup
   const int kbeg = kslice * Kw;
   const int Kp = Kw / WKS;             // K range of the wave
   const int koff = kpart * Kp;
 
-  // dequantisation of this lane's rows n0+4kq.. and n0+16+4kq..
-  float d0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, d1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  // dequantisation of this lane's rows n0+16i+4kq.. of weight tile i
+  float d[NA][4];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[i][r] = 1.0f;
   if constexpr (BS) {  // the MFMA applies the scales
     stage_h_block<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw);
     __syncthreads();
   } else if constexpr (FP8) {
     const float sh = (HFMT == H_F32) ? scale_from_amax(__uint_as_float(*a.h_amax)) : *a.h_scale;
-    row_deq4<PC>(a.w_scale, e, a.H, n0 + kq * 4, sh, d0, a.w_es);
-    row_deq4<PC>(a.w_scale, e, a.H, n0 + 16 + kq * 4, sh, d1, a.w_es);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) row_deq4<PC>(a.w_scale, e, a.H, n0 + 16 * i + kq * 4, sh, d[i], a.w_es);
     if constexpr (QH) {
       stage_h_e4m3<NB>(a, s_tok, seg, cnt, pass0, kbeg, Kw, 1.0f / sh);
       __syncthreads();
@@ -679,9 +710,10 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
   }
 
   const int64_t rowb = (int64_t)a.I * ESZ;
-  const uint8_t* pa[2];
+  const uint8_t* pa[NA];
   pa[0] = a.w2 + ((int64_t)e * a.H + n0 + r16) * rowb + (int64_t)(kbeg + koff) * ESZ + kq * LB;
-  pa[1] = pa[0] + 16 * rowb;
+#pragma unroll
+  for (int i = 1; i < NA; ++i) pa[i] = pa[0] + 16 * i * rowb;
   const uint8_t* pb[NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
@@ -694,43 +726,54 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
     }
   }
 
-  f32x4 acc[2][NB];
+  f32x4 acc[NA][NB];
 #pragma unroll
-  for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int t = 0; t < NB; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (BS) {
-    // both 16-row tiles lie in the 128 x 128 block of rows n0/128; the token
-    // rows' group scales follow the staged slice
-    const uint8_t* qa[2];
-    qa[0] = qa[1] = a.w_block + ((int64_t)e * (a.H / 128) + n0 / 128) * (a.I / 128) + (kbeg + koff) / 128;
+    // each 16-row tile's 128 x 128 weight block; the token rows' group
+    // scales follow the staged slice
+    const uint8_t* qa[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      qa[i] = a.w_block + ((int64_t)e * (a.H / 128) + (n0 + 16 * i) / 128) * (a.I / 128) + (kbeg + koff) / 128;
     const uint8_t* qb[NB];
     const uint8_t* s_scale = s_tok + NB * 16 * gemm2_lds_stride(Kw);
 #pragma unroll
     for (int t = 0; t < NB; ++t) qb[t] = s_scale + (t * 16 + r16) * (Kw / 128) + koff / 128;
-    stream_k<FP8, 2, NB, U, SB, true>(pa, pb, Kp / KSTEP, acc, qa, qb);
+    stream_k<FP8, NA, NB, U, SB, true>(pa, pb, Kp / KSTEP, acc, qa, qb);
   } else {
-    stream_k<FP8, 2, NB, U, SB>(pa, pb, Kp / KSTEP, acc);
+    stream_k<FP8, NA, NB, U, SB>(pa, pb, Kp / KSTEP, acc);
   }
 
   if constexpr (WKS > 1) {
+    // partial tiles of K parts 1..WKS-1: group g of the workgroup, token tile
+    // t, 16-row half h at ((part-1)*TPW + g)*2*NT + 2t + h
     if (kpart > 0) {
-      f32x4* dst = s_red + (((kpart - 1) * TPW + tile) * 2 * NT) * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        dst[(2 * t) * 64] = acc[0][t];
-        dst[(2 * t + 1) * 64] = acc[1][t];
+      for (int g = 0; g < FR; ++g) {
+        f32x4* dst = s_red + (((kpart - 1) * TPW + tile * FR + g) * 2 * NT) * 64 + lane;
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          dst[(2 * t) * 64] = acc[2 * g][t];
+          dst[(2 * t + 1) * 64] = acc[2 * g + 1][t];
+        }
       }
     }
     __syncthreads();
     if (kpart > 0) return;
 #pragma unroll
-    for (int p = 0; p < WKS - 1; ++p) {
-      const f32x4* src = s_red + ((p * TPW + tile) * 2 * NT) * 64 + lane;
+    for (int p = 0; p < WKS - 1; ++p)
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        acc[0][t] += src[(2 * t) * 64];
-        acc[1][t] += src[(2 * t + 1) * 64];
+      for (int g = 0; g < FR; ++g) {
+        const f32x4* src = s_red + ((p * TPW + tile * FR + g) * 2 * NT) * 64 + lane;
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          acc[2 * g][t] += src[(2 * t) * 64];
+          acc[2 * g + 1][t] += src[(2 * t + 1) * 64];
+        }
       }
-    }
   }
 
   float* part = a.part + (int64_t)kslice * a.P * a.H;
@@ -740,18 +783,19 @@ __device__ __forceinline__ void gemm2_body(const Gemm2Args& a, uint8_t* s_tok, f
     if (slot < cnt) {
       const int f = a.seg.sorted_ids[seg + slot];
       float* dst = part + (int64_t)f * a.H + n0 + kq * 4;
-      *(f32x4*)dst = acc[0][t] * f32x4{d0[0], d0[1], d0[2], d0[3]};
-      *(f32x4*)(dst + 16) = acc[1][t] * f32x4{d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        *(f32x4*)(dst + 16 * i) = acc[i][t] * f32x4{d[i][0], d[i][1], d[i][2], d[i][3]};
     }
   }
 }
 
-// Grid: x = groups of 32*(4/WKS) output rows, y = active expert, z = K slice
-// + ksplit * token pass.
-template <bool FP8, int HFMT, int NT, int U, int WKS>
+// Grid: x = groups of 32*FR*(4/WKS) output rows, y = active expert, z = K
+// slice + ksplit * token pass.
+template <bool FP8, int HFMT, int NT, int U, int WKS, int FR = 1>
 static __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
   extern __shared__ __align__(16) uint8_t s_tok[];
-  constexpr int TPW = 4 / WKS;
+  constexpr int TPW = FR * 4 / WKS;
   __shared__ f32x4 s_red[WKS > 1 ? (WKS - 1) * TPW * 2 * NT * 64 : 1];
   const int s = grid_y(a.seg);
   if (s >= *a.seg.num_active) return;
@@ -765,14 +809,14 @@ static __global__ __launch_bounds__(256) void gemm2_decode_kernel(Gemm2Args a) {
     constexpr int WS = decltype(ws_tag)::value;
     if constexpr (NT >= 4)
       if (ntile == 4)
-        return gemm2_body<FP8, HFMT, NT, 4, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+        return gemm2_body<FP8, HFMT, NT, 4, U, WKS, WS, FR>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
     if constexpr (NT >= 3)
       if (ntile == 3)
-        return gemm2_body<FP8, HFMT, NT, 3, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+        return gemm2_body<FP8, HFMT, NT, 3, U, WKS, WS, FR>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
     if constexpr (NT >= 2)
       if (ntile == 2)
-        return gemm2_body<FP8, HFMT, NT, 2, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
-    gemm2_body<FP8, HFMT, NT, 1, U, WKS, WS>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+        return gemm2_body<FP8, HFMT, NT, 2, U, WKS, WS, FR>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
+    gemm2_body<FP8, HFMT, NT, 1, U, WKS, WS, FR>(a, s_tok, s_red, e, seg, cnt, pass0, kslice, blockIdx.x);
   };
   if constexpr (FP8 && HFMT == H_F32)
     if (a.w_bs) return run(std::integral_constant<int, kWsBlock>{});  // block-scaled
@@ -888,9 +932,10 @@ static __global__ __launch_bounds__(256) void gemm2_stream_kernel(Gemm2Args a, i
   run(std::false_type{});
 }
 
-// LDS of a down-product workgroup: the K-split reduction buffer.
-__host__ __device__ constexpr int gemm2_red_bytes(int nt, int wks) {
-  return wks > 1 ? (wks - 1) * (4 / wks) * 2 * nt * 64 * 16 : 16;
+// LDS of a down-product workgroup: the K-split reduction buffer (fr 32-row
+// groups per wave).
+__host__ __device__ constexpr int gemm2_red_bytes(int nt, int wks, int fr = 1) {
+  return wks > 1 ? (wks - 1) * (fr * 4 / wks) * 2 * nt * 64 * 16 : 16;
 }
 
 // Top-k combine and output rounding:

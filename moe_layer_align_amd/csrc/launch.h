@@ -21,6 +21,7 @@ struct DecodeShape {
   int tw;     // > 0: long-stream variant with tw tiles per wave
   dim3 grid;  // grid of the chosen variant
   size_t lds; // dynamic LDS (down product, dynamic fp8 h scale)
+  int ft = 1; // K-split variants: groups per wave (1 or 2) of 16 features (gate/up) or 32 rows (down)
 };
 
 bool launch_gemm1_bf16(const DecodeShape& s, hipStream_t st, const Gemm1Args& a);

@@ -153,8 +153,8 @@ Layout make_layout(int M, int E, int H, int I, int k, moe_dtype_t dt, bool decod
 // 4-token-tile variants keep a workgroup's registers high on purpose) over
 // high occupancy.
 struct Plan {
-  int nt1, passes1, u1, ks1, tw1;          // gate/up (tw1 > 0: long-stream variant)
-  int nt2, passes2, u2, ks2, wks2, lds2, tw2;  // down (tw2 > 0: long-stream variant)
+  int nt1, passes1, u1, ks1, tw1, ft1;     // gate/up (tw1 > 0: long-stream variant; ft1 groups per wave)
+  int nt2, passes2, u2, ks2, wks2, lds2, tw2, fr2;  // down (tw2 > 0: long-stream variant; fr2 groups per wave)
   int rev;                                  // reversed grid order (Segments::rev)
   int tok, tok_chunks;                      // down product and combine per token (down_token_kernel)
 };
@@ -253,6 +253,23 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
     p->wks2 = wks;
   }
   if ((H / p->ks1) % kstep != 0) return MOE_ERR_UNSUPPORTED;
+  // K-split gate/up: 16-feature groups per wave (each output's sums are the
+  // same either way).  bf16: two, with two k-steps per stage unless the
+  // unroll is given, where the halved grid keeps at least 2048 workgroups
+  // (Mixtral shape: M = 63 334 vs 361 us, M = 4..32 1-2 % faster; at M = 1,
+  // 896 workgroups, 86 vs 79 us); fp8: one (DeepSeek shape M = 64, 128: two
+  // are 2 % slower)
+  p->ft1 = 1;
+  if (!fp8 && p->tw1 == 0 && (int64_t)(I / 16) / (8 / p->ks1) * n_act * cdiv(M, p->nt1 * 16) >= 2048) {
+    p->ft1 = 2;
+    if (!(t && t->unroll > 0)) p->u1 = 2;
+  }
+  if (t && t->gemm1_feature_tiles != 0) {
+    if (t->gemm1_feature_tiles != 1 && t->gemm1_feature_tiles != 2) return MOE_ERR_UNSUPPORTED;
+    if (t->gemm1_feature_tiles == 2 && p->tw1 > 0) return MOE_ERR_UNSUPPORTED;  // a long-stream gate/up
+    p->ft1 = t->gemm1_feature_tiles;
+  }
+  if (p->tw1 > 0) p->ft1 = 1;
   p->passes1 = (int)cdiv(M, p->nt1 * 16);
   p->passes2 = (int)cdiv(M, p->nt2 * 16);
 
@@ -261,23 +278,45 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
   // token slice must fit the workgroup's LDS.  Default: the fewest slices
   // that give at least 1024 workgroups (4 per CU), or 256 (one per CU) for
   // the long-stream variant.
+  // K-split down: 32-row groups per wave (each output's sums are the same
+  // for the same K slices); the workgroup's rows must divide H.  Default:
+  // two for bf16 layers with at least 12 pairs per expert that can hold
+  // tokens, where most experts take two token tiles and the token rows
+  // would be read as often as the weights (Mixtral shape M = 63: 170 vs
+  // 182 us; at M <= 32 the halved grid takes more K slices and is slower)
+  const bool fr2_ok = p->tw2 == 0 && (H / 32) % (8 / p->wks2) == 0;
+  const bool fr2_pinned = t && t->gemm2_row_tiles != 0;
+  p->fr2 = (!fp8 && fr2_ok && P >= 12 * (int64_t)n_act) ? 2 : 1;
+  if (fr2_pinned) {
+    if (t->gemm2_row_tiles != 1 && t->gemm2_row_tiles != 2) return MOE_ERR_UNSUPPORTED;
+    if (t->gemm2_row_tiles == 2 && !fr2_ok) return MOE_ERR_UNSUPPORTED;
+    p->fr2 = t->gemm2_row_tiles;
+  }
   const int nsteps2 = I / kstep;
   auto fits = [&](int ks) {
     if (nsteps2 % (ks * p->wks2) != 0) return false;
     if (p->tw2 > 0 && (nsteps2 / ks) % p->u2 != 0) return false;
     const int64_t lds = (qh ? (int64_t)p->nt2 * 16 * gemm2_lds_stride(I / ks) : 0) +
-                        (blk ? gemm2_block_scale_bytes(p->nt2 * 16, I / ks) : 0) + gemm2_red_bytes(p->nt2, p->wks2);
+                        (blk ? gemm2_block_scale_bytes(p->nt2 * 16, I / ks) : 0) +
+                        gemm2_red_bytes(p->nt2, p->wks2, p->fr2);
     return lds <= kDownLdsMax;
   };
   const int ks_cap = down_ksplit_cap(P, H, I, fp8);
-  const int64_t groups2 = p->tw2 > 0 ? cdiv(rtiles, 4 * p->tw2) : H / (32 * (4 / p->wks2));
-  const int64_t wgs_per_slice = groups2 * n_act * p->passes2;
-  p->ks2 = 0;
-  const int64_t wgs_target = p->tw2 > 0 ? 256 : 1024;
-  for (int ks = 1; ks <= (det ? 1 : ks_cap); ++ks) {
-    if (!fits(ks)) continue;
-    p->ks2 = ks;
-    if (wgs_per_slice * ks >= wgs_target) break;
+  auto pick_ks2 = [&] {
+    const int64_t groups2 = p->tw2 > 0 ? cdiv(rtiles, 4 * p->tw2) : H / (32 * (p->fr2 * 4 / p->wks2));
+    const int64_t wgs_per_slice = groups2 * n_act * p->passes2;
+    const int64_t wgs_target = p->tw2 > 0 ? 256 : 1024;
+    p->ks2 = 0;
+    for (int ks = 1; ks <= (det ? 1 : ks_cap); ++ks) {
+      if (!fits(ks)) continue;
+      p->ks2 = ks;
+      if (wgs_per_slice * ks >= wgs_target) break;
+    }
+  };
+  pick_ks2();
+  if (p->ks2 == 0 && p->fr2 == 2 && !fr2_pinned) {  // the default's second group does not fit: one
+    p->fr2 = 1;
+    pick_ks2();
   }
   if (t && t->gemm2_ksplit > 0) {
     const int ks = t->gemm2_ksplit;
@@ -300,7 +339,8 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
   // slower).
   const int mode = t ? t->down_per_token : 0;
   if (mode < -1 || mode > 1) return MOE_ERR_UNSUPPORTED;
-  const bool pinned = t && (t->gemm2_ksplit > 0 || t->gemm2_wave_ksplit > 0 || t->gemm2_stream_tiles != 0);
+  const bool pinned = t && (t->gemm2_ksplit > 0 || t->gemm2_wave_ksplit > 0 || t->gemm2_stream_tiles != 0 ||
+                            t->gemm2_row_tiles != 0);
   const bool tok_fits = !det && !blk && P <= kTokDownPairs && (!qh || (int64_t)k * I <= kTokDownLds);
   if (mode == 1 && !tok_fits) return MOE_ERR_UNSUPPORTED;
   const int Er = E - S, kr = k - S;
@@ -469,7 +509,7 @@ const char* moe_status_string(moe_status_t s) {
   return "MOE_ERR_UNKNOWN";
 }
 
-int32_t moe_abi_version(void) { return 14; }
+int32_t moe_abi_version(void) { return 15; }
 
 moe_status_t moe_route_topk(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t* topk_ids,
                             float* topk_weights, void* stream) {
@@ -717,7 +757,8 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
   if (rmode < -1 || rmode > 1) return MOE_ERR_UNSUPPORTED;
   if (!prefill && !l1_wks) {
     const bool g1_pinned = a->tuning && (a->tuning->gemm1_ksplit > 0 || a->tuning->token_tiles > 0 ||
-                                         a->tuning->unroll > 0 || a->tuning->gemm1_stream_tiles != 0);
+                                         a->tuning->unroll > 0 || a->tuning->gemm1_stream_tiles != 0 ||
+                                         a->tuning->gemm1_feature_tiles != 0);
     // (gate/up K split over four waves in whole MFMA k-steps, as in the single-launch layer)
     const bool fits = plan.tok && M <= kLayer1Tokens && (int64_t)M * k <= kLayer1Pairs && Er <= kLayer1Experts &&
                       (H / 4) % (fp8 ? 128 : 32) == 0 && (!fp8 || (int64_t)M * H <= kTinyXElems);
@@ -942,9 +983,10 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     g.w_bs = blk ? 1 : 0;
     g.w_block = blk ? (const uint8_t*)a->w13_scale : nullptr;
     g.x_block = xs_blk;
-    DecodeShape sh{plan.nt1, plan.u1, plan.ks1, plan.tw1, dim3(), 0};
-    sh.grid = plan.tw1 > 0 ? dim3((unsigned)cdiv(I / 16, 4 * plan.tw1), (unsigned)n_act, (unsigned)plan.passes1)
-                           : dim3((unsigned)(I / 16 / (4 / plan.ks1)), (unsigned)n_act, (unsigned)plan.passes1);
+    DecodeShape sh{plan.nt1, plan.u1, plan.ks1, plan.tw1, dim3(), 0, plan.ft1};
+    sh.grid = plan.tw1 > 0
+                  ? dim3((unsigned)cdiv(I / 16, 4 * plan.tw1), (unsigned)n_act, (unsigned)plan.passes1)
+                  : dim3((unsigned)(I / 16 / (plan.ft1 * 4 / plan.ks1)), (unsigned)n_act, (unsigned)plan.passes1);
     const bool ok = fp8 ? launch_gemm1_fp8(hdyn ? H_F32 : H_E4M3, sh, st, g) : launch_gemm1_bf16(sh, st, g);
     if (!ok) return MOE_ERR_UNSUPPORTED;
   }
@@ -980,10 +1022,11 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     g.w_es = a->weight_scale_mode == 2 ? 1 : 0;
     g.w_bs = blk ? 1 : 0;
     g.w_block = blk ? (const uint8_t*)a->w2_scale : nullptr;
-    DecodeShape sh{plan.nt2, plan.u2, plan.wks2, plan.tw2, dim3(), (size_t)(hf == H_F32 ? plan.lds2 : 0)};
+    DecodeShape sh{plan.nt2, plan.u2, plan.wks2, plan.tw2, dim3(), (size_t)(hf == H_F32 ? plan.lds2 : 0), plan.fr2};
     sh.grid = plan.tw2 > 0
                   ? dim3((unsigned)cdiv(H / 32, 4 * plan.tw2), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2))
-                  : dim3((unsigned)(H / (32 * (4 / plan.wks2))), (unsigned)n_act, (unsigned)(plan.ks2 * plan.passes2));
+                  : dim3((unsigned)(H / (32 * (plan.fr2 * 4 / plan.wks2))), (unsigned)n_act,
+                         (unsigned)(plan.ks2 * plan.passes2));
     const bool ok = fp8 ? launch_gemm2_fp8(hf, sh, st, g) : launch_gemm2_bf16(sh, st, g);
     if (!ok) return MOE_ERR_UNSUPPORTED;
   }

@@ -261,6 +261,59 @@ __global__ __launch_bounds__(256) void ring_dma_kernel(const uint8_t* __restrict
   ring_sink(x, sink, wave, lane);
 }
 
+// modes 0 and 2 with 64-byte K-steps over 256 weight and 256 token rows
+// (half a cache line of each row per step, 32 KB): four slots, loads three
+// steps ahead (96 KB in flight).  A 1 KB load covers 16 rows; lane i loads
+// logical chunk (i%4) ^ ((row/4)%4) of row i/4 into position i%4.
+template <bool READS>
+__global__ __launch_bounds__(256) void ring_half_kernel(const uint8_t* __restrict__ buf, int bytes, int steps,
+                                                        uint32_t* __restrict__ sink) {
+  constexpr int HB = 64, SB = 512 * HB;
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrows = bytes / kRingRow;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)buf, (short)0, bytes, 0x00020000);
+  const int lr = lane >> 2, lc = lane & 3;
+  auto issue = [&](int s) {
+    const int tile = blockIdx.x + (s / 64) * gridDim.x;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // rows 64w + 16q' + lane/4 of the weight block (q < 4) and of the token block
+      const int r = (q < 4 ? 0 : 256) + 64 * wave + 16 * (q & 3) + lr;
+      const int row = (int)(((int64_t)tile * 512 + r) % nrows);
+      const int o = row * kRingRow + (s % 64) * HB + ((lc ^ ((r >> 2) & 3)) << 4);
+      lds_u8* d = smem + (s % 4) * SB + (r - lr) * HB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3)))*)d, 16, o, 0, 0, 0);
+    }
+  };
+  u32x4 x = {0u, 0u, 0u, 0u};
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int s = 0; s < steps; ++s) {
+    ring_wait_vm<16>();  // step s landed; s+1 and s+2 may be in flight
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const lds_u8* st = smem + (s % 4) * SB;
+    if (READS) {
+      // one fp8 MFMA k-step: 2 A tiles and 8 B tiles of 32 rows, 32 bytes per
+      // lane (logical chunks 2*(lane/32), +1)
+#pragma unroll
+      for (int q = 0; q < 20; ++q) {
+        const int t = q >> 1, c = 2 * (lane >> 5) + (q & 1);
+        const int r = t < 2 ? 64 * wave + 32 * t + (lane & 31) : 256 + 32 * (t - 2) + (lane & 31);
+        x ^= *(const __attribute__((address_space(3))) u32x4*)(st + r * HB + ((c ^ ((r >> 2) & 3)) << 4));
+      }
+    } else {
+      x ^= *(const __attribute__((address_space(3))) u32x4*)(st + threadIdx.x * 16);
+    }
+    issue(s + 3);  // into the slot of step s-1, which every wave has read
+  }
+  ring_wait_vm<0>();
+  ring_sink(x, sink, wave, lane);
+}
+
 // mode 1: register loads (steps s+1 and s+2 in flight in registers while
 // step s is stored), then 16-byte LDS stores
 __global__ __launch_bounds__(256) void ring_reg_kernel(const uint8_t* __restrict__ buf, int bytes, int steps,
@@ -352,18 +405,23 @@ moe_status_t moe_probe_ring_load(const void* buf, size_t bytes, int32_t grid, in
   mode &= 3;
   if (!buf || !sink || bytes % kRingRow != 0 || bytes < (size_t)512 * (kRingRow + kRingBK) ||
       bytes > ((size_t)1 << 30) || grid < 1 || grid > 65536 || steps < 3 || steps > (1 << 20) || steps % 3 != 0 ||
-      mode > 2 || flags > 15 || ((flags & 8) && mode == 1))
+      mode > 2 || flags > 31 || ((flags & 24) && mode == 1) || ((flags & 16) && (flags & 15)))
     return MOE_ERR_INVALID_ARG;
   const hipStream_t st = (hipStream_t)stream;
   const bool wide = (flags & 8) != 0;  // 256 token rows per step, two slots
-  const size_t lds = wide ? (size_t)2 * 512 * kRingBK : (size_t)kRingStages * kRingStage;
+  const bool half = (flags & 16) != 0;  // 256 token rows, 64-byte steps, four slots
+  const size_t lds = half ? (size_t)4 * 512 * 64 : wide ? (size_t)2 * 512 * kRingBK : (size_t)kRingStages * kRingStage;
   const void* k = mode == 1 ? (const void*)ring_reg_kernel
+                  : half ? (mode == 0 ? (const void*)ring_half_kernel<false> : (const void*)ring_half_kernel<true>)
                   : wide ? (mode == 0 ? (const void*)ring_dma_kernel<false, 256> : (const void*)ring_dma_kernel<true, 256>)
                          : (mode == 0 ? (const void*)ring_dma_kernel<false, 128> : (const void*)ring_dma_kernel<true, 128>);
   if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return MOE_ERR_DEVICE;
   const uint8_t* b = (const uint8_t*)buf;
   if (mode == 1) ring_reg_kernel<<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
+  if (mode == 0 && half) ring_half_kernel<false><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink);
+  if (mode == 2 && half) ring_half_kernel<true><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink);
+  if (half) return launch_status();
   if (mode == 0 && !wide) ring_dma_kernel<false, 128><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
   if (mode == 2 && !wide) ring_dma_kernel<true, 128><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);
   if (mode == 0 && wide) ring_dma_kernel<false, 256><<<grid, 256, lds, st>>>(b, (int)bytes, steps, sink, flags);

@@ -108,7 +108,8 @@ def ring_load(buf: torch.Tensor, sink: torch.Tensor, grid: int, steps: int, mode
     through a three-slot LDS ring; mode 0 direct-to-LDS loads, 1 register
     loads and LDS stores, 2 mode 0 plus the product's fragment reads, plus 4
     (K start rotated per workgroup), 8 (rows 4224 bytes apart) and 16 (a
-    private 96 KB window per workgroup, re-read from L2).  sink:
+    private 96 KB window per workgroup, re-read from L2), 32 (256 token rows, two
+    slots) and 64 (256 token rows, 64-byte K-steps, four slots).  sink:
     int32 GPU tensor of at least grid*4 elements."""
     if not (buf.is_cuda and buf.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
             and sink.numel() >= grid * 4):

@@ -68,7 +68,9 @@ def test_probe_library_exports_its_header():
     assert plib.moe_probe_publish(16, 16, 0, 0, None) == 1                    # empty grid
     rl, MB = plib.moe_probe_ring_load, 1 << 20
     assert rl(16, 4 * MB, 1, 3, 3, 16, None) == 1          # unknown mode
-    assert rl(16, 4 * MB, 1, 3, 64, 16, None) == 1         # unknown flag
+    assert rl(16, 4 * MB, 1, 3, 128, 16, None) == 1        # unknown flag
+    assert rl(16, 4 * MB, 1, 3, 64 + 32, 16, None) == 1    # 64-byte steps with another flag
+    assert rl(16, 4 * MB, 1, 3, 64 + 1, 16, None) == 1     # 64-byte steps of register loads
     assert rl(16, 4 * MB, 1, 3, 33, 16, None) == 1         # two-slot ring of register loads
     assert rl(16, 4 * MB, 1, 4, 0, 16, None) == 1          # steps not a multiple of 3
     assert rl(16, 4 * MB + 16, 1, 3, 0, 16, None) == 1     # size not a multiple of 4096
@@ -81,7 +83,7 @@ def test_probe_library_exports_its_header():
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 14
+    assert lib.moe_abi_version() == 15
 
 
 def capacity_formula(M, k, E, B):
@@ -305,7 +307,8 @@ def test_fused_tuning_validation(lib):
     for t in (m.Tuning(gemm1_ksplit=3), m.Tuning(token_tiles=5), m.Tuning(unroll=3), m.Tuning(gemm2_ksplit=17),
               m.Tuning(gemm2_wave_ksplit=3), m.Tuning(reverse_order=2), m.Tuning(single_launch=2),
               m.Tuning(single_launch=-2), m.Tuning(down_per_token=2), m.Tuning(down_per_token=-2),
-              m.Tuning(routing_in_gate_up=2), m.Tuning(routing_in_gate_up=-2)):
+              m.Tuning(routing_in_gate_up=2), m.Tuning(routing_in_gate_up=-2), m.Tuning(gemm1_feature_tiles=3),
+              m.Tuning(gemm1_feature_tiles=-1), m.Tuning(gemm2_row_tiles=3), m.Tuning(gemm2_row_tiles=-1)):
         args = fused_args(tuning=ctypes.pointer(t))
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2
 

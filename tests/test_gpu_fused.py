@@ -24,8 +24,8 @@ import torch
 import moe_layer_align_amd as moe
 import oracle
 from gpu_common import DEV, TOL, compare, run_gpu, say
-from synth import (CONFIGS, MoEConfig, gen_logits, gen_router_weights, gen_weights, gen_weights_per_channel,
-                   gen_weights_per_expert, gen_x)
+from synth import (CONFIGS, MoEConfig, gen_logits, gen_router_weights, gen_weights, gen_weights_block,
+                   gen_weights_per_channel, gen_weights_per_expert, gen_x)
 
 pytestmark = pytest.mark.gpu
 
@@ -737,3 +737,64 @@ def test_two_launches_are_the_default_for_tiny_layers():
     c = moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", t13, t2, tuning=THREE)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+# ---- two groups per wave in the K-split products (gemm1_feature_tiles = 2:
+# 16-feature groups of the gate/up product; gemm2_row_tiles = 2: 32-row
+# groups of the down product): every output's k-steps and K-split sum keep
+# their order, so the layer's output is that of one group per wave, bit for
+# bit
+@pytest.mark.parametrize("dtype,scales", [("bf16", "-"), ("fp8", "dynamic"), ("fp8", "static"),
+                                          ("fp8", "per-row"), ("fp8", "per-expert"), ("fp8", "block")])
+def test_two_groups_per_wave_match_one(dtype, scales):
+    # the down product's K slices are pinned (their default count follows the
+    # number of workgroups, which two row groups halve); variants whose LDS
+    # does not fit a workgroup are refused by the plan and skipped here
+    cfg = cfg_of(dtype, 16, 4, 512, 512)
+    fp8 = dtype == "fp8"
+    seed = 120
+    if scales == "per-row":
+        w13, w2, s13, s2 = gen_weights_per_channel(cfg, seed, device=DEV)
+    elif scales == "per-expert":
+        w13, w2, s13, s2 = gen_weights_per_expert(cfg, seed, device=DEV)
+    elif scales == "block":
+        w13, w2, s13, s2 = gen_weights_block(cfg, seed, device=DEV)
+    else:
+        w13, w2, s13, s2 = gen_weights(cfg, seed, device=DEV)
+    sc = lambda v: v if isinstance(v, torch.Tensor) else torch.tensor([v], device=DEV)
+    kw = dict(x_scale=sc(0.02), h_scale=sc(0.004)) if scales == "static" else {}
+    ran, refused = 0, 0
+    for M in (20, 45):
+        x = gen_x(cfg.H, M, seed, sub=M).to(DEV)
+        lg = gen_logits(cfg, M, seed, sub=M).to(DEV)
+        for ks in (1, 2, 4):
+            for tt, u in ((1, 0), (2, 0), (4, 0), (2, 1 if fp8 else 2)):
+                def run(ft, fr):
+                    t = moe.Tuning(gemm1_ksplit=ks, gemm2_ksplit=1, gemm2_wave_ksplit=ks, token_tiles=tt, unroll=u,
+                                   gemm1_stream_tiles=-1, gemm2_stream_tiles=-1, gemm1_feature_tiles=ft,
+                                   gemm2_row_tiles=fr)
+                    return moe.fused_forward(x, lg, w13, w2, cfg.k, dtype, sc(s13) if fp8 else None,
+                                             sc(s2) if fp8 else None, tuning=t, **kw)
+                say("%s %s M=%d ksplit=%d token_tiles=%d unroll=%d" % (dtype, scales, M, ks, tt, u))
+                y0 = run(1, 1)
+                for ft, fr in ((2, 1), (1, 2), (2, 2)):
+                    try:
+                        y = run(ft, fr)
+                    except moe.MoEError as ex:
+                        assert fr == 2 and "UNSUPPORTED" in str(ex), ex  # only the down product's LDS can refuse
+                        refused += 1
+                        continue
+                    torch.cuda.synchronize()
+                    assert torch.equal(y0, y), (M, ks, tt, u, ft, fr)
+                    ran += 1
+    say("  %d variants equal, %d refused" % (ran, refused))
+    assert refused <= ran // 4
+
+
+def test_two_groups_per_wave_parity():
+    # both products with two groups per wave against the oracle, on a
+    # Mixtral-like expert count (more than 16 tokens per expert, two token
+    # tiles) and an fp8 layer
+    t = moe.Tuning(gemm1_feature_tiles=2, gemm2_row_tiles=2, gemm1_stream_tiles=-1, gemm2_stream_tiles=-1)
+    compare(cfg_of("bf16", 8, 2, 512, 384), 63, seed=121, tuning=t)
+    compare(cfg_of("fp8", 16, 4, 512, 384), 60, seed=122, tuning=t)
