@@ -62,14 +62,14 @@ SINGLE_SOURCES = ("moe_layer_align_amd/csrc/layer_small.h", "moe_layer_align_amd
                   "moe_layer_align_amd/csrc/route_align.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "52554b0f49ac9036ea1c2b2eddcb63748126b7881a16ec2a859d0d2385a7f329",
-                "bytes_per_launch": 1511427704},
-    "qwen3": {"src_sha256": "52554b0f49ac9036ea1c2b2eddcb63748126b7881a16ec2a859d0d2385a7f329",
-              "bytes_per_launch": 241792566},
-    "deepseek": {"src_sha256": "52554b0f49ac9036ea1c2b2eddcb63748126b7881a16ec2a859d0d2385a7f329",
-                 "bytes_per_launch": 3292693558},
-    "prefill": {"src_sha256": "ac86f14bf7fa4ac2520e876b28bb05a559a55dcbb407601bf5acb963b45b35cc",
-                "bytes_per_launch": 3051415558},
+    "mixtral": {"src_sha256": "c0512c668dfe9362cee891cb2f22412523498de81ec36ab236a3bbe433d4a740",
+                "bytes_per_launch": 1511749176},
+    "qwen3": {"src_sha256": "c0512c668dfe9362cee891cb2f22412523498de81ec36ab236a3bbe433d4a740",
+              "bytes_per_launch": 241803419},
+    "deepseek": {"src_sha256": "c0512c668dfe9362cee891cb2f22412523498de81ec36ab236a3bbe433d4a740",
+                 "bytes_per_launch": 3292674407},
+    "prefill": {"src_sha256": "2773913f52c614fce1038894c6cc6238753670ceaee3fb4ea90f382fa708f5cb",
+                "bytes_per_launch": 3030166812},
 }
 
 
