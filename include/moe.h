@@ -182,12 +182,13 @@ typedef struct {
                                 set */
   int32_t routing_in_gate_up; /* tiny layers taking the per-token down product (at most 16 tokens and 64
                                 pairs, at most 256 routed experts, H a multiple of 512 in fp8 or of 128 in
-                                bf16, fp8 x of at most 8192 elements, not the single-launch layer): 1 = the
+                                bf16, fp8 x of at most 16384 elements, not the single-launch layer): 1 = the
                                 layer in two launches, every gate/up workgroup routing, quantising and
                                 sorting the few tokens itself before its items (MOE_ERR_UNSUPPORTED where
                                 the layer would take another path); -1 = the routing launch of its own;
                                 0 = default: two launches where it fits and the gate/up product has at
-                                most 1024 items of 16 features (min(E+S, M*(top_k+S)) * I/16), unless a
+                                most 1024 items of 16 features (min(E+S, M*(top_k+S)) * I/16), or at most
+                                4096 items of at most 64 KB (32 weight rows of H), unless a
                                 gate/up field (gemm1_ksplit, token_tiles, unroll, gemm1_stream_tiles,
                                 gemm1_feature_tiles) is set.  The
                                 outputs are those of the routing launch of its own, bit for bit, wherever

@@ -43,12 +43,17 @@ const void* pick_wks(int wks) {
 }  // namespace
 
 bool launch_tiny_gate_up(bool fp8, int hf, int grid, hipStream_t st, const Layer1Args& a) {
+  const bool x4 = (int64_t)a.M * a.H > 2 * 256 * 16;  // fp8 x in four register chunks per thread, else two
   if (!fp8 && hf == H_BF16)
-    tiny_gate_up_kernel<false, H_BF16><<<grid, 256, 0, st>>>(a);
+    tiny_gate_up_kernel<false, H_BF16, 2><<<grid, 256, 0, st>>>(a);
+  else if (fp8 && hf == H_F32 && !x4)
+    tiny_gate_up_kernel<true, H_F32, 2><<<grid, 256, 0, st>>>(a);
   else if (fp8 && hf == H_F32)
-    tiny_gate_up_kernel<true, H_F32><<<grid, 256, 0, st>>>(a);
+    tiny_gate_up_kernel<true, H_F32, 4><<<grid, 256, 0, st>>>(a);
+  else if (fp8 && hf == H_E4M3 && !x4)
+    tiny_gate_up_kernel<true, H_E4M3, 2><<<grid, 256, 0, st>>>(a);
   else if (fp8 && hf == H_E4M3)
-    tiny_gate_up_kernel<true, H_E4M3><<<grid, 256, 0, st>>>(a);
+    tiny_gate_up_kernel<true, H_E4M3, 4><<<grid, 256, 0, st>>>(a);
   else
     return false;
   return true;

@@ -100,7 +100,7 @@ constexpr int kLayer1NPL = 16;
 constexpr int kLayer1Sorted = kLayer1Pairs * 16;  // align capacity bound: P + min(E,P)*15 <= 64*16
 constexpr int kLayer1LdsMax = 65536;   // LDS of one workgroup (static + the dynamic token slice)
 constexpr int kLayer1MaxGrid = 1024;   // slots of the per-workgroup |h| maxima
-constexpr int kTinyXElems = 8192;      // fp8 x of the two-launch layer: every gate/up workgroup's LDS copy
+constexpr int kTinyXElems = 16384;     // fp8 x of the two-launch layer: every gate/up workgroup's LDS copy
 
 struct Layer1Args {
   const float* logits;   // [M][E] routed experts' logits
@@ -165,13 +165,13 @@ struct Layer1Lds {
 // a.xq, which every workgroup writes with the same bytes, or the workgroup's
 // own LDS copy), and the one-wave sort-and-pad into LDS.  The lead workgroup
 // also writes the routing, the sort-and-pad outputs that were asked for, and
-// s_x.  An fp8 x of at most 8192 elements (two 16-element chunks per
+// s_x.  An fp8 x of at most XC*4096 elements (XC 16-element chunks per
 // thread) is loaded into registers before the routing, so that its loads are
 // in flight with the logits' and x is read once.  Ends with the workgroup
 // synchronised.
-constexpr int kX2Reg = 2 * 256 * 16;
-template <bool FP8>
+template <bool FP8, int XC = 2>
 __device__ __forceinline__ void layer1_prologue(const Layer1Args& a, Layer1Lds& s, bool lead, uint8_t* xq) {
+  constexpr int kXChunks = XC, kX2Reg = XC * 256 * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15;
   const int M = a.M, E = a.E, K = a.K, S = a.S, H = a.H;
   const int KS = K + S, ES = E + S, P = M * KS;
@@ -180,12 +180,12 @@ __device__ __forceinline__ void layer1_prologue(const Layer1Args& a, Layer1Lds& 
   // chunk c: elements 16*(tid + 256c) .. +16, loaded from the last chunk
   // where that is past x (no branch around the loads, so no wait for them
   // here; a repeated chunk leaves the largest |x| unchanged)
-  u32x4 xr[4];
+  u32x4 xr[2 * kXChunks];
   // a static s_x is read here too, beside the other loads
   const float sx_given = (xreg && a.x_scale) ? *a.x_scale : 0.0f;
   if (xreg) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < kXChunks; ++c) {
       const int64_t i = min((int64_t)(tid + 256 * c) * 16, nx - 16);
       xr[2 * c] = *(const u32x4*)(a.x + i);
       xr[2 * c + 1] = *(const u32x4*)(a.x + i + 8);
@@ -215,7 +215,7 @@ __device__ __forceinline__ void layer1_prologue(const Layer1Args& a, Layer1Lds& 
       } else {  // largest |x| as layer1_amax_bf16 takes it, from the registers
         unsigned m = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 2 * kXChunks; ++c)
 #pragma unroll
           for (int q = 0; q < 4; ++q) m = max(m, max(xr[c][q] & 0x7fffu, (xr[c][q] >> 16) & 0x7fffu));
         float am = wave_max(__uint_as_float(m << 16));
@@ -226,7 +226,7 @@ __device__ __forceinline__ void layer1_prologue(const Layer1Args& a, Layer1Lds& 
       }
       const float r = 1.0f / sx;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < kXChunks; ++c) {
         const int64_t i = (int64_t)(tid + 256 * c) * 16;
         if (i < nx) *(u32x4*)(xq + i) = quant16_e4m3(xr[2 * c], xr[2 * c + 1], r);
       }
@@ -371,14 +371,14 @@ static __global__ __launch_bounds__(256) void layer1_kernel(Layer1Args a) {
 //      combine per token, reducing those maxima for s_h.
 // The kernel boundary orders the two launches, so no grid barrier is needed;
 // the arithmetic is the multi-launch path's, bit for bit.
-template <bool FP8, int HFMT>
+template <bool FP8, int HFMT, int XC>
 static __global__ __launch_bounds__(256) void tiny_gate_up_kernel(Layer1Args a) {
   constexpr int U1 = FP8 ? 2 : 4;
   __shared__ Layer1Lds s;
   __shared__ f32x4 s_red[3 * 2 * 64];  // three waves' partial tiles (K split over four waves, one token tile)
   __shared__ __align__(16) uint8_t s_xq[FP8 ? kTinyXElems : 16];  // this workgroup's e4m3 copy of x
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  layer1_prologue<FP8>(a, s, blockIdx.x == 0, s_xq);
+  layer1_prologue<FP8, XC>(a, s, blockIdx.x == 0, s_xq);
   const Segments seg{s.sorted, s.offsets, s.counts, s.active, &s.num_active, 0};
   const int KS = a.K + a.S, t1 = a.I / 16, nact = s.num_active;
   auto run = [&](auto pc_tag) {

@@ -453,6 +453,11 @@ moe_status_t check_shape(int M, int E, int k) {
 // (1792: 3.5 items per workgroup, the pipeline drained between them).
 constexpr int kTinyGrid = 512;
 constexpr int64_t kTinyDefaultItems = 1024;
+// Items of at most 64 KB (32 weight rows of H) cost little to switch between:
+// the default takes the two launches up to 4096 of them (Qwen3-shaped layer,
+// 1536 items at M = 4: 42.0 vs 46.0 us).
+constexpr int64_t kTinySmallItemsMax = 4096;
+constexpr int64_t kTinySmallItemBytes = 65536;
 
 // ---------------------------------------------------------------- single-launch layer
 // The single-launch layer's wave split of the down product (4, 2 or 1: the
@@ -762,7 +767,9 @@ static moe_status_t fused_forward(const moe_fused_args_t* a, hipStream_t st, voi
     // (gate/up K split over four waves in whole MFMA k-steps, as in the single-launch layer)
     const bool fits = plan.tok && M <= kLayer1Tokens && (int64_t)M * k <= kLayer1Pairs && Er <= kLayer1Experts &&
                       (H / 4) % (fp8 ? 128 : 32) == 0 && (!fp8 || (int64_t)M * H <= kTinyXElems);
-    const bool pays = (int64_t)std::min<int64_t>(Er + S, (int64_t)M * k) * (I / 16) <= kTinyDefaultItems;
+    const int64_t items = (int64_t)std::min<int64_t>(Er + S, (int64_t)M * k) * (I / 16);
+    const bool pays = items <= kTinyDefaultItems ||
+                      (items <= kTinySmallItemsMax && 32 * (int64_t)H * (fp8 ? 1 : 2) <= kTinySmallItemBytes);
     tiny = fits && (rmode == 1 || (rmode == 0 && !g1_pinned && pays));
   }
   if (rmode == 1 && !tiny) return MOE_ERR_UNSUPPORTED;  // required where the layer takes another path

@@ -241,9 +241,12 @@ def test_fused_validation(lib, kw, code):
 @pytest.mark.parametrize("name,M,path", [
     ("mixtral", 1, "decode_token_down"),  # 2 x 896 gate/up items: above the two-launch default's 1024
     ("mixtral", 4, "decode"), ("mixtral", 63, "decode"),
-    ("qwen3", 1, "two_launches"), ("qwen3", 8, "decode_token_down"),  # 8 x 2048 fp8 x: above 8192 elements
-    ("qwen3", 64, "decode"),
-    ("deepseek", 1, "two_launches"), ("deepseek", 16, "decode"),
+    ("qwen3", 1, "two_launches"),
+    ("qwen3", 8, "two_launches"),  # 3072 gate/up items, but of 64 KB each; x of 16384 elements
+    ("qwen3", 16, "decode"), ("qwen3", 64, "decode"),
+    ("deepseek", 1, "two_launches"),
+    ("deepseek", 2, "decode_token_down"),  # 2048 items of 229 KB: above the two-launch default's 1024
+    ("deepseek", 16, "decode"),
     ("prefill", 4096, "prefill"), ("prefill", 0, "none"),
 ])
 def test_fused_path_of_the_workloads(name, M, path):
@@ -362,12 +365,12 @@ def test_fused_down_per_token_required_where_it_does_not_fit(lib):
 
 def test_fused_routing_in_gate_up_required_where_it_does_not_fit(lib):
     # more than 16 tokens or 64 pairs, the per-expert down product, E above
-    # 256, fp8 x above 8192 elements, a gate/up K that four waves cannot split
+    # 256, fp8 x above 16384 elements, a gate/up K that four waves cannot split
     # into whole MFMA k-steps
     import moe_layer_align_amd as m
     fp8 = dict(dtype=1, w13_scale=FAKE, w2_scale=FAKE)
     for kw in (dict(M=17, top_k=2), dict(M=9, top_k=8), dict(E=300, top_k=2),
-               dict(M=2, H=8192, **fp8), dict(M=2, H=256, **fp8), dict(M=2, H=384, **fp8)):
+               dict(M=2, H=16384, **fp8), dict(M=2, H=256, **fp8), dict(M=2, H=384, **fp8)):
         t = m.Tuning(routing_in_gate_up=1)
         args = fused_args(tuning=ctypes.pointer(t), **kw)
         assert lib.moe_fused_forward(ctypes.byref(args), None) == 2, kw

@@ -710,9 +710,31 @@ def test_two_launches_match_three(dtype, xs, hs, M):
             tuning=TWO)
 
 
+@pytest.mark.parametrize("xs,hs", [(None, None), (0.02, 0.004)])
+@pytest.mark.parametrize("M", [5, 7])
+def test_two_launches_match_three_wide_x(xs, hs, M):
+    # an fp8 x of 10240 and 14336 elements (four register chunks per thread in
+    # the gate/up workgroups), below 8 tokens: the same bits as three launches
+    cfg = cfg_of("fp8", 16, 4, 2048, 256)
+    w13, w2, s13, s2 = gen_weights(cfg, 110 + M, device=DEV)
+    x = gen_x(cfg.H, M, 110 + M, sub=M).to(DEV)
+    lg = gen_logits(cfg, M, 110 + M, sub=M).to(DEV)
+    sc = lambda v: torch.tensor([v], device=DEV)
+    kw = dict(x_scale=sc(xs) if xs else None, h_scale=sc(hs) if hs else None)
+    so = [torch.empty(2, device=DEV) for _ in range(2)]
+    ys = [moe.fused_forward(x, lg, w13, w2, cfg.k, "fp8", sc(s13), sc(s2), tuning=t, scales_out=so[i], **kw)
+          for i, t in enumerate((TWO, THREE))]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]), "two launches and three differ"
+    assert torch.equal(so[0], so[1])
+    compare(cfg, M, seed=110 + M, weights=(w13, w2, s13, s2), x=x.cpu(), logits=lg.cpu(), x_scale=xs, h_scale=hs,
+            tuning=TWO)
+
+
 def test_two_launches_workload_shapes(qwen3_w, deepseek_w):
     compare(CONFIGS["qwen3"], 1, seed=0, weights=qwen3_w, tuning=TWO)
     compare(CONFIGS["qwen3"], 4, seed=0, weights=qwen3_w, tuning=TWO)
+    compare(CONFIGS["qwen3"], 8, seed=0, weights=qwen3_w, tuning=TWO)  # x in four register chunks per thread
     compare(CONFIGS["deepseek"], 1, seed=0, weights=deepseek_w, tuning=TWO)
     compare(CONFIGS["tiny"], 4, seed=0, tuning=TWO)
 
