@@ -62,14 +62,14 @@ SINGLE_SOURCES = ("moe_layer_align_amd/csrc/layer_small.h", "moe_layer_align_amd
                   "moe_layer_align_amd/csrc/route_align.h", "moe_layer_align_amd/csrc/moe_device.h")
 PREFILL_SOURCES = ("moe_layer_align_amd/csrc/gemm_prefill.h", "moe_layer_align_amd/csrc/moe_device.h")
 TRAFFIC = {
-    "mixtral": {"src_sha256": "c0512c668dfe9362cee891cb2f22412523498de81ec36ab236a3bbe433d4a740",
-                "bytes_per_launch": 1511749176},
-    "qwen3": {"src_sha256": "c0512c668dfe9362cee891cb2f22412523498de81ec36ab236a3bbe433d4a740",
-              "bytes_per_launch": 241803419},
-    "deepseek": {"src_sha256": "c0512c668dfe9362cee891cb2f22412523498de81ec36ab236a3bbe433d4a740",
-                 "bytes_per_launch": 3292674407},
+    "mixtral": {"src_sha256": "6f5c6fbb7854f74b5824eaab3d58e3a4d7a0fd3d985fff56850075a58ead077a",
+                "bytes_per_launch": 1511736166},
+    "qwen3": {"src_sha256": "6f5c6fbb7854f74b5824eaab3d58e3a4d7a0fd3d985fff56850075a58ead077a",
+              "bytes_per_launch": 240921788},
+    "deepseek": {"src_sha256": "6f5c6fbb7854f74b5824eaab3d58e3a4d7a0fd3d985fff56850075a58ead077a",
+                 "bytes_per_launch": 3292697022},
     "prefill": {"src_sha256": "2773913f52c614fce1038894c6cc6238753670ceaee3fb4ea90f382fa708f5cb",
-                "bytes_per_launch": 3030166812},
+                "bytes_per_launch": 3031852382},
 }
 
 
