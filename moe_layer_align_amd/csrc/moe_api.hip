@@ -273,11 +273,6 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
   p->passes1 = (int)cdiv(M, p->nt1 * 16);
   p->passes2 = (int)cdiv(M, p->nt2 * 16);
 
-  // down: K slices in separate workgroups; each slice's K range must split
-  // evenly over wks2 waves, and with a dynamic fp8 h scale the quantised
-  // token slice must fit the workgroup's LDS.  Default: the fewest slices
-  // that give at least 1024 workgroups (4 per CU), or 256 (one per CU) for
-  // the long-stream variant.
   // K-split down: 32-row groups per wave (each output's sums are the same
   // for the same K slices); the workgroup's rows must divide H.  Default:
   // two for bf16 layers with at least 12 pairs per expert that can hold
@@ -292,6 +287,11 @@ moe_status_t make_plan(int M, int E, int H, int I, int k, int S, bool fp8, bool 
     if (t->gemm2_row_tiles == 2 && !fr2_ok) return MOE_ERR_UNSUPPORTED;
     p->fr2 = t->gemm2_row_tiles;
   }
+  // down: K slices in separate workgroups; each slice's K range must split
+  // evenly over wks2 waves, and with a dynamic fp8 h scale the quantised
+  // token slice must fit the workgroup's LDS.  Default: the fewest slices
+  // that give at least 1024 workgroups (4 per CU), or 256 (one per CU) for
+  // the long-stream variant.
   const int nsteps2 = I / kstep;
   auto fits = [&](int ks) {
     if (nsteps2 % (ks * p->wks2) != 0) return false;
