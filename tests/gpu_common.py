@@ -54,19 +54,23 @@ def row_errs(y_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
     return num / den
 
 
-# Per-token bound of the block-scaled fp8 mode.  The fp8 matrix instructions
-# of gfx950 do not sum their products at fp32 precision: against exact sums
-# of random e4m3 operands spread over the format's range, their results are
-# off by up to about 2^-13 of the sum of |products| (both the 16x16x128 and
-# the 16x16x32 forms; narrow-range operands and the fp32 accumulator add are
+# Per-token bound of the fp8 modes.  The fp8 matrix instructions of gfx950
+# do not sum their products at fp32 precision: against exact sums of random
+# e4m3 operands spread over the format's range, their results are off by up
+# to about 2^-13 of the sum of |products| (both the 16x16x128 and the
+# 16x16x32 forms; narrow-range operands and the fp32 accumulator add are
 # exact).  So the kernel's fp32 h differs from the definition's by ~1e-4 of
 # its row and some of h's e4m3 rounding decisions come out on the other side
-# of a midpoint.  Block scaling puts every 128-element group's largest
-# values in the format's top binade, where a step is 1/8 to 1/16 of the value,
-# and the per-token maximum of those moves grows with the token count: about
-# 1.3e-2 at 600 tokens, 2.4e-2 at 1100 and 3.0e-2 at 4096.  The whole-output
-# bound TOL holds for every token in every mode.
-TOL_TOKEN_BLOCK = 5e-2
+# of a midpoint.  A step in the format's top binades is 1/8 to 1/16 of the
+# value, so one such decision on a large h element moves its token's outputs
+# by a few percent of their largest value, more often the more tokens and
+# the smaller I.  Block scaling puts every 128-element group's largest values
+# in the top binade: its per-token maximum is about 1.3e-2 at 600 tokens,
+# 2.4e-2 at 1100 and 3.0e-2 at 4096.  With one h scale per layer, a layer of
+# 2780 tokens, top-3 of 31 experts, H = 896, I = 384 reaches 3.1e-2 on one
+# token (whole output 1.1e-2), every one of its worst tokens' differences
+# made of such flips.  The whole-output bound TOL holds in every mode.
+TOL_TOKEN_FP8 = 5e-2
 
 
 def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuning=None, n_shared=0,
@@ -186,8 +190,7 @@ def compare(cfg: MoEConfig, M: int, seed: int = 0, weights=None, tokens=None, x_
     rows = list(range(M)) if tokens is None else list(tokens)
     e = err_norm(gpu["y"][rows], ref["y"])
     er = float(row_errs(gpu["y"][rows], ref["y"]).max()) if rows else 0.0
-    block_scaled = isinstance(weights[2], torch.Tensor) and weights[2].dtype == torch.uint8
-    tol_tok = TOL_TOKEN_BLOCK if block_scaled else TOL[cfg.dtype]
+    tol_tok = TOL_TOKEN_FP8 if cfg.dtype == "fp8" else TOL[cfg.dtype]
     say("  err=%.3e per-token %.3e (tol %.0e, per token %.0e) on %s tokens, oracle %.1fs"
         % (e, er, TOL[cfg.dtype], tol_tok, "all" if tokens is None else len(rows), ref["seconds"]))
     assert np.isfinite(gpu["y"]).all()

@@ -1,0 +1,96 @@
+"""Seeded random layer shapes against the oracle.
+
+The other GPU tests pin the shapes of the five workloads and the edges of
+each path one at a time; these cases draw every knob at once from a fixed
+seed: the expert count and top-k (with and without shared experts), H and I
+(any multiple of 128), the token count (from one token to past the 8192
+pairs where fp8 layers take the tiled prefill products), the logits'
+distribution, the weight-scale mode (per tensor, per row, per expert,
+128 x 128 blocks), static or dynamic activation scales, and the
+deterministic mode.  So the default path choice (single workgroup routing
+or the router launches, two or three launches, per-token or per-expert down
+product, decode or prefill products, the K-split and stream variants the
+plan picks) meets shapes no other test names.  Each case is a full
+`compare`: bit-exact routing and sort-and-pad, outputs within the tolerance.
+The oracle's work per case is capped so that the whole file runs in minutes.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_common import DEV, compare
+from synth import MoEConfig, gen_weights, gen_weights_block, gen_weights_per_channel, gen_weights_per_expert
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 40
+MAX_MACS = 2.5e10  # multiply-adds of the oracle's expert products per case
+MAX_MACS_BLOCK = 6e9  # the same for 128 x 128 block scales, which the oracle applies block by block
+PREFILL_PAIRS = 8192  # fp8 layers with at least this many pairs take the tiled products
+
+
+def _draw(rng: np.random.Generator, i: int) -> dict:
+    dtype = "fp8" if rng.random() < 0.6 else "bf16"
+    E = int(rng.choice([1, 2, 3, 5, 8, 16, 31, 64, 100, 128, 200, 256, 300]))
+    S = int(rng.choice([0, 0, 0, 1, 2]))
+    k = int(rng.integers(1, min(E, 16 - S) + 1))
+    H = 128 * int(rng.integers(1, 17))
+    I = 128 * int(rng.integers(1, 13))
+    logits = str(rng.choice(["normal", "biased", "zipf"]))
+    if logits == "zipf" and E < k + 8:
+        logits = "normal"  # zipf gives four experts the same logit; keep them out of every top-k
+    mode, xs, hs, det = 0, None, None, False
+    if dtype == "fp8":
+        mode = int(rng.choice([0, 0, 1, 2, 3]))
+        if mode != 3 and rng.random() < 0.4:
+            xs, hs = 0.02, float(rng.choice([0.004, 0.02, 0.06]))
+    if mode != 3 and rng.random() < 0.15:
+        det = True
+        if dtype == "fp8":
+            xs, hs = 0.02, 0.02
+    KS = k + S
+    if dtype == "fp8" and not det and rng.random() < 0.3:
+        M = -(-PREFILL_PAIRS // KS) + int(rng.integers(0, 300))
+    else:
+        M = int(round(math.exp(rng.uniform(0.0, math.log(1200.0)))))
+    # keep the oracle's products under the cap: shrink I, then H
+    cap = MAX_MACS_BLOCK if mode == 3 else MAX_MACS
+    while M * KS * 3 * H * I > cap and I > 128:
+        I -= 128
+    while M * KS * 3 * H * I > cap and H > 128:
+        H -= 128
+    return dict(i=i, dtype=dtype, E=E, S=S, k=k, H=H, I=I, M=M, logits=logits, mode=mode, xs=xs, hs=hs, det=det)
+
+
+_RNG = np.random.default_rng(20261203)
+CASES = [_draw(_RNG, i) for i in range(N_CASES)]
+
+
+def _id(c: dict) -> str:
+    sc = "" if c["dtype"] == "bf16" else "-m%d-%s" % (c["mode"], "dyn" if c["xs"] is None else "hs%g" % c["hs"])
+    return "%d-%s-E%dk%dS%d-H%dI%d-M%d-%s%s%s" % (c["i"], c["dtype"], c["E"], c["k"], c["S"], c["H"], c["I"],
+                                                 c["M"], c["logits"], sc, "-det" if c["det"] else "")
+
+
+def test_cases_cover_the_paths():
+    # the draw reaches every path it is meant to exercise
+    fp8 = [c for c in CASES if c["dtype"] == "fp8"]
+    assert any(c["M"] * (c["k"] + c["S"]) >= PREFILL_PAIRS and not c["det"] and c["mode"] != 3 for c in fp8)
+    assert any(c["M"] * (c["k"] + c["S"]) <= 64 for c in CASES)
+    assert any(c["S"] > 0 for c in CASES) and any(c["det"] for c in CASES)
+    assert {c["mode"] for c in fp8} == {0, 1, 2, 3}
+    assert any(c["xs"] is not None for c in fp8) and any(c["xs"] is None for c in fp8)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("c", CASES, ids=_id)
+def test_random_shape(c):
+    cfg = MoEConfig("rand%d" % c["i"], E=c["E"], k=c["k"], H=c["H"], I=c["I"], dtype=c["dtype"], ms=(c["M"],),
+                    logits=c["logits"])
+    seed = 7000 + c["i"]
+    ES = c["E"] + c["S"]
+    gen = {0: gen_weights, 1: gen_weights_per_channel, 2: gen_weights_per_expert, 3: gen_weights_block}[c["mode"]]
+    w = gen(cfg, seed, device=DEV, E=ES)
+    compare(cfg, c["M"], seed=seed, weights=w, x_scale=c["xs"], h_scale=c["hs"], n_shared=c["S"],
+            deterministic=c["det"])
