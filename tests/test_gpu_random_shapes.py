@@ -4,7 +4,8 @@ The other GPU tests pin the shapes of the five workloads and the edges of
 each path one at a time; these cases draw every knob at once from a fixed
 seed: the expert count and top-k (with and without shared experts), H and I
 (any multiple of 128), the token count (from one token to past the 8192
-pairs where fp8 layers take the tiled prefill products), the logits'
+pairs where fp8 layers take the tiled prefill products; a second set holds
+decode-sized layers of 1 to 64 tokens with H up to 8192 and I up to 4096), the logits'
 distribution, the weight-scale mode (per tensor, per row, per expert,
 128 x 128 blocks), static or dynamic activation scales, and the
 deterministic mode.  So the default path choice (single workgroup routing
@@ -67,6 +68,34 @@ _RNG = np.random.default_rng(20261203)
 CASES = [_draw(_RNG, i) for i in range(N_CASES)]
 
 
+def _draw_decode(rng: np.random.Generator, i: int) -> dict:
+    # decode-sized layers with wide matrices: M 1..64, H up to 8192, I up to 4096
+    dtype = "fp8" if rng.random() < 0.6 else "bf16"
+    E = int(rng.choice([1, 2, 4, 8, 16, 64, 128, 256]))
+    S = int(rng.choice([0, 0, 0, 1]))
+    k = int(rng.integers(1, min(E, 16 - S) + 1))
+    H = 128 * int(rng.integers(1, 65))
+    I = 128 * int(rng.integers(1, 33))
+    M = int(round(math.exp(rng.uniform(0.0, math.log(64.0)))))
+    logits = "biased" if rng.random() < 0.5 else "normal"
+    mode, xs, hs, det = 0, None, None, False
+    if dtype == "fp8":
+        mode = int(rng.choice([0, 0, 1, 2, 3]))
+        if mode != 3 and rng.random() < 0.4:
+            xs, hs = 0.02, float(rng.choice([0.004, 0.02, 0.06]))
+    if mode != 3 and rng.random() < 0.15:
+        det = True
+        if dtype == "fp8":
+            xs, hs = 0.02, 0.02
+    cap = MAX_MACS_BLOCK if mode == 3 else MAX_MACS
+    while M * (k + S) * 3 * H * I > cap and I > 128:
+        I -= 128
+    return dict(i=i, dtype=dtype, E=E, S=S, k=k, H=H, I=I, M=M, logits=logits, mode=mode, xs=xs, hs=hs, det=det)
+
+
+CASES += [_draw_decode(_RNG, N_CASES + i) for i in range(N_CASES)]
+
+
 def _id(c: dict) -> str:
     sc = "" if c["dtype"] == "bf16" else "-m%d-%s" % (c["mode"], "dyn" if c["xs"] is None else "hs%g" % c["hs"])
     return "%d-%s-E%dk%dS%d-H%dI%d-M%d-%s%s%s" % (c["i"], c["dtype"], c["E"], c["k"], c["S"], c["H"], c["I"],
@@ -81,6 +110,7 @@ def test_cases_cover_the_paths():
     assert any(c["S"] > 0 for c in CASES) and any(c["det"] for c in CASES)
     assert {c["mode"] for c in fp8} == {0, 1, 2, 3}
     assert any(c["xs"] is not None for c in fp8) and any(c["xs"] is None for c in fp8)
+    assert any(c["H"] > 4096 and c["M"] <= 64 for c in CASES) and any(c["I"] > 2048 and c["M"] <= 64 for c in CASES)
 
 
 @pytest.mark.timeout(300)
