@@ -19,6 +19,7 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 from gpu_common import DEV, compare
 from synth import MoEConfig, gen_weights, gen_weights_block, gen_weights_per_channel, gen_weights_per_expert
@@ -95,6 +96,17 @@ def _draw_decode(rng: np.random.Generator, i: int) -> dict:
 
 CASES += [_draw_decode(_RNG, N_CASES + i) for i in range(N_CASES)]
 
+# Logits from a few integer values, so that most top-k selections break ties
+# (toward the lower expert index): the ids must still match bit for bit on
+# every routing variant the fused call picks (one wave, one workgroup, the
+# multi-workgroup router).
+_TIE_RNG = np.random.default_rng(977)
+TIE_CASES = []
+for _i in range(16):
+    _c = (_draw if _i % 2 else _draw_decode)(_TIE_RNG, 2 * N_CASES + _i)
+    _c["logits"] = "ties%d" % int(_TIE_RNG.integers(2, 6))
+    TIE_CASES.append(_c)
+
 
 def _id(c: dict) -> str:
     sc = "" if c["dtype"] == "bf16" else "-m%d-%s" % (c["mode"], "dyn" if c["xs"] is None else "hs%g" % c["hs"])
@@ -114,13 +126,19 @@ def test_cases_cover_the_paths():
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("c", CASES, ids=_id)
+@pytest.mark.parametrize("c", CASES + TIE_CASES, ids=_id)
 def test_random_shape(c):
+    ties = c["logits"].startswith("ties")
     cfg = MoEConfig("rand%d" % c["i"], E=c["E"], k=c["k"], H=c["H"], I=c["I"], dtype=c["dtype"], ms=(c["M"],),
-                    logits=c["logits"])
+                    logits="normal" if ties else c["logits"])
     seed = 7000 + c["i"]
     ES = c["E"] + c["S"]
     gen = {0: gen_weights, 1: gen_weights_per_channel, 2: gen_weights_per_expert, 3: gen_weights_block}[c["mode"]]
     w = gen(cfg, seed, device=DEV, E=ES)
+    logits = None
+    if ties:
+        levels = int(c["logits"][4:])
+        g = np.random.default_rng(seed)
+        logits = torch.from_numpy(g.integers(0, levels, (c["M"], c["E"])).astype(np.float32) * 0.5)
     compare(cfg, c["M"], seed=seed, weights=w, x_scale=c["xs"], h_scale=c["hs"], n_shared=c["S"],
-            deterministic=c["det"])
+            deterministic=c["det"], logits=logits)
