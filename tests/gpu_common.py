@@ -74,10 +74,11 @@ TOL_TOKEN_FP8 = 5e-2
 
 
 def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuning=None, n_shared=0,
-            deterministic=False):
-    """One fused forward on the GPU; returns host copies of y and intermediates
-    (ids/weights [M,k+n_shared], counts [E+n_shared], the sort-and-pad
-    outputs).  Every output sits between canaries, checked after the call."""
+            deterministic=False, noalloc=False):
+    """One fused forward on the GPU (the no-alloc entry point with noalloc);
+    returns host copies of y and intermediates (ids/weights [M,k+n_shared],
+    counts [E+n_shared], the sort-and-pad outputs).  Every output sits
+    between canaries, checked after the call."""
     w13, w2, s13, s2 = weights
     M = x.shape[0]
     fp8 = cfg.dtype == "fp8"
@@ -103,7 +104,7 @@ def run_gpu(cfg: MoEConfig, x, logits, weights, x_scale=None, h_scale=None, tuni
                           scales_out=out["scales"].t if fp8 else None, tuning=tuning, n_shared=n_shared,
                           align_out={key: out[key].t for key in ("offsets", "sorted_ids", "block_expert",
                                                                   "num_padded")},
-                          deterministic=deterministic)
+                          deterministic=deterministic, noalloc=noalloc)
     torch.cuda.synchronize()
     assert y.data_ptr() == out["y"].t.data_ptr()
     for name, g in out.items():

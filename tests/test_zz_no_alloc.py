@@ -5,15 +5,17 @@ Its output equals the workspace entry point's (moe_fused_forward) bit for
 bit, and the oracle's within the stated tolerance, on two calls in a row, the
 second with a smaller input (the scratch array keeps the first call's
 contents); calls beyond the scratch array, or that pass a workspace, are
-refused before anything runs.
+refused before anything runs.  The seeded random layers of the parity
+tests that fit the array give the same bits through both entry points.
 """
 import numpy as np
 import pytest
 import torch
 
 import moe_layer_align_amd as moe
-from gpu_common import DEV, TOL, err_norm, run_oracle, say
-from synth import MoEConfig, gen_logits, gen_weights, gen_x
+from gpu_common import DEV, TOL, err_norm, run_gpu, run_oracle, say
+from synth import (MoEConfig, gen_logits, gen_weights, gen_weights_block, gen_weights_per_channel,
+                   gen_weights_per_expert, gen_x)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +78,44 @@ def test_noalloc_refuses_oversized_calls_and_workspaces():
                           w2_scale=t(s2).data_ptr(), y=y.data_ptr(), workspace=y.data_ptr(), workspace_bytes=1 << 20)
     import ctypes
     assert moe.load().moe_fused_forward_noalloc(ctypes.byref(args), None) == 1
+
+
+@pytest.mark.timeout(600)
+def test_noalloc_random_shapes_match_workspace_entry_point():
+    # every output of every random layer that fits the scratch array, bit for
+    # bit, the calls one after another on the one array (larger after smaller
+    # and the reverse)
+    import test_gpu_random_shapes as rs
+    fit = 0
+    for c in rs.CASES + rs.TIE_CASES:
+        ties = c["logits"].startswith("ties")
+        cfg = MoEConfig("na%d" % c["i"], E=c["E"], k=c["k"], H=c["H"], I=c["I"], dtype=c["dtype"], ms=(c["M"],),
+                        logits="normal" if ties else c["logits"])
+        M, seed = c["M"], 7000 + c["i"]
+        if c["M"] * (c["k"] + c["S"]) > 2048:
+            continue  # the larger layers need more than the array
+        gen = {0: gen_weights, 1: gen_weights_per_channel, 2: gen_weights_per_expert, 3: gen_weights_block}[c["mode"]]
+        w = gen(cfg, seed, device=DEV, E=c["E"] + c["S"])
+        x = gen_x(cfg.H, M, seed, sub=M)
+        lg = (torch.from_numpy(np.random.default_rng(seed).integers(0, int(c["logits"][4:]), (M, c["E"]))
+                               .astype(np.float32) * 0.5) if ties else gen_logits(cfg, M, seed, sub=M))
+        say("no-alloc random %s" % rs._id(c))
+        kw = dict(x_scale=c["xs"], h_scale=c["hs"], n_shared=c["S"], deterministic=c["det"])
+        ref = run_gpu(cfg, x, lg, w, **kw)
+        try:
+            got = run_gpu(cfg, x, lg, w, noalloc=True, **kw)
+        except moe.MoEError as e:
+            assert e.code == 2, e.code  # beyond the array: refused before anything runs
+            continue
+        fit += 1
+        for name in ("y_bits", "ids", "weights", "counts", "offsets", "sorted_ids", "block_expert", "num_padded",
+                     "scales"):
+            a, b = ref[name], got[name]
+            if name == "sorted_ids":
+                n = int(ref["num_padded"][0])
+                a, b = a[:n], b[:n]
+            assert (a is None and b is None) or np.array_equal(np.asarray(a).view(np.uint8),
+                                                               np.asarray(b).view(np.uint8)), (rs._id(c), name)
+        del w
+    say("no-alloc: %d random layers fit the array" % fit)
+    assert fit >= 40
