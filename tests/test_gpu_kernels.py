@@ -1,7 +1,7 @@
 """GPU parity of the single-step entry points against the CPU oracle:
 e4m3 quantisation (bit-exact codes), router logits (within fp32 summation
 error, bitwise the same for a token in any batch), router top-k (bit-exact
-ids), align (bit-exact counts, offsets, sorted ids, block map)."""
+ids), align (bit-exact counts, offsets, sorted ids, block map), on fixed and on seeded random shapes."""
 import numpy as np
 import pytest
 import torch
@@ -84,6 +84,30 @@ def test_route_ties_and_signed_zero():
         _route_case(lg, k)
 
 
+def _random_route_cases(n=30, seed=4242):
+    # seeded (M, E, k, levels): M across the one-wave, one-workgroup and
+    # multi-workgroup sizes, E up to 512, logits continuous (levels 0) or from
+    # a few values, so that ties decide most selections
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(g.choice([1, 2, 3, 7, 8, 16, 33, 64, 100, 128, 255, 256, 257, 384, 512]))
+        k = int(g.integers(1, min(E, 16) + 1))
+        M = int(round(np.exp(g.uniform(0, np.log(5000)))))
+        out.append((M, E, k, int(g.choice([0, 0, 2, 3, 7]))))
+    return out
+
+
+@pytest.mark.parametrize("M,E,k,levels", _random_route_cases())
+def test_route_random(M, E, k, levels):
+    g = np.random.default_rng(M * 1000003 + E * 17 + k)
+    if levels:
+        lg = (g.integers(0, levels, (M, E)) * 0.25 - 0.5).astype(np.float32)
+    else:
+        lg = g.standard_normal((M, E)).astype(np.float32)
+    _route_case(lg, k)
+
+
 # ------------------------------------------------------------------ align
 def _align_case(ids: np.ndarray, E: int, B: int):
     dev = moe.align(torch.from_numpy(ids).to(DEV), E, B)
@@ -105,6 +129,28 @@ def test_align_random(P, E, B):
     say("align P=%d E=%d B=%d" % (P, E, B))
     g = np.random.default_rng(P + E + B)
     ids = g.integers(0, E, P).astype(np.int32).reshape(-1, 1)
+    _align_case(ids, E, B)
+
+
+def _random_align_cases(n=30, seed=4343):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(g.choice([1, 2, 5, 8, 31, 64, 128, 200, 256, 300, 512]))
+        k = int(g.integers(1, min(E, 16) + 1))
+        M = int(round(np.exp(g.uniform(0, np.log(6000)))))
+        B = int(2 ** g.integers(0, 9))
+        out.append((M, E, k, B))
+    return out
+
+
+@pytest.mark.parametrize("M,E,k,B", _random_align_cases())
+def test_align_random_shapes(M, E, k, B):
+    # ids as routing gives them (distinct experts per token), some experts
+    # far more popular than others
+    g = np.random.default_rng(M * 7919 + E * 31 + k * 7 + B)
+    lg = (g.standard_normal((M, E)) + np.log(np.arange(1, E + 1))[g.permutation(E)] * -1.5).astype(np.float32)
+    ids, _ = oracle.route(lg, k)
     _align_case(ids, E, B)
 
 
