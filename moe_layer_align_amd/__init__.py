@@ -123,6 +123,18 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _keep_for(t: torch.Tensor, stream) -> None:
+    """For a tensor the binding allocates and drops while the call that uses
+    it runs on another stream than the current one: tell torch's caching
+    allocator, so that the memory is not handed out again before that
+    stream's work is done."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream(stream))
+    if s.cuda_stream != torch.cuda.current_stream(t.device).cuda_stream:
+        t.record_stream(s)
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -342,6 +354,7 @@ def fused_forward(x: torch.Tensor, logits: Optional[torch.Tensor], w13: torch.Te
         need = int(lib.moe_fused_workspace_size(M, ES, H, I, KS, DTYPE_FP8 if fp8 else DTYPE_BF16))
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+            _keep_for(workspace, stream)
         if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 GPU tensor")
     args = _FusedArgs(
