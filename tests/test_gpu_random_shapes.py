@@ -21,8 +21,12 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import DEV, compare
-from synth import MoEConfig, gen_weights, gen_weights_block, gen_weights_per_channel, gen_weights_per_expert
+import moe_layer_align_amd as moe
+
+import oracle
+from gpu_common import DEV, TOL, TOL_TOKEN_FP8, compare, err_norm, row_errs, run_oracle, say
+from synth import (MoEConfig, gen_router_weights, gen_weights, gen_weights_block, gen_weights_per_channel,
+                   gen_weights_per_expert, gen_x)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,3 +146,60 @@ def test_random_shape(c):
         logits = torch.from_numpy(g.integers(0, levels, (c["M"], c["E"])).astype(np.float32) * 0.5)
     compare(cfg, c["M"], seed=seed, weights=w, x_scale=c["xs"], h_scale=c["hs"], n_shared=c["S"],
             deterministic=c["det"], logits=logits)
+
+
+def _draw_router(rng: np.random.Generator, i: int) -> dict:
+    dtype = "fp8" if rng.random() < 0.6 else "bf16"
+    E = int(rng.choice([2, 8, 16, 64, 128, 256, 384, 512]))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    H = 128 * int(rng.integers(1, 33))
+    I = 128 * int(rng.integers(1, 13))
+    mode = int(rng.choice([0, 1, 2])) if dtype == "fp8" else 0
+    if dtype == "fp8" and rng.random() < 0.3:
+        M = -(-PREFILL_PAIRS // k) + int(rng.integers(0, 200))
+    else:
+        M = int(round(math.exp(rng.uniform(0.0, math.log(1200.0)))))
+    while M * k * 3 * H * I > MAX_MACS and I > 128:
+        I -= 128
+    while M * k * 3 * H * I > MAX_MACS and H > 128:
+        H -= 128
+    return dict(i=i, dtype=dtype, E=E, S=0, k=k, H=H, I=I, M=M, logits="router", mode=mode, xs=None, hs=None,
+                det=False)
+
+
+_ROUTER_RNG = np.random.default_rng(31337)
+ROUTER_CASES = [_draw_router(_ROUTER_RNG, 3 * N_CASES + i) for i in range(12)]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("c", ROUTER_CASES, ids=_id)
+def test_random_router_weights(c):
+    # the layer computes its logits from router weights: they agree with the
+    # oracle's within fp32 summation error, the routing on them is the
+    # oracle's bit for bit, and y is the oracle's layer on those logits
+    M, E, k, H = c["M"], c["E"], c["k"], c["H"]
+    cfg = MoEConfig("router%d" % c["i"], E=E, k=k, H=H, I=c["I"], dtype=c["dtype"], ms=(M,), logits="normal")
+    seed = 7000 + c["i"]
+    gen = {0: gen_weights, 1: gen_weights_per_channel, 2: gen_weights_per_expert}[c["mode"]]
+    w = gen(cfg, seed, device=DEV)
+    x = gen_x(H, M, seed, sub=M)
+    wg = gen_router_weights(E, H, seed)
+    fp8 = c["dtype"] == "fp8"
+    sc = (lambda v: v.to(DEV) if isinstance(v, torch.Tensor) else torch.tensor([v], device=DEV)) if fp8 else \
+        (lambda v: None)
+    lo = torch.empty(M, E, dtype=torch.float32, device=DEV)
+    ids = torch.empty(M, k, dtype=torch.int32, device=DEV)
+    say("router weights %s" % _id(c))
+    y = moe.fused_forward(x.to(DEV), None, w[0], w[1], k, c["dtype"], sc(w[2]), sc(w[3]), topk_ids=ids,
+                          router_w=wg.to(DEV), logits_out=lo)
+    torch.cuda.synchronize()
+    lg = lo.cpu()
+    ref_lg = oracle.router_logits(x, wg)
+    assert np.abs(lg.numpy() - ref_lg).max() <= 1e-5 * np.abs(ref_lg).max() + 1e-6
+    ref = run_oracle(cfg, x, lg, w)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    yg = y.float().cpu().numpy().astype(np.float64)
+    e, er = err_norm(yg, ref["y"]), float(row_errs(yg, ref["y"]).max())
+    say("  err=%.3e per-token %.3e" % (e, er))
+    assert np.isfinite(yg).all()
+    assert e <= TOL[c["dtype"]] and er <= (TOL_TOKEN_FP8 if fp8 else TOL["bf16"]), (e, er)
