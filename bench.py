@@ -68,8 +68,8 @@ TRAFFIC = {
               "bytes_per_launch": 240921788},
     "deepseek": {"src_sha256": "6f5c6fbb7854f74b5824eaab3d58e3a4d7a0fd3d985fff56850075a58ead077a",
                  "bytes_per_launch": 3292697022},
-    "prefill": {"src_sha256": "2773913f52c614fce1038894c6cc6238753670ceaee3fb4ea90f382fa708f5cb",
-                "bytes_per_launch": 3031852382},
+    "prefill": {"src_sha256": "03c79ae18bdf7882c8bb719695f3be451b6ed688155ea513e78d2fa19b851177",
+                "bytes_per_launch": 3019611436},
 }
 
 
